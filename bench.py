@@ -1,0 +1,245 @@
+"""Benchmark of the CCA / CCGQA forward pass on one MI355X.
+
+One step is one pass of the whole hot path over synthetic inputs resident in
+HBM: a CCA prefill of the 4 x 2048-token batch (E = 2048, 8 latent heads of
+64, compression 4) followed by one CCGQA decode step of 64 sequences against
+a 32768-token latent cache (16 query / 4 kv heads of 64).  Both calls go
+through libcca's C ABI on torch's current HIP stream.
+
+Prints ONE JSON line.  ``value`` is prefill tokens per second of prefill time;
+the decode step's HBM rate and the attention kernel's MFMA rate are reported
+next to it.  A second timed pass launches the same kernels stage by stage
+with HIP events between them to get per-kernel durations for the roofline.
+The fp64 oracle is timed on the host cores on a bounded sample of the same
+prefill workload (``cpu_baseline``).
+
+    python bench.py [--steps K] [--warmup W] [--prefill WORKLOAD] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CCA prefill tokens/sec and attn TFLOP/s vs MFMA peak; decode HBM GB/s"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--prefill", default="cca_prefill_b4_t2048")
+    p.add_argument("--decode", default="ccgqa_decode_b64_l32768")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def upload_weights(cca, T, W, dev):
+    import torch
+    return cca.Weights(T.to_device(W.w_qkv_s, dev), T.to_device(W.w_o_s, dev),
+                       torch.from_numpy(W.q_seq_taps).to(dev), torch.from_numpy(W.k_seq_taps).to(dev),
+                       torch.from_numpy(W.q_chan_taps).to(dev), torch.from_numpy(W.k_chan_taps).to(dev),
+                       torch.from_numpy(W.tau).to(dev))
+
+
+def algorithmic(sp, sd):
+    """Algorithmic work per launch of each kernel (what the method must move or
+    compute, not padded or masked work)."""
+    B, T, E = sp.batch, sp.seq_len, sp.d_model
+    eq, ekv, N = sp.e_q, sp.e_kv, sp.n_qkv
+    esz = 2 if sp.dtype == "bf16" else 4
+    Lk = sd.cache_len + 1
+    return {
+        # bytes: read qkv~ (fp32) + write q, k (16-bit) and v (storage type)
+        "convmix_bytes": B * T * N * 4 + B * T * (eq + ekv) * 2 + B * T * ekv * esz,
+        # causal latent attention: 2 matmuls of 2*d flops per visible (query, key) pair
+        "attn_flops": 2 * 2 * B * sp.n_q_heads * sp.head_dim * T * (T + 1) / 2,
+        "downproj_flops": 2 * B * T * N * E,
+        "upproj_flops": 2 * B * T * E * eq,
+        # decode attention streams K and V of Lk keys once
+        "decode_attn_bytes": 2 * sd.batch * sd.n_kv_heads * Lk * sd.head_dim * 2,
+    }
+
+
+def cpu_baseline(sp, seconds):
+    """The fp64 oracle on the host cores: whole sequences of the prefill
+    workload until about `seconds` of CPU time are spent."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+    import oracle.cca as O
+    from synth import make_prefill
+    one = sp.with_(batch=1)
+    P = make_prefill(one, seed=0)
+    w = P.weights.f64()
+    done, t0 = 0, time.perf_counter()
+    while True:
+        O.prefill(P.x, w, one)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= sp.batch:
+            break
+    return {"value": done * one.seq_len / el, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of the {sp.batch} sequences of the prefill workload "
+                      f"(T={one.seq_len}, E={one.d_model}, {one.n_q_heads}x{one.head_dim} heads), "
+                      f"fp64 NumPy, {el:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_amd import cca, tensors as T
+    from synth import make_decode, make_prefill, workload
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    sp, sd = workload(args.prefill), workload(args.decode)
+
+    # ---- inputs (seeded, synthetic), resident in HBM before timing ----------
+    t_gen = time.perf_counter()
+    P = make_prefill(sp, seed=0)
+    D = make_decode(sd, seed=0)
+    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    pw = upload_weights(cca, T, P.weights, dev)
+    dw = upload_weights(cca, T, D.weights, dev)
+    pcfg, dcfg = cca.make_config(sp), cca.make_config(sd)
+    x = T.to_device(P.x_s, dev)
+    y = torch.empty_like(x)
+    pws = T.workspace(cca.prefill_workspace_size(pcfg), dev)
+    st = cca.State(T.to_device(D.k_cache_s, dev), T.to_device(D.v_cache_s, dev), D.capacity,
+                   T.to_device(D.conv_q_s, dev), T.to_device(D.conv_k_s, dev),
+                   T.to_device(D.vshift_s, dev))
+    del D.k_cache_s, D.v_cache_s
+    xt = T.to_device(D.x_s, dev)
+    yt = torch.empty_like(xt)
+    L = sd.cache_len
+    dws = T.workspace(cca.decode_workspace_size(dcfg, L), dev)
+    torch.cuda.synchronize()
+
+    def step():
+        cca.prefill_forward(pcfg, pw, x, y, pws)
+        cca.decode_step(dcfg, dw, xt, L, st, st, yt, dws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    # ---- timed region 1: the public entry points ---------------------------
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        cca.prefill_forward(pcfg, pw, x, y, pws)
+        ev[i][1].record()
+        cca.decode_step(dcfg, dw, xt, L, st, st, yt, dws)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prefill_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    decode_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ms_per_step = wall * 1e3 / K
+    print(f"[bench] timed {K} steps: prefill {prefill_ms:.3f} ms decode {decode_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+
+    # ---- timed region 2: stage by stage, HIP events between kernels --------
+    names = ["downproj", "convmix", "attention", "upproj",
+             "dec_downproj", "dec_mix", "dec_attention", "dec_upproj"]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        e = sev[i]
+        e[0].record()
+        cca.stage_downproj(pcfg, pw, x, pws); e[1].record()
+        cca.stage_convmix(pcfg, pw, pws); e[2].record()
+        cca.stage_attention(pcfg, pw, pws); e[3].record()
+        cca.stage_upproj(pcfg, pw, y, pws); e[4].record()
+        cca.stage_decode_downproj(dcfg, dw, xt, L, dws); e[5].record()
+        cca.stage_decode_mix(dcfg, dw, L, st, st, dws); e[6].record()
+        cca.stage_decode_attention(dcfg, dw, L, st, dws); e[7].record()
+        cca.stage_decode_upproj(dcfg, dw, L, yt, dws); e[8].record()
+    torch.cuda.synchronize()
+    stage_ms = {n: sum(sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(K)) / K
+                for j, n in enumerate(names)}
+
+    alg = algorithmic(sp, sd)
+    attn_tflops = alg["attn_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
+    conv_gbs = alg["convmix_bytes"] / (stage_ms["convmix"] * 1e-3) / 1e9
+    dec_gbs = alg["decode_attn_bytes"] / (stage_ms["dec_attention"] * 1e-3) / 1e9
+    dec_step_gbs = alg["decode_attn_bytes"] / (decode_ms * 1e-3) / 1e9
+    mfma_peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+
+    rooflines = {
+        "dec_attention": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                          "traffic": None},
+        "attention": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": mfma_peak,
+                      "unit": "TFLOP/s", "frac": round(attn_tflops / mfma_peak, 4), "traffic": None},
+        "convmix": {"bound": "hbm", "achieved": round(conv_gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(conv_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    for g in ("downproj", "upproj"):
+        tf = alg[f"{g}_flops"] / (stage_ms[g] * 1e-3) / 1e12
+        rooflines[g] = {"bound": "mfma", "achieved": round(tf, 1), "peak": mfma_peak,
+                        "unit": "TFLOP/s", "frac": round(tf / mfma_peak, 4), "traffic": None}
+    dominant = max(stage_ms, key=stage_ms.get)
+    dom_key = dominant if dominant in rooflines else "dec_attention"
+
+    out = {
+        "metric": METRIC,
+        "value": round(sp.tokens / (prefill_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": sp.dtype, "data": "synthetic",
+        "config": {
+            "workload": f"{args.prefill} prefill (B={sp.batch}, T={sp.seq_len}, E={sp.d_model}, "
+                        f"{sp.n_q_heads}q/{sp.n_kv_heads}kv x {sp.head_dim}) + {args.decode} decode step "
+                        f"(B={sd.batch}, cache {sd.cache_len}, {sd.n_q_heads}q/{sd.n_kv_heads}kv x {sd.head_dim})",
+            "global_batch": sp.batch, "seq_len": sp.seq_len, "parallelism": "single GPU",
+            "value_is": "prefill tokens / prefill device time (HIP events)",
+        },
+        "prefill_ms": round(prefill_ms, 4),
+        "decode_ms": round(decode_ms, 4),
+        "decode_step_hbm_gbs": round(dec_step_gbs, 1),
+        "attn_tflops": round(attn_tflops, 1),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": dict(rooflines[dom_key], kernel=dom_key,
+                         algorithmic_per_launch=(alg["decode_attn_bytes"] if dom_key == "dec_attention"
+                                                 else None)),
+        "rooflines": rooflines,
+    }
+    if not args.no_cpu:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(sp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,253 @@
+"""ctypes binding of libcca (include/cca.h).
+
+Argument marshalling only: torch tensors are passed as device pointers and
+torch's current HIP stream as the stream; every step of the forward pass runs
+in the library's HIP kernels.  There is no fallback: if libcca.so is missing
+or a call returns a non-OK status, this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcca.so")
+
+CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_WORKSPACE, CCA_ERR_HIP = range(5)
+CCA_BF16, CCA_F32 = 0, 1
+WS_QKV, WS_Q, WS_K, WS_VT, WS_O, WS_PART, WS_COUNT = range(7)
+
+# Every entry point declared in include/cca.h.
+EXPORTS = (
+    "cca_validate_config", "cca_prefill_workspace_size", "cca_decode_workspace_size",
+    "cca_prefill_forward", "cca_decode_step", "cca_status_string",
+    "cca_prefill_workspace_layout", "cca_decode_workspace_layout",
+    "cca_stage_downproj", "cca_stage_convmix", "cca_stage_attention", "cca_stage_upproj",
+    "cca_stage_decode_downproj", "cca_stage_decode_mix", "cca_stage_decode_attention",
+    "cca_stage_decode_upproj",
+)
+
+
+class CCAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Config(C.Structure):
+    _fields_ = [
+        ("batch", C.c_int32), ("seq_len", C.c_int32), ("d_model", C.c_int32),
+        ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+        ("seq_conv_k", C.c_int32), ("chan_conv_k", C.c_int32),
+        ("use_qk_mean", C.c_int32), ("use_value_shift", C.c_int32), ("use_qk_norm", C.c_int32),
+        ("rope_base", C.c_float), ("norm_eps", C.c_float), ("dtype", C.c_int32),
+    ]
+
+
+class _Weights(C.Structure):
+    _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p),
+                ("q_seq_taps", C.c_void_p), ("k_seq_taps", C.c_void_p),
+                ("q_chan_taps", C.c_void_p), ("k_chan_taps", C.c_void_p), ("tau", C.c_void_p)]
+
+
+class _State(C.Structure):
+    _fields_ = [("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("capacity", C.c_int32),
+                ("reserved", C.c_int32), ("conv_q", C.c_void_p), ("conv_k", C.c_void_p),
+                ("vshift", C.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m efficient_transformer_attention_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    P = C.POINTER
+    cfgp, wp, sp, vp, sz = P(Config), P(_Weights), P(_State), C.c_void_p, C.c_size_t
+    sig = {
+        "cca_validate_config": (C.c_int, [cfgp]),
+        "cca_prefill_workspace_size": (sz, [cfgp]),
+        "cca_decode_workspace_size": (sz, [cfgp, C.c_int32]),
+        "cca_prefill_workspace_layout": (C.c_int, [cfgp, P(sz)]),
+        "cca_decode_workspace_layout": (C.c_int, [cfgp, C.c_int32, P(sz)]),
+        "cca_prefill_forward": (C.c_int, [cfgp, wp, vp, vp, sp, vp, sz, vp]),
+        "cca_decode_step": (C.c_int, [cfgp, wp, vp, C.c_int32, sp, sp, vp, vp, sz, vp]),
+        "cca_status_string": (C.c_char_p, [C.c_int]),
+        "cca_stage_downproj": (C.c_int, [cfgp, wp, vp, vp, sz, vp]),
+        "cca_stage_convmix": (C.c_int, [cfgp, wp, sp, vp, sz, vp]),
+        "cca_stage_attention": (C.c_int, [cfgp, wp, vp, sz, vp]),
+        "cca_stage_upproj": (C.c_int, [cfgp, wp, vp, vp, sz, vp]),
+        "cca_stage_decode_downproj": (C.c_int, [cfgp, wp, vp, C.c_int32, vp, sz, vp]),
+        "cca_stage_decode_mix": (C.c_int, [cfgp, wp, C.c_int32, sp, sp, vp, sz, vp]),
+        "cca_stage_decode_attention": (C.c_int, [cfgp, wp, C.c_int32, sp, vp, sz, vp]),
+        "cca_stage_decode_upproj": (C.c_int, [cfgp, wp, C.c_int32, vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.cca_status_string(int(status)).decode()
+
+
+def make_config(shape) -> Config:
+    """Config from any object with the cca_config field names (dtype given as
+    "bf16" / "f32" or as the enum value)."""
+    dt = shape.dtype
+    if isinstance(dt, str):
+        dt = {"bf16": CCA_BF16, "f32": CCA_F32}[dt]
+    return Config(int(shape.batch), int(shape.seq_len), int(shape.d_model), int(shape.n_q_heads),
+                  int(shape.n_kv_heads), int(shape.head_dim), int(shape.seq_conv_k),
+                  int(shape.chan_conv_k), int(shape.use_qk_mean), int(shape.use_value_shift),
+                  int(shape.use_qk_norm), float(shape.rope_base), float(shape.norm_eps), int(dt))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("libcca takes contiguous device tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(getattr(stream, "cuda_stream", stream))
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class Weights:
+    """Device tensors of one layer's weights (see cca_weights in include/cca.h)."""
+    w_qkv: object
+    w_o: object
+    q_seq_taps: object
+    k_seq_taps: object
+    q_chan_taps: object
+    k_chan_taps: object
+    tau: object
+
+    def struct(self) -> _Weights:
+        return _Weights(_ptr(self.w_qkv), _ptr(self.w_o), _ptr(self.q_seq_taps),
+                        _ptr(self.k_seq_taps), _ptr(self.q_chan_taps), _ptr(self.k_chan_taps),
+                        _ptr(self.tau))
+
+
+@dataclass
+class State:
+    """Device tensors of a decode state (see cca_state in include/cca.h)."""
+    k_cache: object = None
+    v_cache: object = None
+    capacity: int = 0
+    conv_q: object = None
+    conv_k: object = None
+    vshift: object = None
+
+    def struct(self) -> _State:
+        return _State(_ptr(self.k_cache), _ptr(self.v_cache), int(self.capacity), 0,
+                      _ptr(self.conv_q), _ptr(self.conv_k), _ptr(self.vshift))
+
+
+def _check(status: int, where: str):
+    if status != CCA_OK:
+        raise CCAError(status, where)
+
+
+def validate_config(cfg: Config) -> int:
+    return lib.cca_validate_config(C.byref(cfg))
+
+
+def prefill_workspace_size(cfg: Config) -> int:
+    return lib.cca_prefill_workspace_size(C.byref(cfg))
+
+
+def decode_workspace_size(cfg: Config, cache_len: int) -> int:
+    return lib.cca_decode_workspace_size(C.byref(cfg), int(cache_len))
+
+
+def prefill_workspace_layout(cfg: Config) -> list:
+    off = (C.c_size_t * WS_COUNT)()
+    _check(lib.cca_prefill_workspace_layout(C.byref(cfg), off), "cca_prefill_workspace_layout")
+    return list(off)
+
+
+def decode_workspace_layout(cfg: Config, cache_len: int) -> list:
+    off = (C.c_size_t * WS_COUNT)()
+    _check(lib.cca_decode_workspace_layout(C.byref(cfg), int(cache_len), off),
+           "cca_decode_workspace_layout")
+    return list(off)
+
+
+def prefill_forward(cfg: Config, w: Weights, x, y, workspace, state_out: Optional[State] = None,
+                    stream=None):
+    so = C.byref(state_out.struct()) if state_out is not None else None
+    _check(lib.cca_prefill_forward(C.byref(cfg), C.byref(w.struct()), _ptr(x), _ptr(y), so,
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "cca_prefill_forward")
+
+
+def decode_step(cfg: Config, w: Weights, x_t, cache_len: int, state_in: State, state_out: State,
+                y_t, workspace, stream=None):
+    _check(lib.cca_decode_step(C.byref(cfg), C.byref(w.struct()), _ptr(x_t), int(cache_len),
+                               C.byref(state_in.struct()), C.byref(state_out.struct()), _ptr(y_t),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream)), "cca_decode_step")
+
+
+def _wsb(ws):
+    return ws.numel() * ws.element_size()
+
+
+def stage_downproj(cfg, w, x, workspace, stream=None):
+    _check(lib.cca_stage_downproj(C.byref(cfg), C.byref(w.struct()), _ptr(x), _ptr(workspace),
+                                  _wsb(workspace), _stream(stream)), "cca_stage_downproj")
+
+
+def stage_convmix(cfg, w, workspace, state_out: Optional[State] = None, stream=None):
+    so = C.byref(state_out.struct()) if state_out is not None else None
+    _check(lib.cca_stage_convmix(C.byref(cfg), C.byref(w.struct()), so, _ptr(workspace),
+                                 _wsb(workspace), _stream(stream)), "cca_stage_convmix")
+
+
+def stage_attention(cfg, w, workspace, stream=None):
+    _check(lib.cca_stage_attention(C.byref(cfg), C.byref(w.struct()), _ptr(workspace),
+                                   _wsb(workspace), _stream(stream)), "cca_stage_attention")
+
+
+def stage_upproj(cfg, w, y, workspace, stream=None):
+    _check(lib.cca_stage_upproj(C.byref(cfg), C.byref(w.struct()), _ptr(y), _ptr(workspace),
+                                _wsb(workspace), _stream(stream)), "cca_stage_upproj")
+
+
+def stage_decode_downproj(cfg, w, x_t, cache_len, workspace, stream=None):
+    _check(lib.cca_stage_decode_downproj(C.byref(cfg), C.byref(w.struct()), _ptr(x_t),
+                                         int(cache_len), _ptr(workspace), _wsb(workspace),
+                                         _stream(stream)), "cca_stage_decode_downproj")
+
+
+def stage_decode_mix(cfg, w, cache_len, state_in: State, state_out: State, workspace, stream=None):
+    _check(lib.cca_stage_decode_mix(C.byref(cfg), C.byref(w.struct()), int(cache_len),
+                                    C.byref(state_in.struct()), C.byref(state_out.struct()),
+                                    _ptr(workspace), _wsb(workspace), _stream(stream)),
+           "cca_stage_decode_mix")
+
+
+def stage_decode_attention(cfg, w, cache_len, state_in: State, workspace, stream=None):
+    _check(lib.cca_stage_decode_attention(C.byref(cfg), C.byref(w.struct()), int(cache_len),
+                                          C.byref(state_in.struct()), _ptr(workspace),
+                                          _wsb(workspace), _stream(stream)),
+           "cca_stage_decode_attention")
+
+
+def stage_decode_upproj(cfg, w, cache_len, y_t, workspace, stream=None):
+    _check(lib.cca_stage_decode_upproj(C.byref(cfg), C.byref(w.struct()), int(cache_len), _ptr(y_t),
+                                       _ptr(workspace), _wsb(workspace), _stream(stream)),
+           "cca_stage_decode_upproj")

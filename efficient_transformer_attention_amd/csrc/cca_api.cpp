@@ -1,0 +1,501 @@
+// Host side of libcca: argument validation, workspace layout and the launch
+// sequence of the prefill and decode passes.  Every check runs before the
+// first launch; launches are asynchronous on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "cca.h"
+#include "cca_device.h"
+#include "cca_launch.h"
+
+using namespace cca;
+
+namespace {
+
+constexpr size_t WS_ALIGN = 256;
+constexpr int TILE_T = 128;   // token padding of the attention operands
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool debug_sync() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = getenv("CCA_DEBUG_SYNC");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+cca_status check_launch(hipError_t e, hipStream_t stream) {
+  if (e != hipSuccess) return CCA_ERR_HIP;
+  if (debug_sync()) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return CCA_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return CCA_ERR_HIP;
+  }
+  return CCA_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == CCA_F32 ? 4 : 2; }
+
+// Storage type of the normalised, rotated q and k handed to the attention
+// kernel: fp16 when they are unit vectors (10 mantissa bits instead of
+// bf16's 7, no range concern), else the storage dtype.
+size_t qk_elem_size(const cca_config &c) {
+  if (c.dtype == CCA_F32) return 4;
+  return 2;
+}
+bool qk_is_f16(const cca_config &c) { return c.dtype == CCA_BF16 && c.use_qk_norm; }
+
+int padded_T(int T) { return (T + TILE_T - 1) / TILE_T * TILE_T; }
+
+MixShape mix_shape(const cca_config &c) {
+  MixShape s;
+  s.B = c.batch;
+  s.T = c.seq_len;
+  s.Tp = padded_T(c.seq_len);
+  s.Hq = c.n_q_heads;
+  s.Hkv = c.n_kv_heads;
+  s.G = c.n_q_heads / c.n_kv_heads;
+  s.d = c.head_dim;
+  s.ks = c.seq_conv_k;
+  s.kc = c.chan_conv_k;
+  s.use_mean = c.use_qk_mean;
+  s.use_shift = c.use_value_shift;
+  s.use_norm = c.use_qk_norm;
+  s.rope_base = c.rope_base;
+  s.eps = c.norm_eps;
+  return s;
+}
+
+cca_status validate_shape(const cca_config *c, bool need_seq) {
+  if (!c) return CCA_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->d_model < 8 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1)
+    return CCA_ERR_INVALID_ARG;
+  if (need_seq && c->seq_len < 1) return CCA_ERR_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads) return CCA_ERR_INVALID_ARG;
+  if (c->d_model % 8) return CCA_ERR_INVALID_ARG;
+  if (c->use_value_shift && (c->n_kv_heads % 2)) return CCA_ERR_INVALID_ARG;
+  if (!(c->norm_eps > 0.f) || !(c->rope_base >= 0.f)) return CCA_ERR_INVALID_ARG;
+  if ((unsigned)c->use_qk_mean > 1u || (unsigned)c->use_value_shift > 1u ||
+      (unsigned)c->use_qk_norm > 1u)
+    return CCA_ERR_INVALID_ARG;
+  if (c->dtype != CCA_BF16 && c->dtype != CCA_F32) return CCA_ERR_UNSUPPORTED;
+  const int d = c->head_dim;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return CCA_ERR_UNSUPPORTED;
+  if (c->seq_conv_k < 1 || c->seq_conv_k > 4 || c->chan_conv_k < 1 || c->chan_conv_k > 4)
+    return CCA_ERR_UNSUPPORTED;
+  if (!convmix_fits(c->n_q_heads / c->n_kv_heads, d)) return CCA_ERR_UNSUPPORTED;
+  // index arithmetic stays in 32-bit for per-row offsets
+  const long long N = (long long)(c->n_q_heads + 2 * c->n_kv_heads) * d;
+  if ((long long)c->batch * (need_seq ? padded_T(c->seq_len) : 1) * (N > c->d_model ? N : c->d_model) >
+      (1ll << 40))
+    return CCA_ERR_UNSUPPORTED;
+  if ((long long)c->batch * (need_seq ? c->seq_len : 1) > (1ll << 31) - 1) return CCA_ERR_UNSUPPORTED;
+  return CCA_OK;
+}
+
+struct Layout {
+  size_t off[CCA_WS_COUNT];
+  size_t total;
+};
+
+Layout prefill_layout(const cca_config &c) {
+  Layout L;
+  for (int i = 0; i < CCA_WS_COUNT; ++i) L.off[i] = SIZE_MAX;
+  const size_t B = c.batch, T = c.seq_len, Tp = padded_T(c.seq_len), d = c.head_dim;
+  const size_t eq = (size_t)c.n_q_heads * d, ekv = (size_t)c.n_kv_heads * d;
+  const size_t N = eq + 2 * ekv;
+  size_t o = 0;
+  L.off[CCA_WS_QKV] = o; o = align_up(o + B * T * N * 4, WS_ALIGN);
+  L.off[CCA_WS_Q] = o;   o = align_up(o + B * c.n_q_heads * Tp * d * qk_elem_size(c), WS_ALIGN);
+  L.off[CCA_WS_K] = o;   o = align_up(o + B * c.n_kv_heads * Tp * d * qk_elem_size(c), WS_ALIGN);
+  L.off[CCA_WS_VT] = o;  o = align_up(o + B * c.n_kv_heads * d * Tp * elem_size(c.dtype), WS_ALIGN);
+  L.off[CCA_WS_O] = o;   o = align_up(o + B * T * eq * elem_size(c.dtype), WS_ALIGN);
+  L.total = o;
+  return L;
+}
+
+Layout decode_layout(const cca_config &c, int cache_len) {
+  Layout L;
+  for (int i = 0; i < CCA_WS_COUNT; ++i) L.off[i] = SIZE_MAX;
+  const size_t B = c.batch, d = c.head_dim;
+  const size_t eq = (size_t)c.n_q_heads * d, ekv = (size_t)c.n_kv_heads * d;
+  const size_t N = eq + 2 * ekv;
+  size_t o = 0;
+  L.off[CCA_WS_QKV] = o;  o = align_up(o + B * N * 4, WS_ALIGN);
+  L.off[CCA_WS_Q] = o;    o = align_up(o + B * c.n_q_heads * d * 4, WS_ALIGN);
+  L.off[CCA_WS_PART] = o;
+  o = align_up(o + decode_partial_floats(c.batch, c.n_q_heads, c.head_dim, cache_len + 1) * 4, WS_ALIGN);
+  L.off[CCA_WS_O] = o;    o = align_up(o + B * eq * elem_size(c.dtype), WS_ALIGN);
+  L.total = o;
+  return L;
+}
+
+cca_status check_weights(const cca_weights *w) {
+  if (!w || !w->w_qkv || !w->w_o || !w->q_seq_taps || !w->k_seq_taps || !w->q_chan_taps ||
+      !w->k_chan_taps || !w->tau)
+    return CCA_ERR_INVALID_ARG;
+  if (!aligned16(w->w_qkv) || !aligned16(w->w_o)) return CCA_ERR_INVALID_ARG;
+  return CCA_OK;
+}
+
+cca_status check_ws(void *ws, size_t bytes, size_t need) {
+  if (bytes < need) return CCA_ERR_WORKSPACE;
+  if (need && !ws) return CCA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & (WS_ALIGN - 1)) return CCA_ERR_WORKSPACE;
+  return CCA_OK;
+}
+
+MixTaps taps_of(const cca_weights *w) {
+  MixTaps t;
+  t.q_seq = w->q_seq_taps;
+  t.k_seq = w->k_seq_taps;
+  t.q_chan = w->q_chan_taps;
+  t.k_chan = w->k_chan_taps;
+  return t;
+}
+
+StateOut state_of(const cca_state *st) {
+  StateOut s;
+  std::memset(&s, 0, sizeof(s));
+  if (st) {
+    s.k_cache = st->k_cache;
+    s.v_cache = st->v_cache;
+    s.capacity = st->capacity;
+    s.conv_q = st->conv_q;
+    s.conv_k = st->conv_k;
+    s.vshift = st->vshift;
+  }
+  return s;
+}
+
+unsigned char *wsp(void *ws, const Layout &L, int slot) {
+  return static_cast<unsigned char *>(ws) + L.off[slot];
+}
+
+// ---- prefill stages --------------------------------------------------------
+
+cca_status run_downproj(const cca_config &c, const cca_weights *w, const void *x, void *ws,
+                        const Layout &L, hipStream_t st) {
+  const int M = c.batch * c.seq_len, E = c.d_model;
+  const int N = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  float *qkv = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_QKV));
+  hipError_t e;
+  if (c.dtype == CCA_BF16)
+    e = launch_gemm_nt<bf16, float>((const bf16 *)x, (const bf16 *)w->w_qkv, qkv, M, N, E, E, E, N, st);
+  else
+    e = launch_gemm_nt<float, float>((const float *)x, (const float *)w->w_qkv, qkv, M, N, E, E, E, N, st);
+  return check_launch(e, st);
+}
+
+cca_status run_convmix(const cca_config &c, const cca_weights *w, const cca_state *so, void *ws,
+                       const Layout &L, hipStream_t st) {
+  const MixShape s = mix_shape(c);
+  const float *qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
+  hipError_t e;
+  if (c.dtype == CCA_F32) {
+    e = launch_convmix_prefill<float, float>(s, taps_of(w), qkv, (float *)wsp(ws, L, CCA_WS_Q),
+                                             (float *)wsp(ws, L, CCA_WS_K),
+                                             (float *)wsp(ws, L, CCA_WS_VT), state_of(so), st);
+  } else if (qk_is_f16(c)) {
+    e = launch_convmix_prefill<f16, bf16>(s, taps_of(w), qkv, (f16 *)wsp(ws, L, CCA_WS_Q),
+                                          (f16 *)wsp(ws, L, CCA_WS_K),
+                                          (bf16 *)wsp(ws, L, CCA_WS_VT), state_of(so), st);
+  } else {
+    e = launch_convmix_prefill<bf16, bf16>(s, taps_of(w), qkv, (bf16 *)wsp(ws, L, CCA_WS_Q),
+                                           (bf16 *)wsp(ws, L, CCA_WS_K),
+                                           (bf16 *)wsp(ws, L, CCA_WS_VT), state_of(so), st);
+  }
+  return check_launch(e, st);
+}
+
+cca_status run_attention(const cca_config &c, const cca_weights *w, void *ws, const Layout &L,
+                         hipStream_t st) {
+  const MixShape s = mix_shape(c);
+  hipError_t e;
+  if (c.dtype == CCA_F32) {
+    e = launch_attention_prefill<float, float>(s, (const float *)wsp(ws, L, CCA_WS_Q),
+                                               (const float *)wsp(ws, L, CCA_WS_K),
+                                               (const float *)wsp(ws, L, CCA_WS_VT), w->tau,
+                                               (float *)wsp(ws, L, CCA_WS_O), st);
+  } else if (qk_is_f16(c)) {
+    e = launch_attention_prefill<f16, bf16>(s, (const f16 *)wsp(ws, L, CCA_WS_Q),
+                                            (const f16 *)wsp(ws, L, CCA_WS_K),
+                                            (const bf16 *)wsp(ws, L, CCA_WS_VT), w->tau,
+                                            (bf16 *)wsp(ws, L, CCA_WS_O), st);
+  } else {
+    e = launch_attention_prefill<bf16, bf16>(s, (const bf16 *)wsp(ws, L, CCA_WS_Q),
+                                             (const bf16 *)wsp(ws, L, CCA_WS_K),
+                                             (const bf16 *)wsp(ws, L, CCA_WS_VT), w->tau,
+                                             (bf16 *)wsp(ws, L, CCA_WS_O), st);
+  }
+  return check_launch(e, st);
+}
+
+cca_status run_upproj(const cca_config &c, const cca_weights *w, void *y, void *ws,
+                      const Layout &L, int M, hipStream_t st) {
+  const int E = c.d_model, eq = c.n_q_heads * c.head_dim;
+  hipError_t e;
+  if (c.dtype == CCA_BF16)
+    e = launch_gemm_nt<bf16, bf16>((const bf16 *)wsp(ws, L, CCA_WS_O), (const bf16 *)w->w_o,
+                                   (bf16 *)y, M, E, eq, eq, eq, E, st);
+  else
+    e = launch_gemm_nt<float, float>((const float *)wsp(ws, L, CCA_WS_O), (const float *)w->w_o,
+                                     (float *)y, M, E, eq, eq, eq, E, st);
+  return check_launch(e, st);
+}
+
+cca_status check_state_out(const cca_config &c, const cca_state *so) {
+  if (!so) return CCA_OK;
+  if ((so->k_cache || so->v_cache) && so->capacity < c.seq_len) return CCA_ERR_INVALID_ARG;
+  if ((so->k_cache && !aligned16(so->k_cache)) || (so->v_cache && !aligned16(so->v_cache)))
+    return CCA_ERR_INVALID_ARG;
+  return CCA_OK;
+}
+
+// ---- decode stages ---------------------------------------------------------
+
+cca_status check_decode_state(const cca_config &c, int32_t L, const cca_state *si,
+                              const cca_state *so) {
+  if (L < 0 || !si || !so) return CCA_ERR_INVALID_ARG;
+  if (!si->k_cache || !si->v_cache || si->capacity <= L) return CCA_ERR_INVALID_ARG;
+  if (!aligned16(si->k_cache) || !aligned16(si->v_cache)) return CCA_ERR_INVALID_ARG;
+  if ((so->k_cache && so->k_cache != si->k_cache) || (so->v_cache && so->v_cache != si->v_cache))
+    return CCA_ERR_INVALID_ARG;
+  if (c.seq_conv_k > 1 && (!si->conv_q || !si->conv_k || !so->conv_q || !so->conv_k))
+    return CCA_ERR_INVALID_ARG;
+  if (c.use_value_shift && (!si->vshift || !so->vshift)) return CCA_ERR_INVALID_ARG;
+  if ((long long)c.batch * c.n_kv_heads * si->capacity * c.head_dim > (1ll << 40))
+    return CCA_ERR_UNSUPPORTED;
+  return CCA_OK;
+}
+
+cca_config decode_cfg(const cca_config *c) {
+  cca_config d = *c;
+  d.seq_len = 1;
+  return d;
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+const char *cca_status_string(cca_status s) {
+  switch (s) {
+    case CCA_OK: return "CCA_OK";
+    case CCA_ERR_INVALID_ARG: return "CCA_ERR_INVALID_ARG: invalid argument";
+    case CCA_ERR_UNSUPPORTED: return "CCA_ERR_UNSUPPORTED: configuration not supported";
+    case CCA_ERR_WORKSPACE: return "CCA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case CCA_ERR_HIP: return "CCA_ERR_HIP: HIP launch or runtime error";
+  }
+  return "CCA_ERR_UNKNOWN";
+}
+
+cca_status cca_validate_config(const cca_config *cfg) { return validate_shape(cfg, true); }
+
+size_t cca_prefill_workspace_size(const cca_config *cfg) {
+  if (validate_shape(cfg, true) != CCA_OK) return 0;
+  return prefill_layout(*cfg).total;
+}
+
+size_t cca_decode_workspace_size(const cca_config *cfg, int32_t cache_len) {
+  if (validate_shape(cfg, false) != CCA_OK || cache_len < 0) return 0;
+  return decode_layout(decode_cfg(cfg), cache_len).total;
+}
+
+cca_status cca_prefill_workspace_layout(const cca_config *cfg, size_t offsets[CCA_WS_COUNT]) {
+  cca_status r = validate_shape(cfg, true);
+  if (r != CCA_OK) return r;
+  if (!offsets) return CCA_ERR_INVALID_ARG;
+  Layout L = prefill_layout(*cfg);
+  for (int i = 0; i < CCA_WS_COUNT; ++i) offsets[i] = L.off[i];
+  return CCA_OK;
+}
+
+cca_status cca_decode_workspace_layout(const cca_config *cfg, int32_t cache_len,
+                                       size_t offsets[CCA_WS_COUNT]) {
+  cca_status r = validate_shape(cfg, false);
+  if (r != CCA_OK) return r;
+  if (!offsets || cache_len < 0) return CCA_ERR_INVALID_ARG;
+  Layout L = decode_layout(decode_cfg(cfg), cache_len);
+  for (int i = 0; i < CCA_WS_COUNT; ++i) offsets[i] = L.off[i];
+  return CCA_OK;
+}
+
+#define CCA_TRY(expr)                 \
+  do {                                \
+    cca_status _r = (expr);           \
+    if (_r != CCA_OK) return _r;      \
+  } while (0)
+
+static cca_status prefill_checks(const cca_config *cfg, const cca_weights *w, void *ws,
+                                 size_t wsb, Layout *L) {
+  CCA_TRY(validate_shape(cfg, true));
+  CCA_TRY(check_weights(w));
+  *L = prefill_layout(*cfg);
+  return check_ws(ws, wsb, L->total);
+}
+
+cca_status cca_prefill_forward(const cca_config *cfg, const cca_weights *w, const void *x, void *y,
+                               const cca_state *state_out, void *ws, size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(prefill_checks(cfg, w, ws, wsb, &L));
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return CCA_ERR_INVALID_ARG;
+  CCA_TRY(check_state_out(*cfg, state_out));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CCA_TRY(run_downproj(*cfg, w, x, ws, L, st));
+  CCA_TRY(run_convmix(*cfg, w, state_out, ws, L, st));
+  CCA_TRY(run_attention(*cfg, w, ws, L, st));
+  return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
+}
+
+cca_status cca_stage_downproj(const cca_config *cfg, const cca_weights *w, const void *x,
+                              void *ws, size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(prefill_checks(cfg, w, ws, wsb, &L));
+  if (!x || !aligned16(x)) return CCA_ERR_INVALID_ARG;
+  return run_downproj(*cfg, w, x, ws, L, reinterpret_cast<hipStream_t>(stream));
+}
+
+cca_status cca_stage_convmix(const cca_config *cfg, const cca_weights *w, const cca_state *so,
+                             void *ws, size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(prefill_checks(cfg, w, ws, wsb, &L));
+  CCA_TRY(check_state_out(*cfg, so));
+  return run_convmix(*cfg, w, so, ws, L, reinterpret_cast<hipStream_t>(stream));
+}
+
+cca_status cca_stage_attention(const cca_config *cfg, const cca_weights *w, void *ws, size_t wsb,
+                               void *stream) {
+  Layout L;
+  CCA_TRY(prefill_checks(cfg, w, ws, wsb, &L));
+  return run_attention(*cfg, w, ws, L, reinterpret_cast<hipStream_t>(stream));
+}
+
+cca_status cca_stage_upproj(const cca_config *cfg, const cca_weights *w, void *y, void *ws,
+                            size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(prefill_checks(cfg, w, ws, wsb, &L));
+  if (!y || !aligned16(y)) return CCA_ERR_INVALID_ARG;
+  return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len,
+                    reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---- decode ----------------------------------------------------------------
+
+static cca_status decode_checks(const cca_config *cfg, const cca_weights *w, int32_t L,
+                                void *ws, size_t wsb, Layout *lay) {
+  CCA_TRY(validate_shape(cfg, false));
+  CCA_TRY(check_weights(w));
+  if (L < 0) return CCA_ERR_INVALID_ARG;
+  *lay = decode_layout(decode_cfg(cfg), L);
+  return check_ws(ws, wsb, lay->total);
+}
+
+static cca_status dec_downproj(const cca_config &c, const cca_weights *w, const void *x_t,
+                               void *ws, const Layout &L, hipStream_t st) {
+  const int M = c.batch, E = c.d_model;
+  const int N = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  float *qkv = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_QKV));
+  hipError_t e;
+  if (c.dtype == CCA_BF16)
+    e = launch_gemm_nt<bf16, float>((const bf16 *)x_t, (const bf16 *)w->w_qkv, qkv, M, N, E, E, E, N, st);
+  else
+    e = launch_gemm_nt<float, float>((const float *)x_t, (const float *)w->w_qkv, qkv, M, N, E, E, E, N, st);
+  return check_launch(e, st);
+}
+
+static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
+                          const cca_state *si, const cca_state *so, void *ws, const Layout &L,
+                          hipStream_t st) {
+  MixShape s = mix_shape(c);
+  s.T = 1;
+  s.Tp = 1;
+  const float *qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
+  float *q = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_Q));
+  hipError_t e;
+  if (c.dtype == CCA_BF16)
+    e = launch_convmix_decode<bf16>(s, taps_of(w), qkv, Lc, state_of(si), state_of(so), q, st);
+  else
+    e = launch_convmix_decode<float>(s, taps_of(w), qkv, Lc, state_of(si), state_of(so), q, st);
+  return check_launch(e, st);
+}
+
+static cca_status dec_attn(const cca_config &c, const cca_weights *w, int32_t Lc,
+                           const cca_state *si, void *ws, const Layout &L, hipStream_t st) {
+  MixShape s = mix_shape(c);
+  s.T = 1;
+  s.Tp = 1;
+  const float *q = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_Q));
+  float *part = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_PART));
+  hipError_t e;
+  if (c.dtype == CCA_BF16)
+    e = launch_attention_decode<bf16>(s, q, (const bf16 *)si->k_cache, (const bf16 *)si->v_cache,
+                                      si->capacity, Lc + 1, w->tau, part,
+                                      (bf16 *)wsp(ws, L, CCA_WS_O), st);
+  else
+    e = launch_attention_decode<float>(s, q, (const float *)si->k_cache,
+                                       (const float *)si->v_cache, si->capacity, Lc + 1, w->tau,
+                                       part, (float *)wsp(ws, L, CCA_WS_O), st);
+  return check_launch(e, st);
+}
+
+cca_status cca_decode_step(const cca_config *cfg, const cca_weights *w, const void *x_t,
+                           int32_t cache_len, const cca_state *si, const cca_state *so, void *y_t,
+                           void *ws, size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
+  if (!x_t || !y_t || !aligned16(x_t) || !aligned16(y_t)) return CCA_ERR_INVALID_ARG;
+  const cca_config c = decode_cfg(cfg);
+  CCA_TRY(check_decode_state(c, cache_len, si, so));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CCA_TRY(dec_downproj(c, w, x_t, ws, L, st));
+  CCA_TRY(dec_mix(c, w, cache_len, si, so, ws, L, st));
+  CCA_TRY(dec_attn(c, w, cache_len, si, ws, L, st));
+  return run_upproj(c, w, y_t, ws, L, c.batch, st);
+}
+
+cca_status cca_stage_decode_downproj(const cca_config *cfg, const cca_weights *w, const void *x_t,
+                                     int32_t cache_len, void *ws, size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
+  if (!x_t || !aligned16(x_t)) return CCA_ERR_INVALID_ARG;
+  return dec_downproj(decode_cfg(cfg), w, x_t, ws, L, reinterpret_cast<hipStream_t>(stream));
+}
+
+cca_status cca_stage_decode_mix(const cca_config *cfg, const cca_weights *w, int32_t cache_len,
+                                const cca_state *si, const cca_state *so, void *ws, size_t wsb,
+                                void *stream) {
+  Layout L;
+  CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
+  const cca_config c = decode_cfg(cfg);
+  CCA_TRY(check_decode_state(c, cache_len, si, so));
+  return dec_mix(c, w, cache_len, si, so, ws, L, reinterpret_cast<hipStream_t>(stream));
+}
+
+cca_status cca_stage_decode_attention(const cca_config *cfg, const cca_weights *w,
+                                      int32_t cache_len, const cca_state *si, void *ws,
+                                      size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
+  const cca_config c = decode_cfg(cfg);
+  CCA_TRY(check_decode_state(c, cache_len, si, si));
+  return dec_attn(c, w, cache_len, si, ws, L, reinterpret_cast<hipStream_t>(stream));
+}
+
+cca_status cca_stage_decode_upproj(const cca_config *cfg, const cca_weights *w, int32_t cache_len,
+                                   void *y_t, void *ws, size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
+  if (!y_t || !aligned16(y_t)) return CCA_ERR_INVALID_ARG;
+  const cca_config c = decode_cfg(cfg);
+  return run_upproj(c, w, y_t, ws, L, c.batch, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

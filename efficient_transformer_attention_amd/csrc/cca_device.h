@@ -1,0 +1,134 @@
+// Device-side building blocks shared by the libcca kernels (gfx950 only).
+//
+// MFMA conventions used throughout (32x32 output tiles, wave64):
+//   A operand (M x K): lane l supplies row (l % 32), k-slots (l / 32) * KS .. + KS-1
+//   B operand (K x N): lane l supplies column (l % 32), the same k-slots
+//   C / accumulator:   lane l holds C[8*j + 4*(l/32) + i][l % 32] in acc[4*j + i]
+// KS = 8 for the 16-bit types (v_mfma_f32_32x32x16_{bf16,f16}) and 1 for fp32
+// (v_mfma_f32_32x32x2_f32).  Only the pairing of A's and B's k-slots matters
+// for a product, so any bijection between k-slots and the contraction index
+// is valid as long as A and B use the same one.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cca {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v) { return (T)v; }
+
+// ---------------------------------------------------------------------------
+// MFMA traits: one 32x32 tile, contraction chunk of 2*KS per instruction
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma32;
+
+template <> struct Mfma32<bf16> {
+  static constexpr int KS = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma32<f16> {
+  static constexpr int KS = 8;
+  typedef f16x8 frag;
+  __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma32<float> {
+  static constexpr int KS = 1;
+  typedef float frag;
+  __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Load KS consecutive elements (one fragment) from LDS or global memory.
+template <typename T>
+__device__ __forceinline__ typename Mfma32<T>::frag load_frag(const T *p) {
+  return *reinterpret_cast<const typename Mfma32<T>::frag *>(p);
+}
+
+// Pack KS fp32 values into a fragment of type T.
+template <typename T>
+__device__ __forceinline__ typename Mfma32<T>::frag pack_frag(const float *v) {
+  typename Mfma32<T>::frag f;
+  if constexpr (Mfma32<T>::KS == 1) {
+    f = (T)v[0];
+  } else {
+#pragma unroll
+    for (int s = 0; s < Mfma32<T>::KS; ++s) f[s] = (T)v[s];
+  }
+  return f;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte vector memory helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+__device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
+
+__device__ __forceinline__ u32x4 zero_u32x4() {
+  u32x4 z;
+  z[0] = z[1] = z[2] = z[3] = 0u;
+  return z;
+}
+
+// XOR swizzle of 16-byte chunks inside an LDS row: keeps the lanes of one
+// ds_read_b128 phase (rows r..r+7, same logical chunk) on distinct banks.
+// `row_chunks` is the number of 16-byte chunks per row (a power of two).
+__device__ __forceinline__ int swz(int row, int byte_in_row, int row_chunks) {
+  int chunk = byte_in_row >> 4;
+  int phys = chunk ^ (row & (row_chunks - 1) & 7);
+  return (phys << 4) | (byte_in_row & 15);
+}
+
+// Bits 2 and 3 of a token index exchanged: the key order inside the
+// transposed value tile, so that the 8 keys one lane feeds to the P*V MFMA
+// (keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key chunk) are contiguous.
+__host__ __device__ __forceinline__ int vt_perm(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
+// Physical XCD-aware block remap: the hardware deals consecutive workgroup
+// ids round-robin to the 8 XCDs; remapping so that each XCD receives a
+// contiguous run of logical blocks keeps blocks that share operands in one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int nx = 8;
+  int per = nblocks / nx;               // full rounds
+  int rem = nblocks - per * nx;
+  int xcd = bid % nx, slot = bid / nx;
+  // XCDs 0..rem-1 own per+1 logical blocks, the rest own per.
+  int base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return base + slot;
+}
+
+}  // namespace cca

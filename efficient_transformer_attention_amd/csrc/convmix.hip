@@ -1,0 +1,418 @@
+// Fused latent mixing of the CCA forward pass (gfx950), memory bound.
+//
+// For every token and latent head, from the fp32 down-projection output:
+//   a2 causal sequence conv, depthwise, lag-indexed k_s taps per channel
+//   a3 channel conv: one k_c-tap filter per head sliding along the channel
+//      index, zero padded inside the head
+//      [GS-EN "2. Methodology" / Convolutional Mixing]
+//   a4 q-k-mean: the mean of the pre-convolution q~ and k~ added to the
+//      convolved q and k; with G query heads per kv head, q head h meets k~ of
+//      its group and kv head g meets the average q~ of its G heads
+//      [GS-EN "2. Methodology" / Q-K-Mean]
+//   a5 value-shift: the upper half of the kv heads take the previous token's
+//      value [GS-EN "2. Methodology" / Value-Shift]
+//   a6 L2 normalisation per head, x / max(||x||, eps)
+//   a7 RoPE, pairs (2i, 2i+1), angle pos * base^(-2i/d) evaluated in double
+//      and reduced modulo 2*pi before the fp32 sin/cos
+//      [GS-EN "2. Methodology" / RoPE Integration]
+//
+// Work split: one workgroup per (batch b, kv group g, chunk of TC tokens).
+// The group's pre-conv columns (G query heads, its key head, its value head)
+// for tokens t0-3 .. t0+TC-1 are staged in LDS with coalesced 16-byte loads
+// (the 3-token halo of the causal window comes along), together with the
+// group's taps and a cos/sin table of the chunk.  A head of d channels is
+// handled by d/4 lanes of 4 consecutive channels each, so the channel
+// convolution needs only three lane shifts and the RoPE pairs stay inside a
+// lane; the L2 norm is a reduction over the d/4 lanes.  The value head is
+// written transposed (d-major) for the attention kernel, straight from the
+// LDS tile.
+#include "cca_device.h"
+#include "cca_launch.h"
+
+namespace cca {
+
+static constexpr int HALO = 3;   // k_s - 1 for the largest supported k_s = 4
+
+// fp64-accurate rotation of pair i at position pos.
+__device__ __forceinline__ float2 rope_cs(int pos, int i, int d, float base) {
+  if (base == 0.f) return make_float2(1.f, 0.f);
+  const double theta = pow((double)base, -2.0 * (double)i / (double)d);
+  const double phi = (double)pos * theta;
+  const double TWO_PI_HI = 6.283185307179586;        // nearest double to 2*pi
+  const double TWO_PI_LO = 2.4492935982947064e-16;   // 2*pi - TWO_PI_HI
+  const double n = rint(phi * (1.0 / TWO_PI_HI));
+  double r = fma(-n, TWO_PI_HI, phi);
+  r = fma(-n, TWO_PI_LO, r);
+  float sn, cs;
+  sincosf((float)r, &sn, &cs);
+  return make_float2(cs, sn);
+}
+
+template <typename T> struct Store4;
+template <> struct Store4<float> {
+  __device__ __forceinline__ static void st(float *p, const float *v) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+};
+template <> struct Store4<f16> {
+  __device__ __forceinline__ static void st(f16 *p, const float *v) {
+    *reinterpret_cast<f16x4 *>(p) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+  }
+};
+template <> struct Store4<bf16> {
+  __device__ __forceinline__ static void st(bf16 *p, const float *v) {
+    *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  }
+};
+
+// Steps a2-a7 for one (token row r of the LDS tile, head slot) unit.  Slot
+// 0..G-1 are the group's query heads, slot G its key head.  The lane holds
+// channels 4*li .. 4*li+3.  `tile` rows are tokens (row r+HALO is the current
+// token), columns [q heads | k head | v head] of the group, CW floats wide.
+template <int D>
+__device__ __forceinline__ void mix_unit(const float *tile, int CW, int r, int slot, int G,
+                                         int li, const float *staps, const float *ctaps,
+                                         const MixShape &s, float2 cs0, float2 cs1, float y[4]) {
+  constexpr int LPU = D / 4;
+  const int col = slot * D + 4 * li;
+  float a[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = fmaf(staps[(col + c) * 4 + j], tile[(r + HALO - j) * CW + col + c], acc);
+    a[c] = acc;
+  }
+  // values of the three channels below this lane's first one (previous lane)
+  float p1 = __shfl_up(a[1], 1, LPU), p2 = __shfl_up(a[2], 1, LPU), p3 = __shfl_up(a[3], 1, LPU);
+  if (li == 0) p1 = p2 = p3 = 0.f;
+  const float w0 = ctaps[slot * 4 + 0], w1 = ctaps[slot * 4 + 1], w2 = ctaps[slot * 4 + 2],
+              w3 = ctaps[slot * 4 + 3];
+  float b[4];
+  b[0] = w0 * a[0] + w1 * p3 + w2 * p2 + w3 * p1;
+  b[1] = w0 * a[1] + w1 * a[0] + w2 * p3 + w3 * p2;
+  b[2] = w0 * a[2] + w1 * a[1] + w2 * a[0] + w3 * p3;
+  b[3] = w0 * a[3] + w1 * a[2] + w2 * a[1] + w3 * a[0];
+
+  if (s.use_mean) {
+    const float *cur = tile + (r + HALO) * CW;
+    if (slot < G) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b[c] += 0.5f * (cur[col + c] + cur[G * D + 4 * li + c]);
+    } else {
+      const float invg = 1.f / (float)G;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float m = 0.f;
+        for (int h = 0; h < G; ++h) m += cur[h * D + 4 * li + c];
+        b[c] += 0.5f * (cur[G * D + 4 * li + c] + m * invg);
+      }
+    }
+  }
+  if (s.use_norm) {
+    float ss = b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
+#pragma unroll
+    for (int o = LPU / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv = 1.f / fmaxf(sqrtf(ss), s.eps);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b[c] *= inv;
+  }
+  y[0] = b[0] * cs0.x - b[1] * cs0.y;
+  y[1] = b[0] * cs0.y + b[1] * cs0.x;
+  y[2] = b[2] * cs1.x - b[3] * cs1.y;
+  y[3] = b[2] * cs1.y + b[3] * cs1.x;
+}
+
+// Group taps into LDS: seq taps [(G+1)*D][4] (q channels, then k), channel
+// taps [(G+1)][4]; taps beyond k_s / k_c are zero.
+template <int D>
+__device__ __forceinline__ void load_taps(const MixShape &s, const MixTaps &w, int g, float *staps,
+                                          float *ctaps) {
+  const int G = s.G;
+  for (int c = threadIdx.x; c < (G + 1) * D; c += blockDim.x) {
+    const float *src = c < G * D ? w.q_seq + (size_t)(g * G * D + c) * s.ks
+                                 : w.k_seq + (size_t)(g * D + c - G * D) * s.ks;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) staps[c * 4 + j] = j < s.ks ? src[j] : 0.f;
+  }
+  for (int c = threadIdx.x; c < G + 1; c += blockDim.x) {
+    const float *src = c < G ? w.q_chan + (size_t)(g * G + c) * s.kc : w.k_chan + (size_t)g * s.kc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ctaps[c * 4 + j] = j < s.kc ? src[j] : 0.f;
+  }
+}
+
+// Map a column of the group tile to its column in the qkv row.
+__device__ __forceinline__ int group_col(int col, int g, int G, int D, int eq, int ekv) {
+  if (col < G * D) return g * G * D + col;
+  if (col < (G + 1) * D) return eq + g * D + (col - G * D);
+  return eq + ekv + g * D + (col - (G + 1) * D);
+}
+
+template <typename TQ, typename TV, int D>
+__global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTaps w,
+                                                              const float *__restrict__ qkv,
+                                                              TQ *__restrict__ q, TQ *__restrict__ k,
+                                                              TV *__restrict__ vt, StateOut st,
+                                                              int TC, int nchunks) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int G = s.G, CW = (G + 2) * D;
+  float *tile = lds;
+  float *staps = tile + (TC + HALO) * CW;
+  float *ctaps = staps + (G + 1) * D * 4;
+  float2 *rot = reinterpret_cast<float2 *>(ctaps + ((G + 1) * 4 + 3) / 4 * 4);
+
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x % nchunks;
+  const int bg = blockIdx.x / nchunks;
+  const int g = bg % s.Hkv, b = bg / s.Hkv;
+  const int t0 = chunk * TC;
+  const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
+
+  // 1. pre-conv tile, tokens t0-HALO .. t0+TC-1 (zeros outside [0, T))
+  const int cpr = CW / 4;
+  for (int c = tid; c < (TC + HALO) * cpr; c += 256) {
+    const int r = c / cpr, col = (c % cpr) * 4;
+    const int tok = t0 - HALO + r;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (tok >= 0 && tok < s.T)
+      v = *reinterpret_cast<const f32x4 *>(qkv + (size_t)(b * s.T + tok) * N +
+                                           group_col(col, g, G, D, eq, ekv));
+    *reinterpret_cast<f32x4 *>(tile + r * CW + col) = v;
+  }
+  // 2. taps, 3. rotation table of the chunk
+  load_taps<D>(s, w, g, staps, ctaps);
+  for (int e = tid; e < TC * (D / 2); e += 256)
+    rot[e] = rope_cs(t0 + e / (D / 2), e % (D / 2), D, s.rope_base);
+  __syncthreads();
+
+  // 4. query and key heads
+  constexpr int LPU = D / 4;
+  const int upp = 256 / LPU;
+  const int li = tid % LPU, ui = tid / LPU;
+  const int nunits = TC * (G + 1);
+  for (int u0 = 0; u0 < nunits; u0 += upp) {
+    const int u = u0 + ui;
+    const bool active = u < nunits;          // whole lane groups are inactive together
+    const int r = active ? u / (G + 1) : 0;
+    const int slot = active ? u % (G + 1) : 0;
+    const int tok = t0 + r;
+    float y[4];
+    mix_unit<D>(tile, CW, r, slot, G, li, staps, ctaps, s, rot[r * (D / 2) + 2 * li],
+                rot[r * (D / 2) + 2 * li + 1], y);
+    if (!active) continue;
+    if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
+    if (slot < G) {
+      const int h = g * G + slot;
+      Store4<TQ>::st(q + ((size_t)(b * s.Hq + h) * s.Tp + tok) * D + 4 * li, y);
+    } else {
+      Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
+      if (st.k_cache && tok < s.T)
+        Store4<TV>::st(reinterpret_cast<TV *>(st.k_cache) +
+                           ((size_t)(b * s.Hkv + g) * st.capacity + tok) * D + 4 * li, y);
+    }
+  }
+
+  // 5. value head, transposed: vt[b, g, dd, perm(t)] for the chunk's tokens
+  const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
+  const int vcol = (G + 1) * D;
+  for (int e = tid; e < D * (TC / 8); e += 256) {
+    const int dd = e / (TC / 8), grp = e % (TC / 8);
+    float vals[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int tl = vt_perm(8 * grp + jj);
+      vals[jj] = (t0 + tl < s.T) ? tile[(tl + HALO - shifted) * CW + vcol + dd] : 0.f;
+    }
+    TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + dd) * s.Tp + t0 + 8 * grp;
+    Store4<TV>::st(dst, vals);
+    Store4<TV>::st(dst + 4, vals + 4);
+  }
+
+  // 6. optional decode state: V cache rows, conv window, value-shift state
+  if (st.v_cache) {
+    for (int e = tid; e < TC * (D / 4); e += 256) {
+      const int r = e / (D / 4), c4 = e % (D / 4), tok = t0 + r;
+      if (tok >= s.T) continue;
+      const float *src = tile + (r + HALO - shifted) * CW + vcol + 4 * c4;
+      Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) +
+                         ((size_t)(b * s.Hkv + g) * st.capacity + tok) * D + 4 * c4, src);
+    }
+  }
+  if (chunk == 0) {
+    const int ks1 = s.ks - 1;
+    if (st.conv_q)
+      for (int e = tid; e < ks1 * G * D; e += 256) {
+        const int sl = e / (G * D), c = e % (G * D), tok = s.T - ks1 + sl;
+        const float v = tok >= 0 ? qkv[(size_t)(b * s.T + tok) * N + g * G * D + c] : 0.f;
+        reinterpret_cast<TV *>(st.conv_q)[(size_t)(b * ks1 + sl) * eq + g * G * D + c] = from_f32<TV>(v);
+      }
+    if (st.conv_k)
+      for (int e = tid; e < ks1 * D; e += 256) {
+        const int sl = e / D, c = e % D, tok = s.T - ks1 + sl;
+        const float v = tok >= 0 ? qkv[(size_t)(b * s.T + tok) * N + eq + g * D + c] : 0.f;
+        reinterpret_cast<TV *>(st.conv_k)[(size_t)(b * ks1 + sl) * ekv + g * D + c] = from_f32<TV>(v);
+      }
+    if (st.vshift && shifted)
+      for (int c = tid; c < D; c += 256)
+        reinterpret_cast<TV *>(st.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
+            from_f32<TV>(qkv[(size_t)(b * s.T + s.T - 1) * N + eq + ekv + g * D + c]);
+  }
+}
+
+// One new token per sequence at position L.  One workgroup per (b, g); the
+// 4-row tile holds tokens L-3 .. L: rows from the carried window, the new row
+// from the down-projection.  All state reads finish before the barrier, so
+// state_out may alias state_in.
+template <typename TV, int D>
+__global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps w,
+                                                             const float *__restrict__ qkv, int L,
+                                                             StateOut in, StateOut out,
+                                                             float *__restrict__ qout) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int G = s.G, CW = (G + 2) * D;
+  float *tile = lds;                               // 4 rows
+  float *staps = tile + 4 * CW;
+  float *ctaps = staps + (G + 1) * D * 4;
+  float2 *rot = reinterpret_cast<float2 *>(ctaps + ((G + 1) * 4 + 3) / 4 * 4);
+
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x % s.Hkv, b = blockIdx.x / s.Hkv;
+  const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
+  const int ks1 = s.ks - 1;
+  const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
+  const TV *cq = reinterpret_cast<const TV *>(in.conv_q);
+  const TV *ck = reinterpret_cast<const TV *>(in.conv_k);
+  const TV *vs = reinterpret_cast<const TV *>(in.vshift);
+
+  for (int e = tid; e < 4 * CW; e += 256) {
+    const int r = e / CW, col = e % CW;
+    float v = 0.f;
+    if (r == 3) {
+      v = qkv[(size_t)b * N + group_col(col, g, G, D, eq, ekv)];
+    } else if (r >= 4 - s.ks) {
+      const int sl = r - (4 - s.ks);             // window slot of token L-3+r
+      if (col < G * D) v = to_f32(cq[(size_t)(b * ks1 + sl) * eq + g * G * D + col]);
+      else if (col < (G + 1) * D) v = to_f32(ck[(size_t)(b * ks1 + sl) * ekv + g * D + col - G * D]);
+      else if (r == 2 && shifted) v = to_f32(vs[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + col - (G + 1) * D]);
+    } else if (r == 2 && shifted && col >= (G + 1) * D) {
+      v = to_f32(vs[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + col - (G + 1) * D]);
+    }
+    tile[e] = v;
+  }
+  load_taps<D>(s, w, g, staps, ctaps);
+  for (int e = tid; e < D / 2; e += 256) rot[e] = rope_cs(L, e, D, s.rope_base);
+  __syncthreads();
+
+  constexpr int LPU = D / 4;
+  const int upp = 256 / LPU;
+  const int li = tid % LPU, ui = tid / LPU;
+  TV *kc = reinterpret_cast<TV *>(in.k_cache);
+  TV *vc = reinterpret_cast<TV *>(in.v_cache);
+  for (int u0 = 0; u0 < G + 1; u0 += upp) {
+    const int slot = u0 + ui;
+    const bool active = slot < G + 1;
+    float y[4];
+    mix_unit<D>(tile, CW, 0, active ? slot : 0, G, li, staps, ctaps, s, rot[2 * li], rot[2 * li + 1], y);
+    if (!active) continue;
+    if (slot < G) {
+      Store4<float>::st(qout + (size_t)(b * s.Hq + g * G + slot) * D + 4 * li, y);
+    } else {
+      Store4<TV>::st(kc + ((size_t)(b * s.Hkv + g) * in.capacity + L) * D + 4 * li, y);
+    }
+  }
+  // value row of the new token into the cache
+  for (int c4 = tid; c4 < D / 4; c4 += 256)
+    Store4<TV>::st(vc + ((size_t)(b * s.Hkv + g) * in.capacity + L) * D + 4 * c4,
+                   tile + (3 - shifted) * CW + (G + 1) * D + 4 * c4);
+  // rolled state: slot sl holds token L - ks1 + 1 + sl = tile row 5 - ks + sl
+  TV *oq = reinterpret_cast<TV *>(out.conv_q);
+  TV *ok = reinterpret_cast<TV *>(out.conv_k);
+  for (int e = tid; e < ks1 * G * D; e += 256) {
+    const int sl = e / (G * D), c = e % (G * D);
+    oq[(size_t)(b * ks1 + sl) * eq + g * G * D + c] = from_f32<TV>(tile[(5 - s.ks + sl) * CW + c]);
+  }
+  for (int e = tid; e < ks1 * D; e += 256) {
+    const int sl = e / D, c = e % D;
+    ok[(size_t)(b * ks1 + sl) * ekv + g * D + c] = from_f32<TV>(tile[(5 - s.ks + sl) * CW + G * D + c]);
+  }
+  if (shifted && out.vshift)
+    for (int c = tid; c < D; c += 256)
+      reinterpret_cast<TV *>(out.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
+          from_f32<TV>(tile[3 * CW + (G + 1) * D + c]);
+}
+
+static size_t mix_lds_bytes(int rows, int G, int D, int TC) {
+  const int CW = (G + 2) * D;
+  size_t f = (size_t)rows * CW + (size_t)(G + 1) * D * 4 + ((G + 1) * 4 + 3) / 4 * 4;
+  return f * 4 + (size_t)TC * (D / 2) * 8;
+}
+
+// Tokens per prefill workgroup: 32, or 16 when the group's tile would not fit.
+static int mix_chunk(int G, int D) { return mix_lds_bytes(32 + HALO, G, D, 32) <= 65536 ? 32 : 16; }
+
+bool convmix_fits(int G, int d) { return mix_lds_bytes(16 + HALO, G, d, 16) <= 65536; }
+
+template <typename TQ, typename TV, int D>
+static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
+                                    TQ *k, TV *vt, const StateOut &st, hipStream_t stream) {
+  const int TC = mix_chunk(s.G, D);
+  const int nchunks = s.Tp / TC;
+  const size_t lds = mix_lds_bytes(TC + HALO, s.G, D, TC);
+  hipLaunchKernelGGL((convmix_prefill_kernel<TQ, TV, D>), dim3(s.B * s.Hkv * nchunks), dim3(256),
+                     lds, stream, s, w, qkv, q, k, vt, st, TC, nchunks);
+  return hipGetLastError();
+}
+
+template <typename TQ, typename TV>
+hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
+                                  TQ *k, TV *vt, const StateOut &st, hipStream_t stream) {
+  switch (s.d) {
+    case 16: return convmix_prefill_d<TQ, TV, 16>(s, w, qkv, q, k, vt, st, stream);
+    case 32: return convmix_prefill_d<TQ, TV, 32>(s, w, qkv, q, k, vt, st, stream);
+    case 64: return convmix_prefill_d<TQ, TV, 64>(s, w, qkv, q, k, vt, st, stream);
+    case 128: return convmix_prefill_d<TQ, TV, 128>(s, w, qkv, q, k, vt, st, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename TV, int D>
+static hipError_t convmix_decode_d(const MixShape &s, const MixTaps &w, const float *qkv, int L,
+                                   const StateOut &in, const StateOut &out, float *q,
+                                   hipStream_t stream) {
+  const size_t lds = mix_lds_bytes(4, s.G, D, 1);
+  hipLaunchKernelGGL((convmix_decode_kernel<TV, D>), dim3(s.B * s.Hkv), dim3(256), lds, stream, s,
+                     w, qkv, L, in, out, q);
+  return hipGetLastError();
+}
+
+template <typename TV>
+hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const float *qkv, int L,
+                                 const StateOut &in, const StateOut &out, float *q,
+                                 hipStream_t stream) {
+  switch (s.d) {
+    case 16: return convmix_decode_d<TV, 16>(s, w, qkv, L, in, out, q, stream);
+    case 32: return convmix_decode_d<TV, 32>(s, w, qkv, L, in, out, q, stream);
+    case 64: return convmix_decode_d<TV, 64>(s, w, qkv, L, in, out, q, stream);
+    case 128: return convmix_decode_d<TV, 128>(s, w, qkv, L, in, out, q, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template hipError_t launch_convmix_prefill<f16, bf16>(const MixShape &, const MixTaps &,
+                                                      const float *, f16 *, f16 *, bf16 *,
+                                                      const StateOut &, hipStream_t);
+template hipError_t launch_convmix_prefill<bf16, bf16>(const MixShape &, const MixTaps &,
+                                                       const float *, bf16 *, bf16 *, bf16 *,
+                                                       const StateOut &, hipStream_t);
+template hipError_t launch_convmix_prefill<float, float>(const MixShape &, const MixTaps &,
+                                                         const float *, float *, float *, float *,
+                                                         const StateOut &, hipStream_t);
+template hipError_t launch_convmix_decode<bf16>(const MixShape &, const MixTaps &, const float *,
+                                                int, const StateOut &, const StateOut &, float *,
+                                                hipStream_t);
+template hipError_t launch_convmix_decode<float>(const MixShape &, const MixTaps &, const float *,
+                                                 int, const StateOut &, const StateOut &, float *,
+                                                 hipStream_t);
+
+}  // namespace cca

@@ -1,0 +1,155 @@
+// Projection GEMMs of the CCA forward pass (gfx950).
+//
+//   down-projection  qkv~[M, N] = x[M, E] * W_qkv[N, E]^T      (N = e_q + 2 e_kv)
+//   up-projection    y[M, E]    = O[M, e_q] * W_o[E, e_q]^T
+// [GS-EN "2. Methodology" / Down-Projection; the output returns to width E
+//  after attention, which happens entirely in the latent space.]
+//
+// Both are "NT" products C = A * B^T with A and B contiguous along the
+// contraction index, the native operand layout of MFMA.  One kernel serves
+// bf16 (v_mfma_f32_32x32x16_bf16) and fp32 (v_mfma_f32_32x32x2_f32) inputs with
+// fp32 accumulation.  Block tile BM x BN x BK with 4 waves (2 x 2), each wave
+// owning (BM/2) x (BN/2) as 32 x 32 MFMA tiles; A and B tiles are staged in
+// LDS with a 16-byte XOR swizzle, double buffered, one barrier per K step.
+// Rows of 128 bytes per tile row: BK = 64 (bf16) or 32 (fp32).
+#include "cca_device.h"
+#include "cca_launch.h"
+
+namespace cca {
+
+template <typename Tin, typename Tout, int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
+                                                      const Tin *__restrict__ Bm,
+                                                      Tout *__restrict__ C, int M, int N,
+                                                      int K, int lda, int ldb, int ldc) {
+  typedef Mfma32<Tin> MF;
+  constexpr int KS = MF::KS;
+  constexpr int ROWB = 128;                       // bytes per LDS tile row
+  constexpr int BK = ROWB / (int)sizeof(Tin);     // 64 (bf16) / 32 (fp32)
+  constexpr int EPC = 16 / (int)sizeof(Tin);      // elements per 16-byte chunk
+  constexpr int CPR = ROWB / 16;                  // chunks per row (8)
+  constexpr int WM = BM / 2, WN = BN / 2;         // wave tile
+  constexpr int TM = WM / 32, TN = WN / 32;       // MFMA tiles per wave
+  constexpr int A_CH = BM * CPR / 256;            // 16-byte chunks per thread
+  constexpr int B_CH = BN * CPR / 256;
+  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (BM + BN) * ROWB];
+  // buffer `buf`: A tile at smem + buf*(BM+BN)*ROWB, B tile right after it
+  auto sA = [&](int buf) { return smem + buf * (BM + BN) * ROWB; };
+  auto sB = [&](int buf) { return smem + buf * (BM + BN) * ROWB + BM * ROWB; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  const int ntn = (N + BN - 1) / BN;
+  const int ntm = (M + BM - 1) / BM;
+  const int lid = xcd_remap(blockIdx.x, ntn * ntm);
+  const int m0 = (lid / ntn) * BM;
+  const int n0 = (lid % ntn) * BN;
+
+  u32x4 ra[A_CH], rb[B_CH];
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < A_CH; ++r) {
+      int c = tid + 256 * r;
+      int row = c / CPR, ch = c % CPR;
+      int gm = m0 + row, gk = k0 + ch * EPC;
+      ra[r] = (gm < M && gk < K) ? ld16(A + (size_t)gm * lda + gk) : zero_u32x4();
+    }
+#pragma unroll
+    for (int r = 0; r < B_CH; ++r) {
+      int c = tid + 256 * r;
+      int row = c / CPR, ch = c % CPR;
+      int gn = n0 + row, gk = k0 + ch * EPC;
+      rb[r] = (gn < N && gk < K) ? ld16(Bm + (size_t)gn * ldb + gk) : zero_u32x4();
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < A_CH; ++r) {
+      int c = tid + 256 * r;
+      int row = c / CPR, ch = c % CPR;
+      st16(sA(buf) + row * ROWB + swz(row, ch * 16, CPR), ra[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < B_CH; ++r) {
+      int c = tid + 256 * r;
+      int row = c / CPR, ch = c % CPR;
+      st16(sB(buf) + row * ROWB + swz(row, ch * 16, CPR), rb[r]);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / (2 * KS); ++kk) {
+      const int kb = (kk * 2 * KS + hl * KS) * (int)sizeof(Tin);   // byte offset in row
+      typename MF::frag fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        int row = wm * WM + i * 32 + l32;
+        fa[i] = load_frag<Tin>(reinterpret_cast<const Tin *>(sA(cur) + row * ROWB + swz(row, kb, CPR)));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        int row = wn * WN + j * 32 + l32;
+        fb[j] = load_frag<Tin>(reinterpret_cast<const Tin *>(sB(cur) + row * ROWB + swz(row, kb, CPR)));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds C[8j + 4*hl + i][l32] of each 32x32 tile
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int gn = n0 + wn * WN + j * 32 + l32;
+      if (gn >= N) continue;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int gm = m0 + wm * WM + i * 32 + 8 * (a >> 2) + 4 * hl + (a & 3);
+        if (gm < M) C[(size_t)gm * ldc + gn] = from_f32<Tout>(acc[i][j][a]);
+      }
+    }
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int K, int lda,
+                          int ldb, int ldc, hipStream_t stream) {
+  constexpr int BM = 128, BN = 128;
+  int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_nt_kernel<Tin, Tout, BM, BN>), dim3(grid), dim3(256), 0, stream, A, B,
+                     C, M, N, K, lda, ldb, ldc);
+  return hipGetLastError();
+}
+
+template hipError_t launch_gemm_nt<bf16, float>(const bf16 *, const bf16 *, float *, int, int, int,
+                                                int, int, int, hipStream_t);
+template hipError_t launch_gemm_nt<bf16, bf16>(const bf16 *, const bf16 *, bf16 *, int, int, int,
+                                               int, int, int, hipStream_t);
+template hipError_t launch_gemm_nt<float, float>(const float *, const float *, float *, int, int,
+                                                 int, int, int, int, hipStream_t);
+
+}  // namespace cca

@@ -1,0 +1,232 @@
+/*
+ * libcca -- Compressed Convolutional Attention (CCA) and its grouped-query
+ * variant (CCGQA), forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The method (page tags as in the oracle's header):
+ *   down-projection of hidden states to a latent q, k, v
+ *       [GS-EN "2. Methodology" / Down-Projection; ABS]
+ *   causal sequence convolution and channel convolution of q and k
+ *       [GS-EN "2. Methodology" / Convolutional Mixing]
+ *   q-k-mean, value-shift
+ *       [GS-EN "2. Methodology" / Q-K-Mean, Value-Shift; EDG "How Compressed
+ *        Convolutional Attention Works"]
+ *   L2 normalisation with a per-head temperature, RoPE on the latent q, k
+ *       [GS-EN "2. Methodology" / RoPE Integration]
+ *   causal softmax attention inside the latent heads, kv heads shared by
+ *   groups of G = H_q / H_kv query heads
+ *       [GS-EN "2. Methodology" / Latent Space Operations, "Extension: CCGQA"]
+ *   up-projection back to the residual width.
+ * The two workloads are prefill over whole sequences and one autoregressive
+ * decode step against a latent KV cache [GS-EN "1. Problem Statement"].
+ *
+ * Page tags: [ABS] mlsanity.com paper index, "Abstract (arXiv)"; [GS-EN]
+ * gist.science English explainer of "Compressed Convolutional Attention:
+ * Efficient Attention in a Compressed Latent Space"; [EDG]
+ * blogs.edgentiq.com, "Boosting Transformer Efficiency with Compressed
+ * Convolutional Attention".
+ *
+ * Readings where the pages leave a step open (they are the library's
+ * definition of the operation):
+ *   - convolution taps are indexed by lag: a[t,c] = sum_j w[c,j] u[t-j,c];
+ *   - the channel convolution is one k_c-tap filter per head sliding along
+ *     the head's channel index, zero padded inside the head;
+ *   - q-k-mean adds the mean of the pre-convolution q and k to the convolved
+ *     q and k (per group for CCGQA: q head h meets k~ of kv head h/G, kv head
+ *     g meets the average q~ of its G query heads);
+ *   - value-shift: kv heads H_kv/2 .. H_kv-1 take the previous token's value
+ *     (zero before the first token);
+ *   - q and k are divided by max(||.||_2, norm_eps) per head; the logit of
+ *     query head h is tau[h] * <q_h, k_g>;
+ *   - RoPE rotates channel pairs (2i, 2i+1) by pos * base^(-2i/d), pos = token
+ *     index from 0, angles evaluated in double precision.
+ *
+ * Conventions for every call
+ *   - All tensor arguments are device pointers to caller-owned, contiguous,
+ *     16-byte aligned memory.  The library never allocates device memory,
+ *     never synchronises the stream and keeps no mutable global state; calls
+ *     on different streams with distinct workspaces may run concurrently.
+ *   - Every launch is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Argument errors are detected on the host before any
+ *     launch and returned as a status; a failed launch returns CCA_ERR_HIP.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - No C++ exception crosses this interface.
+ *   - Matrices are row-major [out, in].  Activations and weights use the
+ *     storage type cfg.dtype (bf16 or fp32); taps and tau are always fp32.
+ *     Accumulation is always fp32.
+ */
+#ifndef CCA_H
+#define CCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CCA_OK = 0,
+  CCA_ERR_INVALID_ARG = 1,   /* null pointer, inconsistent sizes, misaligned pointer */
+  CCA_ERR_UNSUPPORTED = 2,   /* a legal configuration this build does not implement */
+  CCA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the *_workspace_size */
+  CCA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} cca_status;
+
+typedef enum { CCA_BF16 = 0, CCA_F32 = 1 } cca_dtype;
+
+/* Shape and switches of one attention layer.  C (compression) and G are
+ * derived: e_q = n_q_heads*head_dim, e_kv = n_kv_heads*head_dim,
+ * G = n_q_heads / n_kv_heads. */
+typedef struct {
+  int32_t batch;          /* B  >= 1 */
+  int32_t seq_len;        /* T  >= 1 (prefill); ignored by cca_decode_step */
+  int32_t d_model;        /* E  >= 8, multiple of 8 */
+  int32_t n_q_heads;      /* H_q, multiple of n_kv_heads */
+  int32_t n_kv_heads;     /* H_kv >= 1; even when use_value_shift */
+  int32_t head_dim;       /* d in {16, 32, 64, 128} */
+  int32_t seq_conv_k;     /* k_s in 1..4 */
+  int32_t chan_conv_k;    /* k_c in 1..4 */
+  int32_t use_qk_mean;    /* 0 / 1 */
+  int32_t use_value_shift;/* 0 / 1 */
+  int32_t use_qk_norm;    /* 0 / 1 */
+  float rope_base;        /* > 0, or 0 to switch RoPE off */
+  float norm_eps;         /* > 0 (1e-6 by default) */
+  int32_t dtype;          /* cca_dtype: storage of x, y, weights, cache, state */
+} cca_config;
+
+/* Weights.  w_qkv: [e_q + 2*e_kv, E] in cfg.dtype, rows q | k | v.
+ * w_o: [E, e_q] in cfg.dtype (latent output flattened head-major, h*d+i).
+ * q_seq_taps [e_q, k_s], k_seq_taps [e_kv, k_s]: fp32, lag-indexed.
+ * q_chan_taps [H_q, k_c], k_chan_taps [H_kv, k_c]: fp32, lag-indexed.
+ * tau [H_q]: fp32 logit temperature per query head. */
+typedef struct {
+  const void *w_qkv;
+  const void *w_o;
+  const float *q_seq_taps;
+  const float *k_seq_taps;
+  const float *q_chan_taps;
+  const float *k_chan_taps;
+  const float *tau;
+} cca_weights;
+
+/* Decode state, caller-owned, all in cfg.dtype.
+ * k_cache, v_cache: [B, H_kv, capacity, d].  K holds the normalised, rotated
+ *   k (tau not folded in); V the value after value-shift.
+ * conv_q [B, k_s-1, e_q], conv_k [B, k_s-1, e_kv]: pre-convolution q~, k~ of
+ *   the last k_s-1 tokens, slot 0 the oldest; zeros stand for tokens before
+ *   the sequence start.
+ * vshift [B, H_kv/2, d]: pre-shift value of the last token on the shifted
+ *   (upper) kv heads; unused (may be NULL) when use_value_shift is 0. */
+typedef struct {
+  void *k_cache;
+  void *v_cache;
+  int32_t capacity;
+  int32_t reserved;
+  void *conv_q;
+  void *conv_k;
+  void *vshift;
+} cca_state;
+
+/* Host-only check of a configuration; needs no device.  Returns CCA_OK,
+ * CCA_ERR_INVALID_ARG (null cfg, non-positive sizes, H_q % H_kv != 0, odd
+ * H_kv with value-shift, E not a multiple of 8, bad eps/base) or
+ * CCA_ERR_UNSUPPORTED (d outside {16,32,64,128}, taps outside 1..4, dtype). */
+cca_status cca_validate_config(const cca_config *cfg);
+
+/* Bytes of device workspace cca_prefill_forward needs for cfg (0 if cfg is
+ * invalid).  Host-only. */
+size_t cca_prefill_workspace_size(const cca_config *cfg);
+
+/* Bytes of device workspace cca_decode_step needs for cfg and a cache of
+ * cache_len past tokens (0 if invalid).  Host-only. */
+size_t cca_decode_workspace_size(const cca_config *cfg, int32_t cache_len);
+
+/* Prefill: the whole forward pass over x [B, T, E] -> y [B, T, E]
+ * (x, y in cfg.dtype; they must not overlap).
+ * state_out (nullable): when given, also writes the decode state after the
+ * T tokens: k_cache / v_cache slots [0, T) (capacity >= T), conv_q, conv_k
+ * and (with value-shift) vshift.  Members left NULL are skipped.
+ * workspace: >= cca_prefill_workspace_size(cfg) bytes, 256-byte aligned; its
+ * contents are scratch and are overwritten. */
+cca_status cca_prefill_forward(const cca_config *cfg, const cca_weights *w,
+                               const void *x, void *y, const cca_state *state_out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Decode step: one new token per sequence at position cache_len (uniform over
+ * the batch).  x_t [B, E] -> y_t [B, E].
+ * state_in: cache slots [0, cache_len) and the carried conv window / vshift.
+ *   The new k and v rows are written into state_in's cache at slot cache_len
+ *   (capacity must exceed cache_len).
+ * state_out: receives the rolled conv window and vshift; it may alias
+ *   state_in.  Its k_cache / v_cache must be NULL or equal to state_in's.
+ * workspace: >= cca_decode_workspace_size(cfg, cache_len) bytes. */
+cca_status cca_decode_step(const cca_config *cfg, const cca_weights *w,
+                           const void *x_t, int32_t cache_len,
+                           const cca_state *state_in, const cca_state *state_out,
+                           void *y_t, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Static description of a status code. */
+const char *cca_status_string(cca_status s);
+
+/* ------------------------------------------------------------------------
+ * Stage calls.  Each launches exactly the kernel(s) of one step of the
+ * forward pass on the buffers of a prefill or decode workspace, so the steps
+ * can be checked against the oracle's intermediates and timed one by one.
+ * cca_prefill_forward == downproj, convmix, attention, upproj in this order
+ * on the same workspace; cca_decode_step == decode_downproj, decode_mix,
+ * decode_attention, decode_upproj.
+ *
+ * Prefill workspace layout (offsets from cca_prefill_workspace_layout; Tp is
+ * T rounded up to 128):
+ *   CCA_WS_QKV  fp32 [B*T, e_q + 2*e_kv]   down-projection output
+ *   CCA_WS_Q    [B, H_q, Tp, d]   normalised, rotated q; fp16 when
+ *               cfg.dtype is bf16 and use_qk_norm is 1, else cfg.dtype
+ *   CCA_WS_K    [B, H_kv, Tp, d]  same type as CCA_WS_Q
+ *   CCA_WS_VT   [B, H_kv, d, Tp]  value after shift, transposed, cfg.dtype;
+ *               inside each group of 16 tokens, positions 4..7 and 8..11 are
+ *               swapped (bits 2 and 3 of the token index exchanged)
+ *   CCA_WS_O    [B*T, e_q] latent attention output, cfg.dtype
+ * Decode workspace layout:
+ *   CCA_WS_QKV  fp32 [B, e_q + 2*e_kv]
+ *   CCA_WS_Q    fp32 [B, H_q, d]  normalised, rotated q of the new token
+ *   CCA_WS_PART fp32 partial softmax states of the split-KV attention
+ *   CCA_WS_O    [B, e_q] cfg.dtype
+ * ---------------------------------------------------------------------- */
+enum { CCA_WS_QKV = 0, CCA_WS_Q = 1, CCA_WS_K = 2, CCA_WS_VT = 3, CCA_WS_O = 4,
+       CCA_WS_PART = 5, CCA_WS_COUNT = 6 };
+
+/* Byte offsets of the buffers above inside a prefill (decode: cache_len >= 0)
+ * workspace; unused slots are set to SIZE_MAX.  Host-only. */
+cca_status cca_prefill_workspace_layout(const cca_config *cfg, size_t offsets[CCA_WS_COUNT]);
+cca_status cca_decode_workspace_layout(const cca_config *cfg, int32_t cache_len,
+                                       size_t offsets[CCA_WS_COUNT]);
+
+cca_status cca_stage_downproj(const cca_config *cfg, const cca_weights *w, const void *x,
+                              void *workspace, size_t workspace_bytes, void *stream);
+cca_status cca_stage_convmix(const cca_config *cfg, const cca_weights *w,
+                             const cca_state *state_out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+cca_status cca_stage_attention(const cca_config *cfg, const cca_weights *w,
+                               void *workspace, size_t workspace_bytes, void *stream);
+cca_status cca_stage_upproj(const cca_config *cfg, const cca_weights *w, void *y,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+cca_status cca_stage_decode_downproj(const cca_config *cfg, const cca_weights *w,
+                                     const void *x_t, int32_t cache_len, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+cca_status cca_stage_decode_mix(const cca_config *cfg, const cca_weights *w, int32_t cache_len,
+                                const cca_state *state_in, const cca_state *state_out,
+                                void *workspace, size_t workspace_bytes, void *stream);
+cca_status cca_stage_decode_attention(const cca_config *cfg, const cca_weights *w,
+                                      int32_t cache_len, const cca_state *state_in,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+cca_status cca_stage_decode_upproj(const cca_config *cfg, const cca_weights *w,
+                                   int32_t cache_len, void *y_t, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCA_H */

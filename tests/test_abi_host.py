@@ -1,0 +1,122 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/cca.h declares, and rejects bad arguments before any launch (no GPU
+is touched by these tests)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from synth import CCAShape, WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from efficient_transformer_attention_amd import cca
+    return cca
+
+
+def declared_entry_points():
+    src = open(os.path.join(ROOT, "include", "cca.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cca_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_entry_points()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L.lib, n), f"libcca.so does not export {n}"
+    assert sorted(L.EXPORTS) == names
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.status_string(s).startswith("CCA_")
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workloads_validate(L, name):
+    cfg = L.make_config(WORKLOADS[name])
+    assert L.validate_config(cfg) == L.CCA_OK
+    if WORKLOADS[name].cache_len:
+        n = L.decode_workspace_size(cfg, WORKLOADS[name].cache_len)
+        off = L.decode_workspace_layout(cfg, WORKLOADS[name].cache_len)
+    else:
+        n = L.prefill_workspace_size(cfg)
+        off = L.prefill_workspace_layout(cfg)
+    used = [o for o in off if o != 2 ** 64 - 1]
+    assert n > 0 and all(o % 256 == 0 for o in used) and len(set(used)) == len(used) and max(used) < n
+
+
+BAD = [
+    (dict(n_q_heads=6, n_kv_heads=4), "CCA_ERR_INVALID_ARG"),
+    (dict(n_kv_heads=3, n_q_heads=3), "CCA_ERR_INVALID_ARG"),      # odd H_kv with value-shift
+    (dict(d_model=100), "CCA_ERR_INVALID_ARG"),
+    (dict(seq_len=0), "CCA_ERR_INVALID_ARG"),
+    (dict(batch=0), "CCA_ERR_INVALID_ARG"),
+    (dict(norm_eps=0.0), "CCA_ERR_INVALID_ARG"),
+    (dict(rope_base=-1.0), "CCA_ERR_INVALID_ARG"),
+    (dict(use_qk_mean=2), "CCA_ERR_INVALID_ARG"),
+    (dict(head_dim=48), "CCA_ERR_UNSUPPORTED"),
+    (dict(seq_conv_k=5), "CCA_ERR_UNSUPPORTED"),
+    (dict(chan_conv_k=0), "CCA_ERR_UNSUPPORTED"),
+    (dict(n_q_heads=64, n_kv_heads=4, head_dim=128), "CCA_ERR_UNSUPPORTED"),  # group tile too wide
+]
+
+
+@pytest.mark.parametrize("kw,err", BAD)
+def test_invalid_configs(L, kw, err):
+    base = CCAShape(batch=1, seq_len=16, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    cfg = L.make_config(base.with_(**kw))
+    st = L.validate_config(cfg)
+    assert L.status_string(st).startswith(err)
+    assert L.prefill_workspace_size(cfg) == 0
+
+
+def _fake_weights(L):
+    a = 0x10000
+    return L._Weights(a, a, a, a, a, a, a)
+
+
+def test_prefill_rejects_before_launch(L):
+    cfg = L.make_config(CCAShape(batch=1, seq_len=16, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                 head_dim=64))
+    need = L.prefill_workspace_size(cfg)
+    w = _fake_weights(L)
+    f = L.lib.cca_prefill_forward
+    # null config / weights / x
+    assert f(None, C.byref(w), 0x10000, 0x20000, None, 0x100000, need, None) == L.CCA_ERR_INVALID_ARG
+    assert f(C.byref(cfg), None, 0x10000, 0x20000, None, 0x100000, need, None) == L.CCA_ERR_INVALID_ARG
+    assert f(C.byref(cfg), C.byref(w), None, 0x20000, None, 0x100000, need, None) == L.CCA_ERR_INVALID_ARG
+    # misaligned x
+    assert f(C.byref(cfg), C.byref(w), 0x10002, 0x20000, None, 0x100000, need, None) == L.CCA_ERR_INVALID_ARG
+    # workspace too small / missing / misaligned
+    assert f(C.byref(cfg), C.byref(w), 0x10000, 0x20000, None, 0x100000, need - 1, None) == L.CCA_ERR_WORKSPACE
+    assert f(C.byref(cfg), C.byref(w), 0x10000, 0x20000, None, None, need, None) == L.CCA_ERR_WORKSPACE
+    assert f(C.byref(cfg), C.byref(w), 0x10000, 0x20000, None, 0x100080, need, None) == L.CCA_ERR_WORKSPACE
+    # state capacity below T
+    st = L._State(0x30000, 0x40000, 8, 0, None, None, None)
+    assert f(C.byref(cfg), C.byref(w), 0x10000, 0x20000, C.byref(st), 0x100000, need, None) == L.CCA_ERR_INVALID_ARG
+
+
+def test_decode_rejects_before_launch(L):
+    s = CCAShape(batch=2, seq_len=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    cfg = L.make_config(s)
+    need = L.decode_workspace_size(cfg, 10)
+    w = _fake_weights(L)
+    f = L.lib.cca_decode_step
+    good = L._State(0x30000, 0x40000, 11, 0, 0x50000, 0x60000, 0x70000)
+    full = L._State(0x30000, 0x40000, 10, 0, 0x50000, 0x60000, 0x70000)     # no room for slot 10
+    other = L._State(0x90000, 0x40000, 11, 0, 0x50000, 0x60000, 0x70000)    # different k cache
+    novs = L._State(0x30000, 0x40000, 11, 0, 0x50000, 0x60000, None)        # value-shift needs it
+    args = lambda si, so, L_=10, wsb=need: (C.byref(cfg), C.byref(w), 0x10000, L_, C.byref(si),
+                                            C.byref(so), 0x20000, 0x100000, wsb, None)
+    assert f(*args(full, full)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(good, other)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(novs, novs)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(good, good, -1)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(good, good, 10, need - 1)) == L.CCA_ERR_WORKSPACE

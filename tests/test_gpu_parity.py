@@ -1,0 +1,278 @@
+"""GPU parity of libcca against the fp64 oracle, through the C ABI.
+
+Small shapes are compared element by element (several tiles and a ragged
+tail); the full-size workloads are compared on sampled query rows that the
+oracle computes one by one.  Tolerances: bf16 I/O max-abs <= 2e-2 and
+relative L2 <= 5e-3; fp32 validation mode relative L2 <= 1e-5.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.cca as O
+from synth import CCAShape, make_decode, make_prefill, workload
+from gpu_helpers import (PrefillRun, assert_parity, lib, rel_l2, sample_rows, set_taps,
+                         tau_inv_sqrt_d, tens, upload_weights, vt_unpermute)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = {
+    # name: (shape, tau override)
+    "tiny_f32_workload": (workload("cca_prefill_tiny_f32"), None),
+    "bf16_g2_ragged": (CCAShape(batch=2, seq_len=300, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                head_dim=64, rope_base=10000.0), None),
+    "bf16_g4_base5e5": (CCAShape(batch=1, seq_len=200, d_model=512, n_q_heads=8, n_kv_heads=2,
+                                 head_dim=64, rope_base=500000.0), None),
+    "bf16_d16": (CCAShape(batch=2, seq_len=130, d_model=128, n_q_heads=2, n_kv_heads=2,
+                          head_dim=16), None),
+    "bf16_d32_t77": (CCAShape(batch=1, seq_len=77, d_model=256, n_q_heads=4, n_kv_heads=4,
+                              head_dim=32), None),
+    "bf16_d128": (CCAShape(batch=1, seq_len=150, d_model=256, n_q_heads=2, n_kv_heads=2,
+                           head_dim=128), None),
+    "f32_d32_g2_ragged": (CCAShape(batch=2, seq_len=190, d_model=128, n_q_heads=4, n_kv_heads=2,
+                                   head_dim=32, dtype="f32"), None),
+    "f32_d64_g4": (CCAShape(batch=1, seq_len=260, d_model=256, n_q_heads=8, n_kv_heads=2,
+                            head_dim=64, rope_base=500000.0, dtype="f32"), None),
+    "bf16_taps_2_3": (CCAShape(batch=1, seq_len=140, d_model=256, n_q_heads=4, n_kv_heads=2,
+                               head_dim=64, seq_conv_k=2, chan_conv_k=3), None),
+    "bf16_single_token": (CCAShape(batch=3, seq_len=1, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                   head_dim=64), None),
+    "bf16_g8": (CCAShape(batch=1, seq_len=100, d_model=256, n_q_heads=8, n_kv_heads=1,
+                         head_dim=64, use_value_shift=0), None),
+    "bf16_switches_off": (CCAShape(batch=1, seq_len=160, d_model=256, n_q_heads=4, n_kv_heads=4,
+                                   head_dim=64, use_qk_mean=0, use_value_shift=0, use_qk_norm=0,
+                                   rope_base=10000.0), "inv_sqrt_d"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_prefill_small_parity(name):
+    shape, tau = SMALL[name]
+    _say(f"[prefill] {name} {shape}")
+    P = make_prefill(shape, seed=0)
+    if tau == "inv_sqrt_d":
+        set_taps(P, tau=tau_inv_sqrt_d(shape))
+    run = PrefillRun(shape, P)
+    y = run.run()
+    ref = O.prefill(P.x, P.weights.f64(), shape)
+    assert_parity(y, ref, shape.dtype, name)
+
+
+def test_prefill_mha_reduction_gpu():
+    """Compression 1, delta taps, mean / shift / norm off, tau = 1/sqrt(d):
+    the GPU path computes textbook causal RoPE MHA (oracle pinned to it)."""
+    shape = CCAShape(batch=1, seq_len=192, d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                     use_qk_mean=0, use_value_shift=0, use_qk_norm=0, rope_base=10000.0)
+    _say(f"[prefill] mha reduction {shape}")
+    P = make_prefill(shape, seed=3)
+    qs = np.zeros((shape.e_q, 4), np.float32); qs[:, 0] = 1
+    ks = np.zeros((shape.e_kv, 4), np.float32); ks[:, 0] = 1
+    qc = np.zeros((4, 4), np.float32); qc[:, 0] = 1
+    set_taps(P, seq=(qs, ks), chan=(qc, qc.copy()), tau=tau_inv_sqrt_d(shape))
+    y = PrefillRun(shape, P).run()
+    assert_parity(y, O.prefill(P.x, P.weights.f64(), shape), "bf16", "mha")
+
+
+def test_prefill_stage_intermediates():
+    """Each kernel's output against the oracle's intermediate of the same step."""
+    shape = CCAShape(batch=2, seq_len=150, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    _say(f"[stages] {shape}")
+    P = make_prefill(shape, seed=5)
+    run = PrefillRun(shape, P)
+    y = run.run()
+    ref_y, lat = O.prefill(P.x, P.weights.f64(), shape, intermediates=True)
+    s, T = shape, tens()
+    B, Tn, Tp, d = s.batch, s.seq_len, run.padded_T(), s.head_dim
+    L = lib()
+    qkv = T.to_f64(run.ws_view(L.WS_QKV, torch.float32, (B, Tn, s.n_qkv)))
+    ref_qkv = np.concatenate([lat["q_pre"].reshape(B, Tn, -1), lat["k_pre"].reshape(B, Tn, -1),
+                              lat["vbar"].reshape(B, Tn, -1)], axis=-1)
+    assert rel_l2(qkv, ref_qkv) < 1e-6, "down-projection"
+    q = T.to_f64(run.ws_view(L.WS_Q, run.qk_dtype(), (B, s.n_q_heads, Tp, d)))
+    k = T.to_f64(run.ws_view(L.WS_K, run.qk_dtype(), (B, s.n_kv_heads, Tp, d)))
+    assert rel_l2(q[:, :, :Tn], lat["q"].transpose(0, 2, 1, 3)) < 1e-3, "mixed q"
+    assert rel_l2(k[:, :, :Tn], lat["k"].transpose(0, 2, 1, 3)) < 1e-3, "mixed k"
+    assert np.all(q[:, :, Tn:] == 0) and np.all(k[:, :, Tn:] == 0), "padding rows"
+    vt = vt_unpermute(T.to_f64(run.ws_view(L.WS_VT, torch.bfloat16, (B, s.n_kv_heads, d, Tp))))
+    assert rel_l2(vt[..., :Tn], lat["v"].transpose(0, 2, 3, 1)) < 5e-3, "shifted v"
+    assert np.all(vt[..., Tn:] == 0)
+    o = T.to_f64(run.ws_view(L.WS_O, torch.bfloat16, (B, Tn, s.e_q)))
+    assert rel_l2(o, lat["o"].reshape(B, Tn, -1)) < 5e-3, "attention output"
+    assert_parity(y, ref_y, "bf16", "y")
+
+
+@pytest.mark.parametrize("name,nrows", [("cca_prefill_b4_t2048", 48),
+                                        ("ccgqa_prefill_t8192", 48),
+                                        ("ccgqa_prefill_t16384", 48)])
+def test_prefill_workload_sampled(name, nrows):
+    shape = workload(name)
+    _say(f"[workload] {name}")
+    P = make_prefill(shape, seed=0)
+    run = PrefillRun(shape, P)
+    y = run.run()
+    rows = sample_rows(shape.seq_len, nrows)
+    ref = O.prefill(P.x, P.weights.f64(), shape, rows=rows)
+    assert_parity(y[:, rows], ref, "bf16", name)
+
+
+def test_prefill_causality_bitwise():
+    shape = CCAShape(batch=2, seq_len=300, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    _say("[causality]")
+    P = make_prefill(shape, seed=7)
+    run = PrefillRun(shape, P)
+    y0 = run.run().copy()
+    for t in (0, 63, 64, 127, 200, 298):
+        x2 = P.x_s.copy()
+        rng = np.random.default_rng(t)
+        x2[:, t + 1:] = rng.integers(0, 2 ** 16, size=x2[:, t + 1:].shape, dtype=np.uint16) & 0xBFFF
+        run.x.copy_(tens().to_device(x2))
+        y1 = run.run()
+        np.testing.assert_array_equal(y1[:, :t + 1], y0[:, :t + 1])
+        assert np.any(y1[:, t + 1:] != y0[:, t + 1:])
+
+
+def test_prefill_repeat_bitwise():
+    shape = CCAShape(batch=1, seq_len=513, d_model=256, n_q_heads=8, n_kv_heads=2, head_dim=64)
+    P = make_prefill(shape, seed=8)
+    run = PrefillRun(shape, P)
+    a = run.run().copy()
+    b = run.run()
+    np.testing.assert_array_equal(a, b)
+
+
+def test_prefill_state_then_decode():
+    """prefill(x[:L]) with state -> decode(x[L]) -> decode(x[L+1]) equals the
+    oracle prefill over L+1 / L+2 tokens at the last position."""
+    full = CCAShape(batch=2, seq_len=39, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    _say("[prefill->decode]")
+    P = make_prefill(full, seed=9)
+    Lp = 37
+    pshape = full.with_(seq_len=Lp)
+    Pp = make_prefill(full, seed=9)
+    Pp.x_s = np.ascontiguousarray(P.x_s[:, :Lp])
+    Pp.x = P.x[:, :Lp]
+    run = PrefillRun(pshape, Pp, capacity=64)
+    run.run()
+    # the state the GPU wrote equals the oracle's (after bf16 rounding)
+    _, lat = O.prefill(Pp.x, P.weights.f64(), pshape, intermediates=True)
+    K, V, cq, ck, vs = O.prefill_state(lat, pshape)
+    T = tens()
+    st = run.state
+    assert rel_l2(T.to_f64(st.k_cache)[:, :, :Lp], K) < 5e-3
+    assert rel_l2(T.to_f64(st.v_cache)[:, :, :Lp], V) < 5e-3
+    assert rel_l2(T.to_f64(st.conv_q), cq) < 5e-3
+    assert rel_l2(T.to_f64(st.conv_k), ck) < 5e-3
+    assert rel_l2(T.to_f64(st.vshift), vs) < 5e-3
+    L = lib()
+    dshape = full.with_(seq_len=1)
+    cfg = L.make_config(dshape)
+    ref_full = O.prefill(P.x, P.weights.f64(), full)
+    for step, pos in enumerate((Lp, Lp + 1)):
+        x_t = T.to_device(np.ascontiguousarray(P.x_s[:, pos]))
+        y_t = torch.empty_like(x_t)
+        ws = T.workspace(L.decode_workspace_size(cfg, pos))
+        L.decode_step(cfg, run.w, x_t, pos, st, st, y_t, ws)
+        torch.cuda.synchronize()
+        assert_parity(T.to_f64(y_t), ref_full[:, pos], "bf16", f"decode step {step}")
+
+
+def _upload_decode(D, dev="cuda"):
+    T, L = tens(), lib()
+    s = D.shape
+    st = L.State(k_cache=T.to_device(D.k_cache_s, dev), v_cache=T.to_device(D.v_cache_s, dev),
+                 capacity=D.capacity, conv_q=T.to_device(D.conv_q_s, dev),
+                 conv_k=T.to_device(D.conv_k_s, dev), vshift=T.to_device(D.vshift_s, dev))
+    return st
+
+
+def _oracle_decode(D, b_list=None):
+    s = D.shape
+    w = D.weights.f64()
+    cq, ck, vs = D.state_f64()
+    B = s.batch
+    bs = range(B) if b_list is None else b_list
+    ys, news = [], []
+    for b in bs:
+        K = D.cache_f64(b, "k")[None]
+        V = D.cache_f64(b, "v")[None]
+        y, new = O.decode_step(D.x[b:b + 1], w, s, K, V, cq[b:b + 1], ck[b:b + 1], vs[b:b + 1])
+        ys.append(y[0])
+        news.append(new)
+    return np.stack(ys), news
+
+
+@pytest.mark.parametrize("L_", [0, 1, 5, 1023, 1024, 1025, 3000])
+def test_decode_small_parity(L_):
+    shape = CCAShape(batch=3, seq_len=1, d_model=256, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                     rope_base=500000.0, cache_len=L_)
+    _say(f"[decode] L={L_}")
+    D = make_decode(shape, seed=L_, capacity=L_ + 3)
+    T, Lb = tens(), lib()
+    st = _upload_decode(D)
+    w = upload_weights(D.weights)
+    cfg = Lb.make_config(shape)
+    x_t = T.to_device(D.x_s)
+    y_t = torch.empty_like(x_t)
+    ws = T.workspace(Lb.decode_workspace_size(cfg, L_))
+    Lb.decode_step(cfg, w, x_t, L_, st, st, y_t, ws)
+    torch.cuda.synchronize()
+    ref, news = _oracle_decode(D)
+    assert_parity(T.to_f64(y_t), ref, "bf16", "y_t")
+    kc = T.to_f64(st.k_cache)
+    vc = T.to_f64(st.v_cache)
+    for b, new in enumerate(news):
+        assert rel_l2(kc[b, :, L_], new["k_new"][0]) < 5e-3
+        assert rel_l2(vc[b, :, L_], new["v_new"][0]) < 5e-3
+        assert rel_l2(T.to_f64(st.conv_q)[b], new["conv_q"][0]) < 5e-3
+        assert rel_l2(T.to_f64(st.conv_k)[b], new["conv_k"][0]) < 5e-3
+        assert rel_l2(T.to_f64(st.vshift)[b], new["vshift"][0]) < 5e-3
+    # cache slots before L are untouched
+    for b in range(shape.batch):
+        np.testing.assert_array_equal(kc[b, :, :L_], D.cache_f64(b, "k"))
+        np.testing.assert_array_equal(vc[b, :, :L_], D.cache_f64(b, "v"))
+
+
+def test_decode_f32_validation_mode():
+    shape = CCAShape(batch=2, seq_len=1, d_model=128, n_q_heads=4, n_kv_heads=2, head_dim=16,
+                     dtype="f32", cache_len=700)
+    D = make_decode(shape, seed=4)
+    T, Lb = tens(), lib()
+    st = _upload_decode(D)
+    cfg = Lb.make_config(shape)
+    x_t = T.to_device(D.x_s)
+    y_t = torch.empty_like(x_t)
+    ws = T.workspace(Lb.decode_workspace_size(cfg, shape.cache_len))
+    Lb.decode_step(cfg, upload_weights(D.weights), x_t, shape.cache_len, st, st, y_t, ws)
+    torch.cuda.synchronize()
+    ref, _ = _oracle_decode(D)
+    assert_parity(T.to_f64(y_t), ref, "f32", "decode f32")
+
+
+def test_decode_workload_full():
+    shape = workload("ccgqa_decode_b64_l32768")
+    _say("[decode] full workload B=64 L=32768")
+    D = make_decode(shape, seed=0)
+    T, Lb = tens(), lib()
+    st = _upload_decode(D)
+    cfg = Lb.make_config(shape)
+    x_t = T.to_device(D.x_s)
+    y_t = torch.empty_like(x_t)
+    ws = T.workspace(Lb.decode_workspace_size(cfg, shape.cache_len))
+    Lb.decode_step(cfg, upload_weights(D.weights), x_t, shape.cache_len, st, st, y_t, ws)
+    torch.cuda.synchronize()
+    ref, news = _oracle_decode(D)
+    assert_parity(T.to_f64(y_t), ref, "bf16", "decode workload")
+    L_ = shape.cache_len
+    kc = st.k_cache[:, :, L_].float().cpu().numpy()
+    vc = st.v_cache[:, :, L_].float().cpu().numpy()
+    assert rel_l2(kc, np.stack([n["k_new"][0] for n in news])) < 5e-3
+    assert rel_l2(vc, np.stack([n["v_new"][0] for n in news])) < 5e-3
