@@ -42,7 +42,21 @@ def parse():
     p.add_argument("--decode", default="ccgqa_decode_b64_l32768")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
+                        "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
 def upload_weights(cca, T, W, dev):
@@ -102,6 +116,9 @@ def cpu_baseline(sp, seconds):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is a design note, not a measured configuration.", file=sys.stderr)

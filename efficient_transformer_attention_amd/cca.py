@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libcca.so")
 
 CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_WORKSPACE, CCA_ERR_HIP = range(5)
 CCA_BF16, CCA_F32 = 0, 1
-WS_QKV, WS_Q, WS_K, WS_VT, WS_O, WS_PART, WS_COUNT = range(7)
+WS_QKV, WS_Q, WS_K, WS_VT, WS_O, WS_PART, WS_SPLITK, WS_COUNT = range(8)
 
 # Every entry point declared in include/cca.h.
 EXPORTS = (

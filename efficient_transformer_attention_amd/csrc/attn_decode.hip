@@ -6,186 +6,271 @@
 // bandwidth [GS-EN "1. Problem Statement"]; CCGQA's shared latent kv heads
 // make that cache small [GS-EN "2. Methodology" / "Extension: CCGQA"].
 //
-// Design (MI355X): split-KV.  A workgroup (4 waves) streams one chunk of
-// keys of one (sequence, kv head, up to 4 query heads).  A lane reads 16
-// contiguous bytes of a K row and of the matching V row, so one wave load
-// instruction covers whole consecutive 128-byte rows (coalesced); the dot
-// products are reduced across the d/8 lanes of a row, and each lane keeps its
-// own online-softmax state (max, sum, unnormalised output of its 8 channels)
-// over blocks of NB keys, so the rescale costs one exp per block.  The lane
-// states are merged with cross-lane exchanges, the 4 waves through LDS, and
-// each chunk leaves (m, l, o) in fp32 scratch.  A second small kernel merges
-// the chunks with the log-sum-exp rule and writes the latent output.
+// Design (MI355X): split-KV with the arithmetic on the matrix cores, so the
+// kernel is bound by HBM and not by VALU issue.
+//  * A workgroup (4 waves) streams one chunk of keys of one (sequence, kv
+//    head); its G query heads (up to 32) are the N columns of the MFMA tiles.
+//  * Per 32-key tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16:
+//    the K rows are loaded from HBM straight into the A-operand layout (lane:
+//    one key row, 16 contiguous bytes).  q is fp32; it is split into a bf16
+//    high part and a bf16 remainder, two MFMAs, so the logits keep ~16 bits
+//    more than a single bf16 rounding of q would.
+//  * The S^T accumulator holds one query head per lane, which is the B-operand
+//    layout of O^T = V^T P^T; V rows go through a wave-private LDS tile
+//    (coalesced 16-byte writes, 16-bit transposed reads).
+//  * Online softmax per lane in fp32 (exp2, tau * log2(e) folded into q);
+//    the 4 waves merge through LDS and each chunk leaves (m, l, o) in fp32
+//    scratch; a second kernel merges the chunks with the log-sum-exp rule.
 #include "cca_device.h"
 #include "cca_launch.h"
 
 namespace cca {
 
-static constexpr int DEC_CHUNK = 1024;   // keys per workgroup
-static constexpr int NB = 4;             // keys per lane per softmax block
+static constexpr int DEC_CHUNK = 4096;   // keys per workgroup
+static constexpr int DEC_TILE = 32;      // keys per MFMA tile
+static constexpr int DEC_F32_MAXG = 8;   // query heads per workgroup, fp32 path
+
+// Query heads per workgroup of the MFMA path (the N columns of a 32x32 tile);
+// capped lower at d = 128 so the merge buffer stays within 64 KiB of LDS.
+template <int D> struct DecMaxG { static constexpr int value = D <= 64 ? 32 : 16; };
 
 int decode_chunk_keys(int) { return DEC_CHUNK; }
 
-size_t decode_partial_floats(int B, int Hq, int d, int Lk) {
-  const int nch = (Lk + DEC_CHUNK - 1) / DEC_CHUNK;
-  return (size_t)B * Hq * nch * (d + 2);
+// Largest divisor of G that is <= cap.
+static int dec_heads_per_wg(int G, int cap) {
+  for (int gh = cap < G ? cap : G; gh >= 1; --gh)
+    if (G % gh == 0) return gh;
+  return 1;
 }
 
-template <typename TV> struct Row16;
-template <> struct Row16<bf16> {
-  static constexpr int E = 8;
-  __device__ __forceinline__ static void cvt(u32x4 r, float *f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(r[i] << 16);
-      f[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
-    }
+// Number of key chunks per (sequence, kv head): about DEC_CHUNK keys each,
+// chosen so the grid fills whole rounds of the workgroups the chip holds at
+// once (256 CUs x 2 resident workgroups) when that costs little.
+static int dec_num_chunks(int B, int Hkv, int Lk) {
+  const int streams = B * Hkv, slots = 512;
+  int best = (Lk + DEC_CHUNK - 1) / DEC_CHUNK;
+  long long best_cost = -1;
+  for (int n = (Lk + 2 * DEC_CHUNK - 1) / (2 * DEC_CHUNK); n <= (Lk + DEC_CHUNK / 2 - 1) / (DEC_CHUNK / 2); ++n) {
+    if (n < 1) continue;
+    const long long rounds = ((long long)streams * n + slots - 1) / slots;
+    const long long cost = rounds * ((Lk + n - 1) / n);
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = n; }
   }
-};
-template <> struct Row16<float> {
-  static constexpr int E = 4;
-  __device__ __forceinline__ static void cvt(u32x4 r, float *f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(r[i]);
-  }
-};
+  return best;
+}
 
-__device__ __forceinline__ float safe_exp2_diff(float a, float m) {
+static int dec_chunk_len(int Lk, int nch) {
+  const int per = (Lk + nch - 1) / nch;
+  return (per + 2 * DEC_TILE - 1) / (2 * DEC_TILE) * (2 * DEC_TILE);
+}
+
+size_t decode_partial_floats(int B, int Hq, int Hkv, int d, int Lk) {
+  return (size_t)B * Hq * dec_num_chunks(B, Hkv, Lk) * (d + 2);
+}
+
+__device__ __forceinline__ float exp2_or_zero(float a, float m) {
   return a == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a - m);
 }
 
-template <typename TV, int D, int GH>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const float *__restrict__ q,
-                                                          const float *__restrict__ tau,
-                                                          const TV *__restrict__ kc,
-                                                          const TV *__restrict__ vc, int cap,
-                                                          int Lk, int Hq, int Hkv, int G,
-                                                          int nquad, int nch,
-                                                          float *__restrict__ part) {
-  constexpr int E = Row16<TV>::E;          // elements per 16-byte lane load
-  constexpr int DS = D / E;                // lanes per key row
-  constexpr int KPS = 64 / DS;             // keys per wave load
-  __shared__ float red[4][GH][D + 2];
+// ---------------------------------------------------------------------------
+// bf16 cache: MFMA path
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__restrict__ q,
+                                                               const float *__restrict__ tau,
+                                                               const bf16 *__restrict__ kc,
+                                                               const bf16 *__restrict__ vc, int cap,
+                                                               int Lk, int chunk, int Hq, int Hkv,
+                                                               int G, int GH, int nsub, int nch,
+                                                               float *__restrict__ part) {
+  constexpr int QC = D / 16;                 // contraction chunks of S^T
+  constexpr int ND = D < 32 ? 1 : D / 32;    // O^T row blocks
+  constexpr int MAXG = DecMaxG<D>::value;
+  constexpr int TPI = D <= 64 ? 2 : 1;       // 32-key tiles per wave iteration
+  // LDS V row stride: 16 bytes of padding put rows r and r+4 (the two lane
+  // halves of one transposed read) on disjoint banks.
+  constexpr int VROW = D * 2 + 16;
+  constexpr int VTILE = DEC_TILE * VROW;
+  constexpr int VBYTES = 4 * TPI * VTILE;
+  constexpr int RBYTES = 4 * MAXG * (D + 2) * 4;
+  // the per-wave V tiles and, after the key loop, the wave-merge buffer
+  __shared__ __attribute__((aligned(16))) unsigned char smem[VBYTES > RBYTES ? VBYTES : RBYTES];
+  typedef float RedRow[D + 2];
+  RedRow *red = reinterpret_cast<RedRow *>(smem);   // [wave * MAXG + column]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
   int id = blockIdx.x;
   const int c = id % nch; id /= nch;
-  const int quad = id % nquad; id /= nquad;
+  const int sub = id % nsub; id /= nsub;
   const int g = id % Hkv, b = id / Hkv;
-  const int h0 = g * G + quad * GH;
-  const int seg = lane % DS, ksub = lane / DS;
+  const int h0 = g * G + sub * GH;
+  const bool col_ok = l32 < GH;              // this lane's column is a real query head
 
-  float qv[GH][E];
+  // q of head (h0 + l32) scaled by tau*log2(e), split into bf16 hi + lo
+  bf16x8 qhi[QC], qlo[QC];
+  {
+    const float sc = col_ok ? tau[h0 + l32] * 1.4426950408889634f : 0.f;
+    const float *qr = q + (size_t)(b * Hq + h0 + (col_ok ? l32 : 0)) * D;
 #pragma unroll
-  for (int hh = 0; hh < GH; ++hh) {
-    const float sc = tau[h0 + hh] * 1.4426950408889634f;
+    for (int cc = 0; cc < QC; ++cc)
 #pragma unroll
-    for (int e = 0; e < E; ++e) qv[hh][e] = q[(size_t)(b * Hq + h0 + hh) * D + seg * E + e] * sc;
+      for (int s = 0; s < 8; ++s) {
+        const float v = col_ok ? qr[16 * cc + 8 * hl + s] * sc : 0.f;
+        const bf16 hi = (bf16)v;
+        qhi[cc][s] = hi;
+        qlo[cc][s] = (bf16)(v - (float)hi);
+      }
   }
 
-  const int kbeg = c * DEC_CHUNK;
-  const int kend = min(kbeg + DEC_CHUNK, Lk);
-  const TV *kb = kc + (size_t)(b * Hkv + g) * cap * D;
-  const TV *vb = vc + (size_t)(b * Hkv + g) * cap * D;
+  const int kbeg = c * chunk;
+  const int kend = min(kbeg + chunk, Lk);
+  const int ntile = (kend - kbeg + DEC_TILE - 1) / DEC_TILE;
+  const bf16 *kb = kc + (size_t)(b * Hkv + g) * cap * D;
+  const bf16 *vb = vc + (size_t)(b * Hkv + g) * cap * D;
+  unsigned char *myv = smem + wave * TPI * VTILE;
 
-  float m[GH], l[GH], acc[GH][E];
+  f32x16 acc[ND];
 #pragma unroll
-  for (int hh = 0; hh < GH; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
+  for (int i = 0; i < ND; ++i) acc[i] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // tiles of wave w: w*TPI + 4*TPI*it + u; rows past the chunk end are clamped
+  // to its last key (finite data, masked below)
+  constexpr int VPL = (DEC_TILE * D / 8 + 63) / 64;   // 16-byte V pieces per lane per tile
+  u32x4 kreg[TPI][QC], vreg[TPI][VPL];
+  auto gload = [&](int t0) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
+    for (int u = 0; u < TPI; ++u) {
+      const int k0 = kbeg + (t0 + u) * DEC_TILE;
+      const int krow = min(k0 + l32, kend - 1);
+#pragma unroll
+      for (int cc = 0; cc < QC; ++cc) kreg[u][cc] = ld16(kb + (size_t)krow * D + 16 * cc + 8 * hl);
+#pragma unroll
+      for (int r = 0; r < VPL; ++r) {
+        const int e = lane + 64 * r;
+        if (e < DEC_TILE * D / 8) {
+          const int row = e / (D / 8), seg = e % (D / 8);
+          vreg[u][r] = ld16(vb + (size_t)min(k0 + row, kend - 1) * D + 8 * seg);
+        }
+      }
+    }
+  };
+
+  const int step = 4 * TPI;
+  int t = wave * TPI;
+  if (t < ntile) gload(t);
+  for (; t < ntile; t += step) {
+    // stage V (wave-private), then S^T = K Q^T for the TPI tiles
+#pragma unroll
+    for (int u = 0; u < TPI; ++u)
+#pragma unroll
+      for (int r = 0; r < VPL; ++r) {
+        const int e = lane + 64 * r;
+        if (e < DEC_TILE * D / 8) {
+          const int row = e / (D / 8), seg = e % (D / 8);
+          unsigned char *dst = myv + u * VTILE + row * VROW + seg * 16;
+          *reinterpret_cast<u32x2 *>(dst) = u32x2{vreg[u][r][0], vreg[u][r][1]};
+          *reinterpret_cast<u32x2 *>(dst + 8) = u32x2{vreg[u][r][2], vreg[u][r][3]};
+        }
+      }
+    __builtin_amdgcn_wave_barrier();
+    f32x16 s[TPI];
+#pragma unroll
+    for (int u = 0; u < TPI; ++u) {
+      s[u] = zero16();
+#pragma unroll
+      for (int cc = 0; cc < QC; ++cc) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&kreg[u][cc]);
+        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qhi[cc], s[u], 0, 0, 0);
+        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qlo[cc], s[u], 0, 0, 0);
+      }
+    }
+    if (t + step < ntile) gload(t + step);   // next tiles' loads overlap this iteration's math
+    // mask keys past the chunk end, online softmax per column over TPI*32 keys
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < TPI; ++u) {
+      const int k0 = kbeg + (t + u) * DEC_TILE;
+      const bool tail = k0 + DEC_TILE > kend;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        float v = s[u][a];
+        if (tail && k0 + 8 * (a >> 2) + 4 * hl + (a & 3) >= kend) v = -INFINITY;
+        s[u][a] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < TPI; ++u)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const float p = __builtin_amdgcn_exp2f(s[u][a] - m_new);
+        s[u][a] = p;
+        ps += p;
+      }
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) acc[i][a] *= alpha;
+    // O^T += V^T P^T: k-slot sl of lane half hl <-> key 16*cc2 + 8*(sl/4) + 4*hl + sl%4
+#pragma unroll
+    for (int u = 0; u < TPI; ++u)
+#pragma unroll
+      for (int cc2 = 0; cc2 < 2; ++cc2) {
+        bf16x8 pf;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) pf[sl] = (bf16)s[u][8 * cc2 + sl];
+#pragma unroll
+        for (int i = 0; i < ND; ++i) {
+          const int dd = 32 * i + l32;
+          bf16x8 vf;
+#pragma unroll
+          for (int sl = 0; sl < 8; ++sl) {
+            const int key = 16 * cc2 + 8 * (sl >> 2) + 4 * hl + (sl & 3);
+            vf[sl] = dd < D ? *reinterpret_cast<const bf16 *>(myv + u * VTILE + key * VROW + dd * 2)
+                            : (bf16)0.f;
+          }
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[i], 0, 0, 0);
+        }
+      }
   }
 
-  const int per_iter = 4 * NB * KPS;
-  for (int base = kbeg; base < kend; base += per_iter) {
-    float kf[NB][E], vf[NB][E];
-    bool valid[NB];
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      const int key = base + (wave * NB + s) * KPS + ksub;
-      valid[s] = key < kend;
-      const int kk = valid[s] ? key : kbeg;
-      Row16<TV>::cvt(ld16(kb + (size_t)kk * D + seg * E), kf[s]);
-      Row16<TV>::cvt(ld16(vb + (size_t)kk * D + seg * E), vf[s]);
+  // merge the 4 waves: lane (column l32, half hl) holds O^T rows 8j + 4hl + i
+  __syncthreads();                            // every wave is done with its V tiles
+  if (col_ok) {
+    RedRow &row = red[wave * MAXG + l32];
+    if (hl == 0) {
+      row[0] = m_run;
+      row[1] = l_run;
     }
-    float sc[NB][GH];
 #pragma unroll
-    for (int s = 0; s < NB; ++s)
+    for (int i = 0; i < ND; ++i)
 #pragma unroll
-      for (int hh = 0; hh < GH; ++hh) {
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) dot = fmaf(qv[hh][e], kf[s][e], dot);
-#pragma unroll
-        for (int o = DS / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
-        sc[s][hh] = valid[s] ? dot : -INFINITY;
+      for (int a = 0; a < 16; ++a) {
+        const int dd = 32 * i + 8 * (a >> 2) + 4 * hl + (a & 3);
+        if (dd < D) row[2 + dd] = acc[i][a];
       }
-#pragma unroll
-    for (int hh = 0; hh < GH; ++hh) {
-      float mb = sc[0][hh];
-#pragma unroll
-      for (int s = 1; s < NB; ++s) mb = fmaxf(mb, sc[s][hh]);
-      const float m_new = fmaxf(m[hh], mb);
-      if (m_new == -INFINITY) continue;          // no valid key seen yet by this lane
-      const float alpha = safe_exp2_diff(m[hh], m_new);
-      l[hh] *= alpha;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[hh][e] *= alpha;
-#pragma unroll
-      for (int s = 0; s < NB; ++s) {
-        const float p = safe_exp2_diff(sc[s][hh], m_new);
-        l[hh] += p;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(p, vf[s][e], acc[hh][e]);
-      }
-      m[hh] = m_new;
-    }
-  }
-
-  // merge the lanes that share a channel segment (different keys)
-#pragma unroll
-  for (int o = DS; o < 64; o <<= 1) {
-#pragma unroll
-    for (int hh = 0; hh < GH; ++hh) {
-      const float mo = __shfl_xor(m[hh], o, 64);
-      const float lo = __shfl_xor(l[hh], o, 64);
-      const float mn = fmaxf(m[hh], mo);
-      const float a = mn == -INFINITY ? 0.f : safe_exp2_diff(m[hh], mn);
-      const float bo = mn == -INFINITY ? 0.f : safe_exp2_diff(mo, mn);
-      l[hh] = l[hh] * a + lo * bo;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float ao = __shfl_xor(acc[hh][e], o, 64);
-        acc[hh][e] = acc[hh][e] * a + ao * bo;
-      }
-      m[hh] = mn;
-    }
-  }
-  if (ksub == 0) {
-#pragma unroll
-    for (int hh = 0; hh < GH; ++hh) {
-      if (seg == 0) {
-        red[wave][hh][0] = m[hh];
-        red[wave][hh][1] = l[hh];
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) red[wave][hh][2 + seg * E + e] = acc[hh][e];
-    }
   }
   __syncthreads();
-  // merge the 4 waves and write the chunk's partial state
   for (int e = tid; e < GH * D; e += 256) {
     const int hh = e / D, dd = e % D;
     float mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][hh][0]);
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w * MAXG + hh][0]);
     float ll = 0.f, oo = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = safe_exp2_diff(red[w][hh][0], mm);
-      ll += red[w][hh][1] * f;
-      oo += red[w][hh][2 + dd] * f;
+      const float f = exp2_or_zero(red[w * MAXG + hh][0], mm);
+      ll += red[w * MAXG + hh][1] * f;
+      oo += red[w * MAXG + hh][2 + dd] * f;
     }
     float *dst = part + ((size_t)(b * Hq + h0 + hh) * nch + c) * (D + 2);
     dst[2 + dd] = oo;
@@ -196,75 +281,182 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float *__restric
   }
 }
 
-// o[b, h*D + dd] = sum_c 2^(m_c - M) o_c[dd] / sum_c 2^(m_c - M) l_c
-template <typename TV, int D>
-__global__ __launch_bounds__(64) void attn_decode_combine_kernel(const float *__restrict__ part,
-                                                                 int nch, int Hq,
-                                                                 TV *__restrict__ o) {
-  const int bh = blockIdx.x;   // b * Hq + h
-  const float *p = part + (size_t)bh * nch * (D + 2);
-  float mm = -INFINITY;
-  for (int c = 0; c < nch; ++c) mm = fmaxf(mm, p[c * (D + 2)]);
-  for (int dd = threadIdx.x; dd < D; dd += 64) {
-    float ll = 0.f, oo = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float f = safe_exp2_diff(p[c * (D + 2)], mm);
-      ll += p[c * (D + 2) + 1] * f;
-      oo += p[c * (D + 2) + 2 + dd] * f;
+// ---------------------------------------------------------------------------
+// fp32 cache (validation mode): same split and merge, VALU arithmetic
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__restrict__ q,
+                                                              const float *__restrict__ tau,
+                                                              const float *__restrict__ kc,
+                                                              const float *__restrict__ vc,
+                                                              int cap, int Lk, int chunk, int Hq,
+                                                              int Hkv, int G, int GH, int nsub,
+                                                              int nch, float *__restrict__ part) {
+  // one thread per (query head, key) score; waves walk the chunk in 256-key steps
+  __shared__ float qs[DEC_F32_MAXG][D];
+  __shared__ float pbuf[DEC_F32_MAXG][256];
+  __shared__ float mst[DEC_F32_MAXG], lst[DEC_F32_MAXG], alph[DEC_F32_MAXG];
+  __shared__ float oacc[DEC_F32_MAXG][D];
+  const int tid = threadIdx.x;
+  int id = blockIdx.x;
+  const int c = id % nch; id /= nch;
+  const int sub = id % nsub; id /= nsub;
+  const int g = id % Hkv, b = id / Hkv;
+  const int h0 = g * G + sub * GH;
+  for (int e = tid; e < GH * D; e += 256) {
+    const int hh = e / D, dd = e % D;
+    qs[hh][dd] = q[(size_t)(b * Hq + h0 + hh) * D + dd] * tau[h0 + hh] * 1.4426950408889634f;
+    oacc[hh][dd] = 0.f;
+  }
+  for (int e = tid; e < GH; e += 256) { mst[e] = -INFINITY; lst[e] = 0.f; }
+  __syncthreads();
+  const int kbeg = c * chunk, kend = min(kbeg + chunk, Lk);
+  const float *kb = kc + (size_t)(b * Hkv + g) * cap * D;
+  const float *vb = vc + (size_t)(b * Hkv + g) * cap * D;
+  for (int k0 = kbeg; k0 < kend; k0 += 256) {
+    const int key = k0 + tid;
+    for (int hh = 0; hh < GH; ++hh) {
+      float s = -INFINITY;
+      if (key < kend) {
+        s = 0.f;
+        for (int dd = 0; dd < D; ++dd) s = fmaf(qs[hh][dd], kb[(size_t)key * D + dd], s);
+      }
+      pbuf[hh][tid] = s;
     }
-    o[(size_t)bh * D + dd] = from_f32<TV>(oo / ll);
+    __syncthreads();
+    for (int hh = tid; hh < GH; hh += 256) {
+      float mx = mst[hh];
+      for (int j = 0; j < 256; ++j) mx = fmaxf(mx, pbuf[hh][j]);
+      const float a = exp2_or_zero(mst[hh], mx);
+      float ls = 0.f;
+      for (int j = 0; j < 256; ++j) {
+        const float p = exp2_or_zero(pbuf[hh][j], mx);
+        pbuf[hh][j] = p;
+        ls += p;
+      }
+      lst[hh] = lst[hh] * a + ls;
+      mst[hh] = mx;
+      alph[hh] = a;
+    }
+    __syncthreads();
+    for (int e = tid; e < GH * D; e += 256) {
+      const int hh = e / D, dd = e % D;
+      float o = oacc[hh][dd] * alph[hh];
+      const int n = min(256, kend - k0);
+      for (int j = 0; j < n; ++j) o = fmaf(pbuf[hh][j], vb[(size_t)(k0 + j) * D + dd], o);
+      oacc[hh][dd] = o;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < GH * D; e += 256) {
+    const int hh = e / D, dd = e % D;
+    float *dst = part + ((size_t)(b * Hq + h0 + hh) * nch + c) * (D + 2);
+    dst[2 + dd] = oacc[hh][dd];
+    if (dd == 0) { dst[0] = mst[hh]; dst[1] = lst[hh]; }
   }
 }
 
-static int group_heads(int G) {
-  for (int gh = 4; gh >= 1; --gh)
-    if (G % gh == 0) return gh;
-  return 1;
+// o[b, h*D + dd] = sum_c 2^(m_c - M) o_c[dd] / sum_c 2^(m_c - M) l_c
+template <typename TV, int D>
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float *__restrict__ part,
+                                                                  int nch, TV *__restrict__ o) {
+  __shared__ float wts[1024];
+  __shared__ float red[256 / D > 0 ? 256 / D : 1][D];
+  __shared__ float s_m, s_l;
+  const int bh = blockIdx.x, tid = threadIdx.x;   // bh = b * Hq + h
+  const float *p = part + (size_t)bh * nch * (D + 2);
+  if (tid < 64) {
+    float mm = -INFINITY;
+    for (int c = tid; c < nch; c += 64) mm = fmaxf(mm, p[(size_t)c * (D + 2)]);
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o2, 64));
+    float ll = 0.f;
+    for (int c = tid; c < nch; c += 64) {
+      const float w = exp2_or_zero(p[(size_t)c * (D + 2)], mm);
+      if (c < 1024) wts[c] = w;
+      ll += w * p[(size_t)c * (D + 2) + 1];
+    }
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) ll += __shfl_xor(ll, o2, 64);
+    if (tid == 0) { s_m = mm; s_l = ll; }
+  }
+  __syncthreads();
+  constexpr int NG = 256 / D > 0 ? 256 / D : 1;   // chunk groups
+  const int dd = tid % D, grp = tid / D;
+  if (grp < NG) {
+    float oo = 0.f;
+    for (int c = grp; c < nch; c += NG) {
+      const float w = c < 1024 ? wts[c] : exp2_or_zero(p[(size_t)c * (D + 2)], s_m);
+      oo += w * p[(size_t)c * (D + 2) + 2 + dd];
+    }
+    red[grp][dd] = oo;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float oo = 0.f;
+    for (int gi = 0; gi < NG; ++gi) oo += red[gi][tid];
+    o[(size_t)bh * D + tid] = from_f32<TV>(oo / s_l);
+  }
 }
 
-template <typename TV, int D, int GH>
-static hipError_t dec_dgh(const MixShape &s, const float *q, const TV *kc, const TV *vc, int cap,
-                          int Lk, const float *tau, float *part, TV *o, hipStream_t stream) {
-  const int nch = (Lk + DEC_CHUNK - 1) / DEC_CHUNK;
-  const int nquad = s.G / GH;
-  hipLaunchKernelGGL((attn_decode_kernel<TV, D, GH>), dim3(nch * nquad * s.B * s.Hkv), dim3(256),
-                     0, stream, q, tau, kc, vc, cap, Lk, s.Hq, s.Hkv, s.G, nquad, nch, part);
+template <int D>
+static hipError_t dec_bf16(const MixShape &s, const float *q, const bf16 *kc, const bf16 *vc,
+                           int cap, int Lk, const float *tau, float *part, bf16 *o,
+                           hipStream_t stream) {
+  const int nch = dec_num_chunks(s.B, s.Hkv, Lk);
+  const int chunk = dec_chunk_len(Lk, nch);
+  const int GH = dec_heads_per_wg(s.G, DecMaxG<D>::value);
+  const int nsub = s.G / GH;
+  hipLaunchKernelGGL((attn_decode_mfma_kernel<D>), dim3(nch * nsub * s.B * s.Hkv), dim3(256), 0,
+                     stream, q, tau, kc, vc, cap, Lk, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_combine_kernel<TV, D>), dim3(s.B * s.Hq), dim3(64), 0, stream,
-                     part, nch, s.Hq, o);
+  hipLaunchKernelGGL((attn_decode_combine_kernel<bf16, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
+                     part, nch, o);
   return hipGetLastError();
 }
 
-template <typename TV, int D>
-static hipError_t dec_d(const MixShape &s, const float *q, const TV *kc, const TV *vc, int cap,
-                        int Lk, const float *tau, float *part, TV *o, hipStream_t stream) {
-  switch (group_heads(s.G)) {
-    case 4: return dec_dgh<TV, D, 4>(s, q, kc, vc, cap, Lk, tau, part, o, stream);
-    case 3: return dec_dgh<TV, D, 3>(s, q, kc, vc, cap, Lk, tau, part, o, stream);
-    case 2: return dec_dgh<TV, D, 2>(s, q, kc, vc, cap, Lk, tau, part, o, stream);
-    default: return dec_dgh<TV, D, 1>(s, q, kc, vc, cap, Lk, tau, part, o, stream);
-  }
+template <int D>
+static hipError_t dec_f32(const MixShape &s, const float *q, const float *kc, const float *vc,
+                          int cap, int Lk, const float *tau, float *part, float *o,
+                          hipStream_t stream) {
+  const int nch = dec_num_chunks(s.B, s.Hkv, Lk);
+  const int chunk = dec_chunk_len(Lk, nch);
+  const int GH = dec_heads_per_wg(s.G, DEC_F32_MAXG);
+  const int nsub = s.G / GH;
+  hipLaunchKernelGGL((attn_decode_f32_kernel<D>), dim3(nch * nsub * s.B * s.Hkv), dim3(256), 0,
+                     stream, q, tau, kc, vc, cap, Lk, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_decode_combine_kernel<float, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
+                     part, nch, o);
+  return hipGetLastError();
 }
 
-template <typename TV>
-hipError_t launch_attention_decode(const MixShape &s, const float *q, const TV *k_cache,
-                                   const TV *v_cache, int capacity, int Lk, const float *tau,
-                                   float *part, TV *o, hipStream_t stream) {
+template <>
+hipError_t launch_attention_decode<bf16>(const MixShape &s, const float *q, const bf16 *k_cache,
+                                         const bf16 *v_cache, int capacity, int Lk,
+                                         const float *tau, float *part, bf16 *o,
+                                         hipStream_t stream) {
   switch (s.d) {
-    case 16: return dec_d<TV, 16>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 32: return dec_d<TV, 32>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 64: return dec_d<TV, 64>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 128: return dec_d<TV, 128>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 16: return dec_bf16<16>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 32: return dec_bf16<32>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 64: return dec_bf16<64>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 128: return dec_bf16<128>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
   }
   return hipErrorInvalidValue;
 }
 
-template hipError_t launch_attention_decode<bf16>(const MixShape &, const float *, const bf16 *,
-                                                  const bf16 *, int, int, const float *, float *,
-                                                  bf16 *, hipStream_t);
-template hipError_t launch_attention_decode<float>(const MixShape &, const float *, const float *,
-                                                   const float *, int, int, const float *,
-                                                   float *, float *, hipStream_t);
+template <>
+hipError_t launch_attention_decode<float>(const MixShape &s, const float *q, const float *k_cache,
+                                          const float *v_cache, int capacity, int Lk,
+                                          const float *tau, float *part, float *o,
+                                          hipStream_t stream) {
+  switch (s.d) {
+    case 16: return dec_f32<16>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 32: return dec_f32<32>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 64: return dec_f32<64>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 128: return dec_f32<128>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 }  // namespace cca

@@ -130,10 +130,24 @@ Layout decode_layout(const cca_config &c, int cache_len) {
   L.off[CCA_WS_QKV] = o;  o = align_up(o + B * N * 4, WS_ALIGN);
   L.off[CCA_WS_Q] = o;    o = align_up(o + B * c.n_q_heads * d * 4, WS_ALIGN);
   L.off[CCA_WS_PART] = o;
-  o = align_up(o + decode_partial_floats(c.batch, c.n_q_heads, c.head_dim, cache_len + 1) * 4, WS_ALIGN);
+  o = align_up(o + decode_partial_floats(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, cache_len + 1) * 4, WS_ALIGN);
   L.off[CCA_WS_O] = o;    o = align_up(o + B * eq * elem_size(c.dtype), WS_ALIGN);
+  if (c.batch <= 64) {   // split-contraction partial sums of the two skinny projections
+    const int es = (int)elem_size(c.dtype);
+    const size_t down = (size_t)gemm_splitk_slices(c.batch, (int)N, c.d_model, es) * B * N;
+    const size_t up = (size_t)gemm_splitk_slices(c.batch, c.d_model, (int)eq, es) * B * c.d_model;
+    L.off[CCA_WS_SPLITK] = o;
+    o = align_up(o + (down > up ? down : up) * 4, WS_ALIGN);
+  }
   L.total = o;
   return L;
+}
+
+// fp32 scratch of the split-contraction GEMM path (decode only).
+float *splitk_ptr(void *ws, const Layout &L, size_t *floats) {
+  if (L.off[CCA_WS_SPLITK] == SIZE_MAX) { *floats = 0; return nullptr; }
+  *floats = (L.total - L.off[CCA_WS_SPLITK]) / 4;
+  return reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + L.off[CCA_WS_SPLITK]);
 }
 
 cca_status check_weights(const cca_weights *w) {
@@ -240,13 +254,15 @@ cca_status run_attention(const cca_config &c, const cca_weights *w, void *ws, co
 cca_status run_upproj(const cca_config &c, const cca_weights *w, void *y, void *ws,
                       const Layout &L, int M, hipStream_t st) {
   const int E = c.d_model, eq = c.n_q_heads * c.head_dim;
+  size_t skf;
+  float *sk = splitk_ptr(ws, L, &skf);
   hipError_t e;
   if (c.dtype == CCA_BF16)
     e = launch_gemm_nt<bf16, bf16>((const bf16 *)wsp(ws, L, CCA_WS_O), (const bf16 *)w->w_o,
-                                   (bf16 *)y, M, E, eq, eq, eq, E, st);
+                                   (bf16 *)y, M, E, eq, eq, eq, E, st, sk, skf);
   else
     e = launch_gemm_nt<float, float>((const float *)wsp(ws, L, CCA_WS_O), (const float *)w->w_o,
-                                     (float *)y, M, E, eq, eq, eq, E, st);
+                                     (float *)y, M, E, eq, eq, eq, E, st, sk, skf);
   return check_launch(e, st);
 }
 
@@ -403,11 +419,15 @@ static cca_status dec_downproj(const cca_config &c, const cca_weights *w, const 
   const int M = c.batch, E = c.d_model;
   const int N = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   float *qkv = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_QKV));
+  size_t skf;
+  float *sk = splitk_ptr(ws, L, &skf);
   hipError_t e;
   if (c.dtype == CCA_BF16)
-    e = launch_gemm_nt<bf16, float>((const bf16 *)x_t, (const bf16 *)w->w_qkv, qkv, M, N, E, E, E, N, st);
+    e = launch_gemm_nt<bf16, float>((const bf16 *)x_t, (const bf16 *)w->w_qkv, qkv, M, N, E, E, E,
+                                    N, st, sk, skf);
   else
-    e = launch_gemm_nt<float, float>((const float *)x_t, (const float *)w->w_qkv, qkv, M, N, E, E, E, N, st);
+    e = launch_gemm_nt<float, float>((const float *)x_t, (const float *)w->w_qkv, qkv, M, N, E, E,
+                                     E, N, st, sk, skf);
   return check_launch(e, st);
 }
 

@@ -9,10 +9,16 @@
 namespace cca {
 
 // C[M,N] = A[M,K] * B[N,K]^T, fp32 accumulation.  K * sizeof(Tin) must be a
-// multiple of 16 bytes and every row 16-byte aligned.
+// multiple of 16 bytes and every row 16-byte aligned.  With M <= 64 and a
+// fp32 scratch of splitk_floats floats, the contraction is split over
+// workgroups and reduced by a second kernel (deterministic order).
 template <typename Tin, typename Tout>
 hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int K, int lda,
-                          int ldb, int ldc, hipStream_t stream);
+                          int ldb, int ldc, hipStream_t stream, float *splitk_ws = nullptr,
+                          size_t splitk_floats = 0);
+
+// Contraction slices the skinny path uses for an M x N x K product.
+int gemm_splitk_slices(int M, int N, int K, int elem_bytes);
 
 // Sizes shared by the mixing and attention kernels.
 struct MixShape {
@@ -71,6 +77,6 @@ bool convmix_fits(int G, int d);
 // Keys handled by one workgroup of the split-KV decode attention, and the
 // partial-state scratch it needs.
 int decode_chunk_keys(int d);
-size_t decode_partial_floats(int B, int Hq, int d, int Lk);
+size_t decode_partial_floats(int B, int Hq, int Hkv, int d, int Lk);
 
 }  // namespace cca

@@ -17,11 +17,15 @@
 
 namespace cca {
 
+// blockIdx.y selects a slice [y*kchunk, (y+1)*kchunk) of the contraction;
+// with more than one slice, C points at fp32 partial sums laid out
+// [gridDim.y][M][ldc] and a reduction kernel finishes the product.
 template <typename Tin, typename Tout, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
                                                       const Tin *__restrict__ Bm,
                                                       Tout *__restrict__ C, int M, int N,
-                                                      int K, int lda, int ldb, int ldc) {
+                                                      int K, int lda, int ldb, int ldc,
+                                                      int kchunk) {
   typedef Mfma32<Tin> MF;
   constexpr int KS = MF::KS;
   constexpr int ROWB = 128;                       // bytes per LDS tile row
@@ -89,14 +93,16 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
+  const int kbeg = blockIdx.y * kchunk;
+  const int nk = (min(K, kbeg + kchunk) - kbeg + BK - 1) / BK;
+  C += (size_t)blockIdx.y * M * ldc;
+  gload(kbeg);
   lstore(0);
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK / (2 * KS); ++kk) {
       const int kb = (kk * 2 * KS + hl * KS) * (int)sizeof(Tin);   // byte offset in row
@@ -135,21 +141,65 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
     }
 }
 
+// out[i] = sum over the S slices of part[s][i], i < n (n a multiple of 4)
+template <typename Tout>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part,
+                                                            Tout *__restrict__ out, size_t n,
+                                                            int S) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4 *>(part + i);
+  for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4 *>(part + (size_t)s * n + i);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[i + e] = from_f32<Tout>(acc[e]);
+}
+
+int gemm_splitk_slices(int M, int N, int K, int elem_bytes) {
+  const int BK = 128 / elem_bytes;
+  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  const int ksteps = (K + BK - 1) / BK;
+  int S = 512 / tiles;
+  if (S > ksteps / 2) S = ksteps / 2;
+  if (S > 16) S = 16;
+  return S < 1 ? 1 : S;
+}
+
 template <typename Tin, typename Tout>
 hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int K, int lda,
-                          int ldb, int ldc, hipStream_t stream) {
+                          int ldb, int ldc, hipStream_t stream, float *splitk_ws,
+                          size_t splitk_floats) {
+  if (M <= 64 && splitk_ws) {
+    // skinny product (a decode step): 64 x 64 tiles and a split contraction so
+    // the weight stream is spread over enough workgroups
+    constexpr int BM = 64, BN = 64, BK = 128 / (int)sizeof(Tin);
+    const int S = gemm_splitk_slices(M, N, K, (int)sizeof(Tin));
+    const int ksteps = (K + BK - 1) / BK;
+    const int kchunk = (ksteps + S - 1) / S * BK;
+    const int Sused = (K + kchunk - 1) / kchunk;
+    if ((size_t)Sused * M * ldc <= splitk_floats && ldc == N && (N % 4) == 0) {
+      const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+      hipLaunchKernelGGL((gemm_nt_kernel<Tin, float, BM, BN>), dim3(grid, Sused), dim3(256), 0,
+                         stream, A, B, splitk_ws, M, N, K, lda, ldb, ldc, kchunk);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const size_t n = (size_t)M * N;
+      hipLaunchKernelGGL((splitk_reduce_kernel<Tout>), dim3((unsigned)((n / 4 + 255) / 256)),
+                         dim3(256), 0, stream, splitk_ws, C, n, Sused);
+      return hipGetLastError();
+    }
+  }
   constexpr int BM = 128, BN = 128;
   int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<Tin, Tout, BM, BN>), dim3(grid), dim3(256), 0, stream, A, B,
-                     C, M, N, K, lda, ldb, ldc);
+  hipLaunchKernelGGL((gemm_nt_kernel<Tin, Tout, BM, BN>), dim3(grid, 1), dim3(256), 0, stream, A,
+                     B, C, M, N, K, lda, ldb, ldc, K);
   return hipGetLastError();
 }
 
 template hipError_t launch_gemm_nt<bf16, float>(const bf16 *, const bf16 *, float *, int, int, int,
-                                                int, int, int, hipStream_t);
+                                                int, int, int, hipStream_t, float *, size_t);
 template hipError_t launch_gemm_nt<bf16, bf16>(const bf16 *, const bf16 *, bf16 *, int, int, int,
-                                               int, int, int, hipStream_t);
+                                               int, int, int, hipStream_t, float *, size_t);
 template hipError_t launch_gemm_nt<float, float>(const float *, const float *, float *, int, int,
-                                                 int, int, int, int, hipStream_t);
+                                                 int, int, int, int, hipStream_t, float *, size_t);
 
 }  // namespace cca

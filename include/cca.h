@@ -192,9 +192,11 @@ const char *cca_status_string(cca_status s);
  *   CCA_WS_Q    fp32 [B, H_q, d]  normalised, rotated q of the new token
  *   CCA_WS_PART fp32 partial softmax states of the split-KV attention
  *   CCA_WS_O    [B, e_q] cfg.dtype
+ *   CCA_WS_SPLITK fp32 partial sums of the two projections, whose contraction
+ *               is split over workgroups when B <= 64
  * ---------------------------------------------------------------------- */
 enum { CCA_WS_QKV = 0, CCA_WS_Q = 1, CCA_WS_K = 2, CCA_WS_VT = 3, CCA_WS_O = 4,
-       CCA_WS_PART = 5, CCA_WS_COUNT = 6 };
+       CCA_WS_PART = 5, CCA_WS_SPLITK = 6, CCA_WS_COUNT = 7 };
 
 /* Byte offsets of the buffers above inside a prefill (decode: cache_len >= 0)
  * workspace; unused slots are set to SIZE_MAX.  Host-only. */
