@@ -86,6 +86,25 @@ def algorithmic(sp, sd):
     }
 
 
+def measured_traffic():
+    """HBM bytes per launch of each kernel from the committed counter summary
+    (profiles/pmc_traffic.json), kept only while the kernel's sources still
+    hash to what they were when the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return {}
+    rec = json.load(open(path))
+    out = {}
+    for key, k in rec.get("kernels", {}).items():
+        h = hashlib.sha256()
+        for f in k["sources"]:
+            h.update(open(os.path.join(ROOT, "efficient_transformer_attention_amd", "csrc", f), "rb").read())
+        if h.hexdigest()[:16] == k["source_sha256_16"]:
+            out[key] = k["bytes"]
+    return out
+
+
 def cpu_baseline(sp, seconds):
     """The fp64 oracle on the host cores: whole sequences of the prefill
     workload until about `seconds` of CPU time are spent."""
@@ -222,6 +241,10 @@ def main():
         tf = alg[f"{g}_flops"] / (stage_ms[g] * 1e-3) / 1e12
         rooflines[g] = {"bound": "mfma", "achieved": round(tf, 1), "peak": mfma_peak,
                         "unit": "TFLOP/s", "frac": round(tf / mfma_peak, 4), "traffic": None}
+    traffic = measured_traffic() if (args.prefill, args.decode) == (
+        "cca_prefill_b4_t2048", "ccgqa_decode_b64_l32768") else {}
+    for key, r in rooflines.items():
+        r["traffic"] = traffic.get(key)
     dominant = max(stage_ms, key=stage_ms.get)
     dom_key = dominant if dominant in rooflines else "dec_attention"
 

@@ -27,6 +27,7 @@ def assert_parity(got, ref, dtype, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     r = rel_l2(got, ref)
     m = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    print(f"[parity] {what}: max-abs {m:.3e} rel-L2 {r:.3e} ({dtype})", flush=True)
     if dtype == "bf16":
         assert m <= BF16_MAXABS and r <= BF16_REL, f"{what}: max-abs {m:.3e} rel-L2 {r:.3e}"
     else:
