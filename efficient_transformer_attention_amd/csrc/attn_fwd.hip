@@ -17,44 +17,61 @@
 //    probabilities are already in the B-operand layout of O^T = V^T P^T: no
 //    LDS round trip for P.  The O^T accumulator again holds one query per
 //    lane, so the online-softmax rescale and the final 1/l stay in-lane.
-//  * K tiles [64 keys][d] and transposed V tiles [d][64 keys] are double
-//    buffered in LDS with a 16-byte XOR swizzle; the value tile's key order
+//  * K tiles [64 keys][d] and transposed V tiles [d][64 keys] (32 keys when
+//    d = 128) are staged in LDS with a 16-byte XOR swizzle; the value tile's key order
 //    is permuted inside 16-key groups (bits 2 and 3 swapped, done once by the
 //    mixing kernel) so one lane's 8 keys are contiguous.
-//  * tau_h * log2(e) scales the fp32 scores, exp2 is the native v_exp_f32.
-//  * Causal blocks: tiles above the diagonal are skipped per wave; the heavy
-//    (late) position blocks are dispatched first.
+//  * The mixing kernel stores q already scaled by tau_h * log2(e), so the
+//    scores come out of the MFMA in the exp2 domain (native v_exp_f32).
+//  * Three K/V^T buffers: while a wave runs the softmax and P*V of tile j it
+//    has already issued the QK^T MFMAs of tile j+1, and tile j+2 is being
+//    written; one barrier per tile.
+//  * The online-softmax rescale of O runs only when some row's running max
+//    grew (a wave-uniform vote); the row sums add the bf16-rounded
+//    probabilities that the P*V product consumes (v_dot2_f32_bf16).
+//  * Causal blocks: tiles above the diagonal are skipped per wave and only
+//    diagonal tiles are masked; the heavy (late) position blocks are
+//    dispatched first.
 #include "cca_device.h"
 #include "cca_launch.h"
 
 namespace cca {
 
-static constexpr int KB = 64;   // keys per tile
+// Keys per tile: 64 when three K/V^T tiles fit in 48 KiB of LDS, else 32.
+template <typename TQ, typename TV, int D> struct AttnTile {
+  static constexpr int DP = D < 32 ? 32 : D;
+  static constexpr int bytes(int kb) { return kb * D * (int)sizeof(TQ) + DP * kb * (int)sizeof(TV); }
+  static constexpr int KB = 3 * bytes(64) <= 49152 ? 64 : 32;
+  static constexpr bool fits = 3 * bytes(KB) <= 49152;
+};
 
 template <typename TQ, typename TV, int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const TQ *__restrict__ q,
-                                                       const TQ *__restrict__ k,
-                                                       const TV *__restrict__ vt,
-                                                       const float *__restrict__ tau,
-                                                       TV *__restrict__ o, int B, int T, int Tp,
-                                                       int Hq, int Hkv, int G, int hq, int nsub,
-                                                       int npb) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__ q,
+                                                          const TQ *__restrict__ k,
+                                                          const TV *__restrict__ vt,
+                                                          TV *__restrict__ o, int B, int T, int Tp,
+                                                          int Hq, int Hkv, int G, int hq, int nsub,
+                                                          int npb) {
   typedef Mfma32<TQ> MQ;
   typedef Mfma32<TV> MV;
+  typedef AttnTile<TQ, TV, D> TL;
+  constexpr int KB = TL::KB;                          // keys per tile
+  constexpr int NH = KB / 32;                         // 32-key halves per tile
   constexpr int KSQ = MQ::KS, KSV = MV::KS;
-  constexpr int DP = D < 32 ? 32 : D;                 // V^T rows (padded to one MFMA tile)
+  constexpr int DP = TL::DP;                          // V^T rows (padded to one MFMA tile)
   constexpr int ND = DP / 32;                         // O^T row blocks of 32
   constexpr int KROW = D * (int)sizeof(TQ);           // bytes per K tile row
   constexpr int KCPR = KROW / 16;
   constexpr int VROW = KB * (int)sizeof(TV);          // bytes per V^T tile row
   constexpr int VCPR = VROW / 16;
-  constexpr int KTILE = KB * KROW, VTILE = DP * VROW;
+  constexpr int KTILE = KB * KROW, VTILE = DP * VROW, BUF = KTILE + VTILE;
   constexpr int K_CH = (KB * KCPR + 255) / 256;       // 16-byte chunks per thread
   constexpr int V_CH = (D * VCPR + 255) / 256;
   constexpr int QC = D / (2 * KSQ);                   // QK^T contraction chunks
   constexpr int PC = 16 / KSV;                        // P*V chunks per 32-key half
+  static_assert(TL::fits, "K/V tiles exceed the LDS budget");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (KTILE + VTILE)];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
@@ -77,18 +94,17 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const TQ *__restrict__ q,
   const int last_row = min(blk0 + pos_per, T) - 1;    // last valid query of the block
   const int ntiles = last_row / KB + 1;
   const int wave_last = p0 + 31;
-
-  const float scale = tau[h] * 1.4426950408889634f;
+  const int wave_tiles = min(ntiles, wave_last / KB + 1);   // tiles this wave computes
 
   // zero the padding rows of the V^T tiles (d < 32)
   if (D < DP) {
-    for (int e = tid; e < 2 * (DP - D) * VROW / 16; e += 256) {
-      const int buf = e / ((DP - D) * VROW / 16), c = e % ((DP - D) * VROW / 16);
-      st16(smem + buf * (KTILE + VTILE) + KTILE + D * VROW + c * 16, zero_u32x4());
-    }
+    constexpr int PADC = (DP - D) * VROW / 16;
+    for (int e = tid; e < 3 * PADC; e += 256)
+      st16(smem + (e / PADC) * BUF + KTILE + D * VROW + (e % PADC) * 16, zero_u32x4());
   }
 
-  // Q fragments of this lane's query (B operand of S^T = K Q^T)
+  // Q fragments of this lane's query (B operand of S^T = K Q^T); q is stored
+  // already scaled by tau_h * log2(e)
   typename MQ::frag qf[QC];
   {
     const TQ *qrow = q + ((size_t)(b * Hq + h) * Tp + qpos) * D;
@@ -117,7 +133,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const TQ *__restrict__ q,
     }
   };
   auto lstore = [&](int buf) {
-    unsigned char *sk = smem + buf * (KTILE + VTILE);
+    unsigned char *sk = smem + buf * BUF;
     unsigned char *sv = sk + KTILE;
 #pragma unroll
     for (int r = 0; r < K_CH; ++r) {
@@ -136,79 +152,93 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const TQ *__restrict__ q,
       }
     }
   };
+  // S^T = K Q^T for one tile: NH accumulators of 32 keys x 32 queries
+  auto qk = [&](int buf, f32x16 *s) {
+    const unsigned char *sk = smem + buf * BUF;
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      s[hf] = zero16();
+      const int row = hf * 32 + l32;
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const int kb = (c * 2 * KSQ + hl * KSQ) * (int)sizeof(TQ);
+        typename MQ::frag kf = load_frag<TQ>(reinterpret_cast<const TQ *>(sk + row * KROW + swz(row, kb, KCPR)));
+        s[hf] = MQ::mma(kf, qf[c], s[hf]);
+      }
+    }
+  };
 
   f32x16 acc[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc[i] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
+  // prologue: tiles 0 and 1 resident, tile 2 in flight, S of tile 0 computed
   gload(0);
   lstore(0);
+  if (ntiles > 1) {
+    gload(1);
+    lstore(1);
+  }
   __syncthreads();
+  if (ntiles > 2) gload(2);
+  f32x16 s_cur[NH], s_nxt[NH];
+  qk(0, s_cur);
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
-    const int k0 = kt * KB;
-    if (k0 <= wave_last) {
-      const unsigned char *sk = smem + cur * (KTILE + VTILE);
-      const unsigned char *sv = sk + KTILE;
-      // S^T for keys k0 .. k0+63 as two 32-key halves
-      f32x16 s[2];
+    // look ahead: the next tile's QK^T MFMAs overlap this tile's softmax
+    if (kt + 1 < wave_tiles) qk((kt + 1) % 3, s_nxt);
+    if (kt < wave_tiles) {
+      const int k0 = kt * KB;
+      const unsigned char *sv = smem + (kt % 3) * BUF + KTILE;
+      if (k0 + KB - 1 > p0) {                          // diagonal tile: causal mask
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        s[hf] = zero16();
-        const int row = hf * 32 + l32;
+        for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-        for (int c = 0; c < QC; ++c) {
-          const int kb = (c * 2 * KSQ + hl * KSQ) * (int)sizeof(TQ);
-          typename MQ::frag kf = load_frag<TQ>(reinterpret_cast<const TQ *>(sk + row * KROW + swz(row, kb, KCPR)));
-          s[hf] = MQ::mma(kf, qf[c], s[hf]);
-        }
-      }
-      // scale, causal mask, row max
-      const bool diag = k0 + KB - 1 > p0;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          float v = s[hf][a] * scale;
-          if (diag) {
+          for (int a = 0; a < 16; ++a) {
             const int key = k0 + hf * 32 + 8 * (a >> 2) + 4 * hl + (a & 3);
-            if (key > qpos) v = -INFINITY;
+            if (key > qpos) s_cur[hf][a] = -INFINITY;
           }
-          s[hf][a] = v;
-          mx = fmaxf(mx, v);
-        }
+      }
+      float mx = s_cur[0][0];
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s_cur[hf][a]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // rescale only when some row's running max grew (alpha = 1 otherwise)
+      if (__any(mx > m_run)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) acc[i][a] *= alpha;
+        m_run = m_new;
+      }
       float psum = 0.f;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const float p = __builtin_amdgcn_exp2f(s[hf][a] - m_new);
-          s[hf][a] = p;
-          psum += p;
-        }
-      psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < ND; ++i)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) acc[i][a] *= alpha;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+      for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
         for (int cc = 0; cc < PC; ++cc) {
           float pv[KSV];
 #pragma unroll
-          for (int sl = 0; sl < KSV; ++sl) pv[sl] = s[hf][KSV * cc + sl];
+          for (int sl = 0; sl < KSV; ++sl) pv[sl] = __builtin_amdgcn_exp2f(s_cur[hf][KSV * cc + sl] - m_run);
           const typename MV::frag pf = pack_frag<TV>(pv);
+          if constexpr (KSV == 8) {
+            // row sum of the rounded probabilities the P*V product uses
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+              const bf16x2 pair = {pf[2 * e], pf[2 * e + 1]};
+              const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+              psum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, psum, false);
+            }
+          } else {
+#pragma unroll
+            for (int sl = 0; sl < KSV; ++sl) psum += pv[sl];
+          }
           // first key of this lane's k-slots, in the permuted tile order
           const int a0 = KSV * cc;
           const int key_rel = 8 * (a0 >> 2) + 4 * hl + (a0 & 3);
@@ -220,9 +250,14 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const TQ *__restrict__ q,
             acc[i] = MV::mma(vf, pf, acc[i]);
           }
         }
+      psum += __shfl_xor(psum, 32, 64);
+      l_run += psum;
     }
-    if (kt + 1 < ntiles) lstore(cur ^ 1);
+    if (kt + 2 < ntiles) lstore((kt + 2) % 3);
     __syncthreads();
+    if (kt + 3 < ntiles) gload(kt + 3);
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) s_cur[hf] = s_nxt[hf];
   }
 
   if (qpos >= T) return;
@@ -251,38 +286,43 @@ static int gcd_int(int a, int b) {
 }
 
 template <typename TQ, typename TV, int D>
-static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
-                         const float *tau, TV *o, hipStream_t stream) {
+static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *vt, TV *o,
+                         hipStream_t stream) {
   const int hq = gcd_int(s.G, 4);
   const int nsub = s.G / hq;
   const int pos_per = 128 / hq;
   const int npb = (s.T + pos_per - 1) / pos_per;
   const int grid = npb * s.B * s.Hkv * nsub;
-  hipLaunchKernelGGL((attn_fwd_kernel<TQ, TV, D>), dim3(grid), dim3(256), 0, stream, q, k, vt, tau,
-                     o, s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb);
+  hipLaunchKernelGGL((attn_fwd_kernel<TQ, TV, D>), dim3(grid), dim3(256), 0, stream, q, k, vt, o,
+                     s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb);
   return hipGetLastError();
 }
 
 template <typename TQ, typename TV>
 hipError_t launch_attention_prefill(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
-                                    const float *tau, TV *o, hipStream_t stream) {
+                                    TV *o, hipStream_t stream) {
   switch (s.d) {
-    case 16: return attn_d<TQ, TV, 16>(s, q, k, vt, tau, o, stream);
-    case 32: return attn_d<TQ, TV, 32>(s, q, k, vt, tau, o, stream);
-    case 64: return attn_d<TQ, TV, 64>(s, q, k, vt, tau, o, stream);
-    case 128: return attn_d<TQ, TV, 128>(s, q, k, vt, tau, o, stream);
+    case 16: return attn_d<TQ, TV, 16>(s, q, k, vt, o, stream);
+    case 32: return attn_d<TQ, TV, 32>(s, q, k, vt, o, stream);
+    case 64: return attn_d<TQ, TV, 64>(s, q, k, vt, o, stream);
+    case 128:
+      if constexpr (AttnTile<TQ, TV, 128>::fits) return attn_d<TQ, TV, 128>(s, q, k, vt, o, stream);
+      break;
   }
   return hipErrorInvalidValue;
 }
 
+bool attention_supported(int d, bool f32) {
+  return d == 16 || d == 32 || d == 64 || (d == 128 && !f32);
+}
+
 template hipError_t launch_attention_prefill<f16, bf16>(const MixShape &, const f16 *, const f16 *,
-                                                        const bf16 *, const float *, bf16 *,
-                                                        hipStream_t);
+                                                        const bf16 *, bf16 *, hipStream_t);
 template hipError_t launch_attention_prefill<bf16, bf16>(const MixShape &, const bf16 *,
-                                                         const bf16 *, const bf16 *, const float *,
-                                                         bf16 *, hipStream_t);
+                                                         const bf16 *, const bf16 *, bf16 *,
+                                                         hipStream_t);
 template hipError_t launch_attention_prefill<float, float>(const MixShape &, const float *,
-                                                           const float *, const float *,
-                                                           const float *, float *, hipStream_t);
+                                                           const float *, const float *, float *,
+                                                           hipStream_t);
 
 }  // namespace cca

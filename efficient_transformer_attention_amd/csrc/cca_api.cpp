@@ -90,6 +90,7 @@ cca_status validate_shape(const cca_config *c, bool need_seq) {
   if (c->seq_conv_k < 1 || c->seq_conv_k > 4 || c->chan_conv_k < 1 || c->chan_conv_k > 4)
     return CCA_ERR_UNSUPPORTED;
   if (!convmix_fits(c->n_q_heads / c->n_kv_heads, d)) return CCA_ERR_UNSUPPORTED;
+  if (need_seq && !attention_supported(d, c->dtype == CCA_F32)) return CCA_ERR_UNSUPPORTED;
   // index arithmetic stays in 32-bit for per-row offsets
   const long long N = (long long)(c->n_q_heads + 2 * c->n_kv_heads) * d;
   if ((long long)c->batch * (need_seq ? padded_T(c->seq_len) : 1) * (N > c->d_model ? N : c->d_model) >
@@ -171,6 +172,7 @@ MixTaps taps_of(const cca_weights *w) {
   t.k_seq = w->k_seq_taps;
   t.q_chan = w->q_chan_taps;
   t.k_chan = w->k_chan_taps;
+  t.tau = w->tau;
   return t;
 }
 
@@ -235,17 +237,17 @@ cca_status run_attention(const cca_config &c, const cca_weights *w, void *ws, co
   if (c.dtype == CCA_F32) {
     e = launch_attention_prefill<float, float>(s, (const float *)wsp(ws, L, CCA_WS_Q),
                                                (const float *)wsp(ws, L, CCA_WS_K),
-                                               (const float *)wsp(ws, L, CCA_WS_VT), w->tau,
+                                               (const float *)wsp(ws, L, CCA_WS_VT),
                                                (float *)wsp(ws, L, CCA_WS_O), st);
   } else if (qk_is_f16(c)) {
     e = launch_attention_prefill<f16, bf16>(s, (const f16 *)wsp(ws, L, CCA_WS_Q),
                                             (const f16 *)wsp(ws, L, CCA_WS_K),
-                                            (const bf16 *)wsp(ws, L, CCA_WS_VT), w->tau,
+                                            (const bf16 *)wsp(ws, L, CCA_WS_VT),
                                             (bf16 *)wsp(ws, L, CCA_WS_O), st);
   } else {
     e = launch_attention_prefill<bf16, bf16>(s, (const bf16 *)wsp(ws, L, CCA_WS_Q),
                                              (const bf16 *)wsp(ws, L, CCA_WS_K),
-                                             (const bf16 *)wsp(ws, L, CCA_WS_VT), w->tau,
+                                             (const bf16 *)wsp(ws, L, CCA_WS_VT),
                                              (bf16 *)wsp(ws, L, CCA_WS_O), st);
   }
   return check_launch(e, st);

@@ -31,6 +31,7 @@ struct MixShape {
 
 struct MixTaps {
   const float *q_seq, *k_seq, *q_chan, *k_chan;
+  const float *tau;   // [H_q]; the prefill mixing stores tau_h * log2(e) * q_hat
 };
 
 // Optional prefill outputs that seed a decode: cache rows [0, T) and the
@@ -57,11 +58,12 @@ hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const floa
                                  const StateOut &in, const StateOut &out, float *q,
                                  hipStream_t stream);
 
-// Causal flash attention inside the latent heads.  tau [Hq] fp32.
-// o [B*T, Hq*d] in TV.
+// Causal flash attention inside the latent heads; q holds tau_h * log2(e) *
+// q_hat (the mixing kernel applies the temperature).  o [B*T, Hq*d] in TV.
 template <typename TQ, typename TV>
 hipError_t launch_attention_prefill(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
-                                    const float *tau, TV *o, hipStream_t stream);
+                                    TV *o, hipStream_t stream);
+bool attention_supported(int d, bool f32);
 
 // Split-KV decode attention over Lk = L + 1 cached keys, then the log-sum-exp
 // combine.  part: fp32 scratch of decode_partial_floats() floats.

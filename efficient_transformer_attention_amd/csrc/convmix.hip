@@ -203,7 +203,11 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
     if (!active) continue;
     if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
     if (slot < G) {
+      // the attention kernel takes q scaled by tau_h * log2(e) (exp2-domain logits)
       const int h = g * G + slot;
+      const float sc = w.tau[h] * 1.4426950408889634f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) y[c] *= sc;
       Store4<TQ>::st(q + ((size_t)(b * s.Hq + h) * s.Tp + tok) * D + 4 * li, y);
     } else {
       Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);

@@ -130,7 +130,8 @@ typedef struct {
 /* Host-only check of a configuration; needs no device.  Returns CCA_OK,
  * CCA_ERR_INVALID_ARG (null cfg, non-positive sizes, H_q % H_kv != 0, odd
  * H_kv with value-shift, E not a multiple of 8, bad eps/base) or
- * CCA_ERR_UNSUPPORTED (d outside {16,32,64,128}, taps outside 1..4, dtype). */
+ * CCA_ERR_UNSUPPORTED (d outside {16,32,64,128}, fp32 prefill with d = 128,
+ * taps outside 1..4, dtype, a kv group too wide for the mixing kernel). */
 cca_status cca_validate_config(const cca_config *cfg);
 
 /* Bytes of device workspace cca_prefill_forward needs for cfg (0 if cfg is
@@ -180,8 +181,9 @@ const char *cca_status_string(cca_status s);
  * Prefill workspace layout (offsets from cca_prefill_workspace_layout; Tp is
  * T rounded up to 128):
  *   CCA_WS_QKV  fp32 [B*T, e_q + 2*e_kv]   down-projection output
- *   CCA_WS_Q    [B, H_q, Tp, d]   normalised, rotated q; fp16 when
- *               cfg.dtype is bf16 and use_qk_norm is 1, else cfg.dtype
+ *   CCA_WS_Q    [B, H_q, Tp, d]   normalised, rotated q times tau_h*log2(e)
+ *               (logits in the exp2 domain); fp16 when cfg.dtype is bf16 and
+ *               use_qk_norm is 1, else cfg.dtype
  *   CCA_WS_K    [B, H_kv, Tp, d]  same type as CCA_WS_Q
  *   CCA_WS_VT   [B, H_kv, d, Tp]  value after shift, transposed, cfg.dtype;
  *               inside each group of 16 tokens, positions 4..7 and 8..11 are

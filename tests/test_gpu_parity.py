@@ -99,7 +99,8 @@ def test_prefill_stage_intermediates():
     assert rel_l2(qkv, ref_qkv) < 1e-6, "down-projection"
     q = T.to_f64(run.ws_view(L.WS_Q, run.qk_dtype(), (B, s.n_q_heads, Tp, d)))
     k = T.to_f64(run.ws_view(L.WS_K, run.qk_dtype(), (B, s.n_kv_heads, Tp, d)))
-    assert rel_l2(q[:, :, :Tn], lat["q"].transpose(0, 2, 1, 3)) < 1e-3, "mixed q"
+    scale = (P.weights.tau.astype(np.float64) * np.log2(np.e))[None, :, None, None]
+    assert rel_l2(q[:, :, :Tn] / scale, lat["q"].transpose(0, 2, 1, 3)) < 1e-3, "mixed q"
     assert rel_l2(k[:, :, :Tn], lat["k"].transpose(0, 2, 1, 3)) < 1e-3, "mixed k"
     assert np.all(q[:, :, Tn:] == 0) and np.all(k[:, :, Tn:] == 0), "padding rows"
     vt = vt_unpermute(T.to_f64(run.ws_view(L.WS_VT, torch.bfloat16, (B, s.n_kv_heads, d, Tp))))
