@@ -14,7 +14,8 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libcca.so")
+# CCA_LIBRARY may name another build of the same library (same ABI).
+LIB_PATH = os.environ.get("CCA_LIBRARY") or os.path.join(PKG, "libcca.so")
 
 CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_WORKSPACE, CCA_ERR_HIP = range(5)
 CCA_BF16, CCA_F32 = 0, 1

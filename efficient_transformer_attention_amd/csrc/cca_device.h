@@ -102,12 +102,17 @@ __device__ __forceinline__ u32x4 zero_u32x4() {
   return z;
 }
 
-// XOR swizzle of 16-byte chunks inside an LDS row: keeps the lanes of one
-// ds_read_b128 phase (rows r..r+7, same logical chunk) on distinct banks.
-// `row_chunks` is the number of 16-byte chunks per row (a power of two).
+// XOR swizzle of 16-byte chunks inside an LDS row, for lanes that read the
+// same logical chunk of consecutive rows.  With 128-byte rows the pattern
+// f(r) = (r & 7) ^ ((r >> 3) & 1) keeps every 8 consecutive rows on distinct
+// chunks (conflict-free for 32 banks, 8 lanes per phase) and every 16
+// consecutive rows on distinct (row parity, chunk) pairs (conflict-free for
+// 64 banks, 16 lanes per phase).  `row_chunks` is the number of 16-byte
+// chunks per row (a power of two).
 __device__ __forceinline__ int swz(int row, int byte_in_row, int row_chunks) {
-  int chunk = byte_in_row >> 4;
-  int phys = chunk ^ (row & (row_chunks - 1) & 7);
+  const int chunk = byte_in_row >> 4;
+  const int f = row_chunks >= 8 ? ((row & 7) ^ ((row >> 3) & 1)) : (row & (row_chunks - 1));
+  const int phys = chunk ^ f;
   return (phys << 4) | (byte_in_row & 15);
 }
 
