@@ -3,6 +3,7 @@
 // first launch; launches are asynchronous on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -69,6 +70,10 @@ MixShape mix_shape(const cca_config &c) {
   s.use_norm = c.use_qk_norm;
   s.rope_base = c.rope_base;
   s.eps = c.norm_eps;
+  for (int i = 0; i < 64; ++i)
+    s.theta[i] = (c.rope_base > 0.f && 2 * i < c.head_dim)
+                     ? std::pow((double)c.rope_base, -2.0 * (double)i / (double)c.head_dim)
+                     : 0.0;
   return s;
 }
 

@@ -116,6 +116,26 @@ __device__ __forceinline__ int swz(int row, int byte_in_row, int row_chunks) {
   return (phys << 4) | (byte_in_row & 15);
 }
 
+// ---------------------------------------------------------------------------
+// DPP lane exchanges inside rows of 16 lanes (no LDS traffic)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Value of the lane one below inside its row of 16 (0 for the row's lane 0).
+__device__ __forceinline__ float dpp_shr1(float v) { return dpp_f<0x111>(v); }
+// Sum over aligned groups of W lanes (W in 1, 2, 4, 8, 16), every lane gets it.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (W >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+  if constexpr (W >= 16) v += dpp_f<0x140>(v);  // row_mirror
+  if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
+
 // Bits 2 and 3 of a token index exchanged: the key order inside the
 // transposed value tile, so that the 8 keys one lane feeds to the P*V MFMA
 // (keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key chunk) are contiguous.

@@ -27,6 +27,9 @@ struct MixShape {
   int ks, kc;              // conv taps (1..4)
   int use_mean, use_shift, use_norm;
   float rope_base, eps;
+  // RoPE frequencies base^(-2i/d), i < d/2, evaluated on the host in double
+  // precision (all zero when RoPE is off); passed by value with the launch.
+  double theta[64];
 };
 
 struct MixTaps {

@@ -33,20 +33,21 @@ namespace cca {
 
 static constexpr int HALO = 3;   // k_s - 1 for the largest supported k_s = 4
 
-// fp64-accurate rotation of pair i at position pos.
-__device__ __forceinline__ float2 rope_cs(int pos, int i, int d, float base) {
+// fp64-accurate rotation by angle pos * theta (theta from rope_theta).
+__device__ __forceinline__ float2 rope_cs_theta(int pos, double theta, float base) {
   if (base == 0.f) return make_float2(1.f, 0.f);
-  const double theta = pow((double)base, -2.0 * (double)i / (double)d);
   const double phi = (double)pos * theta;
   const double TWO_PI_HI = 6.283185307179586;        // nearest double to 2*pi
   const double TWO_PI_LO = 2.4492935982947064e-16;   // 2*pi - TWO_PI_HI
   const double n = rint(phi * (1.0 / TWO_PI_HI));
   double r = fma(-n, TWO_PI_HI, phi);
   r = fma(-n, TWO_PI_LO, r);
-  float sn, cs;
-  sincosf((float)r, &sn, &cs);
-  return make_float2(cs, sn);
+  // |r| <= pi after the double-precision reduction: the hardware sin/cos
+  // (v_sin_f32 / v_cos_f32) are accurate to a few ulp there
+  const float rf = (float)r;
+  return make_float2(__cosf(rf), __sinf(rf));
 }
+
 
 template <typename T> struct Store4;
 template <> struct Store4<float> {
@@ -71,23 +72,37 @@ template <> struct Store4<bf16> {
 // token), columns [q heads | k head | v head] of the group, CW floats wide.
 template <int D>
 __device__ __forceinline__ void mix_unit(const float *tile, int CW, int r, int slot, int G,
-                                         int li, const float *staps, const float *ctaps,
+                                         int li, const float (&st)[4][4], const float (&ct)[4],
                                          const MixShape &s, float2 cs0, float2 cs1, float y[4]) {
   constexpr int LPU = D / 4;
   const int col = slot * D + 4 * li;
   float a[4];
+  {
+    f32x4 row[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float acc = 0.f;
+    for (int j = 0; j < 4; ++j) row[j] = *reinterpret_cast<const f32x4 *>(tile + (r + HALO - j) * CW + col);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = fmaf(staps[(col + c) * 4 + j], tile[(r + HALO - j) * CW + col + c], acc);
-    a[c] = acc;
+    for (int c = 0; c < 4; ++c) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = fmaf(st[c][j], row[j][c], acc);
+      a[c] = acc;
+    }
   }
-  // values of the three channels below this lane's first one (previous lane)
-  float p1 = __shfl_up(a[1], 1, LPU), p2 = __shfl_up(a[2], 1, LPU), p3 = __shfl_up(a[3], 1, LPU);
+  // values of the three channels below this lane's first one (previous lane;
+  // zero for the head's first lane)
+  float p1, p2, p3;
+  if constexpr (LPU <= 16) {
+    p1 = dpp_shr1(a[1]);
+    p2 = dpp_shr1(a[2]);
+    p3 = dpp_shr1(a[3]);
+  } else {
+    p1 = __shfl_up(a[1], 1, LPU);
+    p2 = __shfl_up(a[2], 1, LPU);
+    p3 = __shfl_up(a[3], 1, LPU);
+  }
   if (li == 0) p1 = p2 = p3 = 0.f;
-  const float w0 = ctaps[slot * 4 + 0], w1 = ctaps[slot * 4 + 1], w2 = ctaps[slot * 4 + 2],
-              w3 = ctaps[slot * 4 + 3];
+  const float w0 = ct[0], w1 = ct[1], w2 = ct[2], w3 = ct[3];
   float b[4];
   b[0] = w0 * a[0] + w1 * p3 + w2 * p2 + w3 * p1;
   b[1] = w0 * a[1] + w1 * a[0] + w2 * p3 + w3 * p2;
@@ -95,25 +110,24 @@ __device__ __forceinline__ void mix_unit(const float *tile, int CW, int r, int s
   b[3] = w0 * a[3] + w1 * a[2] + w2 * a[1] + w3 * a[0];
 
   if (s.use_mean) {
-    const float *cur = tile + (r + HALO) * CW;
+    const float *cur = tile + (r + HALO) * CW + 4 * li;
+    const f32x4 kpre = *reinterpret_cast<const f32x4 *>(cur + G * D);
     if (slot < G) {
+      const f32x4 qpre = *reinterpret_cast<const f32x4 *>(cur + slot * D);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) b[c] += 0.5f * (cur[col + c] + cur[G * D + 4 * li + c]);
+      for (int c = 0; c < 4; ++c) b[c] += 0.5f * (qpre[c] + kpre[c]);
     } else {
+      f32x4 m = *reinterpret_cast<const f32x4 *>(cur);
+      for (int h = 1; h < G; ++h) m += *reinterpret_cast<const f32x4 *>(cur + h * D);
       const float invg = 1.f / (float)G;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float m = 0.f;
-        for (int h = 0; h < G; ++h) m += cur[h * D + 4 * li + c];
-        b[c] += 0.5f * (cur[G * D + 4 * li + c] + m * invg);
-      }
+      for (int c = 0; c < 4; ++c) b[c] += 0.5f * (kpre[c] + m[c] * invg);
     }
   }
   if (s.use_norm) {
-    float ss = b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
-#pragma unroll
-    for (int o = LPU / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    const float inv = 1.f / fmaxf(sqrtf(ss), s.eps);
+    // 1 / max(||b||, eps) == rsqrt(max(||b||^2, eps^2))
+    const float ss = group_sum<LPU>(b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3]);
+    const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, s.eps * s.eps));
 #pragma unroll
     for (int c = 0; c < 4; ++c) b[c] *= inv;
   }
@@ -142,6 +156,23 @@ __device__ __forceinline__ void load_taps(const MixShape &s, const MixTaps &w, i
   }
 }
 
+// This lane's taps for head slot `slot` (channels 4*li .. 4*li+3) from the
+// LDS copies made by load_taps.
+template <int D>
+__device__ __forceinline__ void lane_taps(const float *staps, const float *ctaps, int slot, int li,
+                                          float (&st)[4][4], float (&ct)[4]) {
+  const int col = slot * D + 4 * li;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const f32x4 t = *reinterpret_cast<const f32x4 *>(staps + (col + c) * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st[c][j] = t[j];
+  }
+  const f32x4 t = *reinterpret_cast<const f32x4 *>(ctaps + slot * 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ct[j] = t[j];
+}
+
 // Map a column of the group tile to its column in the qkv row.
 __device__ __forceinline__ int group_col(int col, int g, int G, int D, int eq, int ekv) {
   if (col < G * D) return g * G * D + col;
@@ -149,118 +180,174 @@ __device__ __forceinline__ int group_col(int col, int g, int G, int D, int eq, i
   return eq + ekv + g * D + (col - (G + 1) * D);
 }
 
+// Rows of the next chunk each thread prefetches into registers (16 bytes each).
+static constexpr int MIX_PF = 8;
+
 template <typename TQ, typename TV, int D>
 __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTaps w,
                                                               const float *__restrict__ qkv,
                                                               TQ *__restrict__ q, TQ *__restrict__ k,
                                                               TV *__restrict__ vt, StateOut st,
-                                                              int TC, int nchunks) {
+                                                              int TC, int nchunks, int cpw,
+                                                              int nseg) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int G = s.G, CW = (G + 2) * D;
-  float *tile = lds;
+  float *tile = lds;                                   // rows: tokens t0-HALO .. t0+TC-1
   float *staps = tile + (TC + HALO) * CW;
   float *ctaps = staps + (G + 1) * D * 4;
   float2 *rot = reinterpret_cast<float2 *>(ctaps + ((G + 1) * 4 + 3) / 4 * 4);
 
   const int tid = threadIdx.x;
-  const int chunk = blockIdx.x % nchunks;
-  const int bg = blockIdx.x / nchunks;
+  const int seg = blockIdx.x % nseg;
+  const int bg = blockIdx.x / nseg;
   const int g = bg % s.Hkv, b = bg / s.Hkv;
-  const int t0 = chunk * TC;
+  const int c_beg = seg * cpw, c_end = min(nchunks, c_beg + cpw);
   const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
+  const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
+  const int vcol = (G + 1) * D;
 
-  // 1. pre-conv tile, tokens t0-HALO .. t0+TC-1 (zeros outside [0, T))
+  // each thread owns one 16-byte column chunk of the group and walks rows
+  // with a fixed stride (CW/4 <= 256 chunks per row)
   const int cpr = CW / 4;
-  for (int c = tid; c < (TC + HALO) * cpr; c += 256) {
-    const int r = c / cpr, col = (c % cpr) * 4;
-    const int tok = t0 - HALO + r;
+  const int rstep = 256 / cpr;
+  const int my_col = (tid % cpr) * 4, my_row0 = tid / cpr;
+  const bool col_active = my_row0 < rstep;
+  const float *src_col = qkv + group_col(my_col, g, G, D, eq, ekv) + (size_t)b * s.T * N;
+  auto row_load = [&](int tok) {
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (tok >= 0 && tok < s.T)
-      v = *reinterpret_cast<const f32x4 *>(qkv + (size_t)(b * s.T + tok) * N +
-                                           group_col(col, g, G, D, eq, ekv));
-    *reinterpret_cast<f32x4 *>(tile + r * CW + col) = v;
-  }
-  // 2. taps, 3. rotation table of the chunk
-  load_taps<D>(s, w, g, staps, ctaps);
-  for (int e = tid; e < TC * (D / 2); e += 256)
-    rot[e] = rope_cs(t0 + e / (D / 2), e % (D / 2), D, s.rope_base);
-  __syncthreads();
+    if (tok >= 0 && tok < s.T) v = *reinterpret_cast<const f32x4 *>(src_col + (size_t)tok * N);
+    return v;
+  };
 
-  // 4. query and key heads
+  load_taps<D>(s, w, g, staps, ctaps);
+
+  // first chunk: halo and rows straight into LDS
+  {
+    const int t0 = c_beg * TC;
+    for (int r0 = my_row0; r0 < TC + HALO; r0 += rstep * MIX_PF) {
+      f32x4 v[MIX_PF];
+#pragma unroll
+      for (int u = 0; u < MIX_PF; ++u) {
+        const int r = r0 + rstep * u;
+        v[u] = (col_active && r < TC + HALO) ? row_load(t0 - HALO + r) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < MIX_PF; ++u) {
+        const int r = r0 + rstep * u;
+        if (col_active && r < TC + HALO) *reinterpret_cast<f32x4 *>(tile + r * CW + my_col) = v[u];
+      }
+    }
+  }
+
   constexpr int LPU = D / 4;
   const int upp = 256 / LPU;
   const int li = tid % LPU, ui = tid / LPU;
-  const int nunits = TC * (G + 1);
-  for (int u0 = 0; u0 < nunits; u0 += upp) {
-    const int u = u0 + ui;
-    const bool active = u < nunits;          // whole lane groups are inactive together
-    const int r = active ? u / (G + 1) : 0;
-    const int slot = active ? u % (G + 1) : 0;
-    const int tok = t0 + r;
-    float y[4];
-    mix_unit<D>(tile, CW, r, slot, G, li, staps, ctaps, s, rot[r * (D / 2) + 2 * li],
-                rot[r * (D / 2) + 2 * li + 1], y);
-    if (!active) continue;
-    if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
-    if (slot < G) {
-      // the attention kernel takes q scaled by tau_h * log2(e) (exp2-domain logits)
-      const int h = g * G + slot;
-      const float sc = w.tau[h] * 1.4426950408889634f;
+  f32x4 pf[MIX_PF];
+
+  for (int ch = c_beg; ch < c_end; ++ch) {
+    const int t0 = ch * TC;
+    // rotation table of the chunk: one double multiply and reduction per entry
+    for (int e = tid; e < TC * (D / 2); e += 256)
+      rot[e] = rope_cs_theta(t0 + e / (D / 2), s.theta[e % (D / 2)], s.rope_base);
+    __syncthreads();
+
+    // prefetch the next chunk's rows; their latency overlaps this chunk's math
+    const bool more = ch + 1 < c_end;
+    if (more) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) y[c] *= sc;
-      Store4<TQ>::st(q + ((size_t)(b * s.Hq + h) * s.Tp + tok) * D + 4 * li, y);
-    } else {
-      Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
-      if (st.k_cache && tok < s.T)
-        Store4<TV>::st(reinterpret_cast<TV *>(st.k_cache) +
-                           ((size_t)(b * s.Hkv + g) * st.capacity + tok) * D + 4 * li, y);
+      for (int u = 0; u < MIX_PF; ++u) {
+        const int r = my_row0 + rstep * u;
+        pf[u] = (col_active && r < TC) ? row_load(t0 + TC + r) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+
+    // query and key heads, slot-major so each lane keeps its head's taps in
+    // registers: slot 0..G-1 are the query heads, slot G the key head
+    for (int slot = 0; slot <= G; ++slot) {
+      float stp[4][4], ctp[4];
+      lane_taps<D>(staps, ctaps, slot, li, stp, ctp);
+      const float qscale = slot < G ? w.tau[g * G + slot] * 1.4426950408889634f : 1.f;
+      for (int r = ui; r < TC; r += upp) {
+        const int tok = t0 + r;
+        float y[4];
+        mix_unit<D>(tile, CW, r, slot, G, li, stp, ctp, s, rot[r * (D / 2) + 2 * li],
+                    rot[r * (D / 2) + 2 * li + 1], y);
+        if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
+        if (slot < G) {
+          // the attention kernel takes q scaled by tau_h * log2(e) (exp2-domain logits)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[c] *= qscale;
+          Store4<TQ>::st(q + ((size_t)(b * s.Hq + g * G + slot) * s.Tp + tok) * D + 4 * li, y);
+        } else {
+          Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
+          if (st.k_cache && tok < s.T)
+            Store4<TV>::st(reinterpret_cast<TV *>(st.k_cache) +
+                               ((size_t)(b * s.Hkv + g) * st.capacity + tok) * D + 4 * li, y);
+        }
+      }
+    }
+
+    // value head, transposed: vt[b, g, dd, perm(t)] for the chunk's tokens
+    for (int e = tid; e < D * (TC / 8); e += 256) {
+      const int dd = e / (TC / 8), grp = e % (TC / 8);
+      float vals[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int tl = vt_perm(8 * grp + jj);
+        vals[jj] = (t0 + tl < s.T) ? tile[(tl + HALO - shifted) * CW + vcol + dd] : 0.f;
+      }
+      TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + dd) * s.Tp + t0 + 8 * grp;
+      Store4<TV>::st(dst, vals);
+      Store4<TV>::st(dst + 4, vals + 4);
+    }
+    if (st.v_cache) {
+      for (int e = tid; e < TC * (D / 4); e += 256) {
+        const int r = e / (D / 4), c4 = e % (D / 4), tok = t0 + r;
+        if (tok >= s.T) continue;
+        const float *src = tile + (r + HALO - shifted) * CW + vcol + 4 * c4;
+        Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) +
+                           ((size_t)(b * s.Hkv + g) * st.capacity + tok) * D + 4 * c4, src);
+      }
+    }
+    __syncthreads();                                 // every read of this tile is done
+
+    if (more) {
+      // carry the halo (last HALO rows) to the top, then the prefetched rows
+      for (int e = tid; e < HALO * CW / 4; e += 256) {
+        const int r = e / (CW / 4), c4 = (e % (CW / 4)) * 4;
+        *reinterpret_cast<f32x4 *>(tile + r * CW + c4) =
+            *reinterpret_cast<const f32x4 *>(tile + (TC + r) * CW + c4);
+      }
+      __syncthreads();                               // halo rows read before they are overwritten
+#pragma unroll
+      for (int u = 0; u < MIX_PF; ++u) {
+        const int r = my_row0 + rstep * u;
+        if (col_active && r < TC) *reinterpret_cast<f32x4 *>(tile + (HALO + r) * CW + my_col) = pf[u];
+      }
+      // the rotation table is rewritten after the next barrier-protected use
     }
   }
 
-  // 5. value head, transposed: vt[b, g, dd, perm(t)] for the chunk's tokens
-  const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
-  const int vcol = (G + 1) * D;
-  for (int e = tid; e < D * (TC / 8); e += 256) {
-    const int dd = e / (TC / 8), grp = e % (TC / 8);
-    float vals[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int tl = vt_perm(8 * grp + jj);
-      vals[jj] = (t0 + tl < s.T) ? tile[(tl + HALO - shifted) * CW + vcol + dd] : 0.f;
-    }
-    TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + dd) * s.Tp + t0 + 8 * grp;
-    Store4<TV>::st(dst, vals);
-    Store4<TV>::st(dst + 4, vals + 4);
-  }
-
-  // 6. optional decode state: V cache rows, conv window, value-shift state
-  if (st.v_cache) {
-    for (int e = tid; e < TC * (D / 4); e += 256) {
-      const int r = e / (D / 4), c4 = e % (D / 4), tok = t0 + r;
-      if (tok >= s.T) continue;
-      const float *src = tile + (r + HALO - shifted) * CW + vcol + 4 * c4;
-      Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) +
-                         ((size_t)(b * s.Hkv + g) * st.capacity + tok) * D + 4 * c4, src);
-    }
-  }
-  if (chunk == 0) {
+  // decode state after the last token: conv window and value-shift state
+  if (seg == 0) {
     const int ks1 = s.ks - 1;
+    const float *qb = qkv + (size_t)b * s.T * N;
     if (st.conv_q)
       for (int e = tid; e < ks1 * G * D; e += 256) {
         const int sl = e / (G * D), c = e % (G * D), tok = s.T - ks1 + sl;
-        const float v = tok >= 0 ? qkv[(size_t)(b * s.T + tok) * N + g * G * D + c] : 0.f;
+        const float v = tok >= 0 ? qb[(size_t)tok * N + g * G * D + c] : 0.f;
         reinterpret_cast<TV *>(st.conv_q)[(size_t)(b * ks1 + sl) * eq + g * G * D + c] = from_f32<TV>(v);
       }
     if (st.conv_k)
       for (int e = tid; e < ks1 * D; e += 256) {
         const int sl = e / D, c = e % D, tok = s.T - ks1 + sl;
-        const float v = tok >= 0 ? qkv[(size_t)(b * s.T + tok) * N + eq + g * D + c] : 0.f;
+        const float v = tok >= 0 ? qb[(size_t)tok * N + eq + g * D + c] : 0.f;
         reinterpret_cast<TV *>(st.conv_k)[(size_t)(b * ks1 + sl) * ekv + g * D + c] = from_f32<TV>(v);
       }
     if (st.vshift && shifted)
       for (int c = tid; c < D; c += 256)
         reinterpret_cast<TV *>(st.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
-            from_f32<TV>(qkv[(size_t)(b * s.T + s.T - 1) * N + eq + ekv + g * D + c]);
+            from_f32<TV>(qb[(size_t)(s.T - 1) * N + eq + ekv + g * D + c]);
   }
 }
 
@@ -289,23 +376,34 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
   const TV *ck = reinterpret_cast<const TV *>(in.conv_k);
   const TV *vs = reinterpret_cast<const TV *>(in.vshift);
 
-  for (int e = tid; e < 4 * CW; e += 256) {
-    const int r = e / CW, col = e % CW;
-    float v = 0.f;
-    if (r == 3) {
-      v = qkv[(size_t)b * N + group_col(col, g, G, D, eq, ekv)];
-    } else if (r >= 4 - s.ks) {
-      const int sl = r - (4 - s.ks);             // window slot of token L-3+r
-      if (col < G * D) v = to_f32(cq[(size_t)(b * ks1 + sl) * eq + g * G * D + col]);
-      else if (col < (G + 1) * D) v = to_f32(ck[(size_t)(b * ks1 + sl) * ekv + g * D + col - G * D]);
-      else if (r == 2 && shifted) v = to_f32(vs[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + col - (G + 1) * D]);
-    } else if (r == 2 && shifted && col >= (G + 1) * D) {
-      v = to_f32(vs[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + col - (G + 1) * D]);
+  // all loads of the 4-row tile are issued before their LDS stores
+  constexpr int LB = 8;
+  for (int e0 = 0; e0 < 4 * CW; e0 += 256 * LB) {
+    float v[LB];
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int e = e0 + tid + 256 * u;
+      const int r = e / CW, col = e % CW;
+      v[u] = 0.f;
+      if (e >= 4 * CW) continue;
+      if (r == 3) {
+        v[u] = qkv[(size_t)b * N + group_col(col, g, G, D, eq, ekv)];
+      } else if (r >= 4 - s.ks && col < (G + 1) * D) {
+        const int sl = r - (4 - s.ks);           // window slot of token L-3+r
+        v[u] = col < G * D ? to_f32(cq[(size_t)(b * ks1 + sl) * eq + g * G * D + col])
+                           : to_f32(ck[(size_t)(b * ks1 + sl) * ekv + g * D + col - G * D]);
+      } else if (r == 2 && shifted && col >= (G + 1) * D) {
+        v[u] = to_f32(vs[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + col - (G + 1) * D]);
+      }
     }
-    tile[e] = v;
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int e = e0 + tid + 256 * u;
+      if (e < 4 * CW) tile[e] = v[u];
+    }
   }
   load_taps<D>(s, w, g, staps, ctaps);
-  for (int e = tid; e < D / 2; e += 256) rot[e] = rope_cs(L, e, D, s.rope_base);
+  for (int e = tid; e < D / 2; e += 256) rot[e] = rope_cs_theta(L, s.theta[e], s.rope_base);
   __syncthreads();
 
   constexpr int LPU = D / 4;
@@ -316,8 +414,10 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
   for (int u0 = 0; u0 < G + 1; u0 += upp) {
     const int slot = u0 + ui;
     const bool active = slot < G + 1;
+    float stp[4][4], ctp[4];
+    lane_taps<D>(staps, ctaps, active ? slot : 0, li, stp, ctp);
     float y[4];
-    mix_unit<D>(tile, CW, 0, active ? slot : 0, G, li, staps, ctaps, s, rot[2 * li], rot[2 * li + 1], y);
+    mix_unit<D>(tile, CW, 0, active ? slot : 0, G, li, stp, ctp, s, rot[2 * li], rot[2 * li + 1], y);
     if (!active) continue;
     if (slot < G) {
       Store4<float>::st(qout + (size_t)(b * s.Hq + g * G + slot) * D + 4 * li, y);
@@ -352,19 +452,33 @@ static size_t mix_lds_bytes(int rows, int G, int D, int TC) {
   return f * 4 + (size_t)TC * (D / 2) * 8;
 }
 
-// Tokens per prefill workgroup: 32, or 16 when the group's tile would not fit.
+// Tokens per chunk: 32 when the tile fits in LDS, else 16.
 static int mix_chunk(int G, int D) { return mix_lds_bytes(32 + HALO, G, D, 32) <= 65536 ? 32 : 16; }
 
-bool convmix_fits(int G, int d) { return mix_lds_bytes(16 + HALO, G, d, 16) <= 65536; }
+// Whether a thread's share of one chunk's rows fits the prefetch registers;
+// otherwise each workgroup handles a single chunk and nothing is prefetched.
+static bool mix_prefetch_fits(int G, int D, int TC) {
+  const int cpr = (G + 2) * D / 4, rstep = 256 / cpr;
+  return (TC + rstep - 1) / rstep <= MIX_PF;
+}
+
+bool convmix_fits(int G, int d) {
+  return (G + 2) * d / 4 <= 256 && mix_lds_bytes(16 + HALO, G, d, 16) <= 65536;
+}
 
 template <typename TQ, typename TV, int D>
 static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
                                     TQ *k, TV *vt, const StateOut &st, hipStream_t stream) {
   const int TC = mix_chunk(s.G, D);
   const int nchunks = s.Tp / TC;
+  // about 4 chunks per workgroup, at least ~1024 workgroups when the work allows
+  const int streams = s.B * s.Hkv;
+  int cpw = (nchunks / 4 > 0 && mix_prefetch_fits(s.G, D, TC)) ? 4 : 1;
+  while (cpw > 1 && (long long)streams * ((nchunks + cpw - 1) / cpw) < 1024) --cpw;
+  const int nseg = (nchunks + cpw - 1) / cpw;
   const size_t lds = mix_lds_bytes(TC + HALO, s.G, D, TC);
-  hipLaunchKernelGGL((convmix_prefill_kernel<TQ, TV, D>), dim3(s.B * s.Hkv * nchunks), dim3(256),
-                     lds, stream, s, w, qkv, q, k, vt, st, TC, nchunks);
+  hipLaunchKernelGGL((convmix_prefill_kernel<TQ, TV, D>), dim3(streams * nseg), dim3(256), lds,
+                     stream, s, w, qkv, q, k, vt, st, TC, nchunks, cpw, nseg);
   return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
   const int m0 = (lid / ntn) * BM;
   const int n0 = (lid % ntn) * BN;
 
+  // prefetched global data of the next K tile
   u32x4 ra[A_CH], rb[B_CH];
 
   auto gload = [&](int k0) {
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
 
+  constexpr int KK = BK / (2 * KS);               // MFMA steps per K tile
   const int kbeg = blockIdx.y * kchunk;
   const int nk = (min(K, kbeg + kchunk) - kbeg + BK - 1) / BK;
   C += (size_t)blockIdx.y * M * ldc;
@@ -100,28 +102,38 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
   lstore(0);
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / (2 * KS); ++kk) {
+  // one K tile: the fragments of MFMA step kk+1 are read from LDS while the
+  // MFMAs of step kk run (two fragment sets)
+  auto ktile = [&](int cur) {
+    typename MF::frag fa[2][TM], fb[2][TN];
+    auto fread = [&](int kk, int set) {
       const int kb = (kk * 2 * KS + hl * KS) * (int)sizeof(Tin);   // byte offset in row
-      typename MF::frag fa[TM], fb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         int row = wm * WM + i * 32 + l32;
-        fa[i] = load_frag<Tin>(reinterpret_cast<const Tin *>(sA(cur) + row * ROWB + swz(row, kb, CPR)));
+        fa[set][i] = load_frag<Tin>(reinterpret_cast<const Tin *>(sA(cur) + row * ROWB + swz(row, kb, CPR)));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         int row = wn * WN + j * 32 + l32;
-        fb[j] = load_frag<Tin>(reinterpret_cast<const Tin *>(sB(cur) + row * ROWB + swz(row, kb, CPR)));
+        fb[set][j] = load_frag<Tin>(reinterpret_cast<const Tin *>(sB(cur) + row * ROWB + swz(row, kb, CPR)));
       }
+    };
+    fread(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) fread(kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[kk & 1][i], fb[kk & 1][j], acc[i][j]);
     }
+  };
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
+    ktile(cur);
     if (kt + 1 < nk) lstore(cur ^ 1);
     __syncthreads();
   }
