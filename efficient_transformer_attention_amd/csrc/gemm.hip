@@ -153,6 +153,154 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: the same product with the A and B tiles streamed straight from
+// HBM into LDS (buffer_load ... lds, no register staging) through a 4-stage
+// ring, so three K tiles are in flight while one is multiplied.
+//   K tile = 32 elements: LDS rows of 64 bytes (4 chunks of 16 bytes), chunk
+//   swizzle f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1) (no bank conflicts for 8-
+//   or 16-lane phases).  A DMA instruction fills 1 KiB = 16 rows; lane l
+//   writes LDS bytes [16 l, 16 l + 16) of it, so each lane fetches the global
+//   chunk that the swizzle places there.  Out-of-range rows / columns read as
+//   zero (buffer range check), which also covers a ragged K tail.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);   // vmcnt(N), expcnt and lgkmcnt unconstrained
+}
+
+template <typename Tout, int BM, int BN, int STAGES>
+__global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restrict__ A,
+                                                             const bf16 *__restrict__ Bm,
+                                                             Tout *__restrict__ C, int M, int N,
+                                                             int K, int lda, int ldb, int ldc) {
+  typedef Mfma32<bf16> MF;
+  constexpr int BK = 32, ROWB = 64;
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int A_INS = BM * ROWB / 1024, B_INS = BN * ROWB / 1024;   // DMA instructions per stage
+  constexpr int PER_WAVE = (A_INS + B_INS) / 4;
+  static_assert((A_INS + B_INS) % 4 == 0, "DMA split over 4 waves");
+  static_assert(2 * PER_WAVE < 16, "vmcnt field");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
+  const int lid = xcd_remap(blockIdx.x, ntn * ntm);
+  const int m0 = (lid / ntn) * BM, n0 = (lid % ntn) * BN;
+
+  const unsigned a_bytes = (unsigned)((size_t)M * lda * 2), b_bytes = (unsigned)((size_t)N * ldb * 2);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bm, 0, b_bytes, 0x00020000);
+
+  // per DMA slot of this lane: byte offset of K tile 0 (or an out-of-range
+  // offset for rows past M / N) and the element index of its chunk in a tile
+  unsigned doff[PER_WAVE];
+  int dk[PER_WAVE];
+  bool dvalid[PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int ins = wave * PER_WAVE + u;
+    const bool isA = ins < A_INS;
+    const int row = (isA ? ins : ins - A_INS) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz4(row);
+    const int grow = (isA ? m0 : n0) + row;
+    dvalid[u] = grow < (isA ? M : N);
+    dk[u] = chunk * 8;
+    doff[u] = dvalid[u] ? (unsigned)(((size_t)grow * (isA ? lda : ldb) + chunk * 8) * 2) : 0u;
+  }
+  const bool k_ragged = (K % BK) != 0;
+  auto issue = [&](int kt, int slot) {
+    unsigned char *base = smem + slot * STAGE;
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int ins = wave * PER_WAVE + u;
+      const bool isA = ins < A_INS;                   // wave-uniform
+      bool ok = dvalid[u];
+      if (k_ragged) ok = ok && (kt * BK + dk[u] < K);
+      const unsigned off = ok ? doff[u] + (unsigned)(kt * BK * 2) : (isA ? a_bytes : b_bytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, base + ins * 1024, 16, off, 0, 0, 0);
+    }
+  };
+
+  // per-lane LDS byte offsets of the MFMA fragments inside one stage
+  int aoff[2][TM], boff[2][TN];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int chunk = 2 * kk + hl;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WM + i * 32 + l32;
+      aoff[kk][i] = row * ROWB + ((chunk ^ swz4(row)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int row = wn * WN + j * 32 + l32;
+      boff[kk][j] = BM * ROWB + row * ROWB + ((chunk ^ swz4(row)) << 4);
+    }
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
+
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s0 = 0; s0 < STAGES - 1; ++s0)
+    if (s0 < nk) issue(s0, s0);
+
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt has landed once at most the tiles issued after it are in flight
+    const int after = min(STAGES - 2, nk - 1 - kt);
+    if (after >= 2) wait_vmcnt<2 * PER_WAVE>();
+    else if (after == 1) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
+    // every wave's DMA of tile kt has landed (each waited for its own above)
+    // and every read of the ring slot reused below is done; a plain s_barrier,
+    // since a fence here would also wait for the tiles still in flight
+    asm volatile("s_barrier" ::: "memory");
+    const int nslot = slot == 0 ? STAGES - 1 : slot - 1;   // (kt + STAGES - 1) % STAGES
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, nslot);
+    const unsigned char *sbase = smem + slot * STAGE;
+    MF::frag fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[kk][i] = *reinterpret_cast<const MF::frag *>(sbase + aoff[kk][i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[kk][j] = *reinterpret_cast<const MF::frag *>(sbase + boff[kk][j]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[kk][i], fb[kk][j], acc[i][j]);
+    slot = slot + 1 == STAGES ? 0 : slot + 1;
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int gn = n0 + wn * WN + j * 32 + l32;
+      if (gn >= N) continue;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int gm = m0 + wm * WM + i * 32 + 8 * (a >> 2) + 4 * hl + (a & 3);
+        if (gm < M) C[(size_t)gm * ldc + gn] = from_f32<Tout>(acc[i][j][a]);
+      }
+    }
+}
+
 // out[i] = sum over the S slices of part[s][i], i < n (n a multiple of 4)
 template <typename Tout>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part,
@@ -202,6 +350,28 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
   }
   constexpr int BM = 128, BN = 128;
   int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if constexpr (sizeof(Tin) == 2) {
+    // operands below 4 GiB so the buffer range check covers them
+    if ((size_t)M * lda * 2 < (1ull << 32) && (size_t)N * ldb * 2 < (1ull << 32)) {
+      // N tile of 128 or 192, whichever finishes sooner counted in rounds of
+      // resident workgroups (2 per CU, 256 CUs), a tile's time being
+      // proportional to its width
+      const long long slots = 512;
+      auto cost = [&](int bn) {
+        const long long t = (long long)((M + 127) / 128) * ((N + bn - 1) / bn);
+        return ((t + slots - 1) / slots) * bn;
+      };
+      if (cost(192) < cost(128)) {
+        const int g192 = ((M + 127) / 128) * ((N + 191) / 192);
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 192, 3>), dim3(g192), dim3(256), 0, stream,
+                           A, B, C, M, N, K, lda, ldb, ldc);
+      } else {
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 128, 4>), dim3(grid), dim3(256), 0, stream,
+                           A, B, C, M, N, K, lda, ldb, ldc);
+      }
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_nt_kernel<Tin, Tout, BM, BN>), dim3(grid, 1), dim3(256), 0, stream, A,
                      B, C, M, N, K, lda, ldb, ldc, K);
   return hipGetLastError();
