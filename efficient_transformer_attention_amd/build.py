@@ -51,6 +51,13 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
+    # a kernel whose host launch stub was not emitted leaves an undefined
+    # __device_stub__ reference that only shows up when the library is loaded
+    for obj in objs:
+        r = subprocess.run(["nm", "-u", obj], capture_output=True, text=True)
+        missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+        if missing:
+            raise RuntimeError(f"{obj}: kernel launch stubs not emitted: {missing[:3]}")
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

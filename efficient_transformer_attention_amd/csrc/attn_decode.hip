@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   typedef float RedRow[D + 2];
   RedRow *red = reinterpret_cast<RedRow *>(smem);   // [wave * MAXG + column]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hl = lane >> 5;
   int id = blockIdx.x;
   const int c = id % nch; id /= nch;

@@ -23,35 +23,51 @@
 //    mixing kernel) so one lane's 8 keys are contiguous.
 //  * The mixing kernel stores q already scaled by tau_h * log2(e), so the
 //    scores come out of the MFMA in the exp2 domain (native v_exp_f32).
-//  * Three K/V^T buffers: while a wave runs the softmax and P*V of tile j it
-//    has already issued the QK^T MFMAs of tile j+1, and tile j+2 is being
-//    written; one barrier per tile.
-//  * The online-softmax rescale of O runs only when some row's running max
-//    grew (a wave-uniform vote); the row sums add the bf16-rounded
-//    probabilities that the P*V product consumes (v_dot2_f32_bf16).
+//  * K/V^T tiles travel HBM -> LDS by buffer_load ... lds (no register
+//    staging): every lane fetches the logical chunk that belongs at its
+//    physical slot of the swizzled tile.  A ring of four tiles: while a wave
+//    runs the softmax and P*V of tile j it has already issued the QK^T MFMAs
+//    of tile j+1, and tiles j+2 and j+3 are in flight; one barrier per tile.
+//  * With the L2 norm on, |q_hat| <= 1 and |k_hat| <= 1, so every exp2-domain
+//    logit lies in [-c_h, c_h] with c_h = tau_h * log2(e).  Softmax is
+//    unchanged by a constant shift, so for c_h <= 60 the kernel subtracts c_h
+//    instead of the running row maximum: 2^(s - c_h) stays within
+//    [2^-120, ~1], normal in fp32 and bf16, and no row maximum, rescale or
+//    cross-lane exchange is needed.  The shift enters as the MFMA's initial
+//    accumulator, so the probabilities are one v_exp_f32 away from the
+//    product.  Otherwise the usual online softmax runs: the rescale of O runs
+//    only when some row's running max grew (a wave-uniform vote).
+//  * The row sums add the bf16-rounded probabilities that the P*V product
+//    consumes (v_dot2_f32_bf16); each half-wave keeps its own partial sum
+//    until the end.
 //  * Causal blocks: tiles above the diagonal are skipped per wave and only
 //    diagonal tiles are masked; the heavy (late) position blocks are
 //    dispatched first.
+#include <type_traits>
+
 #include "cca_device.h"
 #include "cca_launch.h"
 
 namespace cca {
 
-// Keys per tile: 64 when three K/V^T tiles fit in 48 KiB of LDS, else 32.
+// Keys per tile: 64 when the ring of four K/V^T tiles fits in 64 KiB of LDS
+// (two workgroups per CU), else 32.
 template <typename TQ, typename TV, int D> struct AttnTile {
+  static constexpr int NBUF = 4;
   static constexpr int DP = D < 32 ? 32 : D;
   static constexpr int bytes(int kb) { return kb * D * (int)sizeof(TQ) + DP * kb * (int)sizeof(TV); }
-  static constexpr int KB = 3 * bytes(64) <= 49152 ? 64 : 32;
-  static constexpr bool fits = 3 * bytes(KB) <= 49152;
+  static constexpr int KB = NBUF * bytes(64) <= 65536 ? 64 : 32;
+  static constexpr bool fits = NBUF * bytes(KB) <= 65536;
 };
 
 template <typename TQ, typename TV, int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__ q,
                                                           const TQ *__restrict__ k,
                                                           const TV *__restrict__ vt,
+                                                          const float *__restrict__ tau,
                                                           TV *__restrict__ o, int B, int T, int Tp,
                                                           int Hq, int Hkv, int G, int hq, int nsub,
-                                                          int npb) {
+                                                          int npb, int use_norm) {
   typedef Mfma32<TQ> MQ;
   typedef Mfma32<TV> MV;
   typedef AttnTile<TQ, TV, D> TL;
@@ -65,15 +81,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   constexpr int VROW = KB * (int)sizeof(TV);          // bytes per V^T tile row
   constexpr int VCPR = VROW / 16;
   constexpr int KTILE = KB * KROW, VTILE = DP * VROW, BUF = KTILE + VTILE;
-  constexpr int K_CH = (KB * KCPR + 255) / 256;       // 16-byte chunks per thread
-  constexpr int V_CH = (D * VCPR + 255) / 256;
+  constexpr int NBUF = TL::NBUF;
+  constexpr int K_INS = KB * KCPR / 64;               // DMA instructions per K tile
+  constexpr int V_INS = D * VCPR / 64;                // and per V^T tile
+  constexpr int PER_WAVE = (K_INS + V_INS) / 4;
+  static_assert(K_INS * 64 == KB * KCPR && V_INS * 64 == D * VCPR && (K_INS + V_INS) % 4 == 0,
+                "tiles split into whole DMA instructions over 4 waves");
+  static_assert(2 * PER_WAVE < 16, "vmcnt field");
   constexpr int QC = D / (2 * KSQ);                   // QK^T contraction chunks
   constexpr int PC = 16 / KSV;                        // P*V chunks per 32-key half
   static_assert(TL::fits, "K/V tiles exceed the LDS budget");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hl = lane >> 5;
   const int pos_per = 128 / hq;
 
@@ -96,10 +117,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   const int wave_last = p0 + 31;
   const int wave_tiles = min(ntiles, wave_last / KB + 1);   // tiles this wave computes
 
+  // constant logit shift when the normalised logits are bounded by c_h
+  const float c_h = tau[h] * 1.4426950408889634f;
+  const bool fixed_shift = use_norm && c_h >= 0.f && c_h <= 60.f;   // wave-uniform
+  f32x16 s_init;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) s_init[a] = fixed_shift ? -c_h : 0.f;
+
   // zero the padding rows of the V^T tiles (d < 32)
   if (D < DP) {
     constexpr int PADC = (DP - D) * VROW / 16;
-    for (int e = tid; e < 3 * PADC; e += 256)
+    for (int e = tid; e < NBUF * PADC; e += 256)
       st16(smem + (e / PADC) * BUF + KTILE + D * VROW + (e % PADC) * 16, zero_u32x4());
   }
 
@@ -114,42 +142,35 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
 
   const TQ *kbase = k + (size_t)(b * Hkv + g) * Tp * D;
   const TV *vbase = vt + (size_t)(b * Hkv + g) * D * Tp;
-  u32x4 rk[K_CH], rv[V_CH];
-
-  auto gload = [&](int kt) {
-    const int k0 = kt * KB;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void *)kbase, 0, (unsigned)(Tp * KROW), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void *)vbase, 0, (unsigned)(D * Tp * (int)sizeof(TV)), 0x00020000);
+  // byte offset (inside tile 0) of the logical chunk this lane fetches for
+  // each of its DMA instructions: the one stored at its physical slot
+  unsigned voff[PER_WAVE];
 #pragma unroll
-    for (int r = 0; r < K_CH; ++r) {
-      const int c = tid + 256 * r;
-      if (c < KB * KCPR) rk[r] = ld16(reinterpret_cast<const unsigned char *>(kbase + (size_t)k0 * D) + c * 16);
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int ins = wave * PER_WAVE + u;
+    if (ins < K_INS) {
+      const int c = ins * 64 + lane, row = c / KCPR, ch = (c % KCPR) ^ swz_key(row, KCPR);
+      voff[u] = (unsigned)(row * KROW + ch * 16);
+    } else {
+      const int c = (ins - K_INS) * 64 + lane, row = c / VCPR, ch = (c % VCPR) ^ swz_key(row, VCPR);
+      voff[u] = (unsigned)(row * Tp * (int)sizeof(TV) + ch * 16);
     }
-#pragma unroll
-    for (int r = 0; r < V_CH; ++r) {
-      const int c = tid + 256 * r;
-      if (c < D * VCPR) {
-        const int row = c / VCPR, ch = c % VCPR;
-        rv[r] = ld16(reinterpret_cast<const unsigned char *>(vbase + (size_t)row * Tp + k0) + ch * 16);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
+  }
+  auto issue = [&](int kt, int buf) {
     unsigned char *sk = smem + buf * BUF;
-    unsigned char *sv = sk + KTILE;
 #pragma unroll
-    for (int r = 0; r < K_CH; ++r) {
-      const int c = tid + 256 * r;
-      if (c < KB * KCPR) {
-        const int row = c / KCPR, ch = c % KCPR;
-        st16(sk + row * KROW + swz(row, ch * 16, KCPR), rk[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < V_CH; ++r) {
-      const int c = tid + 256 * r;
-      if (c < D * VCPR) {
-        const int row = c / VCPR, ch = c % VCPR;
-        st16(sv + row * VROW + swz(row, ch * 16, VCPR), rv[r]);
-      }
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int ins = wave * PER_WAVE + u;             // wave-uniform
+      if (ins < K_INS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, as_lds(sk + ins * 1024), 16, (int)voff[u],
+                                                 (unsigned)(kt * KB * KROW), 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, as_lds(sk + KTILE + (ins - K_INS) * 1024), 16, (int)voff[u],
+                                                 (unsigned)(kt * KB * (int)sizeof(TV)), 0, 0);
     }
   };
   // S^T = K Q^T for one tile: NH accumulators of 32 keys x 32 queries
@@ -157,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
     const unsigned char *sk = smem + buf * BUF;
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
-      s[hf] = zero16();
+      s[hf] = s_init;
       const int row = hf * 32 + l32;
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
@@ -173,24 +194,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   for (int i = 0; i < ND; ++i) acc[i] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  // prologue: tiles 0 and 1 resident, tile 2 in flight, S of tile 0 computed
-  gload(0);
-  lstore(0);
-  if (ntiles > 1) {
-    gload(1);
-    lstore(1);
-  }
-  __syncthreads();
-  if (ntiles > 2) gload(2);
-  f32x16 s_cur[NH], s_nxt[NH];
-  qk(0, s_cur);
-
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // one tile: tiles kt and kt + 1 are resident, kt + 2 is in flight
+  auto step = [&](int kt, f32x16 (&s_cur)[NH], f32x16 (&s_nxt)[NH]) {
+    // the slot of tile kt - 1 is free since the last barrier
+    if (kt + 3 < ntiles) issue(kt + 3, (kt + 3) % NBUF);
     // look ahead: the next tile's QK^T MFMAs overlap this tile's softmax
-    if (kt + 1 < wave_tiles) qk((kt + 1) % 3, s_nxt);
+    if (kt + 1 < wave_tiles) qk((kt + 1) % NBUF, s_nxt);
     if (kt < wave_tiles) {
       const int k0 = kt * KB;
-      const unsigned char *sv = smem + (kt % 3) * BUF + KTILE;
+      const unsigned char *sv = smem + (kt % NBUF) * BUF + KTILE;
       if (k0 + KB - 1 > p0) {                          // diagonal tile: causal mask
 #pragma unroll
         for (int hf = 0; hf < NH; ++hf)
@@ -200,66 +212,90 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
             if (key > qpos) s_cur[hf][a] = -INFINITY;
           }
       }
-      float mx = s_cur[0][0];
+      auto softmax_pv = [&](auto fixed_tag) {
+        constexpr bool FIXED = decltype(fixed_tag)::value;
+        if constexpr (!FIXED) {
+          float mx = s_cur[0][0];
 #pragma unroll
-      for (int hf = 0; hf < NH; ++hf)
+          for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s_cur[hf][a]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // rescale only when some row's running max grew (alpha = 1 otherwise)
-      if (__any(mx > m_run)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
+            for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s_cur[hf][a]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          // rescale only when some row's running max grew (alpha = 1 otherwise)
+          if (__any(mx > m_run)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < ND; ++i)
+            for (int i = 0; i < ND; ++i)
 #pragma unroll
-          for (int a = 0; a < 16; ++a) acc[i][a] *= alpha;
-        m_run = m_new;
-      }
-      float psum = 0.f;
-#pragma unroll
-      for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-        for (int cc = 0; cc < PC; ++cc) {
-          float pv[KSV];
-#pragma unroll
-          for (int sl = 0; sl < KSV; ++sl) pv[sl] = __builtin_amdgcn_exp2f(s_cur[hf][KSV * cc + sl] - m_run);
-          const typename MV::frag pf = pack_frag<TV>(pv);
-          if constexpr (KSV == 8) {
-            // row sum of the rounded probabilities the P*V product uses
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-              const bf16x2 pair = {pf[2 * e], pf[2 * e + 1]};
-              const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-              psum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, psum, false);
-            }
-          } else {
-#pragma unroll
-            for (int sl = 0; sl < KSV; ++sl) psum += pv[sl];
-          }
-          // first key of this lane's k-slots, in the permuted tile order
-          const int a0 = KSV * cc;
-          const int key_rel = 8 * (a0 >> 2) + 4 * hl + (a0 & 3);
-          const int kb = (hf * 32 + vt_perm(key_rel)) * (int)sizeof(TV);
-#pragma unroll
-          for (int i = 0; i < ND; ++i) {
-            const int row = i * 32 + l32;
-            typename MV::frag vf = load_frag<TV>(reinterpret_cast<const TV *>(sv + row * VROW + swz(row, kb, VCPR)));
-            acc[i] = MV::mma(vf, pf, acc[i]);
+              for (int a = 0; a < 16; ++a) acc[i][a] *= alpha;
+            m_run = m_new;
           }
         }
-      psum += __shfl_xor(psum, 32, 64);
-      l_run += psum;
-    }
-    if (kt + 2 < ntiles) lstore((kt + 2) % 3);
-    __syncthreads();
-    if (kt + 3 < ntiles) gload(kt + 3);
 #pragma unroll
-    for (int hf = 0; hf < NH; ++hf) s_cur[hf] = s_nxt[hf];
+        for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+          for (int cc = 0; cc < PC; ++cc) {
+            float pv[KSV];
+#pragma unroll
+            for (int sl = 0; sl < KSV; ++sl)
+              pv[sl] = __builtin_amdgcn_exp2f(FIXED ? s_cur[hf][KSV * cc + sl]
+                                                    : s_cur[hf][KSV * cc + sl] - m_run);
+            const typename MV::frag pf = pack_frag<TV>(pv);
+            if constexpr (KSV == 8) {
+              // row sum of the rounded probabilities the P*V product uses
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                const bf16x2 pair = {pf[2 * e], pf[2 * e + 1]};
+                const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run, false);
+              }
+            } else {
+#pragma unroll
+              for (int sl = 0; sl < KSV; ++sl) l_run += pv[sl];
+            }
+            // first key of this lane's k-slots, in the permuted tile order
+            const int a0 = KSV * cc;
+            const int key_rel = 8 * (a0 >> 2) + 4 * hl + (a0 & 3);
+            const int kb = (hf * 32 + vt_perm(key_rel)) * (int)sizeof(TV);
+#pragma unroll
+            for (int i = 0; i < ND; ++i) {
+              const int row = i * 32 + l32;
+              typename MV::frag vf = load_frag<TV>(reinterpret_cast<const TV *>(sv + row * VROW + swz(row, kb, VCPR)));
+              acc[i] = MV::mma(vf, pf, acc[i]);
+            }
+          }
+      };
+      if (fixed_shift) softmax_pv(std::true_type{});
+      else softmax_pv(std::false_type{});
+    }
+    // tile kt + 2 visible to every wave before the next step's look-ahead
+    if (kt + 3 < ntiles) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+  };
+
+  // prologue: tiles 0..2 issued, 0 and 1 resident, S of tile 0 computed
+  issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+  if (ntiles > 2) {
+    issue(2, 2);
+    wait_vmcnt<PER_WAVE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  f32x16 s_a[NH], s_b[NH];
+  qk(0, s_a);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    step(kt, s_a, s_b);
+    if (kt + 1 < ntiles) step(kt + 1, s_b, s_a);
   }
 
+  // each half-wave summed its own keys (and both saw the same rescales)
+  l_run += __shfl_xor(l_run, 32, 64);
   if (qpos >= T) return;
   const float inv_l = 1.f / l_run;
   TV *orow = o + ((size_t)(b * T + qpos)) * (Hq * D) + h * D;
@@ -286,27 +322,27 @@ static int gcd_int(int a, int b) {
 }
 
 template <typename TQ, typename TV, int D>
-static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *vt, TV *o,
-                         hipStream_t stream) {
+static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
+                         const float *tau, TV *o, hipStream_t stream) {
   const int hq = gcd_int(s.G, 4);
   const int nsub = s.G / hq;
   const int pos_per = 128 / hq;
   const int npb = (s.T + pos_per - 1) / pos_per;
   const int grid = npb * s.B * s.Hkv * nsub;
-  hipLaunchKernelGGL((attn_fwd_kernel<TQ, TV, D>), dim3(grid), dim3(256), 0, stream, q, k, vt, o,
-                     s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb);
+  hipLaunchKernelGGL((attn_fwd_kernel<TQ, TV, D>), dim3(grid), dim3(256), 0, stream, q, k, vt, tau,
+                     o, s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb, s.use_norm);
   return hipGetLastError();
 }
 
 template <typename TQ, typename TV>
 hipError_t launch_attention_prefill(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
-                                    TV *o, hipStream_t stream) {
+                                    const float *tau, TV *o, hipStream_t stream) {
   switch (s.d) {
-    case 16: return attn_d<TQ, TV, 16>(s, q, k, vt, o, stream);
-    case 32: return attn_d<TQ, TV, 32>(s, q, k, vt, o, stream);
-    case 64: return attn_d<TQ, TV, 64>(s, q, k, vt, o, stream);
+    case 16: return attn_d<TQ, TV, 16>(s, q, k, vt, tau, o, stream);
+    case 32: return attn_d<TQ, TV, 32>(s, q, k, vt, tau, o, stream);
+    case 64: return attn_d<TQ, TV, 64>(s, q, k, vt, tau, o, stream);
     case 128:
-      if constexpr (AttnTile<TQ, TV, 128>::fits) return attn_d<TQ, TV, 128>(s, q, k, vt, o, stream);
+      if constexpr (AttnTile<TQ, TV, 128>::fits) return attn_d<TQ, TV, 128>(s, q, k, vt, tau, o, stream);
       break;
   }
   return hipErrorInvalidValue;
@@ -317,12 +353,13 @@ bool attention_supported(int d, bool f32) {
 }
 
 template hipError_t launch_attention_prefill<f16, bf16>(const MixShape &, const f16 *, const f16 *,
-                                                        const bf16 *, bf16 *, hipStream_t);
+                                                        const bf16 *, const float *, bf16 *,
+                                                        hipStream_t);
 template hipError_t launch_attention_prefill<bf16, bf16>(const MixShape &, const bf16 *,
-                                                         const bf16 *, const bf16 *, bf16 *,
-                                                         hipStream_t);
+                                                         const bf16 *, const bf16 *,
+                                                         const float *, bf16 *, hipStream_t);
 template hipError_t launch_attention_prefill<float, float>(const MixShape &, const float *,
-                                                           const float *, const float *, float *,
-                                                           hipStream_t);
+                                                           const float *, const float *,
+                                                           const float *, float *, hipStream_t);
 
 }  // namespace cca

@@ -242,17 +242,17 @@ cca_status run_attention(const cca_config &c, const cca_weights *w, void *ws, co
   if (c.dtype == CCA_F32) {
     e = launch_attention_prefill<float, float>(s, (const float *)wsp(ws, L, CCA_WS_Q),
                                                (const float *)wsp(ws, L, CCA_WS_K),
-                                               (const float *)wsp(ws, L, CCA_WS_VT),
+                                               (const float *)wsp(ws, L, CCA_WS_VT), w->tau,
                                                (float *)wsp(ws, L, CCA_WS_O), st);
   } else if (qk_is_f16(c)) {
     e = launch_attention_prefill<f16, bf16>(s, (const f16 *)wsp(ws, L, CCA_WS_Q),
                                             (const f16 *)wsp(ws, L, CCA_WS_K),
-                                            (const bf16 *)wsp(ws, L, CCA_WS_VT),
+                                            (const bf16 *)wsp(ws, L, CCA_WS_VT), w->tau,
                                             (bf16 *)wsp(ws, L, CCA_WS_O), st);
   } else {
     e = launch_attention_prefill<bf16, bf16>(s, (const bf16 *)wsp(ws, L, CCA_WS_Q),
                                              (const bf16 *)wsp(ws, L, CCA_WS_K),
-                                             (const bf16 *)wsp(ws, L, CCA_WS_VT),
+                                             (const bf16 *)wsp(ws, L, CCA_WS_VT), w->tau,
                                              (bf16 *)wsp(ws, L, CCA_WS_O), st);
   }
   return check_launch(e, st);

@@ -109,10 +109,11 @@ __device__ __forceinline__ u32x4 zero_u32x4() {
 // consecutive rows on distinct (row parity, chunk) pairs (conflict-free for
 // 64 banks, 16 lanes per phase).  `row_chunks` is the number of 16-byte
 // chunks per row (a power of two).
+__host__ __device__ __forceinline__ int swz_key(int row, int row_chunks) {
+  return row_chunks >= 8 ? ((row & 7) ^ ((row >> 3) & 1)) : (row & (row_chunks - 1));
+}
 __device__ __forceinline__ int swz(int row, int byte_in_row, int row_chunks) {
-  const int chunk = byte_in_row >> 4;
-  const int f = row_chunks >= 8 ? ((row & 7) ^ ((row >> 3) & 1)) : (row & (row_chunks - 1));
-  const int phys = chunk ^ f;
+  const int phys = (byte_in_row >> 4) ^ swz_key(row, row_chunks);
   return (phys << 4) | (byte_in_row & 15);
 }
 
@@ -141,6 +142,37 @@ __device__ __forceinline__ float group_sum(float v) {
 // (keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key chunk) are contiguous.
 __host__ __device__ __forceinline__ int vt_perm(int t) {
   return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
+// Index of the calling wave inside its workgroup, as a wave-uniform (scalar)
+// value: values derived from it stay in SGPRs, branches on them stay scalar,
+// and an LDS-DMA destination built from it needs no per-lane loop for M0.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// An LDS address as the LDS-DMA builtins take it.  Inside kernel templates,
+// arguments of those builtins whose types depend on template parameters (an
+// LDS array of dependent size, an element of a dependent-size array) make the
+// host pass reject the call without a diagnostic and drop the kernel's launch
+// stub; pass the LDS pointer through as_lds and offsets as plain int.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void *as_lds(void *p) { return (lds_void *)p; }
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (vmcnt(N)); expcnt and lgkmcnt are left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
+// Workgroup barrier for LDS-DMA pipelines: waits for this wave's own LDS
+// operations, then s_barrier, without the vmcnt(0) that __syncthreads adds
+// (which would also wait for the tiles still in flight).  Callers wait for
+// the DMA tiles they need with wait_vmcnt first.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Physical XCD-aware block remap: the hardware deals consecutive workgroup

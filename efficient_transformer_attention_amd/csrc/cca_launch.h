@@ -62,10 +62,11 @@ hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const floa
                                  hipStream_t stream);
 
 // Causal flash attention inside the latent heads; q holds tau_h * log2(e) *
-// q_hat (the mixing kernel applies the temperature).  o [B*T, Hq*d] in TV.
+// q_hat (the mixing kernel applies the temperature); tau [Hq] (device) bounds
+// the logits when the L2 norm is on.  o [B*T, Hq*d] in TV.
 template <typename TQ, typename TV>
 hipError_t launch_attention_prefill(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
-                                    TV *o, hipStream_t stream);
+                                    const float *tau, TV *o, hipStream_t stream);
 bool attention_supported(int d, bool f32);
 
 // Split-KV decode attention over Lk = L + 1 cached keys, then the log-sum-exp

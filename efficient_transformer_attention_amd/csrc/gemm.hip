@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
   auto sB = [&](int buf) { return smem + buf * (BM + BN) * ROWB + BM * ROWB; };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hl = lane >> 5;
 
@@ -166,11 +166,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);   // vmcnt(N), expcnt and lgkmcnt unconstrained
-}
+
 
 template <typename Tout, int BM, int BN, int STAGES>
 __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restrict__ A,
@@ -187,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
   static_assert(2 * PER_WAVE < 16, "vmcnt field");
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hl = lane >> 5;
   const int ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
@@ -224,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
       bool ok = dvalid[u];
       if (k_ragged) ok = ok && (kt * BK + dk[u] < K);
       const unsigned off = ok ? doff[u] + (unsigned)(kt * BK * 2) : (isA ? a_bytes : b_bytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, base + ins * 1024, 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(base + ins * 1024), 16, off, 0, 0, 0);
     }
   };
 
@@ -264,9 +260,8 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
     else if (after == 1) wait_vmcnt<PER_WAVE>();
     else wait_vmcnt<0>();
     // every wave's DMA of tile kt has landed (each waited for its own above)
-    // and every read of the ring slot reused below is done; a plain s_barrier,
-    // since a fence here would also wait for the tiles still in flight
-    asm volatile("s_barrier" ::: "memory");
+    // and every read of the ring slot reused below is done
+    lds_barrier();
     const int nslot = slot == 0 ? STAGES - 1 : slot - 1;   // (kt + STAGES - 1) % STAGES
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, nslot);
     const unsigned char *sbase = smem + slot * STAGE;
@@ -287,16 +282,23 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
     slot = slot + 1 == STAGES ? 0 : slot + 1;
   }
 
+  const bool full = m0 + BM <= M && n0 + BN <= N;   // workgroup-uniform
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int gn = n0 + wn * WN + j * 32 + l32;
-      if (gn >= N) continue;
+      Tout *cp = C + (size_t)(m0 + wm * WM + i * 32 + 4 * hl) * ldc + gn;
+      if (full) {
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int gm = m0 + wm * WM + i * 32 + 8 * (a >> 2) + 4 * hl + (a & 3);
-        if (gm < M) C[(size_t)gm * ldc + gn] = from_f32<Tout>(acc[i][j][a]);
+        for (int a = 0; a < 16; ++a)
+          cp[(size_t)(8 * (a >> 2) + (a & 3)) * ldc] = from_f32<Tout>(acc[i][j][a]);
+      } else if (gn < N) {
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int r = 8 * (a >> 2) + (a & 3);
+          if (m0 + wm * WM + i * 32 + 4 * hl + r < M) cp[(size_t)r * ldc] = from_f32<Tout>(acc[i][j][a]);
+        }
       }
     }
 }

@@ -51,6 +51,10 @@ SMALL = {
     "bf16_switches_off": (CCAShape(batch=1, seq_len=160, d_model=256, n_q_heads=4, n_kv_heads=4,
                                    head_dim=64, use_qk_mean=0, use_value_shift=0, use_qk_norm=0,
                                    rope_base=10000.0), "inv_sqrt_d"),
+    # norm on with per-head temperatures on both sides of the constant-shift
+    # limit (tau * log2(e) <= 60 uses the fixed shift, above it the running max)
+    "bf16_norm_mixed_tau": (CCAShape(batch=1, seq_len=210, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                     head_dim=64), "mixed"),
 }
 
 
@@ -61,6 +65,8 @@ def test_prefill_small_parity(name):
     P = make_prefill(shape, seed=0)
     if tau == "inv_sqrt_d":
         set_taps(P, tau=tau_inv_sqrt_d(shape))
+    elif tau == "mixed":
+        set_taps(P, tau=np.array([8.0, 50.0, 0.5, 41.0], dtype=np.float32))
     run = PrefillRun(shape, P)
     y = run.run()
     ref = O.prefill(P.x, P.weights.f64(), shape)
