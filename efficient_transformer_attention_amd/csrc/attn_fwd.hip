@@ -194,26 +194,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   for (int i = 0; i < ND; ++i) acc[i] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  // one tile: tiles kt and kt + 1 are resident, kt + 2 is in flight
-  auto step = [&](int kt, f32x16 (&s_cur)[NH], f32x16 (&s_nxt)[NH]) {
-    // the slot of tile kt - 1 is free since the last barrier
-    if (kt + 3 < ntiles) issue(kt + 3, (kt + 3) % NBUF);
-    // look ahead: the next tile's QK^T MFMAs overlap this tile's softmax
-    if (kt + 1 < wave_tiles) qk((kt + 1) % NBUF, s_nxt);
-    if (kt < wave_tiles) {
-      const int k0 = kt * KB;
-      const unsigned char *sv = smem + (kt % NBUF) * BUF + KTILE;
-      if (k0 + KB - 1 > p0) {                          // diagonal tile: causal mask
+  // the whole key loop is instantiated once per softmax form, so that the
+  // branch between them stays outside the loop
+  auto run = [&](auto fixed_tag) {
+    constexpr bool FIXED = decltype(fixed_tag)::value;
+    // one tile: tiles kt and kt + 1 are resident, kt + 2 is in flight
+    auto step = [&](int kt, f32x16 (&s_cur)[NH], f32x16 (&s_nxt)[NH]) {
+      // the slot of tile kt - 1 is free since the last barrier
+      if (kt + 3 < ntiles) issue(kt + 3, (kt + 3) % NBUF);
+      // look ahead: the next tile's QK^T MFMAs overlap this tile's softmax
+      if (kt + 1 < wave_tiles) qk((kt + 1) % NBUF, s_nxt);
+      if (kt < wave_tiles) {
+        const int k0 = kt * KB;
+        const unsigned char *sv = smem + (kt % NBUF) * BUF + KTILE;
+        if (k0 + KB - 1 > p0) {                          // diagonal tile: causal mask
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf)
+          for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-          for (int a = 0; a < 16; ++a) {
-            const int key = k0 + hf * 32 + 8 * (a >> 2) + 4 * hl + (a & 3);
-            if (key > qpos) s_cur[hf][a] = -INFINITY;
-          }
-      }
-      auto softmax_pv = [&](auto fixed_tag) {
-        constexpr bool FIXED = decltype(fixed_tag)::value;
+            for (int a = 0; a < 16; ++a) {
+              const int key = k0 + hf * 32 + 8 * (a >> 2) + 4 * hl + (a & 3);
+              if (key > qpos) s_cur[hf][a] = -INFINITY;
+            }
+        }
         if constexpr (!FIXED) {
           float mx = s_cur[0][0];
 #pragma unroll
@@ -267,32 +269,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
               acc[i] = MV::mma(vf, pf, acc[i]);
             }
           }
-      };
-      if (fixed_shift) softmax_pv(std::true_type{});
-      else softmax_pv(std::false_type{});
-    }
-    // tile kt + 2 visible to every wave before the next step's look-ahead
-    if (kt + 3 < ntiles) wait_vmcnt<PER_WAVE>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-  };
+      }
+      // tile kt + 2 visible to every wave before the next step's look-ahead
+      if (kt + 3 < ntiles) wait_vmcnt<PER_WAVE>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+    };
 
-  // prologue: tiles 0..2 issued, 0 and 1 resident, S of tile 0 computed
-  issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
-  if (ntiles > 2) {
-    issue(2, 2);
-    wait_vmcnt<PER_WAVE>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  lds_barrier();
-  f32x16 s_a[NH], s_b[NH];
-  qk(0, s_a);
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    step(kt, s_a, s_b);
-    if (kt + 1 < ntiles) step(kt + 1, s_b, s_a);
-  }
+    // prologue: tiles 0..2 issued, 0 and 1 resident, S of tile 0 computed
+    issue(0, 0);
+    if (ntiles > 1) issue(1, 1);
+    if (ntiles > 2) {
+      issue(2, 2);
+      wait_vmcnt<PER_WAVE>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    f32x16 s_a[NH], s_b[NH];
+    qk(0, s_a);
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      step(kt, s_a, s_b);
+      if (kt + 1 < ntiles) step(kt + 1, s_b, s_a);
+    }
+  };
+  if (fixed_shift) run(std::true_type{});
+  else run(std::false_type{});
 
   // each half-wave summed its own keys (and both saw the same rescales)
   l_run += __shfl_xor(l_run, 32, 64);
