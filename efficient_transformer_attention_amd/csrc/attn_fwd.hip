@@ -40,9 +40,10 @@
 //  * The row sums add the bf16-rounded probabilities that the P*V product
 //    consumes (v_dot2_f32_bf16); each half-wave keeps its own partial sum
 //    until the end.
-//  * Causal blocks: tiles above the diagonal are skipped per wave and only
-//    diagonal tiles are masked; the heavy (late) position blocks are
-//    dispatched first.
+//  * Causal blocks: a workgroup walks the key tiles up to its last query;
+//    only tiles that reach past a wave's first query are masked (tiles past
+//    its last query come out fully masked and add nothing), and the heavy
+//    (late) position blocks are dispatched first.
 #include <type_traits>
 
 #include "cca_device.h"
@@ -114,8 +115,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   const int qpos = p0 + l32;                          // this lane's query
   const int last_row = min(blk0 + pos_per, T) - 1;    // last valid query of the block
   const int ntiles = last_row / KB + 1;
-  const int wave_last = p0 + 31;
-  const int wave_tiles = min(ntiles, wave_last / KB + 1);   // tiles this wave computes
 
   // constant logit shift when the normalised logits are bounded by c_h
   const float c_h = tau[h] * 1.4426950408889634f;
@@ -202,12 +201,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
     auto step = [&](int kt, f32x16 (&s_cur)[NH], f32x16 (&s_nxt)[NH]) {
       // the slot of tile kt - 1 is free since the last barrier
       if (kt + 3 < ntiles) issue(kt + 3, (kt + 3) % NBUF);
-      // look ahead: the next tile's QK^T MFMAs overlap this tile's softmax
-      if (kt + 1 < wave_tiles) qk((kt + 1) % NBUF, s_nxt);
-      if (kt < wave_tiles) {
+      // one basic block per tile kind, so that the scheduler can interleave
+      // the look-ahead QK^T MFMAs with this tile's softmax VALU work
+      auto tile = [&](auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
         const int k0 = kt * KB;
         const unsigned char *sv = smem + (kt % NBUF) * BUF + KTILE;
-        if (k0 + KB - 1 > p0) {                          // diagonal tile: causal mask
+        // look ahead (past the last tile the ring slot still holds some
+        // tile; that result is never used)
+        qk((kt + 1) % NBUF, s_nxt);
+        if constexpr (DIAG) {                          // causal mask
 #pragma unroll
           for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
@@ -269,7 +272,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
               acc[i] = MV::mma(vf, pf, acc[i]);
             }
           }
-      }
+      };
+      // tiles past this wave's last query are fully masked: they add nothing
+      if (kt * KB + KB - 1 > p0) tile(std::true_type{});
+      else tile(std::false_type{});
       // tile kt + 2 visible to every wave before the next step's look-ahead
       if (kt + 3 < ntiles) wait_vmcnt<PER_WAVE>();
       else wait_vmcnt<0>();
