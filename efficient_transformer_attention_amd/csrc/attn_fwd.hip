@@ -145,13 +145,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
       __builtin_amdgcn_make_buffer_rsrc((void *)kbase, 0, (unsigned)(Tp * KROW), 0x00020000);
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void *)vbase, 0, (unsigned)(D * Tp * (int)sizeof(TV)), 0x00020000);
-  // byte offset (inside tile 0) of the logical chunk this lane fetches for
-  // each of its DMA instructions: the one stored at its physical slot
+  // DMA instruction u of wave w moves 1 KiB chunk u*4 + w of a K/V^T tile
+  // pair (K first).  Per lane: the byte offset (inside tile 0) of the logical
+  // chunk that belongs at its physical slot.
+  auto is_k = [&](int u) {
+    if constexpr (K_INS % 4 == 0) return u < K_INS / 4;   // compile-time
+    else return u * 4 + wave < K_INS;
+  };
   unsigned voff[PER_WAVE];
 #pragma unroll
   for (int u = 0; u < PER_WAVE; ++u) {
-    const int ins = wave * PER_WAVE + u;
-    if (ins < K_INS) {
+    const int ins = u * 4 + wave;
+    if (is_k(u)) {
       const int c = ins * 64 + lane, row = c / KCPR, ch = (c % KCPR) ^ swz_key(row, KCPR);
       voff[u] = (unsigned)(row * KROW + ch * 16);
     } else {
@@ -163,8 +168,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
     unsigned char *sk = smem + buf * BUF;
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
-      const int ins = wave * PER_WAVE + u;             // wave-uniform
-      if (ins < K_INS)
+      const int ins = u * 4 + wave;                    // wave-uniform
+      if (is_k(u))
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, as_lds(sk + ins * 1024), 16, (int)voff[u],
                                                  (unsigned)(kt * KB * KROW), 0, 0);
       else

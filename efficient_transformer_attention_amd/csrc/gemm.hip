@@ -154,19 +154,19 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 inputs: the same product with the A and B tiles streamed straight from
-// HBM into LDS (buffer_load ... lds, no register staging) through a 4-stage
-// ring, so three K tiles are in flight while one is multiplied.
+// bf16 inputs, whole 32-element K tiles: the same product with the A and B
+// tiles streamed straight from HBM into LDS (buffer_load ... lds, no register
+// staging) through a ring of STAGES tiles, and the MFMA fragments double
+// buffered in registers: while the MFMAs of K tile k run, the fragments of
+// tile k + 1 are read from LDS and tiles up to k + STAGES - 2 are in flight.
 //   K tile = 32 elements: LDS rows of 64 bytes (4 chunks of 16 bytes), chunk
 //   swizzle f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1) (no bank conflicts for 8-
 //   or 16-lane phases).  A DMA instruction fills 1 KiB = 16 rows; lane l
 //   writes LDS bytes [16 l, 16 l + 16) of it, so each lane fetches the global
-//   chunk that the swizzle places there.  Out-of-range rows / columns read as
-//   zero (buffer range check), which also covers a ragged K tail.
+//   chunk that the swizzle places there.  Rows past M / N read as zero (buffer
+//   range check).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
-
-
 
 template <typename Tout, int BM, int BN, int STAGES>
 __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restrict__ A,
@@ -174,16 +174,17 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
                                                              Tout *__restrict__ C, int M, int N,
                                                              int K, int lda, int ldb, int ldc) {
   typedef Mfma32<bf16> MF;
+  typedef MF::frag Frag;
   constexpr int BK = 32, ROWB = 64;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int STAGE = (BM + BN) * ROWB;
   constexpr int A_INS = BM * ROWB / 1024, B_INS = BN * ROWB / 1024;   // DMA instructions per stage
   constexpr int PER_WAVE = (A_INS + B_INS) / 4;
-  static_assert((A_INS + B_INS) % 4 == 0, "DMA split over 4 waves");
-  static_assert(2 * PER_WAVE < 16, "vmcnt field");
+  static_assert(A_INS % 4 == 0 && B_INS % 4 == 0, "DMA split over 4 waves");
+  static_assert(STAGES >= 3 && (STAGES - 3) * PER_WAVE < 16, "vmcnt field");
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hl = lane >> 5;
   const int ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
@@ -194,33 +195,29 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bm, 0, b_bytes, 0x00020000);
 
-  // per DMA slot of this lane: byte offset of K tile 0 (or an out-of-range
-  // offset for rows past M / N) and the element index of its chunk in a tile
+  // DMA instruction u of wave w moves 1 KiB chunk u*4 + w of a stage: the
+  // first A_INS/4 instructions of every wave load A, the rest B.  Per lane:
+  // the byte offset of its chunk in K tile 0, or the operand's size for rows
+  // past M / N, which the buffer range check turns into zeros.
   unsigned doff[PER_WAVE];
-  int dk[PER_WAVE];
-  bool dvalid[PER_WAVE];
 #pragma unroll
   for (int u = 0; u < PER_WAVE; ++u) {
-    const int ins = wave * PER_WAVE + u;
-    const bool isA = ins < A_INS;
-    const int row = (isA ? ins : ins - A_INS) * 16 + (lane >> 2);
+    constexpr int AU = A_INS / 4;
+    const bool isA = u < AU;
+    const int row = ((isA ? u : u - AU) * 4 + wave) * 16 + (lane >> 2);
     const int chunk = (lane & 3) ^ swz4(row);
     const int grow = (isA ? m0 : n0) + row;
-    dvalid[u] = grow < (isA ? M : N);
-    dk[u] = chunk * 8;
-    doff[u] = dvalid[u] ? (unsigned)(((size_t)grow * (isA ? lda : ldb) + chunk * 8) * 2) : 0u;
+    doff[u] = grow < (isA ? M : N) ? (unsigned)(((size_t)grow * (isA ? lda : ldb) + chunk * 8) * 2)
+                                   : (isA ? a_bytes : b_bytes);
   }
-  const bool k_ragged = (K % BK) != 0;
   auto issue = [&](int kt, int slot) {
-    unsigned char *base = smem + slot * STAGE;
+    unsigned char *base = smem + slot * STAGE + wave * 1024;
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
-      const int ins = wave * PER_WAVE + u;
-      const bool isA = ins < A_INS;                   // wave-uniform
-      bool ok = dvalid[u];
-      if (k_ragged) ok = ok && (kt * BK + dk[u] < K);
-      const unsigned off = ok ? doff[u] + (unsigned)(kt * BK * 2) : (isA ? a_bytes : b_bytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(base + ins * 1024), 16, off, 0, 0, 0);
+      const bool isA = u < A_INS / 4;
+      unsigned char *dst = isA ? base + u * 4096 : base + A_INS * 1024 + (u - A_INS / 4) * 4096;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(dst), 16, (int)doff[u],
+                                               kt * BK * 2, 0, 0);
     }
   };
 
@@ -240,46 +237,68 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
       boff[kk][j] = BM * ROWB + row * ROWB + ((chunk ^ swz4(row)) << 4);
     }
   }
+  auto load = [&](int slot, Frag (&fa)[2][TM], Frag (&fb)[2][TN]) {
+    const unsigned char *sbase = smem + slot * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[kk][i] = *reinterpret_cast<const Frag *>(sbase + aoff[kk][i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[kk][j] = *reinterpret_cast<const Frag *>(sbase + boff[kk][j]);
+    }
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
-
-  const int nk = (K + BK - 1) / BK;
-#pragma unroll
-  for (int s0 = 0; s0 < STAGES - 1; ++s0)
-    if (s0 < nk) issue(s0, s0);
-
-  int slot = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    // tile kt has landed once at most the tiles issued after it are in flight
-    const int after = min(STAGES - 2, nk - 1 - kt);
-    if (after >= 2) wait_vmcnt<2 * PER_WAVE>();
-    else if (after == 1) wait_vmcnt<PER_WAVE>();
-    else wait_vmcnt<0>();
-    // every wave's DMA of tile kt has landed (each waited for its own above)
-    // and every read of the ring slot reused below is done
-    lds_barrier();
-    const int nslot = slot == 0 ? STAGES - 1 : slot - 1;   // (kt + STAGES - 1) % STAGES
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, nslot);
-    const unsigned char *sbase = smem + slot * STAGE;
-    MF::frag fa[2][TM], fb[2][TN];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[kk][i] = *reinterpret_cast<const MF::frag *>(sbase + aoff[kk][i]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[kk][j] = *reinterpret_cast<const MF::frag *>(sbase + boff[kk][j]);
-    }
+  auto mma = [&](Frag (&fa)[2][TM], Frag (&fb)[2][TN]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[kk][i], fb[kk][j], acc[i][j]);
-    slot = slot + 1 == STAGES ? 0 : slot + 1;
+  };
+  // wait until at most n of this wave's DMA stages are still in flight
+  auto wait_stages = [&](int n) {
+    if constexpr (STAGES >= 5) {
+      if (n >= 2) { wait_vmcnt<2 * PER_WAVE>(); return; }
+    }
+    if constexpr (STAGES >= 4) {
+      if (n >= 1) { wait_vmcnt<PER_WAVE>(); return; }
+    }
+    wait_vmcnt<0>();
+  };
+
+  const int nk = K / BK;
+  // iteration kt: tile kt + 1 is read into registers while tile kt (already
+  // in registers) is multiplied; tiles up to kt + STAGES - 2 are in flight
+  auto iter = [&](int kt, Frag (&ca)[2][TM], Frag (&cb)[2][TN], Frag (&na)[2][TM],
+                  Frag (&nb)[2][TN]) {
+    if (kt + 1 < nk) {
+      // tile kt + 1 landed: of the tiles issued so far, those after it may fly
+      wait_stages(min(nk, kt + STAGES - 1) - (kt + 2));
+      // every wave's DMA of tile kt + 1 has landed, and every read of the
+      // slot refilled below (tile kt - 1, read during iteration kt - 2) is done
+      lds_barrier();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      load((kt + 1) % STAGES, na, nb);
+    }
+    mma(ca, cb);
+  };
+
+#pragma unroll
+  for (int s0 = 0; s0 < STAGES - 1; ++s0)
+    if (s0 < nk) issue(s0, s0);
+  wait_stages(min(nk, STAGES - 1) - 1);
+  lds_barrier();
+  Frag fa0[2][TM], fb0[2][TN], fa1[2][TM], fb1[2][TN];
+  load(0, fa0, fb0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    iter(kt, fa0, fb0, fa1, fb1);
+    if (kt + 1 < nk) iter(kt + 1, fa1, fb1, fa0, fb0);
   }
 
   const bool full = m0 + BM <= M && n0 + BN <= N;   // workgroup-uniform
@@ -353,8 +372,10 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
   constexpr int BM = 128, BN = 128;
   int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if constexpr (sizeof(Tin) == 2) {
-    // operands below 4 GiB so the buffer range check covers them
-    if ((size_t)M * lda * 2 < (1ull << 32) && (size_t)N * ldb * 2 < (1ull << 32)) {
+    // whole 32-element K tiles, and operands small enough that every byte
+    // offset (out-of-range ones included) fits the 32-bit buffer range check
+    const size_t lim = (1ull << 32) - 2 * (size_t)K;
+    if (K % 32 == 0 && (size_t)M * lda * 2 < lim && (size_t)N * ldb * 2 < lim) {
       // N tile of 128 or 192, whichever finishes sooner counted in rounds of
       // resident workgroups (2 per CU, 256 CUs), a tile's time being
       // proportional to its width
@@ -365,10 +386,10 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
       };
       if (cost(192) < cost(128)) {
         const int g192 = ((M + 127) / 128) * ((N + 191) / 192);
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 192, 3>), dim3(g192), dim3(256), 0, stream,
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 192, 4>), dim3(g192), dim3(256), 0, stream,
                            A, B, C, M, N, K, lda, ldb, ldc);
       } else {
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 128, 4>), dim3(grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 128, 5>), dim3(grid), dim3(256), 0, stream,
                            A, B, C, M, N, K, lda, ldb, ldc);
       }
       return hipGetLastError();
