@@ -102,6 +102,8 @@ cca_status validate_shape(const cca_config *c, bool need_seq) {
       (1ll << 40))
     return CCA_ERR_UNSUPPORTED;
   if ((long long)c->batch * (need_seq ? c->seq_len : 1) > (1ll << 31) - 1) return CCA_ERR_UNSUPPORTED;
+  // one sequence's down-projection rows are addressed by 32-bit buffer offsets
+  if (need_seq && (long long)padded_T(c->seq_len) * N * 4 >= (1ll << 31)) return CCA_ERR_UNSUPPORTED;
   return CCA_OK;
 }
 

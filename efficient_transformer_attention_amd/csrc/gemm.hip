@@ -167,15 +167,21 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
 //   range check).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// 128-byte rows (8 chunks): f(r) = (r & 7) ^ ((r >> 3) & 1)
+template <int CPR> __device__ __forceinline__ int swz_rows(int row) {
+  if constexpr (CPR == 4) return swz4(row);
+  else return (row & 7) ^ ((row >> 3) & 1);
+}
 
-template <typename Tout, int BM, int BN, int STAGES>
-__global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restrict__ A,
+template <typename Tout, int BM, int BN, int BK, int STAGES, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__restrict__ A,
                                                              const bf16 *__restrict__ Bm,
                                                              Tout *__restrict__ C, int M, int N,
                                                              int K, int lda, int ldb, int ldc) {
   typedef Mfma32<bf16> MF;
   typedef MF::frag Frag;
-  constexpr int BK = 32, ROWB = 64;
+  constexpr int ROWB = BK * 2, CPR = ROWB / 16, KK = BK / 16;   // row bytes, chunks, k-chunks
+  static_assert(BK == 32 || BK == 64, "K tile");
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int STAGE = (BM + BN) * ROWB;
   constexpr int A_INS = BM * ROWB / 1024, B_INS = BN * ROWB / 1024;   // DMA instructions per stage
@@ -204,8 +210,8 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
   for (int u = 0; u < PER_WAVE; ++u) {
     constexpr int AU = A_INS / 4;
     const bool isA = u < AU;
-    const int row = ((isA ? u : u - AU) * 4 + wave) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz4(row);
+    const int row = ((isA ? u : u - AU) * 4 + wave) * (1024 / ROWB) + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz_rows<CPR>(row);
     const int grow = (isA ? m0 : n0) + row;
     doff[u] = grow < (isA ? M : N) ? (unsigned)(((size_t)grow * (isA ? lda : ldb) + chunk * 8) * 2)
                                    : (isA ? a_bytes : b_bytes);
@@ -222,25 +228,25 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
   };
 
   // per-lane LDS byte offsets of the MFMA fragments inside one stage
-  int aoff[2][TM], boff[2][TN];
+  int aoff[KK][TM], boff[KK][TN];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < KK; ++kk) {
     const int chunk = 2 * kk + hl;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = wm * WM + i * 32 + l32;
-      aoff[kk][i] = row * ROWB + ((chunk ^ swz4(row)) << 4);
+      aoff[kk][i] = row * ROWB + ((chunk ^ swz_rows<CPR>(row)) << 4);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int row = wn * WN + j * 32 + l32;
-      boff[kk][j] = BM * ROWB + row * ROWB + ((chunk ^ swz4(row)) << 4);
+      boff[kk][j] = BM * ROWB + row * ROWB + ((chunk ^ swz_rows<CPR>(row)) << 4);
     }
   }
-  auto load = [&](int slot, Frag (&fa)[2][TM], Frag (&fb)[2][TN]) {
+  auto load = [&](int slot, Frag (&fa)[KK][TM], Frag (&fb)[KK][TN]) {
     const unsigned char *sbase = smem + slot * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) fa[kk][i] = *reinterpret_cast<const Frag *>(sbase + aoff[kk][i]);
 #pragma unroll
@@ -253,9 +259,9 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
-  auto mma = [&](Frag (&fa)[2][TM], Frag (&fb)[2][TN]) {
+  auto mma = [&](Frag (&fa)[KK][TM], Frag (&fb)[KK][TN]) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -273,19 +279,17 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
   };
 
   const int nk = K / BK;
-  // iteration kt: tile kt + 1 is read into registers while tile kt (already
-  // in registers) is multiplied; tiles up to kt + STAGES - 2 are in flight
-  auto iter = [&](int kt, Frag (&ca)[2][TM], Frag (&cb)[2][TN], Frag (&na)[2][TM],
-                  Frag (&nb)[2][TN]) {
-    if (kt + 1 < nk) {
-      // tile kt + 1 landed: of the tiles issued so far, those after it may fly
-      wait_stages(min(nk, kt + STAGES - 1) - (kt + 2));
-      // every wave's DMA of tile kt + 1 has landed, and every read of the
-      // slot refilled below (tile kt - 1, read during iteration kt - 2) is done
-      lds_barrier();
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-      load((kt + 1) % STAGES, na, nb);
-    }
+  // iteration kt < nk - 1: tile kt + 1 is read into registers while tile kt
+  // (already in registers) is multiplied; tiles up to kt + STAGES - 2 fly
+  auto iter = [&](int kt, Frag (&ca)[KK][TM], Frag (&cb)[KK][TN], Frag (&na)[KK][TM],
+                  Frag (&nb)[KK][TN]) {
+    // tile kt + 1 landed: of the tiles issued so far, those after it may fly
+    wait_stages(min(nk, kt + STAGES - 1) - (kt + 2));
+    // every wave's DMA of tile kt + 1 has landed, and every read of the slot
+    // refilled below (tile kt - 1, read during iteration kt - 2) is done
+    lds_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    load((kt + 1) % STAGES, na, nb);
     mma(ca, cb);
   };
 
@@ -294,11 +298,18 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_dma_kernel(const bf16 *__restr
     if (s0 < nk) issue(s0, s0);
   wait_stages(min(nk, STAGES - 1) - 1);
   lds_barrier();
-  Frag fa0[2][TM], fb0[2][TN], fa1[2][TM], fb1[2][TN];
+  Frag fa0[KK][TM], fb0[KK][TN], fa1[KK][TM], fb1[KK][TN];
   load(0, fa0, fb0);
-  for (int kt = 0; kt < nk; kt += 2) {
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
     iter(kt, fa0, fb0, fa1, fb1);
-    if (kt + 1 < nk) iter(kt + 1, fa1, fb1, fa0, fb0);
+    iter(kt + 1, fa1, fb1, fa0, fb0);
+  }
+  if (kt + 1 < nk) {
+    iter(kt, fa0, fb0, fa1, fb1);
+    mma(fa1, fb1);
+  } else {
+    mma(fa0, fb0);
   }
 
   const bool full = m0 + BM <= M && n0 + BN <= N;   // workgroup-uniform
@@ -376,21 +387,15 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
     // offset (out-of-range ones included) fits the 32-bit buffer range check
     const size_t lim = (1ull << 32) - 2 * (size_t)K;
     if (K % 32 == 0 && (size_t)M * lda * 2 < lim && (size_t)N * ldb * 2 < lim) {
-      // N tile of 128 or 192, whichever finishes sooner counted in rounds of
-      // resident workgroups (2 per CU, 256 CUs), a tile's time being
-      // proportional to its width
-      const long long slots = 512;
-      auto cost = [&](int bn) {
-        const long long t = (long long)((M + 127) / 128) * ((N + bn - 1) / bn);
-        return ((t + slots - 1) / slots) * bn;
-      };
-      if (cost(192) < cost(128)) {
-        const int g192 = ((M + 127) / 128) * ((N + 191) / 192);
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 192, 4>), dim3(g192), dim3(256), 0, stream,
-                           A, B, C, M, N, K, lda, ldb, ldc);
+      // one 256 x 192 tile per CU when that covers the product in a single
+      // round, else 128 x 128 tiles (two workgroups per CU)
+      const int g256 = ((M + 255) / 256) * ((N + 191) / 192);
+      if (g256 >= 224 && g256 <= 256) {
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 256, 192, 32, 5, 1>), dim3(g256), dim3(256), 0,
+                           stream, A, B, C, M, N, K, lda, ldb, ldc);
       } else {
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 128, 5>), dim3(grid), dim3(256), 0, stream,
-                           A, B, C, M, N, K, lda, ldb, ldc);
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 128, 32, 5, 2>), dim3(grid), dim3(256), 0,
+                           stream, A, B, C, M, N, K, lda, ldb, ldc);
       }
       return hipGetLastError();
     }
