@@ -14,6 +14,7 @@ The fp64 oracle is timed on the host cores on a bounded sample of the same
 prefill workload (``cpu_baseline``).
 
     python bench.py [--steps K] [--warmup W] [--prefill WORKLOAD] [--no-cpu]
+    python bench.py --compare     # CCGQA vs full-width MHA / GQA-8 prefill, and a T sweep
 """
 
 from __future__ import annotations
@@ -42,6 +43,9 @@ def parse():
     p.add_argument("--decode", default="ccgqa_decode_b64_l32768")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--compare", action="store_true",
+                   help="prefill of ccgqa_prefill_t16384 next to full-width MHA and GQA-8 baselines "
+                        "through the same kernels, plus a sequence-length sweep (prints its own JSON)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -134,10 +138,83 @@ def cpu_baseline(sp, seconds):
                       f"the workload has {sp.batch}), fp64 NumPy, {el:.1f} s wall"}
 
 
+def compare(args):
+    """The pages' prefill comparison reproduced with this library's kernels:
+    CCGQA (ccgqa_prefill_t16384) against full-width MHA and GQA-8 at the same
+    T, E and head size with the extras off, then a sweep over T.  Context for
+    the pages' own ratios, which they measure on other hardware."""
+    import math
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_amd import cca, tensors as T
+    from synth import COMPARISON_OVERRIDES, COMPARISONS, make_prefill, workload
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    K = max(2, min(args.steps, 5))
+
+    def run(name, sp):
+        P = make_prefill(sp, seed=0)
+        W = P.weights
+        if name in COMPARISONS:
+            for a in (W.q_seq_taps, W.k_seq_taps, W.q_chan_taps, W.k_chan_taps):
+                a[...] = COMPARISON_OVERRIDES["taps"]
+            W.tau = np.full(sp.n_q_heads, 1.0 / math.sqrt(sp.head_dim), dtype=np.float32)
+        pw = upload_weights(cca, T, W, dev)
+        cfg = cca.make_config(sp)
+        x = T.to_device(P.x_s, dev)
+        y = torch.empty_like(x)
+        ws = T.workspace(cca.prefill_workspace_size(cfg), dev)
+        del P
+        for _ in range(2):
+            cca.prefill_forward(cfg, pw, x, y, ws)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for e in ev:
+            e[0].record()
+            cca.prefill_forward(cfg, pw, x, y, ws)
+            e[1].record()
+            cca.stage_attention(cfg, pw, ws)
+            e[2].record()
+        torch.cuda.synchronize()
+        pre = sum(a.elapsed_time(b) for a, b, _ in ev) / K
+        att = sum(b.elapsed_time(c) for _, b, c in ev) / K
+        flops = 2 * 2 * sp.batch * sp.n_q_heads * sp.head_dim * sp.seq_len * (sp.seq_len + 1) / 2
+        r = {"T": sp.seq_len, "E": sp.d_model, "heads": f"{sp.n_q_heads}q/{sp.n_kv_heads}kv x {sp.head_dim}",
+             "prefill_ms": round(pre, 4), "tokens_per_s": round(sp.tokens / (pre * 1e-3), 1),
+             "attention_ms": round(att, 4), "attention_tflops": round(flops / (att * 1e-3) / 1e12, 1)}
+        print(f"[compare] {name} T={sp.seq_len}: prefill {pre:.3f} ms, attention {att:.3f} ms",
+              file=sys.stderr, flush=True)
+        del x, y, ws, pw
+        torch.cuda.empty_cache()
+        return r
+
+    main3 = ["ccgqa_prefill_t16384", "gqa8_prefill_t16384", "mha_prefill_t16384"]
+    res = {n: run(n, workload(n)) for n in main3}
+    base = res["ccgqa_prefill_t16384"]
+    ratios = {f"{n}_over_ccgqa": {"prefill": round(res[n]["prefill_ms"] / base["prefill_ms"], 3),
+                                  "attention": round(res[n]["attention_ms"] / base["attention_ms"], 3)}
+              for n in main3[1:]}
+    sweep = []
+    for n in ("ccgqa_prefill_t16384", "mha_prefill_t16384"):
+        for t in (2048, 4096, 8192):
+            r = run(n, workload(n).with_(seq_len=t))
+            sweep.append(dict(r, shape=n))
+    sweep += [dict(res[n], shape=n) for n in ("ccgqa_prefill_t16384", "mha_prefill_t16384")]
+    print(json.dumps({"comparison": res, "ratios": ratios, "sweep": sweep, "steps": K,
+                      "baselines": "same kernels, extras off (unit taps, no q-k-mean / value-shift / "
+                                   "L2 norm, tau = 1/sqrt(d)); GQA-8 = 8 kv heads"}), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.compare:
+        compare(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "

@@ -6,7 +6,8 @@ draws to the storage precision -- and nothing of the method's arithmetic
 (no projection, convolution, normalisation, rotation or attention).
 """
 
-from .configs import CCAShape, WORKLOADS, workload, shape_from_dict  # noqa: F401
+from .configs import (CCAShape, COMPARISONS, COMPARISON_OVERRIDES, WORKLOADS,  # noqa: F401
+                      shape_from_dict, workload)
 from .generate import (  # noqa: F401
     Prefill,
     Decode,

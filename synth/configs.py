@@ -89,8 +89,28 @@ WORKLOADS = {
 
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Full-width baselines for the prefill comparison against ccgqa_prefill_t16384
+# (same T, E and head size): the same kernels with the extras off, i.e. one
+# unit tap in each convolution, no q-k-mean, value-shift or L2 norm, and a
+# logit scale of 1/sqrt(d) (see COMPARISON_OVERRIDES).  "GQA-8" is read as 8
+# key/value heads shared by the 64 query heads.
+COMPARISONS = {
+    "mha_prefill_t16384": CCAShape(
+        batch=1, seq_len=16384, d_model=4096, n_q_heads=64, n_kv_heads=64, head_dim=64,
+        seq_conv_k=1, chan_conv_k=1, use_qk_mean=0, use_value_shift=0, use_qk_norm=0,
+        rope_base=500000.0, dtype="bf16"),
+    "gqa8_prefill_t16384": CCAShape(
+        batch=1, seq_len=16384, d_model=4096, n_q_heads=64, n_kv_heads=8, head_dim=64,
+        seq_conv_k=1, chan_conv_k=1, use_qk_mean=0, use_value_shift=0, use_qk_norm=0,
+        rope_base=500000.0, dtype="bf16"),
+}
+# Weights the comparison baselines use in place of the drawn ones.
+COMPARISON_OVERRIDES = {"taps": 1.0, "tau": "1/sqrt(d)"}
+
 
 def workload(name_or_index) -> CCAShape:
     if isinstance(name_or_index, int):
         return WORKLOADS[WORKLOAD_ORDER[name_or_index]]
+    if name_or_index in COMPARISONS:
+        return COMPARISONS[name_or_index]
     return WORKLOADS[name_or_index]
