@@ -8,7 +8,7 @@ import re
 
 import pytest
 
-from synth import CCAShape, WORKLOADS
+from synth import COMPARISONS, CCAShape, WORKLOADS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -36,6 +36,16 @@ def test_every_declared_symbol_is_exported(L):
 def test_status_strings(L):
     for s in range(5):
         assert L.status_string(s).startswith("CCA_")
+
+
+@pytest.mark.parametrize("name", list(COMPARISONS))
+def test_comparison_baselines_validate(L, name):
+    """The full-width MHA / GQA-8 baselines of the prefill comparison are
+    shapes the library accepts, and their T sweep too."""
+    for t in (2048, 16384):
+        cfg = L.make_config(COMPARISONS[name].with_(seq_len=t))
+        assert L.validate_config(cfg) == L.CCA_OK
+        assert L.prefill_workspace_size(cfg) > 0
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
