@@ -24,7 +24,7 @@ WS_QKV, WS_Q, WS_K, WS_VT, WS_O, WS_PART, WS_SPLITK, WS_COUNT = range(8)
 # Every entry point declared in include/cca.h.
 EXPORTS = (
     "cca_validate_config", "cca_prefill_workspace_size", "cca_decode_workspace_size",
-    "cca_prefill_forward", "cca_decode_step", "cca_status_string",
+    "cca_prefill_forward", "cca_decode_step", "cca_decode_step_varlen", "cca_status_string",
     "cca_prefill_workspace_layout", "cca_decode_workspace_layout",
     "cca_stage_downproj", "cca_stage_convmix", "cca_stage_attention", "cca_stage_upproj",
     "cca_stage_decode_downproj", "cca_stage_decode_mix", "cca_stage_decode_attention",
@@ -74,6 +74,7 @@ def _load():
         "cca_decode_workspace_layout": (C.c_int, [cfgp, C.c_int32, P(sz)]),
         "cca_prefill_forward": (C.c_int, [cfgp, wp, vp, vp, sp, vp, sz, vp]),
         "cca_decode_step": (C.c_int, [cfgp, wp, vp, C.c_int32, sp, sp, vp, vp, sz, vp]),
+        "cca_decode_step_varlen": (C.c_int, [cfgp, wp, vp, vp, C.c_int32, sp, sp, vp, vp, sz, vp]),
         "cca_status_string": (C.c_char_p, [C.c_int]),
         "cca_stage_downproj": (C.c_int, [cfgp, wp, vp, vp, sz, vp]),
         "cca_stage_convmix": (C.c_int, [cfgp, wp, sp, vp, sz, vp]),
@@ -201,6 +202,16 @@ def decode_step(cfg: Config, w: Weights, x_t, cache_len: int, state_in: State, s
                                C.byref(state_in.struct()), C.byref(state_out.struct()), _ptr(y_t),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(stream)), "cca_decode_step")
+
+
+def decode_step_varlen(cfg: Config, w: Weights, x_t, cache_lens, max_cache_len: int,
+                       state_in: State, state_out: State, y_t, workspace, stream=None):
+    """cache_lens: device int32 tensor [B] of per-sequence cache lengths."""
+    _check(lib.cca_decode_step_varlen(C.byref(cfg), C.byref(w.struct()), _ptr(x_t), _ptr(cache_lens),
+                                      int(max_cache_len), C.byref(state_in.struct()),
+                                      C.byref(state_out.struct()), _ptr(y_t), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)),
+           "cca_decode_step_varlen")
 
 
 def _wsb(ws):

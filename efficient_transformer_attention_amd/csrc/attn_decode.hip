@@ -80,7 +80,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
                                                                const float *__restrict__ tau,
                                                                const bf16 *__restrict__ kc,
                                                                const bf16 *__restrict__ vc, int cap,
-                                                               int Lk, int chunk, int Hq, int Hkv,
+                                                               int Lk, const int *__restrict__ lens,
+                                                               int chunk, int Hq, int Hkv,
                                                                int G, int GH, int nsub, int nch,
                                                                float *__restrict__ part) {
   constexpr int QC = D / 16;                 // contraction chunks of S^T
@@ -123,8 +124,10 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
       }
   }
 
+  // keys of this sequence: lens[b] + 1 (clamped to [1, Lk]) when given
+  const int Lkb = lens ? min(max(lens[b], 0), Lk - 1) + 1 : Lk;
   const int kbeg = c * chunk;
-  const int kend = min(kbeg + chunk, Lk);
+  const int kend = min(kbeg + chunk, Lkb);
   const int ntile = (kend - kbeg + DEC_TILE - 1) / DEC_TILE;
   const bf16 *kb = kc + (size_t)(b * Hkv + g) * cap * D;
   const bf16 *vb = vc + (size_t)(b * Hkv + g) * cap * D;
@@ -289,7 +292,9 @@ __global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__res
                                                               const float *__restrict__ tau,
                                                               const float *__restrict__ kc,
                                                               const float *__restrict__ vc,
-                                                              int cap, int Lk, int chunk, int Hq,
+                                                              int cap, int Lk,
+                                                              const int *__restrict__ lens, int chunk,
+                                                              int Hq,
                                                               int Hkv, int G, int GH, int nsub,
                                                               int nch, float *__restrict__ part) {
   // one thread per (query head, key) score; waves walk the chunk in 256-key steps
@@ -310,7 +315,8 @@ __global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__res
   }
   for (int e = tid; e < GH; e += 256) { mst[e] = -INFINITY; lst[e] = 0.f; }
   __syncthreads();
-  const int kbeg = c * chunk, kend = min(kbeg + chunk, Lk);
+  const int Lkb = lens ? min(max(lens[b], 0), Lk - 1) + 1 : Lk;
+  const int kbeg = c * chunk, kend = min(kbeg + chunk, Lkb);
   const float *kb = kc + (size_t)(b * Hkv + g) * cap * D;
   const float *vb = vc + (size_t)(b * Hkv + g) * cap * D;
   for (int k0 = kbeg; k0 < kend; k0 += 256) {
@@ -399,14 +405,15 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float *_
 
 template <int D>
 static hipError_t dec_bf16(const MixShape &s, const float *q, const bf16 *kc, const bf16 *vc,
-                           int cap, int Lk, const float *tau, float *part, bf16 *o,
-                           hipStream_t stream) {
+                           int cap, int Lk, const int *lens, const float *tau, float *part,
+                           bf16 *o, hipStream_t stream) {
   const int nch = dec_num_chunks(s.B, s.Hkv, Lk);
   const int chunk = dec_chunk_len(Lk, nch);
   const int GH = dec_heads_per_wg(s.G, DecMaxG<D>::value);
   const int nsub = s.G / GH;
   hipLaunchKernelGGL((attn_decode_mfma_kernel<D>), dim3(nch * nsub * s.B * s.Hkv), dim3(256), 0,
-                     stream, q, tau, kc, vc, cap, Lk, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
+                     stream, q, tau, kc, vc, cap, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch,
+                     part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_combine_kernel<bf16, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
@@ -416,14 +423,15 @@ static hipError_t dec_bf16(const MixShape &s, const float *q, const bf16 *kc, co
 
 template <int D>
 static hipError_t dec_f32(const MixShape &s, const float *q, const float *kc, const float *vc,
-                          int cap, int Lk, const float *tau, float *part, float *o,
-                          hipStream_t stream) {
+                          int cap, int Lk, const int *lens, const float *tau, float *part,
+                          float *o, hipStream_t stream) {
   const int nch = dec_num_chunks(s.B, s.Hkv, Lk);
   const int chunk = dec_chunk_len(Lk, nch);
   const int GH = dec_heads_per_wg(s.G, DEC_F32_MAXG);
   const int nsub = s.G / GH;
   hipLaunchKernelGGL((attn_decode_f32_kernel<D>), dim3(nch * nsub * s.B * s.Hkv), dim3(256), 0,
-                     stream, q, tau, kc, vc, cap, Lk, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
+                     stream, q, tau, kc, vc, cap, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch,
+                     part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_combine_kernel<float, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
@@ -434,13 +442,13 @@ static hipError_t dec_f32(const MixShape &s, const float *q, const float *kc, co
 template <>
 hipError_t launch_attention_decode<bf16>(const MixShape &s, const float *q, const bf16 *k_cache,
                                          const bf16 *v_cache, int capacity, int Lk,
-                                         const float *tau, float *part, bf16 *o,
+                                         const int *lens, const float *tau, float *part, bf16 *o,
                                          hipStream_t stream) {
   switch (s.d) {
-    case 16: return dec_bf16<16>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 32: return dec_bf16<32>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 64: return dec_bf16<64>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 128: return dec_bf16<128>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 16: return dec_bf16<16>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
+    case 32: return dec_bf16<32>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
+    case 64: return dec_bf16<64>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
+    case 128: return dec_bf16<128>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -448,13 +456,13 @@ hipError_t launch_attention_decode<bf16>(const MixShape &s, const float *q, cons
 template <>
 hipError_t launch_attention_decode<float>(const MixShape &s, const float *q, const float *k_cache,
                                           const float *v_cache, int capacity, int Lk,
-                                          const float *tau, float *part, float *o,
+                                          const int *lens, const float *tau, float *part, float *o,
                                           hipStream_t stream) {
   switch (s.d) {
-    case 16: return dec_f32<16>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 32: return dec_f32<32>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 64: return dec_f32<64>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
-    case 128: return dec_f32<128>(s, q, k_cache, v_cache, capacity, Lk, tau, part, o, stream);
+    case 16: return dec_f32<16>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
+    case 32: return dec_f32<32>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
+    case 64: return dec_f32<64>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
+    case 128: return dec_f32<128>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -441,8 +441,8 @@ static cca_status dec_downproj(const cca_config &c, const cca_weights *w, const 
 }
 
 static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
-                          const cca_state *si, const cca_state *so, void *ws, const Layout &L,
-                          hipStream_t st) {
+                          const int32_t *lens, const cca_state *si, const cca_state *so, void *ws,
+                          const Layout &L, hipStream_t st) {
   MixShape s = mix_shape(c);
   s.T = 1;
   s.Tp = 1;
@@ -450,14 +450,15 @@ static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
   float *q = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_Q));
   hipError_t e;
   if (c.dtype == CCA_BF16)
-    e = launch_convmix_decode<bf16>(s, taps_of(w), qkv, Lc, state_of(si), state_of(so), q, st);
+    e = launch_convmix_decode<bf16>(s, taps_of(w), qkv, Lc, lens, state_of(si), state_of(so), q, st);
   else
-    e = launch_convmix_decode<float>(s, taps_of(w), qkv, Lc, state_of(si), state_of(so), q, st);
+    e = launch_convmix_decode<float>(s, taps_of(w), qkv, Lc, lens, state_of(si), state_of(so), q, st);
   return check_launch(e, st);
 }
 
 static cca_status dec_attn(const cca_config &c, const cca_weights *w, int32_t Lc,
-                           const cca_state *si, void *ws, const Layout &L, hipStream_t st) {
+                           const int32_t *lens, const cca_state *si, void *ws, const Layout &L,
+                           hipStream_t st) {
   MixShape s = mix_shape(c);
   s.T = 1;
   s.Tp = 1;
@@ -466,11 +467,11 @@ static cca_status dec_attn(const cca_config &c, const cca_weights *w, int32_t Lc
   hipError_t e;
   if (c.dtype == CCA_BF16)
     e = launch_attention_decode<bf16>(s, q, (const bf16 *)si->k_cache, (const bf16 *)si->v_cache,
-                                      si->capacity, Lc + 1, w->tau, part,
+                                      si->capacity, Lc + 1, lens, w->tau, part,
                                       (bf16 *)wsp(ws, L, CCA_WS_O), st);
   else
     e = launch_attention_decode<float>(s, q, (const float *)si->k_cache,
-                                       (const float *)si->v_cache, si->capacity, Lc + 1, w->tau,
+                                       (const float *)si->v_cache, si->capacity, Lc + 1, lens, w->tau,
                                        part, (float *)wsp(ws, L, CCA_WS_O), st);
   return check_launch(e, st);
 }
@@ -485,8 +486,25 @@ cca_status cca_decode_step(const cca_config *cfg, const cca_weights *w, const vo
   CCA_TRY(check_decode_state(c, cache_len, si, so));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CCA_TRY(dec_downproj(c, w, x_t, ws, L, st));
-  CCA_TRY(dec_mix(c, w, cache_len, si, so, ws, L, st));
-  CCA_TRY(dec_attn(c, w, cache_len, si, ws, L, st));
+  CCA_TRY(dec_mix(c, w, cache_len, nullptr, si, so, ws, L, st));
+  CCA_TRY(dec_attn(c, w, cache_len, nullptr, si, ws, L, st));
+  return run_upproj(c, w, y_t, ws, L, c.batch, st);
+}
+
+cca_status cca_decode_step_varlen(const cca_config *cfg, const cca_weights *w, const void *x_t,
+                                  const int32_t *cache_lens, int32_t max_cache_len,
+                                  const cca_state *si, const cca_state *so, void *y_t, void *ws,
+                                  size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(decode_checks(cfg, w, max_cache_len, ws, wsb, &L));
+  if (!x_t || !y_t || !aligned16(x_t) || !aligned16(y_t)) return CCA_ERR_INVALID_ARG;
+  if (!cache_lens || reinterpret_cast<uintptr_t>(cache_lens) % 4) return CCA_ERR_INVALID_ARG;
+  const cca_config c = decode_cfg(cfg);
+  CCA_TRY(check_decode_state(c, max_cache_len, si, so));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CCA_TRY(dec_downproj(c, w, x_t, ws, L, st));
+  CCA_TRY(dec_mix(c, w, max_cache_len, cache_lens, si, so, ws, L, st));
+  CCA_TRY(dec_attn(c, w, max_cache_len, cache_lens, si, ws, L, st));
   return run_upproj(c, w, y_t, ws, L, c.batch, st);
 }
 
@@ -505,7 +523,7 @@ cca_status cca_stage_decode_mix(const cca_config *cfg, const cca_weights *w, int
   CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
   const cca_config c = decode_cfg(cfg);
   CCA_TRY(check_decode_state(c, cache_len, si, so));
-  return dec_mix(c, w, cache_len, si, so, ws, L, reinterpret_cast<hipStream_t>(stream));
+  return dec_mix(c, w, cache_len, nullptr, si, so, ws, L, reinterpret_cast<hipStream_t>(stream));
 }
 
 cca_status cca_stage_decode_attention(const cca_config *cfg, const cca_weights *w,
@@ -515,7 +533,7 @@ cca_status cca_stage_decode_attention(const cca_config *cfg, const cca_weights *
   CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
   const cca_config c = decode_cfg(cfg);
   CCA_TRY(check_decode_state(c, cache_len, si, si));
-  return dec_attn(c, w, cache_len, si, ws, L, reinterpret_cast<hipStream_t>(stream));
+  return dec_attn(c, w, cache_len, nullptr, si, ws, L, reinterpret_cast<hipStream_t>(stream));
 }
 
 cca_status cca_stage_decode_upproj(const cca_config *cfg, const cca_weights *w, int32_t cache_len,

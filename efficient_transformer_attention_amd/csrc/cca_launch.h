@@ -53,13 +53,14 @@ template <typename TQ, typename TV>
 hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
                                   TQ *k, TV *vt, const StateOut &st, hipStream_t stream);
 
-// The same mixing for one new token per sequence at position L, using the
+// The same mixing for one new token per sequence at position L (per
+// sequence lens[b], clamped to [0, L], when lens is not null), using the
 // carried window / vshift of state_in; writes q (fp32 [B,Hq,d]), the k and v
-// rows at cache slot L, and the rolled state into state_out.
+// rows at that cache slot, and the rolled state into state_out.
 template <typename TV>
 hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const float *qkv, int L,
-                                 const StateOut &in, const StateOut &out, float *q,
-                                 hipStream_t stream);
+                                 const int *lens, const StateOut &in, const StateOut &out,
+                                 float *q, hipStream_t stream);
 
 // Causal flash attention inside the latent heads; q holds tau_h * log2(e) *
 // q_hat (the mixing kernel applies the temperature); tau [Hq] (device) bounds
@@ -69,12 +70,14 @@ hipError_t launch_attention_prefill(const MixShape &s, const TQ *q, const TQ *k,
                                     const float *tau, TV *o, hipStream_t stream);
 bool attention_supported(int d, bool f32);
 
-// Split-KV decode attention over Lk = L + 1 cached keys, then the log-sum-exp
-// combine.  part: fp32 scratch of decode_partial_floats() floats.
+// Split-KV decode attention over Lk = L + 1 cached keys (per sequence
+// lens[b] + 1, clamped to [1, Lk], when lens is not null; the chunking
+// follows Lk), then the log-sum-exp combine.  part: fp32 scratch of
+// decode_partial_floats() floats.
 template <typename TV>
 hipError_t launch_attention_decode(const MixShape &s, const float *q, const TV *k_cache,
-                                   const TV *v_cache, int capacity, int Lk, const float *tau,
-                                   float *part, TV *o, hipStream_t stream);
+                                   const TV *v_cache, int capacity, int Lk, const int *lens,
+                                   const float *tau, float *part, TV *o, hipStream_t stream);
 
 // Whether the mixing kernel's LDS tile of one kv group (G query heads + k +
 // v, 19 tokens) fits the 64 KiB it may use.

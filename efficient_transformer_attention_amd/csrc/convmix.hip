@@ -351,13 +351,16 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   }
 }
 
-// One new token per sequence at position L.  One workgroup per (b, g); the
-// 4-row tile holds tokens L-3 .. L: rows from the carried window, the new row
-// from the down-projection.  All state reads finish before the barrier, so
+// One new token per sequence at position L (lens[b] when lens is given,
+// clamped to [0, L]).  One workgroup per (b, g); the 4-row tile holds tokens
+// L-3 .. L: rows from the carried window, the new row from the
+// down-projection.  All state reads finish before the barrier, so
 // state_out may alias state_in.
 template <typename TV, int D>
 __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps w,
-                                                             const float *__restrict__ qkv, int L,
+                                                             const float *__restrict__ qkv,
+                                                             int Lmax,
+                                                             const int *__restrict__ lens,
                                                              StateOut in, StateOut out,
                                                              float *__restrict__ qout) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -369,6 +372,7 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
 
   const int tid = threadIdx.x;
   const int g = blockIdx.x % s.Hkv, b = blockIdx.x / s.Hkv;
+  const int L = lens ? min(max(lens[b], 0), Lmax) : Lmax;   // this sequence's position
   const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
   const int ks1 = s.ks - 1;
   const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
@@ -496,23 +500,24 @@ hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const flo
 
 template <typename TV, int D>
 static hipError_t convmix_decode_d(const MixShape &s, const MixTaps &w, const float *qkv, int L,
+                                   const int *lens,
                                    const StateOut &in, const StateOut &out, float *q,
                                    hipStream_t stream) {
   const size_t lds = mix_lds_bytes(4, s.G, D, 1);
   hipLaunchKernelGGL((convmix_decode_kernel<TV, D>), dim3(s.B * s.Hkv), dim3(256), lds, stream, s,
-                     w, qkv, L, in, out, q);
+                     w, qkv, L, lens, in, out, q);
   return hipGetLastError();
 }
 
 template <typename TV>
 hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const float *qkv, int L,
-                                 const StateOut &in, const StateOut &out, float *q,
+                                 const int *lens, const StateOut &in, const StateOut &out, float *q,
                                  hipStream_t stream) {
   switch (s.d) {
-    case 16: return convmix_decode_d<TV, 16>(s, w, qkv, L, in, out, q, stream);
-    case 32: return convmix_decode_d<TV, 32>(s, w, qkv, L, in, out, q, stream);
-    case 64: return convmix_decode_d<TV, 64>(s, w, qkv, L, in, out, q, stream);
-    case 128: return convmix_decode_d<TV, 128>(s, w, qkv, L, in, out, q, stream);
+    case 16: return convmix_decode_d<TV, 16>(s, w, qkv, L, lens, in, out, q, stream);
+    case 32: return convmix_decode_d<TV, 32>(s, w, qkv, L, lens, in, out, q, stream);
+    case 64: return convmix_decode_d<TV, 64>(s, w, qkv, L, lens, in, out, q, stream);
+    case 128: return convmix_decode_d<TV, 128>(s, w, qkv, L, lens, in, out, q, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -527,10 +532,10 @@ template hipError_t launch_convmix_prefill<float, float>(const MixShape &, const
                                                          const float *, float *, float *, float *,
                                                          const StateOut &, hipStream_t);
 template hipError_t launch_convmix_decode<bf16>(const MixShape &, const MixTaps &, const float *,
-                                                int, const StateOut &, const StateOut &, float *,
+                                                int, const int *, const StateOut &, const StateOut &, float *,
                                                 hipStream_t);
 template hipError_t launch_convmix_decode<float>(const MixShape &, const MixTaps &, const float *,
-                                                 int, const StateOut &, const StateOut &, float *,
+                                                int, const int *, const StateOut &, const StateOut &, float *,
                                                  hipStream_t);
 
 }  // namespace cca

@@ -167,6 +167,25 @@ cca_status cca_decode_step(const cca_config *cfg, const cca_weights *w,
                            void *y_t, void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/* Decode step with a cache length per sequence, for batches whose sequences
+ * sit at different positions (continuous batching) [GS-EN "1. Problem
+ * Statement": the decode-time cache grows per sequence].
+ * cache_lens: device int32 [B]; sequence b's new token is at position
+ *   cache_lens[b], attends to cache slots [0, cache_lens[b]] and is written
+ *   at slot cache_lens[b].  Values are clamped to [0, max_cache_len].
+ * max_cache_len: host bound on the lengths; it sizes the launch and the
+ *   workspace (capacity must exceed it).  The key chunking follows it, so
+ *   with every cache_lens[b] == max_cache_len the result equals
+ *   cca_decode_step(..., max_cache_len, ...) bit for bit.
+ * Everything else as cca_decode_step; workspace: >=
+ * cca_decode_workspace_size(cfg, max_cache_len) bytes.  CCA_ERR_INVALID_ARG
+ * for a null or misaligned cache_lens. */
+cca_status cca_decode_step_varlen(const cca_config *cfg, const cca_weights *w,
+                                  const void *x_t, const int32_t *cache_lens,
+                                  int32_t max_cache_len, const cca_state *state_in,
+                                  const cca_state *state_out, void *y_t, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *cca_status_string(cca_status s);
 

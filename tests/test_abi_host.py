@@ -130,3 +130,21 @@ def test_decode_rejects_before_launch(L):
     assert f(*args(novs, novs)) == L.CCA_ERR_INVALID_ARG
     assert f(*args(good, good, -1)) == L.CCA_ERR_INVALID_ARG
     assert f(*args(good, good, 10, need - 1)) == L.CCA_ERR_WORKSPACE
+
+
+def test_decode_varlen_rejects_before_launch(L):
+    s = CCAShape(batch=2, seq_len=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    cfg = L.make_config(s)
+    need = L.decode_workspace_size(cfg, 10)
+    w = _fake_weights(L)
+    f = L.lib.cca_decode_step_varlen
+    good = L._State(0x30000, 0x40000, 11, 0, 0x50000, 0x60000, 0x70000)
+    full = L._State(0x30000, 0x40000, 10, 0, 0x50000, 0x60000, 0x70000)     # no room for slot 10
+    args = lambda si, lens=0xA0000, L_=10, wsb=need: (C.byref(cfg), C.byref(w), 0x10000, lens, L_,
+                                                      C.byref(si), C.byref(si), 0x20000, 0x100000,
+                                                      wsb, None)
+    assert f(*args(good, None)) == L.CCA_ERR_INVALID_ARG            # no per-sequence lengths
+    assert f(*args(good, 0xA0002)) == L.CCA_ERR_INVALID_ARG         # misaligned int32 array
+    assert f(*args(full)) == L.CCA_ERR_INVALID_ARG                  # capacity <= max_cache_len
+    assert f(*args(good, L_=-1)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(good, wsb=need - 1)) == L.CCA_ERR_WORKSPACE

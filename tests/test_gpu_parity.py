@@ -248,6 +248,67 @@ def test_decode_small_parity(L_):
         np.testing.assert_array_equal(vc[b, :, :L_], D.cache_f64(b, "v"))
 
 
+def test_decode_varlen_parity():
+    """Per-sequence cache lengths: every sequence against the oracle with its
+    own cache prefix, the new rows at its own slot, the rest untouched."""
+    lens = [0, 1, 37, 1024, 2999]
+    Lmax = 3000
+    shape = CCAShape(batch=len(lens), seq_len=1, d_model=256, n_q_heads=8, n_kv_heads=2,
+                     head_dim=64, rope_base=500000.0, cache_len=Lmax)
+    _say(f"[decode varlen] lens={lens}")
+    D = make_decode(shape, seed=11, capacity=Lmax + 3)
+    T, Lb = tens(), lib()
+    st = _upload_decode(D)
+    cfg = Lb.make_config(shape)
+    x_t = T.to_device(D.x_s)
+    y_t = torch.empty_like(x_t)
+    ws = T.workspace(Lb.decode_workspace_size(cfg, Lmax))
+    dl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    Lb.decode_step_varlen(cfg, upload_weights(D.weights), x_t, dl, Lmax, st, st, y_t, ws)
+    torch.cuda.synchronize()
+    w = D.weights.f64()
+    cq, ck, vs = D.state_f64()
+    kc, vc, y = T.to_f64(st.k_cache), T.to_f64(st.v_cache), T.to_f64(y_t)
+    for b, L_ in enumerate(lens):
+        K = D.cache_f64(b, "k")[None, :, :L_]
+        V = D.cache_f64(b, "v")[None, :, :L_]
+        ref, new = O.decode_step(D.x[b:b + 1], w, shape, K, V, cq[b:b + 1], ck[b:b + 1], vs[b:b + 1])
+        assert_parity(y[b:b + 1], ref, "bf16", f"varlen b={b} L={L_}")
+        assert rel_l2(kc[b, :, L_], new["k_new"][0]) < 5e-3
+        assert rel_l2(vc[b, :, L_], new["v_new"][0]) < 5e-3
+        assert rel_l2(T.to_f64(st.conv_q)[b], new["conv_q"][0]) < 5e-3
+        assert rel_l2(T.to_f64(st.vshift)[b], new["vshift"][0]) < 5e-3
+        keep = [i for i in range(Lmax) if i != L_]
+        np.testing.assert_array_equal(kc[b][:, keep], D.cache_f64(b, "k")[:, keep])
+        np.testing.assert_array_equal(vc[b][:, keep], D.cache_f64(b, "v")[:, keep])
+
+
+def test_decode_varlen_uniform_bitwise():
+    """With every length equal, the varlen step is the uniform step, bit for bit."""
+    L_ = 777
+    shape = CCAShape(batch=3, seq_len=1, d_model=256, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                     rope_base=500000.0, cache_len=L_)
+    D = make_decode(shape, seed=12, capacity=L_ + 2)
+    T, Lb = tens(), lib()
+    cfg = Lb.make_config(shape)
+    w = upload_weights(D.weights)
+    x_t = T.to_device(D.x_s)
+    outs = []
+    for varlen in (False, True):
+        st = _upload_decode(D)
+        y_t = torch.empty_like(x_t)
+        ws = T.workspace(Lb.decode_workspace_size(cfg, L_))
+        if varlen:
+            dl = torch.full((shape.batch,), L_, dtype=torch.int32, device="cuda")
+            Lb.decode_step_varlen(cfg, w, x_t, dl, L_, st, st, y_t, ws)
+        else:
+            Lb.decode_step(cfg, w, x_t, L_, st, st, y_t, ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (y_t, st.k_cache, st.v_cache, st.conv_q, st.conv_k, st.vshift)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_decode_f32_validation_mode():
     shape = CCAShape(batch=2, seq_len=1, d_model=128, n_q_heads=4, n_kv_heads=2, head_dim=16,
                      dtype="f32", cache_len=700)
