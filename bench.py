@@ -299,6 +299,23 @@ def main():
     stage_ms = {n: sum(sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(K)) / K
                 for j, n in enumerate(names)}
 
+    # ---- timed region 3: the decode step with per-sequence cache lengths ---
+    # (seeded lengths uniform in [L/2, L]; algorithmic bytes: each sequence's
+    # own K and V rows)
+    rng = np.random.default_rng(1)
+    lens = rng.integers(L // 2, L + 1, size=sd.batch).astype(np.int32)
+    dl = torch.from_numpy(lens).to(dev)
+    cca.decode_step_varlen(dcfg, dw, xt, dl, L, st, st, yt, dws)
+    vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for a, b_ in vev:
+        a.record()
+        cca.decode_step_varlen(dcfg, dw, xt, dl, L, st, st, yt, dws)
+        b_.record()
+    torch.cuda.synchronize()
+    varlen_ms = sum(a.elapsed_time(b_) for a, b_ in vev) / K
+    varlen_bytes = float(sum(2 * sd.n_kv_heads * (int(l) + 1) * sd.head_dim * 2 for l in lens))
+
     alg = algorithmic(sp, sd)
     attn_tflops = alg["attn_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
     conv_gbs = alg["convmix_bytes"] / (stage_ms["convmix"] * 1e-3) / 1e9
@@ -344,6 +361,9 @@ def main():
         "prefill_ms": round(prefill_ms, 4),
         "decode_ms": round(decode_ms, 4),
         "decode_step_hbm_gbs": round(dec_step_gbs, 1),
+        "decode_varlen": {"lengths": f"uniform in [{L // 2}, {L}], seeded", "ms": round(varlen_ms, 4),
+                          "kv_bytes": varlen_bytes,
+                          "step_hbm_gbs": round(varlen_bytes / (varlen_ms * 1e-3) / 1e9, 1)},
         "attn_tflops": round(attn_tflops, 1),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": dict(rooflines[dom_key], kernel=dom_key,
