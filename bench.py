@@ -363,7 +363,8 @@ def main():
         "decode_step_hbm_gbs": round(dec_step_gbs, 1),
         "decode_varlen": {"lengths": f"uniform in [{L // 2}, {L}], seeded", "ms": round(varlen_ms, 4),
                           "kv_bytes": varlen_bytes,
-                          "step_hbm_gbs": round(varlen_bytes / (varlen_ms * 1e-3) / 1e9, 1)},
+                          "step_hbm_gbs": round(varlen_bytes / (varlen_ms * 1e-3) / 1e9, 1),
+                          "attention_traffic": traffic.get("dec_attention_varlen")},
         "attn_tflops": round(attn_tflops, 1),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": dict(rooflines[dom_key], kernel=dom_key,

@@ -75,7 +75,9 @@ __device__ __forceinline__ float exp2_or_zero(float a, float m) {
 // ---------------------------------------------------------------------------
 // bf16 cache: MFMA path
 // ---------------------------------------------------------------------------
-template <int D>
+// VARLEN: the cache length comes per sequence from lens[] (a separate
+// instantiation, so the uniform-length kernel carries no per-sequence load)
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__restrict__ q,
                                                                const float *__restrict__ tau,
                                                                const bf16 *__restrict__ kc,
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   }
 
   // keys of this sequence: lens[b] + 1 (clamped to [1, Lk]) when given
-  const int Lkb = lens ? min(max(lens[b], 0), Lk - 1) + 1 : Lk;
+  const int Lkb = VARLEN ? min(max(lens[b], 0), Lk - 1) + 1 : Lk;
   const int kbeg = c * chunk;
   const int kend = min(kbeg + chunk, Lkb);
   const int ntile = (kend - kbeg + DEC_TILE - 1) / DEC_TILE;
@@ -411,9 +413,14 @@ static hipError_t dec_bf16(const MixShape &s, const float *q, const bf16 *kc, co
   const int chunk = dec_chunk_len(Lk, nch);
   const int GH = dec_heads_per_wg(s.G, DecMaxG<D>::value);
   const int nsub = s.G / GH;
-  hipLaunchKernelGGL((attn_decode_mfma_kernel<D>), dim3(nch * nsub * s.B * s.Hkv), dim3(256), 0,
-                     stream, q, tau, kc, vc, cap, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch,
-                     part);
+  if (lens)
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, true>), dim3(nch * nsub * s.B * s.Hkv), dim3(256),
+                       0, stream, q, tau, kc, vc, cap, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub,
+                       nch, part);
+  else
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, false>), dim3(nch * nsub * s.B * s.Hkv),
+                       dim3(256), 0, stream, q, tau, kc, vc, cap, Lk, lens, chunk, s.Hq, s.Hkv, s.G,
+                       GH, nsub, nch, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_combine_kernel<bf16, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
