@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the CCA / CCGQA forward pass -- TEST INFRASTRUCTURE.
+"""fp64 CPU oracle of the CCA / CCGQA forward and backward pass -- TEST INFRASTRUCTURE.
 
 Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import anything from this package.  The GPU library never
@@ -9,6 +9,8 @@ Modules
 ``cca``    vectorised NumPy oracle (prefill, sampled-row prefill, decode step)
 ``brute``  scalar pure-Python twin for tiny inputs, written separately
            from the same readings, used to pin ``cca``
+``backward``  the derivative of every step of ``cca`` (chain rule, fp64) and
+           the whole prefill backward pass
 
 Every step cites the passage of the pages that defines it.  Page tags:
 

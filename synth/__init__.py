@@ -11,7 +11,9 @@ from .configs import (CCAShape, COMPARISONS, COMPARISON_OVERRIDES, WORKLOADS,  #
 from .generate import (  # noqa: F401
     Prefill,
     Decode,
+    Backward,
     make_prefill,
+    make_upstream_grad,
     make_decode,
     round_to_bf16_bits,
     bf16_bits_to_f64,

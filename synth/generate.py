@@ -12,6 +12,9 @@ error.  Distributions:
 * temperature ``tau_h = sqrt(d)`` (fp32, deterministic)
 * decode only: latent key/value cache, carried convolution window and the
   previous token's value, all ``~ N(0, 1)``.
+* backward only: the upstream gradient ``dy ~ N(0, 1)`` of the layer output,
+  drawn from its own generator (seed + 7919) so the prefill draws above
+  are unchanged.
 
 Draw order (prefill): x, W_q, W_k, W_v, W_o, q seq taps, k seq taps,
 q channel taps, k channel taps.  Decode draws the same list (x is the new
@@ -210,3 +213,17 @@ def make_decode(s: CCAShape, seed: int = 0, capacity: Optional[int] = None,
                   k_cache_s=kc, v_cache_s=vc,
                   conv_q_s=_store(cq, s.dtype)[0], conv_k_s=_store(ck, s.dtype)[0],
                   vshift_s=_store(vs, s.dtype)[0])
+
+
+@dataclass
+class Backward:
+    """Upstream gradient of a prefill's output, for the backward pass."""
+    dy_s: np.ndarray           # [B, T, E] storage
+    dy: np.ndarray             # float64
+
+
+def make_upstream_grad(s: CCAShape, seed: int = 0) -> Backward:
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    dy = rng.standard_normal((s.batch, s.seq_len, s.d_model))
+    dy_s, dy64 = _store(dy, s.dtype)
+    return Backward(dy_s=dy_s, dy=dy64)
