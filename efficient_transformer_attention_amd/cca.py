@@ -1,8 +1,8 @@
 """ctypes binding of libcca (include/cca.h).
 
 Argument marshalling only: torch tensors are passed as device pointers and
-torch's current HIP stream as the stream; every step of the forward pass runs
-in the library's HIP kernels.  There is no fallback: if libcca.so is missing
+torch's current HIP stream as the stream; every step of the forward and
+backward passes runs in the library's HIP kernels.  There is no fallback: if libcca.so is missing
 or a call returns a non-OK status, this module raises.
 """
 
@@ -29,6 +29,7 @@ EXPORTS = (
     "cca_stage_downproj", "cca_stage_convmix", "cca_stage_attention", "cca_stage_upproj",
     "cca_stage_decode_downproj", "cca_stage_decode_mix", "cca_stage_decode_attention",
     "cca_stage_decode_upproj",
+    "cca_train_workspace_size", "cca_prefill_forward_train", "cca_prefill_backward",
 )
 
 
@@ -50,6 +51,12 @@ class Config(C.Structure):
 
 class _Weights(C.Structure):
     _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p),
+                ("q_seq_taps", C.c_void_p), ("k_seq_taps", C.c_void_p),
+                ("q_chan_taps", C.c_void_p), ("k_chan_taps", C.c_void_p), ("tau", C.c_void_p)]
+
+
+class _Grads(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("w_qkv", C.c_void_p), ("w_o", C.c_void_p),
                 ("q_seq_taps", C.c_void_p), ("k_seq_taps", C.c_void_p),
                 ("q_chan_taps", C.c_void_p), ("k_chan_taps", C.c_void_p), ("tau", C.c_void_p)]
 
@@ -84,6 +91,9 @@ def _load():
         "cca_stage_decode_mix": (C.c_int, [cfgp, wp, C.c_int32, sp, sp, vp, sz, vp]),
         "cca_stage_decode_attention": (C.c_int, [cfgp, wp, C.c_int32, sp, vp, sz, vp]),
         "cca_stage_decode_upproj": (C.c_int, [cfgp, wp, C.c_int32, vp, vp, sz, vp]),
+        "cca_train_workspace_size": (sz, [cfgp]),
+        "cca_prefill_forward_train": (C.c_int, [cfgp, wp, vp, vp, vp, sz, vp]),
+        "cca_prefill_backward": (C.c_int, [cfgp, wp, vp, vp, P(_Grads), vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -156,6 +166,24 @@ class State:
     def struct(self) -> _State:
         return _State(_ptr(self.k_cache), _ptr(self.v_cache), int(self.capacity), 0,
                       _ptr(self.conv_q), _ptr(self.conv_k), _ptr(self.vshift))
+
+
+@dataclass
+class Grads:
+    """Device tensors receiving the gradients (see cca_grads in include/cca.h)."""
+    x: object
+    w_qkv: object
+    w_o: object
+    q_seq_taps: object
+    k_seq_taps: object
+    q_chan_taps: object
+    k_chan_taps: object
+    tau: object
+
+    def struct(self) -> _Grads:
+        return _Grads(_ptr(self.x), _ptr(self.w_qkv), _ptr(self.w_o), _ptr(self.q_seq_taps),
+                      _ptr(self.k_seq_taps), _ptr(self.q_chan_taps), _ptr(self.k_chan_taps),
+                      _ptr(self.tau))
 
 
 def _check(status: int, where: str):
@@ -263,3 +291,19 @@ def stage_decode_upproj(cfg, w, cache_len, y_t, workspace, stream=None):
     _check(lib.cca_stage_decode_upproj(C.byref(cfg), C.byref(w.struct()), int(cache_len), _ptr(y_t),
                                        _ptr(workspace), _wsb(workspace), _stream(stream)),
            "cca_stage_decode_upproj")
+
+
+def train_workspace_size(cfg: Config) -> int:
+    return lib.cca_train_workspace_size(C.byref(cfg))
+
+
+def prefill_forward_train(cfg: Config, w: Weights, x, y, workspace, stream=None):
+    _check(lib.cca_prefill_forward_train(C.byref(cfg), C.byref(w.struct()), _ptr(x), _ptr(y),
+                                         _ptr(workspace), _wsb(workspace), _stream(stream)),
+           "cca_prefill_forward_train")
+
+
+def prefill_backward(cfg: Config, w: Weights, x, dy, grads: Grads, workspace, stream=None):
+    _check(lib.cca_prefill_backward(C.byref(cfg), C.byref(w.struct()), _ptr(x), _ptr(dy),
+                                    C.byref(grads.struct()), _ptr(workspace), _wsb(workspace),
+                                    _stream(stream)), "cca_prefill_backward")

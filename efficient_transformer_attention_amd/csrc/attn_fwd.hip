@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
                                                           const TQ *__restrict__ k,
                                                           const TV *__restrict__ vt,
                                                           const float *__restrict__ tau,
-                                                          TV *__restrict__ o, int B, int T, int Tp,
+                                                          TV *__restrict__ o,
+                                                          float *__restrict__ lse, int B, int T, int Tp,
                                                           int Hq, int Hkv, int G, int hq, int nsub,
                                                           int npb, int use_norm) {
   typedef Mfma32<TQ> MQ;
@@ -310,6 +311,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   // each half-wave summed its own keys (and both saw the same rescales)
   l_run += __shfl_xor(l_run, 32, 64);
   if (qpos >= T) return;
+  // log2 of the softmax denominator in the exp2 domain, kept for the backward
+  if (lse && hl == 0) lse[(size_t)(b * Hq + h) * Tp + qpos] = (fixed_shift ? c_h : m_run) + __log2f(l_run);
   const float inv_l = 1.f / l_run;
   TV *orow = o + ((size_t)(b * T + qpos)) * (Hq * D) + h * D;
 #pragma unroll
@@ -336,26 +339,26 @@ static int gcd_int(int a, int b) {
 
 template <typename TQ, typename TV, int D>
 static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
-                         const float *tau, TV *o, hipStream_t stream) {
+                         const float *tau, TV *o, float *lse, hipStream_t stream) {
   const int hq = gcd_int(s.G, 4);
   const int nsub = s.G / hq;
   const int pos_per = 128 / hq;
   const int npb = (s.T + pos_per - 1) / pos_per;
   const int grid = npb * s.B * s.Hkv * nsub;
   hipLaunchKernelGGL((attn_fwd_kernel<TQ, TV, D>), dim3(grid), dim3(256), 0, stream, q, k, vt, tau,
-                     o, s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb, s.use_norm);
+                     o, lse, s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb, s.use_norm);
   return hipGetLastError();
 }
 
 template <typename TQ, typename TV>
 hipError_t launch_attention_prefill(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
-                                    const float *tau, TV *o, hipStream_t stream) {
+                                    const float *tau, TV *o, float *lse, hipStream_t stream) {
   switch (s.d) {
-    case 16: return attn_d<TQ, TV, 16>(s, q, k, vt, tau, o, stream);
-    case 32: return attn_d<TQ, TV, 32>(s, q, k, vt, tau, o, stream);
-    case 64: return attn_d<TQ, TV, 64>(s, q, k, vt, tau, o, stream);
+    case 16: return attn_d<TQ, TV, 16>(s, q, k, vt, tau, o, lse, stream);
+    case 32: return attn_d<TQ, TV, 32>(s, q, k, vt, tau, o, lse, stream);
+    case 64: return attn_d<TQ, TV, 64>(s, q, k, vt, tau, o, lse, stream);
     case 128:
-      if constexpr (AttnTile<TQ, TV, 128>::fits) return attn_d<TQ, TV, 128>(s, q, k, vt, tau, o, stream);
+      if constexpr (AttnTile<TQ, TV, 128>::fits) return attn_d<TQ, TV, 128>(s, q, k, vt, tau, o, lse, stream);
       break;
   }
   return hipErrorInvalidValue;
@@ -367,12 +370,14 @@ bool attention_supported(int d, bool f32) {
 
 template hipError_t launch_attention_prefill<f16, bf16>(const MixShape &, const f16 *, const f16 *,
                                                         const bf16 *, const float *, bf16 *,
-                                                        hipStream_t);
+                                                        float *, hipStream_t);
 template hipError_t launch_attention_prefill<bf16, bf16>(const MixShape &, const bf16 *,
                                                          const bf16 *, const bf16 *,
-                                                         const float *, bf16 *, hipStream_t);
+                                                         const float *, bf16 *, float *,
+                                                         hipStream_t);
 template hipError_t launch_attention_prefill<float, float>(const MixShape &, const float *,
                                                            const float *, const float *,
-                                                           const float *, float *, hipStream_t);
+                                                           const float *, float *, float *,
+                                                           hipStream_t);
 
 }  // namespace cca

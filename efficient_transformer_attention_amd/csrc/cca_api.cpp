@@ -14,6 +14,12 @@
 
 using namespace cca;
 
+#define CCA_TRY(expr)                 \
+  do {                                \
+    cca_status _r = (expr);           \
+    if (_r != CCA_OK) return _r;      \
+  } while (0)
+
 namespace {
 
 constexpr size_t WS_ALIGN = 256;
@@ -151,6 +157,60 @@ Layout decode_layout(const cca_config &c, int cache_len) {
   return L;
 }
 
+// Training workspace: the prefill layout (same offsets), then what the
+// backward pass keeps or builds.  Slots of the backward, in order.
+enum {
+  TR_LSE, TR_DO, TR_DSUM, TR_QT, TR_KT, TR_DOT, TR_VR, TR_GQ, TR_DK, TR_DV, TR_DM, TR_DA, TR_DZ,
+  TR_MIXS, TR_WOT, TR_WQKVT, TR_DYT, TR_OT, TR_DZT, TR_XT, TR_COUNT
+};
+
+struct TrainLayout {
+  Layout pre;
+  size_t off[TR_COUNT];
+  size_t total;
+  int BTp;   // B*T rounded up to 64: contraction length of the weight gradients
+};
+
+TrainLayout train_layout(const cca_config &c) {
+  TrainLayout L;
+  L.pre = prefill_layout(c);
+  const size_t B = c.batch, T = c.seq_len, Tp = padded_T(c.seq_len), d = c.head_dim;
+  const size_t Hq = c.n_q_heads, Hkv = c.n_kv_heads, E = c.d_model;
+  const size_t eq = Hq * d, ekv = Hkv * d, N = eq + 2 * ekv, BT = B * T;
+  const size_t es = elem_size(c.dtype);
+  L.BTp = (int)((BT + 63) / 64 * 64);
+  const size_t BTp = (size_t)L.BTp;
+  const size_t sz[TR_COUNT] = {
+      B * Hq * Tp * 4,            // TR_LSE
+      BT * eq * es,               // TR_DO
+      B * Hq * Tp * 4,            // TR_DSUM
+      B * Hq * d * Tp * es,       // TR_QT
+      B * Hkv * d * Tp * es,      // TR_KT
+      B * Hq * d * Tp * es,       // TR_DOT
+      B * Hkv * Tp * d * es,      // TR_VR
+      BT * eq * 4,                // TR_GQ
+      BT * ekv * 4,               // TR_DK
+      BT * ekv * 4,               // TR_DV
+      BT * (eq + ekv) * 4,        // TR_DM
+      BT * (eq + ekv) * 4,        // TR_DA
+      BT * N * es,                // TR_DZ
+      mix_backward_scratch_floats(mix_shape(c)) * 4,   // TR_MIXS
+      eq * E * es,                // TR_WOT
+      E * N * es,                 // TR_WQKVT
+      E * BTp * es,               // TR_DYT
+      eq * BTp * es,              // TR_OT
+      N * BTp * es,               // TR_DZT
+      E * BTp * es,               // TR_XT
+  };
+  size_t o = L.pre.total;
+  for (int i = 0; i < TR_COUNT; ++i) {
+    L.off[i] = o;
+    o = align_up(o + sz[i], WS_ALIGN);
+  }
+  L.total = o;
+  return L;
+}
+
 // fp32 scratch of the split-contraction GEMM path (decode only).
 float *splitk_ptr(void *ws, const Layout &L, size_t *floats) {
   if (L.off[CCA_WS_SPLITK] == SIZE_MAX) { *floats = 0; return nullptr; }
@@ -238,24 +298,24 @@ cca_status run_convmix(const cca_config &c, const cca_weights *w, const cca_stat
 }
 
 cca_status run_attention(const cca_config &c, const cca_weights *w, void *ws, const Layout &L,
-                         hipStream_t st) {
+                         hipStream_t st, float *lse = nullptr) {
   const MixShape s = mix_shape(c);
   hipError_t e;
   if (c.dtype == CCA_F32) {
     e = launch_attention_prefill<float, float>(s, (const float *)wsp(ws, L, CCA_WS_Q),
                                                (const float *)wsp(ws, L, CCA_WS_K),
                                                (const float *)wsp(ws, L, CCA_WS_VT), w->tau,
-                                               (float *)wsp(ws, L, CCA_WS_O), st);
+                                               (float *)wsp(ws, L, CCA_WS_O), lse, st);
   } else if (qk_is_f16(c)) {
     e = launch_attention_prefill<f16, bf16>(s, (const f16 *)wsp(ws, L, CCA_WS_Q),
                                             (const f16 *)wsp(ws, L, CCA_WS_K),
                                             (const bf16 *)wsp(ws, L, CCA_WS_VT), w->tau,
-                                            (bf16 *)wsp(ws, L, CCA_WS_O), st);
+                                            (bf16 *)wsp(ws, L, CCA_WS_O), lse, st);
   } else {
     e = launch_attention_prefill<bf16, bf16>(s, (const bf16 *)wsp(ws, L, CCA_WS_Q),
                                              (const bf16 *)wsp(ws, L, CCA_WS_K),
                                              (const bf16 *)wsp(ws, L, CCA_WS_VT), w->tau,
-                                             (bf16 *)wsp(ws, L, CCA_WS_O), st);
+                                             (bf16 *)wsp(ws, L, CCA_WS_O), lse, st);
   }
   return check_launch(e, st);
 }
@@ -298,6 +358,80 @@ cca_status check_decode_state(const cca_config &c, int32_t L, const cca_state *s
   if ((long long)c.batch * c.n_kv_heads * si->capacity * c.head_dim > (1ll << 40))
     return CCA_ERR_UNSUPPORTED;
   return CCA_OK;
+}
+
+// ---- backward pass ---------------------------------------------------------
+
+template <typename T> T *trp(void *ws, const TrainLayout &L, int slot) {
+  return reinterpret_cast<T *>(static_cast<unsigned char *>(ws) + L.off[slot]);
+}
+
+template <typename TQ, typename TV>
+cca_status run_backward(const cca_config &c, const cca_weights *w, const void *x, const void *dy,
+                        const cca_grads *gr, void *ws, const TrainLayout &L, hipStream_t st) {
+  const MixShape s = mix_shape(c);
+  const int BT = c.batch * c.seq_len, E = c.d_model, d = c.head_dim;
+  const int eq = c.n_q_heads * d, ekv = c.n_kv_heads * d, N = eq + 2 * ekv;
+  const int BTp = L.BTp;
+  const Layout &P = L.pre;
+  TV *dO = trp<TV>(ws, L, TR_DO);
+  TV *dz = trp<TV>(ws, L, TR_DZ);
+  const TV *O = reinterpret_cast<const TV *>(wsp(ws, P, CCA_WS_O));
+  // up-projection: dO = dy W_o, dW_o = dy^T O (contraction over tokens)
+  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>((const TV *)w->w_o, trp<TV>(ws, L, TR_WOT), E, E,
+                                                   eq, eq, E, st), st));
+  CCA_TRY(check_launch(launch_gemm_nt<TV, TV>((const TV *)dy, trp<TV>(ws, L, TR_WOT), dO, BT, eq, E,
+                                              E, E, eq, st), st));
+  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>((const TV *)dy, trp<TV>(ws, L, TR_DYT), BTp, BT,
+                                                   E, E, BTp, st), st));
+  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>(O, trp<TV>(ws, L, TR_OT), BTp, BT, eq, eq, BTp,
+                                                   st), st));
+  CCA_TRY(check_launch(launch_gemm_nt<TV, float>(trp<TV>(ws, L, TR_DYT), trp<TV>(ws, L, TR_OT),
+                                                 gr->w_o, E, eq, BTp, BTp, BTp, eq, st), st));
+  // attention
+  AttnBwdArgs<TQ, TV> aa;
+  aa.q = reinterpret_cast<const TQ *>(wsp(ws, P, CCA_WS_Q));
+  aa.k = reinterpret_cast<const TQ *>(wsp(ws, P, CCA_WS_K));
+  aa.vt = reinterpret_cast<const TV *>(wsp(ws, P, CCA_WS_VT));
+  aa.O = O;
+  aa.dO = dO;
+  aa.lse = trp<float>(ws, L, TR_LSE);
+  aa.qT = trp<TV>(ws, L, TR_QT);
+  aa.kT = trp<TV>(ws, L, TR_KT);
+  aa.dOT = trp<TV>(ws, L, TR_DOT);
+  aa.vr = trp<TV>(ws, L, TR_VR);
+  aa.dsum = trp<float>(ws, L, TR_DSUM);
+  aa.dk = trp<float>(ws, L, TR_DK);
+  aa.dv = trp<float>(ws, L, TR_DV);
+  aa.gq = trp<float>(ws, L, TR_GQ);
+  CCA_TRY(check_launch(launch_attention_backward<TQ, TV>(s, aa, st), st));
+  // mixing steps
+  MixBwdArgs<TV> ma;
+  ma.qkv = reinterpret_cast<const float *>(wsp(ws, P, CCA_WS_QKV));
+  ma.gq = aa.gq;
+  ma.dk = aa.dk;
+  ma.dv = aa.dv;
+  ma.dm = trp<float>(ws, L, TR_DM);
+  ma.da = trp<float>(ws, L, TR_DA);
+  ma.scratch = trp<float>(ws, L, TR_MIXS);
+  ma.dz = dz;
+  ma.d_tau = gr->tau;
+  ma.d_q_chan = gr->q_chan_taps;
+  ma.d_k_chan = gr->k_chan_taps;
+  ma.d_q_seq = gr->q_seq_taps;
+  ma.d_k_seq = gr->k_seq_taps;
+  CCA_TRY(check_launch(launch_mix_backward<TV>(s, taps_of(w), ma, st), st));
+  // down-projection: dx = dz W_qkv, dW_qkv = dz^T x
+  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>((const TV *)w->w_qkv, trp<TV>(ws, L, TR_WQKVT),
+                                                   N, N, E, E, N, st), st));
+  CCA_TRY(check_launch(launch_gemm_nt<TV, TV>(dz, trp<TV>(ws, L, TR_WQKVT), (TV *)gr->x, BT, E, N,
+                                              N, N, E, st), st));
+  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>(dz, trp<TV>(ws, L, TR_DZT), BTp, BT, N, N, BTp,
+                                                   st), st));
+  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>((const TV *)x, trp<TV>(ws, L, TR_XT), BTp, BT, E,
+                                                   E, BTp, st), st));
+  return check_launch(launch_gemm_nt<TV, float>(trp<TV>(ws, L, TR_DZT), trp<TV>(ws, L, TR_XT),
+                                                gr->w_qkv, N, E, BTp, BTp, BTp, E, st), st);
 }
 
 cca_config decode_cfg(const cca_config *c) {
@@ -352,12 +486,6 @@ cca_status cca_decode_workspace_layout(const cca_config *cfg, int32_t cache_len,
   for (int i = 0; i < CCA_WS_COUNT; ++i) offsets[i] = L.off[i];
   return CCA_OK;
 }
-
-#define CCA_TRY(expr)                 \
-  do {                                \
-    cca_status _r = (expr);           \
-    if (_r != CCA_OK) return _r;      \
-  } while (0)
 
 static cca_status prefill_checks(const cca_config *cfg, const cca_weights *w, void *ws,
                                  size_t wsb, Layout *L) {
@@ -543,6 +671,46 @@ cca_status cca_stage_decode_upproj(const cca_config *cfg, const cca_weights *w, 
   if (!y_t || !aligned16(y_t)) return CCA_ERR_INVALID_ARG;
   const cca_config c = decode_cfg(cfg);
   return run_upproj(c, w, y_t, ws, L, c.batch, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---- training ----------------------------------------------------------------
+
+size_t cca_train_workspace_size(const cca_config *cfg) {
+  if (validate_shape(cfg, true) != CCA_OK) return 0;
+  return train_layout(*cfg).total;
+}
+
+cca_status cca_prefill_forward_train(const cca_config *cfg, const cca_weights *w, const void *x,
+                                     void *y, void *ws, size_t wsb, void *stream) {
+  CCA_TRY(validate_shape(cfg, true));
+  CCA_TRY(check_weights(w));
+  const TrainLayout TL = train_layout(*cfg);
+  CCA_TRY(check_ws(ws, wsb, TL.total));
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return CCA_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Layout &L = TL.pre;
+  CCA_TRY(run_downproj(*cfg, w, x, ws, L, st));
+  CCA_TRY(run_convmix(*cfg, w, nullptr, ws, L, st));
+  CCA_TRY(run_attention(*cfg, w, ws, L, st, trp<float>(ws, TL, TR_LSE)));
+  return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
+}
+
+cca_status cca_prefill_backward(const cca_config *cfg, const cca_weights *w, const void *x,
+                                const void *dy, const cca_grads *g, void *ws, size_t wsb,
+                                void *stream) {
+  CCA_TRY(validate_shape(cfg, true));
+  CCA_TRY(check_weights(w));
+  const TrainLayout TL = train_layout(*cfg);
+  CCA_TRY(check_ws(ws, wsb, TL.total));
+  if (!x || !dy || !aligned16(x) || !aligned16(dy)) return CCA_ERR_INVALID_ARG;
+  if (!g || !g->x || !g->w_qkv || !g->w_o || !g->q_seq_taps || !g->k_seq_taps ||
+      !g->q_chan_taps || !g->k_chan_taps || !g->tau)
+    return CCA_ERR_INVALID_ARG;
+  if (!aligned16(g->x) || !aligned16(g->w_qkv) || !aligned16(g->w_o)) return CCA_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (cfg->dtype == CCA_F32) return run_backward<float, float>(*cfg, w, x, dy, g, ws, TL, st);
+  if (qk_is_f16(*cfg)) return run_backward<f16, bf16>(*cfg, w, x, dy, g, ws, TL, st);
+  return run_backward<bf16, bf16>(*cfg, w, x, dy, g, ws, TL, st);
 }
 
 }  // extern "C"

@@ -188,4 +188,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return base + slot;
 }
 
+// cos and sin of the RoPE angle pos * theta (theta = base^(-2i/d), evaluated
+// on the host in double precision); the angle is formed and reduced mod 2*pi
+// in double precision, so large positions keep fp32-accurate rotations.
+__device__ __forceinline__ float2 rope_cs_theta(int pos, double theta, float base) {
+  if (base == 0.f) return make_float2(1.f, 0.f);
+  const double phi = (double)pos * theta;
+  const double TWO_PI_HI = 6.283185307179586;        // nearest double to 2*pi
+  const double TWO_PI_LO = 2.4492935982947064e-16;   // 2*pi - TWO_PI_HI
+  const double n = rint(phi * (1.0 / TWO_PI_HI));
+  double r = fma(-n, TWO_PI_HI, phi);
+  r = fma(-n, TWO_PI_LO, r);
+  // |r| <= pi after the double-precision reduction: the hardware sin/cos
+  // (v_sin_f32 / v_cos_f32) are accurate to a few ulp there
+  const float rf = (float)r;
+  return make_float2(__cosf(rf), __sinf(rf));
+}
+
 }  // namespace cca

@@ -64,10 +64,12 @@ hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const floa
 
 // Causal flash attention inside the latent heads; q holds tau_h * log2(e) *
 // q_hat (the mixing kernel applies the temperature); tau [Hq] (device) bounds
-// the logits when the L2 norm is on.  o [B*T, Hq*d] in TV.
+// the logits when the L2 norm is on.  o [B*T, Hq*d] in TV.  lse (nullable):
+// fp32 [B, Hq, Tp], log2 of each query's softmax denominator in the exp2
+// domain (rows t < T), for the backward pass.
 template <typename TQ, typename TV>
 hipError_t launch_attention_prefill(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
-                                    const float *tau, TV *o, hipStream_t stream);
+                                    const float *tau, TV *o, float *lse, hipStream_t stream);
 bool attention_supported(int d, bool f32);
 
 // Split-KV decode attention over Lk = L + 1 cached keys (per sequence
@@ -87,5 +89,47 @@ bool convmix_fits(int G, int d);
 // partial-state scratch it needs.
 int decode_chunk_keys(int d);
 size_t decode_partial_floats(int B, int Hq, int Hkv, int d, int Lk);
+
+// ---- backward pass ---------------------------------------------------------
+
+// Buffers of the attention backward.  Inputs: q, k (the forward's attention
+// operands, [B,H,Tp,d]), vt ([B,Hkv,d,Tp], token-permuted), O and dO
+// ([B*T, Hq*d]), lse ([B,Hq,Tp], exp2 domain).  Scratch it fills first: qT,
+// dOT [B,Hq,d,Tp] and kT [B,Hkv,d,Tp] (token-permuted), vr [B,Hkv,Tp,d],
+// dsum [B,Hq,Tp].  Outputs (fp32, token-major): gq [B*T, Hq*d] =
+// sum_u ds k_hat (tau not applied), dk and dv [B*T, Hkv*d].
+template <typename TQ, typename TV> struct AttnBwdArgs {
+  const TQ *q, *k;
+  const TV *vt, *O, *dO;
+  const float *lse;
+  TV *qT, *kT, *dOT, *vr;
+  float *dsum, *dk, *dv, *gq;
+};
+template <typename TQ, typename TV>
+hipError_t launch_attention_backward(const MixShape &s, const AttnBwdArgs<TQ, TV> &a,
+                                     hipStream_t stream);
+
+// Buffers of the mixing backward.  Inputs: qkv (fp32 down-projection output),
+// gq, dk, dv from the attention backward.  Scratch: dm, da (fp32
+// [B*T, e_q + e_kv]) and mix_backward_scratch_floats() floats.  Outputs: dz
+// ([B*T, e_q + 2 e_kv], the down-projection output's cotangent) and the
+// gradients of tau [Hq], the channel taps [Hq|Hkv, kc] and the sequence taps
+// [e_q|e_kv, ks] (fp32, overwritten).
+template <typename TZ> struct MixBwdArgs {
+  const float *qkv, *gq, *dk, *dv;
+  float *dm, *da, *scratch;
+  TZ *dz;
+  float *d_tau, *d_q_chan, *d_k_chan, *d_q_seq, *d_k_seq;
+};
+size_t mix_backward_scratch_floats(const MixShape &s);
+template <typename TZ>
+hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwdArgs<TZ> &a,
+                               hipStream_t stream);
+
+// out[c * out_rs + r] = in[r * in_rs + c] for r < R, c < C; rows r >= Rvalid
+// read as zero.
+template <typename Tin, typename Tout>
+hipError_t launch_transpose_2d(const Tin *in, Tout *out, int R, int Rvalid, int C, long long in_rs,
+                               long long out_rs, hipStream_t stream);
 
 }  // namespace cca

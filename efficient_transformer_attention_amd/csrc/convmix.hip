@@ -33,20 +33,6 @@ namespace cca {
 
 static constexpr int HALO = 3;   // k_s - 1 for the largest supported k_s = 4
 
-// fp64-accurate rotation by angle pos * theta (theta from rope_theta).
-__device__ __forceinline__ float2 rope_cs_theta(int pos, double theta, float base) {
-  if (base == 0.f) return make_float2(1.f, 0.f);
-  const double phi = (double)pos * theta;
-  const double TWO_PI_HI = 6.283185307179586;        // nearest double to 2*pi
-  const double TWO_PI_LO = 2.4492935982947064e-16;   // 2*pi - TWO_PI_HI
-  const double n = rint(phi * (1.0 / TWO_PI_HI));
-  double r = fma(-n, TWO_PI_HI, phi);
-  r = fma(-n, TWO_PI_LO, r);
-  // |r| <= pi after the double-precision reduction: the hardware sin/cos
-  // (v_sin_f32 / v_cos_f32) are accurate to a few ulp there
-  const float rf = (float)r;
-  return make_float2(__cosf(rf), __sinf(rf));
-}
 
 
 template <typename T> struct Store4;

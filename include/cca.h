@@ -186,6 +186,56 @@ cca_status cca_decode_step_varlen(const cca_config *cfg, const cca_weights *w,
                                   const cca_state *state_out, void *y_t, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Training: the forward pass keeping what its backward pass needs, and the
+ * backward pass [GS-EN "3. Key Contributions": CCA speeds up training as
+ * well as inference; the gradients are the derivative of the forward pass
+ * defined above, step by step in reverse order].
+ * ---------------------------------------------------------------------- */
+
+/* Gradients of sum(dy * y) for one cca_prefill_forward_train call.  All are
+ * written (overwritten, never accumulated) by cca_prefill_backward.
+ * x: [B, T, E] in cfg.dtype.  w_qkv [e_q + 2*e_kv, E] and w_o [E, e_q]: fp32.
+ * q_seq_taps [e_q, k_s], k_seq_taps [e_kv, k_s], q_chan_taps [H_q, k_c],
+ * k_chan_taps [H_kv, k_c], tau [H_q]: fp32.  x, w_qkv and w_o 16-byte
+ * aligned. */
+typedef struct {
+  void *x;
+  float *w_qkv;
+  float *w_o;
+  float *q_seq_taps;
+  float *k_seq_taps;
+  float *q_chan_taps;
+  float *k_chan_taps;
+  float *tau;
+} cca_grads;
+
+/* Bytes of device workspace the two training calls need (0 if cfg is
+ * invalid).  Its first cca_prefill_workspace_size(cfg) bytes have the
+ * prefill layout.  Host-only. */
+size_t cca_train_workspace_size(const cca_config *cfg);
+
+/* Forward pass of a training step: y = the prefill of x, as
+ * cca_prefill_forward (no decode state), and in the workspace the
+ * activations the backward pass reads: the down-projection output, the
+ * attention operands and output, and the log2 of every query's softmax
+ * denominator.  workspace: >= cca_train_workspace_size(cfg) bytes,
+ * 256-byte aligned. */
+cca_status cca_prefill_forward_train(const cca_config *cfg, const cca_weights *w, const void *x,
+                                     void *y, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* Backward pass: given dy [B, T, E] (cfg.dtype), the cotangent of the y of
+ * the cca_prefill_forward_train call that last wrote `workspace` with the
+ * same cfg, w and x, writes every gradient of *g.  The workspace must hold
+ * that call's activations (stream order; nothing else may write it in
+ * between); its backward scratch is overwritten.  Argument errors as for
+ * the forward; a null member of g is CCA_ERR_INVALID_ARG.  Deterministic:
+ * no atomics, fixed summation orders. */
+cca_status cca_prefill_backward(const cca_config *cfg, const cca_weights *w, const void *x,
+                                const void *dy, const cca_grads *g, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *cca_status_string(cca_status s);
 

@@ -148,3 +148,39 @@ def test_decode_varlen_rejects_before_launch(L):
     assert f(*args(full)) == L.CCA_ERR_INVALID_ARG                  # capacity <= max_cache_len
     assert f(*args(good, L_=-1)) == L.CCA_ERR_INVALID_ARG
     assert f(*args(good, wsb=need - 1)) == L.CCA_ERR_WORKSPACE
+
+
+def test_train_workspace_extends_prefill_layout(L):
+    for s in (WORKLOADS["cca_prefill_b4_t2048"], CCAShape(batch=1, seq_len=7, d_model=16,
+                                                          n_q_heads=2, n_kv_heads=2, head_dim=16)):
+        cfg = L.make_config(s)
+        assert L.train_workspace_size(cfg) > L.prefill_workspace_size(cfg) > 0
+    bad = L.make_config(CCAShape(batch=1, seq_len=7, d_model=16, n_q_heads=3, n_kv_heads=2,
+                                 head_dim=16))
+    assert L.train_workspace_size(bad) == 0
+
+
+def test_backward_rejects_before_launch(L):
+    s = CCAShape(batch=2, seq_len=33, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    cfg = L.make_config(s)
+    need = L.train_workspace_size(cfg)
+    w = _fake_weights(L)
+    f = L.lib.cca_prefill_backward
+    good = L._Grads(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 0x70000, 0x80000)
+    args = lambda g, wsb=need, ws=0x100000, x=0xA0000, dy=0xB0000: (
+        C.byref(cfg), C.byref(w), x, dy, g if g is None else C.byref(g), ws, wsb, None)
+    assert f(*args(None)) == L.CCA_ERR_INVALID_ARG                      # no gradient struct
+    for i in range(8):                                                   # each member required
+        fields = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 0x70000, 0x80000]
+        fields[i] = 0
+        assert f(*args(L._Grads(*fields))) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(L._Grads(0x10008, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 0x70000,
+                            0x80000))) == L.CCA_ERR_INVALID_ARG          # misaligned dx
+    assert f(*args(good, x=0xA0004)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(good, dy=0)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(good, wsb=need - 1)) == L.CCA_ERR_WORKSPACE
+    assert f(*args(good, ws=0x100040)) == L.CCA_ERR_WORKSPACE            # not 256-byte aligned
+    ft = L.lib.cca_prefill_forward_train
+    assert ft(C.byref(cfg), C.byref(w), 0xA0000, 0xB0000, 0x100000, need - 1, None) == \
+        L.CCA_ERR_WORKSPACE
+    assert ft(C.byref(cfg), None, 0xA0000, 0xB0000, 0x100000, need, None) == L.CCA_ERR_INVALID_ARG
