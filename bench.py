@@ -10,8 +10,10 @@ Prints ONE JSON line.  ``value`` is prefill tokens per second of prefill time;
 the decode step's HBM rate and the attention kernel's MFMA rate are reported
 next to it.  A second timed pass launches the same kernels stage by stage
 with HIP events between them to get per-kernel durations for the roofline.
-The fp64 oracle is timed on the host cores on a bounded sample of the same
-prefill workload (``cpu_baseline``).
+A fourth pass times a training step on the prefill workload
+(``cca_prefill_forward_train`` + ``cca_prefill_backward``, reported under
+``train``).  The fp64 oracle is timed on the host cores on a bounded sample
+of the same prefill workload (``cpu_baseline``).
 
     python bench.py [--steps K] [--warmup W] [--prefill WORKLOAD] [--no-cpu]
     python bench.py --compare     # CCGQA vs full-width MHA / GQA-8 prefill, and a T sweep
@@ -136,6 +138,51 @@ def cpu_baseline(sp, seconds):
             "sample": f"{done} passes over one sequence of the prefill workload "
                       f"(T={one.seq_len}, E={one.d_model}, {one.n_q_heads}x{one.head_dim} heads; "
                       f"the workload has {sp.batch}), fp64 NumPy, {el:.1f} s wall"}
+
+
+def training_step(cca, T, sp, pcfg, pw, x, dev, K):
+    """forward_train + backward on the prefill workload, timed with HIP events."""
+    import torch
+    from synth import make_upstream_grad
+    dy = T.to_device(make_upstream_grad(sp, seed=0).dy_s, dev)
+    y = torch.empty_like(x)
+    tws = T.workspace(cca.train_workspace_size(pcfg), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = cca.Grads(torch.empty_like(x), torch.empty((sp.n_qkv, sp.d_model), **f32),
+                  torch.empty((sp.d_model, sp.e_q), **f32), torch.empty((sp.e_q, sp.seq_conv_k), **f32),
+                  torch.empty((sp.e_kv, sp.seq_conv_k), **f32),
+                  torch.empty((sp.n_q_heads, sp.chan_conv_k), **f32),
+                  torch.empty((sp.n_kv_heads, sp.chan_conv_k), **f32),
+                  torch.empty((sp.n_q_heads,), **f32))
+    for _ in range(2):
+        cca.prefill_forward_train(pcfg, pw, x, y, tws)
+        cca.prefill_backward(pcfg, pw, x, dy, g, tws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for e in ev:
+        e[0].record()
+        cca.prefill_forward_train(pcfg, pw, x, y, tws)
+        e[1].record()
+        cca.prefill_backward(pcfg, pw, x, dy, g, tws)
+        e[2].record()
+    torch.cuda.synchronize()
+    fwd = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    bwd = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    print(f"[bench] training step: forward {fwd:.3f} ms backward {bwd:.3f} ms", file=sys.stderr,
+          flush=True)
+    B, Tn, d, H = sp.batch, sp.seq_len, sp.head_dim, sp.n_q_heads
+    pairs = B * H * Tn * (Tn + 1) / 2
+    del tws, g, dy, y
+    torch.cuda.empty_cache()
+    return {"workload": "the prefill workload above, forward_train + backward, seeded dy ~ N(0,1)",
+            "forward_ms": round(fwd, 4), "backward_ms": round(bwd, 4),
+            "step_ms": round(fwd + bwd, 4),
+            "tokens_per_s": round(sp.tokens / ((fwd + bwd) * 1e-3), 1),
+            "backward_over_forward": round(bwd / fwd, 3),
+            # algorithmic flops of the backward: 5 matmuls of 2d flops per visible
+            # pair (S recomputed, dP, dV, dQ, dK) plus the 4 gradient GEMMs
+            "backward_gflop": round((5 * 2 * d * pairs + 2 * 2 * sp.tokens * sp.d_model * (sp.n_qkv + sp.e_q))
+                                    / 1e9, 2)}
 
 
 def compare(args):
@@ -316,6 +363,11 @@ def main():
     varlen_ms = sum(a.elapsed_time(b_) for a, b_ in vev) / K
     varlen_bytes = float(sum(2 * sd.n_kv_heads * (int(l) + 1) * sd.head_dim * 2 for l in lens))
 
+    # ---- timed region 4: a training step on the prefill workload ----------
+    # forward_train (the forward keeping its activations) then the backward
+    # pass with a seeded upstream gradient; every gradient is computed
+    train = training_step(cca, T, sp, pcfg, pw, x, dev, K)
+
     alg = algorithmic(sp, sd)
     attn_tflops = alg["attn_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
     conv_gbs = alg["convmix_bytes"] / (stage_ms["convmix"] * 1e-3) / 1e9
@@ -365,6 +417,7 @@ def main():
                           "kv_bytes": varlen_bytes,
                           "step_hbm_gbs": round(varlen_bytes / (varlen_ms * 1e-3) / 1e9, 1),
                           "attention_traffic": traffic.get("dec_attention_varlen")},
+        "train": train,
         "attn_tflops": round(attn_tflops, 1),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": dict(rooflines[dom_key], kernel=dom_key,

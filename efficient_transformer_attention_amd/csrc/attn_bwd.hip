@@ -40,29 +40,63 @@ namespace cca {
 
 // out[z][c'][r'] = in[z][r][c] for r < R, c < C, with r' = vt_perm(r) when
 // perm_r (else r) and c' = vt_perm(c) when perm_c; rows r >= Rvalid read as
-// zero.  z = z1 * nz2 + z2 selects the strides of both sides.
+// zero.  z = z1 * nz2 + z2 selects the strides of both sides.  64 x 64 tiles
+// through LDS; with VEC-aligned sizes and strides (VEC = 16 bytes of
+// elements) every global access is a 16-byte vector, else element-wise.
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void transpose_kernel(const Tin *__restrict__ in,
                                                         Tout *__restrict__ out, int R, int Rvalid,
                                                         int C, long long in_rs, long long in_bs1,
                                                         long long in_bs2, long long out_rs,
                                                         long long out_bs1, long long out_bs2,
-                                                        int nz2, int perm_r, int perm_c) {
-  __shared__ float tile[64][65];
+                                                        int nz2, int perm_r, int perm_c, int vec) {
+  static_assert(sizeof(Tin) == sizeof(Tout), "same element size on both sides");
+  constexpr int VEC = 16 / (int)sizeof(Tout);
+  constexpr int PAD = VEC;                      // rows offset by 16 bytes
+  __shared__ __attribute__((aligned(16))) Tout tile[64][64 + PAD];
   const int z = blockIdx.z, z1 = z / nz2, z2 = z % nz2;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const Tin *src = in + z1 * in_bs1 + z2 * in_bs2;
   Tout *dst = out + z1 * out_bs1 + z2 * out_bs2;
+  if (vec) {
+    for (int e = threadIdx.x; e < 64 * 64 / VEC; e += 256) {
+      const int r = e / (64 / VEC), cv = (e % (64 / VEC)) * VEC, gr = r0 + r, gc = c0 + cv;
+      Tout v[VEC];
+      if (gr < Rvalid && gr < R && gc < C) {
+        const u32x4 raw = ld16(src + gr * in_rs + gc);
+        const Tin *iv = reinterpret_cast<const Tin *>(&raw);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) v[k] = from_f32<Tout>(to_f32(iv[k]));
+      } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) v[k] = from_f32<Tout>(0.f);
+      }
+      st16(&tile[r][cv], *reinterpret_cast<const u32x4 *>(v));
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64 / VEC; e += 256) {
+      const int oc = e / (64 / VEC), rv = (e % (64 / VEC)) * VEC;
+      const int gc = c0 + oc;                    // output row (before the column permutation)
+      if (gc >= C || r0 + rv >= R) continue;
+      const int tc = perm_c ? vt_perm(oc) : oc;  // tile column that lands in output row c0 + oc
+      Tout v[VEC];
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) v[k] = tile[perm_r ? vt_perm(rv + k) : rv + k][tc];
+      st16(dst + gc * out_rs + r0 + rv, *reinterpret_cast<const u32x4 *>(v));
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int r = e / 64, c = e % 64, gr = r0 + r, gc = c0 + c;
-    tile[r][c] = (gr < Rvalid && gr < R && gc < C) ? to_f32(src[gr * in_rs + gc]) : 0.f;
+    tile[r][c] = (gr < Rvalid && gr < R && gc < C) ? from_f32<Tout>(to_f32(src[gr * in_rs + gc]))
+                                                   : from_f32<Tout>(0.f);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int c = e / 64, r = e % 64, gr = r0 + r, gc = c0 + c;
     if (gr < R && gc < C) {
       const int orr = perm_r ? vt_perm(gr) : gr, occ = perm_c ? vt_perm(gc) : gc;
-      dst[occ * out_rs + orr] = from_f32<Tout>(tile[r][c]);
+      dst[occ * out_rs + orr] = tile[r][c];
     }
   }
 }
@@ -73,28 +107,48 @@ hipError_t launch_transpose(const Tin *in, Tout *out, int R, int Rvalid, int C, 
                             long long out_bs1, long long out_bs2, int nz1, int nz2, int perm_r,
                             int perm_c, hipStream_t stream) {
   if (R <= 0 || C <= 0 || nz1 * nz2 <= 0) return hipSuccess;
+  constexpr int VEC = 16 / (int)sizeof(Tout);
+  // the permutations act inside aligned groups of 16, which the 64-tiles keep whole
+  const bool vec = (reinterpret_cast<uintptr_t>(in) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(out) % 16 == 0) && R % VEC == 0 && C % VEC == 0 &&
+                   in_rs % VEC == 0 && in_bs1 % VEC == 0 && in_bs2 % VEC == 0 &&
+                   out_rs % VEC == 0 && out_bs1 % VEC == 0 && out_bs2 % VEC == 0 &&
+                   (!perm_r || R % 16 == 0) && (!perm_c || C % 16 == 0);
   dim3 grid((C + 63) / 64, (R + 63) / 64, nz1 * nz2);
   hipLaunchKernelGGL((transpose_kernel<Tin, Tout>), grid, dim3(256), 0, stream, in, out, R, Rvalid,
-                     C, in_rs, in_bs1, in_bs2, out_rs, out_bs1, out_bs2, nz2, perm_r, perm_c);
+                     C, in_rs, in_bs1, in_bs2, out_rs, out_bs1, out_bs2, nz2, perm_r, perm_c,
+                     vec ? 1 : 0);
   return hipGetLastError();
 }
 
 // dsum[b, h, t] = <do[b, t, h], o[b, t, h]> for t < T, 0 for T <= t < Tp.
-template <typename TV>
+// LPR lanes share a row (16 bytes each, then a lane reduction); rows are
+// walked token-major, the order of the [B*T, Hq*d] buffers.
+template <typename TV, int D>
 __global__ __launch_bounds__(256) void attn_bwd_rowdot_kernel(const TV *__restrict__ dO,
                                                               const TV *__restrict__ O,
                                                               float *__restrict__ dsum, int B,
-                                                              int T, int Tp, int Hq, int D) {
+                                                              int T, int Tp, int Hq) {
+  constexpr int VEC = 16 / (int)sizeof(TV), LPR = D / VEC;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)B * Hq * Tp) return;
-  const int t = (int)(i % Tp);
-  const int h = (int)((i / Tp) % Hq), b = (int)(i / ((long long)Tp * Hq));
+  const long long row = i / LPR;                 // (b, t, h), t < Tp
+  const int part = (int)(i % LPR);
+  const bool ok = row < (long long)B * Tp * Hq;
+  const int h = (int)(row % Hq);
+  const int t = (int)((row / Hq) % Tp);
+  const int b = (int)(row / ((long long)Hq * Tp));
   float acc = 0.f;
-  if (t < T) {
-    const size_t off = ((size_t)b * T + t) * (size_t)(Hq * D) + (size_t)h * D;
-    for (int dd = 0; dd < D; ++dd) acc += to_f32(dO[off + dd]) * to_f32(O[off + dd]);
+  if (ok && t < T) {
+    const size_t off = ((size_t)b * T + t) * (size_t)(Hq * D) + (size_t)h * D + part * VEC;
+    const u32x4 a = ld16(dO + off), c = ld16(O + off);
+    const TV *av = reinterpret_cast<const TV *>(&a);
+    const TV *cv = reinterpret_cast<const TV *>(&c);
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc += to_f32(av[k]) * to_f32(cv[k]);
   }
-  dsum[i] = acc;
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (ok && part == 0) dsum[((size_t)b * Hq + h) * Tp + t] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -527,9 +581,10 @@ static hipError_t attn_bwd_d(const MixShape &s, const AttnBwdArgs<TQ, TV> &a, hi
                                (long long)D * s.Tp, D, (long long)s.Hkv * s.Tp * D,
                                (long long)s.Tp * D, s.B, s.Hkv, 0, 1, stream);
   if (e != hipSuccess) return e;
-  const long long nrow = (long long)s.B * s.Hq * s.Tp;
-  hipLaunchKernelGGL((attn_bwd_rowdot_kernel<TV>), dim3((unsigned)((nrow + 255) / 256)), dim3(256),
-                     0, stream, a.dO, a.O, a.dsum, s.B, s.T, s.Tp, s.Hq, D);
+  constexpr int LPR = D * (int)sizeof(TV) / 16;
+  const long long nthr = (long long)s.B * s.Hq * s.Tp * LPR;
+  hipLaunchKernelGGL((attn_bwd_rowdot_kernel<TV, D>), dim3((unsigned)((nthr + 255) / 256)),
+                     dim3(256), 0, stream, a.dO, a.O, a.dsum, s.B, s.T, s.Tp, s.Hq);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkb = (s.T + 127) / 128;

@@ -20,7 +20,7 @@
 //    the norms segment reductions.  It writes dm (the mixed q/k cotangent)
 //    and da (the sequence conv output's cotangent), plus per-(token, head)
 //    partial sums of the channel-tap and temperature gradients.
-//  * channel pass: one thread per (channel, 64-token run) combines the
+//  * channel pass: one thread per (channel, 16-token run) combines the
 //    sequence-conv transpose (reads da at t .. t+k_s-1), the q-k-mean skip
 //    terms and the value-shift into dz, the cotangent of the down-projection
 //    output, and accumulates its sequence-tap gradient over the run.
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
 }
 
 // Tokens per thread of the channel pass.
-static constexpr int MIX_BWD_TB = 64;
+static constexpr int MIX_BWD_TB = 16;
 
 template <typename TZ>
 __global__ __launch_bounds__(256) void mix_bwd_chan_kernel(MixShape s, MixTaps w,
@@ -223,11 +223,19 @@ __global__ __launch_bounds__(256) void mix_bwd_chan_kernel(MixShape s, MixTaps w
       ws[j] = j < s.ks ? seqw[j] : 0.f;
       dws[j] = 0.f;
     }
+    // rolling windows: dwin[j] = da[t + j], uwin[j] = u[t - j] (zero outside [0, T))
+    float dwin[4], uwin[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dwin[j] = (j < s.ks && tbeg + j < s.T) ? da[(rb + tbeg + j) * wcols + c] : 0.f;
+      uwin[j] = (j < s.ks && tbeg - j >= 0) ? qkv[(rb + tbeg - j) * N + c] : 0.f;
+    }
     for (int t = tbeg; t < tend; ++t) {
+      const float nxt_d = (t + s.ks < s.T) ? da[(rb + t + s.ks) * wcols + c] : 0.f;
+      const float nxt_u = (t + 1 < s.T) ? qkv[(rb + t + 1) * N + c] : 0.f;
       float acc = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < s.ks && t + j < s.T) acc += ws[j] * da[(rb + t + j) * wcols + c];
+      for (int j = 0; j < 4; ++j) acc += ws[j] * dwin[j];
       if (s.use_mean) {
         const float *dmr = dm + (rb + t) * wcols;
         if (is_q) {
@@ -239,10 +247,18 @@ __global__ __launch_bounds__(256) void mix_bwd_chan_kernel(MixShape s, MixTaps w
         }
       }
       dz[(rb + t) * N + c] = from_f32<TZ>(acc);
-      const float dat = da[(rb + t) * wcols + c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dws[j] += dwin[0] * uwin[j];
+      // slide: window entries j >= ks stay zero (their taps are zero too)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dwin[j] = dwin[j + 1];
+      dwin[3] = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (j < s.ks && t - j >= 0) dws[j] += dat * qkv[(rb + t - j) * N + c];
+        if (j == s.ks - 1) dwin[j] = nxt_d;
+#pragma unroll
+      for (int j = 3; j > 0; --j) uwin[j] = uwin[j - 1];
+      uwin[0] = nxt_u;
     }
     float *dst = seq_part + ((size_t)b * ntb + tb) * wcols * s.ks + (size_t)c * s.ks;
     for (int j = 0; j < s.ks; ++j) dst[j] = dws[j];
@@ -257,48 +273,49 @@ __global__ __launch_bounds__(256) void mix_bwd_chan_kernel(MixShape s, MixTaps w
   }
 }
 
-// part[rb][c] = sum of in[r][c] over rows r of block rb (rows_per_block rows).
-__global__ __launch_bounds__(256) void colsum_partial_kernel(const float *__restrict__ in,
-                                                             long long R, int C,
-                                                             int rows_per_block,
-                                                             float *__restrict__ part) {
+// out[rb * ncols + j] = sum of in[r * C + col0 + j] over the rows r of row
+// block rb (rows_per_block rows), j < ncols: 64 columns per workgroup, four
+// row phases reduced through LDS; fixed order, so the sums are deterministic.
+__global__ __launch_bounds__(256) void colsum_kernel(const float *__restrict__ in, long long R,
+                                                     int C, int col0, int ncols,
+                                                     int rows_per_block, float *__restrict__ out) {
   __shared__ float red[4][64];
   const int cl = threadIdx.x % 64, rs = threadIdx.x / 64;
-  const int c = blockIdx.x * 64 + cl;
+  const int j = blockIdx.x * 64 + cl;
   const long long r0 = (long long)blockIdx.y * rows_per_block;
   const long long r1 = min(R, r0 + rows_per_block);
   float acc = 0.f;
-  if (c < C)
-    for (long long r = r0 + rs; r < r1; r += 4) acc += in[r * C + c];
+  if (j < ncols)
+    for (long long r = r0 + rs; r < r1; r += 4) acc += in[r * C + col0 + j];
   red[rs][cl] = acc;
   __syncthreads();
-  if (rs == 0 && c < C)
-    part[(size_t)blockIdx.y * C + c] = red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl];
+  if (rs == 0 && j < ncols)
+    out[(size_t)blockIdx.y * ncols + j] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
 }
 
-// out[j] = sum_r part[r][col0 + j], j < ncols.
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restrict__ part,
-                                                           int nrows, int C, int col0, int ncols,
-                                                           float *__restrict__ out) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= ncols) return;
-  float acc = 0.f;
-  for (int r = 0; r < nrows; ++r) acc += part[(size_t)r * C + col0 + j];
-  out[j] = acc;
+// Column sums of in [R][C] (columns col0 .. col0 + ncols) into out[ncols]:
+// blocks of 64 rows, then one block over the block sums.
+static hipError_t colsum(const float *in, long long R, int C, int col0, int ncols, float *blk,
+                         float *out, hipStream_t stream) {
+  const unsigned cb = (unsigned)((ncols + 63) / 64);
+  const long long nblk = (R + 63) / 64;
+  hipLaunchKernelGGL(colsum_kernel, dim3(cb, (unsigned)nblk), dim3(256), 0, stream, in, R, C, col0,
+                     ncols, 64, blk);
+  hipLaunchKernelGGL(colsum_kernel, dim3(cb, 1), dim3(256), 0, stream, blk, nblk, ncols, 0, ncols,
+                     (int)nblk, out);
+  return hipGetLastError();
 }
-
-static constexpr int COLSUM_ROWS = 256;
 
 size_t mix_backward_scratch_floats(const MixShape &s) {
   const size_t BT = (size_t)s.B * s.T;
   const int H = s.Hq + s.Hkv;
   const int ntb = (s.T + MIX_BWD_TB - 1) / MIX_BWD_TB;
-  const size_t tau_rows = BT, chan_cols = (size_t)H * s.kc;
-  const size_t nblk = (BT + COLSUM_ROWS - 1) / COLSUM_ROWS;
   const size_t wcols = (size_t)(s.Hq + s.Hkv) * s.d;
-  // tau partials, channel-tap partials, their column-sum blocks, seq-tap partials
-  return tau_rows * s.Hq + BT * chan_cols + nblk * (s.Hq + chan_cols) +
-         (size_t)s.B * ntb * wcols * s.ks;
+  const size_t seq_rows = (size_t)s.B * ntb, seq_cols = wcols * s.ks;
+  const size_t blk = ((BT + 63) / 64) * (size_t)(H * s.kc > s.Hq ? H * s.kc : s.Hq);
+  const size_t blk_seq = ((seq_rows + 63) / 64) * seq_cols;
+  // tau partials, channel-tap partials, seq-tap partials, row-block sums
+  return BT * s.Hq + BT * H * s.kc + seq_rows * seq_cols + (blk > blk_seq ? blk : blk_seq);
 }
 
 template <typename TZ>
@@ -312,12 +329,11 @@ hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwd
   const int H = s.Hq + s.Hkv;
   const int ntb = (s.T + MIX_BWD_TB - 1) / MIX_BWD_TB;
   const int wcols = (s.Hq + s.Hkv) * s.d, N = wcols + s.Hkv * s.d;
+  const int eq = s.Hq * s.d, ekv = s.Hkv * s.d;
   float *tau_part = a.scratch;
   float *chan_part = tau_part + BT * s.Hq;
-  const size_t nblk = (BT + COLSUM_ROWS - 1) / COLSUM_ROWS;
-  float *blk_tau = chan_part + BT * H * s.kc;
-  float *blk_chan = blk_tau + nblk * s.Hq;
-  float *seq_part = blk_chan + nblk * H * s.kc;
+  float *seq_part = chan_part + BT * H * s.kc;
+  float *blk = seq_part + (size_t)s.B * ntb * wcols * s.ks;
 
   switch (s.d) {
     case 16: hipLaunchKernelGGL((mix_bwd_head_kernel<16>), dim3(nwg), dim3(256), 0, stream, s, w, a.qkv, a.gq, a.dk, a.dm, a.da, tau_part, chan_part); break;
@@ -332,25 +348,15 @@ hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwd
                      stream, s, w, a.qkv, a.dm, a.da, a.dv, a.dz, seq_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // temperature: [BT][Hq]; channel taps: [BT][H * kc]
-  hipLaunchKernelGGL(colsum_partial_kernel, dim3((s.Hq + 63) / 64, (unsigned)nblk), dim3(256), 0,
-                     stream, tau_part, (long long)BT, s.Hq, COLSUM_ROWS, blk_tau);
-  hipLaunchKernelGGL(colsum_partial_kernel, dim3((H * s.kc + 63) / 64, (unsigned)nblk), dim3(256),
-                     0, stream, chan_part, (long long)BT, H * s.kc, COLSUM_ROWS, blk_chan);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((s.Hq + 255) / 256), dim3(256), 0, stream, blk_tau,
-                     (int)nblk, s.Hq, 0, s.Hq, a.d_tau);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((s.Hq * s.kc + 255) / 256), dim3(256), 0, stream,
-                     blk_chan, (int)nblk, H * s.kc, 0, s.Hq * s.kc, a.d_q_chan);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((s.Hkv * s.kc + 255) / 256), dim3(256), 0, stream,
-                     blk_chan, (int)nblk, H * s.kc, s.Hq * s.kc, s.Hkv * s.kc, a.d_k_chan);
-  const int eq = s.Hq * s.d, ekv = s.Hkv * s.d;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((eq * s.ks + 255) / 256), dim3(256), 0, stream,
-                     seq_part, s.B * ntb, wcols * s.ks, 0, eq * s.ks, a.d_q_seq);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((ekv * s.ks + 255) / 256), dim3(256), 0, stream,
-                     seq_part, s.B * ntb, wcols * s.ks, eq * s.ks, ekv * s.ks, a.d_k_seq);
-  return hipGetLastError();
+  // temperature [BT][Hq]; channel taps [BT][H * kc] (q heads, then k heads);
+  // sequence taps [B * ntb][(e_q + e_kv) * ks] (q channels, then k channels).
+  // The row-block scratch is reused: each colsum finishes before the next
+  // one starts on the same stream.
+  if ((e = colsum(tau_part, (long long)BT, s.Hq, 0, s.Hq, blk, a.d_tau, stream)) != hipSuccess) return e;
+  if ((e = colsum(chan_part, (long long)BT, H * s.kc, 0, s.Hq * s.kc, blk, a.d_q_chan, stream)) != hipSuccess) return e;
+  if ((e = colsum(chan_part, (long long)BT, H * s.kc, s.Hq * s.kc, s.Hkv * s.kc, blk, a.d_k_chan, stream)) != hipSuccess) return e;
+  if ((e = colsum(seq_part, (long long)s.B * ntb, wcols * s.ks, 0, eq * s.ks, blk, a.d_q_seq, stream)) != hipSuccess) return e;
+  return colsum(seq_part, (long long)s.B * ntb, wcols * s.ks, eq * s.ks, ekv * s.ks, blk, a.d_k_seq, stream);
 }
 
 template hipError_t launch_mix_backward<bf16>(const MixShape &, const MixTaps &,
