@@ -28,6 +28,8 @@
 //    MFMA k-slot run are contiguous in LDS.
 //  * p and ds enter their MFMAs as the value type (bf16: fp32 range, so small
 //    gradients do not underflow); the logits keep the forward's q/k type.
+#include <type_traits>
+
 #include "cca_device.h"
 #include "cca_launch.h"
 
@@ -556,6 +558,371 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// d = 64 with 16-bit operands: the same two products with the streamed tiles
+// moved HBM -> LDS by buffer_load ... lds (no register staging) through a
+// ring of stages of 64 tokens, one barrier per stage.  Every tile row is 128
+// bytes (64 elements), stored with the 16-byte chunk swizzle swz_key(row, 8);
+// DMA instruction u of wave w fills 1 KiB chunk 4u + w of the stage, and
+// each lane fetches the global chunk the swizzle places at its slot.
+// ---------------------------------------------------------------------------
+
+// the LDS bytes of the 16-byte piece starting at element `col` of row `row`
+__device__ __forceinline__ int tile_off(int row, int col) { return row * 128 + swz(row, col * 2, 8); }
+
+template <typename TQ, typename TV>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_dma_kernel(
+    const TQ *__restrict__ q, const TQ *__restrict__ k, const TV *__restrict__ vr,
+    const TV *__restrict__ qT, const TV *__restrict__ dO, const TV *__restrict__ dOT,
+    const float *__restrict__ lse, const float *__restrict__ dsum, float *__restrict__ dk,
+    float *__restrict__ dv, int B, int T, int Tp, int Hq, int Hkv, int G, int nkb) {
+  typedef Mfma32<TQ> MQ;
+  typedef Mfma32<TV> MV;
+  static_assert(MQ::KS == 8 && MV::KS == 8, "16-bit operands");
+  constexpr int D = 64, TILE = 64 * 128;
+  constexpr int OFF_QT = TILE, OFF_DO = 2 * TILE, OFF_DOT = 3 * TILE, OFF_LD = 4 * TILE;
+  constexpr int STAGE = 4 * TILE + 1024, NBUF = 4;
+  constexpr int PER_WAVE = 9;              // 8 tile instructions + 1 for lse / dsum
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int rest = B * Hkv;
+  const int kb = blockIdx.x / rest;                        // low key blocks (most work) first
+  const int g = (blockIdx.x % rest) % Hkv, b = (blockIdx.x % rest) / Hkv;
+  const int kblk0 = kb * 128;
+  const int u0 = kblk0 + 32 * wave;                        // this wave's first key
+  const int eq = Hq * D, ekv = Hkv * D;
+  (void)tid;
+
+  typename MQ::frag kf[4];
+  typename MV::frag vf[4];
+  {
+    const int u = min(u0 + l32, Tp - 1);
+    const TQ *krow = k + ((size_t)(b * Hkv + g) * Tp + u) * D;
+    const TV *vrow = vr + ((size_t)(b * Hkv + g) * Tp + u) * D;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      kf[c] = load_frag<TQ>(krow + c * 16 + hl * 8);
+      vf[c] = load_frag<TV>(vrow + c * 16 + hl * 8);
+    }
+  }
+
+  // buffer resources over the group's G query heads
+  const size_t hq0 = (size_t)b * Hq + (size_t)g * G;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(q + hq0 * Tp * D), 0, (unsigned)((size_t)G * Tp * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rqt = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(qT + hq0 * D * Tp), 0, (unsigned)((size_t)G * D * Tp * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rdo = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(dO + (size_t)b * T * eq + (size_t)g * G * D), 0,
+      (unsigned)((size_t)T * eq * 2 - (size_t)g * G * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rdot = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(dOT + hq0 * D * Tp), 0, (unsigned)((size_t)G * D * Tp * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rld = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((wave < 2 ? lse : dsum) + hq0 * Tp), 0, (unsigned)((size_t)G * Tp * 4), 0x00020000);
+
+  // per-lane static offsets: instruction u covers tile u / 2, rows
+  // ((u % 2) * 4 + wave) * 8 + lane / 8, physical chunk lane % 8
+  unsigned vst[8];
+  int rowv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = ((u & 1) * 4 + wave) * 8 + lane / 8;
+    const int ch = (lane % 8) ^ swz_key(row, 8);
+    const int tile = u >> 1;
+    const unsigned rs = tile == 0 ? 128u : tile == 2 ? (unsigned)eq * 2 : (unsigned)Tp * 2;
+    vst[u] = row * rs + ch * 16;
+    rowv[u] = row;
+  }
+
+  const int ntq = (T - kblk0 + 63) / 64;                   // query stages per head
+  const int nst = ntq * G;
+  auto issue = [&](int it, int slot) {
+    const int hh = it / ntq, t0 = kblk0 + (it % ntq) * 64;
+    unsigned char *sb = smem + slot * STAGE;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tile = u >> 1;
+      lds_void *dst = as_lds(sb + (u * 4 + wave) * 1024);
+      if (tile == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst, 16, (int)(vst[u] + t0 * 128),
+                                                 (unsigned)(hh * Tp * 128), 0, 0);
+      else if (tile == 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rqt, dst, 16, (int)(vst[u] + t0 * 2),
+                                                 (unsigned)(hh * D * Tp * 2), 0, 0);
+      else if (tile == 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rdo, dst, 16, (int)(t0 + rowv[u] < T ? vst[u] + (unsigned)t0 * eq * 2 : 0x7FFFFFF0u),
+            (unsigned)(hh * D * 2), 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rdot, dst, 16, (int)(vst[u] + t0 * 2),
+                                                 (unsigned)(hh * D * Tp * 2), 0, 0);
+    }
+    // lse (waves 0, 1) and dsum (waves 2, 3): 32 floats per wave, lanes 0..7
+    if (lane < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, as_lds(sb + OFF_LD + wave * 128), 16,
+                                               (int)((t0 + 32 * (wave & 1)) * 4 + lane * 16),
+                                               (unsigned)(hh * Tp * 4), 0, 0);
+  };
+
+  f32x16 dvt[2], dkt[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) dvt[i] = dkt[i] = zero16();
+
+  // one 32-query half of a stage
+  auto half = [&](const unsigned char *st, int t0, int sh, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int row = 32 * sh + l32;
+    f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = c * 16 + hl * 8;
+      sacc = MQ::mma(*reinterpret_cast<const typename MQ::frag *>(st + tile_off(row, col)), kf[c], sacc);
+      dpacc = MV::mma(*reinterpret_cast<const typename MV::frag *>(st + OFF_DO + tile_off(row, col)),
+                      vf[c], dpacc);
+    }
+    const float *ld = reinterpret_cast<const float *>(st + OFF_LD);
+    const int u = u0 + l32;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int tr = 32 * sh + 8 * (a >> 2) + 4 * hl + (a & 3);
+      const float p = __builtin_amdgcn_exp2f(sacc[a] - ld[tr]);
+      const float ds = p * (dpacc[a] - ld[64 + tr]);
+      if constexpr (EDGE) {
+        const int t = t0 + tr;
+        const bool ok = t >= u && t < T;
+        sacc[a] = ok ? p : 0.f;
+        dpacc[a] = ok ? ds : 0.f;
+      } else {
+        sacc[a] = p;
+        dpacc[a] = ds;
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = sacc[8 * cc + e];
+        dsv[e] = dpacc[8 * cc + e];
+      }
+      const typename MV::frag pf = pack_frag<TV>(pv), df = pack_frag<TV>(dsv);
+      const int col = 32 * sh + 16 * cc + 8 * hl;          // vt_perm(16 cc + 4 hl) inside the half
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rd = 32 * i + l32;
+        dvt[i] = MV::mma(*reinterpret_cast<const typename MV::frag *>(st + OFF_DOT + tile_off(rd, col)),
+                         pf, dvt[i]);
+        dkt[i] = MV::mma(*reinterpret_cast<const typename MV::frag *>(st + OFF_QT + tile_off(rd, col)),
+                         df, dkt[i]);
+      }
+    }
+  };
+
+  // ring: at the top of stage it, stages it + 1 .. it + 3 may be in flight
+  issue(0, 0);
+  if (nst > 1) issue(1, 1);
+  if (nst > 2) {
+    issue(2, 2);
+    wait_vmcnt<2 * PER_WAVE>();
+  } else if (nst > 1) {
+    wait_vmcnt<PER_WAVE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  for (int it = 0; it < nst; ++it) {
+    // the slot of stage it - 1 is free since the last barrier
+    if (it + 3 < nst) issue(it + 3, (it + 3) % NBUF);
+    const int t0 = kblk0 + (it % ntq) * 64;
+    const unsigned char *st = smem + (it % NBUF) * STAGE;
+    if (u0 < T) {
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const int ts = t0 + 32 * sh;
+        if (ts + 31 < u0) continue;                        // every query before this wave's keys
+        if (ts < u0 + 32 || ts + 31 >= T) half(st, t0, sh, std::true_type{});
+        else half(st, t0, sh, std::false_type{});
+      }
+    }
+    // stage it + 1 landed (this wave's part), then every wave's part
+    if (it + 3 < nst) wait_vmcnt<2 * PER_WAVE>();
+    else if (it + 2 < nst) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+  }
+
+  const int u = u0 + l32;
+  if (u >= T) return;
+  float *dkrow = dk + ((size_t)b * T + u) * ekv + (size_t)g * D;
+  float *dvrow = dv + ((size_t)b * T + u) * ekv + (size_t)g * D;
+  const float ln2 = 0.6931471805599453f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dd = 32 * i + 8 * j + 4 * hl;
+      *reinterpret_cast<f32x4 *>(dkrow + dd) =
+          f32x4{dkt[i][4 * j] * ln2, dkt[i][4 * j + 1] * ln2, dkt[i][4 * j + 2] * ln2,
+                dkt[i][4 * j + 3] * ln2};
+      *reinterpret_cast<f32x4 *>(dvrow + dd) =
+          f32x4{dvt[i][4 * j], dvt[i][4 * j + 1], dvt[i][4 * j + 2], dvt[i][4 * j + 3]};
+    }
+}
+
+template <typename TQ, typename TV>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(
+    const TQ *__restrict__ q, const TQ *__restrict__ k, const TV *__restrict__ kT,
+    const TV *__restrict__ vr, const TV *__restrict__ dO, const float *__restrict__ lse,
+    const float *__restrict__ dsum, float *__restrict__ gq, int B, int T, int Tp, int Hq, int Hkv,
+    int G, int nqb) {
+  typedef Mfma32<TQ> MQ;
+  typedef Mfma32<TV> MV;
+  static_assert(MQ::KS == 8 && MV::KS == 8, "16-bit operands");
+  constexpr int D = 64, TILE = 64 * 128;
+  constexpr int OFF_KT = TILE, OFF_V = 2 * TILE;
+  constexpr int STAGE = 3 * TILE, NBUF = 3;
+  constexpr int PER_WAVE = 6;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * STAGE];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int rest = B * Hq;
+  const int qb = nqb - 1 - blockIdx.x / rest;              // late queries (most keys) first
+  const int h = (blockIdx.x % rest) % Hq, b = (blockIdx.x % rest) / Hq;
+  const int g = h / G;
+  const int t0w = qb * 128 + 32 * wave;
+  const int t = t0w + l32;
+  const int eq = Hq * D;
+
+  typename MQ::frag qf[4];
+  typename MV::frag of[4];
+  {
+    const TQ *qrow = q + ((size_t)(b * Hq + h) * Tp + min(t, Tp - 1)) * D;
+    const TV *orow = dO + ((size_t)b * T + min(t, T - 1)) * eq + (size_t)h * D;
+    const float zz[8] = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qf[c] = load_frag<TQ>(qrow + c * 16 + hl * 8);
+      of[c] = t < T ? load_frag<TV>(orow + c * 16 + hl * 8) : pack_frag<TV>(zz);
+    }
+  }
+  const size_t so = (size_t)(b * Hq + h) * Tp + min(t, Tp - 1);
+  const float lq = t < T ? lse[so] : 0.f;
+  const float dq_sum = t < T ? dsum[so] : 0.f;
+
+  const size_t kv0 = (size_t)b * Hkv + g;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(k + kv0 * Tp * D), 0, (unsigned)((size_t)Tp * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rkt = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(kT + kv0 * D * Tp), 0, (unsigned)((size_t)D * Tp * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(vr + kv0 * Tp * D), 0, (unsigned)((size_t)Tp * D * 2), 0x00020000);
+  unsigned vst[6];
+#pragma unroll
+  for (int u = 0; u < 6; ++u) {
+    const int row = ((u & 1) * 4 + wave) * 8 + lane / 8;
+    const int ch = (lane % 8) ^ swz_key(row, 8);
+    vst[u] = row * ((u >> 1) == 1 ? (unsigned)Tp * 2 : 128u) + ch * 16;
+  }
+  auto issue = [&](int kt, int slot) {
+    const int k0 = kt * 64;
+    unsigned char *sb = smem + slot * STAGE;
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int tile = u >> 1;
+      lds_void *dst = as_lds(sb + (u * 4 + wave) * 1024);
+      if (tile == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, (int)(vst[u] + k0 * 128), 0, 0, 0);
+      else if (tile == 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkt, dst, 16, (int)(vst[u] + k0 * 2), 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, (int)(vst[u] + k0 * 128), 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[2];
+  acc[0] = acc[1] = zero16();
+
+  auto half = [&](const unsigned char *st, int k0, int sh, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int row = 32 * sh + l32;
+    f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = c * 16 + hl * 8;
+      sacc = MQ::mma(*reinterpret_cast<const typename MQ::frag *>(st + tile_off(row, col)), qf[c], sacc);
+      dpacc = MV::mma(*reinterpret_cast<const typename MV::frag *>(st + OFF_V + tile_off(row, col)),
+                      of[c], dpacc);
+    }
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const float p = __builtin_amdgcn_exp2f(sacc[a] - lq);
+      const float ds = p * (dpacc[a] - dq_sum);
+      if constexpr (EDGE) {
+        const int u = k0 + 32 * sh + 8 * (a >> 2) + 4 * hl + (a & 3);
+        dpacc[a] = (u <= t && t < T) ? ds : 0.f;
+      } else {
+        dpacc[a] = ds;
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      float dsv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsv[e] = dpacc[8 * cc + e];
+      const typename MV::frag df = pack_frag<TV>(dsv);
+      const int col = 32 * sh + 16 * cc + 8 * hl;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rd = 32 * i + l32;
+        acc[i] = MV::mma(*reinterpret_cast<const typename MV::frag *>(st + OFF_KT + tile_off(rd, col)),
+                         df, acc[i]);
+      }
+    }
+  };
+
+  const int last = min(qb * 128 + 127, T - 1);
+  const int nkt = last / 64 + 1;
+  issue(0, 0);
+  if (nkt > 1) {
+    issue(1, 1);
+    wait_vmcnt<PER_WAVE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 2 < nkt) issue(kt + 2, (kt + 2) % NBUF);
+    const int k0 = kt * 64;
+    const unsigned char *st = smem + (kt % NBUF) * STAGE;
+    if (t0w < T) {
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const int ks = k0 + 32 * sh;
+        if (ks > t0w + 31) continue;                       // every key after this wave's queries
+        if (ks + 31 > t0w || t0w + 31 >= T) half(st, k0, sh, std::true_type{});
+        else half(st, k0, sh, std::false_type{});
+      }
+    }
+    if (kt + 2 < nkt) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+  }
+
+  if (t >= T) return;
+  float *grow = gq + ((size_t)b * T + t) * eq + (size_t)h * D;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dd = 32 * i + 8 * j + 4 * hl;
+      *reinterpret_cast<f32x4 *>(grow + dd) =
+          f32x4{acc[i][4 * j], acc[i][4 * j + 1], acc[i][4 * j + 2], acc[i][4 * j + 3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -588,6 +955,17 @@ static hipError_t attn_bwd_d(const MixShape &s, const AttnBwdArgs<TQ, TV> &a, hi
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkb = (s.T + 127) / 128;
+  if constexpr (D == 64 && sizeof(TQ) == 2 && sizeof(TV) == 2) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<TQ, TV>), dim3(nkb * s.B * s.Hkv), dim3(256), 0,
+                       stream, a.q, a.k, a.vr, a.qT, a.dO, a.dOT, a.lse, a.dsum, a.dk, a.dv, s.B,
+                       s.T, s.Tp, s.Hq, s.Hkv, s.G, nkb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<TQ, TV>), dim3(nkb * s.B * s.Hq), dim3(256), 0,
+                       stream, a.q, a.k, a.kT, a.vr, a.dO, a.lse, a.dsum, a.gq, s.B, s.T, s.Tp,
+                       s.Hq, s.Hkv, s.G, nkb);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TQ, TV, D>), dim3(nkb * s.B * s.Hkv), dim3(256), 0,
                      stream, a.q, a.k, a.vr, a.qT, a.dO, a.dOT, a.lse, a.dsum, a.dk, a.dv, s.B,
                      s.T, s.Tp, s.Hq, s.Hkv, s.G, nkb);

@@ -161,7 +161,7 @@ Layout decode_layout(const cca_config &c, int cache_len) {
 // backward pass keeps or builds.  Slots of the backward, in order.
 enum {
   TR_LSE, TR_DO, TR_DSUM, TR_QT, TR_KT, TR_DOT, TR_VR, TR_GQ, TR_DK, TR_DV, TR_DM, TR_DA, TR_DZ,
-  TR_MIXS, TR_WOT, TR_WQKVT, TR_DYT, TR_OT, TR_DZT, TR_XT, TR_COUNT
+  TR_MIXS, TR_WOT, TR_WQKVT, TR_DYT, TR_OT, TR_DZT, TR_XT, TR_SPLITK, TR_COUNT
 };
 
 struct TrainLayout {
@@ -170,6 +170,15 @@ struct TrainLayout {
   size_t total;
   int BTp;   // B*T rounded up to 64: contraction length of the weight gradients
 };
+
+// fp32 partials of the two weight-gradient products (contraction over B*T)
+size_t splitk_floats(const cca_config &c, int BTp) {
+  const int E = c.d_model, eq = c.n_q_heads * c.head_dim;
+  const int N = eq + 2 * c.n_kv_heads * c.head_dim;
+  const size_t a = (size_t)gemm_long_k_slices(E, eq, BTp) * E * eq;
+  const size_t b = (size_t)gemm_long_k_slices(N, E, BTp) * N * E;
+  return a > b ? a : b;
+}
 
 TrainLayout train_layout(const cca_config &c) {
   TrainLayout L;
@@ -201,6 +210,7 @@ TrainLayout train_layout(const cca_config &c) {
       eq * BTp * es,              // TR_OT
       N * BTp * es,               // TR_DZT
       E * BTp * es,               // TR_XT
+      splitk_floats(c, (int)BTp) * 4,   // TR_SPLITK
   };
   size_t o = L.pre.total;
   for (int i = 0; i < TR_COUNT; ++i) {
@@ -386,8 +396,10 @@ cca_status run_backward(const cca_config &c, const cca_weights *w, const void *x
                                                    E, E, BTp, st), st));
   CCA_TRY(check_launch(launch_transpose_2d<TV, TV>(O, trp<TV>(ws, L, TR_OT), BTp, BT, eq, eq, BTp,
                                                    st), st));
-  CCA_TRY(check_launch(launch_gemm_nt<TV, float>(trp<TV>(ws, L, TR_DYT), trp<TV>(ws, L, TR_OT),
-                                                 gr->w_o, E, eq, BTp, BTp, BTp, eq, st), st));
+  const size_t skf = splitk_floats(c, BTp);
+  CCA_TRY(check_launch(launch_gemm_nt_long_k<TV>(trp<TV>(ws, L, TR_DYT), trp<TV>(ws, L, TR_OT),
+                                                 gr->w_o, E, eq, BTp, BTp, BTp,
+                                                 trp<float>(ws, L, TR_SPLITK), skf, st), st));
   // attention
   AttnBwdArgs<TQ, TV> aa;
   aa.q = reinterpret_cast<const TQ *>(wsp(ws, P, CCA_WS_Q));
@@ -430,8 +442,9 @@ cca_status run_backward(const cca_config &c, const cca_weights *w, const void *x
                                                    st), st));
   CCA_TRY(check_launch(launch_transpose_2d<TV, TV>((const TV *)x, trp<TV>(ws, L, TR_XT), BTp, BT, E,
                                                    E, BTp, st), st));
-  return check_launch(launch_gemm_nt<TV, float>(trp<TV>(ws, L, TR_DZT), trp<TV>(ws, L, TR_XT),
-                                                gr->w_qkv, N, E, BTp, BTp, BTp, E, st), st);
+  return check_launch(launch_gemm_nt_long_k<TV>(trp<TV>(ws, L, TR_DZT), trp<TV>(ws, L, TR_XT),
+                                                gr->w_qkv, N, E, BTp, BTp, BTp,
+                                                trp<float>(ws, L, TR_SPLITK), skf, st), st);
 }
 
 cca_config decode_cfg(const cca_config *c) {

@@ -163,8 +163,10 @@ __device__ __forceinline__ lds_void *as_lds(void *p) { return (lds_void *)p; }
 // (vmcnt(N)); expcnt and lgkmcnt are left unconstrained.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  // vmcnt is split over bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8)
+  // are set to their maxima
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier for LDS-DMA pipelines: waits for this wave's own LDS

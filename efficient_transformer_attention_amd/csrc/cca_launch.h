@@ -20,6 +20,16 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
 // Contraction slices the skinny path uses for an M x N x K product.
 int gemm_splitk_slices(int M, int N, int K, int elem_bytes);
 
+// C[M,N] (fp32, ldc = N) = A[M,K] * B[N,K]^T for few output tiles and a long
+// contraction (weight gradients): the contraction is split over
+// gemm_long_k_slices() workgroup slices whose fp32 partials go to ws
+// (slices * M * N floats) and are summed in a fixed order; without room in
+// ws it is one plain product.
+int gemm_long_k_slices(int M, int N, int K);
+template <typename Tin>
+hipError_t launch_gemm_nt_long_k(const Tin *A, const Tin *B, float *C, int M, int N, int K, int lda,
+                                 int ldb, float *ws, size_t ws_floats, hipStream_t stream);
+
 // Sizes shared by the mixing and attention kernels.
 struct MixShape {
   int B, T, Tp;            // batch, tokens, tokens padded to the query tile

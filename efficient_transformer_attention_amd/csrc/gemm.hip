@@ -177,7 +177,8 @@ template <typename Tout, int BM, int BN, int BK, int STAGES, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__restrict__ A,
                                                              const bf16 *__restrict__ Bm,
                                                              Tout *__restrict__ C, int M, int N,
-                                                             int K, int lda, int ldb, int ldc) {
+                                                             int K, int lda, int ldb, int ldc,
+                                                             int kchunk) {
   typedef Mfma32<bf16> MF;
   typedef MF::frag Frag;
   constexpr int ROWB = BK * 2, CPR = ROWB / 16, KK = BK / 16;   // row bytes, chunks, k-chunks
@@ -196,6 +197,10 @@ __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__res
   const int ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
   const int lid = xcd_remap(blockIdx.x, ntn * ntm);
   const int m0 = (lid / ntn) * BM, n0 = (lid % ntn) * BN;
+  // split contraction: slice blockIdx.y covers K range [kbeg, kbeg + kchunk)
+  // and writes its own M x ldc block of C
+  const int kbeg = blockIdx.y * kchunk;
+  C += (size_t)blockIdx.y * M * ldc;
 
   const unsigned a_bytes = (unsigned)((size_t)M * lda * 2), b_bytes = (unsigned)((size_t)N * ldb * 2);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, 0x00020000);
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__res
       const bool isA = u < A_INS / 4;
       unsigned char *dst = isA ? base + u * 4096 : base + A_INS * 1024 + (u - A_INS / 4) * 4096;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(dst), 16, (int)doff[u],
-                                               kt * BK * 2, 0, 0);
+                                               (kbeg + kt * BK) * 2, 0, 0);
     }
   };
 
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__res
     wait_vmcnt<0>();
   };
 
-  const int nk = K / BK;
+  const int nk = min(kchunk, K - kbeg) / BK;
   // iteration kt < nk - 1: tile kt + 1 is read into registers while tile kt
   // (already in registers) is multiplied; tiles up to kt + STAGES - 2 fly
   auto iter = [&](int kt, Frag (&ca)[KK][TM], Frag (&cb)[KK][TN], Frag (&na)[KK][TM],
@@ -392,10 +397,10 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
       const int g256 = ((M + 255) / 256) * ((N + 191) / 192);
       if (g256 >= 224 && g256 <= 256) {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 256, 192, 32, 5, 1>), dim3(g256), dim3(256), 0,
-                           stream, A, B, C, M, N, K, lda, ldb, ldc);
+                           stream, A, B, C, M, N, K, lda, ldb, ldc, K);
       } else {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 128, 32, 5, 2>), dim3(grid), dim3(256), 0,
-                           stream, A, B, C, M, N, K, lda, ldb, ldc);
+                           stream, A, B, C, M, N, K, lda, ldb, ldc, K);
       }
       return hipGetLastError();
     }
@@ -405,11 +410,54 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
   return hipGetLastError();
 }
 
+// Contraction slices for a product with few output tiles and a long K (the
+// weight gradients): enough 128 x 128 tiles x slices for one round of two
+// workgroups per CU (more slices only add fp32 partial traffic), slices of
+// at least 1024 elements.
+int gemm_long_k_slices(int M, int N, int K) {
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int S = (512 + tiles - 1) / tiles;
+  const int maxs = K / 1024;
+  if (S > maxs) S = maxs;
+  if (S > 16) S = 16;
+  return S < 1 ? 1 : S;
+}
+
+template <typename Tin>
+hipError_t launch_gemm_nt_long_k(const Tin *A, const Tin *B, float *C, int M, int N, int K, int lda,
+                                 int ldb, float *ws, size_t ws_floats, hipStream_t stream) {
+  const int S = gemm_long_k_slices(M, N, K);
+  if constexpr (sizeof(Tin) == 2) {
+    const size_t lim = (1ull << 32) - 2 * (size_t)K;
+    int kchunk = (K + S - 1) / S;
+    kchunk = (kchunk + 31) / 32 * 32;
+    const int Sused = (K + kchunk - 1) / kchunk;
+    if (S > 1 && K % 32 == 0 && (size_t)M * lda * 2 < lim && (size_t)N * ldb * 2 < lim &&
+        (size_t)Sused * M * N <= ws_floats && (size_t)M * N % 4 == 0) {
+      const int grid = ((M + 127) / 128) * ((N + 127) / 128);
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<float, 128, 128, 32, 5, 2>), dim3(grid, Sused),
+                         dim3(256), 0, stream, A, B, ws, M, N, K, lda, ldb, N, kchunk);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const size_t n = (size_t)M * N;
+      hipLaunchKernelGGL((splitk_reduce_kernel<float>), dim3((unsigned)((n / 4 + 255) / 256)),
+                         dim3(256), 0, stream, ws, C, n, Sused);
+      return hipGetLastError();
+    }
+  }
+  return launch_gemm_nt<Tin, float>(A, B, C, M, N, K, lda, ldb, N, stream);
+}
+
 template hipError_t launch_gemm_nt<bf16, float>(const bf16 *, const bf16 *, float *, int, int, int,
                                                 int, int, int, hipStream_t, float *, size_t);
 template hipError_t launch_gemm_nt<bf16, bf16>(const bf16 *, const bf16 *, bf16 *, int, int, int,
                                                int, int, int, hipStream_t, float *, size_t);
 template hipError_t launch_gemm_nt<float, float>(const float *, const float *, float *, int, int,
                                                  int, int, int, int, hipStream_t, float *, size_t);
+
+template hipError_t launch_gemm_nt_long_k<bf16>(const bf16 *, const bf16 *, float *, int, int, int,
+                                                int, int, float *, size_t, hipStream_t);
+template hipError_t launch_gemm_nt_long_k<float>(const float *, const float *, float *, int, int,
+                                                 int, int, int, float *, size_t, hipStream_t);
 
 }  // namespace cca
