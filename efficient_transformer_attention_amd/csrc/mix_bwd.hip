@@ -58,18 +58,47 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
   const float *chw = is_q ? w.q_chan + (size_t)hh * s.kc : w.k_chan + (size_t)g * s.kc;
   const float *row_t = qkv + ((size_t)b * s.T + t) * N;
 
+  // every global read first, so that they are in flight together: the
+  // k_s pre-conv rows (zero before the sequence start), the skip terms of
+  // q-k-mean, the taps and the incoming cotangent
   float cw[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cw[j] = j < s.kc ? chw[j] : 0.f;
+  for (int j = 0; j < 4; ++j) cw[j] = chw[min(j, s.kc - 1)];
+  float uv[CPL][4], wsv[CPL][4], skip[CPL], gin[CPL];
+#pragma unroll
+  for (int p = 0; p < CPL; ++p) {
+    const int i = li + SEG * p;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uv[p][j] = qkv[((size_t)b * s.T + max(t - j, 0)) * N + colbase + i];
+      wsv[p][j] = seqw[i * s.ks + min(j, s.ks - 1)];
+    }
+    if (is_q) {
+      skip[p] = row_t[eq + g * D + i];
+      gin[p] = gq[((size_t)b * s.T + t) * eq + hh * D + i];
+    } else {
+      float qs = 0.f;
+      for (int h2 = 0; h2 < s.G; ++h2) qs += row_t[(g * s.G + h2) * D + i];
+      skip[p] = qs * (1.f / (float)s.G);
+      gin[p] = dk[((size_t)b * s.T + t) * ekv + g * D + i];
+    }
+  }
+  const float tau_h = is_q ? w.tau[hh] : 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j >= s.kc) cw[j] = 0.f;
+#pragma unroll
+    for (int p = 0; p < CPL; ++p)
+      if (j >= s.ks || t - j < 0) wsv[p][j] = 0.f;
+  }
 
   // channel i of this lane's p-th slot is li + SEG * p
   float a[CPL], m[CPL];
 #pragma unroll
   for (int p = 0; p < CPL; ++p) {
-    const int i = li + SEG * p;
     float acc = 0.f;
-    for (int j = 0; j < s.ks; ++j)
-      if (t - j >= 0) acc += seqw[i * s.ks + j] * qkv[((size_t)b * s.T + t - j) * N + colbase + i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc += wsv[p][j] * uv[p][j];
     a[p] = acc;
   }
   // value of `v` (slots v[0..CPL)) at channel ci of this segment (0 outside [0, D))
@@ -96,15 +125,7 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
     float bb = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) bb += cw[j] * at(a, i - j);
-    if (s.use_mean) {
-      if (is_q) {
-        bb += 0.5f * (row_t[colbase + i] + row_t[eq + g * D + i]);
-      } else {
-        float qs = 0.f;
-        for (int h2 = 0; h2 < s.G; ++h2) qs += row_t[(g * s.G + h2) * D + i];
-        bb += 0.5f * (row_t[colbase + i] + qs * (1.f / (float)s.G));
-      }
-    }
+    if (s.use_mean) bb += 0.5f * (uv[p][0] + skip[p]);
     m[p] = bb;
   }
   float ss = 0.f;
@@ -118,30 +139,22 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
   for (int p = 0; p < CPL; ++p) n[p] = m[p] * inv;
 
   // cotangent of the rotated vector, rotation back, temperature partial
-  float dr[CPL], dn[CPL];
+  float dn[CPL];
   float tau_acc = 0.f;
 #pragma unroll
   for (int p = 0; p < CPL; ++p) {
     const int i = li + SEG * p;
+    const float2 cs = rope_cs_theta(t, s.theta[i >> 1], s.rope_base);
+    const float dr = is_q ? tau_h * gin[p] : gin[p];
     if (is_q) {
-      const float gv = active ? gq[((size_t)b * s.T + t) * eq + hh * D + i] : 0.f;
-      dr[p] = w.tau[hh] * gv;
       // the rotated, normalised q this lane holds: <r, g> summed below
-      const float2 cs = rope_cs_theta(t, s.theta[i >> 1], s.rope_base);
       const float partner = __shfl_xor(n[p], 1, 64);
       const float r = (i & 1) ? partner * cs.y + n[p] * cs.x : n[p] * cs.x - partner * cs.y;
-      tau_acc += r * gv;
-    } else {
-      dr[p] = active ? dk[((size_t)b * s.T + t) * ekv + g * D + i] : 0.f;
+      tau_acc += r * gin[p];
     }
-  }
-#pragma unroll
-  for (int p = 0; p < CPL; ++p) {
-    const int i = li + SEG * p;
-    const float2 cs = rope_cs_theta(t, s.theta[i >> 1], s.rope_base);
-    const float partner = __shfl_xor(dr[p], 1, 64);
+    const float dpartner = __shfl_xor(dr, 1, 64);
     // pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c); transpose: (g0 c + g1 s, -g0 s + g1 c)
-    dn[p] = (i & 1) ? -partner * cs.y + dr[p] * cs.x : dr[p] * cs.x + partner * cs.y;
+    dn[p] = (i & 1) ? -dpartner * cs.y + dr * cs.x : dr * cs.x + dpartner * cs.y;
   }
   const float tau_sum = seg_sum(tau_acc);
 
