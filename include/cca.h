@@ -1,6 +1,6 @@
 /*
  * libcca -- Compressed Convolutional Attention (CCA) and its grouped-query
- * variant (CCGQA), forward pass on AMD Instinct MI355X (gfx950).
+ * variant (CCGQA), forward and backward pass on AMD Instinct MI355X (gfx950).
  *
  * The method (page tags as in the oracle's header):
  *   down-projection of hidden states to a latent q, k, v
