@@ -140,6 +140,42 @@ def cpu_baseline(sp, seconds):
                       f"the workload has {sp.batch}), fp64 NumPy, {el:.1f} s wall"}
 
 
+def paged_decode(cca, T, sd, dcfg, dw, xt, dl, L, st, K, dev, page=256):
+    """cca_decode_step_paged over a paged copy of the decode cache: each
+    sequence's rows cut into `page`-token pages stored in a seeded random
+    order, timed with HIP events."""
+    import numpy as np
+    import torch
+    B, H, cap, d = st.k_cache.shape
+    mpps = (cap + page - 1) // page
+    perm = torch.from_numpy(np.random.default_rng(2).permutation(B * mpps)).to(dev)
+
+    def pages_of(c):
+        padded = torch.zeros((B, H, mpps * page, d), dtype=c.dtype, device=dev)
+        padded[:, :, :cap] = c
+        blocks = padded.view(B, H, mpps, page, d).permute(0, 2, 1, 3, 4).reshape(B * mpps, H, page, d)
+        out = torch.empty_like(blocks)
+        out[perm] = blocks
+        return out
+    kp, vp = pages_of(st.k_cache), pages_of(st.v_cache)
+    table = perm.view(B, mpps).to(torch.int32).contiguous()
+    ps = cca.PagedState(kp, vp, table, page, st.conv_q.clone(), st.conv_k.clone(), st.vshift.clone())
+    yt = torch.empty_like(xt)
+    ws = T.workspace(cca.decode_workspace_size(dcfg, L), dev)
+    cca.decode_step_paged(dcfg, dw, xt, dl, L, ps, ps, yt, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b_ in ev:
+        a.record()
+        cca.decode_step_paged(dcfg, dw, xt, dl, L, ps, ps, yt, ws)
+        b_.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b_) for a, b_ in ev) / K
+    del kp, vp, ps, ws
+    torch.cuda.empty_cache()
+    return ms, page
+
+
 def training_step(cca, T, sp, pcfg, pw, x, dev, K):
     """forward_train + backward on the prefill workload, timed with HIP events."""
     import torch
@@ -363,6 +399,10 @@ def main():
     varlen_ms = sum(a.elapsed_time(b_) for a, b_ in vev) / K
     varlen_bytes = float(sum(2 * sd.n_kv_heads * (int(l) + 1) * sd.head_dim * 2 for l in lens))
 
+    # ---- timed region 3b: the same step on a paged copy of the cache -------
+    # (256-token pages in a seeded random order, the same per-sequence lengths)
+    paged_ms, page = paged_decode(cca, T, sd, dcfg, dw, xt, dl, L, st, K, dev)
+
     # ---- timed region 4: a training step on the prefill workload ----------
     # forward_train (the forward keeping its activations) then the backward
     # pass with a seeded upstream gradient; every gradient is computed
@@ -417,6 +457,9 @@ def main():
                           "kv_bytes": varlen_bytes,
                           "step_hbm_gbs": round(varlen_bytes / (varlen_ms * 1e-3) / 1e9, 1),
                           "attention_traffic": traffic.get("dec_attention_varlen")},
+        "decode_paged": {"page_size": page, "lengths": "as decode_varlen",
+                         "pages": "seeded random order", "ms": round(paged_ms, 4),
+                         "step_hbm_gbs": round(varlen_bytes / (paged_ms * 1e-3) / 1e9, 1)},
         "train": train,
         "attn_tflops": round(attn_tflops, 1),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},

@@ -30,6 +30,7 @@ EXPORTS = (
     "cca_stage_decode_downproj", "cca_stage_decode_mix", "cca_stage_decode_attention",
     "cca_stage_decode_upproj",
     "cca_train_workspace_size", "cca_prefill_forward_train", "cca_prefill_backward",
+    "cca_decode_step_paged", "cca_prefill_forward_paged",
 )
 
 
@@ -67,6 +68,13 @@ class _State(C.Structure):
                 ("vshift", C.c_void_p)]
 
 
+class _PagedState(C.Structure):
+    _fields_ = [("k_pages", C.c_void_p), ("v_pages", C.c_void_p), ("block_table", C.c_void_p),
+                ("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("max_pages_per_seq", C.c_int32), ("reserved", C.c_int32),
+                ("conv_q", C.c_void_p), ("conv_k", C.c_void_p), ("vshift", C.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m efficient_transformer_attention_amd.build`")
@@ -94,6 +102,9 @@ def _load():
         "cca_train_workspace_size": (sz, [cfgp]),
         "cca_prefill_forward_train": (C.c_int, [cfgp, wp, vp, vp, vp, sz, vp]),
         "cca_prefill_backward": (C.c_int, [cfgp, wp, vp, vp, P(_Grads), vp, sz, vp]),
+        "cca_decode_step_paged": (C.c_int, [cfgp, wp, vp, vp, C.c_int32, P(_PagedState),
+                                            P(_PagedState), vp, vp, sz, vp]),
+        "cca_prefill_forward_paged": (C.c_int, [cfgp, wp, vp, vp, P(_PagedState), vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -166,6 +177,25 @@ class State:
     def struct(self) -> _State:
         return _State(_ptr(self.k_cache), _ptr(self.v_cache), int(self.capacity), 0,
                       _ptr(self.conv_q), _ptr(self.conv_k), _ptr(self.vshift))
+
+
+@dataclass
+class PagedState:
+    """Device tensors of a paged decode state (see cca_paged_state in include/cca.h)."""
+    k_pages: object
+    v_pages: object
+    block_table: object
+    page_size: int
+    conv_q: object = None
+    conv_k: object = None
+    vshift: object = None
+
+    def struct(self) -> _PagedState:
+        return _PagedState(_ptr(self.k_pages), _ptr(self.v_pages), _ptr(self.block_table),
+                           int(self.k_pages.shape[0]) if self.k_pages is not None else 0,
+                           int(self.page_size),
+                           int(self.block_table.shape[1]) if self.block_table is not None else 0, 0,
+                           _ptr(self.conv_q), _ptr(self.conv_k), _ptr(self.vshift))
 
 
 @dataclass
@@ -307,3 +337,20 @@ def prefill_backward(cfg: Config, w: Weights, x, dy, grads: Grads, workspace, st
     _check(lib.cca_prefill_backward(C.byref(cfg), C.byref(w.struct()), _ptr(x), _ptr(dy),
                                     C.byref(grads.struct()), _ptr(workspace), _wsb(workspace),
                                     _stream(stream)), "cca_prefill_backward")
+
+
+def decode_step_paged(cfg: Config, w: Weights, x_t, cache_lens, max_cache_len: int,
+                      state_in: PagedState, state_out: PagedState, y_t, workspace, stream=None):
+    """cache_lens: device int32 [B]; the pages and block table live in the states."""
+    _check(lib.cca_decode_step_paged(C.byref(cfg), C.byref(w.struct()), _ptr(x_t), _ptr(cache_lens),
+                                     int(max_cache_len), C.byref(state_in.struct()),
+                                     C.byref(state_out.struct()), _ptr(y_t), _ptr(workspace),
+                                     _wsb(workspace), _stream(stream)), "cca_decode_step_paged")
+
+
+def prefill_forward_paged(cfg: Config, w: Weights, x, y, workspace, state_out: PagedState,
+                          stream=None):
+    _check(lib.cca_prefill_forward_paged(C.byref(cfg), C.byref(w.struct()), _ptr(x), _ptr(y),
+                                         C.byref(state_out.struct()), _ptr(workspace),
+                                         _wsb(workspace), _stream(stream)),
+           "cca_prefill_forward_paged")

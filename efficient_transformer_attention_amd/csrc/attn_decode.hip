@@ -76,12 +76,14 @@ __device__ __forceinline__ float exp2_or_zero(float a, float m) {
 // bf16 cache: MFMA path
 // ---------------------------------------------------------------------------
 // VARLEN: the cache length comes per sequence from lens[] (a separate
-// instantiation, so the uniform-length kernel carries no per-sequence load)
-template <int D, bool VARLEN>
+// instantiation, so the uniform-length kernel carries no per-sequence load).
+// PAGED: cache rows are found through the page table of `cm` (one table
+// lookup per row gather); otherwise cm is contiguous.
+template <int D, bool VARLEN, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__restrict__ q,
                                                                const float *__restrict__ tau,
                                                                const bf16 *__restrict__ kc,
-                                                               const bf16 *__restrict__ vc, int cap,
+                                                               const bf16 *__restrict__ vc, StateOut cm,
                                                                int Lk, const int *__restrict__ lens,
                                                                int chunk, int Hq, int Hkv,
                                                                int G, int GH, int nsub, int nch,
@@ -131,9 +133,14 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   const int kbeg = c * chunk;
   const int kend = min(kbeg + chunk, Lkb);
   const int ntile = (kend - kbeg + DEC_TILE - 1) / DEC_TILE;
-  const bf16 *kb = kc + (size_t)(b * Hkv + g) * cap * D;
-  const bf16 *vb = vc + (size_t)(b * Hkv + g) * cap * D;
+  const bf16 *kb = kc + (size_t)(b * Hkv + g) * cm.capacity * D;
+  const bf16 *vb = vc + (size_t)(b * Hkv + g) * cm.capacity * D;
   unsigned char *myv = smem + wave * TPI * VTILE;
+  // element offset of a cache row: contiguous from this (b, g) base, or paged
+  auto krow_ptr = [&](const bf16 *base_c, const bf16 *pool, int row) {
+    if constexpr (PAGED) return pool + cache_row(cm, b, Hkv, g, row) * D;
+    else return base_c + (size_t)row * D;
+  };
 
   f32x16 acc[ND];
 #pragma unroll
@@ -149,14 +156,15 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
     for (int u = 0; u < TPI; ++u) {
       const int k0 = kbeg + (t0 + u) * DEC_TILE;
       const int krow = min(k0 + l32, kend - 1);
+      const bf16 *kp = krow_ptr(kb, kc, krow);
 #pragma unroll
-      for (int cc = 0; cc < QC; ++cc) kreg[u][cc] = ld16(kb + (size_t)krow * D + 16 * cc + 8 * hl);
+      for (int cc = 0; cc < QC; ++cc) kreg[u][cc] = ld16(kp + 16 * cc + 8 * hl);
 #pragma unroll
       for (int r = 0; r < VPL; ++r) {
         const int e = lane + 64 * r;
         if (e < DEC_TILE * D / 8) {
           const int row = e / (D / 8), seg = e % (D / 8);
-          vreg[u][r] = ld16(vb + (size_t)min(k0 + row, kend - 1) * D + 8 * seg);
+          vreg[u][r] = ld16(krow_ptr(vb, vc, min(k0 + row, kend - 1)) + 8 * seg);
         }
       }
     }
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__res
                                                               const float *__restrict__ tau,
                                                               const float *__restrict__ kc,
                                                               const float *__restrict__ vc,
-                                                              int cap, int Lk,
+                                                              StateOut cm, int Lk,
                                                               const int *__restrict__ lens, int chunk,
                                                               int Hq,
                                                               int Hkv, int G, int GH, int nsub,
@@ -319,15 +327,15 @@ __global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__res
   __syncthreads();
   const int Lkb = lens ? min(max(lens[b], 0), Lk - 1) + 1 : Lk;
   const int kbeg = c * chunk, kend = min(kbeg + chunk, Lkb);
-  const float *kb = kc + (size_t)(b * Hkv + g) * cap * D;
-  const float *vb = vc + (size_t)(b * Hkv + g) * cap * D;
+  auto row_of = [&](int key) { return cache_row(cm, b, Hkv, g, key); };
   for (int k0 = kbeg; k0 < kend; k0 += 256) {
     const int key = k0 + tid;
     for (int hh = 0; hh < GH; ++hh) {
       float s = -INFINITY;
       if (key < kend) {
         s = 0.f;
-        for (int dd = 0; dd < D; ++dd) s = fmaf(qs[hh][dd], kb[(size_t)key * D + dd], s);
+        const float *kr = kc + row_of(key) * D;
+        for (int dd = 0; dd < D; ++dd) s = fmaf(qs[hh][dd], kr[dd], s);
       }
       pbuf[hh][tid] = s;
     }
@@ -351,7 +359,7 @@ __global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__res
       const int hh = e / D, dd = e % D;
       float o = oacc[hh][dd] * alph[hh];
       const int n = min(256, kend - k0);
-      for (int j = 0; j < n; ++j) o = fmaf(pbuf[hh][j], vb[(size_t)(k0 + j) * D + dd], o);
+      for (int j = 0; j < n; ++j) o = fmaf(pbuf[hh][j], vc[row_of(k0 + j) * D + dd], o);
       oacc[hh][dd] = o;
     }
     __syncthreads();
@@ -406,21 +414,25 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float *_
 }
 
 template <int D>
-static hipError_t dec_bf16(const MixShape &s, const float *q, const bf16 *kc, const bf16 *vc,
-                           int cap, int Lk, const int *lens, const float *tau, float *part,
-                           bf16 *o, hipStream_t stream) {
+static hipError_t dec_bf16(const MixShape &s, const float *q, const StateOut &cm, int Lk,
+                           const int *lens, const float *tau, float *part, bf16 *o,
+                           hipStream_t stream) {
   const int nch = dec_num_chunks(s.B, s.Hkv, Lk);
   const int chunk = dec_chunk_len(Lk, nch);
   const int GH = dec_heads_per_wg(s.G, DecMaxG<D>::value);
   const int nsub = s.G / GH;
-  if (lens)
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, true>), dim3(nch * nsub * s.B * s.Hkv), dim3(256),
-                       0, stream, q, tau, kc, vc, cap, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub,
-                       nch, part);
+  const bf16 *kc = reinterpret_cast<const bf16 *>(cm.k_cache);
+  const bf16 *vc = reinterpret_cast<const bf16 *>(cm.v_cache);
+  const dim3 grid(nch * nsub * s.B * s.Hkv);
+  if (cm.table)   // paged caches serve batches of per-sequence lengths
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, true, true>), grid, dim3(256), 0, stream, q, tau,
+                       kc, vc, cm, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
+  else if (lens)
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, true, false>), grid, dim3(256), 0, stream, q,
+                       tau, kc, vc, cm, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
   else
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, false>), dim3(nch * nsub * s.B * s.Hkv),
-                       dim3(256), 0, stream, q, tau, kc, vc, cap, Lk, lens, chunk, s.Hq, s.Hkv, s.G,
-                       GH, nsub, nch, part);
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, false, false>), grid, dim3(256), 0, stream, q,
+                       tau, kc, vc, cm, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_combine_kernel<bf16, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
@@ -429,16 +441,17 @@ static hipError_t dec_bf16(const MixShape &s, const float *q, const bf16 *kc, co
 }
 
 template <int D>
-static hipError_t dec_f32(const MixShape &s, const float *q, const float *kc, const float *vc,
-                          int cap, int Lk, const int *lens, const float *tau, float *part,
-                          float *o, hipStream_t stream) {
+static hipError_t dec_f32(const MixShape &s, const float *q, const StateOut &cm, int Lk,
+                          const int *lens, const float *tau, float *part, float *o,
+                          hipStream_t stream) {
   const int nch = dec_num_chunks(s.B, s.Hkv, Lk);
   const int chunk = dec_chunk_len(Lk, nch);
   const int GH = dec_heads_per_wg(s.G, DEC_F32_MAXG);
   const int nsub = s.G / GH;
   hipLaunchKernelGGL((attn_decode_f32_kernel<D>), dim3(nch * nsub * s.B * s.Hkv), dim3(256), 0,
-                     stream, q, tau, kc, vc, cap, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch,
-                     part);
+                     stream, q, tau, reinterpret_cast<const float *>(cm.k_cache),
+                     reinterpret_cast<const float *>(cm.v_cache), cm, Lk, lens, chunk, s.Hq, s.Hkv,
+                     s.G, GH, nsub, nch, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_combine_kernel<float, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
@@ -447,29 +460,27 @@ static hipError_t dec_f32(const MixShape &s, const float *q, const float *kc, co
 }
 
 template <>
-hipError_t launch_attention_decode<bf16>(const MixShape &s, const float *q, const bf16 *k_cache,
-                                         const bf16 *v_cache, int capacity, int Lk,
-                                         const int *lens, const float *tau, float *part, bf16 *o,
-                                         hipStream_t stream) {
+hipError_t launch_attention_decode<bf16>(const MixShape &s, const float *q, const StateOut &cm,
+                                         int Lk, const int *lens, const float *tau, float *part,
+                                         bf16 *o, hipStream_t stream) {
   switch (s.d) {
-    case 16: return dec_bf16<16>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
-    case 32: return dec_bf16<32>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
-    case 64: return dec_bf16<64>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
-    case 128: return dec_bf16<128>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
+    case 16: return dec_bf16<16>(s, q, cm, Lk, lens, tau, part, o, stream);
+    case 32: return dec_bf16<32>(s, q, cm, Lk, lens, tau, part, o, stream);
+    case 64: return dec_bf16<64>(s, q, cm, Lk, lens, tau, part, o, stream);
+    case 128: return dec_bf16<128>(s, q, cm, Lk, lens, tau, part, o, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <>
-hipError_t launch_attention_decode<float>(const MixShape &s, const float *q, const float *k_cache,
-                                          const float *v_cache, int capacity, int Lk,
-                                          const int *lens, const float *tau, float *part, float *o,
-                                          hipStream_t stream) {
+hipError_t launch_attention_decode<float>(const MixShape &s, const float *q, const StateOut &cm,
+                                          int Lk, const int *lens, const float *tau, float *part,
+                                          float *o, hipStream_t stream) {
   switch (s.d) {
-    case 16: return dec_f32<16>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
-    case 32: return dec_f32<32>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
-    case 64: return dec_f32<64>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
-    case 128: return dec_f32<128>(s, q, k_cache, v_cache, capacity, Lk, lens, tau, part, o, stream);
+    case 16: return dec_f32<16>(s, q, cm, Lk, lens, tau, part, o, stream);
+    case 32: return dec_f32<32>(s, q, cm, Lk, lens, tau, part, o, stream);
+    case 64: return dec_f32<64>(s, q, cm, Lk, lens, tau, part, o, stream);
+    case 128: return dec_f32<128>(s, q, cm, Lk, lens, tau, part, o, stream);
   }
   return hipErrorInvalidValue;
 }

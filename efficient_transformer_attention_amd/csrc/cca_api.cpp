@@ -267,6 +267,23 @@ StateOut state_of(const cca_state *st) {
   return s;
 }
 
+StateOut state_of(const cca_paged_state *st) {
+  StateOut s;
+  std::memset(&s, 0, sizeof(s));
+  if (st) {
+    s.k_cache = st->k_pages;
+    s.v_cache = st->v_pages;
+    s.conv_q = st->conv_q;
+    s.conv_k = st->conv_k;
+    s.vshift = st->vshift;
+    s.table = st->block_table;
+    s.page = st->page_size;
+    s.mpps = st->max_pages_per_seq;
+    s.npages = st->num_pages;
+  }
+  return s;
+}
+
 unsigned char *wsp(void *ws, const Layout &L, int slot) {
   return static_cast<unsigned char *>(ws) + L.off[slot];
 }
@@ -286,7 +303,7 @@ cca_status run_downproj(const cca_config &c, const cca_weights *w, const void *x
   return check_launch(e, st);
 }
 
-cca_status run_convmix(const cca_config &c, const cca_weights *w, const cca_state *so, void *ws,
+cca_status run_convmix(const cca_config &c, const cca_weights *w, const StateOut &so, void *ws,
                        const Layout &L, hipStream_t st) {
   const MixShape s = mix_shape(c);
   const float *qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
@@ -294,15 +311,15 @@ cca_status run_convmix(const cca_config &c, const cca_weights *w, const cca_stat
   if (c.dtype == CCA_F32) {
     e = launch_convmix_prefill<float, float>(s, taps_of(w), qkv, (float *)wsp(ws, L, CCA_WS_Q),
                                              (float *)wsp(ws, L, CCA_WS_K),
-                                             (float *)wsp(ws, L, CCA_WS_VT), state_of(so), st);
+                                             (float *)wsp(ws, L, CCA_WS_VT), so, st);
   } else if (qk_is_f16(c)) {
     e = launch_convmix_prefill<f16, bf16>(s, taps_of(w), qkv, (f16 *)wsp(ws, L, CCA_WS_Q),
                                           (f16 *)wsp(ws, L, CCA_WS_K),
-                                          (bf16 *)wsp(ws, L, CCA_WS_VT), state_of(so), st);
+                                          (bf16 *)wsp(ws, L, CCA_WS_VT), so, st);
   } else {
     e = launch_convmix_prefill<bf16, bf16>(s, taps_of(w), qkv, (bf16 *)wsp(ws, L, CCA_WS_Q),
                                            (bf16 *)wsp(ws, L, CCA_WS_K),
-                                           (bf16 *)wsp(ws, L, CCA_WS_VT), state_of(so), st);
+                                           (bf16 *)wsp(ws, L, CCA_WS_VT), so, st);
   }
   return check_launch(e, st);
 }
@@ -516,7 +533,7 @@ cca_status cca_prefill_forward(const cca_config *cfg, const cca_weights *w, cons
   CCA_TRY(check_state_out(*cfg, state_out));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CCA_TRY(run_downproj(*cfg, w, x, ws, L, st));
-  CCA_TRY(run_convmix(*cfg, w, state_out, ws, L, st));
+  CCA_TRY(run_convmix(*cfg, w, state_of(state_out), ws, L, st));
   CCA_TRY(run_attention(*cfg, w, ws, L, st));
   return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
 }
@@ -534,7 +551,7 @@ cca_status cca_stage_convmix(const cca_config *cfg, const cca_weights *w, const 
   Layout L;
   CCA_TRY(prefill_checks(cfg, w, ws, wsb, &L));
   CCA_TRY(check_state_out(*cfg, so));
-  return run_convmix(*cfg, w, so, ws, L, reinterpret_cast<hipStream_t>(stream));
+  return run_convmix(*cfg, w, state_of(so), ws, L, reinterpret_cast<hipStream_t>(stream));
 }
 
 cca_status cca_stage_attention(const cca_config *cfg, const cca_weights *w, void *ws, size_t wsb,
@@ -582,7 +599,7 @@ static cca_status dec_downproj(const cca_config &c, const cca_weights *w, const 
 }
 
 static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
-                          const int32_t *lens, const cca_state *si, const cca_state *so, void *ws,
+                          const int32_t *lens, const StateOut &si, const StateOut &so, void *ws,
                           const Layout &L, hipStream_t st) {
   MixShape s = mix_shape(c);
   s.T = 1;
@@ -591,14 +608,14 @@ static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
   float *q = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_Q));
   hipError_t e;
   if (c.dtype == CCA_BF16)
-    e = launch_convmix_decode<bf16>(s, taps_of(w), qkv, Lc, lens, state_of(si), state_of(so), q, st);
+    e = launch_convmix_decode<bf16>(s, taps_of(w), qkv, Lc, lens, si, so, q, st);
   else
-    e = launch_convmix_decode<float>(s, taps_of(w), qkv, Lc, lens, state_of(si), state_of(so), q, st);
+    e = launch_convmix_decode<float>(s, taps_of(w), qkv, Lc, lens, si, so, q, st);
   return check_launch(e, st);
 }
 
 static cca_status dec_attn(const cca_config &c, const cca_weights *w, int32_t Lc,
-                           const int32_t *lens, const cca_state *si, void *ws, const Layout &L,
+                           const int32_t *lens, const StateOut &cache, void *ws, const Layout &L,
                            hipStream_t st) {
   MixShape s = mix_shape(c);
   s.T = 1;
@@ -607,13 +624,11 @@ static cca_status dec_attn(const cca_config &c, const cca_weights *w, int32_t Lc
   float *part = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_PART));
   hipError_t e;
   if (c.dtype == CCA_BF16)
-    e = launch_attention_decode<bf16>(s, q, (const bf16 *)si->k_cache, (const bf16 *)si->v_cache,
-                                      si->capacity, Lc + 1, lens, w->tau, part,
+    e = launch_attention_decode<bf16>(s, q, cache, Lc + 1, lens, w->tau, part,
                                       (bf16 *)wsp(ws, L, CCA_WS_O), st);
   else
-    e = launch_attention_decode<float>(s, q, (const float *)si->k_cache,
-                                       (const float *)si->v_cache, si->capacity, Lc + 1, lens, w->tau,
-                                       part, (float *)wsp(ws, L, CCA_WS_O), st);
+    e = launch_attention_decode<float>(s, q, cache, Lc + 1, lens, w->tau, part,
+                                       (float *)wsp(ws, L, CCA_WS_O), st);
   return check_launch(e, st);
 }
 
@@ -627,8 +642,8 @@ cca_status cca_decode_step(const cca_config *cfg, const cca_weights *w, const vo
   CCA_TRY(check_decode_state(c, cache_len, si, so));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CCA_TRY(dec_downproj(c, w, x_t, ws, L, st));
-  CCA_TRY(dec_mix(c, w, cache_len, nullptr, si, so, ws, L, st));
-  CCA_TRY(dec_attn(c, w, cache_len, nullptr, si, ws, L, st));
+  CCA_TRY(dec_mix(c, w, cache_len, nullptr, state_of(si), state_of(so), ws, L, st));
+  CCA_TRY(dec_attn(c, w, cache_len, nullptr, state_of(si), ws, L, st));
   return run_upproj(c, w, y_t, ws, L, c.batch, st);
 }
 
@@ -644,8 +659,8 @@ cca_status cca_decode_step_varlen(const cca_config *cfg, const cca_weights *w, c
   CCA_TRY(check_decode_state(c, max_cache_len, si, so));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CCA_TRY(dec_downproj(c, w, x_t, ws, L, st));
-  CCA_TRY(dec_mix(c, w, max_cache_len, cache_lens, si, so, ws, L, st));
-  CCA_TRY(dec_attn(c, w, max_cache_len, cache_lens, si, ws, L, st));
+  CCA_TRY(dec_mix(c, w, max_cache_len, cache_lens, state_of(si), state_of(so), ws, L, st));
+  CCA_TRY(dec_attn(c, w, max_cache_len, cache_lens, state_of(si), ws, L, st));
   return run_upproj(c, w, y_t, ws, L, c.batch, st);
 }
 
@@ -664,7 +679,8 @@ cca_status cca_stage_decode_mix(const cca_config *cfg, const cca_weights *w, int
   CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
   const cca_config c = decode_cfg(cfg);
   CCA_TRY(check_decode_state(c, cache_len, si, so));
-  return dec_mix(c, w, cache_len, nullptr, si, so, ws, L, reinterpret_cast<hipStream_t>(stream));
+  return dec_mix(c, w, cache_len, nullptr, state_of(si), state_of(so), ws, L,
+                 reinterpret_cast<hipStream_t>(stream));
 }
 
 cca_status cca_stage_decode_attention(const cca_config *cfg, const cca_weights *w,
@@ -674,7 +690,8 @@ cca_status cca_stage_decode_attention(const cca_config *cfg, const cca_weights *
   CCA_TRY(decode_checks(cfg, w, cache_len, ws, wsb, &L));
   const cca_config c = decode_cfg(cfg);
   CCA_TRY(check_decode_state(c, cache_len, si, si));
-  return dec_attn(c, w, cache_len, nullptr, si, ws, L, reinterpret_cast<hipStream_t>(stream));
+  return dec_attn(c, w, cache_len, nullptr, state_of(si), ws, L,
+                  reinterpret_cast<hipStream_t>(stream));
 }
 
 cca_status cca_stage_decode_upproj(const cca_config *cfg, const cca_weights *w, int32_t cache_len,
@@ -703,7 +720,7 @@ cca_status cca_prefill_forward_train(const cca_config *cfg, const cca_weights *w
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const Layout &L = TL.pre;
   CCA_TRY(run_downproj(*cfg, w, x, ws, L, st));
-  CCA_TRY(run_convmix(*cfg, w, nullptr, ws, L, st));
+  CCA_TRY(run_convmix(*cfg, w, state_of((const cca_state *)nullptr), ws, L, st));
   CCA_TRY(run_attention(*cfg, w, ws, L, st, trp<float>(ws, TL, TR_LSE)));
   return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
 }
@@ -724,6 +741,66 @@ cca_status cca_prefill_backward(const cca_config *cfg, const cca_weights *w, con
   if (cfg->dtype == CCA_F32) return run_backward<float, float>(*cfg, w, x, dy, g, ws, TL, st);
   if (qk_is_f16(*cfg)) return run_backward<f16, bf16>(*cfg, w, x, dy, g, ws, TL, st);
   return run_backward<bf16, bf16>(*cfg, w, x, dy, g, ws, TL, st);
+}
+
+}  // extern "C"
+
+// ---- paged cache -------------------------------------------------------------
+
+static cca_status check_paged(const cca_config &c, const cca_paged_state *p, long long need_rows) {
+  if (!p) return CCA_ERR_INVALID_ARG;
+  if (!p->k_pages || !p->v_pages || !p->block_table) return CCA_ERR_INVALID_ARG;
+  if (!aligned16(p->k_pages) || !aligned16(p->v_pages) ||
+      reinterpret_cast<uintptr_t>(p->block_table) % 4)
+    return CCA_ERR_INVALID_ARG;
+  if (p->page_size < 32 || p->page_size % 32 || p->num_pages < 1 || p->max_pages_per_seq < 1)
+    return CCA_ERR_INVALID_ARG;
+  if ((long long)p->max_pages_per_seq * p->page_size < need_rows) return CCA_ERR_INVALID_ARG;
+  if ((long long)p->num_pages * c.n_kv_heads * p->page_size * c.head_dim > (1ll << 40))
+    return CCA_ERR_UNSUPPORTED;
+  return CCA_OK;
+}
+
+extern "C" {
+
+cca_status cca_decode_step_paged(const cca_config *cfg, const cca_weights *w, const void *x_t,
+                                 const int32_t *cache_lens, int32_t max_cache_len,
+                                 const cca_paged_state *si, const cca_paged_state *so, void *y_t,
+                                 void *ws, size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(decode_checks(cfg, w, max_cache_len, ws, wsb, &L));
+  if (!x_t || !y_t || !aligned16(x_t) || !aligned16(y_t)) return CCA_ERR_INVALID_ARG;
+  if (!cache_lens || reinterpret_cast<uintptr_t>(cache_lens) % 4) return CCA_ERR_INVALID_ARG;
+  const cca_config c = decode_cfg(cfg);
+  CCA_TRY(check_paged(c, si, (long long)max_cache_len + 1));
+  if (!so) return CCA_ERR_INVALID_ARG;
+  if ((so->k_pages && so->k_pages != si->k_pages) || (so->v_pages && so->v_pages != si->v_pages) ||
+      (so->block_table && so->block_table != si->block_table))
+    return CCA_ERR_INVALID_ARG;
+  if (c.seq_conv_k > 1 && (!si->conv_q || !si->conv_k || !so->conv_q || !so->conv_k))
+    return CCA_ERR_INVALID_ARG;
+  if (c.use_value_shift && (!si->vshift || !so->vshift)) return CCA_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const StateOut in = state_of(si), out = state_of(so);
+  CCA_TRY(dec_downproj(c, w, x_t, ws, L, st));
+  CCA_TRY(dec_mix(c, w, max_cache_len, cache_lens, in, out, ws, L, st));
+  CCA_TRY(dec_attn(c, w, max_cache_len, cache_lens, in, ws, L, st));
+  return run_upproj(c, w, y_t, ws, L, c.batch, st);
+}
+
+cca_status cca_prefill_forward_paged(const cca_config *cfg, const cca_weights *w, const void *x,
+                                     void *y, const cca_paged_state *so, void *ws, size_t wsb,
+                                     void *stream) {
+  Layout L;
+  CCA_TRY(prefill_checks(cfg, w, ws, wsb, &L));
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return CCA_ERR_INVALID_ARG;
+  if (!so) return CCA_ERR_INVALID_ARG;
+  if (so->k_pages || so->v_pages) CCA_TRY(check_paged(*cfg, so, cfg->seq_len));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CCA_TRY(run_downproj(*cfg, w, x, ws, L, st));
+  CCA_TRY(run_convmix(*cfg, w, state_of(so), ws, L, st));
+  CCA_TRY(run_attention(*cfg, w, ws, L, st));
+  return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
 }
 
 }  // extern "C"

@@ -47,13 +47,27 @@ struct MixTaps {
   const float *tau;   // [H_q]; the prefill mixing stores tau_h * log2(e) * q_hat
 };
 
-// Optional prefill outputs that seed a decode: cache rows [0, T) and the
-// carried conv window / value-shift state (any pointer may be null).
+// A latent KV cache and the carried conv window / value-shift state (any
+// pointer may be null).  The cache is either contiguous, [B, Hkv, capacity,
+// d], or paged: pages [npages, Hkv, page, d] with table[b * mpps + key /
+// page] the page that holds sequence b's keys [page * j, page * (j + 1));
+// table entries outside [0, npages) are clamped (wrong rows, never a fault).
 struct StateOut {
   void *k_cache, *v_cache;
   int capacity;
   void *conv_q, *conv_k, *vshift;
+  const int *table;     // null: contiguous
+  int page, mpps, npages;
 };
+
+// Row index (times d gives the element offset) of sequence b's key `key` of
+// kv head g in the cache described by st.
+__host__ __device__ inline size_t cache_row(const StateOut &st, int b, int Hkv, int g, int key) {
+  if (!st.table) return (size_t)(b * Hkv + g) * st.capacity + key;
+  int pg = st.table[(size_t)b * st.mpps + key / st.page];
+  pg = pg < 0 ? 0 : (pg >= st.npages ? st.npages - 1 : pg);
+  return ((size_t)pg * Hkv + g) * st.page + key % st.page;
+}
 
 // Fused sequence conv + channel conv + q-k-mean + value-shift + L2 norm + RoPE
 // over a prefill.  qkv: fp32 [B*T, e_q + 2 e_kv].  Writes q [B,Hq,Tp,d] and
@@ -84,12 +98,12 @@ bool attention_supported(int d, bool f32);
 
 // Split-KV decode attention over Lk = L + 1 cached keys (per sequence
 // lens[b] + 1, clamped to [1, Lk], when lens is not null; the chunking
-// follows Lk), then the log-sum-exp combine.  part: fp32 scratch of
-// decode_partial_floats() floats.
+// follows Lk) of the cache `cache` (contiguous or paged), then the
+// log-sum-exp combine.  part: fp32 scratch of decode_partial_floats() floats.
 template <typename TV>
-hipError_t launch_attention_decode(const MixShape &s, const float *q, const TV *k_cache,
-                                   const TV *v_cache, int capacity, int Lk, const int *lens,
-                                   const float *tau, float *part, TV *o, hipStream_t stream);
+hipError_t launch_attention_decode(const MixShape &s, const float *q, const StateOut &cache, int Lk,
+                                   const int *lens, const float *tau, float *part, TV *o,
+                                   hipStream_t stream);
 
 // Whether the mixing kernel's LDS tile of one kv group (G query heads + k +
 // v, 19 tokens) fits the 64 KiB it may use.

@@ -267,8 +267,8 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
         } else {
           Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
           if (st.k_cache && tok < s.T)
-            Store4<TV>::st(reinterpret_cast<TV *>(st.k_cache) +
-                               ((size_t)(b * s.Hkv + g) * st.capacity + tok) * D + 4 * li, y);
+            Store4<TV>::st(reinterpret_cast<TV *>(st.k_cache) + cache_row(st, b, s.Hkv, g, tok) * D +
+                               4 * li, y);
         }
       }
     }
@@ -291,8 +291,8 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
         const int r = e / (D / 4), c4 = e % (D / 4), tok = t0 + r;
         if (tok >= s.T) continue;
         const float *src = tile + (r + HALO - shifted) * CW + vcol + 4 * c4;
-        Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) +
-                           ((size_t)(b * s.Hkv + g) * st.capacity + tok) * D + 4 * c4, src);
+        Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) + cache_row(st, b, s.Hkv, g, tok) * D +
+                           4 * c4, src);
       }
     }
     __syncthreads();                                 // every read of this tile is done
@@ -412,12 +412,12 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
     if (slot < G) {
       Store4<float>::st(qout + (size_t)(b * s.Hq + g * G + slot) * D + 4 * li, y);
     } else {
-      Store4<TV>::st(kc + ((size_t)(b * s.Hkv + g) * in.capacity + L) * D + 4 * li, y);
+      Store4<TV>::st(kc + cache_row(in, b, s.Hkv, g, L) * D + 4 * li, y);
     }
   }
   // value row of the new token into the cache
   for (int c4 = tid; c4 < D / 4; c4 += 256)
-    Store4<TV>::st(vc + ((size_t)(b * s.Hkv + g) * in.capacity + L) * D + 4 * c4,
+    Store4<TV>::st(vc + cache_row(in, b, s.Hkv, g, L) * D + 4 * c4,
                    tile + (3 - shifted) * CW + (G + 1) * D + 4 * c4);
   // rolled state: slot sl holds token L - ks1 + 1 + sl = tile row 5 - ks + sl
   TV *oq = reinterpret_cast<TV *>(out.conv_q);

@@ -236,6 +236,52 @@ cca_status cca_prefill_backward(const cca_config *cfg, const cca_weights *w, con
                                 const void *dy, const cca_grads *g, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* Paged latent cache, for serving many sequences from one pool of pages
+ * [GS-EN "1. Problem Statement": the cache grows per sequence; CCGQA keeps it
+ * small, GS-EN "2. Methodology" / "Extension: CCGQA"].  Caller-owned.
+ * k_pages, v_pages: [num_pages, H_kv, page_size, d] in cfg.dtype, 16-byte
+ *   aligned; page p holds page_size consecutive tokens of one sequence.
+ * block_table: device int32 [B, max_pages_per_seq]; entry [b, j] is the page
+ *   that holds sequence b's tokens [j * page_size, (j + 1) * page_size).
+ *   Entries outside [0, num_pages) are clamped (wrong rows, never a fault).
+ * page_size: a multiple of 32.  conv_q, conv_k, vshift as in cca_state. */
+typedef struct {
+  void *k_pages;
+  void *v_pages;
+  const int32_t *block_table;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t reserved;
+  void *conv_q;
+  void *conv_k;
+  void *vshift;
+} cca_paged_state;
+
+/* cca_decode_step_varlen on a paged cache: sequence b's new token at
+ * position cache_lens[b] attends to its rows [0, cache_lens[b]] found through
+ * the block table, and its k, v rows are written into the page that holds
+ * position cache_lens[b].  state_in and state_out share pages and table
+ * (state_out's k_pages / v_pages / block_table must be NULL or equal);
+ * conv_q / conv_k / vshift roll as in cca_decode_step.  With the same rows,
+ * lengths and max_cache_len the result equals cca_decode_step_varlen on a
+ * contiguous cache bit for bit.  CCA_ERR_INVALID_ARG when page_size is not a
+ * positive multiple of 32, max_pages_per_seq * page_size <= max_cache_len,
+ * num_pages < 1, or a pointer is null or misaligned. */
+cca_status cca_decode_step_paged(const cca_config *cfg, const cca_weights *w, const void *x_t,
+                                 const int32_t *cache_lens, int32_t max_cache_len,
+                                 const cca_paged_state *state_in,
+                                 const cca_paged_state *state_out, void *y_t, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* cca_prefill_forward writing its decode state into a paged cache: rows
+ * [0, T) of every sequence go to the pages its block-table row names
+ * (max_pages_per_seq * page_size >= T).  Members left NULL are skipped as in
+ * cca_prefill_forward. */
+cca_status cca_prefill_forward_paged(const cca_config *cfg, const cca_weights *w, const void *x,
+                                     void *y, const cca_paged_state *state_out, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *cca_status_string(cca_status s);
 

@@ -184,3 +184,34 @@ def test_backward_rejects_before_launch(L):
     assert ft(C.byref(cfg), C.byref(w), 0xA0000, 0xB0000, 0x100000, need - 1, None) == \
         L.CCA_ERR_WORKSPACE
     assert ft(C.byref(cfg), None, 0xA0000, 0xB0000, 0x100000, need, None) == L.CCA_ERR_INVALID_ARG
+
+
+def test_paged_decode_rejects_before_launch(L):
+    s = CCAShape(batch=2, seq_len=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    cfg = L.make_config(s)
+    need = L.decode_workspace_size(cfg, 100)
+    w = _fake_weights(L)
+    f = L.lib.cca_decode_step_paged
+
+    def st(page=64, mpps=2, npages=4, table=0xC0000, k=0x30000):
+        return L._PagedState(k, 0x40000, table, npages, page, mpps, 0, 0x50000, 0x60000, 0x70000)
+    args = lambda si, so=None, lens=0xA0000, L_=100, wsb=need: (
+        C.byref(cfg), C.byref(w), 0x10000, lens, L_, C.byref(si), C.byref(so or si), 0x20000,
+        0x100000, wsb, None)
+    assert f(*args(st(), lens=None)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(st(page=48))) == L.CCA_ERR_INVALID_ARG              # not a multiple of 32
+    assert f(*args(st(page=0))) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(st(mpps=1))) == L.CCA_ERR_INVALID_ARG               # 64 rows < 101 needed
+    assert f(*args(st(npages=0))) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(st(table=0))) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(st(table=0xC0002))) == L.CCA_ERR_INVALID_ARG        # misaligned table
+    assert f(*args(st(k=0x30008))) == L.CCA_ERR_INVALID_ARG            # misaligned pages
+    assert f(*args(st(), st(k=0x90000))) == L.CCA_ERR_INVALID_ARG     # out pages differ
+    assert f(*args(st(), wsb=need - 1)) == L.CCA_ERR_WORKSPACE
+    fp = L.lib.cca_prefill_forward_paged
+    cfg2 = L.make_config(s.with_(seq_len=200))
+    need2 = L.prefill_workspace_size(cfg2)
+    assert fp(C.byref(cfg2), C.byref(w), 0x10000, 0x20000, C.byref(st(mpps=3)), 0x100000, need2,
+              None) == L.CCA_ERR_INVALID_ARG                           # 192 rows < T = 200
+    assert fp(C.byref(cfg2), C.byref(w), 0x10000, 0x20000, None, 0x100000, need2,
+              None) == L.CCA_ERR_INVALID_ARG
