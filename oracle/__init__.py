@@ -6,7 +6,8 @@ calls it and shares no code with it.
 
 Modules
 -------
-``cca``    vectorised NumPy oracle (prefill, sampled-row prefill, decode step)
+``cca``    vectorised NumPy oracle (prefill, sampled-row prefill, decode step,
+           multi-token decode step)
 ``brute``  scalar pure-Python twin for tiny inputs, written separately
            from the same readings, used to pin ``cca``
 ``backward``  the derivative of every step of ``cca`` (chain rule, fp64) and
@@ -48,4 +49,5 @@ from .cca import (  # noqa: F401
     prefill,
     prefill_state,
     decode_step,
+    decode_multi,
 )

@@ -362,3 +362,30 @@ def decode_step(x_t, w, cfg, k_cache, v_cache, conv_q, conv_k, vshift,
     new_vs = lat["vbar"][:, 0][:, sh, :]
     return y, dict(k_new=k_new, v_new=v_new, q=lat["q"][:, 0], o=o[:, 0],
                    conv_q=new_cq, conv_k=new_ck, vshift=new_vs)
+
+
+def decode_multi(x_new, w, cfg, k_cache, v_cache, conv_q, conv_k, vshift,
+                 readings: Readings = DEFAULT_READINGS):
+    """m new tokens per sequence against a cache of L = k_cache.shape[2] past
+    tokens (a speculative-verification or chunked step): x_new [B, m, E]; the
+    new tokens sit at positions L .. L+m-1.  Steps a1-a7 run over the m tokens
+    with the carried window (the same code path as a prefill that continues
+    from that state), their k and v are appended at slots L .. L+m-1, query j
+    attends to keys 0 .. L+j, then the up-projection.  Returns (y [B, m, E],
+    dict with k_new, v_new [B, H_kv, m, d] and the rolled state)."""
+    B, m, _ = x_new.shape
+    L = k_cache.shape[2]
+    lat = latents(x_new, w, cfg, pos0=L, history=(conv_q, conv_k, vshift), readings=readings)
+    k_new = lat["k"].transpose(0, 2, 1, 3)            # [B, H_kv, m, d]
+    v_new = lat["v"].transpose(0, 2, 1, 3)
+    kk = np.concatenate([k_cache, k_new], axis=2).transpose(0, 2, 1, 3)
+    vv = np.concatenate([v_cache, v_new], axis=2).transpose(0, 2, 1, 3)
+    o = causal_attention(lat["q"], kk, vv, w["tau"], list(range(L, L + m)))
+    y = up_project(o, w["w_o"])
+    ks1 = cfg.seq_conv_k - 1
+    cq_all = np.concatenate([conv_q, lat["q_pre"].reshape(B, m, -1)], axis=1)
+    ck_all = np.concatenate([conv_k, lat["k_pre"].reshape(B, m, -1)], axis=1)
+    sh = shifted_heads(cfg.n_kv_heads, readings)
+    return y, dict(k_new=k_new, v_new=v_new, q=lat["q"],
+                   conv_q=cq_all[:, cq_all.shape[1] - ks1:], conv_k=ck_all[:, ck_all.shape[1] - ks1:],
+                   vshift=lat["vbar"][:, -1][:, sh, :])

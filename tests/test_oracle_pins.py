@@ -350,6 +350,30 @@ def test_multi_step_decode_matches_prefill():
         cq, ck, vs = new["conv_q"], new["conv_k"], new["vshift"]
 
 
+@pytest.mark.parametrize("L0,m", [(0, 1), (0, 3), (2, 2), (4, 5), (6, 1)])
+def test_multi_token_decode_matches_prefill(L0, m):
+    """m new tokens at once after a prefill of L0 equal a prefill of L0 + m
+    (outputs, appended k / v rows and the rolled state)."""
+    s, x, w = tiny(B=2, T=L0 + m, Hq=4, Hkv=2)
+    y_full = O.prefill(x, w, s)
+    Hkv, d = s.n_kv_heads, s.head_dim
+    if L0 > 0:
+        _, lat = O.prefill(x[:, :L0], w, s.with_(seq_len=L0), intermediates=True)
+        K, V, cq, ck, vs = O.prefill_state(lat, s)
+    else:
+        K = np.zeros((2, Hkv, 0, d)); V = np.zeros((2, Hkv, 0, d))
+        cq = np.zeros((2, 3, s.e_q)); ck = np.zeros((2, 3, s.e_kv)); vs = np.zeros((2, Hkv // 2, d))
+    y, new = O.decode_multi(x[:, L0:], w, s, K, V, cq, ck, vs)
+    assert rel(y, y_full[:, L0:]) < 1e-12
+    _, lat2 = O.prefill(x, w, s, intermediates=True)
+    K2, V2, cq2, ck2, vs2 = O.prefill_state(lat2, s)
+    np.testing.assert_allclose(new["k_new"], K2[:, :, L0:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(new["v_new"], V2[:, :, L0:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(new["conv_q"], cq2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(new["conv_k"], ck2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(new["vshift"], vs2, rtol=1e-12, atol=1e-14)
+
+
 def test_sampled_rows_match_full():
     s, x, w = tiny(B=2, T=12, Hq=4, Hkv=2)
     y = O.prefill(x, w, s)
