@@ -31,6 +31,7 @@ EXPORTS = (
     "cca_stage_decode_upproj",
     "cca_train_workspace_size", "cca_prefill_forward_train", "cca_prefill_backward",
     "cca_decode_step_paged", "cca_prefill_forward_paged",
+    "cca_decode_multi_workspace_size", "cca_decode_multi", "cca_decode_multi_paged",
 )
 
 
@@ -105,6 +106,11 @@ def _load():
         "cca_decode_step_paged": (C.c_int, [cfgp, wp, vp, vp, C.c_int32, P(_PagedState),
                                             P(_PagedState), vp, vp, sz, vp]),
         "cca_prefill_forward_paged": (C.c_int, [cfgp, wp, vp, vp, P(_PagedState), vp, sz, vp]),
+        "cca_decode_multi_workspace_size": (sz, [cfgp, C.c_int32, C.c_int32]),
+        "cca_decode_multi": (C.c_int, [cfgp, wp, vp, C.c_int32, vp, C.c_int32, sp, sp, vp, vp, sz,
+                                       vp]),
+        "cca_decode_multi_paged": (C.c_int, [cfgp, wp, vp, C.c_int32, vp, C.c_int32,
+                                             P(_PagedState), P(_PagedState), vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -354,3 +360,25 @@ def prefill_forward_paged(cfg: Config, w: Weights, x, y, workspace, state_out: P
                                          C.byref(state_out.struct()), _ptr(workspace),
                                          _wsb(workspace), _stream(stream)),
            "cca_prefill_forward_paged")
+
+
+def decode_multi_workspace_size(cfg: Config, n_new: int, max_cache_len: int) -> int:
+    return lib.cca_decode_multi_workspace_size(C.byref(cfg), int(n_new), int(max_cache_len))
+
+
+def decode_multi(cfg: Config, w: Weights, x_new, n_new: int, cache_lens, max_cache_len: int,
+                 state_in: State, state_out: State, y_new, workspace, stream=None):
+    """x_new, y_new: [B, n_new, E]; cache_lens: device int32 [B]."""
+    _check(lib.cca_decode_multi(C.byref(cfg), C.byref(w.struct()), _ptr(x_new), int(n_new),
+                                _ptr(cache_lens), int(max_cache_len), C.byref(state_in.struct()),
+                                C.byref(state_out.struct()), _ptr(y_new), _ptr(workspace),
+                                _wsb(workspace), _stream(stream)), "cca_decode_multi")
+
+
+def decode_multi_paged(cfg: Config, w: Weights, x_new, n_new: int, cache_lens, max_cache_len: int,
+                       state_in: PagedState, state_out: PagedState, y_new, workspace, stream=None):
+    _check(lib.cca_decode_multi_paged(C.byref(cfg), C.byref(w.struct()), _ptr(x_new), int(n_new),
+                                      _ptr(cache_lens), int(max_cache_len),
+                                      C.byref(state_in.struct()), C.byref(state_out.struct()),
+                                      _ptr(y_new), _ptr(workspace), _wsb(workspace),
+                                      _stream(stream)), "cca_decode_multi_paged")

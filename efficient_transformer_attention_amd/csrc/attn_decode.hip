@@ -64,8 +64,8 @@ static int dec_chunk_len(int Lk, int nch) {
   return (per + 2 * DEC_TILE - 1) / (2 * DEC_TILE) * (2 * DEC_TILE);
 }
 
-size_t decode_partial_floats(int B, int Hq, int Hkv, int d, int Lk) {
-  return (size_t)B * Hq * dec_num_chunks(B, Hkv, Lk) * (d + 2);
+size_t decode_partial_floats(int B, int Hq, int Hkv, int d, int Lk, int m) {
+  return (size_t)B * Hq * m * dec_num_chunks(B, Hkv, Lk) * (d + 2);
 }
 
 __device__ __forceinline__ float exp2_or_zero(float a, float m) {
@@ -79,7 +79,10 @@ __device__ __forceinline__ float exp2_or_zero(float a, float m) {
 // instantiation, so the uniform-length kernel carries no per-sequence load).
 // PAGED: cache rows are found through the page table of `cm` (one table
 // lookup per row gather); otherwise cm is contiguous.
-template <int D, bool VARLEN, bool PAGED>
+// MULTI: m new tokens per sequence; the MFMA columns are (query head, new
+// token) pairs, GH of them per workgroup, and column j of a sequence at
+// length L sees keys 0 .. L + j (causal among the new tokens).
+template <int D, bool VARLEN, bool PAGED, bool MULTI>
 __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__restrict__ q,
                                                                const float *__restrict__ tau,
                                                                const bf16 *__restrict__ kc,
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
                                                                int Lk, const int *__restrict__ lens,
                                                                int chunk, int Hq, int Hkv,
                                                                int G, int GH, int nsub, int nch,
-                                                               float *__restrict__ part) {
+                                                               int m, float *__restrict__ part) {
   constexpr int QC = D / 16;                 // contraction chunks of S^T
   constexpr int ND = D < 32 ? 1 : D / 32;    // O^T row blocks
   constexpr int MAXG = DecMaxG<D>::value;
@@ -110,13 +113,26 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   const int sub = id % nsub; id /= nsub;
   const int g = id % Hkv, b = id / Hkv;
   const int h0 = g * G + sub * GH;
-  const bool col_ok = l32 < GH;              // this lane's column is a real query head
+  // this lane's column: query head hcol (of new token jcol)
+  bool col_ok;
+  int hcol, jcol;
+  if constexpr (MULTI) {
+    const int pr = sub * GH + l32;
+    col_ok = l32 < GH && pr < G * m;
+    hcol = g * G + (col_ok ? pr : 0) / m;
+    jcol = (col_ok ? pr : 0) % m;
+  } else {
+    col_ok = l32 < GH;
+    hcol = h0 + (col_ok ? l32 : 0);
+    jcol = 0;
+  }
 
-  // q of head (h0 + l32) scaled by tau*log2(e), split into bf16 hi + lo
+  // q of head hcol scaled by tau*log2(e), split into bf16 hi + lo
   bf16x8 qhi[QC], qlo[QC];
   {
-    const float sc = col_ok ? tau[h0 + l32] * 1.4426950408889634f : 0.f;
-    const float *qr = q + (size_t)(b * Hq + h0 + (col_ok ? l32 : 0)) * D;
+    const float sc = col_ok ? tau[hcol] * 1.4426950408889634f : 0.f;
+    const float *qr = MULTI ? q + ((size_t)(b * m + jcol) * Hq + hcol) * D
+                            : q + (size_t)(b * Hq + hcol) * D;
 #pragma unroll
     for (int cc = 0; cc < QC; ++cc)
 #pragma unroll
@@ -128,10 +144,14 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
       }
   }
 
-  // keys of this sequence: lens[b] + 1 (clamped to [1, Lk]) when given
-  const int Lkb = VARLEN ? min(max(lens[b], 0), Lk - 1) + 1 : Lk;
+  // keys of this sequence: lens[b] + M (lens clamped to [0, Lk - M]) when
+  // given, M = the new tokens; column jcol sees keys below klim
+  const int M = MULTI ? m : 1;
+  const int Lkb = VARLEN ? min(max(lens[b], 0), Lk - M) + M : Lk;
   const int kbeg = c * chunk;
   const int kend = min(kbeg + chunk, Lkb);
+  const int klim = min(kend, Lkb - M + jcol + 1);
+  const int kcut = MULTI ? min(kend, Lkb - M + 1) : kend;   // first key some column masks
   const int ntile = (kend - kbeg + DEC_TILE - 1) / DEC_TILE;
   const bf16 *kb = kc + (size_t)(b * Hkv + g) * cm.capacity * D;
   const bf16 *vb = vc + (size_t)(b * Hkv + g) * cm.capacity * D;
@@ -205,24 +225,27 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
 #pragma unroll
     for (int u = 0; u < TPI; ++u) {
       const int k0 = kbeg + (t + u) * DEC_TILE;
-      const bool tail = k0 + DEC_TILE > kend;
+      const bool tail = k0 + DEC_TILE > kcut;
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         float v = s[u][a];
-        if (tail && k0 + 8 * (a >> 2) + 4 * hl + (a & 3) >= kend) v = -INFINITY;
+        if (tail && k0 + 8 * (a >> 2) + 4 * hl + (a & 3) >= (MULTI ? klim : kend)) v = -INFINITY;
         s[u][a] = v;
         mx = fmaxf(mx, v);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // a column can see no key yet only with several new tokens: keep its
+    // state at (-inf, 0) instead of exp2(-inf + inf)
+    const float m_use = (MULTI && m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float ps = 0.f;
 #pragma unroll
     for (int u = 0; u < TPI; ++u)
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
-        const float p = __builtin_amdgcn_exp2f(s[u][a] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[u][a] - m_use);
         s[u][a] = p;
         ps += p;
       }
@@ -285,7 +308,15 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
       ll += red[w * MAXG + hh][1] * f;
       oo += red[w * MAXG + hh][2 + dd] * f;
     }
-    float *dst = part + ((size_t)(b * Hq + h0 + hh) * nch + c) * (D + 2);
+    size_t prow;
+    if constexpr (MULTI) {
+      const int pr = sub * GH + hh;
+      if (pr >= G * m) continue;
+      prow = (size_t)(b * Hq + g * G + pr / m) * m + pr % m;
+    } else {
+      prow = (size_t)(b * Hq + h0 + hh);
+    }
+    float *dst = part + (prow * nch + c) * (D + 2);
     dst[2 + dd] = oo;
     if (dd == 0) {
       dst[0] = mm;
@@ -306,8 +337,10 @@ __global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__res
                                                               const int *__restrict__ lens, int chunk,
                                                               int Hq,
                                                               int Hkv, int G, int GH, int nsub,
-                                                              int nch, float *__restrict__ part) {
-  // one thread per (query head, key) score; waves walk the chunk in 256-key steps
+                                                              int nch, int m,
+                                                              float *__restrict__ part) {
+  // one thread per (column, key) score, a column being a (query head, new
+  // token) pair; waves walk the chunk in 256-key steps
   __shared__ float qs[DEC_F32_MAXG][D];
   __shared__ float pbuf[DEC_F32_MAXG][256];
   __shared__ float mst[DEC_F32_MAXG], lst[DEC_F32_MAXG], alph[DEC_F32_MAXG];
@@ -317,22 +350,25 @@ __global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__res
   const int c = id % nch; id /= nch;
   const int sub = id % nsub; id /= nsub;
   const int g = id % Hkv, b = id / Hkv;
-  const int h0 = g * G + sub * GH;
+  const int P = G * m;                           // columns of this (b, g)
+  auto col_head = [&](int hh) { return g * G + min(sub * GH + hh, P - 1) / m; };
+  auto col_tok = [&](int hh) { return min(sub * GH + hh, P - 1) % m; };
   for (int e = tid; e < GH * D; e += 256) {
     const int hh = e / D, dd = e % D;
-    qs[hh][dd] = q[(size_t)(b * Hq + h0 + hh) * D + dd] * tau[h0 + hh] * 1.4426950408889634f;
+    const int h = col_head(hh), j = col_tok(hh);
+    qs[hh][dd] = q[((size_t)(b * m + j) * Hq + h) * D + dd] * tau[h] * 1.4426950408889634f;
     oacc[hh][dd] = 0.f;
   }
   for (int e = tid; e < GH; e += 256) { mst[e] = -INFINITY; lst[e] = 0.f; }
   __syncthreads();
-  const int Lkb = lens ? min(max(lens[b], 0), Lk - 1) + 1 : Lk;
+  const int Lkb = lens ? min(max(lens[b], 0), Lk - m) + m : Lk;
   const int kbeg = c * chunk, kend = min(kbeg + chunk, Lkb);
   auto row_of = [&](int key) { return cache_row(cm, b, Hkv, g, key); };
   for (int k0 = kbeg; k0 < kend; k0 += 256) {
     const int key = k0 + tid;
     for (int hh = 0; hh < GH; ++hh) {
       float s = -INFINITY;
-      if (key < kend) {
+      if (key < min(kend, Lkb - m + col_tok(hh) + 1)) {
         s = 0.f;
         const float *kr = kc + row_of(key) * D;
         for (int dd = 0; dd < D; ++dd) s = fmaf(qs[hh][dd], kr[dd], s);
@@ -366,20 +402,24 @@ __global__ __launch_bounds__(256) void attn_decode_f32_kernel(const float *__res
   }
   for (int e = tid; e < GH * D; e += 256) {
     const int hh = e / D, dd = e % D;
-    float *dst = part + ((size_t)(b * Hq + h0 + hh) * nch + c) * (D + 2);
+    if (sub * GH + hh >= P) continue;
+    const size_t prow = (size_t)(b * Hq + col_head(hh)) * m + col_tok(hh);
+    float *dst = part + (prow * nch + c) * (D + 2);
     dst[2 + dd] = oacc[hh][dd];
     if (dd == 0) { dst[0] = mst[hh]; dst[1] = lst[hh]; }
   }
 }
 
 // o[b, h*D + dd] = sum_c 2^(m_c - M) o_c[dd] / sum_c 2^(m_c - M) l_c
+// (part row (b*Hq + h)*m + j holds new token j of head h; o is [B*m, Hq*D])
 template <typename TV, int D>
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float *__restrict__ part,
-                                                                  int nch, TV *__restrict__ o) {
+                                                                  int nch, int Hq, int m,
+                                                                  TV *__restrict__ o) {
   __shared__ float wts[1024];
   __shared__ float red[256 / D > 0 ? 256 / D : 1][D];
   __shared__ float s_m, s_l;
-  const int bh = blockIdx.x, tid = threadIdx.x;   // bh = b * Hq + h
+  const int bh = blockIdx.x, tid = threadIdx.x;   // bh = (b * Hq + h) * m + j
   const float *p = part + (size_t)bh * nch * (D + 2);
   if (tid < 64) {
     float mm = -INFINITY;
@@ -409,7 +449,8 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float *_
   if (tid < D) {
     float oo = 0.f;
     for (int gi = 0; gi < NG; ++gi) oo += red[gi][tid];
-    o[(size_t)bh * D + tid] = from_f32<TV>(oo / s_l);
+    const int bb = bh / (Hq * m), h = (bh / m) % Hq, j = bh % m;
+    o[((size_t)(bb * m + j) * Hq + h) * D + tid] = from_f32<TV>(oo / s_l);
   }
 }
 
@@ -417,26 +458,33 @@ template <int D>
 static hipError_t dec_bf16(const MixShape &s, const float *q, const StateOut &cm, int Lk,
                            const int *lens, const float *tau, float *part, bf16 *o,
                            hipStream_t stream) {
+  const int m = s.T;                                   // new tokens per sequence
   const int nch = dec_num_chunks(s.B, s.Hkv, Lk);
   const int chunk = dec_chunk_len(Lk, nch);
-  const int GH = dec_heads_per_wg(s.G, DecMaxG<D>::value);
-  const int nsub = s.G / GH;
+  const int GH = m == 1 ? dec_heads_per_wg(s.G, DecMaxG<D>::value)
+                        : (s.G * m < DecMaxG<D>::value ? s.G * m : DecMaxG<D>::value);
+  const int nsub = (s.G * m + GH - 1) / GH;
   const bf16 *kc = reinterpret_cast<const bf16 *>(cm.k_cache);
   const bf16 *vc = reinterpret_cast<const bf16 *>(cm.v_cache);
   const dim3 grid(nch * nsub * s.B * s.Hkv);
-  if (cm.table)   // paged caches serve batches of per-sequence lengths
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, true, true>), grid, dim3(256), 0, stream, q, tau,
-                       kc, vc, cm, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
-  else if (lens)
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, true, false>), grid, dim3(256), 0, stream, q,
-                       tau, kc, vc, cm, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
-  else
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, false, false>), grid, dim3(256), 0, stream, q,
-                       tau, kc, vc, cm, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, part);
+#define DEC_LAUNCH(VL, PG, MU)                                                                  \
+  hipLaunchKernelGGL((attn_decode_mfma_kernel<D, VL, PG, MU>), grid, dim3(256), 0, stream, q, tau, \
+                     kc, vc, cm, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, m, part)
+  if (m > 1) {   // several new tokens: per-sequence lengths, contiguous or paged
+    if (cm.table) DEC_LAUNCH(true, true, true);
+    else DEC_LAUNCH(true, false, true);
+  } else if (cm.table) {   // paged caches serve batches of per-sequence lengths
+    DEC_LAUNCH(true, true, false);
+  } else if (lens) {
+    DEC_LAUNCH(true, false, false);
+  } else {
+    DEC_LAUNCH(false, false, false);
+  }
+#undef DEC_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_combine_kernel<bf16, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
-                     part, nch, o);
+  hipLaunchKernelGGL((attn_decode_combine_kernel<bf16, D>), dim3(s.B * s.Hq * m), dim3(256), 0,
+                     stream, part, nch, s.Hq, m, o);
   return hipGetLastError();
 }
 
@@ -444,18 +492,20 @@ template <int D>
 static hipError_t dec_f32(const MixShape &s, const float *q, const StateOut &cm, int Lk,
                           const int *lens, const float *tau, float *part, float *o,
                           hipStream_t stream) {
+  const int m = s.T;
   const int nch = dec_num_chunks(s.B, s.Hkv, Lk);
   const int chunk = dec_chunk_len(Lk, nch);
-  const int GH = dec_heads_per_wg(s.G, DEC_F32_MAXG);
-  const int nsub = s.G / GH;
+  const int GH = m == 1 ? dec_heads_per_wg(s.G, DEC_F32_MAXG)
+                        : (s.G * m < DEC_F32_MAXG ? s.G * m : DEC_F32_MAXG);
+  const int nsub = (s.G * m + GH - 1) / GH;
   hipLaunchKernelGGL((attn_decode_f32_kernel<D>), dim3(nch * nsub * s.B * s.Hkv), dim3(256), 0,
                      stream, q, tau, reinterpret_cast<const float *>(cm.k_cache),
                      reinterpret_cast<const float *>(cm.v_cache), cm, Lk, lens, chunk, s.Hq, s.Hkv,
-                     s.G, GH, nsub, nch, part);
+                     s.G, GH, nsub, nch, m, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_combine_kernel<float, D>), dim3(s.B * s.Hq), dim3(256), 0, stream,
-                     part, nch, o);
+  hipLaunchKernelGGL((attn_decode_combine_kernel<float, D>), dim3(s.B * s.Hq * m), dim3(256), 0,
+                     stream, part, nch, s.Hq, m, o);
   return hipGetLastError();
 }
 

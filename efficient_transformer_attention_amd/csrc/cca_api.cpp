@@ -134,22 +134,25 @@ Layout prefill_layout(const cca_config &c) {
   return L;
 }
 
-Layout decode_layout(const cca_config &c, int cache_len) {
+// m new tokens per sequence (1 for the single-token step): the projections
+// see B*m rows.
+Layout decode_layout(const cca_config &c, int cache_len, int m = 1) {
   Layout L;
   for (int i = 0; i < CCA_WS_COUNT; ++i) L.off[i] = SIZE_MAX;
-  const size_t B = c.batch, d = c.head_dim;
+  const size_t B = (size_t)c.batch * m, d = c.head_dim;
   const size_t eq = (size_t)c.n_q_heads * d, ekv = (size_t)c.n_kv_heads * d;
   const size_t N = eq + 2 * ekv;
   size_t o = 0;
   L.off[CCA_WS_QKV] = o;  o = align_up(o + B * N * 4, WS_ALIGN);
   L.off[CCA_WS_Q] = o;    o = align_up(o + B * c.n_q_heads * d * 4, WS_ALIGN);
   L.off[CCA_WS_PART] = o;
-  o = align_up(o + decode_partial_floats(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, cache_len + 1) * 4, WS_ALIGN);
+  o = align_up(o + decode_partial_floats(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim,
+                                         cache_len + m, m) * 4, WS_ALIGN);
   L.off[CCA_WS_O] = o;    o = align_up(o + B * eq * elem_size(c.dtype), WS_ALIGN);
-  if (c.batch <= 64) {   // split-contraction partial sums of the two skinny projections
+  if (B <= 64) {   // split-contraction partial sums of the two skinny projections
     const int es = (int)elem_size(c.dtype);
-    const size_t down = (size_t)gemm_splitk_slices(c.batch, (int)N, c.d_model, es) * B * N;
-    const size_t up = (size_t)gemm_splitk_slices(c.batch, c.d_model, (int)eq, es) * B * c.d_model;
+    const size_t down = (size_t)gemm_splitk_slices((int)B, (int)N, c.d_model, es) * B * N;
+    const size_t up = (size_t)gemm_splitk_slices((int)B, c.d_model, (int)eq, es) * B * c.d_model;
     L.off[CCA_WS_SPLITK] = o;
     o = align_up(o + (down > up ? down : up) * 4, WS_ALIGN);
   }
@@ -582,8 +585,8 @@ static cca_status decode_checks(const cca_config *cfg, const cca_weights *w, int
 }
 
 static cca_status dec_downproj(const cca_config &c, const cca_weights *w, const void *x_t,
-                               void *ws, const Layout &L, hipStream_t st) {
-  const int M = c.batch, E = c.d_model;
+                               void *ws, const Layout &L, hipStream_t st, int m = 1) {
+  const int M = c.batch * m, E = c.d_model;
   const int N = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   float *qkv = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_QKV));
   size_t skf;
@@ -600,10 +603,10 @@ static cca_status dec_downproj(const cca_config &c, const cca_weights *w, const 
 
 static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
                           const int32_t *lens, const StateOut &si, const StateOut &so, void *ws,
-                          const Layout &L, hipStream_t st) {
+                          const Layout &L, hipStream_t st, int m = 1) {
   MixShape s = mix_shape(c);
-  s.T = 1;
-  s.Tp = 1;
+  s.T = m;                       // new tokens per sequence
+  s.Tp = m;
   const float *qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
   float *q = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_Q));
   hipError_t e;
@@ -616,18 +619,18 @@ static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
 
 static cca_status dec_attn(const cca_config &c, const cca_weights *w, int32_t Lc,
                            const int32_t *lens, const StateOut &cache, void *ws, const Layout &L,
-                           hipStream_t st) {
+                           hipStream_t st, int m = 1) {
   MixShape s = mix_shape(c);
-  s.T = 1;
-  s.Tp = 1;
+  s.T = m;                       // new tokens per sequence
+  s.Tp = m;
   const float *q = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_Q));
   float *part = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_PART));
   hipError_t e;
   if (c.dtype == CCA_BF16)
-    e = launch_attention_decode<bf16>(s, q, cache, Lc + 1, lens, w->tau, part,
+    e = launch_attention_decode<bf16>(s, q, cache, Lc + m, lens, w->tau, part,
                                       (bf16 *)wsp(ws, L, CCA_WS_O), st);
   else
-    e = launch_attention_decode<float>(s, q, cache, Lc + 1, lens, w->tau, part,
+    e = launch_attention_decode<float>(s, q, cache, Lc + m, lens, w->tau, part,
                                        (float *)wsp(ws, L, CCA_WS_O), st);
   return check_launch(e, st);
 }
@@ -801,6 +804,77 @@ cca_status cca_prefill_forward_paged(const cca_config *cfg, const cca_weights *w
   CCA_TRY(run_convmix(*cfg, w, state_of(so), ws, L, st));
   CCA_TRY(run_attention(*cfg, w, ws, L, st));
   return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
+}
+
+}  // extern "C"
+
+// ---- several new tokens per sequence -----------------------------------------
+
+static constexpr int MAX_NEW_TOKENS = 16;
+
+static cca_status multi_checks(const cca_config *cfg, const cca_weights *w, int32_t n_new,
+                               int32_t Lmax, void *ws, size_t wsb, Layout *lay) {
+  CCA_TRY(validate_shape(cfg, false));
+  CCA_TRY(check_weights(w));
+  if (n_new < 1 || Lmax < 0) return CCA_ERR_INVALID_ARG;
+  if (n_new > MAX_NEW_TOKENS || !convmix_decode_fits(cfg->n_q_heads / cfg->n_kv_heads,
+                                                     cfg->head_dim, n_new))
+    return CCA_ERR_UNSUPPORTED;
+  *lay = decode_layout(decode_cfg(cfg), Lmax, n_new);
+  return check_ws(ws, wsb, lay->total);
+}
+
+extern "C" {
+
+size_t cca_decode_multi_workspace_size(const cca_config *cfg, int32_t n_new, int32_t max_cache_len) {
+  if (validate_shape(cfg, false) != CCA_OK || n_new < 1 || n_new > MAX_NEW_TOKENS ||
+      max_cache_len < 0)
+    return 0;
+  return decode_layout(decode_cfg(cfg), max_cache_len, n_new).total;
+}
+
+cca_status cca_decode_multi(const cca_config *cfg, const cca_weights *w, const void *x_new,
+                            int32_t n_new, const int32_t *cache_lens, int32_t max_cache_len,
+                            const cca_state *si, const cca_state *so, void *y_new, void *ws,
+                            size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(multi_checks(cfg, w, n_new, max_cache_len, ws, wsb, &L));
+  if (!x_new || !y_new || !aligned16(x_new) || !aligned16(y_new)) return CCA_ERR_INVALID_ARG;
+  if (!cache_lens || reinterpret_cast<uintptr_t>(cache_lens) % 4) return CCA_ERR_INVALID_ARG;
+  const cca_config c = decode_cfg(cfg);
+  // the last new token's slot must fit: capacity > max_cache_len + n_new - 1
+  CCA_TRY(check_decode_state(c, max_cache_len + n_new - 1, si, so));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CCA_TRY(dec_downproj(c, w, x_new, ws, L, st, n_new));
+  CCA_TRY(dec_mix(c, w, max_cache_len, cache_lens, state_of(si), state_of(so), ws, L, st, n_new));
+  CCA_TRY(dec_attn(c, w, max_cache_len, cache_lens, state_of(si), ws, L, st, n_new));
+  return run_upproj(c, w, y_new, ws, L, c.batch * n_new, st);
+}
+
+cca_status cca_decode_multi_paged(const cca_config *cfg, const cca_weights *w, const void *x_new,
+                                  int32_t n_new, const int32_t *cache_lens,
+                                  int32_t max_cache_len, const cca_paged_state *si,
+                                  const cca_paged_state *so, void *y_new, void *ws, size_t wsb,
+                                  void *stream) {
+  Layout L;
+  CCA_TRY(multi_checks(cfg, w, n_new, max_cache_len, ws, wsb, &L));
+  if (!x_new || !y_new || !aligned16(x_new) || !aligned16(y_new)) return CCA_ERR_INVALID_ARG;
+  if (!cache_lens || reinterpret_cast<uintptr_t>(cache_lens) % 4) return CCA_ERR_INVALID_ARG;
+  const cca_config c = decode_cfg(cfg);
+  CCA_TRY(check_paged(c, si, (long long)max_cache_len + n_new));
+  if (!so) return CCA_ERR_INVALID_ARG;
+  if ((so->k_pages && so->k_pages != si->k_pages) || (so->v_pages && so->v_pages != si->v_pages) ||
+      (so->block_table && so->block_table != si->block_table))
+    return CCA_ERR_INVALID_ARG;
+  if (c.seq_conv_k > 1 && (!si->conv_q || !si->conv_k || !so->conv_q || !so->conv_k))
+    return CCA_ERR_INVALID_ARG;
+  if (c.use_value_shift && (!si->vshift || !so->vshift)) return CCA_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const StateOut in = state_of(si), out = state_of(so);
+  CCA_TRY(dec_downproj(c, w, x_new, ws, L, st, n_new));
+  CCA_TRY(dec_mix(c, w, max_cache_len, cache_lens, in, out, ws, L, st, n_new));
+  CCA_TRY(dec_attn(c, w, max_cache_len, cache_lens, in, ws, L, st, n_new));
+  return run_upproj(c, w, y_new, ws, L, c.batch * n_new, st);
 }
 
 }  // extern "C"

@@ -77,10 +77,11 @@ template <typename TQ, typename TV>
 hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
                                   TQ *k, TV *vt, const StateOut &st, hipStream_t stream);
 
-// The same mixing for one new token per sequence at position L (per
-// sequence lens[b], clamped to [0, L], when lens is not null), using the
-// carried window / vshift of state_in; writes q (fp32 [B,Hq,d]), the k and v
-// rows at that cache slot, and the rolled state into state_out.
+// The same mixing for m = s.T new tokens per sequence at positions L .. L+m-1
+// (L per sequence lens[b], clamped to [0, L], when lens is not null), using
+// the carried window / vshift of state_in; qkv is [B*m, e_q + 2 e_kv]; writes
+// q (fp32 [B, m, Hq, d]), the k and v rows at those cache slots, and the
+// rolled state into state_out.
 template <typename TV>
 hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const float *qkv, int L,
                                  const int *lens, const StateOut &in, const StateOut &out,
@@ -96,10 +97,12 @@ hipError_t launch_attention_prefill(const MixShape &s, const TQ *q, const TQ *k,
                                     const float *tau, TV *o, float *lse, hipStream_t stream);
 bool attention_supported(int d, bool f32);
 
-// Split-KV decode attention over Lk = L + 1 cached keys (per sequence
-// lens[b] + 1, clamped to [1, Lk], when lens is not null; the chunking
-// follows Lk) of the cache `cache` (contiguous or paged), then the
-// log-sum-exp combine.  part: fp32 scratch of decode_partial_floats() floats.
+// Split-KV decode attention of m = s.T new tokens per sequence (q [B, m, Hq,
+// d]) over Lk = L + m cached keys (per sequence lens[b] + m, lens clamped to
+// [0, Lk - m], when lens is not null; the chunking follows Lk) of the cache
+// `cache` (contiguous or paged); new token j sees keys 0 .. L + j.  Then the
+// log-sum-exp combine into o [B*m, Hq*d].  part: fp32 scratch of
+// decode_partial_floats(..., m) floats.
 template <typename TV>
 hipError_t launch_attention_decode(const MixShape &s, const float *q, const StateOut &cache, int Lk,
                                    const int *lens, const float *tau, float *part, TV *o,
@@ -108,11 +111,13 @@ hipError_t launch_attention_decode(const MixShape &s, const float *q, const Stat
 // Whether the mixing kernel's LDS tile of one kv group (G query heads + k +
 // v, 19 tokens) fits the 64 KiB it may use.
 bool convmix_fits(int G, int d);
+// Whether the decode mixing tile of m new tokens fits its LDS.
+bool convmix_decode_fits(int G, int d, int m);
 
 // Keys handled by one workgroup of the split-KV decode attention, and the
 // partial-state scratch it needs.
 int decode_chunk_keys(int d);
-size_t decode_partial_floats(int B, int Hq, int Hkv, int d, int Lk);
+size_t decode_partial_floats(int B, int Hq, int Hkv, int d, int Lk, int m = 1);
 
 // ---- backward pass ---------------------------------------------------------
 

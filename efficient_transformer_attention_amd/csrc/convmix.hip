@@ -337,11 +337,11 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   }
 }
 
-// One new token per sequence at position L (lens[b] when lens is given,
-// clamped to [0, L]).  One workgroup per (b, g); the 4-row tile holds tokens
-// L-3 .. L: rows from the carried window, the new row from the
-// down-projection.  All state reads finish before the barrier, so
-// state_out may alias state_in.
+// m = s.T new tokens per sequence at positions L .. L+m-1 (L = lens[b] when
+// lens is given, clamped to [0, L]).  One workgroup per (b, g); the tile
+// holds tokens L-3 .. L+m-1: three rows from the carried window, then the m
+// new rows from the down-projection.  All state reads finish before the
+// barrier, so state_out may alias state_in.
 template <typename TV, int D>
 __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps w,
                                                              const float *__restrict__ qkv,
@@ -351,8 +351,9 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
                                                              float *__restrict__ qout) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int G = s.G, CW = (G + 2) * D;
-  float *tile = lds;                               // 4 rows
-  float *staps = tile + 4 * CW;
+  const int m = s.T, R = 3 + m;
+  float *tile = lds;                               // R rows
+  float *staps = tile + R * CW;
   float *ctaps = staps + (G + 1) * D * 4;
   float2 *rot = reinterpret_cast<float2 *>(ctaps + ((G + 1) * 4 + 3) / 4 * 4);
 
@@ -366,18 +367,18 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
   const TV *ck = reinterpret_cast<const TV *>(in.conv_k);
   const TV *vs = reinterpret_cast<const TV *>(in.vshift);
 
-  // all loads of the 4-row tile are issued before their LDS stores
+  // all loads of the tile are issued before their LDS stores
   constexpr int LB = 8;
-  for (int e0 = 0; e0 < 4 * CW; e0 += 256 * LB) {
+  for (int e0 = 0; e0 < R * CW; e0 += 256 * LB) {
     float v[LB];
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
       const int e = e0 + tid + 256 * u;
       const int r = e / CW, col = e % CW;
       v[u] = 0.f;
-      if (e >= 4 * CW) continue;
-      if (r == 3) {
-        v[u] = qkv[(size_t)b * N + group_col(col, g, G, D, eq, ekv)];
+      if (e >= R * CW) continue;
+      if (r >= 3) {
+        v[u] = qkv[(size_t)(b * m + r - 3) * N + group_col(col, g, G, D, eq, ekv)];
       } else if (r >= 4 - s.ks && col < (G + 1) * D) {
         const int sl = r - (4 - s.ks);           // window slot of token L-3+r
         v[u] = col < G * D ? to_f32(cq[(size_t)(b * ks1 + sl) * eq + g * G * D + col])
@@ -389,11 +390,12 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
       const int e = e0 + tid + 256 * u;
-      if (e < 4 * CW) tile[e] = v[u];
+      if (e < R * CW) tile[e] = v[u];
     }
   }
   load_taps<D>(s, w, g, staps, ctaps);
-  for (int e = tid; e < D / 2; e += 256) rot[e] = rope_cs_theta(L, s.theta[e], s.rope_base);
+  for (int e = tid; e < m * (D / 2); e += 256)
+    rot[e] = rope_cs_theta(L + e / (D / 2), s.theta[e % (D / 2)], s.rope_base);
   __syncthreads();
 
   constexpr int LPU = D / 4;
@@ -401,39 +403,44 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
   const int li = tid % LPU, ui = tid / LPU;
   TV *kc = reinterpret_cast<TV *>(in.k_cache);
   TV *vc = reinterpret_cast<TV *>(in.v_cache);
-  for (int u0 = 0; u0 < G + 1; u0 += upp) {
-    const int slot = u0 + ui;
-    const bool active = slot < G + 1;
+  // units: (new token j, head slot), slot 0..G-1 the query heads, G the key head
+  for (int u0 = 0; u0 < m * (G + 1); u0 += upp) {
+    const int unit = u0 + ui;
+    const bool active = unit < m * (G + 1);
+    const int j = active ? unit / (G + 1) : 0, slot = active ? unit % (G + 1) : 0;
     float stp[4][4], ctp[4];
-    lane_taps<D>(staps, ctaps, active ? slot : 0, li, stp, ctp);
+    lane_taps<D>(staps, ctaps, slot, li, stp, ctp);
     float y[4];
-    mix_unit<D>(tile, CW, 0, active ? slot : 0, G, li, stp, ctp, s, rot[2 * li], rot[2 * li + 1], y);
+    mix_unit<D>(tile, CW, j, slot, G, li, stp, ctp, s, rot[j * (D / 2) + 2 * li],
+                rot[j * (D / 2) + 2 * li + 1], y);
     if (!active) continue;
     if (slot < G) {
-      Store4<float>::st(qout + (size_t)(b * s.Hq + g * G + slot) * D + 4 * li, y);
+      Store4<float>::st(qout + ((size_t)(b * m + j) * s.Hq + g * G + slot) * D + 4 * li, y);
     } else {
-      Store4<TV>::st(kc + cache_row(in, b, s.Hkv, g, L) * D + 4 * li, y);
+      Store4<TV>::st(kc + cache_row(in, b, s.Hkv, g, L + j) * D + 4 * li, y);
     }
   }
-  // value row of the new token into the cache
-  for (int c4 = tid; c4 < D / 4; c4 += 256)
-    Store4<TV>::st(vc + cache_row(in, b, s.Hkv, g, L) * D + 4 * c4,
-                   tile + (3 - shifted) * CW + (G + 1) * D + 4 * c4);
-  // rolled state: slot sl holds token L - ks1 + 1 + sl = tile row 5 - ks + sl
+  // value rows of the new tokens into the cache
+  for (int e = tid; e < m * (D / 4); e += 256) {
+    const int j = e / (D / 4), c4 = e % (D / 4);
+    Store4<TV>::st(vc + cache_row(in, b, s.Hkv, g, L + j) * D + 4 * c4,
+                   tile + (3 + j - shifted) * CW + (G + 1) * D + 4 * c4);
+  }
+  // rolled state: slot sl holds token L + m - ks1 + sl = tile row m + 3 - ks1 + sl
   TV *oq = reinterpret_cast<TV *>(out.conv_q);
   TV *ok = reinterpret_cast<TV *>(out.conv_k);
   for (int e = tid; e < ks1 * G * D; e += 256) {
     const int sl = e / (G * D), c = e % (G * D);
-    oq[(size_t)(b * ks1 + sl) * eq + g * G * D + c] = from_f32<TV>(tile[(5 - s.ks + sl) * CW + c]);
+    oq[(size_t)(b * ks1 + sl) * eq + g * G * D + c] = from_f32<TV>(tile[(m + 3 - ks1 + sl) * CW + c]);
   }
   for (int e = tid; e < ks1 * D; e += 256) {
     const int sl = e / D, c = e % D;
-    ok[(size_t)(b * ks1 + sl) * ekv + g * D + c] = from_f32<TV>(tile[(5 - s.ks + sl) * CW + G * D + c]);
+    ok[(size_t)(b * ks1 + sl) * ekv + g * D + c] = from_f32<TV>(tile[(m + 3 - ks1 + sl) * CW + G * D + c]);
   }
   if (shifted && out.vshift)
     for (int c = tid; c < D; c += 256)
       reinterpret_cast<TV *>(out.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
-          from_f32<TV>(tile[3 * CW + (G + 1) * D + c]);
+          from_f32<TV>(tile[(m + 2) * CW + (G + 1) * D + c]);
 }
 
 static size_t mix_lds_bytes(int rows, int G, int D, int TC) {
@@ -450,6 +457,10 @@ static int mix_chunk(int G, int D) { return mix_lds_bytes(32 + HALO, G, D, 32) <
 static bool mix_prefetch_fits(int G, int D, int TC) {
   const int cpr = (G + 2) * D / 4, rstep = 256 / cpr;
   return (TC + rstep - 1) / rstep <= MIX_PF;
+}
+
+bool convmix_decode_fits(int G, int d, int m) {
+  return m >= 1 && mix_lds_bytes(3 + m, G, d, m) <= 65536;
 }
 
 bool convmix_fits(int G, int d) {
@@ -489,7 +500,7 @@ static hipError_t convmix_decode_d(const MixShape &s, const MixTaps &w, const fl
                                    const int *lens,
                                    const StateOut &in, const StateOut &out, float *q,
                                    hipStream_t stream) {
-  const size_t lds = mix_lds_bytes(4, s.G, D, 1);
+  const size_t lds = mix_lds_bytes(3 + s.T, s.G, D, s.T);
   hipLaunchKernelGGL((convmix_decode_kernel<TV, D>), dim3(s.B * s.Hkv), dim3(256), lds, stream, s,
                      w, qkv, L, lens, in, out, q);
   return hipGetLastError();

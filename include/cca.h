@@ -282,6 +282,33 @@ cca_status cca_prefill_forward_paged(const cca_config *cfg, const cca_weights *w
                                      void *y, const cca_paged_state *state_out, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* Several new tokens per sequence in one step (speculative verification,
+ * chunked appends) [GS-EN "1. Problem Statement": autoregressive decode
+ * against the cache].  x_new [B, n_new, E] -> y_new [B, n_new, E].
+ * Sequence b's new tokens sit at positions cache_lens[b] .. cache_lens[b] +
+ * n_new - 1: steps a1-a7 run over them with the carried window, their k and
+ * v rows are written at those slots, new token j attends to keys
+ * 0 .. cache_lens[b] + j, and the state rolls past the last one.  The result
+ * equals n_new single-token steps.  cache_lens: device int32 [B], clamped to
+ * [0, max_cache_len]; capacity must exceed max_cache_len + n_new - 1.
+ * 1 <= n_new <= 16 (CCA_ERR_UNSUPPORTED beyond, or when the kv group's
+ * mixing tile does not fit).  workspace: >=
+ * cca_decode_multi_workspace_size(cfg, n_new, max_cache_len) bytes. */
+size_t cca_decode_multi_workspace_size(const cca_config *cfg, int32_t n_new,
+                                       int32_t max_cache_len);
+cca_status cca_decode_multi(const cca_config *cfg, const cca_weights *w, const void *x_new,
+                            int32_t n_new, const int32_t *cache_lens, int32_t max_cache_len,
+                            const cca_state *state_in, const cca_state *state_out, void *y_new,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* cca_decode_multi on a paged cache (max_pages_per_seq * page_size >=
+ * max_cache_len + n_new); as cca_decode_step_paged otherwise. */
+cca_status cca_decode_multi_paged(const cca_config *cfg, const cca_weights *w, const void *x_new,
+                                  int32_t n_new, const int32_t *cache_lens,
+                                  int32_t max_cache_len, const cca_paged_state *state_in,
+                                  const cca_paged_state *state_out, void *y_new, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *cca_status_string(cca_status s);
 

@@ -215,3 +215,24 @@ def test_paged_decode_rejects_before_launch(L):
               None) == L.CCA_ERR_INVALID_ARG                           # 192 rows < T = 200
     assert fp(C.byref(cfg2), C.byref(w), 0x10000, 0x20000, None, 0x100000, need2,
               None) == L.CCA_ERR_INVALID_ARG
+
+
+def test_decode_multi_rejects_before_launch(L):
+    s = CCAShape(batch=2, seq_len=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    cfg = L.make_config(s)
+    need = L.decode_multi_workspace_size(cfg, 4, 100)
+    assert need > L.decode_workspace_size(cfg, 100)
+    assert L.decode_multi_workspace_size(cfg, 0, 100) == 0
+    assert L.decode_multi_workspace_size(cfg, 17, 100) == 0
+    w = _fake_weights(L)
+    f = L.lib.cca_decode_multi
+    good = L._State(0x30000, 0x40000, 104, 0, 0x50000, 0x60000, 0x70000)   # slots 0 .. 103
+    small = L._State(0x30000, 0x40000, 103, 0, 0x50000, 0x60000, 0x70000)  # no room for slot 103
+    args = lambda si, m=4, lens=0xA0000, wsb=need: (C.byref(cfg), C.byref(w), 0x10000, m, lens, 100,
+                                                    C.byref(si), C.byref(si), 0x20000, 0x100000,
+                                                    wsb, None)
+    assert f(*args(good, lens=None)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(small)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(good, m=0)) == L.CCA_ERR_INVALID_ARG
+    assert f(*args(good, m=17)) == L.CCA_ERR_UNSUPPORTED
+    assert f(*args(good, wsb=need - 1)) == L.CCA_ERR_WORKSPACE
