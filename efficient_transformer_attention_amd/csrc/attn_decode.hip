@@ -29,6 +29,10 @@ namespace cca {
 static constexpr int DEC_CHUNK = 4096;   // keys per workgroup
 static constexpr int DEC_TILE = 32;      // keys per MFMA tile
 static constexpr int DEC_F32_MAXG = 8;   // query heads per workgroup, fp32 path
+// Pages one chunk of keys can span: chunks hold at most 2 * DEC_CHUNK + 64
+// keys (dec_num_chunks starts at Lk / (2 * DEC_CHUNK)) and pages are at least
+// 32 rows.
+static constexpr int DEC_MAX_PAGES = (2 * 4096 + 64) / 32 + 2;
 
 // Query heads per workgroup of the MFMA path (the N columns of a 32x32 tile);
 // capped lower at d = 128 so the merge buffer stays within 64 KiB of LDS.
@@ -156,10 +160,26 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   const bf16 *kb = kc + (size_t)(b * Hkv + g) * cm.capacity * D;
   const bf16 *vb = vc + (size_t)(b * Hkv + g) * cm.capacity * D;
   unsigned char *myv = smem + wave * TPI * VTILE;
+  // paged: the pages of this chunk's rows, staged once in LDS (a chunk is at
+  // most DEC_MAX_PAGES pages), so a row's page is an LDS read
+  __shared__ int spages[PAGED ? DEC_MAX_PAGES : 1];
+  const int pb0 = PAGED ? kbeg / cm.page : 0;
+  if constexpr (PAGED) {
+    const int npb = kend > kbeg ? (kend - 1) / cm.page - pb0 + 1 : 0;
+    for (int i = tid; i < npb; i += 256) {
+      const int pg = cm.table[(size_t)b * cm.mpps + pb0 + i];
+      spages[i] = pg < 0 ? 0 : (pg >= cm.npages ? cm.npages - 1 : pg);
+    }
+    __syncthreads();
+  }
   // element offset of a cache row: contiguous from this (b, g) base, or paged
   auto krow_ptr = [&](const bf16 *base_c, const bf16 *pool, int row) {
-    if constexpr (PAGED) return pool + cache_row(cm, b, Hkv, g, row) * D;
-    else return base_c + (size_t)row * D;
+    if constexpr (PAGED) {
+      const int pi = row / cm.page;
+      return pool + (((size_t)spages[pi - pb0] * Hkv + g) * cm.page + (row - pi * cm.page)) * D;
+    } else {
+      return base_c + (size_t)row * D;
+    }
   };
 
   f32x16 acc[ND];
@@ -467,6 +487,7 @@ static hipError_t dec_bf16(const MixShape &s, const float *q, const StateOut &cm
   const bf16 *kc = reinterpret_cast<const bf16 *>(cm.k_cache);
   const bf16 *vc = reinterpret_cast<const bf16 *>(cm.v_cache);
   const dim3 grid(nch * nsub * s.B * s.Hkv);
+  if (cm.table && (chunk + cm.page - 1) / cm.page + 1 > DEC_MAX_PAGES) return hipErrorInvalidValue;
 #define DEC_LAUNCH(VL, PG, MU)                                                                  \
   hipLaunchKernelGGL((attn_decode_mfma_kernel<D, VL, PG, MU>), grid, dim3(256), 0, stream, q, tau, \
                      kc, vc, cm, Lk, lens, chunk, s.Hq, s.Hkv, s.G, GH, nsub, nch, m, part)
