@@ -176,6 +176,28 @@ def paged_decode(cca, T, sd, dcfg, dw, xt, dl, L, st, K, dev, page=256):
     return ms, page
 
 
+def multi_decode(cca, T, sd, dcfg, dw, dl, Lmax, st, K, dev, m):
+    """cca_decode_multi with m new tokens per sequence at the per-sequence
+    lengths dl (clamped to Lmax), timed with HIP events."""
+    import numpy as np
+    import torch
+    x = torch.from_numpy(np.random.default_rng(3).standard_normal(
+        (sd.batch, m, sd.d_model)).astype(np.float32)).to(dev, torch.bfloat16)
+    y = torch.empty_like(x)
+    dlm = torch.clamp(dl, max=Lmax).contiguous()
+    ws = T.workspace(cca.decode_multi_workspace_size(dcfg, m, Lmax), dev)
+    cca.decode_multi(dcfg, dw, x, m, dlm, Lmax, st, st, y, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b_ in ev:
+        a.record()
+        cca.decode_multi(dcfg, dw, x, m, dlm, Lmax, st, st, y, ws)
+        b_.record()
+    torch.cuda.synchronize()
+    del ws
+    return sum(a.elapsed_time(b_) for a, b_ in ev) / K
+
+
 def training_step(cca, T, sp, pcfg, pw, x, dev, K):
     """forward_train + backward on the prefill workload, timed with HIP events."""
     import torch
@@ -403,6 +425,11 @@ def main():
     # (256-token pages in a seeded random order, the same per-sequence lengths)
     paged_ms, page = paged_decode(cca, T, sd, dcfg, dw, xt, dl, L, st, K, dev)
 
+    # ---- timed region 3c: four new tokens per sequence in one step ---------
+    # (the same lengths; the cache is read once for the four tokens)
+    multi_m = 4
+    multi_ms = multi_decode(cca, T, sd, dcfg, dw, dl, L - multi_m, st, K, dev, multi_m)
+
     # ---- timed region 4: a training step on the prefill workload ----------
     # forward_train (the forward keeping its activations) then the backward
     # pass with a seeded upstream gradient; every gradient is computed
@@ -460,6 +487,10 @@ def main():
         "decode_paged": {"page_size": page, "lengths": "as decode_varlen",
                          "pages": "seeded random order", "ms": round(paged_ms, 4),
                          "step_hbm_gbs": round(varlen_bytes / (paged_ms * 1e-3) / 1e9, 1)},
+        "decode_multi": {"new_tokens": multi_m, "lengths": "as decode_varlen, minus the new tokens",
+                         "ms": round(multi_ms, 4),
+                         "tokens_per_s": round(sd.batch * multi_m / (multi_ms * 1e-3), 1),
+                         "single_token_tokens_per_s": round(sd.batch / (varlen_ms * 1e-3), 1)},
         "train": train,
         "attn_tflops": round(attn_tflops, 1),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
