@@ -18,6 +18,9 @@
 //  * The S^T accumulator holds one query head per lane, which is the B-operand
 //    layout of O^T = V^T P^T; V rows go through a wave-private LDS tile
 //    (coalesced 16-byte writes, 16-bit transposed reads).
+//  * The next tiles' V rows are requested as soon as this tile's V is staged
+//    in LDS, their K rows as soon as the QK^T MFMAs have read K, so each
+//    load has most of an iteration to land.
 //  * Online softmax per lane in fp32 (exp2, tau * log2(e) folded into q);
 //    the 4 waves merge through LDS and each chunk leaves (m, l, o) in fp32
 //    scratch; a second kernel merges the chunks with the log-sum-exp rule.
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   // to its last key (finite data, masked below)
   constexpr int VPL = (DEC_TILE * D / 8 + 63) / 64;   // 16-byte V pieces per lane per tile
   u32x4 kreg[TPI][QC], vreg[TPI][VPL];
-  auto gload = [&](int t0) {
+  auto gload_k = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < TPI; ++u) {
       const int k0 = kbeg + (t0 + u) * DEC_TILE;
@@ -199,6 +202,12 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
       const bf16 *kp = krow_ptr(kb, kc, krow);
 #pragma unroll
       for (int cc = 0; cc < QC; ++cc) kreg[u][cc] = ld16(kp + 16 * cc + 8 * hl);
+    }
+  };
+  auto gload_v = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < TPI; ++u) {
+      const int k0 = kbeg + (t0 + u) * DEC_TILE;
 #pragma unroll
       for (int r = 0; r < VPL; ++r) {
         const int e = lane + 64 * r;
@@ -209,6 +218,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
       }
     }
   };
+  auto gload = [&](int t0) { gload_k(t0); gload_v(t0); };
 
   const int step = 4 * TPI;
   int t = wave * TPI;
@@ -228,6 +238,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
         }
       }
     __builtin_amdgcn_wave_barrier();
+    if (t + step < ntile) gload_v(t + step);   // V registers are free once staged
     f32x16 s[TPI];
 #pragma unroll
     for (int u = 0; u < TPI; ++u) {
@@ -239,7 +250,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
         s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qlo[cc], s[u], 0, 0, 0);
       }
     }
-    if (t + step < ntile) gload(t + step);   // next tiles' loads overlap this iteration's math
+    if (t + step < ntile) gload_k(t + step);   // K registers are free after the QK MFMAs
     // mask keys past the chunk end, online softmax per column over TPI*32 keys
     float mx = -INFINITY;
 #pragma unroll
