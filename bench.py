@@ -430,6 +430,21 @@ def main():
     multi_m = 4
     multi_ms = multi_decode(cca, T, sd, dcfg, dw, dl, L - multi_m, st, K, dev, multi_m)
 
+    # ---- timed region 3d: the fused down-projection + mixing prefill -------
+    fused_ms = None
+    if cca.validate_config(pcfg) == cca.CCA_OK and sp.n_q_heads == sp.n_kv_heads and \
+            sp.head_dim == 64 and sp.seq_len % 128 == 0 and sp.dtype == "bf16":
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        cca.prefill_forward_fused(pcfg, pw, x, y, pws)
+        torch.cuda.synchronize()
+        for a, b_ in fev:
+            a.record()
+            cca.prefill_forward_fused(pcfg, pw, x, y, pws)
+            b_.record()
+        torch.cuda.synchronize()
+        fused_ms = sum(a.elapsed_time(b_) for a, b_ in fev) / K
+
     # ---- timed region 4: a training step on the prefill workload ----------
     # forward_train (the forward keeping its activations) then the backward
     # pass with a seeded upstream gradient; every gradient is computed
@@ -491,6 +506,7 @@ def main():
                          "ms": round(multi_ms, 4),
                          "tokens_per_s": round(sd.batch * multi_m / (multi_ms * 1e-3), 1),
                          "single_token_tokens_per_s": round(sd.batch / (varlen_ms * 1e-3), 1)},
+        "prefill_fused_ms": None if fused_ms is None else round(fused_ms, 4),
         "train": train,
         "attn_tflops": round(attn_tflops, 1),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},

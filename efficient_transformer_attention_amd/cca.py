@@ -32,6 +32,7 @@ EXPORTS = (
     "cca_train_workspace_size", "cca_prefill_forward_train", "cca_prefill_backward",
     "cca_decode_step_paged", "cca_prefill_forward_paged",
     "cca_decode_multi_workspace_size", "cca_decode_multi", "cca_decode_multi_paged",
+    "cca_prefill_forward_fused",
 )
 
 
@@ -107,6 +108,7 @@ def _load():
                                             P(_PagedState), vp, vp, sz, vp]),
         "cca_prefill_forward_paged": (C.c_int, [cfgp, wp, vp, vp, P(_PagedState), vp, sz, vp]),
         "cca_decode_multi_workspace_size": (sz, [cfgp, C.c_int32, C.c_int32]),
+        "cca_prefill_forward_fused": (C.c_int, [cfgp, wp, vp, vp, vp, sz, vp]),
         "cca_decode_multi": (C.c_int, [cfgp, wp, vp, C.c_int32, vp, C.c_int32, sp, sp, vp, vp, sz,
                                        vp]),
         "cca_decode_multi_paged": (C.c_int, [cfgp, wp, vp, C.c_int32, vp, C.c_int32,
@@ -382,3 +384,9 @@ def decode_multi_paged(cfg: Config, w: Weights, x_new, n_new: int, cache_lens, m
                                       C.byref(state_in.struct()), C.byref(state_out.struct()),
                                       _ptr(y_new), _ptr(workspace), _wsb(workspace),
                                       _stream(stream)), "cca_decode_multi_paged")
+
+
+def prefill_forward_fused(cfg: Config, w: Weights, x, y, workspace, stream=None):
+    _check(lib.cca_prefill_forward_fused(C.byref(cfg), C.byref(w.struct()), _ptr(x), _ptr(y),
+                                         _ptr(workspace), _wsb(workspace), _stream(stream)),
+           "cca_prefill_forward_fused")

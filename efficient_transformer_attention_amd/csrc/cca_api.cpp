@@ -113,6 +113,17 @@ cca_status validate_shape(const cca_config *c, bool need_seq) {
   return CCA_OK;
 }
 
+// Shapes cca_prefill_forward_fused takes: bf16 kv groups of one query head
+// with d = 64 and T a multiple of 128.
+bool fused_downproj_mix(const cca_config &c) {
+  if (c.dtype != CCA_BF16) return false;
+  const int G = c.n_q_heads / c.n_kv_heads;
+  if (!downproj_mix_supported(G, c.head_dim, c.seq_len, c.d_model)) return false;
+  const size_t N = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const size_t lim = (1ull << 32) - 2 * (size_t)c.d_model;
+  return (size_t)c.batch * c.seq_len * c.d_model * 2 < lim && N * c.d_model * 2 < lim;
+}
+
 struct Layout {
   size_t off[CCA_WS_COUNT];
   size_t total;
@@ -130,6 +141,10 @@ Layout prefill_layout(const cca_config &c) {
   L.off[CCA_WS_K] = o;   o = align_up(o + B * c.n_kv_heads * Tp * d * qk_elem_size(c), WS_ALIGN);
   L.off[CCA_WS_VT] = o;  o = align_up(o + B * c.n_kv_heads * d * Tp * elem_size(c.dtype), WS_ALIGN);
   L.off[CCA_WS_O] = o;   o = align_up(o + B * T * eq * elem_size(c.dtype), WS_ALIGN);
+  if (fused_downproj_mix(c)) {   // halo rows of the fused down-projection + mixing
+    L.off[CCA_WS_PART] = o;
+    o = align_up(o + downproj_mix_halo_bytes(c.batch, c.seq_len, c.d_model, (int)N), WS_ALIGN);
+  }
   L.total = o;
   return L;
 }
@@ -324,6 +339,23 @@ cca_status run_convmix(const cca_config &c, const cca_weights *w, const StateOut
                                            (bf16 *)wsp(ws, L, CCA_WS_K),
                                            (bf16 *)wsp(ws, L, CCA_WS_VT), so, st);
   }
+  return check_launch(e, st);
+}
+
+cca_status run_downproj_mix(const cca_config &c, const cca_weights *w, const void *x, void *ws,
+                            const Layout &L, hipStream_t st) {
+  const MixShape s = mix_shape(c);
+  hipError_t e;
+  if (qk_is_f16(c))
+    e = launch_downproj_mix<f16, bf16>(s, taps_of(w), (const bf16 *)x, (const bf16 *)w->w_qkv,
+                                       c.d_model, wsp(ws, L, CCA_WS_PART),
+                                       (f16 *)wsp(ws, L, CCA_WS_Q), (f16 *)wsp(ws, L, CCA_WS_K),
+                                       (bf16 *)wsp(ws, L, CCA_WS_VT), st);
+  else
+    e = launch_downproj_mix<bf16, bf16>(s, taps_of(w), (const bf16 *)x, (const bf16 *)w->w_qkv,
+                                        c.d_model, wsp(ws, L, CCA_WS_PART),
+                                        (bf16 *)wsp(ws, L, CCA_WS_Q), (bf16 *)wsp(ws, L, CCA_WS_K),
+                                        (bf16 *)wsp(ws, L, CCA_WS_VT), st);
   return check_launch(e, st);
 }
 
@@ -537,6 +569,18 @@ cca_status cca_prefill_forward(const cca_config *cfg, const cca_weights *w, cons
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CCA_TRY(run_downproj(*cfg, w, x, ws, L, st));
   CCA_TRY(run_convmix(*cfg, w, state_of(state_out), ws, L, st));
+  CCA_TRY(run_attention(*cfg, w, ws, L, st));
+  return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
+}
+
+cca_status cca_prefill_forward_fused(const cca_config *cfg, const cca_weights *w, const void *x,
+                                     void *y, void *ws, size_t wsb, void *stream) {
+  Layout L;
+  CCA_TRY(prefill_checks(cfg, w, ws, wsb, &L));
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return CCA_ERR_INVALID_ARG;
+  if (!fused_downproj_mix(*cfg)) return CCA_ERR_UNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CCA_TRY(run_downproj_mix(*cfg, w, x, ws, L, st));
   CCA_TRY(run_attention(*cfg, w, ws, L, st));
   return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
 }

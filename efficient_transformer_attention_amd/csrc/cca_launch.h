@@ -108,6 +108,18 @@ hipError_t launch_attention_decode(const MixShape &s, const float *q, const Stat
                                    const int *lens, const float *tau, float *part, TV *o,
                                    hipStream_t stream);
 
+// Down-projection fused with the mixing steps (bf16 x and W_qkv; kv groups
+// of one query head, d = 64, T a multiple of 128): writes q, k, vt as
+// launch_convmix_prefill does, without the fp32 qkv~ in HBM.  halo_ws:
+// downproj_mix_halo_bytes() bytes of scratch (the 3 rows before each
+// 128-token tile, through a small GEMM).
+bool downproj_mix_supported(int G, int d, int T, int E);
+size_t downproj_mix_halo_bytes(int B, int T, int E, int N);
+template <typename TQ, typename TV>
+hipError_t launch_downproj_mix(const MixShape &s, const MixTaps &w, const bf16 *x,
+                               const bf16 *wqkv, int E, void *halo_ws, TQ *q, TQ *k, TV *vt,
+                               hipStream_t stream);
+
 // Whether the mixing kernel's LDS tile of one kv group (G query heads + k +
 // v, 19 tokens) fits the 64 KiB it may use.
 bool convmix_fits(int G, int d);

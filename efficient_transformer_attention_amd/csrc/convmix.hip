@@ -27,6 +27,7 @@
 // written transposed (d-major) for the attention kernel, straight from the
 // LDS tile.
 #include "cca_device.h"
+#include "gemm_tile.h"
 #include "cca_launch.h"
 
 namespace cca {
@@ -442,6 +443,160 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
       reinterpret_cast<TV *>(out.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
           from_f32<TV>(tile[(m + 2) * CW + (G + 1) * D + c]);
 }
+
+// ---------------------------------------------------------------------------
+// Down-projection fused with the mixing steps (a1 + a2..a7) for kv groups of
+// one query head (G = 1), d = 64 and sequences of a multiple of 128 tokens.
+// A workgroup computes the 128-token x (q | k | v columns of one kv group)
+// tile of qkv~ = x W_qkv^T with the DMA GEMM main loop, leaves it in LDS as
+// fp32 below the 3-token halo that the previous tile's tokens form (computed
+// beforehand by a small GEMM over just those rows), and runs the mixing of
+// convmix_prefill_kernel on it: qkv~ never goes to HBM.
+// ---------------------------------------------------------------------------
+static constexpr int FUSE_BM = 128;
+
+// xh[mt * 3 + r] = x row of token t0 - 3 + r of tile mt (t0 = its first token;
+// zero rows for the first tile of a sequence)
+__global__ __launch_bounds__(256) void halo_rows_kernel(const bf16 *__restrict__ x,
+                                                        bf16 *__restrict__ xh, int T, int E,
+                                                        int nrows) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int per = E / 8;
+  if (e >= (long long)nrows * per) return;
+  const int row = (int)(e / per), c8 = (int)(e % per);
+  const int tps = T / FUSE_BM;
+  const int mt = row / HALO, r = row % HALO, b = mt / tps, tt = mt % tps;
+  const u32x4 v = tt > 0 ? ld16(x + ((size_t)b * T + tt * FUSE_BM - HALO + r) * E + 8 * c8)
+                         : zero_u32x4();
+  st16(xh + (size_t)row * E + 8 * c8, v);
+}
+
+template <typename TQ, typename TV>
+__global__ __launch_bounds__(256, 1) void downproj_mix_kernel(MixShape s, MixTaps w,
+                                                             const bf16 *__restrict__ x,
+                                                             const bf16 *__restrict__ wqkv,
+                                                             const float *__restrict__ halo,
+                                                             TQ *__restrict__ q,
+                                                             TQ *__restrict__ k,
+                                                             TV *__restrict__ vt, int E) {
+  constexpr int D = 64, G = 1, BM = FUSE_BM, CW = (G + 2) * D, BN = CW, BK = 32, STAGES = 5;
+  constexpr int TM = BM / 64, TN = BN / 64;
+  constexpr int RING = STAGES * (BM + BN) * 2 * BK;
+  constexpr int TILE_F = (BM + HALO) * CW;
+  constexpr int TAPS_F = (G + 1) * D * 4 + ((G + 1) * 4 + 3) / 4 * 4;
+  constexpr int EPI = (TILE_F + TAPS_F) * 4 + BM * (D / 2) * 8;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[RING > EPI ? RING : EPI];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, hl = lane >> 5;
+  const int tps = s.T / BM;
+  const int lid = xcd_remap(blockIdx.x, s.B * tps * s.Hkv);
+  const int g = lid % s.Hkv, mt = lid / s.Hkv;
+  const int b = mt / tps, tt = mt % tps;
+  const int t0 = tt * BM;
+  const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
+
+  f32x16 acc[TM][TN];
+  dma_gemm_tile<BM, BN, BK, STAGES>(x, wqkv, s.B * s.T, N, E, E, b * s.T + t0,
+                                    [&](int r) { return group_col(r, g, G, D, eq, ekv); }, 0, E,
+                                    smem, acc);
+  __syncthreads();                                  // every wave is done with the ring
+
+  float *tile = reinterpret_cast<float *>(smem);    // rows: tokens t0-HALO .. t0+BM-1
+  float *staps = tile + TILE_F;
+  float *ctaps = staps + (G + 1) * D * 4;
+  float2 *rot = reinterpret_cast<float2 *>(staps + TAPS_F);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int row = wm * (BM / 2) + i * 32 + 8 * (a >> 2) + 4 * hl + (a & 3);
+        tile[(HALO + row) * CW + wn * (BN / 2) + j * 32 + l32] = acc[i][j][a];
+      }
+  for (int e = tid; e < HALO * CW; e += 256) {
+    const int r = e / CW, c = e % CW;
+    tile[e] = tt > 0 ? halo[((size_t)mt * HALO + r) * N + group_col(c, g, G, D, eq, ekv)] : 0.f;
+  }
+  load_taps<D>(s, w, g, staps, ctaps);
+  for (int e = tid; e < BM * (D / 2); e += 256)
+    rot[e] = rope_cs_theta(t0 + e / (D / 2), s.theta[e % (D / 2)], s.rope_base);
+  __syncthreads();
+
+  // the mixing of convmix_prefill_kernel on the tile's rows
+  constexpr int LPU = D / 4;
+  const int upp = 256 / LPU;
+  const int li = tid % LPU, ui = tid / LPU;
+  for (int slot = 0; slot <= G; ++slot) {
+    float stp[4][4], ctp[4];
+    lane_taps<D>(staps, ctaps, slot, li, stp, ctp);
+    const float qscale = slot < G ? w.tau[g * G + slot] * 1.4426950408889634f : 1.f;
+    for (int r = ui; r < BM; r += upp) {
+      const int tok = t0 + r;
+      float y[4];
+      mix_unit<D>(tile, CW, r, slot, G, li, stp, ctp, s, rot[r * (D / 2) + 2 * li],
+                  rot[r * (D / 2) + 2 * li + 1], y);
+      if (slot < G) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] *= qscale;
+        Store4<TQ>::st(q + ((size_t)(b * s.Hq + g * G + slot) * s.Tp + tok) * D + 4 * li, y);
+      } else {
+        Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
+      }
+    }
+  }
+  // value head, transposed: vt[b, g, dd, perm(t)]
+  const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
+  const int vcol = (G + 1) * D;
+  for (int e = tid; e < D * (BM / 8); e += 256) {
+    const int dd = e / (BM / 8), grp = e % (BM / 8);
+    float vals[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      vals[jj] = tile[(vt_perm(8 * grp + jj) + HALO - shifted) * CW + vcol + dd];
+    TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + dd) * s.Tp + t0 + 8 * grp;
+    Store4<TV>::st(dst, vals);
+    Store4<TV>::st(dst + 4, vals + 4);
+  }
+}
+
+bool downproj_mix_supported(int G, int d, int T, int E) {
+  return G == 1 && d == 64 && T % FUSE_BM == 0 && E % 32 == 0;
+}
+
+size_t downproj_mix_halo_bytes(int B, int T, int E, int N) {
+  const size_t rows = (size_t)B * (T / FUSE_BM) * HALO;
+  return rows * E * 2 + rows * N * 4 + 256;
+}
+
+template <typename TQ, typename TV>
+hipError_t launch_downproj_mix(const MixShape &s, const MixTaps &w, const bf16 *x,
+                               const bf16 *wqkv, int E, void *halo_ws, TQ *q, TQ *k, TV *vt,
+                               hipStream_t stream) {
+  const int N = (s.Hq + 2 * s.Hkv) * s.d;
+  const int nrows = s.B * (s.T / FUSE_BM) * HALO;
+  bf16 *xh = reinterpret_cast<bf16 *>(halo_ws);
+  float *hq = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(halo_ws) +
+                                        ((size_t)nrows * E * 2 + 255) / 256 * 256);
+  const long long nthr = (long long)nrows * (E / 8);
+  hipLaunchKernelGGL(halo_rows_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream,
+                     x, xh, s.T, E, nrows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_gemm_nt<bf16, float>(xh, wqkv, hq, nrows, N, E, E, E, N, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((downproj_mix_kernel<TQ, TV>), dim3(s.B * (s.T / FUSE_BM) * s.Hkv), dim3(256),
+                     0, stream, s, w, x, wqkv, hq, q, k, vt, E);
+  return hipGetLastError();
+}
+
+template hipError_t launch_downproj_mix<f16, bf16>(const MixShape &, const MixTaps &, const bf16 *,
+                                                   const bf16 *, int, void *, f16 *, f16 *, bf16 *,
+                                                   hipStream_t);
+template hipError_t launch_downproj_mix<bf16, bf16>(const MixShape &, const MixTaps &, const bf16 *,
+                                                    const bf16 *, int, void *, bf16 *, bf16 *,
+                                                    bf16 *, hipStream_t);
 
 static size_t mix_lds_bytes(int rows, int G, int D, int TC) {
   const int CW = (G + 2) * D;

@@ -13,6 +13,7 @@
 // LDS with a 16-byte XOR swizzle, double buffered, one barrier per K step.
 // Rows of 128 bytes per tile row: BK = 64 (bf16) or 32 (fp32).
 #include "cca_device.h"
+#include "gemm_tile.h"
 #include "cca_launch.h"
 
 namespace cca {
@@ -166,13 +167,6 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
 //   chunk that the swizzle places there.  Rows past M / N read as zero (buffer
 //   range check).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
-// 128-byte rows (8 chunks): f(r) = (r & 7) ^ ((r >> 3) & 1)
-template <int CPR> __device__ __forceinline__ int swz_rows(int row) {
-  if constexpr (CPR == 4) return swz4(row);
-  else return (row & 7) ^ ((row >> 3) & 1);
-}
-
 template <typename Tout, int BM, int BN, int BK, int STAGES, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__restrict__ A,
                                                              const bf16 *__restrict__ Bm,
@@ -202,120 +196,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__res
   const int kbeg = blockIdx.y * kchunk;
   C += (size_t)blockIdx.y * M * ldc;
 
-  const unsigned a_bytes = (unsigned)((size_t)M * lda * 2), b_bytes = (unsigned)((size_t)N * ldb * 2);
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bm, 0, b_bytes, 0x00020000);
-
-  // DMA instruction u of wave w moves 1 KiB chunk u*4 + w of a stage: the
-  // first A_INS/4 instructions of every wave load A, the rest B.  Per lane:
-  // the byte offset of its chunk in K tile 0, or the operand's size for rows
-  // past M / N, which the buffer range check turns into zeros.
-  unsigned doff[PER_WAVE];
-#pragma unroll
-  for (int u = 0; u < PER_WAVE; ++u) {
-    constexpr int AU = A_INS / 4;
-    const bool isA = u < AU;
-    const int row = ((isA ? u : u - AU) * 4 + wave) * (1024 / ROWB) + lane / CPR;
-    const int chunk = (lane % CPR) ^ swz_rows<CPR>(row);
-    const int grow = (isA ? m0 : n0) + row;
-    doff[u] = grow < (isA ? M : N) ? (unsigned)(((size_t)grow * (isA ? lda : ldb) + chunk * 8) * 2)
-                                   : (isA ? a_bytes : b_bytes);
-  }
-  auto issue = [&](int kt, int slot) {
-    unsigned char *base = smem + slot * STAGE + wave * 1024;
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      const bool isA = u < A_INS / 4;
-      unsigned char *dst = isA ? base + u * 4096 : base + A_INS * 1024 + (u - A_INS / 4) * 4096;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(dst), 16, (int)doff[u],
-                                               (kbeg + kt * BK) * 2, 0, 0);
-    }
-  };
-
-  // per-lane LDS byte offsets of the MFMA fragments inside one stage
-  int aoff[KK][TM], boff[KK][TN];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const int chunk = 2 * kk + hl;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * WM + i * 32 + l32;
-      aoff[kk][i] = row * ROWB + ((chunk ^ swz_rows<CPR>(row)) << 4);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = wn * WN + j * 32 + l32;
-      boff[kk][j] = BM * ROWB + row * ROWB + ((chunk ^ swz_rows<CPR>(row)) << 4);
-    }
-  }
-  auto load = [&](int slot, Frag (&fa)[KK][TM], Frag (&fb)[KK][TN]) {
-    const unsigned char *sbase = smem + slot * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[kk][i] = *reinterpret_cast<const Frag *>(sbase + aoff[kk][i]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[kk][j] = *reinterpret_cast<const Frag *>(sbase + boff[kk][j]);
-    }
-  };
-
   f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
-  auto mma = [&](Frag (&fa)[KK][TM], Frag (&fb)[KK][TN]) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[kk][i], fb[kk][j], acc[i][j]);
-  };
-  // wait until at most n of this wave's DMA stages are still in flight
-  auto wait_stages = [&](int n) {
-    if constexpr (STAGES >= 5) {
-      if (n >= 2) { wait_vmcnt<2 * PER_WAVE>(); return; }
-    }
-    if constexpr (STAGES >= 4) {
-      if (n >= 1) { wait_vmcnt<PER_WAVE>(); return; }
-    }
-    wait_vmcnt<0>();
-  };
-
-  const int nk = min(kchunk, K - kbeg) / BK;
-  // iteration kt < nk - 1: tile kt + 1 is read into registers while tile kt
-  // (already in registers) is multiplied; tiles up to kt + STAGES - 2 fly
-  auto iter = [&](int kt, Frag (&ca)[KK][TM], Frag (&cb)[KK][TN], Frag (&na)[KK][TM],
-                  Frag (&nb)[KK][TN]) {
-    // tile kt + 1 landed: of the tiles issued so far, those after it may fly
-    wait_stages(min(nk, kt + STAGES - 1) - (kt + 2));
-    // every wave's DMA of tile kt + 1 has landed, and every read of the slot
-    // refilled below (tile kt - 1, read during iteration kt - 2) is done
-    lds_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    load((kt + 1) % STAGES, na, nb);
-    mma(ca, cb);
-  };
-
-#pragma unroll
-  for (int s0 = 0; s0 < STAGES - 1; ++s0)
-    if (s0 < nk) issue(s0, s0);
-  wait_stages(min(nk, STAGES - 1) - 1);
-  lds_barrier();
-  Frag fa0[KK][TM], fb0[KK][TN], fa1[KK][TM], fb1[KK][TN];
-  load(0, fa0, fb0);
-  int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
-    iter(kt, fa0, fb0, fa1, fb1);
-    iter(kt + 1, fa1, fb1, fa0, fb0);
-  }
-  if (kt + 1 < nk) {
-    iter(kt, fa0, fb0, fa1, fb1);
-    mma(fa1, fb1);
-  } else {
-    mma(fa0, fb0);
-  }
+  dma_gemm_tile<BM, BN, BK, STAGES>(A, Bm, M, N, lda, ldb, m0, [&](int r) { return n0 + r; },
+                                    kbeg, min(kchunk, K - kbeg), smem, acc);
 
   const bool full = m0 + BM <= M && n0 + BN <= N;   // workgroup-uniform
 #pragma unroll

@@ -153,6 +153,18 @@ cca_status cca_prefill_forward(const cca_config *cfg, const cca_weights *w,
                                const void *x, void *y, const cca_state *state_out,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* cca_prefill_forward with the down-projection and the mixing steps fused
+ * into one kernel, so qkv~ stays on chip (the deeper fusion the pages' own
+ * kernel uses [GS-EN "3. Key Contributions"]).  Same outputs up to fp32
+ * rounding order; no decode state.  CCA_ERR_UNSUPPORTED unless cfg.dtype is
+ * bf16, H_q == H_kv, head_dim == 64, seq_len is a multiple of 128 and
+ * d_model a multiple of 32.  On MI355X it measures slower than the separate
+ * kernels that cca_prefill_forward uses; it is kept for comparison.
+ * workspace: >= cca_prefill_workspace_size(cfg) bytes. */
+cca_status cca_prefill_forward_fused(const cca_config *cfg, const cca_weights *w, const void *x,
+                                     void *y, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 /* Decode step: one new token per sequence at position cache_len (uniform over
  * the batch).  x_t [B, E] -> y_t [B, E].
  * state_in: cache slots [0, cache_len) and the carried conv window / vshift.
@@ -331,6 +343,8 @@ const char *cca_status_string(cca_status s);
  *               inside each group of 16 tokens, positions 4..7 and 8..11 are
  *               swapped (bits 2 and 3 of the token index exchanged)
  *   CCA_WS_O    [B*T, e_q] latent attention output, cfg.dtype
+ *   CCA_WS_PART scratch of cca_prefill_forward_fused (the 3 rows before each
+ *               128-token tile), for the shapes it takes
  * Decode workspace layout:
  *   CCA_WS_QKV  fp32 [B, e_q + 2*e_kv]
  *   CCA_WS_Q    fp32 [B, H_q, d]  normalised, rotated q of the new token

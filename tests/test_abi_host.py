@@ -236,3 +236,25 @@ def test_decode_multi_rejects_before_launch(L):
     assert f(*args(good, m=0)) == L.CCA_ERR_INVALID_ARG
     assert f(*args(good, m=17)) == L.CCA_ERR_UNSUPPORTED
     assert f(*args(good, wsb=need - 1)) == L.CCA_ERR_WORKSPACE
+
+
+def test_prefill_fused_rejects_unsupported_shapes(L):
+    w = _fake_weights(L)
+    f = L.lib.cca_prefill_forward_fused
+    for s, want in [
+        (CCAShape(batch=1, seq_len=200, d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=64),
+         L.CCA_ERR_UNSUPPORTED),                                           # T not a multiple of 128
+        (CCAShape(batch=1, seq_len=256, d_model=256, n_q_heads=8, n_kv_heads=4, head_dim=64),
+         L.CCA_ERR_UNSUPPORTED),                                           # G = 2
+        (CCAShape(batch=1, seq_len=256, d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=32),
+         L.CCA_ERR_UNSUPPORTED),                                           # d = 32
+        (CCAShape(batch=1, seq_len=256, d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                  dtype="f32"), L.CCA_ERR_UNSUPPORTED),
+    ]:
+        cfg = L.make_config(s)
+        need = L.prefill_workspace_size(cfg)
+        assert f(C.byref(cfg), C.byref(w), 0x10000, 0x20000, 0x100000, need, None) == want
+    ok = L.make_config(CCAShape(batch=1, seq_len=256, d_model=256, n_q_heads=4, n_kv_heads=4,
+                                head_dim=64))
+    need = L.prefill_workspace_size(ok)
+    assert f(C.byref(ok), C.byref(w), 0x10000, 0x20000, 0x100000, need - 1, None) == L.CCA_ERR_WORKSPACE

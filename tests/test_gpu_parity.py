@@ -344,3 +344,45 @@ def test_decode_workload_full():
     vc = st.v_cache[:, :, L_].float().cpu().numpy()
     assert rel_l2(kc, np.stack([n["k_new"][0] for n in news])) < 5e-3
     assert rel_l2(vc, np.stack([n["v_new"][0] for n in news])) < 5e-3
+
+
+FUSED = {
+    "g1_norm_t256": CCAShape(batch=2, seq_len=256, d_model=256, n_q_heads=4, n_kv_heads=4,
+                             head_dim=64, rope_base=10000.0),
+    "g1_nonorm_noshift_t384": CCAShape(batch=1, seq_len=384, d_model=512, n_q_heads=2, n_kv_heads=2,
+                                       head_dim=64, use_qk_norm=0, use_value_shift=0,
+                                       seq_conv_k=2, chan_conv_k=3),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_prefill_fused_matches_stages_and_oracle(name):
+    """cca_prefill_forward_fused (down-projection + mixing in one kernel) gives
+    the q, k, v^T of the separate stage kernels and the oracle's output."""
+    shape = FUSED[name]
+    _say(f"[fused] {name} {shape}")
+    P = make_prefill(shape, seed=2)
+    if not shape.use_qk_norm:
+        set_taps(P, tau=tau_inv_sqrt_d(shape))
+    run = PrefillRun(shape, P)
+    L = lib()
+    y = torch.empty_like(run.x)
+    L.prefill_forward_fused(run.cfg, run.w, run.x, y, run.ws)
+    torch.cuda.synchronize()
+    B, T, d = shape.batch, shape.seq_len, shape.head_dim
+    Tp = run.padded_T()
+    qv = lambda: run.ws_view(L.WS_Q, run.qk_dtype(), (B, shape.n_q_heads, Tp, d)).clone()
+    kv = lambda: run.ws_view(L.WS_K, run.qk_dtype(), (B, shape.n_kv_heads, Tp, d)).clone()
+    vv = lambda: run.ws_view(L.WS_VT, torch.bfloat16, (B, shape.n_kv_heads, d, Tp)).clone()
+    fused = (qv(), kv(), vv())
+    L.stage_downproj(run.cfg, run.w, run.x, run.ws)
+    L.stage_convmix(run.cfg, run.w, run.ws)
+    torch.cuda.synchronize()
+    staged = (qv(), kv(), vv())
+    for what, a, b in zip(("q", "k", "vt"), fused, staged):
+        fa, fb = a.float(), b.float()
+        err = float((fa - fb).abs().max())
+        _say(f"[fused] {what}: max |fused - staged| = {err:.3e}, bitwise {torch.equal(a, b)}")
+        assert err <= 2e-3 * max(float(fb.abs().max()), 1.0), what
+    ref = O.prefill(P.x, P.weights.f64(), shape)
+    assert_parity(tens().to_f64(y), ref, "bf16", name)
