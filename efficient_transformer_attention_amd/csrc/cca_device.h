@@ -126,6 +126,8 @@ __device__ __forceinline__ float dpp_f(float v) {
 }
 // Value of the lane one below inside its row of 16 (0 for the row's lane 0).
 __device__ __forceinline__ float dpp_shr1(float v) { return dpp_f<0x111>(v); }
+// Value of the lane one above inside its row of 16 (0 for the row's lane 15).
+__device__ __forceinline__ float dpp_shl1(float v) { return dpp_f<0x101>(v); }
 // Sum over aligned groups of W lanes (W in 1, 2, 4, 8, 16), every lane gets it.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {

@@ -13,13 +13,13 @@
 //   value-shift: the shifted heads' token t feeds token t+1.
 //
 // Design (MI355X): two passes over fp32 activations.
-//  * head pass: one d-lane segment per (token, q or k head) recomputes the
-//    forward from the fp32 down-projection output (sequence and channel conv,
-//    q-k-mean, norm, rotation) and runs the per-head backward (RoPE, norm,
-//    channel conv): channel neighbours and pair partners are lane shuffles,
-//    the norms segment reductions.  It writes dm (the mixed q/k cotangent)
-//    and da (the sequence conv output's cotangent), plus per-(token, head)
-//    partial sums of the channel-tap and temperature gradients.
+//  * head pass: d/4 lanes per (run of 8 tokens, q or k head), 4 channels per
+//    lane, recompute the forward from the fp32 down-projection output
+//    (sequence and channel conv, q-k-mean, norm, rotation) and run the
+//    per-head backward (RoPE, norm, channel conv) token by token over the
+//    run.  It writes dm (the mixed q/k cotangent) and da (the sequence conv
+//    output's cotangent), plus per-(run, head) partial sums of the
+//    channel-tap and temperature gradients.
 //  * channel pass: one thread per (channel, 16-token run) combines the
 //    sequence-conv transpose (reads da at t .. t+k_s-1), the q-k-mean skip
 //    terms and the value-shift into dz, the cotangent of the down-projection
@@ -30,6 +30,9 @@
 
 namespace cca {
 
+// Tokens per run of the head pass.
+static constexpr int MIX_BWD_HTB = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w,
                                                            const float *__restrict__ qkv,
@@ -39,171 +42,179 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
                                                            float *__restrict__ da_out,
                                                            float *__restrict__ tau_part,
                                                            float *__restrict__ chan_part) {
-  constexpr int SEG = D < 64 ? D : 64;      // lanes per (token, head)
-  constexpr int CPL = D / SEG;              // channels per lane (1, or 2 at d = 128)
-  constexpr int UPW = 64 / SEG;             // units per wave
+  // d/4 lanes per (run of MIX_BWD_HTB tokens, head), 4 consecutive channels
+  // per lane (the layout of the forward mixing): the channel conv's
+  // neighbours are one lane away, RoPE pairs stay in-lane, the norms are
+  // d/4-lane reductions.  A lane group walks its run with a rolling window
+  // of the k_s pre-conv rows, so every qkv row and tap is read once per run,
+  // and the tap / temperature partials are summed over the run in registers.
+  constexpr int LPU = D / 4;
+  constexpr int UPW = 64 / LPU;             // units per wave (consecutive heads)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane % SEG, sbase = lane - li;
+  const int li = lane % LPU;
   const int H = s.Hq + s.Hkv;
-  const long long unit = ((long long)blockIdx.x * 4 + wave) * UPW + lane / SEG;
-  const bool active = unit < (long long)s.B * s.T * H;
-  const long long bt = active ? unit / H : 0;
-  const int hh = active ? (int)(unit % H) : 0;
-  const int b = (int)(bt / s.T), t = (int)(bt % s.T);
+  const int ntb = (s.T + MIX_BWD_HTB - 1) / MIX_BWD_HTB;
+  // the host keeps B * ntb * (Hq + Hkv) below 2^31
+  const int unit = ((int)blockIdx.x * 4 + wave) * UPW + lane / LPU;
+  const bool active = unit < s.B * ntb * H;
+  const int run = active ? unit / H : 0;   // b * ntb + tb
+  const int hh = active ? unit - run * H : 0;
+  const int b = run / ntb, t0 = (run - b * ntb) * MIX_BWD_HTB;
+  const int t1 = active ? min(s.T, t0 + MIX_BWD_HTB) : t0;
   const bool is_q = hh < s.Hq;
   const int g = is_q ? hh / s.G : hh - s.Hq;
   const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
+  const int i0 = 4 * li;                                   // this lane's first channel
   const int colbase = is_q ? hh * D : eq + g * D;          // in the qkv row and in dm / da rows
+  const int wcols = eq + ekv;
   const float *seqw = is_q ? w.q_seq + (size_t)hh * D * s.ks : w.k_seq + (size_t)g * D * s.ks;
   const float *chw = is_q ? w.q_chan + (size_t)hh * s.kc : w.k_chan + (size_t)g * s.kc;
-  const float *row_t = qkv + ((size_t)b * s.T + t) * N;
+  const float *seq0 = qkv + (size_t)b * s.T * N;           // this sequence's rows
+  const float *gin0 = is_q ? gq + (size_t)b * s.T * eq + hh * D + i0
+                           : dk + (size_t)b * s.T * ekv + g * D + i0;
+  const int gstride = is_q ? eq : ekv;
 
-  // every global read first, so that they are in flight together: the
-  // k_s pre-conv rows (zero before the sequence start), the skip terms of
-  // q-k-mean, the taps and the incoming cotangent
+  float ws[4][4];                                           // [channel][tap], zero past k_s
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ws[c][j] = j < s.ks ? seqw[(i0 + c) * s.ks + j] : 0.f;
   float cw[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cw[j] = chw[min(j, s.kc - 1)];
-  float uv[CPL][4], wsv[CPL][4], skip[CPL], gin[CPL];
-#pragma unroll
-  for (int p = 0; p < CPL; ++p) {
-    const int i = li + SEG * p;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uv[p][j] = qkv[((size_t)b * s.T + max(t - j, 0)) * N + colbase + i];
-      wsv[p][j] = seqw[i * s.ks + min(j, s.ks - 1)];
-    }
-    if (is_q) {
-      skip[p] = row_t[eq + g * D + i];
-      gin[p] = gq[((size_t)b * s.T + t) * eq + hh * D + i];
-    } else {
-      float qs = 0.f;
-      for (int h2 = 0; h2 < s.G; ++h2) qs += row_t[(g * s.G + h2) * D + i];
-      skip[p] = qs * (1.f / (float)s.G);
-      gin[p] = dk[((size_t)b * s.T + t) * ekv + g * D + i];
-    }
-  }
+  for (int j = 0; j < 4; ++j) cw[j] = j < s.kc ? chw[j] : 0.f;
+  const double th0 = s.theta[li * 2], th1 = s.theta[li * 2 + 1];
   const float tau_h = is_q ? w.tau[hh] : 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (j >= s.kc) cw[j] = 0.f;
-#pragma unroll
-    for (int p = 0; p < CPL; ++p)
-      if (j >= s.ks || t - j < 0) wsv[p][j] = 0.f;
-  }
+  const float invg = __builtin_amdgcn_rcpf((float)s.G);
 
-  // channel i of this lane's p-th slot is li + SEG * p
-  float a[CPL], m[CPL];
-#pragma unroll
-  for (int p = 0; p < CPL; ++p) {
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc += wsv[p][j] * uv[p][j];
-    a[p] = acc;
-  }
-  // value of `v` (slots v[0..CPL)) at channel ci of this segment (0 outside [0, D))
-  auto at = [&](const float (&v)[CPL], int ci) {
-    const int cc = ci < 0 ? 0 : (ci >= D ? D - 1 : ci);
-    const int src = sbase + cc % SEG, pp = cc / SEG;
-    float r = __shfl(v[0], src, 64);
-    if constexpr (CPL == 2) {
-      const float r1 = __shfl(v[1], src, 64);
-      r = pp ? r1 : r;
-    }
-    return (ci < 0 || ci >= D) ? 0.f : r;
+  // pre-conv row of token t (zero before the sequence start), the q-k-mean
+  // skip term and the incoming cotangent of token t
+  auto load_row = [&](int t) -> f32x4 {
+    if (t < 0) return f32x4{0.f, 0.f, 0.f, 0.f};
+    return *reinterpret_cast<const f32x4 *>(seq0 + (size_t)t * N + colbase + i0);
   };
-  auto seg_sum = [&](float v) {
-#pragma unroll
-    for (int o = 1; o < SEG; o <<= 1) v += __shfl_xor(v, o, 64);
-    return v;
+  auto load_skip = [&](int t) -> f32x4 {
+    const float *row = seq0 + (size_t)t * N;
+    if (is_q) return *reinterpret_cast<const f32x4 *>(row + eq + g * D + i0);
+    f32x4 m = *reinterpret_cast<const f32x4 *>(row + g * s.G * D + i0);
+    for (int h2 = 1; h2 < s.G; ++h2) m += *reinterpret_cast<const f32x4 *>(row + (g * s.G + h2) * D + i0);
+    return m * invg;
+  };
+  auto load_gin = [&](int t) -> f32x4 {
+    return *reinterpret_cast<const f32x4 *>(gin0 + (size_t)t * gstride);
   };
 
-  // forward recompute: channel conv, q-k-mean, norm
-#pragma unroll
-  for (int p = 0; p < CPL; ++p) {
-    const int i = li + SEG * p;
-    float bb = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bb += cw[j] * at(a, i - j);
-    if (s.use_mean) bb += 0.5f * (uv[p][0] + skip[p]);
-    m[p] = bb;
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int p = 0; p < CPL; ++p) ss += m[p] * m[p];
-  const float nrm = sqrtf(seg_sum(ss));
-  const bool big = nrm > s.eps;
-  const float inv = s.use_norm ? 1.f / (big ? nrm : s.eps) : 1.f;
-  float n[CPL];
-#pragma unroll
-  for (int p = 0; p < CPL; ++p) n[p] = m[p] * inv;
+  // lane exchanges: DPP inside rows of 16 lanes, shuffles across rows (d = 128)
+  auto prev = [&](float v) {                               // value of the lane below (0 for li = 0)
+    float r;
+    if constexpr (LPU <= 16) r = dpp_shr1(v);
+    else r = __shfl_up(v, 1, LPU);
+    return li == 0 ? 0.f : r;
+  };
+  auto next = [&](float v) {                               // value of the lane above (0 for the last)
+    float r;
+    if constexpr (LPU <= 16) r = dpp_shl1(v);
+    else r = __shfl_down(v, 1, LPU);
+    return li == LPU - 1 ? 0.f : r;
+  };
+  auto grp_sum = [&](float v) { return group_sum<LPU>(v); };
 
-  // cotangent of the rotated vector, rotation back, temperature partial
-  float dn[CPL];
-  float tau_acc = 0.f;
+  f32x4 u[4];                                               // rows t, t-1, t-2, t-3
 #pragma unroll
-  for (int p = 0; p < CPL; ++p) {
-    const int i = li + SEG * p;
-    const float2 cs = rope_cs_theta(t, s.theta[i >> 1], s.rope_base);
-    const float dr = is_q ? tau_h * gin[p] : gin[p];
-    if (is_q) {
-      // the rotated, normalised q this lane holds: <r, g> summed below
-      const float partner = __shfl_xor(n[p], 1, 64);
-      const float r = (i & 1) ? partner * cs.y + n[p] * cs.x : n[p] * cs.x - partner * cs.y;
-      tau_acc += r * gin[p];
+  for (int j = 0; j < 4; ++j) u[j] = load_row(t0 - j);
+  f32x4 skip = load_skip(t0), gin = load_gin(t0);
+  float tau_acc = 0.f, cacc[4] = {0.f, 0.f, 0.f, 0.f};
+
+  // a uniform trip count keeps every lane in the wave-wide exchanges; tokens
+  // past the run's end are computed on clamped rows and dropped
+  for (int k = 0; k < MIX_BWD_HTB; ++k) {
+    const int t = t0 + k;
+    const bool valid = t < t1;
+    // next token's inputs, in flight while this one is computed
+    const int tn = min(t + 1, t1 - 1 < t0 ? t0 : t1 - 1);
+    const f32x4 u_n = load_row(tn), skip_n = load_skip(tn), gin_n = load_gin(tn);
+
+    // forward recompute: sequence conv, channel conv, q-k-mean, norm
+    float a[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = fmaf(ws[c][j], u[j][c], acc);
+      a[c] = acc;
     }
-    const float dpartner = __shfl_xor(dr, 1, 64);
-    // pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c); transpose: (g0 c + g1 s, -g0 s + g1 c)
-    dn[p] = (i & 1) ? -dpartner * cs.y + dr * cs.x : dr * cs.x + dpartner * cs.y;
-  }
-  const float tau_sum = seg_sum(tau_acc);
+    const float p1 = prev(a[1]), p2 = prev(a[2]), p3 = prev(a[3]);   // a[i0-3], a[i0-2], a[i0-1]
+    float m[4];
+    m[0] = cw[0] * a[0] + cw[1] * p3 + cw[2] * p2 + cw[3] * p1;
+    m[1] = cw[0] * a[1] + cw[1] * a[0] + cw[2] * p3 + cw[3] * p2;
+    m[2] = cw[0] * a[2] + cw[1] * a[1] + cw[2] * a[0] + cw[3] * p3;
+    m[3] = cw[0] * a[3] + cw[1] * a[2] + cw[2] * a[1] + cw[3] * a[0];
+    if (s.use_mean)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) m[c] += 0.5f * (u[0][c] + skip[c]);
+    // 1 / max(||m||, eps) == rsqrt(max(||m||^2, eps^2))
+    const float ss = grp_sum(m[0] * m[0] + m[1] * m[1] + m[2] * m[2] + m[3] * m[3]);
+    const bool big = ss > s.eps * s.eps;
+    const float inv = s.use_norm ? __builtin_amdgcn_rsqf(fmaxf(ss, s.eps * s.eps)) : 1.f;
+    float n[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) n[c] = m[c] * inv;
 
-  // norm backward
-  float dm[CPL];
-  if (s.use_norm) {
-    float nd = 0.f;
+    // RoPE pairs (i0, i0+1) and (i0+2, i0+3): rotate back, and the
+    // temperature partial <r, g> of the rotated q
+    float dn[4];
 #pragma unroll
-    for (int p = 0; p < CPL; ++p) nd += n[p] * dn[p];
-    nd = seg_sum(nd);
+    for (int pp = 0; pp < 2; ++pp) {
+      const float2 cs = rope_cs_theta(t, pp ? th1 : th0, s.rope_base);
+      const float g0 = gin[2 * pp], g1 = gin[2 * pp + 1];
+      const float d0 = is_q ? tau_h * g0 : g0, d1 = is_q ? tau_h * g1 : g1;
+      const float x0 = n[2 * pp], x1 = n[2 * pp + 1];
+      if (valid) tau_acc += (x0 * cs.x - x1 * cs.y) * g0 + (x0 * cs.y + x1 * cs.x) * g1;
+      dn[2 * pp] = d0 * cs.x + d1 * cs.y;
+      dn[2 * pp + 1] = -d0 * cs.y + d1 * cs.x;
+    }
+
+    // norm backward
+    float dm[4];
+    if (s.use_norm) {
+      const float nd = grp_sum(n[0] * dn[0] + n[1] * dn[1] + n[2] * dn[2] + n[3] * dn[3]);
 #pragma unroll
-    for (int p = 0; p < CPL; ++p) dm[p] = big ? (dn[p] - n[p] * nd) / nrm : dn[p] / s.eps;
-  } else {
+      for (int c = 0; c < 4; ++c) dm[c] = (big ? dn[c] - n[c] * nd : dn[c]) * inv;
+    } else {
 #pragma unroll
-    for (int p = 0; p < CPL; ++p) dm[p] = dn[p];
+      for (int c = 0; c < 4; ++c) dm[c] = dn[c];
+    }
+
+    // channel conv backward (da[i] = sum_j w_j dm[i+j]) and its tap partials
+    const float x0 = next(dm[0]), x1 = next(dm[1]), x2 = next(dm[2]);   // dm[i0+4 .. i0+6]
+    f32x4 da;
+    da[0] = cw[0] * dm[0] + cw[1] * dm[1] + cw[2] * dm[2] + cw[3] * dm[3];
+    da[1] = cw[0] * dm[1] + cw[1] * dm[2] + cw[2] * dm[3] + cw[3] * x0;
+    da[2] = cw[0] * dm[2] + cw[1] * dm[3] + cw[2] * x0 + cw[3] * x1;
+    da[3] = cw[0] * dm[3] + cw[1] * x0 + cw[2] * x1 + cw[3] * x2;
+    if (valid) {
+      cacc[0] += dm[0] * a[0] + dm[1] * a[1] + dm[2] * a[2] + dm[3] * a[3];
+      cacc[1] += dm[0] * p3 + dm[1] * a[0] + dm[2] * a[1] + dm[3] * a[2];
+      cacc[2] += dm[0] * p2 + dm[1] * p3 + dm[2] * a[0] + dm[3] * a[1];
+      cacc[3] += dm[0] * p1 + dm[1] * p2 + dm[2] * p3 + dm[3] * a[0];
+      const size_t o = ((size_t)b * s.T + t) * wcols + colbase + i0;
+      *reinterpret_cast<f32x4 *>(dm_out + o) = f32x4{dm[0], dm[1], dm[2], dm[3]};
+      *reinterpret_cast<f32x4 *>(da_out + o) = da;
+    }
+    u[3] = u[2];
+    u[2] = u[1];
+    u[1] = u[0];
+    u[0] = u_n;
+    skip = skip_n;
+    gin = gin_n;
   }
 
-  // channel conv backward and its tap partials
-  float da[CPL];
-#pragma unroll
-  for (int p = 0; p < CPL; ++p) {
-    const int i = li + SEG * p;
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc += cw[j] * at(dm, i + j);
-    da[p] = acc;
-  }
+  const float tau_sum = grp_sum(tau_acc);
   float cpart[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float acc = 0.f;
-#pragma unroll
-    for (int p = 0; p < CPL; ++p) acc += dm[p] * at(a, li + SEG * p - j);
-    cpart[j] = seg_sum(acc);
-  }
-
-  if (!active) return;
-  const int wcols = eq + ekv;
-#pragma unroll
-  for (int p = 0; p < CPL; ++p) {
-    const int i = li + SEG * p;
-    const size_t o = (size_t)bt * wcols + (is_q ? hh * D : eq + g * D) + i;
-    dm_out[o] = dm[p];
-    da_out[o] = da[p];
-  }
-  if (li == 0) {
-    if (is_q) tau_part[(size_t)bt * s.Hq + hh] = tau_sum;
-    for (int j = 0; j < s.kc; ++j) chan_part[((size_t)bt * H + hh) * s.kc + j] = cpart[j];
-  }
+  for (int j = 0; j < 4; ++j) cpart[j] = grp_sum(cacc[j]);
+  if (!active || li != 0) return;
+  if (is_q) tau_part[(size_t)run * s.Hq + hh] = tau_sum;
+  for (int j = 0; j < s.kc; ++j) chan_part[((size_t)run * H + hh) * s.kc + j] = cpart[j];
 }
 
 // Tokens per thread of the channel pass.
@@ -286,66 +297,118 @@ __global__ __launch_bounds__(256) void mix_bwd_chan_kernel(MixShape s, MixTaps w
   }
 }
 
-// out[rb * ncols + j] = sum of in[r * C + col0 + j] over the rows r of row
-// block rb (rows_per_block rows), j < ncols: 64 columns per workgroup, four
-// row phases reduced through LDS; fixed order, so the sums are deterministic.
-__global__ __launch_bounds__(256) void colsum_kernel(const float *__restrict__ in, long long R,
-                                                     int C, int col0, int ncols,
-                                                     int rows_per_block, float *__restrict__ out) {
+// Column sums of the per-row partials into the tap and temperature gradients.
+// Each job sums columns col0 .. col0 + ncols of in [R][C] into out[ncols], in
+// two launches for all jobs together: row blocks of COLSUM_ROWS rows into
+// blk [nblk][ncols], then the block sums.  Fixed orders, so deterministic.
+constexpr int COLSUM_ROWS = 64;
+constexpr int COLSUM_JOBS = 5;
+struct ColJob {
+  const float *in;
+  float *blk, *out;
+  long long R;
+  int C, col0, ncols, nblk;
+};
+struct ColJobs {
+  ColJob j[COLSUM_JOBS];
+  int first[COLSUM_JOBS + 1];   // first workgroup of each job in the row-block launch
+};
+
+// one workgroup per (job, row block, 64-column block), jobs back to back;
+// 4 row phases of 16 rows each
+__global__ __launch_bounds__(256) void colsum_rows_kernel(ColJobs jobs) {
   __shared__ float red[4][64];
+  int z = 0;
+  while (z + 1 < COLSUM_JOBS && (int)blockIdx.x >= jobs.first[z + 1]) ++z;
+  const ColJob &jb = jobs.j[z];
+  const int cb = (jb.ncols + 63) / 64;
+  const int local = (int)blockIdx.x - jobs.first[z];
+  const int bx = local % cb, by = local / cb;
   const int cl = threadIdx.x % 64, rs = threadIdx.x / 64;
-  const int j = blockIdx.x * 64 + cl;
-  const long long r0 = (long long)blockIdx.y * rows_per_block;
-  const long long r1 = min(R, r0 + rows_per_block);
+  const int j = bx * 64 + cl;
+  const long long r0 = (long long)by * COLSUM_ROWS;
+  float v[COLSUM_ROWS / 4];
+#pragma unroll
+  for (int k = 0; k < COLSUM_ROWS / 4; ++k) {
+    const long long r = r0 + rs + 4 * k;
+    v[k] = (j < jb.ncols && r < jb.R) ? jb.in[r * jb.C + jb.col0 + j] : 0.f;
+  }
   float acc = 0.f;
-  if (j < ncols)
-    for (long long r = r0 + rs; r < r1; r += 4) acc += in[r * C + col0 + j];
+#pragma unroll
+  for (int k = 0; k < COLSUM_ROWS / 4; ++k) acc += v[k];
   red[rs][cl] = acc;
   __syncthreads();
-  if (rs == 0 && j < ncols)
-    out[(size_t)blockIdx.y * ncols + j] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
+  if (rs == 0 && j < jb.ncols)
+    jb.blk[(size_t)by * jb.ncols + j] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
 }
 
-// Column sums of in [R][C] (columns col0 .. col0 + ncols) into out[ncols]:
-// blocks of 64 rows, then one block over the block sums.
-static hipError_t colsum(const float *in, long long R, int C, int col0, int ncols, float *blk,
-                         float *out, hipStream_t stream) {
-  const unsigned cb = (unsigned)((ncols + 63) / 64);
-  const long long nblk = (R + 63) / 64;
-  hipLaunchKernelGGL(colsum_kernel, dim3(cb, (unsigned)nblk), dim3(256), 0, stream, in, R, C, col0,
-                     ncols, 64, blk);
-  hipLaunchKernelGGL(colsum_kernel, dim3(cb, 1), dim3(256), 0, stream, blk, nblk, ncols, 0, ncols,
-                     (int)nblk, out);
+// grid (64-column blocks, 1, jobs): the row-block sums, 4 row phases with
+// four running sums each
+__global__ __launch_bounds__(256) void colsum_blocks_kernel(ColJobs jobs) {
+  __shared__ float red[4][64];
+  const ColJob &jb = jobs.j[blockIdx.z];
+  if ((int)blockIdx.x * 64 >= jb.ncols) return;
+  const int cl = threadIdx.x % 64, rs = threadIdx.x / 64;
+  const int j = blockIdx.x * 64 + cl;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (j < jb.ncols) {
+    int r = rs;
+    for (; r + 12 < jb.nblk; r += 16)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += jb.blk[(size_t)(r + 4 * k) * jb.ncols + j];
+    for (int k = 0; r < jb.nblk; r += 4, ++k) acc[k] += jb.blk[(size_t)r * jb.ncols + j];
+  }
+  red[rs][cl] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (rs == 0 && j < jb.ncols) jb.out[j] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
+}
+
+static hipError_t colsum_all(ColJobs jobs, hipStream_t stream) {
+  int cbmax = 1;
+  jobs.first[0] = 0;
+  for (int z = 0; z < COLSUM_JOBS; ++z) {
+    const int cb = (jobs.j[z].ncols + 63) / 64;
+    cbmax = max(cbmax, cb);
+    jobs.first[z + 1] = jobs.first[z] + cb * jobs.j[z].nblk;
+  }
+  if (jobs.first[COLSUM_JOBS] > 0)
+    hipLaunchKernelGGL(colsum_rows_kernel, dim3(jobs.first[COLSUM_JOBS]), dim3(256), 0, stream, jobs);
+  hipLaunchKernelGGL(colsum_blocks_kernel, dim3(cbmax, 1, COLSUM_JOBS), dim3(256), 0, stream, jobs);
   return hipGetLastError();
 }
 
+static long long colsum_nblk(long long R) { return (R + COLSUM_ROWS - 1) / COLSUM_ROWS; }
+
 size_t mix_backward_scratch_floats(const MixShape &s) {
-  const size_t BT = (size_t)s.B * s.T;
+  const size_t BR = (size_t)s.B * ((s.T + MIX_BWD_HTB - 1) / MIX_BWD_HTB);
   const int H = s.Hq + s.Hkv;
   const int ntb = (s.T + MIX_BWD_TB - 1) / MIX_BWD_TB;
   const size_t wcols = (size_t)(s.Hq + s.Hkv) * s.d;
   const size_t seq_rows = (size_t)s.B * ntb, seq_cols = wcols * s.ks;
-  const size_t blk = ((BT + 63) / 64) * (size_t)(H * s.kc > s.Hq ? H * s.kc : s.Hq);
-  const size_t blk_seq = ((seq_rows + 63) / 64) * seq_cols;
-  // tau partials, channel-tap partials, seq-tap partials, row-block sums
-  return BT * s.Hq + BT * H * s.kc + seq_rows * seq_cols + (blk > blk_seq ? blk : blk_seq);
+  // tau partials, channel-tap partials (per head-pass run), seq-tap partials
+  // (per channel-pass run), then the row-block sums of the five column sums
+  // (each job its own)
+  const size_t blk = colsum_nblk((long long)BR) * (size_t)(s.Hq + H * s.kc) +
+                     colsum_nblk((long long)seq_rows) * seq_cols;
+  return BR * s.Hq + BR * H * s.kc + seq_rows * seq_cols + blk;
 }
 
 template <typename TZ>
 hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwdArgs<TZ> &a,
                                hipStream_t stream) {
-  const long long units = (long long)s.B * s.T * (s.Hq + s.Hkv);
-  const int seg = s.d < 64 ? s.d : 64;
-  const long long per_wg = 4LL * (64 / seg);
+  const int nhr = (s.T + MIX_BWD_HTB - 1) / MIX_BWD_HTB;   // head-pass runs per sequence
+  const long long units = (long long)s.B * nhr * (s.Hq + s.Hkv);
+  const long long per_wg = 4LL * (64 / (s.d / 4));
+  if (units + per_wg >= (1LL << 31)) return hipErrorInvalidValue;   // 32-bit unit indices
   const unsigned nwg = (unsigned)((units + per_wg - 1) / per_wg);
-  const size_t BT = (size_t)s.B * s.T;
+  const size_t BR = (size_t)s.B * nhr;
   const int H = s.Hq + s.Hkv;
   const int ntb = (s.T + MIX_BWD_TB - 1) / MIX_BWD_TB;
   const int wcols = (s.Hq + s.Hkv) * s.d, N = wcols + s.Hkv * s.d;
   const int eq = s.Hq * s.d, ekv = s.Hkv * s.d;
   float *tau_part = a.scratch;
-  float *chan_part = tau_part + BT * s.Hq;
-  float *seq_part = chan_part + BT * H * s.kc;
+  float *chan_part = tau_part + BR * s.Hq;
+  float *seq_part = chan_part + BR * H * s.kc;
   float *blk = seq_part + (size_t)s.B * ntb * wcols * s.ks;
 
   switch (s.d) {
@@ -361,15 +424,21 @@ hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwd
                      stream, s, w, a.qkv, a.dm, a.da, a.dv, a.dz, seq_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // temperature [BT][Hq]; channel taps [BT][H * kc] (q heads, then k heads);
-  // sequence taps [B * ntb][(e_q + e_kv) * ks] (q channels, then k channels).
-  // The row-block scratch is reused: each colsum finishes before the next
-  // one starts on the same stream.
-  if ((e = colsum(tau_part, (long long)BT, s.Hq, 0, s.Hq, blk, a.d_tau, stream)) != hipSuccess) return e;
-  if ((e = colsum(chan_part, (long long)BT, H * s.kc, 0, s.Hq * s.kc, blk, a.d_q_chan, stream)) != hipSuccess) return e;
-  if ((e = colsum(chan_part, (long long)BT, H * s.kc, s.Hq * s.kc, s.Hkv * s.kc, blk, a.d_k_chan, stream)) != hipSuccess) return e;
-  if ((e = colsum(seq_part, (long long)s.B * ntb, wcols * s.ks, 0, eq * s.ks, blk, a.d_q_seq, stream)) != hipSuccess) return e;
-  return colsum(seq_part, (long long)s.B * ntb, wcols * s.ks, eq * s.ks, ekv * s.ks, blk, a.d_k_seq, stream);
+  // temperature [B * nhr][Hq]; channel taps [B * nhr][H * kc] (q heads, then
+  // k heads); sequence taps [B * ntb][(e_q + e_kv) * ks] (q channels, then k)
+  const long long sr = (long long)s.B * ntb;
+  const int nb_br = (int)colsum_nblk((long long)BR), nb_sr = (int)colsum_nblk(sr);
+  ColJobs jobs;
+  jobs.j[0] = ColJob{tau_part, blk, a.d_tau, (long long)BR, s.Hq, 0, s.Hq, nb_br};
+  blk += (size_t)nb_br * s.Hq;
+  jobs.j[1] = ColJob{chan_part, blk, a.d_q_chan, (long long)BR, H * s.kc, 0, s.Hq * s.kc, nb_br};
+  blk += (size_t)nb_br * s.Hq * s.kc;
+  jobs.j[2] = ColJob{chan_part, blk, a.d_k_chan, (long long)BR, H * s.kc, s.Hq * s.kc, s.Hkv * s.kc, nb_br};
+  blk += (size_t)nb_br * s.Hkv * s.kc;
+  jobs.j[3] = ColJob{seq_part, blk, a.d_q_seq, sr, wcols * s.ks, 0, eq * s.ks, nb_sr};
+  blk += (size_t)nb_sr * eq * s.ks;
+  jobs.j[4] = ColJob{seq_part, blk, a.d_k_seq, sr, wcols * s.ks, eq * s.ks, ekv * s.ks, nb_sr};
+  return colsum_all(jobs, stream);
 }
 
 template hipError_t launch_mix_backward<bf16>(const MixShape &, const MixTaps &,
