@@ -38,6 +38,8 @@ from .cca import (  # noqa: F401
     down_project,
     seq_conv,
     chan_conv,
+    chan_conv_grouped,
+    conv_window_rows,
     qk_mean,
     value_shift,
     l2_normalize,

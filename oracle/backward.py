@@ -248,6 +248,8 @@ def prefill_backward(x: np.ndarray, w: dict, cfg, dy: np.ndarray,
     ``k_seq_taps``, ``q_chan_taps``, ``k_chan_taps``, ``tau``), each the shape
     of its argument.  With ``intermediates`` also the cotangents of the
     latent q, k (rotated), v and of the mixed, pre-norm q and k."""
+    if readings.chan_conv != "per_head":
+        raise NotImplementedError("the backward follows the per-head channel conv reading")
     Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     B, T, E = x.shape
     G = Hq // Hkv

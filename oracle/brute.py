@@ -20,8 +20,11 @@ def _matvec(w, x):
     return [sum(w[r][c] * x[c] for c in range(len(x))) for r in range(len(w))]
 
 
-def brute_prefill(x, w, cfg):
+def brute_prefill(x, w, cfg, chan_conv="per_head"):
     """x: nested lists [B][T][E] (floats); w: dict of nested lists.
+    ``chan_conv="grouped"`` takes the dense lag-by-channel reading of the
+    channel convolution (weights ``q_chan_dense`` / ``k_chan_dense``
+    [H][d_out][k_c][d_in]).
 
     Returns y as nested lists [B][T][E]."""
     Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -61,8 +64,28 @@ def brute_prefill(x, w, cfg):
                         r[t][h * d + i] = acc
             return r
 
-        bq = conv_chan(conv_seq(qt, w["q_seq_taps"], eq), w["q_chan_taps"], Hq)
-        bk = conv_chan(conv_seq(kt, w["k_seq_taps"], ekv), w["k_chan_taps"], Hkv)
+        def conv_grouped(a, dense, H):
+            # b[t][h, i] = sum over lags j and input channels c of
+            # dense[h][i][j][c] * a[t - j][h, c] (nothing before t = 0)
+            r = [[0.0] * (H * d) for _ in range(T)]
+            for t in range(T):
+                for h in range(H):
+                    for i in range(d):
+                        acc = 0.0
+                        for j in range(kc):
+                            if t - j < 0:
+                                continue
+                            for c in range(d):
+                                acc += dense[h][i][j][c] * a[t - j][h * d + c]
+                        r[t][h * d + i] = acc
+            return r
+
+        if chan_conv == "grouped":
+            bq = conv_grouped(conv_seq(qt, w["q_seq_taps"], eq), w["q_chan_dense"], Hq)
+            bk = conv_grouped(conv_seq(kt, w["k_seq_taps"], ekv), w["k_chan_dense"], Hkv)
+        else:
+            bq = conv_chan(conv_seq(qt, w["q_seq_taps"], eq), w["q_chan_taps"], Hq)
+            bk = conv_chan(conv_seq(kt, w["k_seq_taps"], ekv), w["k_chan_taps"], Hkv)
 
         q = [row[:] for row in bq]
         k = [row[:] for row in bk]

@@ -37,10 +37,17 @@ class Readings:
                    (pairs (i, i + d/2)).
     shift_half:    "upper" (default: kv heads H_kv/2 .. H_kv-1 take token t-1)
                    or "lower".
+    chan_conv:     "per_head" (default: one k_c-tap filter per head sliding
+                   along the channel index) or "grouped" (a k_c-lag causal
+                   convolution over tokens that mixes all d channels of a
+                   head, weights ``q_chan_dense`` / ``k_chan_dense``).  With
+                   "grouped" the carried decode window holds the last
+                   (k_s - 1) + (k_c - 1) pre-conv rows.
     """
     qk_mean: str = "M1"
     rope_pairing: str = "interleaved"
     shift_half: str = "upper"
+    chan_conv: str = "per_head"
 
 
 DEFAULT_READINGS = Readings()
@@ -101,6 +108,36 @@ def chan_conv(a: np.ndarray, taps: np.ndarray):
     for j in range(min(taps.shape[1], d)):
         out[..., j:] += taps[:, j][:, None] * a[..., :d - j]
     return out
+
+
+# Alternative reading of a3 (parity unpinned, selected by Readings.chan_conv
+# = "grouped"): the channel dimension is mixed by a dense d x d matrix per lag
+# and head, a causal convolution over tokens grouped by head:
+# b[t, h, i] = sum_j sum_c W[h, i, j, c] * a[t - j, h, c], a = 0 before the
+# sequence start (or the carried values in decode).
+# ---------------------------------------------------------------------------
+
+def chan_conv_grouped(a: np.ndarray, w: np.ndarray, history: Optional[np.ndarray] = None):
+    """a [B, T, H, d], w [H, d_out, k_c, d_in], history [B, k_c-1, H, d]
+    (a of the tokens before t = 0, slot 0 oldest) -> [B, T, H, d]."""
+    B, T, H, d = a.shape
+    kc = w.shape[2]
+    if history is None:
+        history = np.zeros((B, kc - 1, H, d), dtype=a.dtype)
+    ext = np.concatenate([history, a], axis=1)       # ext[:, t + kc - 1] = a[:, t]
+    out = np.zeros_like(a)
+    for j in range(kc):
+        lagged = ext[:, kc - 1 - j: kc - 1 - j + T]  # a[t - j]
+        out += np.einsum("hic,bthc->bthi", w[:, :, j, :], lagged)
+    return out
+
+
+def conv_window_rows(cfg, readings: "Readings" = None) -> int:
+    """Pre-conv rows the decode state carries: k_s - 1, plus k_c - 1 under
+    the grouped channel conv (its lagged inputs a[t-j] need them)."""
+    readings = DEFAULT_READINGS if readings is None else readings
+    extra = cfg.chan_conv_k - 1 if readings.chan_conv == "grouped" else 0
+    return cfg.seq_conv_k - 1 + extra
 
 
 # ---------------------------------------------------------------------------
@@ -261,9 +298,10 @@ def latents(x, w, cfg, pos0: int = 0, history=None, readings: Readings = DEFAULT
     """Steps a1-a7 for tokens x [B, T, E] at positions pos0 .. pos0+T-1.
 
     ``w`` holds float64 weights (keys of ``synth.Weights.f64()``), ``cfg`` a
-    shape with the method switches.  ``history`` = (conv_q [B, ks-1, e_q],
-    conv_k [B, ks-1, e_kv], vshift [B, H_kv/2, d]) of the tokens before pos0.
-    Returns a dict of every intermediate."""
+    shape with the method switches.  ``history`` = (conv_q [B, W, e_q],
+    conv_k [B, W, e_kv], vshift [B, H_kv/2, d]) of the tokens before pos0,
+    W = conv_window_rows(cfg, readings).  Returns a dict of every
+    intermediate."""
     Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     B, T, _ = x.shape
     G = Hq // Hkv
@@ -271,10 +309,30 @@ def latents(x, w, cfg, pos0: int = 0, history=None, readings: Readings = DEFAULT
     hq = hk = hv = None
     if history is not None:
         hq, hk, hv = history
-    a_q = seq_conv(qt.reshape(B, T, Hq * d), w["q_seq_taps"], hq).reshape(B, T, Hq, d)
-    a_k = seq_conv(kt.reshape(B, T, Hkv * d), w["k_seq_taps"], hk).reshape(B, T, Hkv, d)
-    b_q = chan_conv(a_q, w["q_chan_taps"])
-    b_k = chan_conv(a_k, w["k_chan_taps"])
+    if readings.chan_conv == "grouped":
+        # a over the carried rows and the new ones; the rows before the first
+        # k_s - 1 carried ones are unknown, so the first k_s - 1 results are
+        # dropped and the next k_c - 1 are the lagged inputs of the first token
+        W = conv_window_rows(cfg, readings)
+        ks1, kc1 = cfg.seq_conv_k - 1, cfg.chan_conv_k - 1
+
+        def grouped(pre, hist, seq_taps, dense, H):
+            hist = np.zeros((B, W, H * d)) if hist is None else hist
+            ext = np.concatenate([hist, pre.reshape(B, T, H * d)], axis=1)
+            a_ext = seq_conv(ext, seq_taps).reshape(B, W + T, H, d)
+            a_hist = a_ext[:, ks1:ks1 + kc1]
+            a = a_ext[:, W:]
+            return a, chan_conv_grouped(a, dense, a_hist)
+
+        a_q, b_q = grouped(qt, hq, w["q_seq_taps"], w["q_chan_dense"], Hq)
+        a_k, b_k = grouped(kt, hk, w["k_seq_taps"], w["k_chan_dense"], Hkv)
+    elif readings.chan_conv == "per_head":
+        a_q = seq_conv(qt.reshape(B, T, Hq * d), w["q_seq_taps"], hq).reshape(B, T, Hq, d)
+        a_k = seq_conv(kt.reshape(B, T, Hkv * d), w["k_seq_taps"], hk).reshape(B, T, Hkv, d)
+        b_q = chan_conv(a_q, w["q_chan_taps"])
+        b_k = chan_conv(a_k, w["k_chan_taps"])
+    else:
+        raise ValueError(readings.chan_conv)
     if cfg.use_qk_mean:
         m_q, m_k = qk_mean(b_q, b_k, qt, kt, G, readings)
     else:
@@ -319,9 +377,10 @@ def prefill_state(lat: dict, cfg, readings: Readings = DEFAULT_READINGS):
     K holds the normalised, rotated k (tau not folded in), V the post-shift v,
     both [B, H_kv, T, d]; the convolution window holds the pre-conv q~, k~ of
     the last k_s - 1 tokens (slot 0 oldest, zeros before the sequence start);
-    vshift holds vbar of the last token on the shifted heads."""
+    vshift holds vbar of the last token on the shifted heads.  Under the
+    grouped channel conv the window holds conv_window_rows() tokens."""
     B, T = lat["q_pre"].shape[:2]
-    ks1 = cfg.seq_conv_k - 1
+    ks1 = conv_window_rows(cfg, readings)
     Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     cq = np.zeros((B, ks1, Hq * d))
     ck = np.zeros((B, ks1, Hkv * d))
@@ -340,8 +399,9 @@ def decode_step(x_t, w, cfg, k_cache, v_cache, conv_q, conv_k, vshift,
                 readings: Readings = DEFAULT_READINGS):
     """One token per sequence against a cache of L = k_cache.shape[2] past tokens.
 
-    x_t [B, E]; k_cache, v_cache [B, H_kv, L, d]; conv_q [B, ks-1, e_q];
-    conv_k [B, ks-1, e_kv]; vshift [B, H_kv/2, d].
+    x_t [B, E]; k_cache, v_cache [B, H_kv, L, d]; conv_q [B, W, e_q];
+    conv_k [B, W, e_kv] (W = conv_window_rows(cfg, readings)); vshift
+    [B, H_kv/2, d].
     The new token sits at position L: steps a1-a7 run there with the carried
     window, its k and v are appended at cache index L, attention runs over the
     L + 1 keys, then the up-projection.  Returns (y_t [B, E], dict with the new
@@ -356,8 +416,10 @@ def decode_step(x_t, w, cfg, k_cache, v_cache, conv_q, conv_k, vshift,
     vv = np.concatenate([v_cache, v_new[:, :, None, :]], axis=2).transpose(0, 2, 1, 3)
     o = causal_attention(lat["q"], kk, vv, w["tau"], [L])
     y = up_project(o, w["w_o"])[:, 0]
-    new_cq = np.concatenate([conv_q[:, 1:], lat["q_pre"].reshape(B, 1, -1)], axis=1)
-    new_ck = np.concatenate([conv_k[:, 1:], lat["k_pre"].reshape(B, 1, -1)], axis=1)
+    W = conv_window_rows(cfg, readings)
+    cq_all = np.concatenate([conv_q, lat["q_pre"].reshape(B, 1, -1)], axis=1)
+    ck_all = np.concatenate([conv_k, lat["k_pre"].reshape(B, 1, -1)], axis=1)
+    new_cq, new_ck = cq_all[:, cq_all.shape[1] - W:], ck_all[:, ck_all.shape[1] - W:]
     sh = shifted_heads(cfg.n_kv_heads, readings)
     new_vs = lat["vbar"][:, 0][:, sh, :]
     return y, dict(k_new=k_new, v_new=v_new, q=lat["q"][:, 0], o=o[:, 0],
@@ -382,7 +444,7 @@ def decode_multi(x_new, w, cfg, k_cache, v_cache, conv_q, conv_k, vshift,
     vv = np.concatenate([v_cache, v_new], axis=2).transpose(0, 2, 1, 3)
     o = causal_attention(lat["q"], kk, vv, w["tau"], list(range(L, L + m)))
     y = up_project(o, w["w_o"])
-    ks1 = cfg.seq_conv_k - 1
+    ks1 = conv_window_rows(cfg, readings)
     cq_all = np.concatenate([conv_q, lat["q_pre"].reshape(B, m, -1)], axis=1)
     ck_all = np.concatenate([conv_k, lat["k_pre"].reshape(B, m, -1)], axis=1)
     sh = shifted_heads(cfg.n_kv_heads, readings)

@@ -14,6 +14,7 @@ from .generate import (  # noqa: F401
     Backward,
     make_prefill,
     make_upstream_grad,
+    add_chan_dense,
     make_decode,
     round_to_bf16_bits,
     bf16_bits_to_f64,

@@ -101,15 +101,22 @@ class Weights:
     tau: np.ndarray            # [H_q] fp32
     w_qkv: np.ndarray          # float64 values of the above
     w_o: np.ndarray
+    # grouped channel conv only: [H, d_out, k_c, d_in] fp32 (add_chan_dense)
+    q_chan_dense: Optional[np.ndarray] = None
+    k_chan_dense: Optional[np.ndarray] = None
 
     def f64(self):
         """The weights as float64 arrays, in the order the oracle takes them."""
-        return dict(w_qkv=self.w_qkv, w_o=self.w_o,
-                    q_seq_taps=self.q_seq_taps.astype(np.float64),
-                    k_seq_taps=self.k_seq_taps.astype(np.float64),
-                    q_chan_taps=self.q_chan_taps.astype(np.float64),
-                    k_chan_taps=self.k_chan_taps.astype(np.float64),
-                    tau=self.tau.astype(np.float64))
+        out = dict(w_qkv=self.w_qkv, w_o=self.w_o,
+                   q_seq_taps=self.q_seq_taps.astype(np.float64),
+                   k_seq_taps=self.k_seq_taps.astype(np.float64),
+                   q_chan_taps=self.q_chan_taps.astype(np.float64),
+                   k_chan_taps=self.k_chan_taps.astype(np.float64),
+                   tau=self.tau.astype(np.float64))
+        if self.q_chan_dense is not None:
+            out["q_chan_dense"] = self.q_chan_dense.astype(np.float64)
+            out["k_chan_dense"] = self.k_chan_dense.astype(np.float64)
+        return out
 
 
 @dataclass
@@ -177,8 +184,11 @@ def make_prefill(s: CCAShape, seed: int = 0) -> Prefill:
 
 
 def make_decode(s: CCAShape, seed: int = 0, capacity: Optional[int] = None,
-                cache_fill: str = "normal") -> Decode:
+                cache_fill: str = "normal", window: Optional[int] = None) -> Decode:
     """A decode step against a cache of ``s.cache_len`` past tokens.
+
+    ``window``: rows of the carried pre-conv window (default k_s - 1; the
+    grouped channel conv carries (k_s - 1) + (k_c - 1)).
 
     ``cache_fill="normal"`` draws the cache and the carried state ~ N(0, 1)
     (the synthetic long-cache workload).  The cache is drawn per sequence in
@@ -205,7 +215,7 @@ def make_decode(s: CCAShape, seed: int = 0, capacity: Optional[int] = None,
         vb = rng.standard_normal((H, L, d), dtype=np.float32)
         kc[b, :, :L, :] = _store(kb, s.dtype)[0]
         vc[b, :, :L, :] = _store(vb, s.dtype)[0]
-    ks1 = s.seq_conv_k - 1
+    ks1 = s.seq_conv_k - 1 if window is None else window
     cq = rng.standard_normal((B, ks1, s.e_q))
     ck = rng.standard_normal((B, ks1, s.e_kv))
     vs = rng.standard_normal((B, max(H // 2, 0), d))
@@ -227,3 +237,15 @@ def make_upstream_grad(s: CCAShape, seed: int = 0) -> Backward:
     dy = rng.standard_normal((s.batch, s.seq_len, s.d_model))
     dy_s, dy64 = _store(dy, s.dtype)
     return Backward(dy_s=dy_s, dy=dy64)
+
+
+def add_chan_dense(w: Weights, s: CCAShape, seed: int = 0) -> Weights:
+    """Weights of the grouped channel conv, W[h, i, j, c] ~ N(0, 1 / (k_c d))
+    (fan-in k_c d), fp32, drawn from their own stream so the other draws of
+    a seed stay as they are."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    sc = np.sqrt(1.0 / (s.chan_conv_k * s.head_dim))
+    d, kc = s.head_dim, s.chan_conv_k
+    w.q_chan_dense = _f32(rng.standard_normal((s.n_q_heads, d, kc, d)) * sc)[0]
+    w.k_chan_dense = _f32(rng.standard_normal((s.n_kv_heads, d, kc, d)) * sc)[0]
+    return w
