@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcca.so")
 
-SOURCES = ["gemm.hip", "convmix.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip",
+SOURCES = ["gemm.hip", "convmix.hip", "grouped_conv.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip",
            "mix_bwd.hip", "cca_api.cpp"]
 
 # Packed fp32 VALU ops are switched off for every device compile.

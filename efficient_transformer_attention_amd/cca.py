@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("CCA_LIBRARY") or os.path.join(PKG, "libcca.so")
 
 CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_WORKSPACE, CCA_ERR_HIP = range(5)
 CCA_BF16, CCA_F32 = 0, 1
+CCA_CHAN_PER_HEAD, CCA_CHAN_GROUPED = 0, 1
 WS_QKV, WS_Q, WS_K, WS_VT, WS_O, WS_PART, WS_SPLITK, WS_COUNT = range(8)
 
 # Every entry point declared in include/cca.h.
@@ -49,13 +50,15 @@ class Config(C.Structure):
         ("seq_conv_k", C.c_int32), ("chan_conv_k", C.c_int32),
         ("use_qk_mean", C.c_int32), ("use_value_shift", C.c_int32), ("use_qk_norm", C.c_int32),
         ("rope_base", C.c_float), ("norm_eps", C.c_float), ("dtype", C.c_int32),
+        ("chan_conv_mode", C.c_int32),
     ]
 
 
 class _Weights(C.Structure):
     _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p),
                 ("q_seq_taps", C.c_void_p), ("k_seq_taps", C.c_void_p),
-                ("q_chan_taps", C.c_void_p), ("k_chan_taps", C.c_void_p), ("tau", C.c_void_p)]
+                ("q_chan_taps", C.c_void_p), ("k_chan_taps", C.c_void_p), ("tau", C.c_void_p),
+                ("q_chan_dense", C.c_void_p), ("k_chan_dense", C.c_void_p)]
 
 
 class _Grads(C.Structure):
@@ -128,16 +131,19 @@ def status_string(status: int) -> str:
     return lib.cca_status_string(int(status)).decode()
 
 
-def make_config(shape) -> Config:
+def make_config(shape, chan_conv: str = "per_head") -> Config:
     """Config from any object with the cca_config field names (dtype given as
-    "bf16" / "f32" or as the enum value)."""
+    "bf16" / "f32" or as the enum value); ``chan_conv`` "per_head" or
+    "grouped" selects the channel-conv reading."""
     dt = shape.dtype
     if isinstance(dt, str):
         dt = {"bf16": CCA_BF16, "f32": CCA_F32}[dt]
+    mode = {"per_head": CCA_CHAN_PER_HEAD, "grouped": CCA_CHAN_GROUPED}[chan_conv]
     return Config(int(shape.batch), int(shape.seq_len), int(shape.d_model), int(shape.n_q_heads),
                   int(shape.n_kv_heads), int(shape.head_dim), int(shape.seq_conv_k),
                   int(shape.chan_conv_k), int(shape.use_qk_mean), int(shape.use_value_shift),
-                  int(shape.use_qk_norm), float(shape.rope_base), float(shape.norm_eps), int(dt))
+                  int(shape.use_qk_norm), float(shape.rope_base), float(shape.norm_eps), int(dt),
+                  mode)
 
 
 def _ptr(t) -> Optional[int]:
@@ -165,11 +171,13 @@ class Weights:
     q_chan_taps: object
     k_chan_taps: object
     tau: object
+    q_chan_dense: object = None      # grouped channel conv only: [H_q, d, k_c, d] fp32
+    k_chan_dense: object = None      # [H_kv, d, k_c, d] fp32
 
     def struct(self) -> _Weights:
         return _Weights(_ptr(self.w_qkv), _ptr(self.w_o), _ptr(self.q_seq_taps),
                         _ptr(self.k_seq_taps), _ptr(self.q_chan_taps), _ptr(self.k_chan_taps),
-                        _ptr(self.tau))
+                        _ptr(self.tau), _ptr(self.q_chan_dense), _ptr(self.k_chan_dense))
 
 
 @dataclass

@@ -74,6 +74,7 @@ MixShape mix_shape(const cca_config &c) {
   s.use_mean = c.use_qk_mean;
   s.use_shift = c.use_value_shift;
   s.use_norm = c.use_qk_norm;
+  s.grouped = c.chan_conv_mode == CCA_CHAN_GROUPED ? 1 : 0;
   s.rope_base = c.rope_base;
   s.eps = c.norm_eps;
   for (int i = 0; i < 64; ++i)
@@ -96,11 +97,17 @@ cca_status validate_shape(const cca_config *c, bool need_seq) {
       (unsigned)c->use_qk_norm > 1u)
     return CCA_ERR_INVALID_ARG;
   if (c->dtype != CCA_BF16 && c->dtype != CCA_F32) return CCA_ERR_UNSUPPORTED;
+  if (c->chan_conv_mode != CCA_CHAN_PER_HEAD && c->chan_conv_mode != CCA_CHAN_GROUPED)
+    return CCA_ERR_INVALID_ARG;
   const int d = c->head_dim;
   if (d != 16 && d != 32 && d != 64 && d != 128) return CCA_ERR_UNSUPPORTED;
   if (c->seq_conv_k < 1 || c->seq_conv_k > 4 || c->chan_conv_k < 1 || c->chan_conv_k > 4)
     return CCA_ERR_UNSUPPORTED;
   if (!convmix_fits(c->n_q_heads / c->n_kv_heads, d)) return CCA_ERR_UNSUPPORTED;
+  if (c->chan_conv_mode == CCA_CHAN_GROUPED &&
+      (!grouped_conv_supported(d, c->dtype == CCA_F32) ||
+       !convmix_decode_grouped_fits(c->n_q_heads / c->n_kv_heads, d, 1, c->seq_conv_k, c->chan_conv_k)))
+    return CCA_ERR_UNSUPPORTED;
   if (need_seq && !attention_supported(d, c->dtype == CCA_F32)) return CCA_ERR_UNSUPPORTED;
   // index arithmetic stays in 32-bit for per-row offsets
   const long long N = (long long)(c->n_q_heads + 2 * c->n_kv_heads) * d;
@@ -116,7 +123,7 @@ cca_status validate_shape(const cca_config *c, bool need_seq) {
 // Shapes cca_prefill_forward_fused takes: bf16 kv groups of one query head
 // with d = 64 and T a multiple of 128.
 bool fused_downproj_mix(const cca_config &c) {
-  if (c.dtype != CCA_BF16) return false;
+  if (c.dtype != CCA_BF16 || c.chan_conv_mode != CCA_CHAN_PER_HEAD) return false;
   const int G = c.n_q_heads / c.n_kv_heads;
   if (!downproj_mix_supported(G, c.head_dim, c.seq_len, c.d_model)) return false;
   const size_t N = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
@@ -144,6 +151,9 @@ Layout prefill_layout(const cca_config &c) {
   if (fused_downproj_mix(c)) {   // halo rows of the fused down-projection + mixing
     L.off[CCA_WS_PART] = o;
     o = align_up(o + downproj_mix_halo_bytes(c.batch, c.seq_len, c.d_model, (int)N), WS_ALIGN);
+  } else if (c.chan_conv_mode == CCA_CHAN_GROUPED) {   // the grouped channel conv's output
+    L.off[CCA_WS_PART] = o;
+    o = align_up(o + B * T * (eq + ekv) * 4, WS_ALIGN);
   }
   L.total = o;
   return L;
@@ -246,11 +256,15 @@ float *splitk_ptr(void *ws, const Layout &L, size_t *floats) {
   return reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + L.off[CCA_WS_SPLITK]);
 }
 
-cca_status check_weights(const cca_weights *w) {
+cca_status check_weights(const cca_config &c, const cca_weights *w) {
   if (!w || !w->w_qkv || !w->w_o || !w->q_seq_taps || !w->k_seq_taps || !w->q_chan_taps ||
       !w->k_chan_taps || !w->tau)
     return CCA_ERR_INVALID_ARG;
   if (!aligned16(w->w_qkv) || !aligned16(w->w_o)) return CCA_ERR_INVALID_ARG;
+  if (c.chan_conv_mode == CCA_CHAN_GROUPED &&
+      (!w->q_chan_dense || !w->k_chan_dense || !aligned16(w->q_chan_dense) ||
+       !aligned16(w->k_chan_dense)))
+    return CCA_ERR_INVALID_ARG;
   return CCA_OK;
 }
 
@@ -325,19 +339,26 @@ cca_status run_convmix(const cca_config &c, const cca_weights *w, const StateOut
                        const Layout &L, hipStream_t st) {
   const MixShape s = mix_shape(c);
   const float *qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
+  float *r1b = nullptr;
   hipError_t e;
+  if (c.chan_conv_mode == CCA_CHAN_GROUPED) {   // the channel conv on MFMA first
+    r1b = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_PART));
+    e = launch_grouped_conv_prefill(s, taps_of(w), w->q_chan_dense, w->k_chan_dense, qkv, r1b,
+                                    c.dtype == CCA_F32, st);
+    CCA_TRY(check_launch(e, st));
+  }
   if (c.dtype == CCA_F32) {
     e = launch_convmix_prefill<float, float>(s, taps_of(w), qkv, (float *)wsp(ws, L, CCA_WS_Q),
                                              (float *)wsp(ws, L, CCA_WS_K),
-                                             (float *)wsp(ws, L, CCA_WS_VT), so, st);
+                                             (float *)wsp(ws, L, CCA_WS_VT), so, st, r1b);
   } else if (qk_is_f16(c)) {
     e = launch_convmix_prefill<f16, bf16>(s, taps_of(w), qkv, (f16 *)wsp(ws, L, CCA_WS_Q),
                                           (f16 *)wsp(ws, L, CCA_WS_K),
-                                          (bf16 *)wsp(ws, L, CCA_WS_VT), so, st);
+                                          (bf16 *)wsp(ws, L, CCA_WS_VT), so, st, r1b);
   } else {
     e = launch_convmix_prefill<bf16, bf16>(s, taps_of(w), qkv, (bf16 *)wsp(ws, L, CCA_WS_Q),
                                            (bf16 *)wsp(ws, L, CCA_WS_K),
-                                           (bf16 *)wsp(ws, L, CCA_WS_VT), so, st);
+                                           (bf16 *)wsp(ws, L, CCA_WS_VT), so, st, r1b);
   }
   return check_launch(e, st);
 }
@@ -555,7 +576,7 @@ cca_status cca_decode_workspace_layout(const cca_config *cfg, int32_t cache_len,
 static cca_status prefill_checks(const cca_config *cfg, const cca_weights *w, void *ws,
                                  size_t wsb, Layout *L) {
   CCA_TRY(validate_shape(cfg, true));
-  CCA_TRY(check_weights(w));
+  CCA_TRY(check_weights(*cfg, w));
   *L = prefill_layout(*cfg);
   return check_ws(ws, wsb, L->total);
 }
@@ -622,7 +643,7 @@ cca_status cca_stage_upproj(const cca_config *cfg, const cca_weights *w, void *y
 static cca_status decode_checks(const cca_config *cfg, const cca_weights *w, int32_t L,
                                 void *ws, size_t wsb, Layout *lay) {
   CCA_TRY(validate_shape(cfg, false));
-  CCA_TRY(check_weights(w));
+  CCA_TRY(check_weights(*cfg, w));
   if (L < 0) return CCA_ERR_INVALID_ARG;
   *lay = decode_layout(decode_cfg(cfg), L);
   return check_ws(ws, wsb, lay->total);
@@ -654,10 +675,18 @@ static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
   const float *qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
   float *q = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_Q));
   hipError_t e;
-  if (c.dtype == CCA_BF16)
+  if (c.chan_conv_mode == CCA_CHAN_GROUPED) {
+    if (c.dtype == CCA_BF16)
+      e = launch_convmix_decode_grouped<bf16>(s, taps_of(w), w->q_chan_dense, w->k_chan_dense, qkv,
+                                              Lc, lens, si, so, q, st);
+    else
+      e = launch_convmix_decode_grouped<float>(s, taps_of(w), w->q_chan_dense, w->k_chan_dense, qkv,
+                                               Lc, lens, si, so, q, st);
+  } else if (c.dtype == CCA_BF16) {
     e = launch_convmix_decode<bf16>(s, taps_of(w), qkv, Lc, lens, si, so, q, st);
-  else
+  } else {
     e = launch_convmix_decode<float>(s, taps_of(w), qkv, Lc, lens, si, so, q, st);
+  }
   return check_launch(e, st);
 }
 
@@ -753,14 +782,15 @@ cca_status cca_stage_decode_upproj(const cca_config *cfg, const cca_weights *w, 
 // ---- training ----------------------------------------------------------------
 
 size_t cca_train_workspace_size(const cca_config *cfg) {
-  if (validate_shape(cfg, true) != CCA_OK) return 0;
+  if (validate_shape(cfg, true) != CCA_OK || cfg->chan_conv_mode != CCA_CHAN_PER_HEAD) return 0;
   return train_layout(*cfg).total;
 }
 
 cca_status cca_prefill_forward_train(const cca_config *cfg, const cca_weights *w, const void *x,
                                      void *y, void *ws, size_t wsb, void *stream) {
   CCA_TRY(validate_shape(cfg, true));
-  CCA_TRY(check_weights(w));
+  if (cfg->chan_conv_mode != CCA_CHAN_PER_HEAD) return CCA_ERR_UNSUPPORTED;
+  CCA_TRY(check_weights(*cfg, w));
   const TrainLayout TL = train_layout(*cfg);
   CCA_TRY(check_ws(ws, wsb, TL.total));
   if (!x || !y || !aligned16(x) || !aligned16(y)) return CCA_ERR_INVALID_ARG;
@@ -776,7 +806,8 @@ cca_status cca_prefill_backward(const cca_config *cfg, const cca_weights *w, con
                                 const void *dy, const cca_grads *g, void *ws, size_t wsb,
                                 void *stream) {
   CCA_TRY(validate_shape(cfg, true));
-  CCA_TRY(check_weights(w));
+  if (cfg->chan_conv_mode != CCA_CHAN_PER_HEAD) return CCA_ERR_UNSUPPORTED;
+  CCA_TRY(check_weights(*cfg, w));
   const TrainLayout TL = train_layout(*cfg);
   CCA_TRY(check_ws(ws, wsb, TL.total));
   if (!x || !dy || !aligned16(x) || !aligned16(dy)) return CCA_ERR_INVALID_ARG;
@@ -859,11 +890,14 @@ static constexpr int MAX_NEW_TOKENS = 16;
 static cca_status multi_checks(const cca_config *cfg, const cca_weights *w, int32_t n_new,
                                int32_t Lmax, void *ws, size_t wsb, Layout *lay) {
   CCA_TRY(validate_shape(cfg, false));
-  CCA_TRY(check_weights(w));
+  CCA_TRY(check_weights(*cfg, w));
   if (n_new < 1 || Lmax < 0) return CCA_ERR_INVALID_ARG;
-  if (n_new > MAX_NEW_TOKENS || !convmix_decode_fits(cfg->n_q_heads / cfg->n_kv_heads,
-                                                     cfg->head_dim, n_new))
-    return CCA_ERR_UNSUPPORTED;
+  const int G = cfg->n_q_heads / cfg->n_kv_heads;
+  const bool fits = cfg->chan_conv_mode == CCA_CHAN_GROUPED
+                        ? convmix_decode_grouped_fits(G, cfg->head_dim, n_new, cfg->seq_conv_k,
+                                                      cfg->chan_conv_k)
+                        : convmix_decode_fits(G, cfg->head_dim, n_new);
+  if (n_new > MAX_NEW_TOKENS || !fits) return CCA_ERR_UNSUPPORTED;
   *lay = decode_layout(decode_cfg(cfg), Lmax, n_new);
   return check_ws(ws, wsb, lay->total);
 }

@@ -36,6 +36,7 @@ struct MixShape {
   int Hq, Hkv, G, d;       // heads and head dim
   int ks, kc;              // conv taps (1..4)
   int use_mean, use_shift, use_norm;
+  int grouped;             // channel conv: 0 per-head filter along channels, 1 dense per lag
   float rope_base, eps;
   // RoPE frequencies base^(-2i/d), i < d/2, evaluated on the host in double
   // precision (all zero when RoPE is off); passed by value with the launch.
@@ -72,10 +73,25 @@ __host__ __device__ inline size_t cache_row(const StateOut &st, int b, int Hkv, 
 // Fused sequence conv + channel conv + q-k-mean + value-shift + L2 norm + RoPE
 // over a prefill.  qkv: fp32 [B*T, e_q + 2 e_kv].  Writes q [B,Hq,Tp,d] and
 // k [B,Hkv,Tp,d] in TQ, vt [B,Hkv,d,Tp] in TV (token order permuted inside
-// 16-token groups), zeros in the padding tokens [T, Tp).
+// 16-token groups), zeros in the padding tokens [T, Tp).  With r1b (the
+// grouped channel conv's output, fp32 [B*T, e_q + e_kv]) the two convolutions
+// are taken from there instead.
 template <typename TQ, typename TV>
 hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
-                                  TQ *k, TV *vt, const StateOut &st, hipStream_t stream);
+                                  TQ *k, TV *vt, const StateOut &st, hipStream_t stream,
+                                  const float *r1b = nullptr);
+
+// Grouped reading of the channel conv over a prefill (d in {16, 32, 64}):
+// outb[b*T + t, col] = sum over lags j < k_c and channels c of
+// W[h, i, j, c] * a[t - j, h, c], a the sequence conv of qkv's q / k columns,
+// for every q head (columns h*d + i) and k head (e_q + g*d + i); W is fp32
+// [H, d, k_c, d] per kind (dense_q for the H_q query heads, dense_k for the
+// H_kv key heads).  bf16 mode multiplies in fp16 on MFMA, fp32 mode on the
+// VALU in fp32.
+hipError_t launch_grouped_conv_prefill(const MixShape &s, const MixTaps &w, const float *dense_q,
+                                       const float *dense_k, const float *qkv, float *outb,
+                                       bool f32, hipStream_t stream);
+bool grouped_conv_supported(int d, bool f32);
 
 // The same mixing for m = s.T new tokens per sequence at positions L .. L+m-1
 // (L per sequence lens[b], clamped to [0, L], when lens is not null), using
@@ -86,6 +102,16 @@ template <typename TV>
 hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const float *qkv, int L,
                                  const int *lens, const StateOut &in, const StateOut &out,
                                  float *q, hipStream_t stream);
+
+// The decode mixing under the grouped channel conv: the same outputs as
+// launch_convmix_decode, with the window of (k_s - 1) + (k_c - 1) pre-conv
+// rows and the dense per-lag channel weights (fp32 [H, d, k_c, d]).
+template <typename TV>
+hipError_t launch_convmix_decode_grouped(const MixShape &s, const MixTaps &w, const float *dense_q,
+                                         const float *dense_k, const float *qkv, int L,
+                                         const int *lens, const StateOut &in, const StateOut &out,
+                                         float *q, hipStream_t stream);
+bool convmix_decode_grouped_fits(int G, int d, int m, int ks, int kc);
 
 // Causal flash attention inside the latent heads; q holds tau_h * log2(e) *
 // q_hat (the mixing kernel applies the temperature); tau [Hq] (device) bounds

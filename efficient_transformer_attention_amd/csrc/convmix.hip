@@ -53,6 +53,10 @@ template <> struct Store4<bf16> {
   }
 };
 
+template <int D>
+__device__ __forceinline__ void mix_tail(const float *cur, int slot, int G, const MixShape &s,
+                                         float2 cs0, float2 cs1, float (&b)[4], float y[4]);
+
 // Steps a2-a7 for one (token row r of the LDS tile, head slot) unit.  Slot
 // 0..G-1 are the group's query heads, slot G its key head.  The lane holds
 // channels 4*li .. 4*li+3.  `tile` rows are tokens (row r+HALO is the current
@@ -95,9 +99,17 @@ __device__ __forceinline__ void mix_unit(const float *tile, int CW, int r, int s
   b[1] = w0 * a[1] + w1 * a[0] + w2 * p3 + w3 * p2;
   b[2] = w0 * a[2] + w1 * a[1] + w2 * a[0] + w3 * p3;
   b[3] = w0 * a[3] + w1 * a[2] + w2 * a[1] + w3 * a[0];
+  mix_tail<D>(tile + (r + HALO) * CW + 4 * li, slot, G, s, cs0, cs1, b, y);
+}
 
+// Steps a4, a6, a7 after the channel conv: b (the channel-conv output of this
+// lane's 4 channels) plus the q-k-mean skip from the pre-conv row `cur` (the
+// token's tile row, offset to this lane's channels), normalised and rotated.
+template <int D>
+__device__ __forceinline__ void mix_tail(const float *cur, int slot, int G, const MixShape &s,
+                                         float2 cs0, float2 cs1, float (&b)[4], float y[4]) {
+  constexpr int LPU = D / 4;
   if (s.use_mean) {
-    const float *cur = tile + (r + HALO) * CW + 4 * li;
     const f32x4 kpre = *reinterpret_cast<const f32x4 *>(cur + G * D);
     if (slot < G) {
       const f32x4 qpre = *reinterpret_cast<const f32x4 *>(cur + slot * D);
@@ -175,6 +187,7 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
                                                               const float *__restrict__ qkv,
                                                               TQ *__restrict__ q, TQ *__restrict__ k,
                                                               TV *__restrict__ vt, StateOut st,
+                                                              const float *__restrict__ r1b,
                                                               int TC, int nchunks, int cpw,
                                                               int nseg) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -257,8 +270,21 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
       for (int r = ui; r < TC; r += upp) {
         const int tok = t0 + r;
         float y[4];
-        mix_unit<D>(tile, CW, r, slot, G, li, stp, ctp, s, rot[r * (D / 2) + 2 * li],
-                    rot[r * (D / 2) + 2 * li + 1], y);
+        if (r1b) {
+          // grouped channel conv: b comes from the MFMA kernel's output rows
+          float bb[4] = {0.f, 0.f, 0.f, 0.f};
+          if (tok < s.T) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(
+                r1b + (size_t)(b * s.T + tok) * (eq + ekv) + (slot < G ? (g * G + slot) * D : eq + g * D) + 4 * li);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bb[c] = v[c];
+          }
+          mix_tail<D>(tile + (r + HALO) * CW + 4 * li, slot, G, s, rot[r * (D / 2) + 2 * li],
+                      rot[r * (D / 2) + 2 * li + 1], bb, y);
+        } else {
+          mix_unit<D>(tile, CW, r, slot, G, li, stp, ctp, s, rot[r * (D / 2) + 2 * li],
+                      rot[r * (D / 2) + 2 * li + 1], y);
+        }
         if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
         if (slot < G) {
           // the attention kernel takes q scaled by tau_h * log2(e) (exp2-domain logits)
@@ -315,9 +341,10 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
     }
   }
 
-  // decode state after the last token: conv window and value-shift state
+  // decode state after the last token: conv window (k_s - 1 pre-conv rows,
+  // plus k_c - 1 under the grouped channel conv) and value-shift state
   if (seg == 0) {
-    const int ks1 = s.ks - 1;
+    const int ks1 = s.ks - 1 + (s.grouped ? s.kc - 1 : 0);
     const float *qb = qkv + (size_t)b * s.T * N;
     if (st.conv_q)
       for (int e = tid; e < ks1 * G * D; e += 256) {
@@ -442,6 +469,124 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
     for (int c = tid; c < D; c += 256)
       reinterpret_cast<TV *>(out.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
           from_f32<TV>(tile[(m + 2) * CW + (G + 1) * D + c]);
+}
+
+// The decode mixing under the grouped channel conv (m = s.T new tokens per
+// sequence at positions L .. L+m-1).  The carried window holds W = (k_s - 1)
+// + (k_c - 1) pre-conv rows; one workgroup per (b, g) stages them with the m
+// new rows, computes a (the sequence conv) for tokens L-k_c+1 .. L+m-1 into
+// LDS, then each (new token, head) unit forms its 4 channels of
+// b = sum_j W[h, i, j, :] . a[t - j] on the VALU (one (sequence, group) holds
+// at most a few hundred of them) and finishes with mix_tail.  All state reads
+// finish before the first barrier, so state_out may alias state_in.
+template <typename TV, int D>
+__global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
+    MixShape s, MixTaps w, const float *__restrict__ dense_q, const float *__restrict__ dense_k,
+    const float *__restrict__ qkv, int Lmax, const int *__restrict__ lens, StateOut in,
+    StateOut out, float *__restrict__ qout) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int G = s.G, CW = (G + 2) * D, QK = (G + 1) * D;
+  const int m = s.T;
+  const int ks1 = s.ks - 1, kc1 = s.kc - 1, W = ks1 + kc1;
+  const int Wt = W > 0 ? W : 1;          // carried tile rows (one at least, for the shifted value)
+  const int R = Wt + m, AR = kc1 + m;
+  float *tile = lds;                     // [R][CW]: rows 0..Wt-1 carried, then the new tokens
+  float *at = tile + R * CW;             // [AR][QK]: a of tokens L-kc1 .. L+m-1
+  float2 *rot = reinterpret_cast<float2 *>(at + AR * QK);
+
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x % s.Hkv, b = blockIdx.x / s.Hkv;
+  const int L = lens ? min(max(lens[b], 0), Lmax) : Lmax;
+  const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
+  const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
+  const TV *cq = reinterpret_cast<const TV *>(in.conv_q);
+  const TV *ck = reinterpret_cast<const TV *>(in.conv_k);
+  const TV *vs = reinterpret_cast<const TV *>(in.vshift);
+
+  for (int e = tid; e < R * CW; e += 256) {
+    const int r = e / CW, col = e % CW;
+    float v = 0.f;
+    if (r >= Wt) {
+      v = qkv[(size_t)(b * m + r - Wt) * N + group_col(col, g, G, D, eq, ekv)];
+    } else if (col < QK) {
+      const int sl = r - (Wt - W);               // window slot of token L - Wt + r
+      if (sl >= 0)
+        v = col < G * D ? to_f32(cq[(size_t)(b * W + sl) * eq + g * G * D + col])
+                        : to_f32(ck[(size_t)(b * W + sl) * ekv + g * D + col - G * D]);
+    } else if (r == Wt - 1 && shifted) {
+      v = to_f32(vs[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + col - QK]);
+    }
+    tile[e] = v;
+  }
+  for (int e = tid; e < m * (D / 2); e += 256)
+    rot[e] = rope_cs_theta(L + e / (D / 2), s.theta[e % (D / 2)], s.rope_base);
+  __syncthreads();
+
+  // a of token L - kc1 + r' is tile row Wt - kc1 + r'; its k_s inputs reach
+  // back to row Wt - W >= 0
+  for (int e = tid; e < AR * QK; e += 256) {
+    const int rr = e / QK, c = e % QK, row = Wt - kc1 + rr;
+    const float *tp = c < G * D ? w.q_seq + (size_t)(g * G * D + c) * s.ks
+                                : w.k_seq + (size_t)(g * D + c - G * D) * s.ks;
+    float acc = 0.f;
+    for (int j = 0; j < s.ks; ++j) acc = fmaf(tp[j], tile[(row - j) * CW + c], acc);
+    at[e] = acc;
+  }
+  __syncthreads();
+
+  constexpr int LPU = D / 4;
+  const int upp = 256 / LPU;
+  const int li = tid % LPU, ui = tid / LPU;
+  TV *kc = reinterpret_cast<TV *>(in.k_cache);
+  TV *vc = reinterpret_cast<TV *>(in.v_cache);
+  for (int u0 = 0; u0 < m * (G + 1); u0 += upp) {
+    const int unit = u0 + ui;
+    const bool active = unit < m * (G + 1);
+    const int j = active ? unit / (G + 1) : 0, slot = active ? unit % (G + 1) : 0;
+    const float *wd = slot < G ? dense_q + (size_t)(g * G + slot) * D * s.kc * D
+                               : dense_k + (size_t)g * D * s.kc * D;
+    float bb[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int lag = 0; lag < s.kc; ++lag) {
+      const float *arow = at + (kc1 + j - lag) * QK + slot * D;     // a of token L + j - lag
+      for (int c4 = 0; c4 < D; c4 += 4) {
+        const f32x4 av = *reinterpret_cast<const f32x4 *>(arow + c4);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const f32x4 wv = *reinterpret_cast<const f32x4 *>(wd + ((size_t)(4 * li + cc) * s.kc + lag) * D + c4);
+          bb[cc] += wv[0] * av[0] + wv[1] * av[1] + wv[2] * av[2] + wv[3] * av[3];
+        }
+      }
+    }
+    float y[4];
+    mix_tail<D>(tile + (Wt + j) * CW + 4 * li, slot, G, s, rot[j * (D / 2) + 2 * li],
+                rot[j * (D / 2) + 2 * li + 1], bb, y);
+    if (!active) continue;
+    if (slot < G) {
+      Store4<float>::st(qout + ((size_t)(b * m + j) * s.Hq + g * G + slot) * D + 4 * li, y);
+    } else {
+      Store4<TV>::st(kc + cache_row(in, b, s.Hkv, g, L + j) * D + 4 * li, y);
+    }
+  }
+  for (int e = tid; e < m * (D / 4); e += 256) {
+    const int j = e / (D / 4), c4 = e % (D / 4);
+    Store4<TV>::st(vc + cache_row(in, b, s.Hkv, g, L + j) * D + 4 * c4,
+                   tile + (Wt + j - shifted) * CW + QK + 4 * c4);
+  }
+  // rolled window: slot sl holds token L + m - W + sl = tile row Wt + m - W + sl
+  TV *oq = reinterpret_cast<TV *>(out.conv_q);
+  TV *ok = reinterpret_cast<TV *>(out.conv_k);
+  for (int e = tid; e < W * G * D; e += 256) {
+    const int sl = e / (G * D), c = e % (G * D);
+    oq[(size_t)(b * W + sl) * eq + g * G * D + c] = from_f32<TV>(tile[(Wt + m - W + sl) * CW + c]);
+  }
+  for (int e = tid; e < W * D; e += 256) {
+    const int sl = e / D, c = e % D;
+    ok[(size_t)(b * W + sl) * ekv + g * D + c] = from_f32<TV>(tile[(Wt + m - W + sl) * CW + G * D + c]);
+  }
+  if (shifted && out.vshift)
+    for (int c = tid; c < D; c += 256)
+      reinterpret_cast<TV *>(out.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
+          from_f32<TV>(tile[(Wt + m - 1) * CW + QK + c]);
 }
 
 // ---------------------------------------------------------------------------
@@ -624,7 +769,8 @@ bool convmix_fits(int G, int d) {
 
 template <typename TQ, typename TV, int D>
 static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
-                                    TQ *k, TV *vt, const StateOut &st, hipStream_t stream) {
+                                    TQ *k, TV *vt, const StateOut &st, const float *r1b,
+                                    hipStream_t stream) {
   const int TC = mix_chunk(s.G, D);
   const int nchunks = s.Tp / TC;
   // about 4 chunks per workgroup, at least ~1024 workgroups when the work allows
@@ -634,18 +780,19 @@ static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const f
   const int nseg = (nchunks + cpw - 1) / cpw;
   const size_t lds = mix_lds_bytes(TC + HALO, s.G, D, TC);
   hipLaunchKernelGGL((convmix_prefill_kernel<TQ, TV, D>), dim3(streams * nseg), dim3(256), lds,
-                     stream, s, w, qkv, q, k, vt, st, TC, nchunks, cpw, nseg);
+                     stream, s, w, qkv, q, k, vt, st, r1b, TC, nchunks, cpw, nseg);
   return hipGetLastError();
 }
 
 template <typename TQ, typename TV>
 hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
-                                  TQ *k, TV *vt, const StateOut &st, hipStream_t stream) {
+                                  TQ *k, TV *vt, const StateOut &st, hipStream_t stream,
+                                  const float *r1b) {
   switch (s.d) {
-    case 16: return convmix_prefill_d<TQ, TV, 16>(s, w, qkv, q, k, vt, st, stream);
-    case 32: return convmix_prefill_d<TQ, TV, 32>(s, w, qkv, q, k, vt, st, stream);
-    case 64: return convmix_prefill_d<TQ, TV, 64>(s, w, qkv, q, k, vt, st, stream);
-    case 128: return convmix_prefill_d<TQ, TV, 128>(s, w, qkv, q, k, vt, st, stream);
+    case 16: return convmix_prefill_d<TQ, TV, 16>(s, w, qkv, q, k, vt, st, r1b, stream);
+    case 32: return convmix_prefill_d<TQ, TV, 32>(s, w, qkv, q, k, vt, st, r1b, stream);
+    case 64: return convmix_prefill_d<TQ, TV, 64>(s, w, qkv, q, k, vt, st, r1b, stream);
+    case 128: return convmix_prefill_d<TQ, TV, 128>(s, w, qkv, q, k, vt, st, r1b, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -674,15 +821,59 @@ hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const floa
   return hipErrorInvalidValue;
 }
 
+static size_t decode_grouped_lds_bytes(int G, int D, int m, int ks, int kc) {
+  const int W = ks - 1 + kc - 1, Wt = W > 0 ? W : 1;
+  return ((size_t)(Wt + m) * (G + 2) * D + (size_t)(kc - 1 + m) * (G + 1) * D) * 4 +
+         (size_t)m * (D / 2) * 8;
+}
+
+bool convmix_decode_grouped_fits(int G, int d, int m, int ks, int kc) {
+  return m >= 1 && decode_grouped_lds_bytes(G, d, m, ks, kc) <= 65536;
+}
+
+template <typename TV, int D>
+static hipError_t convmix_decode_grouped_d(const MixShape &s, const MixTaps &w, const float *dq,
+                                           const float *dk, const float *qkv, int L,
+                                           const int *lens, const StateOut &in,
+                                           const StateOut &out, float *q, hipStream_t stream) {
+  const size_t lds = decode_grouped_lds_bytes(s.G, D, s.T, s.ks, s.kc);
+  if (lds > 65536) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((convmix_decode_grouped_kernel<TV, D>), dim3(s.B * s.Hkv), dim3(256), lds,
+                     stream, s, w, dq, dk, qkv, L, lens, in, out, q);
+  return hipGetLastError();
+}
+
+template <typename TV>
+hipError_t launch_convmix_decode_grouped(const MixShape &s, const MixTaps &w, const float *dense_q,
+                                         const float *dense_k, const float *qkv, int L,
+                                         const int *lens, const StateOut &in, const StateOut &out,
+                                         float *q, hipStream_t stream) {
+  switch (s.d) {
+    case 16: return convmix_decode_grouped_d<TV, 16>(s, w, dense_q, dense_k, qkv, L, lens, in, out, q, stream);
+    case 32: return convmix_decode_grouped_d<TV, 32>(s, w, dense_q, dense_k, qkv, L, lens, in, out, q, stream);
+    case 64: return convmix_decode_grouped_d<TV, 64>(s, w, dense_q, dense_k, qkv, L, lens, in, out, q, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template hipError_t launch_convmix_decode_grouped<bf16>(const MixShape &, const MixTaps &,
+                                                        const float *, const float *, const float *,
+                                                        int, const int *, const StateOut &,
+                                                        const StateOut &, float *, hipStream_t);
+template hipError_t launch_convmix_decode_grouped<float>(const MixShape &, const MixTaps &,
+                                                         const float *, const float *, const float *,
+                                                         int, const int *, const StateOut &,
+                                                         const StateOut &, float *, hipStream_t);
+
 template hipError_t launch_convmix_prefill<f16, bf16>(const MixShape &, const MixTaps &,
                                                       const float *, f16 *, f16 *, bf16 *,
-                                                      const StateOut &, hipStream_t);
+                                                      const StateOut &, hipStream_t, const float *);
 template hipError_t launch_convmix_prefill<bf16, bf16>(const MixShape &, const MixTaps &,
                                                        const float *, bf16 *, bf16 *, bf16 *,
-                                                       const StateOut &, hipStream_t);
+                                                       const StateOut &, hipStream_t, const float *);
 template hipError_t launch_convmix_prefill<float, float>(const MixShape &, const MixTaps &,
                                                          const float *, float *, float *, float *,
-                                                         const StateOut &, hipStream_t);
+                                                         const StateOut &, hipStream_t, const float *);
 template hipError_t launch_convmix_decode<bf16>(const MixShape &, const MixTaps &, const float *,
                                                 int, const int *, const StateOut &, const StateOut &, float *,
                                                 hipStream_t);

@@ -74,6 +74,15 @@ typedef enum {
 
 typedef enum { CCA_BF16 = 0, CCA_F32 = 1 } cca_dtype;
 
+/* Reading of the channel convolution [GS-EN "2. Methodology" / Convolutional
+ * Mixing: 1-D convolutions across the sequence and channel dimensions].
+ * CCA_CHAN_PER_HEAD: one k_c-tap filter per head sliding along the head's
+ *   channel index, b[t,h,i] = sum_j w[h,j] a[t,h,i-j] (the default).
+ * CCA_CHAN_GROUPED: a k_c-lag causal convolution over tokens that mixes the
+ *   d channels of each head densely, b[t,h,i] = sum_j sum_c W[h,i,j,c]
+ *   a[t-j,h,c], a = 0 before the sequence start. */
+typedef enum { CCA_CHAN_PER_HEAD = 0, CCA_CHAN_GROUPED = 1 } cca_chan_conv;
+
 /* Shape and switches of one attention layer.  C (compression) and G are
  * derived: e_q = n_q_heads*head_dim, e_kv = n_kv_heads*head_dim,
  * G = n_q_heads / n_kv_heads. */
@@ -92,13 +101,21 @@ typedef struct {
   float rope_base;        /* > 0, or 0 to switch RoPE off */
   float norm_eps;         /* > 0 (1e-6 by default) */
   int32_t dtype;          /* cca_dtype: storage of x, y, weights, cache, state */
+  int32_t chan_conv_mode; /* cca_chan_conv; 0 (zero-initialised) is the per-head filter.
+                           * CCA_CHAN_GROUPED needs d in {16, 32, 64}; the training and
+                           * fused prefill entry points reject it (CCA_ERR_UNSUPPORTED) */
 } cca_config;
 
 /* Weights.  w_qkv: [e_q + 2*e_kv, E] in cfg.dtype, rows q | k | v.
  * w_o: [E, e_q] in cfg.dtype (latent output flattened head-major, h*d+i).
  * q_seq_taps [e_q, k_s], k_seq_taps [e_kv, k_s]: fp32, lag-indexed.
- * q_chan_taps [H_q, k_c], k_chan_taps [H_kv, k_c]: fp32, lag-indexed.
- * tau [H_q]: fp32 logit temperature per query head. */
+ * q_chan_taps [H_q, k_c], k_chan_taps [H_kv, k_c]: fp32, lag-indexed (the
+ *   per-head channel filter; unused under CCA_CHAN_GROUPED).
+ * tau [H_q]: fp32 logit temperature per query head.
+ * q_chan_dense [H_q, d, k_c, d], k_chan_dense [H_kv, d, k_c, d]: fp32, the
+ *   grouped channel conv's W[h, i_out, lag, c_in], 16-byte aligned; read only
+ *   under CCA_CHAN_GROUPED (NULL otherwise is fine).  bf16 configurations
+ *   multiply them in fp16 (MFMA, fp32 accumulation). */
 typedef struct {
   const void *w_qkv;
   const void *w_o;
@@ -107,14 +124,17 @@ typedef struct {
   const float *q_chan_taps;
   const float *k_chan_taps;
   const float *tau;
+  const float *q_chan_dense;
+  const float *k_chan_dense;
 } cca_weights;
 
 /* Decode state, caller-owned, all in cfg.dtype.
  * k_cache, v_cache: [B, H_kv, capacity, d].  K holds the normalised, rotated
  *   k (tau not folded in); V the value after value-shift.
- * conv_q [B, k_s-1, e_q], conv_k [B, k_s-1, e_kv]: pre-convolution q~, k~ of
- *   the last k_s-1 tokens, slot 0 the oldest; zeros stand for tokens before
- *   the sequence start.
+ * conv_q [B, W, e_q], conv_k [B, W, e_kv]: pre-convolution q~, k~ of the
+ *   last W tokens, slot 0 the oldest; zeros stand for tokens before the
+ *   sequence start.  W = k_s-1, or (k_s-1) + (k_c-1) under CCA_CHAN_GROUPED
+ *   (its lagged inputs a[t-j] need the extra rows).
  * vshift [B, H_kv/2, d]: pre-shift value of the last token on the shifted
  *   (upper) kv heads; unused (may be NULL) when use_value_shift is 0. */
 typedef struct {
@@ -344,7 +364,9 @@ const char *cca_status_string(cca_status s);
  *               swapped (bits 2 and 3 of the token index exchanged)
  *   CCA_WS_O    [B*T, e_q] latent attention output, cfg.dtype
  *   CCA_WS_PART scratch of cca_prefill_forward_fused (the 3 rows before each
- *               128-token tile), for the shapes it takes
+ *               128-token tile), for the shapes it takes; under
+ *               CCA_CHAN_GROUPED fp32 [B*T, e_q + e_kv], the channel conv's
+ *               output (q heads, then k heads)
  * Decode workspace layout:
  *   CCA_WS_QKV  fp32 [B, e_q + 2*e_kv]
  *   CCA_WS_Q    fp32 [B, H_q, d]  normalised, rotated q of the new token

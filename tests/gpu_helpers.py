@@ -54,7 +54,9 @@ def upload_weights(Wt, dev="cuda"):
         k_seq_taps=torch.from_numpy(Wt.k_seq_taps).to(dev),
         q_chan_taps=torch.from_numpy(Wt.q_chan_taps).to(dev),
         k_chan_taps=torch.from_numpy(Wt.k_chan_taps).to(dev),
-        tau=torch.from_numpy(Wt.tau).to(dev))
+        tau=torch.from_numpy(Wt.tau).to(dev),
+        q_chan_dense=None if Wt.q_chan_dense is None else torch.from_numpy(Wt.q_chan_dense).to(dev),
+        k_chan_dense=None if Wt.k_chan_dense is None else torch.from_numpy(Wt.k_chan_dense).to(dev))
 
 
 def set_taps(P, seq=None, chan=None, tau=None):
@@ -73,10 +75,10 @@ def set_taps(P, seq=None, chan=None, tau=None):
 class PrefillRun:
     """Device buffers and one prefill through cca_prefill_forward."""
 
-    def __init__(self, shape: CCAShape, P, capacity: int = 0, dev="cuda"):
+    def __init__(self, shape: CCAShape, P, capacity: int = 0, dev="cuda", chan_conv="per_head"):
         L, T = lib(), tens()
         self.shape, self.P = shape, P
-        self.cfg = L.make_config(shape)
+        self.cfg = L.make_config(shape, chan_conv=chan_conv)
         assert L.validate_config(self.cfg) == L.CCA_OK
         self.w = upload_weights(P.weights, dev)
         self.x = T.to_device(P.x_s, dev)
@@ -87,12 +89,14 @@ class PrefillRun:
         if capacity:
             s = shape
             sd = T.storage_dtype(s.dtype)
+            # carried pre-conv rows: k_s - 1, plus k_c - 1 under the grouped channel conv
+            win = s.seq_conv_k - 1 + (s.chan_conv_k - 1 if chan_conv == "grouped" else 0)
             self.state = L.State(
                 k_cache=torch.zeros((s.batch, s.n_kv_heads, capacity, s.head_dim), dtype=sd, device=dev),
                 v_cache=torch.zeros((s.batch, s.n_kv_heads, capacity, s.head_dim), dtype=sd, device=dev),
                 capacity=capacity,
-                conv_q=torch.zeros((s.batch, s.seq_conv_k - 1, s.e_q), dtype=sd, device=dev),
-                conv_k=torch.zeros((s.batch, s.seq_conv_k - 1, s.e_kv), dtype=sd, device=dev),
+                conv_q=torch.zeros((s.batch, win, s.e_q), dtype=sd, device=dev),
+                conv_k=torch.zeros((s.batch, win, s.e_kv), dtype=sd, device=dev),
                 vshift=torch.zeros((s.batch, max(s.n_kv_heads // 2, 1), s.head_dim), dtype=sd, device=dev))
 
     def run(self):

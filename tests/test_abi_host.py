@@ -87,9 +87,9 @@ def test_invalid_configs(L, kw, err):
     assert L.prefill_workspace_size(cfg) == 0
 
 
-def _fake_weights(L):
+def _fake_weights(L, dense=0x10000):
     a = 0x10000
-    return L._Weights(a, a, a, a, a, a, a)
+    return L._Weights(a, a, a, a, a, a, a, dense, dense)
 
 
 def test_prefill_rejects_before_launch(L):
@@ -258,3 +258,40 @@ def test_prefill_fused_rejects_unsupported_shapes(L):
                                 head_dim=64))
     need = L.prefill_workspace_size(ok)
     assert f(C.byref(ok), C.byref(w), 0x10000, 0x20000, 0x100000, need - 1, None) == L.CCA_ERR_WORKSPACE
+
+
+def test_grouped_channel_conv_validation(L):
+    """The grouped channel-conv mode: d up to 64, its extra workspace, the
+    dense weights required, and the entry points that do not take it."""
+    base = CCAShape(batch=2, seq_len=40, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    per = L.make_config(base)
+    grp = L.make_config(base, chan_conv="grouped")
+    assert L.validate_config(grp) == L.CCA_OK
+    bad = L.make_config(base)
+    bad.chan_conv_mode = 7
+    assert L.validate_config(bad) == L.CCA_ERR_INVALID_ARG
+    assert L.validate_config(L.make_config(base.with_(head_dim=128, d_model=512),
+                                           chan_conv="grouped")) == L.CCA_ERR_UNSUPPORTED
+    # the channel conv's fp32 output lives in CCA_WS_PART
+    off = (C.c_size_t * 7)()
+    assert L.lib.cca_prefill_workspace_layout(C.byref(grp), off) == L.CCA_OK
+    assert off[5] != (1 << 64) - 1
+    assert L.prefill_workspace_size(grp) - L.prefill_workspace_size(per) >= 2 * 40 * (4 + 2) * 64 * 4
+    # training does not take it
+    assert L.train_workspace_size(grp) == 0
+    ft = L.lib.cca_prefill_forward_train
+    w = _fake_weights(L)
+    assert ft(C.byref(grp), C.byref(w), 0xA0000, 0xB0000, 0x100000, 1 << 30, None) == \
+        L.CCA_ERR_UNSUPPORTED
+    # dense weights required (and 16-byte aligned) before anything launches
+    f = L.lib.cca_prefill_forward
+    need = L.prefill_workspace_size(grp)
+    for dense in (0, 0x10004):
+        wd = _fake_weights(L, dense=dense)
+        assert f(C.byref(grp), C.byref(wd), 0x10000, 0x20000, None, 0x100000, need, None) == \
+            L.CCA_ERR_INVALID_ARG
+    # the fused prefill follows the per-head reading only
+    fused = L.make_config(CCAShape(batch=1, seq_len=256, d_model=256, n_q_heads=4, n_kv_heads=4,
+                                   head_dim=64), chan_conv="grouped")
+    assert L.lib.cca_prefill_forward_fused(C.byref(fused), C.byref(w), 0x10000, 0x20000, 0x100000,
+                                           1 << 30, None) == L.CCA_ERR_UNSUPPORTED
