@@ -67,10 +67,57 @@ def calibrate_copy():
 
 def upload_weights(cca, T, W, dev):
     import torch
+    dense = lambda a: None if a is None else torch.from_numpy(a).to(dev)
     return cca.Weights(T.to_device(W.w_qkv_s, dev), T.to_device(W.w_o_s, dev),
                        torch.from_numpy(W.q_seq_taps).to(dev), torch.from_numpy(W.k_seq_taps).to(dev),
                        torch.from_numpy(W.q_chan_taps).to(dev), torch.from_numpy(W.k_chan_taps).to(dev),
-                       torch.from_numpy(W.tau).to(dev))
+                       torch.from_numpy(W.tau).to(dev), dense(W.q_chan_dense), dense(W.k_chan_dense))
+
+
+def grouped_reading(cca, T, sp, sd, P, D_weights, x, y, st, xt, yt, L, K, dev):
+    """The prefill and decode workloads under the grouped channel-conv
+    reading (dense d x d weights per lag and head, drawn from their own seeded
+    stream): the prefill through cca_prefill_forward and its mixing stage
+    alone (the MFMA channel conv plus the mixing kernel), and the decode step
+    with its (k_s-1)+(k_c-1)-row window.  None when the shapes do not take it."""
+    import torch
+    from synth import add_chan_dense
+    gp, gd = cca.make_config(sp, chan_conv="grouped"), cca.make_config(sd, chan_conv="grouped")
+    if cca.validate_config(gp) != cca.CCA_OK or cca.validate_config(gd) != cca.CCA_OK:
+        return None
+    add_chan_dense(P.weights, sp, 0)
+    add_chan_dense(D_weights, sd, 0)
+    pw, dw = upload_weights(cca, T, P.weights, dev), upload_weights(cca, T, D_weights, dev)
+    ws = T.workspace(cca.prefill_workspace_size(gp), dev)
+    win = sd.seq_conv_k - 1 + sd.chan_conv_k - 1
+    sdt = st.conv_q.dtype
+    stg = cca.State(st.k_cache, st.v_cache, st.capacity,
+                    torch.zeros((sd.batch, win, sd.e_q), dtype=sdt, device=dev),
+                    torch.zeros((sd.batch, win, sd.e_kv), dtype=sdt, device=dev), st.vshift)
+    dws = T.workspace(cca.decode_workspace_size(gd, L), dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        for a, b_ in evs:
+            a.record()
+            fn()
+            b_.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b_) for a, b_ in evs) / K
+
+    prefill = timed(lambda: cca.prefill_forward(gp, pw, x, y, ws))
+    cca.stage_downproj(gp, pw, x, ws)
+    mix = timed(lambda: cca.stage_convmix(gp, pw, ws))
+    decode = timed(lambda: cca.decode_step(gd, dw, xt, L, stg, stg, yt, dws))
+    flops = 2.0 * sp.batch * sp.seq_len * (sp.n_q_heads + sp.n_kv_heads) * sp.head_dim * \
+        sp.chan_conv_k * sp.head_dim
+    return {"reading": "grouped channel conv, dense d x d weights per lag and head",
+            "prefill_ms": round(prefill, 4), "mix_stage_ms": round(mix, 4),
+            "channel_conv_gflop": round(flops / 1e9, 3),
+            "decode_ms": round(decode, 4)}
 
 
 def algorithmic(sp, sd):
@@ -445,6 +492,9 @@ def main():
         torch.cuda.synchronize()
         fused_ms = sum(a.elapsed_time(b_) for a, b_ in fev) / K
 
+    # ---- timed region 3e: the grouped channel-conv reading -----------------
+    grouped = grouped_reading(cca, T, sp, sd, P, D.weights, x, y, st, xt, yt, L, K, dev)
+
     # ---- timed region 4: a training step on the prefill workload ----------
     # forward_train (the forward keeping its activations) then the backward
     # pass with a seeded upstream gradient; every gradient is computed
@@ -507,6 +557,7 @@ def main():
                          "tokens_per_s": round(sd.batch * multi_m / (multi_ms * 1e-3), 1),
                          "single_token_tokens_per_s": round(sd.batch / (varlen_ms * 1e-3), 1)},
         "prefill_fused_ms": None if fused_ms is None else round(fused_ms, 4),
+        "grouped_chan_conv": grouped,
         "train": train,
         "attn_tflops": round(attn_tflops, 1),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},

@@ -67,27 +67,74 @@ __global__ __launch_bounds__(256) void grouped_conv_prefill_kernel(MixShape s, M
   const float *u0 = qkv + (size_t)b * s.T * N + colbase;
 
   // W: column K = jp * d + c of output row i holds W[h, i, kc-1-jp, c] (A
-  // row t, column jp * d + c, is a[t - kc + 1 + jp, c])
-  for (int e = tid; e < DP * KD; e += 256) {
-    const int i = e / KD, K = e % KD, jp = K / D, c = K % D;
-    const float v = i < D ? dense[((size_t)i * kc + (kc - 1 - jp)) * D + c] : 0.f;
-    if constexpr (F32) w_lds[K * DP + i] = v;
-    else w_lds[i * WPAD + K] = (f16)v;
-  }
-  // a rows (zero outside [0, T)), four channels per item
-  for (int e = tid; e < arows * (D / 4); e += 256) {
-    const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
-    const int t = t0 - (kc - 1) + r;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t >= 0 && t < s.T) {
-      for (int j = 0; j < ks && t - j >= 0; ++j) {
-        const f32x4 u = *reinterpret_cast<const f32x4 *>(u0 + (size_t)(t - j) * N + c0);
+  // row t, column jp * d + c, is a[t - kc + 1 + jp, c]).  Four channels per
+  // item; every load of a thread is issued before the first store.
+  {
+    constexpr int NW4 = (DP * TL::KMAX / 4 + 255) / 256;   // items per thread at k_c = 4
+    const int kd4 = KD / 4, nw4 = DP * kd4;
+    f32x4 wv[NW4];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) acc[cc] = fmaf(seqw[(c0 + cc) * ks + j], u[cc], acc[cc]);
+    for (int k = 0; k < NW4; ++k) {
+      const int e = tid + 256 * k;
+      wv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (e < nw4) {
+        const int i = e / kd4, K = 4 * (e - i * kd4), jp = K / D, c = K % D;
+        if (i < D) wv[k] = *reinterpret_cast<const f32x4 *>(dense + ((size_t)i * kc + (kc - 1 - jp)) * D + c);
       }
     }
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) a_lds[r * APAD + c0 + cc] = (TE)acc[cc];
+    for (int k = 0; k < NW4; ++k) {
+      const int e = tid + 256 * k;
+      if (e < nw4) {
+        const int i = e / kd4, K = 4 * (e - i * kd4);
+        if constexpr (F32) {
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) w_lds[(K + cc) * DP + i] = wv[k][cc];
+        } else {
+          *reinterpret_cast<f16x4 *>(w_lds + i * WPAD + K) =
+              f16x4{(f16)wv[k][0], (f16)wv[k][1], (f16)wv[k][2], (f16)wv[k][3]};
+        }
+      }
+    }
+  }
+  // a rows (zero outside [0, T)).  A thread always owns the same 4 channels
+  // (256 is a multiple of d / 4), so its taps load once; the pre-conv rows of
+  // three items at a time are in flight together.
+  {
+    const int c0 = 4 * (tid % (D / 4)), r0 = tid / (D / 4);
+    constexpr int RSTEP = 256 / (D / 4);
+    float tp[4][4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tp[cc][j] = j < ks ? seqw[(c0 + cc) * ks + j] : 0.f;
+    constexpr int NA = (TL::AROWS + RSTEP - 1) / RSTEP, BATCH = 3;
+#pragma unroll
+    for (int k0 = 0; k0 < NA; k0 += BATCH) {
+      f32x4 u[BATCH][4];
+#pragma unroll
+      for (int kb = 0; kb < BATCH; ++kb) {
+        const int r = r0 + RSTEP * (k0 + kb), t = t0 - (kc - 1) + r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = k0 + kb < NA && r < arows && j < ks && t - j >= 0 && t < s.T;
+          u[kb][j] = ok ? *reinterpret_cast<const f32x4 *>(u0 + (size_t)(t - j) * N + c0)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < BATCH; ++kb) {
+        const int r = r0 + RSTEP * (k0 + kb);
+        if (k0 + kb >= NA || r >= arows) continue;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc = fmaf(tp[cc][j], u[kb][j][cc], acc);
+          a_lds[r * APAD + c0 + cc] = (TE)acc;
+        }
+      }
+    }
   }
   __syncthreads();
 
