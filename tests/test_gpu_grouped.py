@@ -128,3 +128,51 @@ def test_grouped_prefill_state_then_decode(dtype):
     _, _, cq2, ck2, _ = O.prefill_state(lat_all, full, GROUPED)
     assert rel_l2(T.to_f64(st.conv_q), cq2) < tol
     assert rel_l2(T.to_f64(st.conv_k), ck2) < tol
+
+
+def test_grouped_paged_and_varlen_equal_contiguous():
+    """Under the grouped reading the paged prefill writes the same cache rows
+    and window as the contiguous one, and the per-sequence-length and paged
+    decode steps equal the uniform step bit for bit when every length is the
+    same."""
+    from test_gpu_paged import _gather, _paged_from
+    shape = CCAShape(batch=2, seq_len=150, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    _say(f"[grouped] paged / varlen {shape}")
+    P = _prefill(shape, seed=12)
+    T, L = tens(), lib()
+    run = PrefillRun(shape, P, capacity=160, chan_conv="grouped")
+    run.run()
+    st = run.state
+    page = 32
+    mpps = (160 + page - 1) // page
+    kp, table = _paged_from(torch.zeros_like(st.k_cache), page, mpps, seed=3)
+    vp, _ = _paged_from(torch.zeros_like(st.v_cache), page, mpps, seed=3)
+    pst = L.PagedState(kp, vp, table, page, torch.zeros_like(st.conv_q), torch.zeros_like(st.conv_k),
+                       torch.zeros_like(st.vshift))
+    y2 = torch.empty_like(run.y)
+    L.prefill_forward_paged(run.cfg, run.w, run.x, y2, run.ws, pst)
+    torch.cuda.synchronize()
+    assert torch.equal(run.y.view(torch.int16), y2.view(torch.int16))
+    for b in range(shape.batch):
+        rows = list(range(shape.seq_len))
+        assert torch.equal(_gather(kp, table, b, rows).view(torch.int16),
+                           st.k_cache[b, :, :shape.seq_len].view(torch.int16))
+    assert torch.equal(pst.conv_q.view(torch.int16), st.conv_q.view(torch.int16))
+    # one more token: uniform, per-sequence-length and paged steps agree
+    dcfg = L.make_config(shape.with_(seq_len=1), chan_conv="grouped")
+    xt = T.to_device(np.ascontiguousarray(
+        np.random.default_rng(2).standard_normal((shape.batch, shape.d_model)).astype(np.float32)))
+    xt = xt.to(torch.bfloat16)
+    Lc = shape.seq_len
+    st_u = L.State(st.k_cache.clone(), st.v_cache.clone(), st.capacity, st.conv_q.clone(),
+                   st.conv_k.clone(), st.vshift.clone())
+    ya, yb, yc = torch.empty_like(xt), torch.empty_like(xt), torch.empty_like(xt)
+    ws = T.workspace(L.decode_workspace_size(dcfg, Lc))
+    L.decode_step(dcfg, run.w, xt, Lc, st_u, st_u, ya, ws)
+    dl = torch.full((shape.batch,), Lc, dtype=torch.int32, device="cuda")
+    L.decode_step_varlen(dcfg, run.w, xt, dl, Lc, st, st, yb, ws)
+    L.decode_step_paged(dcfg, run.w, xt, dl, Lc, pst, pst, yc, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+    assert torch.equal(ya.view(torch.int16), yc.view(torch.int16))
+    assert torch.equal(st_u.conv_q.view(torch.int16), pst.conv_q.view(torch.int16))
