@@ -475,9 +475,9 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
 // sequence at positions L .. L+m-1).  The carried window holds W = (k_s - 1)
 // + (k_c - 1) pre-conv rows; one workgroup per (b, g) stages them with the m
 // new rows, computes a (the sequence conv) for tokens L-k_c+1 .. L+m-1 into
-// LDS, then each (new token, head) unit forms its 4 channels of
-// b = sum_j W[h, i, j, :] . a[t - j] on the VALU (one (sequence, group) holds
-// at most a few hundred of them) and finishes with mix_tail.  All state reads
+// LDS, then one thread per output forms b = sum_j W[h, i, j, :] . a[t - j]
+// on the VALU (one (sequence, group) holds at most a few thousand of them)
+// into LDS, and each (new token, head) unit finishes with mix_tail.  All state reads
 // finish before the first barrier, so state_out may alias state_in.
 template <typename TV, int D>
 __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
   const int R = Wt + m, AR = kc1 + m;
   float *tile = lds;                     // [R][CW]: rows 0..Wt-1 carried, then the new tokens
   float *at = tile + R * CW;             // [AR][QK]: a of tokens L-kc1 .. L+m-1
-  float2 *rot = reinterpret_cast<float2 *>(at + AR * QK);
+  float2 *rot = reinterpret_cast<float2 *>(at + AR * QK);   // [m][D/2], then b [m][QK]
 
   const int tid = threadIdx.x;
   const int g = blockIdx.x % s.Hkv, b = blockIdx.x / s.Hkv;
@@ -534,6 +534,28 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
   }
   __syncthreads();
 
+  // b of every (new token j, head slot, channel i): one thread per output,
+  // a dot product of the row W[h, i, :, :] (k_c * d contiguous floats) with
+  // the a rows of the k_c lags; results to LDS for the per-head tails below
+  float *bt = reinterpret_cast<float *>(rot + m * (D / 2));
+  for (int e = tid; e < m * QK; e += 256) {
+    const int j = e / QK, col = e % QK, slot = col / D, i = col % D;
+    const float *wrow = (slot < G ? dense_q + (size_t)(g * G + slot) * D * s.kc * D
+                                  : dense_k + (size_t)g * D * s.kc * D) + (size_t)i * s.kc * D;
+    float acc = 0.f;
+    for (int lag = 0; lag < s.kc; ++lag) {
+      const float *arow = at + (kc1 + j - lag) * QK + slot * D;   // a of token L + j - lag
+#pragma unroll
+      for (int c4 = 0; c4 < D; c4 += 4) {
+        const f32x4 wv = *reinterpret_cast<const f32x4 *>(wrow + lag * D + c4);
+        const f32x4 av = *reinterpret_cast<const f32x4 *>(arow + c4);
+        acc += wv[0] * av[0] + wv[1] * av[1] + wv[2] * av[2] + wv[3] * av[3];
+      }
+    }
+    bt[e] = acc;
+  }
+  __syncthreads();
+
   constexpr int LPU = D / 4;
   const int upp = 256 / LPU;
   const int li = tid % LPU, ui = tid / LPU;
@@ -543,20 +565,8 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
     const int unit = u0 + ui;
     const bool active = unit < m * (G + 1);
     const int j = active ? unit / (G + 1) : 0, slot = active ? unit % (G + 1) : 0;
-    const float *wd = slot < G ? dense_q + (size_t)(g * G + slot) * D * s.kc * D
-                               : dense_k + (size_t)g * D * s.kc * D;
-    float bb[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int lag = 0; lag < s.kc; ++lag) {
-      const float *arow = at + (kc1 + j - lag) * QK + slot * D;     // a of token L + j - lag
-      for (int c4 = 0; c4 < D; c4 += 4) {
-        const f32x4 av = *reinterpret_cast<const f32x4 *>(arow + c4);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const f32x4 wv = *reinterpret_cast<const f32x4 *>(wd + ((size_t)(4 * li + cc) * s.kc + lag) * D + c4);
-          bb[cc] += wv[0] * av[0] + wv[1] * av[1] + wv[2] * av[2] + wv[3] * av[3];
-        }
-      }
-    }
+    const f32x4 bv = *reinterpret_cast<const f32x4 *>(bt + j * QK + slot * D + 4 * li);
+    float bb[4] = {bv[0], bv[1], bv[2], bv[3]};
     float y[4];
     mix_tail<D>(tile + (Wt + j) * CW + 4 * li, slot, G, s, rot[j * (D / 2) + 2 * li],
                 rot[j * (D / 2) + 2 * li + 1], bb, y);
@@ -823,8 +833,8 @@ hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const floa
 
 static size_t decode_grouped_lds_bytes(int G, int D, int m, int ks, int kc) {
   const int W = ks - 1 + kc - 1, Wt = W > 0 ? W : 1;
-  return ((size_t)(Wt + m) * (G + 2) * D + (size_t)(kc - 1 + m) * (G + 1) * D) * 4 +
-         (size_t)m * (D / 2) * 8;
+  return ((size_t)(Wt + m) * (G + 2) * D + (size_t)(kc - 1 + m) * (G + 1) * D +
+          (size_t)m * (G + 1) * D) * 4 + (size_t)m * (D / 2) * 8;
 }
 
 bool convmix_decode_grouped_fits(int G, int d, int m, int ks, int kc) {
