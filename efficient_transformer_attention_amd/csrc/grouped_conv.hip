@@ -207,12 +207,11 @@ template <int D, bool F32>
 static hipError_t gc_launch(const MixShape &s, const MixTaps &w, const float *dq, const float *dk,
                             const float *qkv, float *outb, hipStream_t stream) {
   const size_t lds = gc_lds_bytes<D, F32>();
-  static bool attr_set = false;   // per process: the attribute is a property of the function
-  if (!attr_set) {
+  if (lds > 65536) {   // above the default dynamic LDS limit (the fp32 mode); set on every call,
+                       // so each device the library runs on gets it
     hipError_t e = hipFuncSetAttribute((const void *)grouped_conv_prefill_kernel<D, F32>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int ntb = (s.T + GC_RB - 1) / GC_RB;
   const long long grid = (long long)s.B * (s.Hq + s.Hkv) * ntb;
