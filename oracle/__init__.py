@@ -28,7 +28,8 @@ Every step cites the passage of the pages that defines it.  Page tags:
 Where the pages leave a step open, the oracle takes one stated reading; the
 steps that rest on such a reading are marked "parity unpinned" below and in
 the design notes: the channel convolution's form (per-head taps sliding
-along the channel index), the exact q-k-mean formula, the temperature value,
+along the channel index, or the grouped switch: dense d x d weights per lag
+and head), the exact q-k-mean formula, the temperature value,
 the RoPE pair convention, and which half of the value heads is shifted.
 """
 
