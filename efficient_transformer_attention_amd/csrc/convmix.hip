@@ -783,10 +783,11 @@ static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const f
                                     hipStream_t stream) {
   const int TC = mix_chunk(s.G, D);
   const int nchunks = s.Tp / TC;
-  // about 4 chunks per workgroup, at least ~1024 workgroups when the work allows
+  // about 4 chunks per workgroup (the prefetch of chunk i+1 hides behind the
+  // mixing of chunk i), at least ~512 workgroups when the work allows
   const int streams = s.B * s.Hkv;
   int cpw = (nchunks / 4 > 0 && mix_prefetch_fits(s.G, D, TC)) ? 4 : 1;
-  while (cpw > 1 && (long long)streams * ((nchunks + cpw - 1) / cpw) < 1024) --cpw;
+  while (cpw > 1 && (long long)streams * ((nchunks + cpw - 1) / cpw) < 512) --cpw;
   const int nseg = (nchunks + cpw - 1) / cpw;
   const size_t lds = mix_lds_bytes(TC + HALO, s.G, D, TC);
   hipLaunchKernelGGL((convmix_prefill_kernel<TQ, TV, D>), dim3(streams * nseg), dim3(256), lds,
