@@ -42,52 +42,92 @@ namespace cca {
 
 // out[z][c'][r'] = in[z][r][c] for r < R, c < C, with r' = vt_perm(r) when
 // perm_r (else r) and c' = vt_perm(c) when perm_c; rows r >= Rvalid read as
-// zero.  z = z1 * nz2 + z2 selects the strides of both sides.  64 x 64 tiles
-// through LDS; with VEC-aligned sizes and strides (VEC = 16 bytes of
-// elements) every global access is a 16-byte vector, else element-wise.
+// zero.  z = z1 * nz2 + z2 selects the strides of both sides.
+//
+// Vector form (16-byte aligned sizes and strides): no LDS.  Each lane loads a
+// VEC x VEC block (VEC rows of 16 bytes), transposes it in registers and
+// stores VEC rows of 16 bytes; a wave covers a 64 x 64 (16-bit) or 32 x 32
+// (32-bit) tile, and a workgroup holds one or four waves.  Lanes 8j .. 8j+7
+// take consecutive row blocks of one column block, so each store instruction
+// writes eight 128-byte output segments (the load instructions read eight
+// 128-byte input segments either way).  The
+// permutations only move whole 4-row groups, so they become load / store
+// addresses.
+template <typename T> struct TrBits;
+template <> struct TrBits<bf16> { using U = unsigned short; };
+template <> struct TrBits<f16> { using U = unsigned short; };
+template <> struct TrBits<float> { using U = unsigned int; };
+
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void transpose_vec_kernel(const Tin *__restrict__ in,
+                                                            Tout *__restrict__ out, int R,
+                                                            int Rvalid, int C, long long in_rs,
+                                                            long long in_bs1, long long in_bs2,
+                                                            long long out_rs, long long out_bs1,
+                                                            long long out_bs2, int nz2, int ncx,
+                                                            int nry, int ntiles, int perm_r,
+                                                            int perm_c) {
+  static_assert(sizeof(Tin) == sizeof(Tout), "same element size on both sides");
+  constexpr int VEC = 16 / (int)sizeof(Tout);   // elements per 16 bytes
+  constexpr int TS = 8 * VEC;                   // tile side
+  const int tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (tile >= ntiles) return;
+  const int lane = threadIdx.x & 63, rb = lane & 7, cc = lane >> 3;
+  const int cx = tile % ncx, rest = tile / ncx, ry = rest % nry, z = rest / nry;
+  const int z1 = z / nz2, z2 = z % nz2;
+  const int r0 = ry * TS + rb * VEC, col = cx * TS + cc * VEC;
+  if (r0 >= R || col >= C) return;
+  const Tin *src = in + z1 * in_bs1 + z2 * in_bs2 + col;
+  Tout *dst = out + z1 * out_bs1 + z2 * out_bs2 + r0;
+  using U = typename TrBits<Tout>::U;
+  U e[VEC][VEC];                                // e[k][j]: input row r0 + k, column col + j
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) {
+    // input row that lands at output position r0 + k
+    const int gr = perm_r ? vt_perm(r0 + k) : r0 + k;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (gr < Rvalid) raw = ld16(src + gr * in_rs);
+    if constexpr (std::is_same<Tin, Tout>::value) {
+      const U *u = reinterpret_cast<const U *>(&raw);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) e[k][j] = u[j];
+    } else {
+      const Tin *iv = reinterpret_cast<const Tin *>(&raw);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const Tout o = from_f32<Tout>(to_f32(iv[j]));
+        e[k][j] = *reinterpret_cast<const U *>(&o);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    u32x4 o;
+    if constexpr (sizeof(U) == 2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = (unsigned)e[2 * w][j] | ((unsigned)e[2 * w + 1][j] << 16);
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = e[w][j];
+    }
+    const int gc = col + j;
+    st16(dst + (perm_c ? vt_perm(gc) : gc) * out_rs, o);
+  }
+}
+
+// element-wise form for unaligned sizes or strides: 64 x 64 tiles through LDS
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void transpose_kernel(const Tin *__restrict__ in,
                                                         Tout *__restrict__ out, int R, int Rvalid,
                                                         int C, long long in_rs, long long in_bs1,
                                                         long long in_bs2, long long out_rs,
                                                         long long out_bs1, long long out_bs2,
-                                                        int nz2, int perm_r, int perm_c, int vec) {
-  static_assert(sizeof(Tin) == sizeof(Tout), "same element size on both sides");
-  constexpr int VEC = 16 / (int)sizeof(Tout);
-  constexpr int PAD = VEC;                      // rows offset by 16 bytes
-  __shared__ __attribute__((aligned(16))) Tout tile[64][64 + PAD];
+                                                        int nz2, int perm_r, int perm_c) {
+  __shared__ Tout tile[64][65];
   const int z = blockIdx.z, z1 = z / nz2, z2 = z % nz2;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const Tin *src = in + z1 * in_bs1 + z2 * in_bs2;
   Tout *dst = out + z1 * out_bs1 + z2 * out_bs2;
-  if (vec) {
-    for (int e = threadIdx.x; e < 64 * 64 / VEC; e += 256) {
-      const int r = e / (64 / VEC), cv = (e % (64 / VEC)) * VEC, gr = r0 + r, gc = c0 + cv;
-      Tout v[VEC];
-      if (gr < Rvalid && gr < R && gc < C) {
-        const u32x4 raw = ld16(src + gr * in_rs + gc);
-        const Tin *iv = reinterpret_cast<const Tin *>(&raw);
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) v[k] = from_f32<Tout>(to_f32(iv[k]));
-      } else {
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) v[k] = from_f32<Tout>(0.f);
-      }
-      st16(&tile[r][cv], *reinterpret_cast<const u32x4 *>(v));
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64 / VEC; e += 256) {
-      const int oc = e / (64 / VEC), rv = (e % (64 / VEC)) * VEC;
-      const int gc = c0 + oc;                    // output row (before the column permutation)
-      if (gc >= C || r0 + rv >= R) continue;
-      const int tc = perm_c ? vt_perm(oc) : oc;  // tile column that lands in output row c0 + oc
-      Tout v[VEC];
-#pragma unroll
-      for (int k = 0; k < VEC; ++k) v[k] = tile[perm_r ? vt_perm(rv + k) : rv + k][tc];
-      st16(dst + gc * out_rs + r0 + rv, *reinterpret_cast<const u32x4 *>(v));
-    }
-    return;
-  }
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int r = e / 64, c = e % 64, gr = r0 + r, gc = c0 + c;
     tile[r][c] = (gr < Rvalid && gr < R && gc < C) ? from_f32<Tout>(to_f32(src[gr * in_rs + gc]))
@@ -110,16 +150,27 @@ hipError_t launch_transpose(const Tin *in, Tout *out, int R, int Rvalid, int C, 
                             int perm_c, hipStream_t stream) {
   if (R <= 0 || C <= 0 || nz1 * nz2 <= 0) return hipSuccess;
   constexpr int VEC = 16 / (int)sizeof(Tout);
-  // the permutations act inside aligned groups of 16, which the 64-tiles keep whole
+  // the permutations act inside aligned groups of 16, which the tiles keep whole
   const bool vec = (reinterpret_cast<uintptr_t>(in) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(out) % 16 == 0) && R % VEC == 0 && C % VEC == 0 &&
                    in_rs % VEC == 0 && in_bs1 % VEC == 0 && in_bs2 % VEC == 0 &&
                    out_rs % VEC == 0 && out_bs1 % VEC == 0 && out_bs2 % VEC == 0 &&
                    (!perm_r || R % 16 == 0) && (!perm_c || C % 16 == 0);
+  if (vec) {
+    constexpr int TS = 8 * VEC;
+    const int ncx = (C + TS - 1) / TS, nry = (R + TS - 1) / TS;
+    const long long nt = (long long)ncx * nry * nz1 * nz2;
+    if (nt > (1ll << 31) - 4) return hipErrorInvalidValue;
+    // one wave per workgroup for small transposes, so they still reach every CU
+    const int wpg = nt >= 4096 ? 4 : 1;
+    hipLaunchKernelGGL((transpose_vec_kernel<Tin, Tout>), dim3((unsigned)((nt + wpg - 1) / wpg)),
+                       dim3(64 * wpg), 0, stream, in, out, R, Rvalid, C, in_rs, in_bs1, in_bs2, out_rs, out_bs1,
+                       out_bs2, nz2, ncx, nry, (int)nt, perm_r, perm_c);
+    return hipGetLastError();
+  }
   dim3 grid((C + 63) / 64, (R + 63) / 64, nz1 * nz2);
   hipLaunchKernelGGL((transpose_kernel<Tin, Tout>), grid, dim3(256), 0, stream, in, out, R, Rvalid,
-                     C, in_rs, in_bs1, in_bs2, out_rs, out_bs1, out_bs2, nz2, perm_r, perm_c,
-                     vec ? 1 : 0);
+                     C, in_rs, in_bs1, in_bs2, out_rs, out_bs1, out_bs2, nz2, perm_r, perm_c);
   return hipGetLastError();
 }
 

@@ -304,12 +304,23 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
 // workgroups per CU (more slices only add fp32 partial traffic), slices of
 // at least 1024 elements.
 int gemm_long_k_slices(int M, int N, int K) {
-  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  int S = (512 + tiles - 1) / tiles;
-  const int maxs = K / 1024;
-  if (S > maxs) S = maxs;
-  if (S > 16) S = 16;
-  return S < 1 ? 1 : S;
+  // 128 x 128 tiles, S slices of the contraction: each CU runs
+  // ceil(tiles * S / 256) workgroups of K / S steps (two at a time).  Take the
+  // S that minimises that product, the smaller S on a tie (less to reduce).
+  const long long tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
+  int maxs = K / 1024;
+  if (maxs > 16) maxs = 16;
+  int best = 1;
+  long long best_cost = -1;
+  for (int S = 1; S <= maxs; ++S) {
+    const long long chunk = ((K + S - 1) / S + 31) / 32 * 32;
+    const long long cost = (tiles * S + 255) / 256 * chunk;
+    if (best_cost < 0 || cost < best_cost) {
+      best = S;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 template <typename Tin>
