@@ -277,13 +277,14 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
     if (K % 32 == 0 && (size_t)M * lda * 2 < lim && (size_t)N * ldb * 2 < lim) {
       // one 256 x 192 tile per CU when that covers the product in a single
       // round; 128 x 256 tiles for wide products with a long contraction (the
-      // backward's dx = dz W_qkv: 12% faster than 128 x 128 there, slower at
-      // K = 512); else 128 x 128 tiles (two workgroups per CU)
+      // backward's dx = dz W_qkv at K = 1536: 12% faster than 128 x 128 there,
+      // slower at K = 512 and no faster at K = 1024); else 128 x 128 tiles (two
+      // workgroups per CU)
       const int g256 = ((M + 255) / 256) * ((N + 191) / 192);
       if (g256 >= 224 && g256 <= 256) {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 256, 192, 32, 5, 1>), dim3(g256), dim3(256), 0,
                            stream, A, B, C, M, N, K, lda, ldb, ldc, K);
-      } else if (N % 256 == 0 && N >= 2048 && K >= 1024 && M >= 4096) {
+      } else if (N % 256 == 0 && N >= 2048 && K >= 1536 && M >= 4096) {
         const int g = ((M + 127) / 128) * (N / 256);
         hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 256, 32, 5, 1>), dim3(g), dim3(256), 0,
                            stream, A, B, C, M, N, K, lda, ldb, ldc, K);
