@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "cca.h"
 #include "cca_device.h"
@@ -203,8 +204,14 @@ struct TrainLayout {
 size_t splitk_floats(const cca_config &c, int BTp) {
   const int E = c.d_model, eq = c.n_q_heads * c.head_dim;
   const int N = eq + 2 * c.n_kv_heads * c.head_dim;
-  const size_t a = (size_t)gemm_long_k_slices(E, eq, BTp) * E * eq;
-  const size_t b = (size_t)gemm_long_k_slices(N, E, BTp) * N * E;
+  // the token-major products contract over B*T rows, the transposed ones over BTp
+  const int BT = c.batch * c.seq_len;
+  auto sl = [](int m, int n, int k1, int k2) {
+    const int a = gemm_long_k_slices(m, n, k1), b = gemm_long_k_slices(m, n, k2);
+    return (size_t)(a > b ? a : b);
+  };
+  const size_t a = sl(E, eq, BTp, BT) * E * eq;
+  const size_t b = sl(N, E, BTp, BT) * N * E;
   return a > b ? a : b;
 }
 
@@ -449,6 +456,23 @@ template <typename T> T *trp(void *ws, const TrainLayout &L, int slot) {
   return reinterpret_cast<T *>(static_cast<unsigned char *>(ws) + L.off[slot]);
 }
 
+// g[M, N] = a^T b for token-major a [BT, M], b [BT, N] (a weight gradient):
+// read in place (bf16, tile-aligned M and N), else transposed to [M, BTp] and
+// [N, BTp] copies (rows past BT zero) for the K-contiguous product.
+template <typename TV>
+hipError_t weight_grad(const TV *a, const TV *b, float *g, int M, int N, int BT, int BTp, TV *aT,
+                       TV *bT, float *splitk, size_t skf, hipStream_t st) {
+  if constexpr (std::is_same<TV, bf16>::value) {
+    const hipError_t e = launch_gemm_tn_long_k(a, b, g, M, N, BT, M, N, splitk, skf, st);
+    if (e != hipErrorNotSupported) return e;
+  }
+  hipError_t e = launch_transpose_2d<TV, TV>(a, aT, BTp, BT, M, M, BTp, st);
+  if (e != hipSuccess) return e;
+  e = launch_transpose_2d<TV, TV>(b, bT, BTp, BT, N, N, BTp, st);
+  if (e != hipSuccess) return e;
+  return launch_gemm_nt_long_k<TV>(aT, bT, g, M, N, BTp, BTp, BTp, splitk, skf, st);
+}
+
 template <typename TQ, typename TV>
 cca_status run_backward(const cca_config &c, const cca_weights *w, const void *x, const void *dy,
                         const cca_grads *gr, void *ws, const TrainLayout &L, hipStream_t st) {
@@ -465,14 +489,10 @@ cca_status run_backward(const cca_config &c, const cca_weights *w, const void *x
                                                    eq, eq, E, st), st));
   CCA_TRY(check_launch(launch_gemm_nt<TV, TV>((const TV *)dy, trp<TV>(ws, L, TR_WOT), dO, BT, eq, E,
                                               E, E, eq, st), st));
-  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>((const TV *)dy, trp<TV>(ws, L, TR_DYT), BTp, BT,
-                                                   E, E, BTp, st), st));
-  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>(O, trp<TV>(ws, L, TR_OT), BTp, BT, eq, eq, BTp,
-                                                   st), st));
   const size_t skf = splitk_floats(c, BTp);
-  CCA_TRY(check_launch(launch_gemm_nt_long_k<TV>(trp<TV>(ws, L, TR_DYT), trp<TV>(ws, L, TR_OT),
-                                                 gr->w_o, E, eq, BTp, BTp, BTp,
-                                                 trp<float>(ws, L, TR_SPLITK), skf, st), st));
+  CCA_TRY(check_launch(weight_grad<TV>((const TV *)dy, O, gr->w_o, E, eq, BT, BTp,
+                                       trp<TV>(ws, L, TR_DYT), trp<TV>(ws, L, TR_OT),
+                                       trp<float>(ws, L, TR_SPLITK), skf, st), st));
   // attention
   AttnBwdArgs<TQ, TV> aa;
   aa.q = reinterpret_cast<const TQ *>(wsp(ws, P, CCA_WS_Q));
@@ -511,13 +531,9 @@ cca_status run_backward(const cca_config &c, const cca_weights *w, const void *x
                                                    N, N, E, E, N, st), st));
   CCA_TRY(check_launch(launch_gemm_nt<TV, TV>(dz, trp<TV>(ws, L, TR_WQKVT), (TV *)gr->x, BT, E, N,
                                               N, N, E, st), st));
-  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>(dz, trp<TV>(ws, L, TR_DZT), BTp, BT, N, N, BTp,
-                                                   st), st));
-  CCA_TRY(check_launch(launch_transpose_2d<TV, TV>((const TV *)x, trp<TV>(ws, L, TR_XT), BTp, BT, E,
-                                                   E, BTp, st), st));
-  return check_launch(launch_gemm_nt_long_k<TV>(trp<TV>(ws, L, TR_DZT), trp<TV>(ws, L, TR_XT),
-                                                gr->w_qkv, N, E, BTp, BTp, BTp,
-                                                trp<float>(ws, L, TR_SPLITK), skf, st), st);
+  return check_launch(weight_grad<TV>(dz, (const TV *)x, gr->w_qkv, N, E, BT, BTp,
+                                      trp<TV>(ws, L, TR_DZT), trp<TV>(ws, L, TR_XT),
+                                      trp<float>(ws, L, TR_SPLITK), skf, st), st);
 }
 
 cca_config decode_cfg(const cca_config *c) {

@@ -30,6 +30,16 @@ template <typename Tin>
 hipError_t launch_gemm_nt_long_k(const Tin *A, const Tin *B, float *C, int M, int N, int K, int lda,
                                  int ldb, float *ws, size_t ws_floats, hipStream_t stream);
 
+// C[M,N] (fp32, ldc = N) = A^T B for row-major A [K][lda] and B [K][ldb]
+// (bf16), the contraction over rows (tokens): the same slices as above, the
+// operands read in place through LDS transpose reads.  hipErrorNotSupported
+// (nothing launched) unless M and N are multiples of 128, lda and ldb
+// multiples of 8 (16-byte rows), A and B 16-byte aligned and (K + 64) rows of
+// either operand under 2 GiB.
+hipError_t launch_gemm_tn_long_k(const bf16 *A, const bf16 *B, float *C, int M, int N, int K,
+                                 int lda, int ldb, float *ws, size_t ws_floats,
+                                 hipStream_t stream);
+
 // Sizes shared by the mixing and attention kernels.
 struct MixShape {
   int B, T, Tp;            // batch, tokens, tokens padded to the query tile

@@ -221,6 +221,201 @@ __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__res
     }
 }
 
+// ---------------------------------------------------------------------------
+// Token-major operands: C[m][n] = sum_k A[k][m] B[k][n] with A [K][lda] and
+// B [K][ldb] row-major, i.e. the contraction runs over rows (the weight
+// gradients dW_o = dy^T O and dW_qkv = dz^T x contract over tokens).  Same
+// ring, barriers and MFMA schedule as gemm_nt_dma_kernel; what changes is the
+// layout:
+//   * a stage holds 32 k-rows of BM (A) and BN (B) elements as they lie in
+//     memory (rows of 256 bytes for 128 columns), 16-byte chunks XOR-swizzled
+//     by ((k & 3) << 2), so the four k-rows that one fragment read touches sit
+//     in four different 64-byte bank groups;
+//   * the fragments come out with ds_read_b64_tr_b16: inside each 16-lane
+//     group, lane 4j + q fetches columns [c + 4q, c + 4q + 4) of k-row k0 + j
+//     and the instruction hands lane i the four k-rows k0 .. k0 + 3 of column
+//     c + i.  Two such reads (k0 and k0 + 4) give a lane the 8 consecutive k
+//     of one column that the 32 x 32 x 16 MFMA operand holds.
+// k-rows at or past K read as zero through the buffer range check, so K needs
+// no padding; M and N must be multiples of the block tile.
+// ---------------------------------------------------------------------------
+typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tr_v4i16 lds_v4i16;
+
+__device__ __forceinline__ tr_v4i16 lds_read_tr16(const unsigned char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(as_lds(const_cast<unsigned char *>(p))));
+}
+
+template <int BM, int BN, int STAGES>
+__device__ __forceinline__ void dma_gemm_tile_tn(const bf16 *__restrict__ A,
+                                                 const bf16 *__restrict__ Bm, int K, int lda,
+                                                 int ldb, int m0, int n0, int kbeg, int klen,
+                                                 unsigned char *smem,
+                                                 f32x16 (&acc)[BM / 64][BN / 64]) {
+  typedef Mfma32<bf16> MF;
+  typedef MF::frag Frag;
+  constexpr int BK = 32, KK = 2;
+  constexpr int ROWA = BM * 2, ROWB = BN * 2;          // bytes per k-row
+  constexpr int CPA = ROWA / 16, CPB = ROWB / 16;      // 16-byte chunks per k-row
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int ATILE = BK * ROWA, STAGE = BK * (ROWA + ROWB);
+  constexpr int A_INS = ATILE / 1024, B_INS = BK * ROWB / 1024;   // DMA instructions per stage
+  constexpr int PER_WAVE = (A_INS + B_INS) / 4;
+  static_assert(CPA >= 16 && CPB >= 16 && 1024 % ROWA == 0 && 1024 % ROWB == 0,
+                "the swizzle moves chunk bits 2..3 inside rows of 16 or more chunks");
+  static_assert(A_INS % 4 == 0 && B_INS % 4 == 0, "DMA split over 4 waves");
+  static_assert(STAGES >= 3 && (STAGES - 3) * PER_WAVE < 16, "vmcnt field");
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1;
+  const unsigned a_bytes = (unsigned)((size_t)K * lda * 2), b_bytes = (unsigned)((size_t)K * ldb * 2);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bm, 0, b_bytes, 0x00020000);
+
+  // DMA instruction u of wave w moves 1 KiB piece u*4 + w of a stage (A
+  // first).  Lane l writes LDS bytes [16 l, 16 l + 16) of the piece: k-row
+  // l / CP of it, physical chunk l % CP, which holds logical chunk
+  // (l % CP) ^ ((row & 3) << 2).  Per lane: the byte offset inside k-tile 0.
+  unsigned doff[PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    constexpr int AU = A_INS / 4;
+    const bool isA = u < AU;
+    const int cp = isA ? CPA : CPB;
+    const int row = ((isA ? u : u - AU) * 4 + wave) * (64 / cp) + lane / cp;
+    const int chunk = (lane % cp) ^ ((row & 3) << 2);
+    doff[u] = isA ? (unsigned)(((size_t)row * lda + m0 + chunk * 8) * 2)
+                  : (unsigned)(((size_t)row * ldb + n0 + chunk * 8) * 2);
+  }
+  auto issue = [&](int kt, int slot) {
+    unsigned char *base = smem + slot * STAGE + wave * 1024;
+    const int krow = kbeg + kt * BK;
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const bool isA = u < A_INS / 4;
+      unsigned char *dst = isA ? base + u * 4096 : base + ATILE + (u - A_INS / 4) * 4096;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(dst), 16, (int)doff[u],
+                                               krow * (isA ? lda : ldb) * 2, 0, 0);
+    }
+  };
+
+  // per-lane LDS byte offsets of the transpose reads for k-chunk 0, first
+  // half: lane 16g + 4j + q reads k-row 8 (g >> 1) + j at column
+  // 16 (g & 1) + 4q of its 32-column MFMA tile.  The other k-chunk and half
+  // are +16 and +4 rows, which leave the swizzle unchanged.
+  const int g = lane >> 4, jr = (lane >> 2) & 3, q = lane & 3;
+  const int krow0 = 8 * (g >> 1) + jr;
+  int aoff[TM], boff[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int col = wm * WM + i * 32 + 16 * (g & 1) + 4 * q;
+    aoff[i] = krow0 * ROWA + (((col >> 3) ^ ((krow0 & 3) << 2)) << 4) + (col & 7) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = wn * WN + j * 32 + 16 * (g & 1) + 4 * q;
+    boff[j] = ATILE + krow0 * ROWB + (((col >> 3) ^ ((krow0 & 3) << 2)) << 4) + (col & 7) * 2;
+  }
+  auto frag = [&](const unsigned char *p, int rowbytes, int kk) {
+    const tr_v4i16 lo = lds_read_tr16(p + kk * 16 * rowbytes);
+    const tr_v4i16 hi = lds_read_tr16(p + (kk * 16 + 4) * rowbytes);
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(Frag, v);
+  };
+  auto load = [&](int slot, Frag (&fa)[KK][TM], Frag (&fb)[KK][TN]) {
+    const unsigned char *sbase = smem + slot * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[kk][i] = frag(sbase + aoff[i], ROWA, kk);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[kk][j] = frag(sbase + boff[j], ROWB, kk);
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
+  auto mma = [&](Frag (&fa)[KK][TM], Frag (&fb)[KK][TN]) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[kk][i], fb[kk][j], acc[i][j]);
+  };
+  auto wait_stages = [&](int n) {
+    if constexpr (STAGES >= 5) {
+      if (n >= 2) { wait_vmcnt<2 * PER_WAVE>(); return; }
+    }
+    if constexpr (STAGES >= 4) {
+      if (n >= 1) { wait_vmcnt<PER_WAVE>(); return; }
+    }
+    wait_vmcnt<0>();
+  };
+
+  const int nk = (klen + BK - 1) / BK;
+  auto iter = [&](int kt, Frag (&ca)[KK][TM], Frag (&cb)[KK][TN], Frag (&na)[KK][TM],
+                  Frag (&nb)[KK][TN]) {
+    wait_stages(min(nk, kt + STAGES - 1) - (kt + 2));
+    lds_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    load((kt + 1) % STAGES, na, nb);
+    mma(ca, cb);
+  };
+
+#pragma unroll
+  for (int s0 = 0; s0 < STAGES - 1; ++s0)
+    if (s0 < nk) issue(s0, s0);
+  wait_stages(min(nk, STAGES - 1) - 1);
+  lds_barrier();
+  Frag fa0[KK][TM], fb0[KK][TN], fa1[KK][TM], fb1[KK][TN];
+  load(0, fa0, fb0);
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    iter(kt, fa0, fb0, fa1, fb1);
+    iter(kt + 1, fa1, fb1, fa0, fb0);
+  }
+  if (kt + 1 < nk) {
+    iter(kt, fa0, fb0, fa1, fb1);
+    mma(fa1, fb1);
+  } else {
+    mma(fa0, fb0);
+  }
+}
+
+// C (+ blockIdx.y * M * ldc with split slices) = A^T B over the k-rows
+// [blockIdx.y * kchunk, min(K, (blockIdx.y + 1) * kchunk)); fp32 out.
+template <int BM, int BN, int STAGES, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_tn_dma_kernel(const bf16 *__restrict__ A,
+                                                             const bf16 *__restrict__ Bm,
+                                                             float *__restrict__ C, int M, int N,
+                                                             int K, int lda, int ldb, int ldc,
+                                                             int kchunk) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * 32 * (BM + BN) * 2];
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int ntn = N / BN, ntm = M / BM;
+  const int lid = xcd_remap(blockIdx.x, ntn * ntm);
+  const int m0 = (lid / ntn) * BM, n0 = (lid % ntn) * BN;
+  const int kbeg = blockIdx.y * kchunk;
+  C += (size_t)blockIdx.y * M * ldc;
+  f32x16 acc[TM][TN];
+  dma_gemm_tile_tn<BM, BN, STAGES>(A, Bm, K, lda, ldb, m0, n0, kbeg, min(kchunk, K - kbeg), smem,
+                                   acc);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      float *cp = C + (size_t)(m0 + wm * WM + i * 32 + 4 * hl) * ldc + n0 + wn * WN + j * 32 + l32;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) cp[(size_t)(8 * (a >> 2) + (a & 3)) * ldc] = acc[i][j][a];
+    }
+}
+
 // out[i] = sum over the S slices of part[s][i], i < n (n a multiple of 4)
 template <typename Tout>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part,
@@ -347,6 +542,35 @@ hipError_t launch_gemm_nt_long_k(const Tin *A, const Tin *B, float *C, int M, in
     }
   }
   return launch_gemm_nt<Tin, float>(A, B, C, M, N, K, lda, ldb, N, stream);
+}
+
+hipError_t launch_gemm_tn_long_k(const bf16 *A, const bf16 *B, float *C, int M, int N, int K,
+                                 int lda, int ldb, float *ws, size_t ws_floats,
+                                 hipStream_t stream) {
+  constexpr int BM = 128, BN = 128;
+  const bool fits = M > 0 && N > 0 && K > 0 && M % BM == 0 && N % BN == 0 && lda % 8 == 0 &&
+                    ldb % 8 == 0 && lda >= M && ldb >= N &&
+                    reinterpret_cast<uintptr_t>(A) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(B) % 16 == 0 &&
+                    (size_t)(K + 64) * lda * 2 < (1ull << 31) &&
+                    (size_t)(K + 64) * ldb * 2 < (1ull << 31);
+  if (!fits) return hipErrorNotSupported;
+  const int S = gemm_long_k_slices(M, N, K);
+  int kchunk = ((K + S - 1) / S + 31) / 32 * 32;
+  int Sused = (K + kchunk - 1) / kchunk;
+  if (Sused > 1 && (!ws || (size_t)Sused * M * N > ws_floats)) {
+    Sused = 1;
+    kchunk = K;
+  }
+  const int grid = (M / BM) * (N / BN);
+  hipLaunchKernelGGL((gemm_tn_dma_kernel<BM, BN, 5, 2>), dim3(grid, Sused), dim3(256), 0, stream, A,
+                     B, Sused > 1 ? ws : C, M, N, K, lda, ldb, N, kchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || Sused == 1) return e;
+  const size_t n = (size_t)M * N;
+  hipLaunchKernelGGL((splitk_reduce_kernel<float>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256),
+                     0, stream, ws, C, n, Sused);
+  return hipGetLastError();
 }
 
 template hipError_t launch_gemm_nt<bf16, float>(const bf16 *, const bf16 *, float *, int, int, int,

@@ -89,6 +89,10 @@ def check_grads(got, ref, dtype, what):
 SMALL = {
     "bf16_g2_ragged": (CCAShape(batch=2, seq_len=300, d_model=256, n_q_heads=4, n_kv_heads=2,
                                 head_dim=64, rope_base=10000.0), None),
+    # weight gradients read token-major in place, the 2100 tokens split into
+    # two contraction slices, the second ending in a partial 32-row tile
+    "bf16_split_ragged": (CCAShape(batch=1, seq_len=2100, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                   head_dim=64, rope_base=10000.0), None),
     "bf16_g4_base5e5": (CCAShape(batch=1, seq_len=200, d_model=512, n_q_heads=8, n_kv_heads=2,
                                  head_dim=64, rope_base=500000.0), None),
     "bf16_d16": (CCAShape(batch=2, seq_len=130, d_model=128, n_q_heads=2, n_kv_heads=2,
