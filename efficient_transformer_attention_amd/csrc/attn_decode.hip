@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   // halves of one transposed read) on disjoint banks.
   constexpr int VROW = D * 2 + 16;
   constexpr int VTILE = DEC_TILE * VROW;
-  constexpr int VBYTES = 4 * TPI * VTILE;
+  constexpr int VBYTES = 2 * 4 * TPI * VTILE;      // V tiles, then K tiles (same row stride)
   constexpr int RBYTES = 4 * MAXG * (D + 2) * 4;
   // the per-wave V tiles and, after the key loop, the wave-merge buffer
   __shared__ __attribute__((aligned(16))) unsigned char smem[VBYTES > RBYTES ? VBYTES : RBYTES];
@@ -163,6 +163,11 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   const bf16 *kb = kc + (size_t)(b * Hkv + g) * cm.capacity * D;
   const bf16 *vb = vc + (size_t)(b * Hkv + g) * cm.capacity * D;
   unsigned char *myv = smem + wave * TPI * VTILE;
+  unsigned char *myk = smem + (4 + wave) * TPI * VTILE;
+  // transpose-read address of this lane inside a V tile (d a multiple of 32):
+  // lane 16 gq + 4 j + q fetches key row 4 (gq >> 1) + j, columns
+  // 16 (gq & 1) + 4 q .. + 3
+  const int vtr_off = (4 * (lane >> 5) + ((lane >> 2) & 3)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   // paged: the pages of this chunk's rows, staged once in LDS (a chunk is at
   // most DEC_MAX_PAGES pages), so a row's page is an LDS read
   __shared__ int spages[PAGED ? DEC_MAX_PAGES : 1];
@@ -194,14 +199,21 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   // to its last key (finite data, masked below)
   constexpr int VPL = (DEC_TILE * D / 8 + 63) / 64;   // 16-byte V pieces per lane per tile
   u32x4 kreg[TPI][QC], vreg[TPI][VPL];
+  static_assert(VPL == QC, "K and V tiles load as the same 16-byte pieces");
+  // K and V rows load whole (D / 8 consecutive lanes per row, so every load
+  // instruction reads whole 128-byte lines), marked non-temporal
   auto gload_k = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < TPI; ++u) {
       const int k0 = kbeg + (t0 + u) * DEC_TILE;
-      const int krow = min(k0 + l32, kend - 1);
-      const bf16 *kp = krow_ptr(kb, kc, krow);
 #pragma unroll
-      for (int cc = 0; cc < QC; ++cc) kreg[u][cc] = ld16(kp + 16 * cc + 8 * hl);
+      for (int r = 0; r < VPL; ++r) {
+        const int e = lane + 64 * r;
+        if (e < DEC_TILE * D / 8) {
+          const int row = e / (D / 8), seg = e % (D / 8);
+          kreg[u][r] = ld16_nt(krow_ptr(kb, kc, min(k0 + row, kend - 1)) + 8 * seg);
+        }
+      }
     }
   };
   auto gload_v = [&](int t0) {
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
         const int e = lane + 64 * r;
         if (e < DEC_TILE * D / 8) {
           const int row = e / (D / 8), seg = e % (D / 8);
-          vreg[u][r] = ld16(krow_ptr(vb, vc, min(k0 + row, kend - 1)) + 8 * seg);
+          vreg[u][r] = ld16_nt(krow_ptr(vb, vc, min(k0 + row, kend - 1)) + 8 * seg);
         }
       }
     }
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   int t = wave * TPI;
   if (t < ntile) gload(t);
   for (; t < ntile; t += step) {
-    // stage V (wave-private), then S^T = K Q^T for the TPI tiles
+    // stage K and V (wave-private), then S^T = K Q^T for the TPI tiles
 #pragma unroll
     for (int u = 0; u < TPI; ++u)
 #pragma unroll
@@ -232,25 +244,27 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
         const int e = lane + 64 * r;
         if (e < DEC_TILE * D / 8) {
           const int row = e / (D / 8), seg = e % (D / 8);
-          unsigned char *dst = myv + u * VTILE + row * VROW + seg * 16;
-          *reinterpret_cast<u32x2 *>(dst) = u32x2{vreg[u][r][0], vreg[u][r][1]};
-          *reinterpret_cast<u32x2 *>(dst + 8) = u32x2{vreg[u][r][2], vreg[u][r][3]};
+          unsigned char *dv = myv + u * VTILE + row * VROW + seg * 16;
+          *reinterpret_cast<u32x2 *>(dv) = u32x2{vreg[u][r][0], vreg[u][r][1]};
+          *reinterpret_cast<u32x2 *>(dv + 8) = u32x2{vreg[u][r][2], vreg[u][r][3]};
+          unsigned char *dk = myk + u * VTILE + row * VROW + seg * 16;
+          *reinterpret_cast<u32x2 *>(dk) = u32x2{kreg[u][r][0], kreg[u][r][1]};
+          *reinterpret_cast<u32x2 *>(dk + 8) = u32x2{kreg[u][r][2], kreg[u][r][3]};
         }
       }
     __builtin_amdgcn_wave_barrier();
-    if (t + step < ntile) gload_v(t + step);   // V registers are free once staged
+    if (t + step < ntile) gload(t + step);     // K / V registers are free once staged
     f32x16 s[TPI];
 #pragma unroll
     for (int u = 0; u < TPI; ++u) {
       s[u] = zero16();
 #pragma unroll
       for (int cc = 0; cc < QC; ++cc) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&kreg[u][cc]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(myk + u * VTILE + l32 * VROW + 32 * cc + 16 * hl);
         s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qhi[cc], s[u], 0, 0, 0);
         s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qlo[cc], s[u], 0, 0, 0);
       }
     }
-    if (t + step < ntile) gload_k(t + step);   // K registers are free after the QK MFMAs
     // mask keys past the chunk end, online softmax per column over TPI*32 keys
     float mx = -INFINITY;
 #pragma unroll
@@ -297,13 +311,19 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
         for (int sl = 0; sl < 8; ++sl) pf[sl] = (bf16)s[u][8 * cc2 + sl];
 #pragma unroll
         for (int i = 0; i < ND; ++i) {
-          const int dd = 32 * i + l32;
           bf16x8 vf;
+          if constexpr (D % 32 == 0) {
+            // two transpose reads: keys 16 cc2 + 4 hl + 0..3 and + 8..11 of column 32 i + l32
+            const unsigned char *p0 = myv + u * VTILE + 16 * cc2 * VROW + 64 * i + vtr_off;
+            vf = tr_frag<bf16x8>(p0, p0 + 8 * VROW);
+          } else {
+            const int dd = 32 * i + l32;
 #pragma unroll
-          for (int sl = 0; sl < 8; ++sl) {
-            const int key = 16 * cc2 + 8 * (sl >> 2) + 4 * hl + (sl & 3);
-            vf[sl] = dd < D ? *reinterpret_cast<const bf16 *>(myv + u * VTILE + key * VROW + dd * 2)
-                            : (bf16)0.f;
+            for (int sl = 0; sl < 8; ++sl) {
+              const int key = 16 * cc2 + 8 * (sl >> 2) + 4 * hl + (sl & 3);
+              vf[sl] = dd < D ? *reinterpret_cast<const bf16 *>(myv + u * VTILE + key * VROW + dd * 2)
+                              : (bf16)0.f;
+            }
           }
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[i], 0, 0, 0);
         }

@@ -93,6 +93,31 @@ __device__ __forceinline__ f32x16 zero16() {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Inside each group of 16
+// lanes, lane 4j + q gives the address of 4 consecutive 16-bit elements,
+// which a caller points at row j, columns 4q .. 4q + 3 of a 4 x 16 block;
+// lane i then receives column i of rows 0 .. 3 (element i % 4 of the fetches
+// of lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4).
+typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tr_v4i16 lds_v4i16;
+__device__ __forceinline__ tr_v4i16 lds_read_tr16(const unsigned char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16 *)((__attribute__((address_space(3))) void *)(const_cast<unsigned char *>(p))));
+}
+// an 8-element 16-bit MFMA operand from two transpose reads: slots 0..3 from
+// rows k0 .. k0 + 3 (address lo), slots 4..7 from the rows at address hi
+template <typename Frag>
+__device__ __forceinline__ Frag tr_frag(const unsigned char *lo, const unsigned char *hi) {
+  const tr_v4i16 a = lds_read_tr16(lo), b = lds_read_tr16(hi);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(Frag, v);
+}
+
+// 16-byte load marked non-temporal (streamed data read once: the KV cache)
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
 __device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
 

@@ -239,13 +239,6 @@ __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__res
 // k-rows at or past K read as zero through the buffer range check, so K needs
 // no padding; M and N must be multiples of the block tile.
 // ---------------------------------------------------------------------------
-typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) tr_v4i16 lds_v4i16;
-
-__device__ __forceinline__ tr_v4i16 lds_read_tr16(const unsigned char *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(as_lds(const_cast<unsigned char *>(p))));
-}
-
 template <int BM, int BN, int STAGES>
 __device__ __forceinline__ void dma_gemm_tile_tn(const bf16 *__restrict__ A,
                                                  const bf16 *__restrict__ Bm, int K, int lda,
@@ -316,11 +309,7 @@ __device__ __forceinline__ void dma_gemm_tile_tn(const bf16 *__restrict__ A,
     boff[j] = ATILE + krow0 * ROWB + (((col >> 3) ^ ((krow0 & 3) << 2)) << 4) + (col & 7) * 2;
   }
   auto frag = [&](const unsigned char *p, int rowbytes, int kk) {
-    const tr_v4i16 lo = lds_read_tr16(p + kk * 16 * rowbytes);
-    const tr_v4i16 hi = lds_read_tr16(p + (kk * 16 + 4) * rowbytes);
-    typedef short v8i16 __attribute__((ext_vector_type(8)));
-    const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(Frag, v);
+    return tr_frag<Frag>(p + kk * 16 * rowbytes, p + (kk * 16 + 4) * rowbytes);
   };
   auto load = [&](int slot, Frag (&fa)[KK][TM], Frag (&fb)[KK][TN]) {
     const unsigned char *sbase = smem + slot * STAGE;
