@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
     __syncthreads();
   }
   // element offset of a cache row: contiguous from this (b, g) base, or paged
-  auto krow_ptr = [&](const bf16 *base_c, const bf16 *pool, int row) {
+  auto krow_ptr = [&](const bf16 *base_c, const bf16 *pool, int row) __attribute__((always_inline)) {
     if constexpr (PAGED) {
       const int pi = row / cm.page;
       return pool + (((size_t)spages[pi - pb0] * Hkv + g) * cm.page + (row - pi * cm.page)) * D;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
   static_assert(VPL == QC, "K and V tiles load as the same 16-byte pieces");
   // K and V rows load whole (D / 8 consecutive lanes per row, so every load
   // instruction reads whole 128-byte lines), marked non-temporal
-  auto gload_k = [&](int t0) {
+  auto gload_k = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < TPI; ++u) {
       const int k0 = kbeg + (t0 + u) * DEC_TILE;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
       }
     }
   };
-  auto gload_v = [&](int t0) {
+  auto gload_v = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < TPI; ++u) {
       const int k0 = kbeg + (t0 + u) * DEC_TILE;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(const float *__re
       }
     }
   };
-  auto gload = [&](int t0) { gload_k(t0); gload_v(t0); };
+  auto gload = [&](int t0) __attribute__((always_inline)) { gload_k(t0); gload_v(t0); };
 
   const int step = 4 * TPI;
   int t = wave * TPI;
