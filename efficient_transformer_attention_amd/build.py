@@ -11,6 +11,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import os
 import shutil
+import re
 import subprocess
 import sys
 
@@ -39,12 +40,43 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libcca)")
 
 
+# Known scratch users, with the reason they are accepted.
+SCRATCH_OK = {
+    # head size 128 in the two-workgroups-per-CU register budget: 26 spilled
+    # registers outside the key loop's MFMA chains (no benchmark shape uses it)
+    ("attn_fwd_kernel", "Li128E"),
+}
+
+
+def _scratch_users(remarks: str) -> list:
+    """Kernels whose resource-usage remarks show a scratch (stack) frame or
+    spilled vector registers: per-lane memory traffic inside a hot loop, which
+    has come from a lambda the compiler declined to inline.  (Scalar spills
+    land in vector-register lanes and are left alone.)"""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)", line)
+        if m and int(m.group(2)) > 0 and name and not name.startswith("__") and \
+                not any(all(part in name for part in ok) for ok in SCRATCH_OK):
+            bad.append(f"{name}: {m.group(1)} {m.group(2)}")
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
+    if src.endswith(".hip"):
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    bad = _scratch_users(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels using scratch memory:\n  " + "\n  ".join(bad[:8]))
     return obj
 
 
