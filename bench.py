@@ -300,9 +300,10 @@ def training_step(cca, T, sp, pcfg, pw, x, dev, K):
 
 
 def compare(args):
-    """The pages' prefill comparison reproduced with this library's kernels:
-    CCGQA (ccgqa_prefill_t16384) against full-width MHA and GQA-8 at the same
-    T, E and head size with the extras off, then a sweep over T.  Context for
+    """The pages' prefill and backward comparisons reproduced with this
+    library's kernels: CCGQA (ccgqa_prefill_t16384) against full-width MHA and
+    GQA-8 at the same T, E and head size with the extras off (forward, then a
+    training step: forward_train + backward), then a prefill sweep over T.  Context for
     the pages' own ratios, which they measure on other hardware."""
     import math
     import numpy as np
@@ -315,7 +316,7 @@ def compare(args):
     torch.cuda.set_device(0)
     K = max(2, min(args.steps, 5))
 
-    def run(name, sp):
+    def run(name, sp, train=False):
         P = make_prefill(sp, seed=0)
         W = P.weights
         if name in COMPARISONS:
@@ -348,15 +349,22 @@ def compare(args):
              "attention_ms": round(att, 4), "attention_tflops": round(flops / (att * 1e-3) / 1e12, 1)}
         print(f"[compare] {name} T={sp.seq_len}: prefill {pre:.3f} ms, attention {att:.3f} ms",
               file=sys.stderr, flush=True)
-        del x, y, ws, pw
+        del ws
+        if train:
+            # forward_train + backward on the same shape (the pages' backward comparison)
+            r["train"] = training_step(cca, T, sp, cfg, pw, x, dev, K)
+            r["train"]["workload"] = "forward_train + backward on this shape, seeded dy ~ N(0,1)"
+        del x, y, pw
         torch.cuda.empty_cache()
         return r
 
     main3 = ["ccgqa_prefill_t16384", "gqa8_prefill_t16384", "mha_prefill_t16384"]
-    res = {n: run(n, workload(n)) for n in main3}
+    res = {n: run(n, workload(n), train=True) for n in main3}
     base = res["ccgqa_prefill_t16384"]
     ratios = {f"{n}_over_ccgqa": {"prefill": round(res[n]["prefill_ms"] / base["prefill_ms"], 3),
-                                  "attention": round(res[n]["attention_ms"] / base["attention_ms"], 3)}
+                                  "attention": round(res[n]["attention_ms"] / base["attention_ms"], 3),
+                                  "backward": round(res[n]["train"]["backward_ms"]
+                                                    / base["train"]["backward_ms"], 3)}
               for n in main3[1:]}
     sweep = []
     for n in ("ccgqa_prefill_t16384", "mha_prefill_t16384"):
