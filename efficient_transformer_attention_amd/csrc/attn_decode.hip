@@ -32,10 +32,10 @@ namespace cca {
 static constexpr int DEC_CHUNK = 4096;   // keys per workgroup
 static constexpr int DEC_TILE = 32;      // keys per MFMA tile
 static constexpr int DEC_F32_MAXG = 8;   // query heads per workgroup, fp32 path
-// Pages one chunk of keys can span: chunks hold at most 2 * DEC_CHUNK + 64
-// keys (dec_num_chunks starts at Lk / (2 * DEC_CHUNK)) and pages are at least
+// Pages one chunk of keys can span: chunks hold at most 4 * DEC_CHUNK + 63
+// keys (dec_num_chunks starts at Lk / (4 * DEC_CHUNK)) and pages are at least
 // 32 rows.
-static constexpr int DEC_MAX_PAGES = (2 * 4096 + 64) / 32 + 2;
+static constexpr int DEC_MAX_PAGES = (4 * DEC_CHUNK + 64) / 32 + 2;
 
 // Query heads per workgroup of the MFMA path (the N columns of a 32x32 tile);
 // capped lower at d = 128 so the merge buffer stays within 64 KiB of LDS.
