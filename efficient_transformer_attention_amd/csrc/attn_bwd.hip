@@ -58,20 +58,27 @@ template <> struct TrBits<bf16> { using U = unsigned short; };
 template <> struct TrBits<f16> { using U = unsigned short; };
 template <> struct TrBits<float> { using U = unsigned int; };
 
+// One transpose of the vector form: sizes, strides and tile counts.
+struct TrJob {
+  const void *in;
+  void *out;
+  int R, Rvalid, C;
+  long long in_rs, in_bs1, in_bs2, out_rs, out_bs1, out_bs2;
+  int nz2, ncx, nry, perm_r, perm_c;
+};
+
+// The wave's part of one 64 x 64 (16-bit) or 32 x 32 (32-bit) tile of job t.
 template <typename Tin, typename Tout>
-__global__ __launch_bounds__(256) void transpose_vec_kernel(const Tin *__restrict__ in,
-                                                            Tout *__restrict__ out, int R,
-                                                            int Rvalid, int C, long long in_rs,
-                                                            long long in_bs1, long long in_bs2,
-                                                            long long out_rs, long long out_bs1,
-                                                            long long out_bs2, int nz2, int ncx,
-                                                            int nry, int ntiles, int perm_r,
-                                                            int perm_c) {
+__device__ __forceinline__ void transpose_vec_tile(const TrJob &t, int tile) {
   static_assert(sizeof(Tin) == sizeof(Tout), "same element size on both sides");
   constexpr int VEC = 16 / (int)sizeof(Tout);   // elements per 16 bytes
   constexpr int TS = 8 * VEC;                   // tile side
-  const int tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (tile >= ntiles) return;
+  const Tin *__restrict__ in = static_cast<const Tin *>(t.in);
+  Tout *__restrict__ out = static_cast<Tout *>(t.out);
+  const int R = t.R, Rvalid = t.Rvalid, C = t.C, nz2 = t.nz2, ncx = t.ncx, nry = t.nry;
+  const int perm_r = t.perm_r, perm_c = t.perm_c;
+  const long long in_rs = t.in_rs, in_bs1 = t.in_bs1, in_bs2 = t.in_bs2;
+  const long long out_rs = t.out_rs, out_bs1 = t.out_bs1, out_bs2 = t.out_bs2;
   const int lane = threadIdx.x & 63, rb = lane & 7, cc = lane >> 3;
   const int cx = tile % ncx, rest = tile / ncx, ry = rest % nry, z = rest / nry;
   const int z1 = z / nz2, z2 = z % nz2;
@@ -115,6 +122,30 @@ __global__ __launch_bounds__(256) void transpose_vec_kernel(const Tin *__restric
   }
 }
 
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void transpose_vec_kernel(TrJob t, int ntiles) {
+  const int tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (tile < ntiles) transpose_vec_tile<Tin, Tout>(t, tile);
+}
+
+// Several transposes in one launch: job k owns tiles [first[k], first[k+1]);
+// jobs with conv set read TQ and write TV, the others read and write TV.
+struct TrJobs {
+  TrJob j[4];
+  int conv[4];
+  int first[5];
+  int n;
+};
+template <typename TQ, typename TV>
+__global__ __launch_bounds__(256) void transpose_multi_kernel(TrJobs jobs) {
+  const int tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (tile >= jobs.first[jobs.n]) return;
+  int k = 0;
+  while (k + 1 < jobs.n && tile >= jobs.first[k + 1]) ++k;
+  if (jobs.conv[k]) transpose_vec_tile<TQ, TV>(jobs.j[k], tile - jobs.first[k]);
+  else transpose_vec_tile<TV, TV>(jobs.j[k], tile - jobs.first[k]);
+}
+
 // element-wise form for unaligned sizes or strides: 64 x 64 tiles through LDS
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void transpose_kernel(const Tin *__restrict__ in,
@@ -143,29 +174,45 @@ __global__ __launch_bounds__(256) void transpose_kernel(const Tin *__restrict__ 
   }
 }
 
+// The vector form's job for a transpose, or false when sizes, strides or
+// alignment need the element-wise form (the permutations act inside aligned
+// groups of 16, which the tiles keep whole).
+template <typename Tin, typename Tout>
+static bool transpose_job(const Tin *in, Tout *out, int R, int Rvalid, int C, long long in_rs,
+                          long long in_bs1, long long in_bs2, long long out_rs, long long out_bs1,
+                          long long out_bs2, int nz1, int nz2, int perm_r, int perm_c, TrJob &j,
+                          long long &ntiles) {
+  constexpr int VEC = 16 / (int)sizeof(Tout);
+  const bool vec = (reinterpret_cast<uintptr_t>(in) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(out) % 16 == 0) && R % VEC == 0 && C % VEC == 0 &&
+                   in_rs % VEC == 0 && in_bs1 % VEC == 0 && in_bs2 % VEC == 0 &&
+                   out_rs % VEC == 0 && out_bs1 % VEC == 0 && out_bs2 % VEC == 0 &&
+                   (!perm_r || R % 16 == 0) && (!perm_c || C % 16 == 0);
+  if (!vec) return false;
+  constexpr int TS = 8 * VEC;
+  j = TrJob{in, out, R, Rvalid, C, in_rs, in_bs1, in_bs2, out_rs, out_bs1, out_bs2, nz2,
+            (C + TS - 1) / TS, (R + TS - 1) / TS, perm_r, perm_c};
+  ntiles = (long long)j.ncx * j.nry * nz1 * nz2;
+  return true;
+}
+
+// one wave per workgroup for small transposes, so they still reach every CU
+static int transpose_waves_per_wg(long long ntiles) { return ntiles >= 4096 ? 4 : 1; }
+
 template <typename Tin, typename Tout>
 hipError_t launch_transpose(const Tin *in, Tout *out, int R, int Rvalid, int C, long long in_rs,
                             long long in_bs1, long long in_bs2, long long out_rs,
                             long long out_bs1, long long out_bs2, int nz1, int nz2, int perm_r,
                             int perm_c, hipStream_t stream) {
   if (R <= 0 || C <= 0 || nz1 * nz2 <= 0) return hipSuccess;
-  constexpr int VEC = 16 / (int)sizeof(Tout);
-  // the permutations act inside aligned groups of 16, which the tiles keep whole
-  const bool vec = (reinterpret_cast<uintptr_t>(in) % 16 == 0) &&
-                   (reinterpret_cast<uintptr_t>(out) % 16 == 0) && R % VEC == 0 && C % VEC == 0 &&
-                   in_rs % VEC == 0 && in_bs1 % VEC == 0 && in_bs2 % VEC == 0 &&
-                   out_rs % VEC == 0 && out_bs1 % VEC == 0 && out_bs2 % VEC == 0 &&
-                   (!perm_r || R % 16 == 0) && (!perm_c || C % 16 == 0);
-  if (vec) {
-    constexpr int TS = 8 * VEC;
-    const int ncx = (C + TS - 1) / TS, nry = (R + TS - 1) / TS;
-    const long long nt = (long long)ncx * nry * nz1 * nz2;
+  TrJob j;
+  long long nt;
+  if (transpose_job(in, out, R, Rvalid, C, in_rs, in_bs1, in_bs2, out_rs, out_bs1, out_bs2, nz1,
+                    nz2, perm_r, perm_c, j, nt)) {
     if (nt > (1ll << 31) - 4) return hipErrorInvalidValue;
-    // one wave per workgroup for small transposes, so they still reach every CU
-    const int wpg = nt >= 4096 ? 4 : 1;
+    const int wpg = transpose_waves_per_wg(nt);
     hipLaunchKernelGGL((transpose_vec_kernel<Tin, Tout>), dim3((unsigned)((nt + wpg - 1) / wpg)),
-                       dim3(64 * wpg), 0, stream, in, out, R, Rvalid, C, in_rs, in_bs1, in_bs2, out_rs, out_bs1,
-                       out_bs2, nz2, ncx, nry, (int)nt, perm_r, perm_c);
+                       dim3(64 * wpg), 0, stream, j, (int)nt);
     return hipGetLastError();
   }
   dim3 grid((C + 63) / 64, (R + 63) / 64, nz1 * nz2);
@@ -983,22 +1030,54 @@ static hipError_t attn_bwd_d(const MixShape &s, const AttnBwdArgs<TQ, TV> &a, hi
   hipError_t e;
   // transposed, token-permuted copies: q^T and dO^T per query head, k^T per kv
   // head; v back to row-major
-  e = launch_transpose<TQ, TV>(a.q, a.qT, s.Tp, s.Tp, D, D, (long long)s.Hq * s.Tp * D,
-                               (long long)s.Tp * D, s.Tp, (long long)s.Hq * D * s.Tp,
-                               (long long)D * s.Tp, s.B, s.Hq, 1, 0, stream);
-  if (e != hipSuccess) return e;
-  e = launch_transpose<TQ, TV>(a.k, a.kT, s.Tp, s.Tp, D, D, (long long)s.Hkv * s.Tp * D,
-                               (long long)s.Tp * D, s.Tp, (long long)s.Hkv * D * s.Tp,
-                               (long long)D * s.Tp, s.B, s.Hkv, 1, 0, stream);
-  if (e != hipSuccess) return e;
-  e = launch_transpose<TV, TV>(a.dO, a.dOT, s.Tp, s.T, D, eq, (long long)s.T * eq, D, s.Tp,
-                               (long long)s.Hq * D * s.Tp, (long long)D * s.Tp, s.B, s.Hq, 1, 0,
-                               stream);
-  if (e != hipSuccess) return e;
-  e = launch_transpose<TV, TV>(a.vt, a.vr, D, D, s.Tp, s.Tp, (long long)s.Hkv * D * s.Tp,
-                               (long long)D * s.Tp, D, (long long)s.Hkv * s.Tp * D,
-                               (long long)s.Tp * D, s.B, s.Hkv, 0, 1, stream);
-  if (e != hipSuccess) return e;
+  {
+    // the four as one launch when all take the vector form (their waits overlap)
+    TrJobs jobs{};
+    long long nt[4];
+    bool all = transpose_job<TQ, TV>(a.q, a.qT, s.Tp, s.Tp, D, D, (long long)s.Hq * s.Tp * D,
+                                     (long long)s.Tp * D, s.Tp, (long long)s.Hq * D * s.Tp,
+                                     (long long)D * s.Tp, s.B, s.Hq, 1, 0, jobs.j[0], nt[0]);
+    all = all && transpose_job<TQ, TV>(a.k, a.kT, s.Tp, s.Tp, D, D, (long long)s.Hkv * s.Tp * D,
+                                       (long long)s.Tp * D, s.Tp, (long long)s.Hkv * D * s.Tp,
+                                       (long long)D * s.Tp, s.B, s.Hkv, 1, 0, jobs.j[1], nt[1]);
+    all = all && transpose_job<TV, TV>(a.dO, a.dOT, s.Tp, s.T, D, eq, (long long)s.T * eq, D, s.Tp,
+                                       (long long)s.Hq * D * s.Tp, (long long)D * s.Tp, s.B, s.Hq,
+                                       1, 0, jobs.j[2], nt[2]);
+    all = all && transpose_job<TV, TV>(a.vt, a.vr, D, D, s.Tp, s.Tp, (long long)s.Hkv * D * s.Tp,
+                                       (long long)D * s.Tp, D, (long long)s.Hkv * s.Tp * D,
+                                       (long long)s.Tp * D, s.B, s.Hkv, 0, 1, jobs.j[3], nt[3]);
+    const long long total = all ? nt[0] + nt[1] + nt[2] + nt[3] : 0;
+    if (all && total > 0 && total <= (1ll << 31) - 4) {
+      jobs.n = 4;
+      jobs.first[0] = 0;
+      for (int k = 0; k < 4; ++k) {
+        jobs.conv[k] = k < 2 && !std::is_same<TQ, TV>::value;
+        jobs.first[k + 1] = jobs.first[k] + (int)nt[k];
+      }
+      const int wpg = transpose_waves_per_wg(total);
+      hipLaunchKernelGGL((transpose_multi_kernel<TQ, TV>), dim3((unsigned)((total + wpg - 1) / wpg)),
+                         dim3(64 * wpg), 0, stream, jobs);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else {
+      e = launch_transpose<TQ, TV>(a.q, a.qT, s.Tp, s.Tp, D, D, (long long)s.Hq * s.Tp * D,
+                                   (long long)s.Tp * D, s.Tp, (long long)s.Hq * D * s.Tp,
+                                   (long long)D * s.Tp, s.B, s.Hq, 1, 0, stream);
+      if (e != hipSuccess) return e;
+      e = launch_transpose<TQ, TV>(a.k, a.kT, s.Tp, s.Tp, D, D, (long long)s.Hkv * s.Tp * D,
+                                   (long long)s.Tp * D, s.Tp, (long long)s.Hkv * D * s.Tp,
+                                   (long long)D * s.Tp, s.B, s.Hkv, 1, 0, stream);
+      if (e != hipSuccess) return e;
+      e = launch_transpose<TV, TV>(a.dO, a.dOT, s.Tp, s.T, D, eq, (long long)s.T * eq, D, s.Tp,
+                                   (long long)s.Hq * D * s.Tp, (long long)D * s.Tp, s.B, s.Hq, 1, 0,
+                                   stream);
+      if (e != hipSuccess) return e;
+      e = launch_transpose<TV, TV>(a.vt, a.vr, D, D, s.Tp, s.Tp, (long long)s.Hkv * D * s.Tp,
+                                   (long long)D * s.Tp, D, (long long)s.Hkv * s.Tp * D,
+                                   (long long)s.Tp * D, s.B, s.Hkv, 0, 1, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
   constexpr int LPR = D * (int)sizeof(TV) / 16;
   const long long nthr = (long long)s.B * s.Hq * s.Tp * LPR;
   hipLaunchKernelGGL((attn_bwd_rowdot_kernel<TV, D>), dim3((unsigned)((nthr + 255) / 256)),
