@@ -20,11 +20,13 @@ def _matvec(w, x):
     return [sum(w[r][c] * x[c] for c in range(len(x))) for r in range(len(w))]
 
 
-def brute_prefill(x, w, cfg, chan_conv="per_head"):
+def brute_prefill(x, w, cfg, chan_conv="per_head", qk_mean="M2"):
     """x: nested lists [B][T][E] (floats); w: dict of nested lists.
     ``chan_conv="grouped"`` takes the dense lag-by-channel reading of the
     channel convolution (weights ``q_chan_dense`` / ``k_chan_dense``
-    [H][d_out][k_c][d_in]).
+    [H][d_out][k_c][d_in]).  ``qk_mean``: "M2" adds the average of the four
+    values q~, k~ (before the convolutions) and bq, bk (after them) to each
+    convolved value; "M1" the average of q~ and k~ only.
 
     Returns y as nested lists [B][T][E]."""
     Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -94,13 +96,23 @@ def brute_prefill(x, w, cfg, chan_conv="per_head"):
                 for h in range(Hq):
                     g = h // G
                     for i in range(d):
-                        q[t][h * d + i] = bq[t][h * d + i] + 0.5 * (qt[t][h * d + i] + kt[t][g * d + i])
+                        qc, kc_ = h * d + i, g * d + i
+                        if qk_mean == "M2":
+                            mean = (qt[t][qc] + kt[t][kc_] + bq[t][qc] + bk[t][kc_]) / 4.0
+                        else:
+                            mean = (qt[t][qc] + kt[t][kc_]) / 2.0
+                        q[t][qc] = bq[t][qc] + mean
                 for g in range(Hkv):
                     for i in range(d):
-                        s = 0.0
-                        for m in range(G):
-                            s += qt[t][(g * G + m) * d + i]
-                        k[t][g * d + i] = bk[t][g * d + i] + 0.5 * (kt[t][g * d + i] + s / G)
+                        # the group's query heads enter through their average
+                        pre_q = sum(qt[t][(g * G + m) * d + i] for m in range(G)) / G
+                        post_q = sum(bq[t][(g * G + m) * d + i] for m in range(G)) / G
+                        kc_ = g * d + i
+                        if qk_mean == "M2":
+                            mean = (pre_q + kt[t][kc_] + post_q + bk[t][kc_]) / 4.0
+                        else:
+                            mean = (pre_q + kt[t][kc_]) / 2.0
+                        k[t][kc_] = bk[t][kc_] + mean
 
         v = [[0.0] * ekv for _ in range(T)]
         for t in range(T):

@@ -9,14 +9,19 @@ Plain NumPy in float64, in the order the pages describe the method:
 Inputs are the exact values the GPU receives (bf16 or fp32 upcast to fp64), so
 the only differences to the GPU are its roundings and summation order.
 
+This module is test infrastructure: only the tests, the smoke check and the
+benchmark's CPU baseline import it; the library never does.
+
 Array conventions: tokens are ``[B, T, ...]``; latent heads are ``[..., H, d]``
 with flat channel index ``h * d + i``; weights are ``[out, in]``.
 
 Parity status of each step (see the tests under ``tests/test_oracle_*.py``):
 pinned by closed forms, brute force, the MHA reduction and invariants; the
-readings of the channel convolution, the q-k-mean formula, tau, the RoPE pair
-convention and the shifted half are parity unpinned against the original
-paper (the pages fix none of them).
+readings of the channel convolution, tau, the RoPE pair convention and the
+shifted half are parity unpinned against the original paper (the pages fix
+none of them); the q-k-mean follows the pages' wording (the mean of the pre-
+and post-convolution q and k) and is pinned by the brute-force twin and
+closed forms of that reading, not by a number from the paper.
 """
 
 from __future__ import annotations
@@ -31,8 +36,9 @@ import numpy as np
 class Readings:
     """Switches for the steps the pages leave open.
 
-    qk_mean:       "M1" (default) mean of the pre-conv q and k added to the
-                   convolved q and k; "M2" quarter of pre- plus post-conv q, k.
+    qk_mean:       "M2" (default) the mean of the pre- and post-convolution q
+                   and k, a quarter of their sum, added to the convolved q and
+                   k; "M1" the mean of the pre-convolution q and k only.
     rope_pairing:  "interleaved" (default, pairs (2i, 2i+1)) or "half"
                    (pairs (i, i + d/2)).
     shift_half:    "upper" (default: kv heads H_kv/2 .. H_kv-1 take token t-1)
@@ -44,7 +50,7 @@ class Readings:
                    "grouped" the carried decode window holds the last
                    (k_s - 1) + (k_c - 1) pre-conv rows.
     """
-    qk_mean: str = "M1"
+    qk_mean: str = "M2"
     rope_pairing: str = "interleaved"
     shift_half: str = "upper"
     chan_conv: str = "per_head"
@@ -143,10 +149,16 @@ def conv_window_rows(cfg, readings: "Readings" = None) -> int:
 # ---------------------------------------------------------------------------
 # a4  q-k-mean  [GS-EN "2. Methodology" / Q-K-Mean; EDG "How Compressed
 #     Convolutional Attention Works"; GS-DE "2. Methodik" / Q-K-Mean]
-# Reading M1 (parity unpinned): the mean of the pre-convolution q and k is a
-# skip path added to both convolved tensors, so q_t and k_t share a term.
-# With G query heads per kv head (CCGQA) q head h meets the k of its group
-# g(h) = floor(h / G), and kv head g meets the average of its group's q heads.
+# All three pages describe one operation: the mean of the query and key
+# values taken before and after the convolutions is added back to the
+# convolved tensors, a skip path that lets q and k share information.
+# Reading M2 (the default; parity unpinned against the paper itself): the
+# mean of the four tensors q~, k~ (pre-conv) and b_q, b_k (post-conv),
+#   m = (q~ + k~ + b_q + b_k) / 4,   q = b_q + m,   k = b_k + m.
+# With G query heads per kv head (CCGQA) q head h meets the k~ and b_k of its
+# group g(h) = floor(h / G), and kv head g meets the averages of q~ and b_q
+# over its G query heads.  Reading M1 (a switch) keeps only the pre-conv
+# terms: q = b_q + (q~ + k~) / 2, k = b_k + (k~ + q~) / 2.
 # ---------------------------------------------------------------------------
 
 def qk_mean(bq, bk, q_pre, k_pre, group: int, readings: Readings = DEFAULT_READINGS):

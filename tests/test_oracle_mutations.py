@@ -1,10 +1,13 @@
 """Planted mistakes in the oracle must fail at least one pin (CPU only).
 
 Each mutant replaces one step of ``oracle.cca`` with a plausible mistake (a
-wrong sign, index, direction, dropped term or swapped operand).  The test
-runs the independent pins -- the scalar brute force, the textbook MHA
-reduction and the single-token closed form -- and requires that one of them
-notices.  The mistakes live only in this test, on the CPU.
+wrong sign, index, direction, dropped term, wrong coefficient or swapped
+operand).  ``_pins_hold`` runs four independent pins -- the scalar brute
+force, the textbook causal MHA reduction, the single-token closed form and
+the closed form of the q-k-mean under scaled delta taps -- and every mutant
+must make at least one of them fail.  Each pin also runs on the unmutated
+oracle, where all four must hold.  The mistakes live only in this test, on
+the CPU.
 """
 
 import math
@@ -26,14 +29,99 @@ def _case(Hq=4, Hkv=2, T=6, d=4, E=10, seed=3, **kw):
     return s, P.x, w
 
 
-def _pins_hold():
-    """True when every pin passes with the oracle as currently bound."""
-    ok = True
+def _rel(a, b):
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+def _delta(w, c=1.0, c2=1.0):
+    w = dict(w)
+    for name, scale in (("q_seq_taps", c), ("k_seq_taps", c), ("q_chan_taps", c2),
+                        ("k_chan_taps", c2)):
+        t = np.zeros_like(w[name])
+        t[:, 0] = scale
+        w[name] = t
+    return w
+
+
+def _pin_brute():
     s, x, w = _case()
     y = O.prefill(x, w, s)
     yb = np.array(brute_prefill(x.tolist(), {k: v.tolist() for k, v in w.items()}, s))
-    ok &= np.linalg.norm(y - yb) <= 1e-12 * np.linalg.norm(yb)
+    return _rel(y, yb) <= 1e-12
+
+
+def _pin_mha():
+    """Compression 1, delta taps, extras off: textbook causal RoPE MHA with
+    grouped kv heads, written here with explicit complex rotations."""
+    Hq, Hkv, d, T, B, base = 4, 2, 4, 6, 2, 100.0
+    s = CCAShape(batch=B, seq_len=T, d_model=Hq * d, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                 rope_base=base, dtype="f32", use_qk_mean=0, use_value_shift=0, use_qk_norm=0)
+    P = make_prefill(s, 5)
+    w = _delta(P.weights.f64())
+    w["tau"] = np.full(Hq, 1.0 / math.sqrt(d))
+    x = P.x
+    eq, ekv, G = Hq * d, Hkv * d, Hq // Hkv
+    Q = (x @ w["w_qkv"][:eq].T).reshape(B, T, Hq, d)
+    K = (x @ w["w_qkv"][eq:eq + ekv].T).reshape(B, T, Hkv, d)
+    V = (x @ w["w_qkv"][eq + ekv:].T).reshape(B, T, Hkv, d)
+    theta = base ** (-2.0 * np.arange(d // 2) / d)
+    rot = np.exp(1j * np.outer(np.arange(T), theta))[None, :, None, :]
+
+    def rope(u):
+        z = (u[..., 0::2] + 1j * u[..., 1::2]) * rot
+        r = np.empty_like(u)
+        r[..., 0::2], r[..., 1::2] = z.real, z.imag
+        return r
+    Q, K = rope(Q), rope(K)
+    o = np.zeros((B, T, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            S = Q[b, :, h] @ K[b, :, h // G].T / math.sqrt(d)
+            S[np.triu_indices(T, 1)] = -np.inf
+            p = np.exp(S - S.max(axis=1, keepdims=True))
+            o[b, :, h] = (p / p.sum(axis=1, keepdims=True)) @ V[b, :, h // G]
+    ref = o.reshape(B, T, eq) @ w["w_o"].T
+    return _rel(O.prefill(x, w, s), ref) <= 1e-12
+
+
+def _pin_single_token():
+    """T = 1: o is the token's own value on unshifted kv heads, zero on the
+    shifted (upper) ones, whatever q and k are."""
+    s, x, w = _case(T=1)
+    eq, ekv, d = s.e_q, s.e_kv, s.head_dim
+    vbar = x[:, 0] @ w["w_qkv"][eq + ekv:].T
+    vbar[:, d:] = 0.0
+    o = np.repeat(vbar.reshape(2, 2, d), 2, axis=1).reshape(2, eq)
+    return _rel(O.prefill(x, w, s)[:, 0], o @ w["w_o"].T) <= 1e-12
+
+
+def _pin_qk_mean_closed_form():
+    """Taps (c,0,0,0) and (c',0,0,0) make both convolutions a scaling by
+    alpha = c c'; the mean of the pre- and post-convolution q and k then
+    gives q = (alpha + (1+alpha)/4) q~ + ((1+alpha)/4) k~ per query head, and
+    k = (alpha + (1+alpha)/4) k~ + ((1+alpha)/4) avg q~ per kv head."""
+    s, x, w = _case(Hq=6, Hkv=2)
+    s = s.with_(use_qk_norm=0, rope_base=0.0, use_value_shift=0)
+    c, c2 = 1.5, -2.0
+    w = _delta(w, c, c2)
+    alpha = c * c2
+    lat = O.latents(x, w, s)
+    B, T, d, Hq, Hkv = 2, s.seq_len, s.head_dim, 6, 2
+    G, eq, ekv = 3, s.e_q, s.e_kv
+    qt = (x @ w["w_qkv"][:eq].T).reshape(B, T, Hq, d)
+    kt = (x @ w["w_qkv"][eq:eq + ekv].T).reshape(B, T, Hkv, d)
+    own, other = alpha + (1 + alpha) / 4, (1 + alpha) / 4
+    ok = _rel(lat["q"], own * qt + other * kt[:, :, np.arange(Hq) // G]) <= 1e-12
+    ok &= _rel(lat["k"], own * kt + other * qt.reshape(B, T, Hkv, G, d).mean(axis=3)) <= 1e-12
     return bool(ok)
+
+
+PINS = (_pin_brute, _pin_mha, _pin_single_token, _pin_qk_mean_closed_form)
+
+
+def _pins_hold():
+    """True when every pin passes with the oracle as currently bound."""
+    return all(bool(pin()) for pin in PINS)
 
 
 def _rope_bad_sign(x, pos, base, readings=O.DEFAULT_READINGS):
@@ -79,16 +167,41 @@ def _chan_conv_wrong_direction(a, taps):
 
 
 def _qk_mean_drop_k(bq, bk, q_pre, k_pre, group, readings=O.DEFAULT_READINGS):
-    q, k = _orig["qk_mean"](bq, bk, q_pre, 0 * k_pre, group, readings)
-    return q, k + 0.5 * k_pre
+    # the query heads' mean forgets the key's pre-conv value
+    q, _ = _orig["qk_mean"](bq, bk, q_pre, 0 * k_pre, group, readings)
+    _, k = _orig["qk_mean"](bq, bk, q_pre, k_pre, group, readings)
+    return q, k
 
 
 def _qk_mean_wrong_group(bq, bk, q_pre, k_pre, group, readings=O.DEFAULT_READINGS):
-    k_for_q = np.tile(k_pre, (1,) * (k_pre.ndim - 2) + (group, 1))
+    # query head h meets kv head h mod H_kv instead of h // G
+    rep = lambda a: np.tile(a, (1,) * (a.ndim - 2) + (group, 1))
     lead = q_pre.shape[:-2]
     Hkv, d = k_pre.shape[-2:]
-    qm = q_pre.reshape(*lead, Hkv, group, d).mean(axis=-2)
-    return bq + 0.5 * (q_pre + k_for_q), bk + 0.5 * (k_pre + qm)
+    mean = lambda a: a.reshape(*lead, Hkv, group, d).mean(axis=-2)
+    return (bq + 0.25 * (q_pre + rep(k_pre) + bq + rep(bk)),
+            bk + 0.25 * (k_pre + mean(q_pre) + bk + mean(bq)))
+
+
+def _qk_mean_half_not_quarter(bq, bk, q_pre, k_pre, group, readings=O.DEFAULT_READINGS):
+    # the four terms halved instead of averaged
+    q, k = _orig["qk_mean"](bq, bk, q_pre, k_pre, group, readings)
+    return 2 * q - bq, 2 * k - bk
+
+
+def _qk_mean_first_head_not_group_mean(bq, bk, q_pre, k_pre, group, readings=O.DEFAULT_READINGS):
+    # kv head g takes the post-conv q of the group's first head instead of the average
+    lead = q_pre.shape[:-2]
+    Hkv, d = k_pre.shape[-2:]
+    mean = lambda a: a.reshape(*lead, Hkv, group, d).mean(axis=-2)
+    first = bq.reshape(*lead, Hkv, group, d)[..., 0, :]
+    q, _ = _orig["qk_mean"](bq, bk, q_pre, k_pre, group, readings)
+    return q, bk + 0.25 * (k_pre + mean(q_pre) + bk + first)
+
+
+def _qk_mean_pre_only(bq, bk, q_pre, k_pre, group, readings=O.DEFAULT_READINGS):
+    # the other reading (pre-convolution mean only) in place of the default
+    return _orig["qk_mean"](bq, bk, q_pre, k_pre, group, O.Readings(qk_mean="M1"))
 
 
 def _value_shift_lower(vbar, prev=None, readings=O.DEFAULT_READINGS):
@@ -143,6 +256,9 @@ MUTANTS = {
     "chan conv direction": ("chan_conv", _chan_conv_wrong_direction),
     "q-k-mean drops k~": ("qk_mean", _qk_mean_drop_k),
     "q-k-mean wrong group": ("qk_mean", _qk_mean_wrong_group),
+    "q-k-mean halves instead of averaging": ("qk_mean", _qk_mean_half_not_quarter),
+    "q-k-mean first head not group mean": ("qk_mean", _qk_mean_first_head_not_group_mean),
+    "q-k-mean pre-conv terms only": ("qk_mean", _qk_mean_pre_only),
     "value-shift lower half": ("value_shift", _value_shift_lower),
     "value-shift looks ahead": ("value_shift", _value_shift_forward),
     "no normalisation": ("l2_normalize", _no_norm),
@@ -153,8 +269,9 @@ MUTANTS = {
 }
 
 
-def test_unmutated_pins_hold():
-    assert _pins_hold()
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_unmutated_pins_hold(pin):
+    assert pin()
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -47,13 +47,24 @@ def rel(a, b):
 # brute force: every step, all switches on, several head layouts
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("reading", ["M2", "M1"])
 @pytest.mark.parametrize("Hq,Hkv,T,d", [(2, 2, 7, 4), (4, 2, 6, 4), (4, 4, 5, 2), (2, 1, 8, 4), (4, 1, 3, 8)])
-def test_brute_force_matches_oracle(Hq, Hkv, T, d):
+def test_brute_force_matches_oracle(Hq, Hkv, T, d, reading):
     shift = 1 if Hkv % 2 == 0 else 0
     s, x, w = tiny(T=T, Hq=Hq, Hkv=Hkv, d=d, E=10, use_value_shift=shift, seed=Hq * 7 + T)
-    y = O.prefill(x, w, s)
-    yb = np.array(brute_prefill(x.tolist(), {k: v.tolist() for k, v in w.items()}, s))
+    y = O.prefill(x, w, s, readings=O.Readings(qk_mean=reading))
+    yb = np.array(brute_prefill(x.tolist(), {k: v.tolist() for k, v in w.items()}, s,
+                                qk_mean=reading))
     assert rel(y, yb) < 1e-12
+
+
+def test_qk_mean_readings_differ():
+    """The two readings give different outputs on the same inputs (so the
+    brute-force comparison above can tell them apart)."""
+    s, x, w = tiny(T=6, Hq=4, Hkv=2)
+    y2 = O.prefill(x, w, s, readings=O.Readings(qk_mean="M2"))
+    y1 = O.prefill(x, w, s, readings=O.Readings(qk_mean="M1"))
+    assert rel(y1, y2) > 1e-3
 
 
 def test_brute_force_switches_off():
@@ -387,10 +398,52 @@ def test_sampled_rows_match_full():
 # q_t and k_t over random inputs is clearly higher with the mean on.
 # ---------------------------------------------------------------------------
 
-def test_qk_mean_strengthens_diagonal():
-    s, x, w = tiny(B=4, T=64, E=64, Hq=4, Hkv=4, d=16, base=0.0, seed=11)
-    on = O.latents(x, w, s)
-    off = O.latents(x, w, s.with_(use_qk_mean=0))
-    cos_on = np.mean(np.sum(on["q"] * on["k"], axis=-1))
-    cos_off = np.mean(np.sum(off["q"] * off["k"], axis=-1))
+@pytest.mark.parametrize("reading", ["M2", "M1"])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+def test_qk_mean_strengthens_diagonal(reading, Hq, Hkv):
+    s, x, w = tiny(B=4, T=64, E=64, Hq=Hq, Hkv=Hkv, d=16, base=0.0, seed=11)
+    r = O.Readings(qk_mean=reading)
+    on = O.latents(x, w, s, readings=r)
+    off = O.latents(x, w, s.with_(use_qk_mean=0), readings=r)
+    G = Hq // Hkv
+    cos_on = np.mean(np.sum(on["q"] * np.repeat(on["k"], G, axis=2), axis=-1))
+    cos_off = np.mean(np.sum(off["q"] * np.repeat(off["k"], G, axis=2), axis=-1))
     assert cos_on > cos_off + 0.2
+
+
+# ---------------------------------------------------------------------------
+# closed form of the q-k-mean under scaled delta taps.  With the sequence and
+# channel taps (c, 0, 0, 0) and (c', 0, 0, 0) both convolutions are a scaling
+# by alpha = c * c': b_q = alpha q~, b_k = alpha k~.  The mean of the pre- and
+# post-convolution q and k of a CCA head is then (1 + alpha)(q~ + k~) / 4, so
+#   q = (alpha + (1 + alpha) / 4) q~ + ((1 + alpha) / 4) k~          (M2)
+# and with only the pre-convolution mean (q~ + k~) / 2,
+#   q = (alpha + 1 / 2) q~ + (1 / 2) k~                                (M1).
+# For CCGQA the kv head meets the average q~ of its G query heads.  At
+# alpha = 1 the two readings coincide; at alpha = 3 they do not.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("reading", ["M2", "M1"])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (6, 2)])
+@pytest.mark.parametrize("c,c2", [(1.0, 1.0), (1.5, 2.0), (-0.5, 3.0)])
+def test_qk_mean_closed_form_scaled_delta(reading, Hq, Hkv, c, c2):
+    s, x, w = tiny(B=2, T=5, E=10, Hq=Hq, Hkv=Hkv, d=4, base=0.0, use_value_shift=0,
+                   use_qk_norm=0, seed=Hq + 3)
+    w = delta_taps(w, s)
+    w["q_seq_taps"] *= c
+    w["k_seq_taps"] *= c
+    w["q_chan_taps"] *= c2
+    w["k_chan_taps"] *= c2
+    alpha = c * c2
+    lat = O.latents(x, w, s, readings=O.Readings(qk_mean=reading))
+    d, G, eq, ekv = s.head_dim, Hq // Hkv, s.e_q, s.e_kv
+    qt = (x @ w["w_qkv"][:eq].T).reshape(2, 5, Hq, d)
+    kt = (x @ w["w_qkv"][eq:eq + ekv].T).reshape(2, 5, Hkv, d)
+    k_of_q = kt[:, :, np.arange(Hq) // G]                  # kv head of each query head
+    q_avg = qt.reshape(2, 5, Hkv, G, d).mean(axis=3)      # average q~ of each group
+    if reading == "M2":
+        own, other = alpha + (1 + alpha) / 4, (1 + alpha) / 4
+    else:
+        own, other = alpha + 0.5, 0.5
+    np.testing.assert_allclose(lat["q"], own * qt + other * k_of_q, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lat["k"], own * kt + other * q_avg, rtol=1e-12, atol=1e-13)
