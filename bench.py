@@ -12,7 +12,9 @@ next to it.  A second timed pass launches the same kernels stage by stage
 with HIP events between them to get per-kernel durations for the roofline.
 A fourth pass times a training step on the prefill workload
 (``cca_prefill_forward_train`` + ``cca_prefill_backward``, reported under
-``train``).  The fp64 oracle is timed on the host cores on a bounded sample
+``train``).  A fifth pass measures the two longer CCGQA prefill workloads
+(8192 and 16384 tokens) on their own, kernel by kernel, under
+``prefill_configs``.  The fp64 oracle is timed on the host cores on a bounded sample
 of the same prefill workload (``cpu_baseline``).
 
     python bench.py [--steps K] [--warmup W] [--prefill WORKLOAD] [--no-cpu]
@@ -44,6 +46,8 @@ def parse():
     p.add_argument("--prefill", default="cca_prefill_b4_t2048")
     p.add_argument("--decode", default="ccgqa_decode_b64_l32768")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-kernel measurement of the 8192- and 16384-token CCGQA prefills")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--compare", action="store_true",
                    help="prefill of ccgqa_prefill_t16384 next to full-width MHA and GQA-8 baselines "
@@ -126,17 +130,19 @@ def algorithmic(sp, sd):
     B, T, E = sp.batch, sp.seq_len, sp.d_model
     eq, ekv, N = sp.e_q, sp.e_kv, sp.n_qkv
     esz = 2 if sp.dtype == "bf16" else 4
-    Lk = sd.cache_len + 1
-    return {
-        # bytes: read qkv~ (fp32) + write q, k (16-bit) and v (storage type)
-        "convmix_bytes": B * T * N * 4 + B * T * (eq + ekv) * 2 + B * T * ekv * esz,
+    out = {
+        # bytes the mixing step must move: read qkv~ once (16-bit in bf16 mode)
+        # and write q, k (16-bit) and v (storage type) once
+        "convmix_bytes": B * T * N * esz + B * T * (eq + ekv) * esz + B * T * ekv * esz,
         # causal latent attention: 2 matmuls of 2*d flops per visible (query, key) pair
         "attn_flops": 2 * 2 * B * sp.n_q_heads * sp.head_dim * T * (T + 1) / 2,
         "downproj_flops": 2 * B * T * N * E,
         "upproj_flops": 2 * B * T * E * eq,
-        # decode attention streams K and V of Lk keys once
-        "decode_attn_bytes": 2 * sd.batch * sd.n_kv_heads * Lk * sd.head_dim * 2,
     }
+    if sd is not None:
+        # decode attention streams K and V of Lk = L + 1 keys once
+        out["decode_attn_bytes"] = 2 * sd.batch * sd.n_kv_heads * (sd.cache_len + 1) * sd.head_dim * 2
+    return out
 
 
 def measured_traffic():
@@ -297,6 +303,86 @@ def training_step(cca, T, sp, pcfg, pw, x, dev, K):
             # pair (S recomputed, dP, dV, dQ, dK) plus the 4 gradient GEMMs
             "backward_gflop": round((5 * 2 * d * pairs + 2 * 2 * sp.tokens * sp.d_model * (sp.n_qkv + sp.e_q))
                                     / 1e9, 2)}
+
+
+def prefill_config(cca, T, name, K, dev):
+    """One prefill workload on its own: cca_prefill_forward timed with HIP
+    events (K iterations after two warm-up calls), then each stage call timed
+    with events between them, then the mixing kernel again with the Infinity
+    Cache flushed before each call (its HBM figure).  Rooflines per kernel
+    from the algorithmic work of algorithmic()."""
+    import numpy as np
+    import torch
+    from synth import make_prefill, workload
+    sp = workload(name)
+    P = make_prefill(sp, seed=0)
+    pw = upload_weights(cca, T, P.weights, dev)
+    cfg = cca.make_config(sp)
+    x = T.to_device(P.x_s, dev)
+    y = torch.empty_like(x)
+    ws = T.workspace(cca.prefill_workspace_size(cfg), dev)
+    del P
+    for _ in range(2):
+        cca.prefill_forward(cfg, pw, x, y, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b_ in ev:
+        a.record()
+        cca.prefill_forward(cfg, pw, x, y, ws)
+        b_.record()
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b_) for a, b_ in ev]
+    pre_ms = sum(times) / K
+    names = ["downproj", "convmix", "attention", "upproj"]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    for e in sev:
+        e[0].record()
+        cca.stage_downproj(cfg, pw, x, ws); e[1].record()
+        cca.stage_convmix(cfg, pw, ws); e[2].record()
+        cca.stage_attention(cfg, pw, ws); e[3].record()
+        cca.stage_upproj(cfg, pw, y, ws); e[4].record()
+    torch.cuda.synchronize()
+    st = {n: sum(e[j].elapsed_time(e[j + 1]) for e in sev) / K for j, n in enumerate(names)}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = 0.0
+    for _ in range(K):
+        cca.stage_downproj(cfg, pw, x, ws)
+        flush.fill_(1)
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cca.stage_convmix(cfg, pw, ws)
+        b_.record()
+        torch.cuda.synchronize()
+        cold += a.elapsed_time(b_) / K
+    del flush, ws, x, y
+    torch.cuda.empty_cache()
+    alg = algorithmic(sp, None)
+    peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+
+    def mfma(flops, ms):
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(tf, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tf / peak, 4), "ms": round(ms, 4)}
+    conv_cold = alg["convmix_bytes"] / (cold * 1e-3) / 1e9
+    print(f"[bench] {name}: prefill {pre_ms:.3f} ms, attention {st['attention']:.3f} ms, "
+          f"mixing {cold * 1e3:.1f} us cold", file=sys.stderr, flush=True)
+    return {
+        "shape": f"B={sp.batch}, T={sp.seq_len}, E={sp.d_model}, {sp.n_q_heads}q/{sp.n_kv_heads}kv x "
+                 f"{sp.head_dim}, {sp.dtype}",
+        "prefill_ms": round(pre_ms, 4), "prefill_ms_median": round(float(np.median(times)), 4),
+        "tokens_per_s": round(sp.tokens / (pre_ms * 1e-3), 1),
+        "stage_ms": {k: round(v, 4) for k, v in st.items()},
+        "rooflines": {
+            "attention": mfma(alg["attn_flops"], st["attention"]),
+            "downproj": mfma(alg["downproj_flops"], st["downproj"]),
+            "upproj": mfma(alg["upproj_flops"], st["upproj"]),
+            "convmix": {"bound": "hbm", "achieved": round(conv_cold, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(conv_cold / PEAK_HBM_GBS, 4),
+                        "ms": round(cold, 4), "bytes": alg["convmix_bytes"],
+                        "timing": "Infinity Cache flushed before each call",
+                        "warm_ms": round(st["convmix"], 4)},
+        },
+    }
 
 
 def compare(args):
@@ -542,9 +628,21 @@ def main():
     # pass with a seeded upstream gradient; every gradient is computed
     train = training_step(cca, T, sp, pcfg, pw, x, dev, K)
 
+    # ---- timed region 5: the two longer CCGQA prefill workloads, each on
+    # its own (per-kernel rooflines; the mixing kernel with a cold cache) --
+    configs = {}
+    if not args.no_configs:
+        del pws
+        torch.cuda.empty_cache()
+        for name in ("ccgqa_prefill_t8192", "ccgqa_prefill_t16384"):
+            configs[name] = prefill_config(cca, T, name, K, dev)
+
     alg = algorithmic(sp, sd)
     attn_tflops = alg["attn_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
-    conv_gbs = alg["convmix_bytes"] / (stage_ms["convmix"] * 1e-3) / 1e9
+    # the mixing kernel's HBM figure: with the Infinity Cache flushed before
+    # each call (in the pipeline it reads qkv~ that the down-projection has
+    # just left in the cache; that warm time is reported next to it)
+    conv_gbs = alg["convmix_bytes"] / (cold["convmix"] * 1e-3) / 1e9
     dec_gbs = alg["decode_attn_bytes"] / (stage_ms["dec_attention"] * 1e-3) / 1e9
     dec_step_gbs = alg["decode_attn_bytes"] / (decode_ms * 1e-3) / 1e9
     mfma_peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
@@ -556,7 +654,10 @@ def main():
         "attention": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": mfma_peak,
                       "unit": "TFLOP/s", "frac": round(attn_tflops / mfma_peak, 4), "traffic": None},
         "convmix": {"bound": "hbm", "achieved": round(conv_gbs, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(conv_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                    "unit": "GB/s", "frac": round(conv_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                    "bytes": alg["convmix_bytes"], "ms": round(cold["convmix"], 4),
+                    "timing": "Infinity Cache flushed before each call",
+                    "warm_ms": round(stage_ms["convmix"], 4)},
     }
     for g in ("downproj", "upproj"):
         tf = alg[f"{g}_flops"] / (stage_ms[g] * 1e-3) / 1e12
@@ -617,6 +718,7 @@ def main():
                          algorithmic_per_launch=(alg["decode_attn_bytes"] if dom_key == "dec_attention"
                                                  else None)),
         "rooflines": rooflines,
+        "prefill_configs": configs,
     }
     if not args.no_cpu:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

@@ -20,6 +20,7 @@ LIB_PATH = os.environ.get("CCA_LIBRARY") or os.path.join(PKG, "libcca.so")
 CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_WORKSPACE, CCA_ERR_HIP = range(5)
 CCA_BF16, CCA_F32 = 0, 1
 CCA_CHAN_PER_HEAD, CCA_CHAN_GROUPED = 0, 1
+CCA_QK_MEAN_PRE_POST, CCA_QK_MEAN_PRE = 0, 1
 WS_QKV, WS_Q, WS_K, WS_VT, WS_O, WS_PART, WS_SPLITK, WS_COUNT = range(8)
 
 # Every entry point declared in include/cca.h.
@@ -50,7 +51,7 @@ class Config(C.Structure):
         ("seq_conv_k", C.c_int32), ("chan_conv_k", C.c_int32),
         ("use_qk_mean", C.c_int32), ("use_value_shift", C.c_int32), ("use_qk_norm", C.c_int32),
         ("rope_base", C.c_float), ("norm_eps", C.c_float), ("dtype", C.c_int32),
-        ("chan_conv_mode", C.c_int32),
+        ("chan_conv_mode", C.c_int32), ("qk_mean_mode", C.c_int32),
     ]
 
 
@@ -131,19 +132,21 @@ def status_string(status: int) -> str:
     return lib.cca_status_string(int(status)).decode()
 
 
-def make_config(shape, chan_conv: str = "per_head") -> Config:
+def make_config(shape, chan_conv: str = "per_head", qk_mean: str = "pre_post") -> Config:
     """Config from any object with the cca_config field names (dtype given as
     "bf16" / "f32" or as the enum value); ``chan_conv`` "per_head" or
-    "grouped" selects the channel-conv reading."""
+    "grouped" selects the channel-conv reading, ``qk_mean`` "pre_post" or
+    "pre" the q-k-mean reading."""
     dt = shape.dtype
     if isinstance(dt, str):
         dt = {"bf16": CCA_BF16, "f32": CCA_F32}[dt]
     mode = {"per_head": CCA_CHAN_PER_HEAD, "grouped": CCA_CHAN_GROUPED}[chan_conv]
+    mean = {"pre_post": CCA_QK_MEAN_PRE_POST, "pre": CCA_QK_MEAN_PRE}[qk_mean]
     return Config(int(shape.batch), int(shape.seq_len), int(shape.d_model), int(shape.n_q_heads),
                   int(shape.n_kv_heads), int(shape.head_dim), int(shape.seq_conv_k),
                   int(shape.chan_conv_k), int(shape.use_qk_mean), int(shape.use_value_shift),
                   int(shape.use_qk_norm), float(shape.rope_base), float(shape.norm_eps), int(dt),
-                  mode)
+                  mode, mean)
 
 
 def _ptr(t) -> Optional[int]:

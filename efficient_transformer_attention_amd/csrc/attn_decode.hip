@@ -43,6 +43,14 @@ template <int D> struct DecMaxG { static constexpr int value = D <= 64 ? 32 : 16
 
 int decode_chunk_keys(int) { return DEC_CHUNK; }
 
+static int dec_num_chunks(int B, int Hkv, int Lk);
+static int dec_chunk_len(int Lk, int nch);
+
+bool decode_pages_fit(int B, int Hkv, int Lk, int page) {
+  const int chunk = dec_chunk_len(Lk, dec_num_chunks(B, Hkv, Lk));
+  return page >= 1 && (chunk + page - 1) / page + 1 <= DEC_MAX_PAGES;
+}
+
 // Largest divisor of G that is <= cap.
 static int dec_heads_per_wg(int G, int cap) {
   for (int gh = cap < G ? cap : G; gh >= 1; --gh)

@@ -50,6 +50,10 @@ cca_status check_launch(hipError_t e, hipStream_t stream) {
 
 size_t elem_size(int dtype) { return dtype == CCA_F32 ? 4 : 2; }
 
+// The down-projection output qkv~: fp16 in bf16 mode (10 mantissa bits, half
+// the bytes of fp32 for the mixing kernel to read), fp32 in fp32 mode.
+size_t qkv_elem_size(int dtype) { return dtype == CCA_F32 ? 4 : 2; }
+
 // Storage type of the normalised, rotated q and k handed to the attention
 // kernel: fp16 when they are unit vectors (10 mantissa bits instead of
 // bf16's 7, no range concern), else the storage dtype.
@@ -72,7 +76,8 @@ MixShape mix_shape(const cca_config &c) {
   s.d = c.head_dim;
   s.ks = c.seq_conv_k;
   s.kc = c.chan_conv_k;
-  s.use_mean = c.use_qk_mean;
+  // q-k-mean: 0 off, 1 the pre-convolution values, 2 the pre- and post-convolution values
+  s.use_mean = c.use_qk_mean ? (c.qk_mean_mode == CCA_QK_MEAN_PRE ? 1 : 2) : 0;
   s.use_shift = c.use_value_shift;
   s.use_norm = c.use_qk_norm;
   s.grouped = c.chan_conv_mode == CCA_CHAN_GROUPED ? 1 : 0;
@@ -100,11 +105,14 @@ cca_status validate_shape(const cca_config *c, bool need_seq) {
   if (c->dtype != CCA_BF16 && c->dtype != CCA_F32) return CCA_ERR_UNSUPPORTED;
   if (c->chan_conv_mode != CCA_CHAN_PER_HEAD && c->chan_conv_mode != CCA_CHAN_GROUPED)
     return CCA_ERR_INVALID_ARG;
+  if (c->qk_mean_mode != CCA_QK_MEAN_PRE_POST && c->qk_mean_mode != CCA_QK_MEAN_PRE)
+    return CCA_ERR_INVALID_ARG;
   const int d = c->head_dim;
   if (d != 16 && d != 32 && d != 64 && d != 128) return CCA_ERR_UNSUPPORTED;
   if (c->seq_conv_k < 1 || c->seq_conv_k > 4 || c->chan_conv_k < 1 || c->chan_conv_k > 4)
     return CCA_ERR_UNSUPPORTED;
-  if (!convmix_fits(c->n_q_heads / c->n_kv_heads, d)) return CCA_ERR_UNSUPPORTED;
+  if (!convmix_fits(c->n_q_heads / c->n_kv_heads, d, (int)qkv_elem_size(c->dtype)))
+    return CCA_ERR_UNSUPPORTED;
   if (c->chan_conv_mode == CCA_CHAN_GROUPED &&
       (!grouped_conv_supported(d, c->dtype == CCA_F32) ||
        !convmix_decode_grouped_fits(c->n_q_heads / c->n_kv_heads, d, 1, c->seq_conv_k, c->chan_conv_k)))
@@ -144,7 +152,7 @@ Layout prefill_layout(const cca_config &c) {
   const size_t eq = (size_t)c.n_q_heads * d, ekv = (size_t)c.n_kv_heads * d;
   const size_t N = eq + 2 * ekv;
   size_t o = 0;
-  L.off[CCA_WS_QKV] = o; o = align_up(o + B * T * N * 4, WS_ALIGN);
+  L.off[CCA_WS_QKV] = o; o = align_up(o + B * T * N * qkv_elem_size(c.dtype), WS_ALIGN);
   L.off[CCA_WS_Q] = o;   o = align_up(o + B * c.n_q_heads * Tp * d * qk_elem_size(c), WS_ALIGN);
   L.off[CCA_WS_K] = o;   o = align_up(o + B * c.n_kv_heads * Tp * d * qk_elem_size(c), WS_ALIGN);
   L.off[CCA_WS_VT] = o;  o = align_up(o + B * c.n_kv_heads * d * Tp * elem_size(c.dtype), WS_ALIGN);
@@ -189,9 +197,16 @@ Layout decode_layout(const cca_config &c, int cache_len, int m = 1) {
 // Training workspace: the prefill layout (same offsets), then what the
 // backward pass keeps or builds.  Slots of the backward, in order.
 enum {
-  TR_LSE, TR_DO, TR_DSUM, TR_QT, TR_KT, TR_DOT, TR_VR, TR_GQ, TR_DK, TR_DV, TR_DM, TR_DA, TR_DZ,
-  TR_MIXS, TR_WOT, TR_WQKVT, TR_DYT, TR_OT, TR_DZT, TR_XT, TR_SPLITK, TR_COUNT
+  TR_LSE, TR_BPOST, TR_DO, TR_DSUM, TR_QT, TR_KT, TR_DOT, TR_VR, TR_GQ, TR_DK, TR_DV, TR_DM, TR_DA,
+  TR_DZ, TR_MIXS, TR_WOT, TR_WQKVT, TR_DYT, TR_OT, TR_DZT, TR_XT, TR_SPLITK, TR_COUNT
 };
+
+// Whether the training forward keeps the channel-conv output b (fp32) for the
+// backward: the q-k-mean of the pre- and post-convolution values mixes b of
+// the group's heads.
+bool keeps_bpost(const cca_config &c) {
+  return c.use_qk_mean && c.qk_mean_mode == CCA_QK_MEAN_PRE_POST;
+}
 
 struct TrainLayout {
   Layout pre;
@@ -226,6 +241,7 @@ TrainLayout train_layout(const cca_config &c) {
   const size_t BTp = (size_t)L.BTp;
   const size_t sz[TR_COUNT] = {
       B * Hq * Tp * 4,            // TR_LSE
+      keeps_bpost(c) ? BT * (eq + ekv) * 4 : 0,   // TR_BPOST
       BT * eq * es,               // TR_DO
       B * Hq * Tp * 4,            // TR_DSUM
       B * Hq * d * Tp * es,       // TR_QT
@@ -333,19 +349,23 @@ cca_status run_downproj(const cca_config &c, const cca_weights *w, const void *x
                         const Layout &L, hipStream_t st) {
   const int M = c.batch * c.seq_len, E = c.d_model;
   const int N = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
-  float *qkv = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_QKV));
+  void *qkv = wsp(ws, L, CCA_WS_QKV);
   hipError_t e;
   if (c.dtype == CCA_BF16)
-    e = launch_gemm_nt<bf16, float>((const bf16 *)x, (const bf16 *)w->w_qkv, qkv, M, N, E, E, E, N, st);
+    e = launch_gemm_nt<bf16, f16>((const bf16 *)x, (const bf16 *)w->w_qkv, (f16 *)qkv, M, N, E, E,
+                                  E, N, st);
   else
-    e = launch_gemm_nt<float, float>((const float *)x, (const float *)w->w_qkv, qkv, M, N, E, E, E, N, st);
+    e = launch_gemm_nt<float, float>((const float *)x, (const float *)w->w_qkv, (float *)qkv, M, N,
+                                     E, E, E, N, st);
   return check_launch(e, st);
 }
 
+// bout (nullable): receives the channel-conv output of every q and k head
+// (the training forward under the pre- and post-convolution mean).
 cca_status run_convmix(const cca_config &c, const cca_weights *w, const StateOut &so, void *ws,
-                       const Layout &L, hipStream_t st) {
+                       const Layout &L, hipStream_t st, float *bout = nullptr) {
   const MixShape s = mix_shape(c);
-  const float *qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
+  const void *qkv = wsp(ws, L, CCA_WS_QKV);
   float *r1b = nullptr;
   hipError_t e;
   if (c.chan_conv_mode == CCA_CHAN_GROUPED) {   // the channel conv on MFMA first
@@ -355,17 +375,17 @@ cca_status run_convmix(const cca_config &c, const cca_weights *w, const StateOut
     CCA_TRY(check_launch(e, st));
   }
   if (c.dtype == CCA_F32) {
-    e = launch_convmix_prefill<float, float>(s, taps_of(w), qkv, (float *)wsp(ws, L, CCA_WS_Q),
-                                             (float *)wsp(ws, L, CCA_WS_K),
-                                             (float *)wsp(ws, L, CCA_WS_VT), so, st, r1b);
+    e = launch_convmix_prefill<float, float, float>(
+        s, taps_of(w), (const float *)qkv, (float *)wsp(ws, L, CCA_WS_Q),
+        (float *)wsp(ws, L, CCA_WS_K), (float *)wsp(ws, L, CCA_WS_VT), so, st, r1b, bout);
   } else if (qk_is_f16(c)) {
-    e = launch_convmix_prefill<f16, bf16>(s, taps_of(w), qkv, (f16 *)wsp(ws, L, CCA_WS_Q),
-                                          (f16 *)wsp(ws, L, CCA_WS_K),
-                                          (bf16 *)wsp(ws, L, CCA_WS_VT), so, st, r1b);
+    e = launch_convmix_prefill<f16, f16, bf16>(
+        s, taps_of(w), (const f16 *)qkv, (f16 *)wsp(ws, L, CCA_WS_Q), (f16 *)wsp(ws, L, CCA_WS_K),
+        (bf16 *)wsp(ws, L, CCA_WS_VT), so, st, r1b, bout);
   } else {
-    e = launch_convmix_prefill<bf16, bf16>(s, taps_of(w), qkv, (bf16 *)wsp(ws, L, CCA_WS_Q),
-                                           (bf16 *)wsp(ws, L, CCA_WS_K),
-                                           (bf16 *)wsp(ws, L, CCA_WS_VT), so, st, r1b);
+    e = launch_convmix_prefill<f16, bf16, bf16>(
+        s, taps_of(w), (const f16 *)qkv, (bf16 *)wsp(ws, L, CCA_WS_Q),
+        (bf16 *)wsp(ws, L, CCA_WS_K), (bf16 *)wsp(ws, L, CCA_WS_VT), so, st, r1b, bout);
   }
   return check_launch(e, st);
 }
@@ -511,8 +531,10 @@ cca_status run_backward(const cca_config &c, const cca_weights *w, const void *x
   aa.gq = trp<float>(ws, L, TR_GQ);
   CCA_TRY(check_launch(launch_attention_backward<TQ, TV>(s, aa, st), st));
   // mixing steps
-  MixBwdArgs<TV> ma;
-  ma.qkv = reinterpret_cast<const float *>(wsp(ws, P, CCA_WS_QKV));
+  typedef typename std::conditional<std::is_same<TV, float>::value, float, f16>::type TI;
+  MixBwdArgs<TI, TV> ma;
+  ma.qkv = reinterpret_cast<const TI *>(wsp(ws, P, CCA_WS_QKV));
+  ma.bpost = keeps_bpost(c) ? trp<float>(ws, L, TR_BPOST) : nullptr;
   ma.gq = aa.gq;
   ma.dk = aa.dk;
   ma.dv = aa.dv;
@@ -525,7 +547,7 @@ cca_status run_backward(const cca_config &c, const cca_weights *w, const void *x
   ma.d_k_chan = gr->k_chan_taps;
   ma.d_q_seq = gr->q_seq_taps;
   ma.d_k_seq = gr->k_seq_taps;
-  CCA_TRY(check_launch(launch_mix_backward<TV>(s, taps_of(w), ma, st), st));
+  CCA_TRY(check_launch(launch_mix_backward<TI, TV>(s, taps_of(w), ma, st), st));
   // down-projection: dx = dz W_qkv, dW_qkv = dz^T x
   CCA_TRY(check_launch(launch_transpose_2d<TV, TV>((const TV *)w->w_qkv, trp<TV>(ws, L, TR_WQKVT),
                                                    N, N, E, E, N, st), st));
@@ -813,7 +835,8 @@ cca_status cca_prefill_forward_train(const cca_config *cfg, const cca_weights *w
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const Layout &L = TL.pre;
   CCA_TRY(run_downproj(*cfg, w, x, ws, L, st));
-  CCA_TRY(run_convmix(*cfg, w, state_of((const cca_state *)nullptr), ws, L, st));
+  CCA_TRY(run_convmix(*cfg, w, state_of((const cca_state *)nullptr), ws, L, st,
+                      keeps_bpost(*cfg) ? trp<float>(ws, TL, TR_BPOST) : nullptr));
   CCA_TRY(run_attention(*cfg, w, ws, L, st, trp<float>(ws, TL, TR_LSE)));
   return run_upproj(*cfg, w, y, ws, L, cfg->batch * cfg->seq_len, st);
 }
@@ -874,6 +897,8 @@ cca_status cca_decode_step_paged(const cca_config *cfg, const cca_weights *w, co
   if (c.seq_conv_k > 1 && (!si->conv_q || !si->conv_k || !so->conv_q || !so->conv_k))
     return CCA_ERR_INVALID_ARG;
   if (c.use_value_shift && (!si->vshift || !so->vshift)) return CCA_ERR_INVALID_ARG;
+  if (c.dtype == CCA_BF16 && !decode_pages_fit(c.batch, c.n_kv_heads, max_cache_len + 1, si->page_size))
+    return CCA_ERR_UNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const StateOut in = state_of(si), out = state_of(so);
   CCA_TRY(dec_downproj(c, w, x_t, ws, L, st));
@@ -963,6 +988,9 @@ cca_status cca_decode_multi_paged(const cca_config *cfg, const cca_weights *w, c
   if (c.seq_conv_k > 1 && (!si->conv_q || !si->conv_k || !so->conv_q || !so->conv_k))
     return CCA_ERR_INVALID_ARG;
   if (c.use_value_shift && (!si->vshift || !so->vshift)) return CCA_ERR_INVALID_ARG;
+  if (c.dtype == CCA_BF16 &&
+      !decode_pages_fit(c.batch, c.n_kv_heads, max_cache_len + n_new, si->page_size))
+    return CCA_ERR_UNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const StateOut in = state_of(si), out = state_of(so);
   CCA_TRY(dec_downproj(c, w, x_new, ws, L, st, n_new));

@@ -119,6 +119,19 @@ __device__ __forceinline__ u32x4 ld16_nt(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+// Four consecutive elements as fp32 (16 bytes of fp32, or 8 bytes of a 16-bit type).
+template <typename T> __device__ __forceinline__ f32x4 ld4f(const T *p);
+template <> __device__ __forceinline__ f32x4 ld4f<float>(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
+}
+template <> __device__ __forceinline__ f32x4 ld4f<f16>(const f16 *p) {
+  const f16x4 v = *reinterpret_cast<const f16x4 *>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <> __device__ __forceinline__ f32x4 ld4f<bf16>(const bf16 *p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
 __device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
 
 __device__ __forceinline__ u32x4 zero_u32x4() {

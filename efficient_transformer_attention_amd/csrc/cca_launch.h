@@ -45,7 +45,8 @@ struct MixShape {
   int B, T, Tp;            // batch, tokens, tokens padded to the query tile
   int Hq, Hkv, G, d;       // heads and head dim
   int ks, kc;              // conv taps (1..4)
-  int use_mean, use_shift, use_norm;
+  int use_mean;            // q-k-mean: 0 off, 1 pre-conv q and k, 2 pre- and post-conv q and k
+  int use_shift, use_norm;
   int grouped;             // channel conv: 0 per-head filter along channels, 1 dense per lag
   float rope_base, eps;
   // RoPE frequencies base^(-2i/d), i < d/2, evaluated on the host in double
@@ -72,7 +73,8 @@ struct StateOut {
 };
 
 // Row index (times d gives the element offset) of sequence b's key `key` of
-// kv head g in the cache described by st.
+// kv head g in the cache described by st.  For reads: a block-table entry
+// outside [0, npages) is clamped (a wrong row, never a fault).
 __host__ __device__ inline size_t cache_row(const StateOut &st, int b, int Hkv, int g, int key) {
   if (!st.table) return (size_t)(b * Hkv + g) * st.capacity + key;
   int pg = st.table[(size_t)b * st.mpps + key / st.page];
@@ -80,16 +82,34 @@ __host__ __device__ inline size_t cache_row(const StateOut &st, int b, int Hkv, 
   return ((size_t)pg * Hkv + g) * st.page + key % st.page;
 }
 
+// The same row for a store, or false when the block-table entry lies outside
+// [0, npages): then nothing is written (a clamped row would belong to another
+// sequence).
+__host__ __device__ inline bool cache_row_store(const StateOut &st, int b, int Hkv, int g, int key,
+                                                size_t *row) {
+  if (!st.table) {
+    *row = (size_t)(b * Hkv + g) * st.capacity + key;
+    return true;
+  }
+  const int pg = st.table[(size_t)b * st.mpps + key / st.page];
+  if (pg < 0 || pg >= st.npages) return false;
+  *row = ((size_t)pg * Hkv + g) * st.page + key % st.page;
+  return true;
+}
+
 // Fused sequence conv + channel conv + q-k-mean + value-shift + L2 norm + RoPE
-// over a prefill.  qkv: fp32 [B*T, e_q + 2 e_kv].  Writes q [B,Hq,Tp,d] and
-// k [B,Hkv,Tp,d] in TQ, vt [B,Hkv,d,Tp] in TV (token order permuted inside
-// 16-token groups), zeros in the padding tokens [T, Tp).  With r1b (the
-// grouped channel conv's output, fp32 [B*T, e_q + e_kv]) the two convolutions
-// are taken from there instead.
-template <typename TQ, typename TV>
-hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
+// over a prefill.  qkv: [B*T, e_q + 2 e_kv] in TI (fp16 in bf16 mode, fp32 in
+// fp32 mode).  Writes q [B,Hq,Tp,d] and k [B,Hkv,Tp,d] in TQ, vt [B,Hkv,d,Tp]
+// in TV (token order permuted inside 16-token groups), zeros in the padding
+// tokens [T, Tp).  With r1b (the grouped channel conv's output, fp32
+// [B*T, e_q + e_kv]) the two convolutions are taken from there instead.
+// bout (nullable): receives the channel-conv output b of every q and k head,
+// fp32 [B*T, e_q + e_kv] (the backward of the pre- and post-convolution mean
+// reads it).
+template <typename TI, typename TQ, typename TV>
+hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const TI *qkv, TQ *q,
                                   TQ *k, TV *vt, const StateOut &st, hipStream_t stream,
-                                  const float *r1b = nullptr);
+                                  const float *r1b = nullptr, float *bout = nullptr);
 
 // Grouped reading of the channel conv over a prefill (d in {16, 32, 64}):
 // outb[b*T + t, col] = sum over lags j < k_c and channels c of
@@ -98,8 +118,9 @@ hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const flo
 // [H, d, k_c, d] per kind (dense_q for the H_q query heads, dense_k for the
 // H_kv key heads).  bf16 mode multiplies in fp16 on MFMA, fp32 mode on the
 // VALU in fp32.
+// qkv: fp32 in fp32 mode, fp16 in bf16 mode (the down-projection's output).
 hipError_t launch_grouped_conv_prefill(const MixShape &s, const MixTaps &w, const float *dense_q,
-                                       const float *dense_k, const float *qkv, float *outb,
+                                       const float *dense_k, const void *qkv, float *outb,
                                        bool f32, hipStream_t stream);
 bool grouped_conv_supported(int d, bool f32);
 
@@ -156,15 +177,19 @@ hipError_t launch_downproj_mix(const MixShape &s, const MixTaps &w, const bf16 *
                                const bf16 *wqkv, int E, void *halo_ws, TQ *q, TQ *k, TV *vt,
                                hipStream_t stream);
 
-// Whether the mixing kernel's LDS tile of one kv group (G query heads + k +
-// v, 19 tokens) fits the 64 KiB it may use.
-bool convmix_fits(int G, int d);
+// Whether the mixing kernels' LDS tiles of one kv group (G query heads + k +
+// v; 19 prefill tokens of es-byte elements, 4 decode rows of fp32) fit the
+// 64 KiB they may use.
+bool convmix_fits(int G, int d, int es);
 // Whether the decode mixing tile of m new tokens fits its LDS.
 bool convmix_decode_fits(int G, int d, int m);
 
 // Keys handled by one workgroup of the split-KV decode attention, and the
 // partial-state scratch it needs.
 int decode_chunk_keys(int d);
+// Whether one key chunk of a decode over Lk keys spans few enough pages of
+// `page` rows for the page list the attention kernel keeps in LDS.
+bool decode_pages_fit(int B, int Hkv, int Lk, int page);
 size_t decode_partial_floats(int B, int Hq, int Hkv, int d, int Lk, int m = 1);
 
 // ---- backward pass ---------------------------------------------------------
@@ -186,21 +211,24 @@ template <typename TQ, typename TV>
 hipError_t launch_attention_backward(const MixShape &s, const AttnBwdArgs<TQ, TV> &a,
                                      hipStream_t stream);
 
-// Buffers of the mixing backward.  Inputs: qkv (fp32 down-projection output),
+// Buffers of the mixing backward.  Inputs: qkv (the down-projection output,
+// TI: fp16 in bf16 mode, fp32 in fp32 mode),
 // gq, dk, dv from the attention backward.  Scratch: dm, da (fp32
 // [B*T, e_q + e_kv]) and mix_backward_scratch_floats() floats.  Outputs: dz
 // ([B*T, e_q + 2 e_kv], the down-projection output's cotangent) and the
 // gradients of tau [Hq], the channel taps [Hq|Hkv, kc] and the sequence taps
 // [e_q|e_kv, ks] (fp32, overwritten).
-template <typename TZ> struct MixBwdArgs {
-  const float *qkv, *gq, *dk, *dv;
+template <typename TI, typename TZ> struct MixBwdArgs {
+  const TI *qkv;
+  const float *bpost;   // q-k-mean of pre- and post-conv values: the forward's channel-conv output
+  const float *gq, *dk, *dv;
   float *dm, *da, *scratch;
   TZ *dz;
   float *d_tau, *d_q_chan, *d_k_chan, *d_q_seq, *d_k_seq;
 };
 size_t mix_backward_scratch_floats(const MixShape &s);
-template <typename TZ>
-hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwdArgs<TZ> &a,
+template <typename TI, typename TZ>
+hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwdArgs<TI, TZ> &a,
                                hipStream_t stream);
 
 // out[c * out_rs + r] = in[r * in_rs + c] for r < R, c < C; rows r >= Rvalid

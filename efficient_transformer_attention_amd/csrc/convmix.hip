@@ -1,14 +1,19 @@
 // Fused latent mixing of the CCA forward pass (gfx950), memory bound.
 //
-// For every token and latent head, from the fp32 down-projection output:
+// For every token and latent head, from the down-projection output:
 //   a2 causal sequence conv, depthwise, lag-indexed k_s taps per channel
 //   a3 channel conv: one k_c-tap filter per head sliding along the channel
 //      index, zero padded inside the head
 //      [GS-EN "2. Methodology" / Convolutional Mixing]
-//   a4 q-k-mean: the mean of the pre-convolution q~ and k~ added to the
-//      convolved q and k; with G query heads per kv head, q head h meets k~ of
-//      its group and kv head g meets the average q~ of its G heads
-//      [GS-EN "2. Methodology" / Q-K-Mean]
+//   a4 q-k-mean: the mean of the query and key values before and after the
+//      convolutions is added to the convolved q and k,
+//        m = (q~ + k~ + b_q + b_k) / 4,  q = b_q + m,  k = b_k + m
+//      (mean mode 2, the default), or the mean of the pre-convolution values
+//      only, (q~ + k~) / 2 (mean mode 1).  With G query heads per kv head,
+//      query head h meets its group's key head, and the key head meets the
+//      average over the group's query heads
+//      [GS-EN "2. Methodology" / Q-K-Mean; EDG "How Compressed Convolutional
+//       Attention Works"; GS-DE "2. Methodik"]
 //   a5 value-shift: the upper half of the kv heads take the previous token's
 //      value [GS-EN "2. Methodology" / Value-Shift]
 //   a6 L2 normalisation per head, x / max(||x||, eps)
@@ -16,16 +21,19 @@
 //      and reduced modulo 2*pi before the fp32 sin/cos
 //      [GS-EN "2. Methodology" / RoPE Integration]
 //
-// Work split: one workgroup per (batch b, kv group g, chunk of TC tokens).
-// The group's pre-conv columns (G query heads, its key head, its value head)
-// for tokens t0-3 .. t0+TC-1 are staged in LDS with coalesced 16-byte loads
-// (the 3-token halo of the causal window comes along), together with the
-// group's taps and a cos/sin table of the chunk.  A head of d channels is
-// handled by d/4 lanes of 4 consecutive channels each, so the channel
-// convolution needs only three lane shifts and the RoPE pairs stay inside a
-// lane; the L2 norm is a reduction over the d/4 lanes.  The value head is
-// written transposed (d-major) for the attention kernel, straight from the
-// LDS tile.
+// Work split (prefill): one workgroup per (batch b, kv group g, chunk of TC
+// tokens).  The group's pre-conv columns (G query heads, its key head, its
+// value head) for tokens t0-3 .. t0+TC-1 are staged in LDS in the type the
+// down-projection wrote (fp16 in bf16 mode), every 16-byte load of a batch
+// issued before its LDS stores; the 3-token halo of the causal window comes
+// along.  A lane group of d/4 lanes takes one token row and walks every head
+// slot of the group, 4 channels per lane: the channel convolution is three
+// lane shifts, RoPE pairs stay inside a lane, the L2 norm is a reduction over
+// the d/4 lanes, and the q-k-mean finds the pre- and post-convolution values
+// of the other heads of its group in its own registers (key head first, then
+// the query heads with a running sum for the key head's mean).  The value
+// head is written transposed (d-major) for the attention kernel, straight
+// from the LDS tile.
 #include "cca_device.h"
 #include "gemm_tile.h"
 #include "cca_launch.h"
@@ -33,8 +41,6 @@
 namespace cca {
 
 static constexpr int HALO = 3;   // k_s - 1 for the largest supported k_s = 4
-
-
 
 template <typename T> struct Store4;
 template <> struct Store4<float> {
@@ -53,32 +59,47 @@ template <> struct Store4<bf16> {
   }
 };
 
+// a6 and a7 on this lane's 4 channels of one head: b / max(||b||, eps) over
+// the d/4 lanes of the head, then the rotation of the pairs (4li, 4li+1) and
+// (4li+2, 4li+3) by (cos, sin) = cs0, cs1.
 template <int D>
-__device__ __forceinline__ void mix_tail(const float *cur, int slot, int G, const MixShape &s,
-                                         float2 cs0, float2 cs1, float (&b)[4], float y[4]);
+__device__ __forceinline__ void norm_rope(const MixShape &s, float2 cs0, float2 cs1,
+                                          float (&b)[4], float y[4]) {
+  constexpr int LPU = D / 4;
+  if (s.use_norm) {
+    // 1 / max(||b||, eps) == rsqrt(max(||b||^2, eps^2))
+    const float ss = group_sum<LPU>(b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3]);
+    const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, s.eps * s.eps));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b[c] *= inv;
+  }
+  y[0] = b[0] * cs0.x - b[1] * cs0.y;
+  y[1] = b[0] * cs0.y + b[1] * cs0.x;
+  y[2] = b[2] * cs1.x - b[3] * cs1.y;
+  y[3] = b[2] * cs1.y + b[3] * cs1.x;
+}
 
-// Steps a2-a7 for one (token row r of the LDS tile, head slot) unit.  Slot
-// 0..G-1 are the group's query heads, slot G its key head.  The lane holds
-// channels 4*li .. 4*li+3.  `tile` rows are tokens (row r+HALO is the current
-// token), columns [q heads | k head | v head] of the group, CW floats wide.
-template <int D>
-__device__ __forceinline__ void mix_unit(const float *tile, int CW, int r, int slot, int G,
-                                         int li, const float (&st)[4][4], const float (&ct)[4],
-                                         const MixShape &s, float2 cs0, float2 cs1, float y[4]) {
+// a2 and a3 of one head slot at one token: `tile` rows are tokens (row `row`
+// the current one, the rows above it the earlier ones), columns [q heads | k
+// head | v head] of the group, CW elements wide; slot 0..G-1 are the query
+// heads, slot G the key head.  staps [(G+1) d][4] and ctaps [G+1][4] hold the
+// group's taps (zero past k_s / k_c).  The lane holds channels 4li .. 4li+3.
+template <int D, typename TT>
+__device__ __forceinline__ void conv_slot(const TT *tile, int CW, int row, int slot, int li,
+                                          const float *staps, const float *ctaps, float (&b)[4]) {
   constexpr int LPU = D / 4;
   const int col = slot * D + 4 * li;
+  f32x4 u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) u[j] = ld4f<TT>(tile + (row - j) * CW + col);
   float a[4];
-  {
-    f32x4 row[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) row[j] = *reinterpret_cast<const f32x4 *>(tile + (r + HALO - j) * CW + col);
+  for (int c = 0; c < 4; ++c) {
+    const f32x4 t = *reinterpret_cast<const f32x4 *>(staps + (col + c) * 4);
+    float acc = t[0] * u[0][c];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = fmaf(st[c][j], row[j][c], acc);
-      a[c] = acc;
-    }
+    for (int j = 1; j < 4; ++j) acc = fmaf(t[j], u[j][c], acc);
+    a[c] = acc;
   }
   // values of the three channels below this lane's first one (previous lane;
   // zero for the head's first lane)
@@ -93,54 +114,65 @@ __device__ __forceinline__ void mix_unit(const float *tile, int CW, int r, int s
     p3 = __shfl_up(a[3], 1, LPU);
   }
   if (li == 0) p1 = p2 = p3 = 0.f;
-  const float w0 = ct[0], w1 = ct[1], w2 = ct[2], w3 = ct[3];
-  float b[4];
-  b[0] = w0 * a[0] + w1 * p3 + w2 * p2 + w3 * p1;
-  b[1] = w0 * a[1] + w1 * a[0] + w2 * p3 + w3 * p2;
-  b[2] = w0 * a[2] + w1 * a[1] + w2 * a[0] + w3 * p3;
-  b[3] = w0 * a[3] + w1 * a[2] + w2 * a[1] + w3 * a[0];
-  mix_tail<D>(tile + (r + HALO) * CW + 4 * li, slot, G, s, cs0, cs1, b, y);
+  const f32x4 w = *reinterpret_cast<const f32x4 *>(ctaps + slot * 4);
+  b[0] = w[0] * a[0] + w[1] * p3 + w[2] * p2 + w[3] * p1;
+  b[1] = w[0] * a[1] + w[1] * a[0] + w[2] * p3 + w[3] * p2;
+  b[2] = w[0] * a[2] + w[1] * a[1] + w[2] * a[0] + w[3] * p3;
+  b[3] = w[0] * a[3] + w[1] * a[2] + w[2] * a[1] + w[3] * a[0];
 }
 
-// Steps a4, a6, a7 after the channel conv: b (the channel-conv output of this
-// lane's 4 channels) plus the q-k-mean skip from the pre-conv row `cur` (the
-// token's tile row, offset to this lane's channels), normalised and rotated.
-template <int D>
-__device__ __forceinline__ void mix_tail(const float *cur, int slot, int G, const MixShape &s,
-                                         float2 cs0, float2 cs1, float (&b)[4], float y[4]) {
-  constexpr int LPU = D / 4;
-  if (s.use_mean) {
-    const f32x4 kpre = *reinterpret_cast<const f32x4 *>(cur + G * D);
-    if (slot < G) {
-      const f32x4 qpre = *reinterpret_cast<const f32x4 *>(cur + slot * D);
+// a4, a6, a7 for every head slot of one kv group at one token, this lane's 4
+// channels: the key head (slot G) first, then the G query heads.
+//   conv(slot, b)  the slot's channel-conv output b
+//   pre(slot)      the slot's pre-convolution values (f32x4)
+//   emit(slot, y)  receives the normalised, rotated result
+// s.use_mean: 0 off; 1 q += (q~ + k~)/2, k += (k~ + avg q~)/2; 2 q += (q~ + b_q
+// + k~ + b_k)/4, k += (k~ + b_k + avg q~ + avg b_q)/4.
+template <int D, typename ConvFn, typename PreFn, typename EmitFn>
+__device__ __forceinline__ void mix_row(int G, const MixShape &s, float2 cs0, float2 cs1,
+                                        ConvFn &&conv, PreFn &&pre, EmitFn &&emit) {
+  const bool mean = s.use_mean != 0, post = s.use_mean == 2;
+  const float coef = post ? 0.25f : 0.5f;
+  float bk[4];
+  conv(G, bk);
+  float sk[4] = {0.f, 0.f, 0.f, 0.f}, sq[4] = {0.f, 0.f, 0.f, 0.f};
+  if (mean) {
+    const f32x4 kp = pre(G);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) b[c] += 0.5f * (qpre[c] + kpre[c]);
-    } else {
-      f32x4 m = *reinterpret_cast<const f32x4 *>(cur);
-      for (int h = 1; h < G; ++h) m += *reinterpret_cast<const f32x4 *>(cur + h * D);
-      const float invg = 1.f / (float)G;
+    for (int c = 0; c < 4; ++c) sk[c] = post ? kp[c] + bk[c] : kp[c];
+  }
+  for (int h = 0; h < G; ++h) {
+    float b[4];
+    conv(h, b);
+    if (mean) {
+      const f32x4 qp = pre(h);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) b[c] += 0.5f * (kpre[c] + m[c] * invg);
+      for (int c = 0; c < 4; ++c) {
+        const float own = post ? qp[c] + b[c] : qp[c];
+        sq[c] += own;
+        b[c] += coef * (own + sk[c]);
+      }
     }
+    float y[4];
+    norm_rope<D>(s, cs0, cs1, b, y);
+    emit(h, y);
   }
-  if (s.use_norm) {
-    // 1 / max(||b||, eps) == rsqrt(max(||b||^2, eps^2))
-    const float ss = group_sum<LPU>(b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3]);
-    const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, s.eps * s.eps));
+  if (mean) {
+    const float invg = 1.f / (float)G;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) b[c] *= inv;
+    for (int c = 0; c < 4; ++c) bk[c] += coef * (sk[c] + sq[c] * invg);
   }
-  y[0] = b[0] * cs0.x - b[1] * cs0.y;
-  y[1] = b[0] * cs0.y + b[1] * cs0.x;
-  y[2] = b[2] * cs1.x - b[3] * cs1.y;
-  y[3] = b[2] * cs1.y + b[3] * cs1.x;
+  float y[4];
+  norm_rope<D>(s, cs0, cs1, bk, y);
+  emit(G, y);
 }
 
 // Group taps into LDS: seq taps [(G+1)*D][4] (q channels, then k), channel
-// taps [(G+1)][4]; taps beyond k_s / k_c are zero.
+// taps [(G+1)][4], taps beyond k_s / k_c zero; tsc [G] = tau_h * log2(e) of
+// the group's query heads (the attention kernel takes exp2-domain logits).
 template <int D>
 __device__ __forceinline__ void load_taps(const MixShape &s, const MixTaps &w, int g, float *staps,
-                                          float *ctaps) {
+                                          float *ctaps, float *tsc) {
   const int G = s.G;
   for (int c = threadIdx.x; c < (G + 1) * D; c += blockDim.x) {
     const float *src = c < G * D ? w.q_seq + (size_t)(g * G * D + c) * s.ks
@@ -153,23 +185,12 @@ __device__ __forceinline__ void load_taps(const MixShape &s, const MixTaps &w, i
 #pragma unroll
     for (int j = 0; j < 4; ++j) ctaps[c * 4 + j] = j < s.kc ? src[j] : 0.f;
   }
+  for (int h = threadIdx.x; h < G; h += blockDim.x) tsc[h] = w.tau[g * G + h] * 1.4426950408889634f;
 }
 
-// This lane's taps for head slot `slot` (channels 4*li .. 4*li+3) from the
-// LDS copies made by load_taps.
-template <int D>
-__device__ __forceinline__ void lane_taps(const float *staps, const float *ctaps, int slot, int li,
-                                          float (&st)[4][4], float (&ct)[4]) {
-  const int col = slot * D + 4 * li;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const f32x4 t = *reinterpret_cast<const f32x4 *>(staps + (col + c) * 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) st[c][j] = t[j];
-  }
-  const f32x4 t = *reinterpret_cast<const f32x4 *>(ctaps + slot * 4);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ct[j] = t[j];
+// Floats of the tap area after the tile: seq taps, channel taps, tau scales.
+__host__ __device__ inline int taps_floats(int G, int D) {
+  return (G + 1) * D * 4 + (G + 1) * 4 + (G + 3) / 4 * 4;
 }
 
 // Map a column of the group tile to its column in the qkv row.
@@ -179,194 +200,161 @@ __device__ __forceinline__ int group_col(int col, int g, int G, int D, int eq, i
   return eq + ekv + g * D + (col - (G + 1) * D);
 }
 
-// Rows of the next chunk each thread prefetches into registers (16 bytes each).
-static constexpr int MIX_PF = 8;
+// Bytes of a tile of `rows` token rows of one group (16-byte multiple).
+__host__ __device__ inline size_t tile_bytes(int rows, int G, int D, int es) {
+  return ((size_t)rows * (G + 2) * D * es + 15) / 16 * 16;
+}
 
-template <typename TQ, typename TV, int D>
+template <typename TI, typename TQ, typename TV, int D>
 __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTaps w,
-                                                              const float *__restrict__ qkv,
+                                                              const TI *__restrict__ qkv,
                                                               TQ *__restrict__ q, TQ *__restrict__ k,
                                                               TV *__restrict__ vt, StateOut st,
                                                               const float *__restrict__ r1b,
-                                                              int TC, int nchunks, int cpw,
-                                                              int nseg) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];
+                                                              float *__restrict__ bout, int TC) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char mix_smem[];
   const int G = s.G, CW = (G + 2) * D;
-  float *tile = lds;                                   // rows: tokens t0-HALO .. t0+TC-1
-  float *staps = tile + (TC + HALO) * CW;
+  TI *tile = reinterpret_cast<TI *>(mix_smem);                 // rows: tokens t0-HALO .. t0+TC-1
+  float *staps = reinterpret_cast<float *>(mix_smem + tile_bytes(TC + HALO, G, D, sizeof(TI)));
   float *ctaps = staps + (G + 1) * D * 4;
-  float2 *rot = reinterpret_cast<float2 *>(ctaps + ((G + 1) * 4 + 3) / 4 * 4);
+  float *tsc = ctaps + (G + 1) * 4;
 
   const int tid = threadIdx.x;
-  const int seg = blockIdx.x % nseg;
-  const int bg = blockIdx.x / nseg;
+  const int nchunks = s.Tp / TC;
+  const int chunk = blockIdx.x % nchunks, bg = blockIdx.x / nchunks;
   const int g = bg % s.Hkv, b = bg / s.Hkv;
-  const int c_beg = seg * cpw, c_end = min(nchunks, c_beg + cpw);
+  const int t0 = chunk * TC;
   const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
   const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
   const int vcol = (G + 1) * D;
+  const TI *src = qkv + (size_t)b * s.T * N;
 
-  // each thread owns one 16-byte column chunk of the group and walks rows
-  // with a fixed stride (CW/4 <= 256 chunks per row)
-  const int cpr = CW / 4;
-  const int rstep = 256 / cpr;
-  const int my_col = (tid % cpr) * 4, my_row0 = tid / cpr;
-  const bool col_active = my_row0 < rstep;
-  const float *src_col = qkv + group_col(my_col, g, G, D, eq, ekv) + (size_t)b * s.T * N;
-  auto row_load = [&](int tok) {
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (tok >= 0 && tok < s.T) v = *reinterpret_cast<const f32x4 *>(src_col + (size_t)tok * N);
-    return v;
-  };
-
-  load_taps<D>(s, w, g, staps, ctaps);
-
-  // first chunk: halo and rows straight into LDS
+  // the tile, in batches of 8 16-byte chunks per thread; tokens outside
+  // [0, T) read as zero
   {
-    const int t0 = c_beg * TC;
-    for (int r0 = my_row0; r0 < TC + HALO; r0 += rstep * MIX_PF) {
-      f32x4 v[MIX_PF];
+    constexpr int EPC = 16 / (int)sizeof(TI), NB = 8;
+    const int cpr = CW / EPC, total = (TC + HALO) * cpr;
+    for (int e0 = 0; e0 < total; e0 += 256 * NB) {
+      u32x4 v[NB];
 #pragma unroll
-      for (int u = 0; u < MIX_PF; ++u) {
-        const int r = r0 + rstep * u;
-        v[u] = (col_active && r < TC + HALO) ? row_load(t0 - HALO + r) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < NB; ++u) {
+        const int e = e0 + tid + 256 * u;
+        const int r = e / cpr, cc = e - r * cpr, tok = t0 - HALO + r;
+        v[u] = zero_u32x4();
+        if (e < total && tok >= 0 && tok < s.T)
+          v[u] = ld16(src + (size_t)tok * N + group_col(cc * EPC, g, G, D, eq, ekv));
       }
 #pragma unroll
-      for (int u = 0; u < MIX_PF; ++u) {
-        const int r = r0 + rstep * u;
-        if (col_active && r < TC + HALO) *reinterpret_cast<f32x4 *>(tile + r * CW + my_col) = v[u];
+      for (int u = 0; u < NB; ++u) {
+        const int e = e0 + tid + 256 * u;
+        if (e < total) {
+          const int r = e / cpr, cc = e - r * cpr;
+          st16(tile + r * CW + cc * EPC, v[u]);
+        }
       }
     }
   }
+  load_taps<D>(s, w, g, staps, ctaps, tsc);
+  __syncthreads();
 
+  // one token row per lane group, every head slot of the group
   constexpr int LPU = D / 4;
   const int upp = 256 / LPU;
   const int li = tid % LPU, ui = tid / LPU;
-  f32x4 pf[MIX_PF];
-
-  for (int ch = c_beg; ch < c_end; ++ch) {
-    const int t0 = ch * TC;
-    // rotation table of the chunk: one double multiply and reduction per entry
-    for (int e = tid; e < TC * (D / 2); e += 256)
-      rot[e] = rope_cs_theta(t0 + e / (D / 2), s.theta[e % (D / 2)], s.rope_base);
-    __syncthreads();
-
-    // prefetch the next chunk's rows; their latency overlaps this chunk's math
-    const bool more = ch + 1 < c_end;
-    if (more) {
+  TV *kcache = reinterpret_cast<TV *>(st.k_cache);
+  for (int r = ui; r < TC; r += upp) {
+    const int tok = t0 + r;
+    const float2 cs0 = rope_cs_theta(tok, s.theta[2 * li], s.rope_base);
+    const float2 cs1 = rope_cs_theta(tok, s.theta[2 * li + 1], s.rope_base);
+    const TI *cur = tile + (r + HALO) * CW + 4 * li;
+    auto pre = [&](int slot) { return ld4f<TI>(cur + slot * D); };
+    auto emit = [&](int slot, float *y) {
+      if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
+      if (slot < G) {
+        const float sc = tsc[slot];
 #pragma unroll
-      for (int u = 0; u < MIX_PF; ++u) {
-        const int r = my_row0 + rstep * u;
-        pf[u] = (col_active && r < TC) ? row_load(t0 + TC + r) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 4; ++c) y[c] *= sc;
+        Store4<TQ>::st(q + ((size_t)(b * s.Hq + g * G + slot) * s.Tp + tok) * D + 4 * li, y);
+      } else {
+        Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
+        size_t row;
+        if (kcache && tok < s.T && cache_row_store(st, b, s.Hkv, g, tok, &row))
+          Store4<TV>::st(kcache + row * D + 4 * li, y);
       }
+    };
+    if (r1b) {
+      // grouped channel conv: b comes from the MFMA kernel's output rows
+      const float *brow = r1b + (size_t)(b * s.T + min(tok, s.T - 1)) * (eq + ekv) + 4 * li;
+      auto conv = [&](int slot, float (&bb)[4]) {
+        const f32x4 v = tok < s.T ? *reinterpret_cast<const f32x4 *>(
+                                        brow + (slot < G ? (g * G + slot) * D : eq + g * D))
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bb[c] = v[c];
+      };
+      mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
+    } else {
+      auto conv = [&](int slot, float (&bb)[4]) {
+        conv_slot<D, TI>(tile, CW, r + HALO, slot, li, staps, ctaps, bb);
+        if (bout && tok < s.T)
+          *reinterpret_cast<f32x4 *>(bout + (size_t)(b * s.T + tok) * (eq + ekv) +
+                                     (slot < G ? (g * G + slot) * D : eq + g * D) + 4 * li) =
+              f32x4{bb[0], bb[1], bb[2], bb[3]};
+      };
+      mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
     }
+  }
 
-    // query and key heads, slot-major so each lane keeps its head's taps in
-    // registers: slot 0..G-1 are the query heads, slot G the key head
-    for (int slot = 0; slot <= G; ++slot) {
-      float stp[4][4], ctp[4];
-      lane_taps<D>(staps, ctaps, slot, li, stp, ctp);
-      const float qscale = slot < G ? w.tau[g * G + slot] * 1.4426950408889634f : 1.f;
-      for (int r = ui; r < TC; r += upp) {
-        const int tok = t0 + r;
-        float y[4];
-        if (r1b) {
-          // grouped channel conv: b comes from the MFMA kernel's output rows
-          float bb[4] = {0.f, 0.f, 0.f, 0.f};
-          if (tok < s.T) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(
-                r1b + (size_t)(b * s.T + tok) * (eq + ekv) + (slot < G ? (g * G + slot) * D : eq + g * D) + 4 * li);
+  // value head, transposed: vt[b, g, dd, perm(t)] for the chunk's tokens
+  for (int e = tid; e < D * (TC / 8); e += 256) {
+    const int dd = e / (TC / 8), grp = e % (TC / 8);
+    float vals[8];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) bb[c] = v[c];
-          }
-          mix_tail<D>(tile + (r + HALO) * CW + 4 * li, slot, G, s, rot[r * (D / 2) + 2 * li],
-                      rot[r * (D / 2) + 2 * li + 1], bb, y);
-        } else {
-          mix_unit<D>(tile, CW, r, slot, G, li, stp, ctp, s, rot[r * (D / 2) + 2 * li],
-                      rot[r * (D / 2) + 2 * li + 1], y);
-        }
-        if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
-        if (slot < G) {
-          // the attention kernel takes q scaled by tau_h * log2(e) (exp2-domain logits)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) y[c] *= qscale;
-          Store4<TQ>::st(q + ((size_t)(b * s.Hq + g * G + slot) * s.Tp + tok) * D + 4 * li, y);
-        } else {
-          Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
-          if (st.k_cache && tok < s.T)
-            Store4<TV>::st(reinterpret_cast<TV *>(st.k_cache) + cache_row(st, b, s.Hkv, g, tok) * D +
-                               4 * li, y);
-        }
-      }
+    for (int jj = 0; jj < 8; ++jj) {
+      const int tl = vt_perm(8 * grp + jj);
+      vals[jj] = (t0 + tl < s.T) ? to_f32(tile[(tl + HALO - shifted) * CW + vcol + dd]) : 0.f;
     }
-
-    // value head, transposed: vt[b, g, dd, perm(t)] for the chunk's tokens
-    for (int e = tid; e < D * (TC / 8); e += 256) {
-      const int dd = e / (TC / 8), grp = e % (TC / 8);
-      float vals[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int tl = vt_perm(8 * grp + jj);
-        vals[jj] = (t0 + tl < s.T) ? tile[(tl + HALO - shifted) * CW + vcol + dd] : 0.f;
-      }
-      TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + dd) * s.Tp + t0 + 8 * grp;
-      Store4<TV>::st(dst, vals);
-      Store4<TV>::st(dst + 4, vals + 4);
-    }
-    if (st.v_cache) {
-      for (int e = tid; e < TC * (D / 4); e += 256) {
-        const int r = e / (D / 4), c4 = e % (D / 4), tok = t0 + r;
-        if (tok >= s.T) continue;
-        const float *src = tile + (r + HALO - shifted) * CW + vcol + 4 * c4;
-        Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) + cache_row(st, b, s.Hkv, g, tok) * D +
-                           4 * c4, src);
-      }
-    }
-    __syncthreads();                                 // every read of this tile is done
-
-    if (more) {
-      // carry the halo (last HALO rows) to the top, then the prefetched rows
-      for (int e = tid; e < HALO * CW / 4; e += 256) {
-        const int r = e / (CW / 4), c4 = (e % (CW / 4)) * 4;
-        *reinterpret_cast<f32x4 *>(tile + r * CW + c4) =
-            *reinterpret_cast<const f32x4 *>(tile + (TC + r) * CW + c4);
-      }
-      __syncthreads();                               // halo rows read before they are overwritten
-#pragma unroll
-      for (int u = 0; u < MIX_PF; ++u) {
-        const int r = my_row0 + rstep * u;
-        if (col_active && r < TC) *reinterpret_cast<f32x4 *>(tile + (HALO + r) * CW + my_col) = pf[u];
-      }
-      // the rotation table is rewritten after the next barrier-protected use
+    TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + dd) * s.Tp + t0 + 8 * grp;
+    Store4<TV>::st(dst, vals);
+    Store4<TV>::st(dst + 4, vals + 4);
+  }
+  if (st.v_cache) {
+    for (int e = tid; e < TC * (D / 4); e += 256) {
+      const int r = e / (D / 4), c4 = e % (D / 4), tok = t0 + r;
+      if (tok >= s.T) continue;
+      size_t row;
+      if (!cache_row_store(st, b, s.Hkv, g, tok, &row)) continue;
+      const f32x4 v = ld4f<TI>(tile + (r + HALO - shifted) * CW + vcol + 4 * c4);
+      const float vv[4] = {v[0], v[1], v[2], v[3]};
+      Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) + row * D + 4 * c4, vv);
     }
   }
 
   // decode state after the last token: conv window (k_s - 1 pre-conv rows,
   // plus k_c - 1 under the grouped channel conv) and value-shift state
-  if (seg == 0) {
+  if (chunk == 0) {
     const int ks1 = s.ks - 1 + (s.grouped ? s.kc - 1 : 0);
-    const float *qb = qkv + (size_t)b * s.T * N;
     if (st.conv_q)
       for (int e = tid; e < ks1 * G * D; e += 256) {
         const int sl = e / (G * D), c = e % (G * D), tok = s.T - ks1 + sl;
-        const float v = tok >= 0 ? qb[(size_t)tok * N + g * G * D + c] : 0.f;
+        const float v = tok >= 0 ? to_f32(src[(size_t)tok * N + g * G * D + c]) : 0.f;
         reinterpret_cast<TV *>(st.conv_q)[(size_t)(b * ks1 + sl) * eq + g * G * D + c] = from_f32<TV>(v);
       }
     if (st.conv_k)
       for (int e = tid; e < ks1 * D; e += 256) {
         const int sl = e / D, c = e % D, tok = s.T - ks1 + sl;
-        const float v = tok >= 0 ? qb[(size_t)tok * N + eq + g * D + c] : 0.f;
+        const float v = tok >= 0 ? to_f32(src[(size_t)tok * N + eq + g * D + c]) : 0.f;
         reinterpret_cast<TV *>(st.conv_k)[(size_t)(b * ks1 + sl) * ekv + g * D + c] = from_f32<TV>(v);
       }
     if (st.vshift && shifted)
       for (int c = tid; c < D; c += 256)
         reinterpret_cast<TV *>(st.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
-            from_f32<TV>(qb[(size_t)(s.T - 1) * N + eq + ekv + g * D + c]);
+            from_f32<TV>(to_f32(src[(size_t)(s.T - 1) * N + eq + ekv + g * D + c]));
   }
 }
 
 // m = s.T new tokens per sequence at positions L .. L+m-1 (L = lens[b] when
-// lens is given, clamped to [0, L]).  One workgroup per (b, g); the tile
+// lens is given, clamped to [0, L]).  One workgroup per (b, g); the fp32 tile
 // holds tokens L-3 .. L+m-1: three rows from the carried window, then the m
 // new rows from the down-projection.  All state reads finish before the
 // barrier, so state_out may alias state_in.
@@ -377,13 +365,13 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
                                                              const int *__restrict__ lens,
                                                              StateOut in, StateOut out,
                                                              float *__restrict__ qout) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];
+  extern __shared__ __attribute__((aligned(16))) unsigned char mix_smem[];
   const int G = s.G, CW = (G + 2) * D;
   const int m = s.T, R = 3 + m;
-  float *tile = lds;                               // R rows
-  float *staps = tile + R * CW;
+  float *tile = reinterpret_cast<float *>(mix_smem);    // R rows
+  float *staps = reinterpret_cast<float *>(mix_smem + tile_bytes(R, G, D, 4));
   float *ctaps = staps + (G + 1) * D * 4;
-  float2 *rot = reinterpret_cast<float2 *>(ctaps + ((G + 1) * 4 + 3) / 4 * 4);
+  float *tsc = ctaps + (G + 1) * 4;
 
   const int tid = threadIdx.x;
   const int g = blockIdx.x % s.Hkv, b = blockIdx.x / s.Hkv;
@@ -421,9 +409,7 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
       if (e < R * CW) tile[e] = v[u];
     }
   }
-  load_taps<D>(s, w, g, staps, ctaps);
-  for (int e = tid; e < m * (D / 2); e += 256)
-    rot[e] = rope_cs_theta(L + e / (D / 2), s.theta[e % (D / 2)], s.rope_base);
+  load_taps<D>(s, w, g, staps, ctaps, tsc);
   __syncthreads();
 
   constexpr int LPU = D / 4;
@@ -431,28 +417,35 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
   const int li = tid % LPU, ui = tid / LPU;
   TV *kc = reinterpret_cast<TV *>(in.k_cache);
   TV *vc = reinterpret_cast<TV *>(in.v_cache);
-  // units: (new token j, head slot), slot 0..G-1 the query heads, G the key head
-  for (int u0 = 0; u0 < m * (G + 1); u0 += upp) {
-    const int unit = u0 + ui;
-    const bool active = unit < m * (G + 1);
-    const int j = active ? unit / (G + 1) : 0, slot = active ? unit % (G + 1) : 0;
-    float stp[4][4], ctp[4];
-    lane_taps<D>(staps, ctaps, slot, li, stp, ctp);
-    float y[4];
-    mix_unit<D>(tile, CW, j, slot, G, li, stp, ctp, s, rot[j * (D / 2) + 2 * li],
-                rot[j * (D / 2) + 2 * li + 1], y);
-    if (!active) continue;
-    if (slot < G) {
-      Store4<float>::st(qout + ((size_t)(b * m + j) * s.Hq + g * G + slot) * D + 4 * li, y);
-    } else {
-      Store4<TV>::st(kc + cache_row(in, b, s.Hkv, g, L + j) * D + 4 * li, y);
-    }
+  // one new token per lane group; groups past the last token compute on row
+  // 0 and store nothing
+  for (int j0 = 0; j0 < m; j0 += upp) {
+    const int j = j0 + ui;
+    const bool active = j < m;
+    const int jr = active ? j : 0;
+    const float2 cs0 = rope_cs_theta(L + jr, s.theta[2 * li], s.rope_base);
+    const float2 cs1 = rope_cs_theta(L + jr, s.theta[2 * li + 1], s.rope_base);
+    const float *cur = tile + (3 + jr) * CW + 4 * li;
+    auto conv = [&](int slot, float (&bb)[4]) {
+      conv_slot<D, float>(tile, CW, 3 + jr, slot, li, staps, ctaps, bb);
+    };
+    auto pre = [&](int slot) { return ld4f<float>(cur + slot * D); };
+    auto emit = [&](int slot, float *y) {
+      if (!active) return;
+      size_t row;
+      if (slot < G)
+        Store4<float>::st(qout + ((size_t)(b * m + j) * s.Hq + g * G + slot) * D + 4 * li, y);
+      else if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
+        Store4<TV>::st(kc + row * D + 4 * li, y);
+    };
+    mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
   }
   // value rows of the new tokens into the cache
   for (int e = tid; e < m * (D / 4); e += 256) {
     const int j = e / (D / 4), c4 = e % (D / 4);
-    Store4<TV>::st(vc + cache_row(in, b, s.Hkv, g, L + j) * D + 4 * c4,
-                   tile + (3 + j - shifted) * CW + (G + 1) * D + 4 * c4);
+    size_t row;
+    if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
+      Store4<TV>::st(vc + row * D + 4 * c4, tile + (3 + j - shifted) * CW + (G + 1) * D + 4 * c4);
   }
   // rolled state: slot sl holds token L + m - ks1 + sl = tile row m + 3 - ks1 + sl
   TV *oq = reinterpret_cast<TV *>(out.conv_q);
@@ -477,7 +470,7 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
 // new rows, computes a (the sequence conv) for tokens L-k_c+1 .. L+m-1 into
 // LDS, then one thread per output forms b = sum_j W[h, i, j, :] . a[t - j]
 // on the VALU (one (sequence, group) holds at most a few thousand of them)
-// into LDS, and each (new token, head) unit finishes with mix_tail.  All state reads
+// into LDS, and each (new token) row finishes with mix_row.  All state reads
 // finish before the first barrier, so state_out may alias state_in.
 template <typename TV, int D>
 __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
@@ -492,7 +485,7 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
   const int R = Wt + m, AR = kc1 + m;
   float *tile = lds;                     // [R][CW]: rows 0..Wt-1 carried, then the new tokens
   float *at = tile + R * CW;             // [AR][QK]: a of tokens L-kc1 .. L+m-1
-  float2 *rot = reinterpret_cast<float2 *>(at + AR * QK);   // [m][D/2], then b [m][QK]
+  float *bt = at + AR * QK;              // [m][QK]: b of the new tokens
 
   const int tid = threadIdx.x;
   const int g = blockIdx.x % s.Hkv, b = blockIdx.x / s.Hkv;
@@ -518,8 +511,6 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
     }
     tile[e] = v;
   }
-  for (int e = tid; e < m * (D / 2); e += 256)
-    rot[e] = rope_cs_theta(L + e / (D / 2), s.theta[e % (D / 2)], s.rope_base);
   __syncthreads();
 
   // a of token L - kc1 + r' is tile row Wt - kc1 + r'; its k_s inputs reach
@@ -536,8 +527,7 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
 
   // b of every (new token j, head slot, channel i): one thread per output,
   // a dot product of the row W[h, i, :, :] (k_c * d contiguous floats) with
-  // the a rows of the k_c lags; results to LDS for the per-head tails below
-  float *bt = reinterpret_cast<float *>(rot + m * (D / 2));
+  // the a rows of the k_c lags
   for (int e = tid; e < m * QK; e += 256) {
     const int j = e / QK, col = e % QK, slot = col / D, i = col % D;
     const float *wrow = (slot < G ? dense_q + (size_t)(g * G + slot) * D * s.kc * D
@@ -561,26 +551,34 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
   const int li = tid % LPU, ui = tid / LPU;
   TV *kc = reinterpret_cast<TV *>(in.k_cache);
   TV *vc = reinterpret_cast<TV *>(in.v_cache);
-  for (int u0 = 0; u0 < m * (G + 1); u0 += upp) {
-    const int unit = u0 + ui;
-    const bool active = unit < m * (G + 1);
-    const int j = active ? unit / (G + 1) : 0, slot = active ? unit % (G + 1) : 0;
-    const f32x4 bv = *reinterpret_cast<const f32x4 *>(bt + j * QK + slot * D + 4 * li);
-    float bb[4] = {bv[0], bv[1], bv[2], bv[3]};
-    float y[4];
-    mix_tail<D>(tile + (Wt + j) * CW + 4 * li, slot, G, s, rot[j * (D / 2) + 2 * li],
-                rot[j * (D / 2) + 2 * li + 1], bb, y);
-    if (!active) continue;
-    if (slot < G) {
-      Store4<float>::st(qout + ((size_t)(b * m + j) * s.Hq + g * G + slot) * D + 4 * li, y);
-    } else {
-      Store4<TV>::st(kc + cache_row(in, b, s.Hkv, g, L + j) * D + 4 * li, y);
-    }
+  for (int j0 = 0; j0 < m; j0 += upp) {
+    const int j = j0 + ui;
+    const bool active = j < m;
+    const int jr = active ? j : 0;
+    const float2 cs0 = rope_cs_theta(L + jr, s.theta[2 * li], s.rope_base);
+    const float2 cs1 = rope_cs_theta(L + jr, s.theta[2 * li + 1], s.rope_base);
+    const float *cur = tile + (Wt + jr) * CW + 4 * li;
+    auto conv = [&](int slot, float (&bb)[4]) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(bt + jr * QK + slot * D + 4 * li);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bb[c] = v[c];
+    };
+    auto pre = [&](int slot) { return ld4f<float>(cur + slot * D); };
+    auto emit = [&](int slot, float *y) {
+      if (!active) return;
+      size_t row;
+      if (slot < G)
+        Store4<float>::st(qout + ((size_t)(b * m + j) * s.Hq + g * G + slot) * D + 4 * li, y);
+      else if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
+        Store4<TV>::st(kc + row * D + 4 * li, y);
+    };
+    mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
   }
   for (int e = tid; e < m * (D / 4); e += 256) {
     const int j = e / (D / 4), c4 = e % (D / 4);
-    Store4<TV>::st(vc + cache_row(in, b, s.Hkv, g, L + j) * D + 4 * c4,
-                   tile + (Wt + j - shifted) * CW + QK + 4 * c4);
+    size_t row;
+    if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
+      Store4<TV>::st(vc + row * D + 4 * c4, tile + (Wt + j - shifted) * CW + QK + 4 * c4);
   }
   // rolled window: slot sl holds token L + m - W + sl = tile row Wt + m - W + sl
   TV *oq = reinterpret_cast<TV *>(out.conv_q);
@@ -638,8 +636,8 @@ __global__ __launch_bounds__(256, 1) void downproj_mix_kernel(MixShape s, MixTap
   constexpr int TM = BM / 64, TN = BN / 64;
   constexpr int RING = STAGES * (BM + BN) * 2 * BK;
   constexpr int TILE_F = (BM + HALO) * CW;
-  constexpr int TAPS_F = (G + 1) * D * 4 + ((G + 1) * 4 + 3) / 4 * 4;
-  constexpr int EPI = (TILE_F + TAPS_F) * 4 + BM * (D / 2) * 8;
+  constexpr int TAPS_F = (G + 1) * D * 4 + (G + 1) * 4 + 4;
+  constexpr int EPI = (TILE_F + TAPS_F) * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[RING > EPI ? RING : EPI];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -660,7 +658,7 @@ __global__ __launch_bounds__(256, 1) void downproj_mix_kernel(MixShape s, MixTap
   float *tile = reinterpret_cast<float *>(smem);    // rows: tokens t0-HALO .. t0+BM-1
   float *staps = tile + TILE_F;
   float *ctaps = staps + (G + 1) * D * 4;
-  float2 *rot = reinterpret_cast<float2 *>(staps + TAPS_F);
+  float *tsc = ctaps + (G + 1) * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -674,32 +672,33 @@ __global__ __launch_bounds__(256, 1) void downproj_mix_kernel(MixShape s, MixTap
     const int r = e / CW, c = e % CW;
     tile[e] = tt > 0 ? halo[((size_t)mt * HALO + r) * N + group_col(c, g, G, D, eq, ekv)] : 0.f;
   }
-  load_taps<D>(s, w, g, staps, ctaps);
-  for (int e = tid; e < BM * (D / 2); e += 256)
-    rot[e] = rope_cs_theta(t0 + e / (D / 2), s.theta[e % (D / 2)], s.rope_base);
+  load_taps<D>(s, w, g, staps, ctaps, tsc);
   __syncthreads();
 
   // the mixing of convmix_prefill_kernel on the tile's rows
   constexpr int LPU = D / 4;
   const int upp = 256 / LPU;
   const int li = tid % LPU, ui = tid / LPU;
-  for (int slot = 0; slot <= G; ++slot) {
-    float stp[4][4], ctp[4];
-    lane_taps<D>(staps, ctaps, slot, li, stp, ctp);
-    const float qscale = slot < G ? w.tau[g * G + slot] * 1.4426950408889634f : 1.f;
-    for (int r = ui; r < BM; r += upp) {
-      const int tok = t0 + r;
-      float y[4];
-      mix_unit<D>(tile, CW, r, slot, G, li, stp, ctp, s, rot[r * (D / 2) + 2 * li],
-                  rot[r * (D / 2) + 2 * li + 1], y);
+  for (int r = ui; r < BM; r += upp) {
+    const int tok = t0 + r;
+    const float2 cs0 = rope_cs_theta(tok, s.theta[2 * li], s.rope_base);
+    const float2 cs1 = rope_cs_theta(tok, s.theta[2 * li + 1], s.rope_base);
+    const float *cur = tile + (r + HALO) * CW + 4 * li;
+    auto conv = [&](int slot, float (&bb)[4]) {
+      conv_slot<D, float>(tile, CW, r + HALO, slot, li, staps, ctaps, bb);
+    };
+    auto pre = [&](int slot) { return ld4f<float>(cur + slot * D); };
+    auto emit = [&](int slot, float *y) {
       if (slot < G) {
+        const float sc = tsc[slot];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) y[c] *= qscale;
+        for (int c = 0; c < 4; ++c) y[c] *= sc;
         Store4<TQ>::st(q + ((size_t)(b * s.Hq + g * G + slot) * s.Tp + tok) * D + 4 * li, y);
       } else {
         Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
       }
-    }
+    };
+    mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
   }
   // value head, transposed: vt[b, g, dd, perm(t)]
   const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
@@ -753,57 +752,53 @@ template hipError_t launch_downproj_mix<bf16, bf16>(const MixShape &, const MixT
                                                     const bf16 *, int, void *, bf16 *, bf16 *,
                                                     bf16 *, hipStream_t);
 
-static size_t mix_lds_bytes(int rows, int G, int D, int TC) {
-  const int CW = (G + 2) * D;
-  size_t f = (size_t)rows * CW + (size_t)(G + 1) * D * 4 + ((G + 1) * 4 + 3) / 4 * 4;
-  return f * 4 + (size_t)TC * (D / 2) * 8;
+// LDS of the prefill kernel for chunks of TC tokens, es-byte tile elements.
+static size_t mix_lds_bytes(int TC, int G, int D, int es) {
+  return tile_bytes(TC + HALO, G, D, es) + (size_t)taps_floats(G, D) * 4;
 }
 
-// Tokens per chunk: 32 when the tile fits in LDS, else 16.
-static int mix_chunk(int G, int D) { return mix_lds_bytes(32 + HALO, G, D, 32) <= 65536 ? 32 : 16; }
+// Tokens per workgroup: the largest of 64 / 32 / 16 whose tile stays within
+// 40 KiB (several workgroups per CU keep many rows in flight).
+static int mix_chunk(int G, int D, int es) {
+  for (int tc = 64; tc > 16; tc /= 2)
+    if (mix_lds_bytes(tc, G, D, es) <= 40 * 1024) return tc;
+  return 16;
+}
 
-// Whether a thread's share of one chunk's rows fits the prefetch registers;
-// otherwise each workgroup handles a single chunk and nothing is prefetched.
-static bool mix_prefetch_fits(int G, int D, int TC) {
-  const int cpr = (G + 2) * D / 4, rstep = 256 / cpr;
-  return (TC + rstep - 1) / rstep <= MIX_PF;
+static size_t decode_lds_bytes(int rows, int G, int D) {
+  return tile_bytes(rows, G, D, 4) + (size_t)taps_floats(G, D) * 4;
 }
 
 bool convmix_decode_fits(int G, int d, int m) {
-  return m >= 1 && mix_lds_bytes(3 + m, G, d, m) <= 65536;
+  return m >= 1 && decode_lds_bytes(3 + m, G, d) <= 65536;
 }
 
-bool convmix_fits(int G, int d) {
-  return (G + 2) * d / 4 <= 256 && mix_lds_bytes(16 + HALO, G, d, 16) <= 65536;
+bool convmix_fits(int G, int d, int es) {
+  return mix_lds_bytes(16, G, d, es) <= 65536 && convmix_decode_fits(G, d, 1);
 }
 
-template <typename TQ, typename TV, int D>
-static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
+template <typename TI, typename TQ, typename TV, int D>
+static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const TI *qkv, TQ *q,
                                     TQ *k, TV *vt, const StateOut &st, const float *r1b,
-                                    hipStream_t stream) {
-  const int TC = mix_chunk(s.G, D);
-  const int nchunks = s.Tp / TC;
-  // about 4 chunks per workgroup (the prefetch of chunk i+1 hides behind the
-  // mixing of chunk i), at least ~512 workgroups when the work allows
-  const int streams = s.B * s.Hkv;
-  int cpw = (nchunks / 4 > 0 && mix_prefetch_fits(s.G, D, TC)) ? 4 : 1;
-  while (cpw > 1 && (long long)streams * ((nchunks + cpw - 1) / cpw) < 512) --cpw;
-  const int nseg = (nchunks + cpw - 1) / cpw;
-  const size_t lds = mix_lds_bytes(TC + HALO, s.G, D, TC);
-  hipLaunchKernelGGL((convmix_prefill_kernel<TQ, TV, D>), dim3(streams * nseg), dim3(256), lds,
-                     stream, s, w, qkv, q, k, vt, st, r1b, TC, nchunks, cpw, nseg);
+                                    float *bout, hipStream_t stream) {
+  const int TC = mix_chunk(s.G, D, (int)sizeof(TI));
+  const long long grid = (long long)s.B * s.Hkv * (s.Tp / TC);
+  if (grid >= (1ll << 31)) return hipErrorInvalidValue;
+  const size_t lds = mix_lds_bytes(TC, s.G, D, (int)sizeof(TI));
+  hipLaunchKernelGGL((convmix_prefill_kernel<TI, TQ, TV, D>), dim3((unsigned)grid), dim3(256), lds,
+                     stream, s, w, qkv, q, k, vt, st, r1b, bout, TC);
   return hipGetLastError();
 }
 
-template <typename TQ, typename TV>
-hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const float *qkv, TQ *q,
+template <typename TI, typename TQ, typename TV>
+hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const TI *qkv, TQ *q,
                                   TQ *k, TV *vt, const StateOut &st, hipStream_t stream,
-                                  const float *r1b) {
+                                  const float *r1b, float *bout) {
   switch (s.d) {
-    case 16: return convmix_prefill_d<TQ, TV, 16>(s, w, qkv, q, k, vt, st, r1b, stream);
-    case 32: return convmix_prefill_d<TQ, TV, 32>(s, w, qkv, q, k, vt, st, r1b, stream);
-    case 64: return convmix_prefill_d<TQ, TV, 64>(s, w, qkv, q, k, vt, st, r1b, stream);
-    case 128: return convmix_prefill_d<TQ, TV, 128>(s, w, qkv, q, k, vt, st, r1b, stream);
+    case 16: return convmix_prefill_d<TI, TQ, TV, 16>(s, w, qkv, q, k, vt, st, r1b, bout, stream);
+    case 32: return convmix_prefill_d<TI, TQ, TV, 32>(s, w, qkv, q, k, vt, st, r1b, bout, stream);
+    case 64: return convmix_prefill_d<TI, TQ, TV, 64>(s, w, qkv, q, k, vt, st, r1b, bout, stream);
+    case 128: return convmix_prefill_d<TI, TQ, TV, 128>(s, w, qkv, q, k, vt, st, r1b, bout, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -813,7 +808,7 @@ static hipError_t convmix_decode_d(const MixShape &s, const MixTaps &w, const fl
                                    const int *lens,
                                    const StateOut &in, const StateOut &out, float *q,
                                    hipStream_t stream) {
-  const size_t lds = mix_lds_bytes(3 + s.T, s.G, D, s.T);
+  const size_t lds = decode_lds_bytes(3 + s.T, s.G, D);
   hipLaunchKernelGGL((convmix_decode_kernel<TV, D>), dim3(s.B * s.Hkv), dim3(256), lds, stream, s,
                      w, qkv, L, lens, in, out, q);
   return hipGetLastError();
@@ -835,7 +830,7 @@ hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const floa
 static size_t decode_grouped_lds_bytes(int G, int D, int m, int ks, int kc) {
   const int W = ks - 1 + kc - 1, Wt = W > 0 ? W : 1;
   return ((size_t)(Wt + m) * (G + 2) * D + (size_t)(kc - 1 + m) * (G + 1) * D +
-          (size_t)m * (G + 1) * D) * 4 + (size_t)m * (D / 2) * 8;
+          (size_t)m * (G + 1) * D) * 4;
 }
 
 bool convmix_decode_grouped_fits(int G, int d, int m, int ks, int kc) {
@@ -876,15 +871,18 @@ template hipError_t launch_convmix_decode_grouped<float>(const MixShape &, const
                                                          int, const int *, const StateOut &,
                                                          const StateOut &, float *, hipStream_t);
 
-template hipError_t launch_convmix_prefill<f16, bf16>(const MixShape &, const MixTaps &,
-                                                      const float *, f16 *, f16 *, bf16 *,
-                                                      const StateOut &, hipStream_t, const float *);
-template hipError_t launch_convmix_prefill<bf16, bf16>(const MixShape &, const MixTaps &,
-                                                       const float *, bf16 *, bf16 *, bf16 *,
-                                                       const StateOut &, hipStream_t, const float *);
-template hipError_t launch_convmix_prefill<float, float>(const MixShape &, const MixTaps &,
-                                                         const float *, float *, float *, float *,
-                                                         const StateOut &, hipStream_t, const float *);
+template hipError_t launch_convmix_prefill<f16, f16, bf16>(const MixShape &, const MixTaps &,
+                                                           const f16 *, f16 *, f16 *, bf16 *,
+                                                           const StateOut &, hipStream_t,
+                                                           const float *, float *);
+template hipError_t launch_convmix_prefill<f16, bf16, bf16>(const MixShape &, const MixTaps &,
+                                                            const f16 *, bf16 *, bf16 *, bf16 *,
+                                                            const StateOut &, hipStream_t,
+                                                            const float *, float *);
+template hipError_t launch_convmix_prefill<float, float, float>(const MixShape &, const MixTaps &,
+                                                                const float *, float *, float *,
+                                                                float *, const StateOut &,
+                                                                hipStream_t, const float *, float *);
 template hipError_t launch_convmix_decode<bf16>(const MixShape &, const MixTaps &, const float *,
                                                 int, const int *, const StateOut &, const StateOut &, float *,
                                                 hipStream_t);

@@ -564,6 +564,8 @@ hipError_t launch_gemm_tn_long_k(const bf16 *A, const bf16 *B, float *C, int M, 
 
 template hipError_t launch_gemm_nt<bf16, float>(const bf16 *, const bf16 *, float *, int, int, int,
                                                 int, int, int, hipStream_t, float *, size_t);
+template hipError_t launch_gemm_nt<bf16, f16>(const bf16 *, const bf16 *, f16 *, int, int, int,
+                                              int, int, int, hipStream_t, float *, size_t);
 template hipError_t launch_gemm_nt<bf16, bf16>(const bf16 *, const bf16 *, bf16 *, int, int, int,
                                                int, int, int, hipStream_t, float *, size_t);
 template hipError_t launch_gemm_nt<float, float>(const float *, const float *, float *, int, int,

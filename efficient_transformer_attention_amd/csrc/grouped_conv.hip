@@ -9,8 +9,8 @@
 //
 // Prefill: a dense contraction of k_c * d inputs into d outputs per (token,
 // head), so it runs on MFMA.  One workgroup per (sequence, head, 128 tokens)
-// recomputes a (the k_s-tap sequence conv of the fp32 down-projection
-// output) for its tokens and the k_c - 1 before them into LDS as fp16, stages
+// recomputes a (the k_s-tap sequence conv of the down-projection output,
+// fp16 in bf16 mode) for its tokens and the k_c - 1 before them into LDS as fp16, stages
 // the head's W as fp16 rows [i][lag-major, channel], and multiplies: row t of
 // the A operand is the k_c consecutive a rows t-k_c+1 .. t, read straight
 // from the tile (overlapping rows, no copy).  v_mfma_f32_32x32x16_f16, fp32
@@ -35,10 +35,12 @@ template <int D, bool F32>
 __global__ __launch_bounds__(256) void grouped_conv_prefill_kernel(MixShape s, MixTaps w,
                                                                    const float *__restrict__ dense_q,
                                                                    const float *__restrict__ dense_k,
-                                                                   const float *__restrict__ qkv,
+                                                                   const void *__restrict__ qkv_v,
                                                                    float *__restrict__ outb) {
   typedef GcTile<D> TL;
   typedef typename std::conditional<F32, float, f16>::type TE;
+  typedef TE TI;   // the down-projection output: fp32 in fp32 mode, fp16 in bf16 mode
+  const TI *qkv = reinterpret_cast<const TI *>(qkv_v);
   constexpr int DP = TL::DP;
   // LDS rows padded by 16 bytes (fp16) so that lanes reading the same
   // columns of consecutive rows spread over the banks
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void grouped_conv_prefill_kernel(MixShape s, M
   const int arows = GC_RB + kc - 1;                  // a of tokens t0-kc+1 .. t0+GC_RB-1
   const float *dense = is_q ? dense_q + (size_t)hh * D * kc * D : dense_k + (size_t)g * D * kc * D;
   const float *seqw = is_q ? w.q_seq + (size_t)hh * D * ks : w.k_seq + (size_t)g * D * ks;
-  const float *u0 = qkv + (size_t)b * s.T * N + colbase;
+  const TI *u0 = qkv + (size_t)b * s.T * N + colbase;
 
   // W: column K = jp * d + c of output row i holds W[h, i, kc-1-jp, c] (A
   // row t, column jp * d + c, is a[t - kc + 1 + jp, c]).  Four channels per
@@ -118,8 +120,7 @@ __global__ __launch_bounds__(256) void grouped_conv_prefill_kernel(MixShape s, M
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bool ok = k0 + kb < NA && r < arows && j < ks && t - j >= 0 && t < s.T;
-          u[kb][j] = ok ? *reinterpret_cast<const f32x4 *>(u0 + (size_t)(t - j) * N + c0)
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+          u[kb][j] = ok ? ld4f<TI>(u0 + (size_t)(t - j) * N + c0) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
 #pragma unroll
@@ -205,7 +206,7 @@ bool grouped_conv_supported(int d, bool f32) {
 
 template <int D, bool F32>
 static hipError_t gc_launch(const MixShape &s, const MixTaps &w, const float *dq, const float *dk,
-                            const float *qkv, float *outb, hipStream_t stream) {
+                            const void *qkv, float *outb, hipStream_t stream) {
   const size_t lds = gc_lds_bytes<D, F32>();
   if (lds > 65536) {   // above the default dynamic LDS limit (the fp32 mode); set on every call,
                        // so each device the library runs on gets it
@@ -222,7 +223,7 @@ static hipError_t gc_launch(const MixShape &s, const MixTaps &w, const float *dq
 }
 
 hipError_t launch_grouped_conv_prefill(const MixShape &s, const MixTaps &w, const float *dense_q,
-                                       const float *dense_k, const float *qkv, float *outb,
+                                       const float *dense_k, const void *qkv, float *outb,
                                        bool f32, hipStream_t stream) {
   if (s.kc < 1 || s.kc > 4 || s.ks < 1 || s.ks > 4) return hipErrorInvalidValue;
   switch (s.d) {

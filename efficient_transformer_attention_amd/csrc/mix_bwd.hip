@@ -33,12 +33,22 @@ namespace cca {
 // Tokens per run of the head pass.
 static constexpr int MIX_BWD_HTB = 8;
 
-template <int D>
+// Head-pass phases.  With the q-k-mean of the pre-convolution values only
+// (or none) the channel conv's input cotangent is dm itself and one pass does
+// everything (PH_ALL).  With the pre- and post-convolution mean, b_q of head h
+// also reaches k of its group (and b_k every q head of the group), so
+// db = 1.25 dm + (partner terms) needs the other heads' dm: PH_DM writes dm
+// and the temperature partials, then PH_DA forms db from the dm of the head
+// and its partners and runs the channel-conv transpose.
+enum { PH_ALL = 0, PH_DM = 1, PH_DA = 2 };
+
+template <typename TI, int D, int PH>
 __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w,
-                                                           const float *__restrict__ qkv,
+                                                           const TI *__restrict__ qkv,
+                                                           const float *__restrict__ bpost,
                                                            const float *__restrict__ gq,
                                                            const float *__restrict__ dk,
-                                                           float *__restrict__ dm_out,
+                                                           float *__restrict__ dm_io,
                                                            float *__restrict__ da_out,
                                                            float *__restrict__ tau_part,
                                                            float *__restrict__ chan_part) {
@@ -65,14 +75,18 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
   const int g = is_q ? hh / s.G : hh - s.Hq;
   const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
   const int i0 = 4 * li;                                   // this lane's first channel
-  const int colbase = is_q ? hh * D : eq + g * D;          // in the qkv row and in dm / da rows
+  const int colbase = is_q ? hh * D : eq + g * D;          // in the qkv row and in dm / da / b rows
   const int wcols = eq + ekv;
   const float *seqw = is_q ? w.q_seq + (size_t)hh * D * s.ks : w.k_seq + (size_t)g * D * s.ks;
   const float *chw = is_q ? w.q_chan + (size_t)hh * s.kc : w.k_chan + (size_t)g * s.kc;
-  const float *seq0 = qkv + (size_t)b * s.T * N;           // this sequence's rows
+  const TI *seq0 = qkv + (size_t)b * s.T * N;              // this sequence's rows
   const float *gin0 = is_q ? gq + (size_t)b * s.T * eq + hh * D + i0
                            : dk + (size_t)b * s.T * ekv + g * D + i0;
   const int gstride = is_q ? eq : ekv;
+  // the q-k-mean: m = cb * b + coef * (own pre-conv + partner pre-conv +
+  // partner post-conv); the post-conv partner term only in mean mode 2
+  const bool post = s.use_mean == 2;
+  const float cb = post ? 1.25f : 1.f, coef = post ? 0.25f : 0.5f;
 
   float ws[4][4];                                           // [channel][tap], zero past k_s
 #pragma unroll
@@ -86,21 +100,44 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
   const float tau_h = is_q ? w.tau[hh] : 0.f;
   const float invg = __builtin_amdgcn_rcpf((float)s.G);
 
-  // pre-conv row of token t (zero before the sequence start), the q-k-mean
-  // skip term and the incoming cotangent of token t
+  // pre-conv row of token t (zero before the sequence start), the partner
+  // sum of the q-k-mean (PH_ALL, PH_DM) or the partner cotangent of db
+  // (PH_DA), and the incoming cotangent of token t (PH_ALL, PH_DM)
   auto load_row = [&](int t) -> f32x4 {
     if (t < 0) return f32x4{0.f, 0.f, 0.f, 0.f};
-    return *reinterpret_cast<const f32x4 *>(seq0 + (size_t)t * N + colbase + i0);
+    return ld4f<TI>(seq0 + (size_t)t * N + colbase + i0);
   };
   auto load_skip = [&](int t) -> f32x4 {
-    const float *row = seq0 + (size_t)t * N;
-    if (is_q) return *reinterpret_cast<const f32x4 *>(row + eq + g * D + i0);
-    f32x4 m = *reinterpret_cast<const f32x4 *>(row + g * s.G * D + i0);
-    for (int h2 = 1; h2 < s.G; ++h2) m += *reinterpret_cast<const f32x4 *>(row + (g * s.G + h2) * D + i0);
-    return m * invg;
+    const size_t r = (size_t)b * s.T + t;
+    if constexpr (PH == PH_DA) {
+      // q head: dm of its key head / (4G); key head: the group's summed q dm / 4
+      const float *row = dm_io + r * wcols;
+      if (is_q) return *reinterpret_cast<const f32x4 *>(row + eq + g * D + i0) * (0.25f * invg);
+      f32x4 m = *reinterpret_cast<const f32x4 *>(row + g * s.G * D + i0);
+      for (int h2 = 1; h2 < s.G; ++h2) m += *reinterpret_cast<const f32x4 *>(row + (g * s.G + h2) * D + i0);
+      return m * 0.25f;
+    } else {
+      const TI *row = seq0 + (size_t)t * N;
+      f32x4 p;
+      if (is_q) {
+        p = ld4f<TI>(row + eq + g * D + i0);
+        if (post) p += *reinterpret_cast<const f32x4 *>(bpost + r * wcols + eq + g * D + i0);
+      } else {
+        p = ld4f<TI>(row + g * s.G * D + i0);
+        for (int h2 = 1; h2 < s.G; ++h2) p += ld4f<TI>(row + (g * s.G + h2) * D + i0);
+        if (post)
+          for (int h2 = 0; h2 < s.G; ++h2)
+            p += *reinterpret_cast<const f32x4 *>(bpost + r * wcols + (g * s.G + h2) * D + i0);
+        p = p * invg;
+      }
+      return p;
+    }
   };
   auto load_gin = [&](int t) -> f32x4 {
-    return *reinterpret_cast<const f32x4 *>(gin0 + (size_t)t * gstride);
+    if constexpr (PH == PH_DA)
+      return *reinterpret_cast<const f32x4 *>(dm_io + ((size_t)b * s.T + t) * wcols + colbase + i0);
+    else
+      return *reinterpret_cast<const f32x4 *>(gin0 + (size_t)t * gstride);
   };
 
   // lane exchanges: DPP inside rows of 16 lanes, shuffles across rows (d = 128)
@@ -121,7 +158,8 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
   f32x4 u[4];                                               // rows t, t-1, t-2, t-3
 #pragma unroll
   for (int j = 0; j < 4; ++j) u[j] = load_row(t0 - j);
-  f32x4 skip = load_skip(t0), gin = load_gin(t0);
+  const bool need_skip = PH == PH_DA || s.use_mean;
+  f32x4 skip = need_skip ? load_skip(t0) : f32x4{0.f, 0.f, 0.f, 0.f}, gin = load_gin(t0);
   float tau_acc = 0.f, cacc[4] = {0.f, 0.f, 0.f, 0.f};
 
   // a uniform trip count keeps every lane in the wave-wide exchanges; tokens
@@ -131,9 +169,11 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
     const bool valid = t < t1;
     // next token's inputs, in flight while this one is computed
     const int tn = min(t + 1, t1 - 1 < t0 ? t0 : t1 - 1);
-    const f32x4 u_n = load_row(tn), skip_n = load_skip(tn), gin_n = load_gin(tn);
+    const f32x4 u_n = load_row(tn);
+    const f32x4 skip_n = need_skip ? load_skip(tn) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 gin_n = load_gin(tn);
 
-    // forward recompute: sequence conv, channel conv, q-k-mean, norm
+    // sequence conv of the pre-conv rows
     float a[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -143,62 +183,76 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
       a[c] = acc;
     }
     const float p1 = prev(a[1]), p2 = prev(a[2]), p3 = prev(a[3]);   // a[i0-3], a[i0-2], a[i0-1]
-    float m[4];
-    m[0] = cw[0] * a[0] + cw[1] * p3 + cw[2] * p2 + cw[3] * p1;
-    m[1] = cw[0] * a[1] + cw[1] * a[0] + cw[2] * p3 + cw[3] * p2;
-    m[2] = cw[0] * a[2] + cw[1] * a[1] + cw[2] * a[0] + cw[3] * p3;
-    m[3] = cw[0] * a[3] + cw[1] * a[2] + cw[2] * a[1] + cw[3] * a[0];
-    if (s.use_mean)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) m[c] += 0.5f * (u[0][c] + skip[c]);
-    // 1 / max(||m||, eps) == rsqrt(max(||m||^2, eps^2))
-    const float ss = grp_sum(m[0] * m[0] + m[1] * m[1] + m[2] * m[2] + m[3] * m[3]);
-    const bool big = ss > s.eps * s.eps;
-    const float inv = s.use_norm ? __builtin_amdgcn_rsqf(fmaxf(ss, s.eps * s.eps)) : 1.f;
-    float n[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) n[c] = m[c] * inv;
 
-    // RoPE pairs (i0, i0+1) and (i0+2, i0+3): rotate back, and the
-    // temperature partial <r, g> of the rotated q
-    float dn[4];
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const float2 cs = rope_cs_theta(t, pp ? th1 : th0, s.rope_base);
-      const float g0 = gin[2 * pp], g1 = gin[2 * pp + 1];
-      const float d0 = is_q ? tau_h * g0 : g0, d1 = is_q ? tau_h * g1 : g1;
-      const float x0 = n[2 * pp], x1 = n[2 * pp + 1];
-      if (valid) tau_acc += (x0 * cs.x - x1 * cs.y) * g0 + (x0 * cs.y + x1 * cs.x) * g1;
-      dn[2 * pp] = d0 * cs.x + d1 * cs.y;
-      dn[2 * pp + 1] = -d0 * cs.y + d1 * cs.x;
-    }
-
-    // norm backward
     float dm[4];
-    if (s.use_norm) {
-      const float nd = grp_sum(n[0] * dn[0] + n[1] * dn[1] + n[2] * dn[2] + n[3] * dn[3]);
+    if constexpr (PH == PH_DA) {
+      // db = 1.25 dm + the partners' terms
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dm[c] = (big ? dn[c] - n[c] * nd : dn[c]) * inv;
+      for (int c = 0; c < 4; ++c) dm[c] = 1.25f * gin[c] + skip[c];
     } else {
+      // forward recompute: channel conv, q-k-mean, norm
+      float m[4];
+      m[0] = cw[0] * a[0] + cw[1] * p3 + cw[2] * p2 + cw[3] * p1;
+      m[1] = cw[0] * a[1] + cw[1] * a[0] + cw[2] * p3 + cw[3] * p2;
+      m[2] = cw[0] * a[2] + cw[1] * a[1] + cw[2] * a[0] + cw[3] * p3;
+      m[3] = cw[0] * a[3] + cw[1] * a[2] + cw[2] * a[1] + cw[3] * a[0];
+      if (s.use_mean)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dm[c] = dn[c];
+        for (int c = 0; c < 4; ++c) m[c] = cb * m[c] + coef * (u[0][c] + skip[c]);
+      // 1 / max(||m||, eps) == rsqrt(max(||m||^2, eps^2))
+      const float ss = grp_sum(m[0] * m[0] + m[1] * m[1] + m[2] * m[2] + m[3] * m[3]);
+      const bool big = ss > s.eps * s.eps;
+      const float inv = s.use_norm ? __builtin_amdgcn_rsqf(fmaxf(ss, s.eps * s.eps)) : 1.f;
+      float n[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) n[c] = m[c] * inv;
+
+      // RoPE pairs (i0, i0+1) and (i0+2, i0+3): rotate back, and the
+      // temperature partial <r, g> of the rotated q
+      float dn[4];
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const float2 cs = rope_cs_theta(t, pp ? th1 : th0, s.rope_base);
+        const float g0 = gin[2 * pp], g1 = gin[2 * pp + 1];
+        const float d0 = is_q ? tau_h * g0 : g0, d1 = is_q ? tau_h * g1 : g1;
+        const float x0 = n[2 * pp], x1 = n[2 * pp + 1];
+        if (valid) tau_acc += (x0 * cs.x - x1 * cs.y) * g0 + (x0 * cs.y + x1 * cs.x) * g1;
+        dn[2 * pp] = d0 * cs.x + d1 * cs.y;
+        dn[2 * pp + 1] = -d0 * cs.y + d1 * cs.x;
+      }
+
+      // norm backward
+      if (s.use_norm) {
+        const float nd = grp_sum(n[0] * dn[0] + n[1] * dn[1] + n[2] * dn[2] + n[3] * dn[3]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dm[c] = (big ? dn[c] - n[c] * nd : dn[c]) * inv;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dm[c] = dn[c];
+      }
+      if (PH == PH_DM && valid) {
+        const size_t o = ((size_t)b * s.T + t) * wcols + colbase + i0;
+        *reinterpret_cast<f32x4 *>(dm_io + o) = f32x4{dm[0], dm[1], dm[2], dm[3]};
+      }
     }
 
-    // channel conv backward (da[i] = sum_j w_j dm[i+j]) and its tap partials
-    const float x0 = next(dm[0]), x1 = next(dm[1]), x2 = next(dm[2]);   // dm[i0+4 .. i0+6]
-    f32x4 da;
-    da[0] = cw[0] * dm[0] + cw[1] * dm[1] + cw[2] * dm[2] + cw[3] * dm[3];
-    da[1] = cw[0] * dm[1] + cw[1] * dm[2] + cw[2] * dm[3] + cw[3] * x0;
-    da[2] = cw[0] * dm[2] + cw[1] * dm[3] + cw[2] * x0 + cw[3] * x1;
-    da[3] = cw[0] * dm[3] + cw[1] * x0 + cw[2] * x1 + cw[3] * x2;
-    if (valid) {
-      cacc[0] += dm[0] * a[0] + dm[1] * a[1] + dm[2] * a[2] + dm[3] * a[3];
-      cacc[1] += dm[0] * p3 + dm[1] * a[0] + dm[2] * a[1] + dm[3] * a[2];
-      cacc[2] += dm[0] * p2 + dm[1] * p3 + dm[2] * a[0] + dm[3] * a[1];
-      cacc[3] += dm[0] * p1 + dm[1] * p2 + dm[2] * p3 + dm[3] * a[0];
-      const size_t o = ((size_t)b * s.T + t) * wcols + colbase + i0;
-      *reinterpret_cast<f32x4 *>(dm_out + o) = f32x4{dm[0], dm[1], dm[2], dm[3]};
-      *reinterpret_cast<f32x4 *>(da_out + o) = da;
+    if constexpr (PH != PH_DM) {
+      // channel conv backward (da[i] = sum_j w_j db[i+j]) and its tap partials
+      const float x0 = next(dm[0]), x1 = next(dm[1]), x2 = next(dm[2]);   // db[i0+4 .. i0+6]
+      f32x4 da;
+      da[0] = cw[0] * dm[0] + cw[1] * dm[1] + cw[2] * dm[2] + cw[3] * dm[3];
+      da[1] = cw[0] * dm[1] + cw[1] * dm[2] + cw[2] * dm[3] + cw[3] * x0;
+      da[2] = cw[0] * dm[2] + cw[1] * dm[3] + cw[2] * x0 + cw[3] * x1;
+      da[3] = cw[0] * dm[3] + cw[1] * x0 + cw[2] * x1 + cw[3] * x2;
+      if (valid) {
+        cacc[0] += dm[0] * a[0] + dm[1] * a[1] + dm[2] * a[2] + dm[3] * a[3];
+        cacc[1] += dm[0] * p3 + dm[1] * a[0] + dm[2] * a[1] + dm[3] * a[2];
+        cacc[2] += dm[0] * p2 + dm[1] * p3 + dm[2] * a[0] + dm[3] * a[1];
+        cacc[3] += dm[0] * p1 + dm[1] * p2 + dm[2] * p3 + dm[3] * a[0];
+        const size_t o = ((size_t)b * s.T + t) * wcols + colbase + i0;
+        if (PH == PH_ALL) *reinterpret_cast<f32x4 *>(dm_io + o) = f32x4{dm[0], dm[1], dm[2], dm[3]};
+        *reinterpret_cast<f32x4 *>(da_out + o) = da;
+      }
     }
     u[3] = u[2];
     u[2] = u[1];
@@ -208,21 +262,25 @@ __global__ __launch_bounds__(256) void mix_bwd_head_kernel(MixShape s, MixTaps w
     gin = gin_n;
   }
 
-  const float tau_sum = grp_sum(tau_acc);
-  float cpart[4];
+  if constexpr (PH != PH_DA) {
+    const float tau_sum = grp_sum(tau_acc);
+    if (active && li == 0 && is_q) tau_part[(size_t)run * s.Hq + hh] = tau_sum;
+  }
+  if constexpr (PH != PH_DM) {
+    float cpart[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cpart[j] = grp_sum(cacc[j]);
-  if (!active || li != 0) return;
-  if (is_q) tau_part[(size_t)run * s.Hq + hh] = tau_sum;
-  for (int j = 0; j < s.kc; ++j) chan_part[((size_t)run * H + hh) * s.kc + j] = cpart[j];
+    for (int j = 0; j < 4; ++j) cpart[j] = grp_sum(cacc[j]);
+    if (!active || li != 0) return;
+    for (int j = 0; j < s.kc; ++j) chan_part[((size_t)run * H + hh) * s.kc + j] = cpart[j];
+  }
 }
 
 // Tokens per thread of the channel pass.
 static constexpr int MIX_BWD_TB = 16;
 
-template <typename TZ>
+template <typename TI, typename TZ>
 __global__ __launch_bounds__(256) void mix_bwd_chan_kernel(MixShape s, MixTaps w,
-                                                           const float *__restrict__ qkv,
+                                                           const TI *__restrict__ qkv,
                                                            const float *__restrict__ dm,
                                                            const float *__restrict__ da,
                                                            const float *__restrict__ dv,
@@ -236,6 +294,7 @@ __global__ __launch_bounds__(256) void mix_bwd_chan_kernel(MixShape s, MixTaps w
   const int tbeg = tb * MIX_BWD_TB, tend = min(s.T, tbeg + MIX_BWD_TB);
   if (c >= N) return;
   const size_t rb = (size_t)b * s.T;
+  const float coef = s.use_mean == 2 ? 0.25f : 0.5f;
   if (c < wcols) {
     const bool is_q = c < eq;
     const int i = (is_q ? c : c - eq) % D;
@@ -252,22 +311,24 @@ __global__ __launch_bounds__(256) void mix_bwd_chan_kernel(MixShape s, MixTaps w
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       dwin[j] = (j < s.ks && tbeg + j < s.T) ? da[(rb + tbeg + j) * wcols + c] : 0.f;
-      uwin[j] = (j < s.ks && tbeg - j >= 0) ? qkv[(rb + tbeg - j) * N + c] : 0.f;
+      uwin[j] = (j < s.ks && tbeg - j >= 0) ? to_f32(qkv[(rb + tbeg - j) * N + c]) : 0.f;
     }
     for (int t = tbeg; t < tend; ++t) {
       const float nxt_d = (t + s.ks < s.T) ? da[(rb + t + s.ks) * wcols + c] : 0.f;
-      const float nxt_u = (t + 1 < s.T) ? qkv[(rb + t + 1) * N + c] : 0.f;
+      const float nxt_u = (t + 1 < s.T) ? to_f32(qkv[(rb + t + 1) * N + c]) : 0.f;
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc += ws[j] * dwin[j];
       if (s.use_mean) {
+        // the pre-conv values enter the mean with weight 1/2 (pre only) or
+        // 1/4 (pre and post)
         const float *dmr = dm + (rb + t) * wcols;
         if (is_q) {
-          acc += 0.5f * dmr[c] + (0.5f / (float)s.G) * dmr[eq + g * D + i];
+          acc += coef * dmr[c] + (coef / (float)s.G) * dmr[eq + g * D + i];
         } else {
           float qsum = 0.f;
           for (int h2 = 0; h2 < s.G; ++h2) qsum += dmr[(g * s.G + h2) * D + i];
-          acc += 0.5f * (dmr[c] + qsum);
+          acc += coef * (dmr[c] + qsum);
         }
       }
       dz[(rb + t) * N + c] = from_f32<TZ>(acc);
@@ -393,9 +454,29 @@ size_t mix_backward_scratch_floats(const MixShape &s) {
   return BR * s.Hq + BR * H * s.kc + seq_rows * seq_cols + blk;
 }
 
-template <typename TZ>
-hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwdArgs<TZ> &a,
+template <typename TI, int D>
+static hipError_t mix_bwd_heads(const MixShape &s, const MixTaps &w, const TI *qkv,
+                                const float *bpost, const float *gq, const float *dk, float *dm,
+                                float *da, float *tau_part, float *chan_part, unsigned nwg,
+                                hipStream_t stream) {
+  if (s.use_mean != 2) {
+    hipLaunchKernelGGL((mix_bwd_head_kernel<TI, D, PH_ALL>), dim3(nwg), dim3(256), 0, stream, s, w,
+                       qkv, bpost, gq, dk, dm, da, tau_part, chan_part);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((mix_bwd_head_kernel<TI, D, PH_DM>), dim3(nwg), dim3(256), 0, stream, s, w,
+                     qkv, bpost, gq, dk, dm, da, tau_part, chan_part);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mix_bwd_head_kernel<TI, D, PH_DA>), dim3(nwg), dim3(256), 0, stream, s, w,
+                     qkv, bpost, gq, dk, dm, da, tau_part, chan_part);
+  return hipGetLastError();
+}
+
+template <typename TI, typename TZ>
+hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwdArgs<TI, TZ> &a,
                                hipStream_t stream) {
+  if (s.use_mean == 2 && !a.bpost) return hipErrorInvalidValue;
   const int nhr = (s.T + MIX_BWD_HTB - 1) / MIX_BWD_HTB;   // head-pass runs per sequence
   const long long units = (long long)s.B * nhr * (s.Hq + s.Hkv);
   const long long per_wg = 4LL * (64 / (s.d / 4));
@@ -411,16 +492,16 @@ hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwd
   float *seq_part = chan_part + BR * H * s.kc;
   float *blk = seq_part + (size_t)s.B * ntb * wcols * s.ks;
 
+  hipError_t e;
   switch (s.d) {
-    case 16: hipLaunchKernelGGL((mix_bwd_head_kernel<16>), dim3(nwg), dim3(256), 0, stream, s, w, a.qkv, a.gq, a.dk, a.dm, a.da, tau_part, chan_part); break;
-    case 32: hipLaunchKernelGGL((mix_bwd_head_kernel<32>), dim3(nwg), dim3(256), 0, stream, s, w, a.qkv, a.gq, a.dk, a.dm, a.da, tau_part, chan_part); break;
-    case 64: hipLaunchKernelGGL((mix_bwd_head_kernel<64>), dim3(nwg), dim3(256), 0, stream, s, w, a.qkv, a.gq, a.dk, a.dm, a.da, tau_part, chan_part); break;
-    case 128: hipLaunchKernelGGL((mix_bwd_head_kernel<128>), dim3(nwg), dim3(256), 0, stream, s, w, a.qkv, a.gq, a.dk, a.dm, a.da, tau_part, chan_part); break;
+    case 16: e = mix_bwd_heads<TI, 16>(s, w, a.qkv, a.bpost, a.gq, a.dk, a.dm, a.da, tau_part, chan_part, nwg, stream); break;
+    case 32: e = mix_bwd_heads<TI, 32>(s, w, a.qkv, a.bpost, a.gq, a.dk, a.dm, a.da, tau_part, chan_part, nwg, stream); break;
+    case 64: e = mix_bwd_heads<TI, 64>(s, w, a.qkv, a.bpost, a.gq, a.dk, a.dm, a.da, tau_part, chan_part, nwg, stream); break;
+    case 128: e = mix_bwd_heads<TI, 128>(s, w, a.qkv, a.bpost, a.gq, a.dk, a.dm, a.da, tau_part, chan_part, nwg, stream); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mix_bwd_chan_kernel<TZ>), dim3((N + 255) / 256, s.B * ntb), dim3(256), 0,
+  hipLaunchKernelGGL((mix_bwd_chan_kernel<TI, TZ>), dim3((N + 255) / 256, s.B * ntb), dim3(256), 0,
                      stream, s, w, a.qkv, a.dm, a.da, a.dv, a.dz, seq_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -441,9 +522,9 @@ hipError_t launch_mix_backward(const MixShape &s, const MixTaps &w, const MixBwd
   return colsum_all(jobs, stream);
 }
 
-template hipError_t launch_mix_backward<bf16>(const MixShape &, const MixTaps &,
-                                              const MixBwdArgs<bf16> &, hipStream_t);
-template hipError_t launch_mix_backward<float>(const MixShape &, const MixTaps &,
-                                               const MixBwdArgs<float> &, hipStream_t);
+template hipError_t launch_mix_backward<f16, bf16>(const MixShape &, const MixTaps &,
+                                                   const MixBwdArgs<f16, bf16> &, hipStream_t);
+template hipError_t launch_mix_backward<float, float>(const MixShape &, const MixTaps &,
+                                                      const MixBwdArgs<float, float> &, hipStream_t);
 
 }  // namespace cca

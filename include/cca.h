@@ -30,9 +30,14 @@
  *   - convolution taps are indexed by lag: a[t,c] = sum_j w[c,j] u[t-j,c];
  *   - the channel convolution is one k_c-tap filter per head sliding along
  *     the head's channel index, zero padded inside the head;
- *   - q-k-mean adds the mean of the pre-convolution q and k to the convolved
- *     q and k (per group for CCGQA: q head h meets k~ of kv head h/G, kv head
- *     g meets the average q~ of its G query heads);
+ *   - q-k-mean adds the mean of the query and key values before and after
+ *     the convolutions to the convolved q and k [GS-EN "2. Methodology" /
+ *     Q-K-Mean; EDG "How Compressed Convolutional Attention Works"; GS-DE
+ *     "2. Methodik"]: m = (q~ + k~ + b_q + b_k) / 4, q = b_q + m, k = b_k + m,
+ *     with b the convolutions' output and ~ the down-projection's; for CCGQA
+ *     query head h meets kv head h/G and kv head g the averages over its G
+ *     query heads.  cca_config.qk_mean_mode selects the other reading, the
+ *     mean of the pre-convolution values only;
  *   - value-shift: kv heads H_kv/2 .. H_kv-1 take the previous token's value
  *     (zero before the first token);
  *   - q and k are divided by max(||.||_2, norm_eps) per head; the logit of
@@ -83,6 +88,16 @@ typedef enum { CCA_BF16 = 0, CCA_F32 = 1 } cca_dtype;
  *   a[t-j,h,c], a = 0 before the sequence start. */
 typedef enum { CCA_CHAN_PER_HEAD = 0, CCA_CHAN_GROUPED = 1 } cca_chan_conv;
 
+/* Reading of the q-k-mean [GS-EN "2. Methodology" / Q-K-Mean: q and k each
+ * receive an average of the query and key values taken before and after the
+ * convolutions].
+ * CCA_QK_MEAN_PRE_POST: q += (q~ + b_q + k~ + b_k) / 4, k += (k~ + b_k +
+ *   avg q~ + avg b_q) / 4 (avg over the kv head's G query heads) -- the
+ *   default.
+ * CCA_QK_MEAN_PRE: the pre-convolution values only, q += (q~ + k~) / 2,
+ *   k += (k~ + avg q~) / 2. */
+typedef enum { CCA_QK_MEAN_PRE_POST = 0, CCA_QK_MEAN_PRE = 1 } cca_qk_mean;
+
 /* Shape and switches of one attention layer.  C (compression) and G are
  * derived: e_q = n_q_heads*head_dim, e_kv = n_kv_heads*head_dim,
  * G = n_q_heads / n_kv_heads. */
@@ -104,6 +119,8 @@ typedef struct {
   int32_t chan_conv_mode; /* cca_chan_conv; 0 (zero-initialised) is the per-head filter.
                            * CCA_CHAN_GROUPED needs d in {16, 32, 64}; the training and
                            * fused prefill entry points reject it (CCA_ERR_UNSUPPORTED) */
+  int32_t qk_mean_mode;   /* cca_qk_mean; 0 (zero-initialised) is the pre- and
+                           * post-convolution mean.  Only read when use_qk_mean is 1. */
 } cca_config;
 
 /* Weights.  w_qkv: [e_q + 2*e_kv, E] in cfg.dtype, rows q | k | v.
@@ -151,7 +168,8 @@ typedef struct {
  * CCA_ERR_INVALID_ARG (null cfg, non-positive sizes, H_q % H_kv != 0, odd
  * H_kv with value-shift, E not a multiple of 8, bad eps/base) or
  * CCA_ERR_UNSUPPORTED (d outside {16,32,64,128}, fp32 prefill with d = 128,
- * taps outside 1..4, dtype, a kv group too wide for the mixing kernel). */
+ * taps outside 1..4, dtype, a kv group too wide for the mixing kernel).
+ * A qk_mean_mode or chan_conv_mode outside its enum is CCA_ERR_INVALID_ARG. */
 cca_status cca_validate_config(const cca_config *cfg);
 
 /* Bytes of device workspace cca_prefill_forward needs for cfg (0 if cfg is
@@ -354,7 +372,9 @@ const char *cca_status_string(cca_status s);
  *
  * Prefill workspace layout (offsets from cca_prefill_workspace_layout; Tp is
  * T rounded up to 128):
- *   CCA_WS_QKV  fp32 [B*T, e_q + 2*e_kv]   down-projection output
+ *   CCA_WS_QKV  [B*T, e_q + 2*e_kv]   down-projection output: fp16 when
+ *               cfg.dtype is bf16 (10 mantissa bits; |values| above 65504
+ *               overflow), fp32 when it is fp32
  *   CCA_WS_Q    [B, H_q, Tp, d]   normalised, rotated q times tau_h*log2(e)
  *               (logits in the exp2 domain); fp16 when cfg.dtype is bf16 and
  *               use_qk_norm is 1, else cfg.dtype

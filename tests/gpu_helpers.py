@@ -75,10 +75,11 @@ def set_taps(P, seq=None, chan=None, tau=None):
 class PrefillRun:
     """Device buffers and one prefill through cca_prefill_forward."""
 
-    def __init__(self, shape: CCAShape, P, capacity: int = 0, dev="cuda", chan_conv="per_head"):
+    def __init__(self, shape: CCAShape, P, capacity: int = 0, dev="cuda", chan_conv="per_head",
+                 qk_mean="pre_post"):
         L, T = lib(), tens()
         self.shape, self.P = shape, P
-        self.cfg = L.make_config(shape, chan_conv=chan_conv)
+        self.cfg = L.make_config(shape, chan_conv=chan_conv, qk_mean=qk_mean)
         assert L.validate_config(self.cfg) == L.CCA_OK
         self.w = upload_weights(P.weights, dev)
         self.x = T.to_device(P.x_s, dev)
@@ -108,6 +109,10 @@ class PrefillRun:
         off = self.layout[slot]
         n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
         return self.ws[off:off + n].view(dtype).view(*shape)
+
+    def qkv_dtype(self):
+        """The down-projection output: fp16 in bf16 mode, fp32 in fp32 mode."""
+        return torch.float32 if self.shape.dtype == "f32" else torch.float16
 
     def qk_dtype(self):
         s = self.shape

@@ -87,6 +87,27 @@ def test_invalid_configs(L, kw, err):
     assert L.prefill_workspace_size(cfg) == 0
 
 
+@pytest.mark.parametrize("field,value", [("qk_mean_mode", 2), ("qk_mean_mode", -1),
+                                         ("chan_conv_mode", 2)])
+def test_reading_switch_out_of_range(L, field, value):
+    cfg = L.make_config(CCAShape(batch=1, seq_len=16, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                 head_dim=64))
+    setattr(cfg, field, value)
+    assert L.validate_config(cfg) == L.CCA_ERR_INVALID_ARG
+    assert L.prefill_workspace_size(cfg) == 0
+
+
+def test_both_qk_mean_readings_validate(L):
+    s = CCAShape(batch=1, seq_len=16, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    for mode in ("pre_post", "pre"):
+        cfg = L.make_config(s, qk_mean=mode)
+        assert L.validate_config(cfg) == L.CCA_OK
+        assert L.train_workspace_size(cfg) > 0
+    # the default reading keeps the channel-conv output for the backward
+    assert (L.train_workspace_size(L.make_config(s)) >
+            L.train_workspace_size(L.make_config(s, qk_mean="pre")))
+
+
 def _fake_weights(L, dense=0x10000):
     a = 0x10000
     return L._Weights(a, a, a, a, a, a, a, dense, dense)

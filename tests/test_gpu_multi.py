@@ -54,10 +54,10 @@ CASES = {
 }
 
 
-def _run_multi(shape, D, lens, m, seed, paged=False, page=64):
+def _run_multi(shape, D, lens, m, seed, paged=False, page=64, qk_mean="pre_post"):
     T, Lb = tens(), lib()
     Lmax = shape.cache_len
-    cfg = Lb.make_config(shape)
+    cfg = Lb.make_config(shape, qk_mean=qk_mean)
     st = _upload(D)
     xs, x64 = _new_tokens(shape, m, seed)
     x_new = T.to_device(xs)
@@ -141,3 +141,37 @@ def test_decode_multi_paged_equals_contiguous():
                            st1.k_cache[b, :, L_:L_ + m].view(torch.int16))
         assert torch.equal(_gather(vp, table, b, rows).view(torch.int16),
                            st1.v_cache[b, :, L_:L_ + m].view(torch.int16))
+
+
+def test_decode_multi_full_length():
+    """Four new tokens per sequence at the decode workload's shape (B=64,
+    16 query / 4 kv heads of 64) with lengths up to 32764, so the 32768 keys
+    split into two 16384-key chunks: contiguous and paged (32-row pages, 513
+    per chunk) agree bit for bit, and 6 sequences match the oracle."""
+    from synth import workload
+    m, Lmax = 4, 32764
+    shape = workload("ccgqa_decode_b64_l32768").with_(cache_len=Lmax)
+    rng = np.random.default_rng(61)
+    lens = rng.integers(30000, Lmax + 1, size=shape.batch).astype(np.int32).tolist()
+    lens[0] = Lmax
+    _say(f"[multi] full length B={shape.batch} Lmax={Lmax} m={m}")
+    D = make_decode(shape, seed=61, capacity=Lmax + m)
+    y1, st1, x64 = _run_multi(shape, D, lens, m, seed=62)
+    y2, (ps, kp, vp, table), _ = _run_multi(shape, D, lens, m, seed=62, paged=True, page=32)
+    _say("[multi] full length: steps done")
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    from test_gpu_paged import _gather
+    for b in (0, 1, 63):
+        rows = list(range(lens[b], lens[b] + m))
+        assert torch.equal(_gather(kp, table, b, rows).view(torch.int16),
+                           st1.k_cache[b, :, lens[b]:lens[b] + m].view(torch.int16))
+    T = tens()
+    w = D.weights.f64()
+    cq, ck, vs = D.state_f64()
+    yy = T.to_f64(y1)
+    for b in [0] + sorted(rng.choice(np.arange(1, shape.batch), size=5, replace=False).tolist()):
+        L_ = lens[b]
+        ref, _ = O.decode_multi(x64[b:b + 1], w, shape, D.cache_f64(b, "k")[None, :, :L_],
+                                D.cache_f64(b, "v")[None, :, :L_], cq[b:b + 1], ck[b:b + 1],
+                                vs[b:b + 1])
+        assert_parity(yy[b:b + 1], ref, "bf16", f"multi full b={b} L={L_}")

@@ -189,3 +189,62 @@ def test_paged_prefill_then_decode_equals_contiguous():
         assert torch.equal(_gather(kp, table, b, rows).view(torch.int16),
                            cst.k_cache[b].view(torch.int16))
     assert rel_l2(T.to_f64(pst.conv_q), T.to_f64(cst.conv_q)) == 0.0
+
+
+@pytest.mark.parametrize("page", [32, 256])
+def test_paged_decode_full_length(page):
+    """The decode workload's shape (B=64, 16 query / 4 kv heads of 64) at
+    per-sequence lengths up to 32767.  Lk = 32768 keys split into two chunks
+    of 16384 (the longest the chunking makes), so with 32-row pages one chunk
+    spans 513 pages: the largest page list the attention kernel keeps in LDS.
+    The paged step equals the contiguous per-sequence-length step bit for bit
+    (outputs, new cache rows, rolled state); 8 sequences against the oracle."""
+    from synth import workload
+    Lmax = 32767
+    shape = workload("ccgqa_decode_b64_l32768").with_(cache_len=Lmax)
+    rng = np.random.default_rng(50 + page)
+    lens = rng.integers(30000, Lmax + 1, size=shape.batch).astype(np.int32)
+    lens[0], lens[1] = Lmax, 30000
+    _say(f"[paged] full length page={page} B={shape.batch} Lmax={Lmax}")
+    D = make_decode(shape, seed=51, capacity=Lmax + 1)
+    T, Lb = tens(), lib()
+    cfg = Lb.make_config(shape)
+    w = upload_weights(D.weights)
+    x_t = T.to_device(D.x_s)
+    dl = torch.from_numpy(lens).to("cuda")
+    ws = T.workspace(Lb.decode_workspace_size(cfg, Lmax))
+
+    ref_st = _upload_contig(D)
+    y_ref = torch.empty_like(x_t)
+    Lb.decode_step_varlen(cfg, w, x_t, dl, Lmax, ref_st, ref_st, y_ref, ws)
+    torch.cuda.synchronize()
+
+    mpps = (Lmax + 1 + page - 1) // page
+    src = _upload_contig(D)
+    kp, table = _paged_from(src.k_cache, page, mpps, seed=page + 1)
+    vp, _ = _paged_from(src.v_cache, page, mpps, seed=page + 1)
+    del src.k_cache, src.v_cache
+    pst = Lb.PagedState(kp, vp, table, page, src.conv_q, src.conv_k, src.vshift)
+    y = torch.empty_like(x_t)
+    Lb.decode_step_paged(cfg, w, x_t, dl, Lmax, pst, pst, y, ws)
+    torch.cuda.synchronize()
+    _say(f"[paged] full length page={page}: step done")
+
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    for b, L_ in enumerate(lens):
+        assert torch.equal(_gather(kp, table, b, [int(L_)])[:, 0].view(torch.int16),
+                           ref_st.k_cache[b, :, L_].view(torch.int16))
+        assert torch.equal(_gather(vp, table, b, [int(L_)])[:, 0].view(torch.int16),
+                           ref_st.v_cache[b, :, L_].view(torch.int16))
+    for a, c in ((pst.conv_q, ref_st.conv_q), (pst.conv_k, ref_st.conv_k),
+                 (pst.vshift, ref_st.vshift)):
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    wd = D.weights.f64()
+    cq, ck, vs = D.state_f64()
+    yy = T.to_f64(y)
+    for b in [0, 1] + sorted(rng.choice(np.arange(2, shape.batch), size=6, replace=False).tolist()):
+        L_ = int(lens[b])
+        K = D.cache_f64(b, "k")[None, :, :L_]
+        V = D.cache_f64(b, "v")[None, :, :L_]
+        ref, _ = O.decode_step(D.x[b:b + 1], wd, shape, K, V, cq[b:b + 1], ck[b:b + 1], vs[b:b + 1])
+        assert_parity(yy[b:b + 1], ref, "bf16", f"paged full b={b} L={L_}")

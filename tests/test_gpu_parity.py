@@ -99,10 +99,12 @@ def test_prefill_stage_intermediates():
     s, T = shape, tens()
     B, Tn, Tp, d = s.batch, s.seq_len, run.padded_T(), s.head_dim
     L = lib()
-    qkv = T.to_f64(run.ws_view(L.WS_QKV, torch.float32, (B, Tn, s.n_qkv)))
+    qkv = T.to_f64(run.ws_view(L.WS_QKV, run.qkv_dtype(), (B, Tn, s.n_qkv)))
     ref_qkv = np.concatenate([lat["q_pre"].reshape(B, Tn, -1), lat["k_pre"].reshape(B, Tn, -1),
                               lat["vbar"].reshape(B, Tn, -1)], axis=-1)
-    assert rel_l2(qkv, ref_qkv) < 1e-6, "down-projection"
+    # the fp16 output rounding moves each element by at most 2^-11 of itself
+    # (fp32 accumulation adds ~1e-7)
+    assert rel_l2(qkv, ref_qkv) < 2.0 ** -11 + 1e-6, "down-projection"
     q = T.to_f64(run.ws_view(L.WS_Q, run.qk_dtype(), (B, s.n_q_heads, Tp, d)))
     k = T.to_f64(run.ws_view(L.WS_K, run.qk_dtype(), (B, s.n_kv_heads, Tp, d)))
     scale = (P.weights.tau.astype(np.float64) * np.log2(np.e))[None, :, None, None]
@@ -379,10 +381,14 @@ def test_prefill_fused_matches_stages_and_oracle(name):
     L.stage_convmix(run.cfg, run.w, run.ws)
     torch.cuda.synchronize()
     staged = (qv(), kv(), vv())
+    # the fused kernel keeps qkv~ in fp32, the staged path rounds it to fp16
+    # (2^-11 relative) before mixing; both round their outputs (fp16 q, k:
+    # 2^-11; bf16 v: 2^-8, where the fp16 step can tip a tie): the two agree
+    # to 2e-3 relative L2
     for what, a, b in zip(("q", "k", "vt"), fused, staged):
-        fa, fb = a.float(), b.float()
-        err = float((fa - fb).abs().max())
-        _say(f"[fused] {what}: max |fused - staged| = {err:.3e}, bitwise {torch.equal(a, b)}")
-        assert err <= 2e-3 * max(float(fb.abs().max()), 1.0), what
+        fa, fb = a.double().cpu().numpy(), b.double().cpu().numpy()
+        r = rel_l2(fa, fb)
+        _say(f"[fused] {what}: rel-L2 |fused - staged| = {r:.3e}, bitwise {torch.equal(a, b)}")
+        assert r <= 2e-3, what
     ref = O.prefill(P.x, P.weights.f64(), shape)
     assert_parity(tens().to_f64(y), ref, "bf16", name)
