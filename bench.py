@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--compare", action="store_true",
                    help="prefill of ccgqa_prefill_t16384 next to full-width MHA and GQA-8 baselines "
                         "through the same kernels, plus a sequence-length sweep (prints its own JSON)")
+    p.add_argument("--kernels-only", action="store_true",
+                   help="only run the stage calls of the three bf16 prefill workloads and the decode "
+                        "step, --steps times each (a short program for counter collection)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -385,6 +388,48 @@ def prefill_config(cca, T, name, K, dev):
     }
 
 
+def kernels_only(args):
+    """The stage calls of the three bf16 prefill workloads and of the decode
+    step, --steps times each after one warm-up call: a short program whose
+    dispatches a counter pass can attribute to kernels."""
+    import torch
+    from efficient_transformer_attention_amd import cca, tensors as T
+    from synth import make_decode, make_prefill, workload
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    for name in ("cca_prefill_b4_t2048", "ccgqa_prefill_t8192", "ccgqa_prefill_t16384"):
+        sp = workload(name)
+        P = make_prefill(sp, seed=0)
+        pw = upload_weights(cca, T, P.weights, dev)
+        cfg = cca.make_config(sp)
+        x = T.to_device(P.x_s, dev)
+        y = torch.empty_like(x)
+        ws = T.workspace(cca.prefill_workspace_size(cfg), dev)
+        for _ in range(args.steps + 1):
+            cca.stage_downproj(cfg, pw, x, ws)
+            cca.stage_convmix(cfg, pw, ws)
+            cca.stage_attention(cfg, pw, ws)
+            cca.stage_upproj(cfg, pw, y, ws)
+        torch.cuda.synchronize()
+        print(f"[kernels] {name} done", file=sys.stderr, flush=True)
+        del ws, x, y, pw, P
+        torch.cuda.empty_cache()
+    sd = workload("ccgqa_decode_b64_l32768")
+    D = make_decode(sd, seed=0)
+    dw = upload_weights(cca, T, D.weights, dev)
+    cfg = cca.make_config(sd)
+    st = cca.State(T.to_device(D.k_cache_s, dev), T.to_device(D.v_cache_s, dev), D.capacity,
+                   T.to_device(D.conv_q_s, dev), T.to_device(D.conv_k_s, dev),
+                   T.to_device(D.vshift_s, dev))
+    xt = T.to_device(D.x_s, dev)
+    yt = torch.empty_like(xt)
+    ws = T.workspace(cca.decode_workspace_size(cfg, sd.cache_len), dev)
+    for _ in range(args.steps + 1):
+        cca.decode_step(cfg, dw, xt, sd.cache_len, st, st, yt, ws)
+    torch.cuda.synchronize()
+    print("[kernels] decode done", file=sys.stderr, flush=True)
+
+
 def compare(args):
     """The pages' prefill and backward comparisons reproduced with this
     library's kernels: CCGQA (ccgqa_prefill_t16384) against full-width MHA and
@@ -470,6 +515,9 @@ def main():
         return
     if args.compare:
         compare(args)
+        return
+    if args.kernels_only:
+        kernels_only(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "

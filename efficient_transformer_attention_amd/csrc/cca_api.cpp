@@ -111,8 +111,7 @@ cca_status validate_shape(const cca_config *c, bool need_seq) {
   if (d != 16 && d != 32 && d != 64 && d != 128) return CCA_ERR_UNSUPPORTED;
   if (c->seq_conv_k < 1 || c->seq_conv_k > 4 || c->chan_conv_k < 1 || c->chan_conv_k > 4)
     return CCA_ERR_UNSUPPORTED;
-  if (!convmix_fits(c->n_q_heads / c->n_kv_heads, d, (int)qkv_elem_size(c->dtype)))
-    return CCA_ERR_UNSUPPORTED;
+  if (!convmix_fits(c->n_q_heads / c->n_kv_heads, d)) return CCA_ERR_UNSUPPORTED;
   if (c->chan_conv_mode == CCA_CHAN_GROUPED &&
       (!grouped_conv_supported(d, c->dtype == CCA_F32) ||
        !convmix_decode_grouped_fits(c->n_q_heads / c->n_kv_heads, d, 1, c->seq_conv_k, c->chan_conv_k)))

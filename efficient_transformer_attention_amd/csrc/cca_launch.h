@@ -177,10 +177,9 @@ hipError_t launch_downproj_mix(const MixShape &s, const MixTaps &w, const bf16 *
                                const bf16 *wqkv, int E, void *halo_ws, TQ *q, TQ *k, TV *vt,
                                hipStream_t stream);
 
-// Whether the mixing kernels' LDS tiles of one kv group (G query heads + k +
-// v; 19 prefill tokens of es-byte elements, 4 decode rows of fp32) fit the
-// 64 KiB they may use.
-bool convmix_fits(int G, int d, int es);
+// Whether the mixing kernels' fp32 LDS tiles of one kv group (G query heads
+// + k + v; 19 prefill tokens, 4 decode rows) fit the 64 KiB they may use.
+bool convmix_fits(int G, int d);
 // Whether the decode mixing tile of m new tokens fits its LDS.
 bool convmix_decode_fits(int G, int d, int m);
 

@@ -86,12 +86,14 @@ __device__ __forceinline__ void norm_rope(const MixShape &s, float2 cs0, float2 
 // group's taps (zero past k_s / k_c).  The lane holds channels 4li .. 4li+3.
 template <int D, typename TT>
 __device__ __forceinline__ void conv_slot(const TT *tile, int CW, int row, int slot, int li,
-                                          const float *staps, const float *ctaps, float (&b)[4]) {
+                                          const float *staps, const float *ctaps, float (&b)[4],
+                                          f32x4 &pre) {
   constexpr int LPU = D / 4;
   const int col = slot * D + 4 * li;
   f32x4 u[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) u[j] = ld4f<TT>(tile + (row - j) * CW + col);
+  pre = u[0];
   float a[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -123,29 +125,29 @@ __device__ __forceinline__ void conv_slot(const TT *tile, int CW, int row, int s
 
 // a4, a6, a7 for every head slot of one kv group at one token, this lane's 4
 // channels: the key head (slot G) first, then the G query heads.
-//   conv(slot, b)  the slot's channel-conv output b
-//   pre(slot)      the slot's pre-convolution values (f32x4)
-//   emit(slot, y)  receives the normalised, rotated result
+//   conv(slot, b, p)  the slot's channel-conv output b and its
+//                     pre-convolution values p (f32x4)
+//   emit(slot, y)     receives the normalised, rotated result
 // s.use_mean: 0 off; 1 q += (q~ + k~)/2, k += (k~ + avg q~)/2; 2 q += (q~ + b_q
 // + k~ + b_k)/4, k += (k~ + b_k + avg q~ + avg b_q)/4.
-template <int D, typename ConvFn, typename PreFn, typename EmitFn>
+template <int D, typename ConvFn, typename EmitFn>
 __device__ __forceinline__ void mix_row(int G, const MixShape &s, float2 cs0, float2 cs1,
-                                        ConvFn &&conv, PreFn &&pre, EmitFn &&emit) {
+                                        ConvFn &&conv, EmitFn &&emit) {
   const bool mean = s.use_mean != 0, post = s.use_mean == 2;
   const float coef = post ? 0.25f : 0.5f;
   float bk[4];
-  conv(G, bk);
+  f32x4 kp;
+  conv(G, bk, kp);
   float sk[4] = {0.f, 0.f, 0.f, 0.f}, sq[4] = {0.f, 0.f, 0.f, 0.f};
   if (mean) {
-    const f32x4 kp = pre(G);
 #pragma unroll
     for (int c = 0; c < 4; ++c) sk[c] = post ? kp[c] + bk[c] : kp[c];
   }
   for (int h = 0; h < G; ++h) {
     float b[4];
-    conv(h, b);
+    f32x4 qp;
+    conv(h, b, qp);
     if (mean) {
-      const f32x4 qp = pre(h);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float own = post ? qp[c] + b[c] : qp[c];
@@ -214,14 +216,17 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
                                                               float *__restrict__ bout, int TC) {
   extern __shared__ __attribute__((aligned(16))) unsigned char mix_smem[];
   const int G = s.G, CW = (G + 2) * D;
-  TI *tile = reinterpret_cast<TI *>(mix_smem);                 // rows: tokens t0-HALO .. t0+TC-1
-  float *staps = reinterpret_cast<float *>(mix_smem + tile_bytes(TC + HALO, G, D, sizeof(TI)));
+  float *tile = reinterpret_cast<float *>(mix_smem);           // rows: tokens t0-HALO .. t0+TC-1
+  float *staps = reinterpret_cast<float *>(mix_smem + tile_bytes(TC + HALO, G, D, 4));
   float *ctaps = staps + (G + 1) * D * 4;
   float *tsc = ctaps + (G + 1) * 4;
 
   const int tid = threadIdx.x;
   const int nchunks = s.Tp / TC;
-  const int chunk = blockIdx.x % nchunks, bg = blockIdx.x / nchunks;
+  // consecutive chunks of a (b, g) on one XCD: the halo rows and the value
+  // tile's partial lines meet in one L2
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int chunk = lid % nchunks, bg = lid / nchunks;
   const int g = bg % s.Hkv, b = bg / s.Hkv;
   const int t0 = chunk * TC;
   const int eq = s.Hq * D, ekv = s.Hkv * D, N = eq + 2 * ekv;
@@ -229,8 +234,9 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   const int vcol = (G + 1) * D;
   const TI *src = qkv + (size_t)b * s.T * N;
 
-  // the tile, in batches of 8 16-byte chunks per thread; tokens outside
-  // [0, T) read as zero
+  // the tile, in fp32: 16-byte chunks of the down-projection output, in
+  // batches of 8 per thread (every load of a batch issued before its LDS
+  // stores), converted once on the way in; tokens outside [0, T) read as zero
   {
     constexpr int EPC = 16 / (int)sizeof(TI), NB = 8;
     const int cpr = CW / EPC, total = (TC + HALO) * cpr;
@@ -249,7 +255,15 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
         const int e = e0 + tid + 256 * u;
         if (e < total) {
           const int r = e / cpr, cc = e - r * cpr;
-          st16(tile + r * CW + cc * EPC, v[u]);
+          float *dst = tile + r * CW + cc * EPC;
+          if constexpr (EPC == 8) {
+            const f32x4 lo = ld4f<TI>(reinterpret_cast<const TI *>(&v[u])),
+                        hi = ld4f<TI>(reinterpret_cast<const TI *>(&v[u]) + 4);
+            *reinterpret_cast<f32x4 *>(dst) = lo;
+            *reinterpret_cast<f32x4 *>(dst + 4) = hi;
+          } else {
+            st16(dst, v[u]);
+          }
         }
       }
     }
@@ -266,8 +280,7 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
     const int tok = t0 + r;
     const float2 cs0 = rope_cs_theta(tok, s.theta[2 * li], s.rope_base);
     const float2 cs1 = rope_cs_theta(tok, s.theta[2 * li + 1], s.rope_base);
-    const TI *cur = tile + (r + HALO) * CW + 4 * li;
-    auto pre = [&](int slot) { return ld4f<TI>(cur + slot * D); };
+    const float *cur = tile + (r + HALO) * CW + 4 * li;
     auto emit = [&](int slot, float *y) {
       if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
       if (slot < G) {
@@ -285,23 +298,24 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
     if (r1b) {
       // grouped channel conv: b comes from the MFMA kernel's output rows
       const float *brow = r1b + (size_t)(b * s.T + min(tok, s.T - 1)) * (eq + ekv) + 4 * li;
-      auto conv = [&](int slot, float (&bb)[4]) {
+      auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
         const f32x4 v = tok < s.T ? *reinterpret_cast<const f32x4 *>(
                                         brow + (slot < G ? (g * G + slot) * D : eq + g * D))
                                   : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) bb[c] = v[c];
+        pre = *reinterpret_cast<const f32x4 *>(cur + slot * D);
       };
-      mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
+      mix_row<D>(G, s, cs0, cs1, conv, emit);
     } else {
-      auto conv = [&](int slot, float (&bb)[4]) {
-        conv_slot<D, TI>(tile, CW, r + HALO, slot, li, staps, ctaps, bb);
+      auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
+        conv_slot<D, float>(tile, CW, r + HALO, slot, li, staps, ctaps, bb, pre);
         if (bout && tok < s.T)
           *reinterpret_cast<f32x4 *>(bout + (size_t)(b * s.T + tok) * (eq + ekv) +
                                      (slot < G ? (g * G + slot) * D : eq + g * D) + 4 * li) =
               f32x4{bb[0], bb[1], bb[2], bb[3]};
       };
-      mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
+      mix_row<D>(G, s, cs0, cs1, conv, emit);
     }
   }
 
@@ -312,7 +326,7 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const int tl = vt_perm(8 * grp + jj);
-      vals[jj] = (t0 + tl < s.T) ? to_f32(tile[(tl + HALO - shifted) * CW + vcol + dd]) : 0.f;
+      vals[jj] = (t0 + tl < s.T) ? tile[(tl + HALO - shifted) * CW + vcol + dd] : 0.f;
     }
     TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + dd) * s.Tp + t0 + 8 * grp;
     Store4<TV>::st(dst, vals);
@@ -324,7 +338,7 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
       if (tok >= s.T) continue;
       size_t row;
       if (!cache_row_store(st, b, s.Hkv, g, tok, &row)) continue;
-      const f32x4 v = ld4f<TI>(tile + (r + HALO - shifted) * CW + vcol + 4 * c4);
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(tile + (r + HALO - shifted) * CW + vcol + 4 * c4);
       const float vv[4] = {v[0], v[1], v[2], v[3]};
       Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) + row * D + 4 * c4, vv);
     }
@@ -425,11 +439,9 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
     const int jr = active ? j : 0;
     const float2 cs0 = rope_cs_theta(L + jr, s.theta[2 * li], s.rope_base);
     const float2 cs1 = rope_cs_theta(L + jr, s.theta[2 * li + 1], s.rope_base);
-    const float *cur = tile + (3 + jr) * CW + 4 * li;
-    auto conv = [&](int slot, float (&bb)[4]) {
-      conv_slot<D, float>(tile, CW, 3 + jr, slot, li, staps, ctaps, bb);
+    auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
+      conv_slot<D, float>(tile, CW, 3 + jr, slot, li, staps, ctaps, bb, pre);
     };
-    auto pre = [&](int slot) { return ld4f<float>(cur + slot * D); };
     auto emit = [&](int slot, float *y) {
       if (!active) return;
       size_t row;
@@ -438,7 +450,7 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
       else if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
         Store4<TV>::st(kc + row * D + 4 * li, y);
     };
-    mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
+    mix_row<D>(G, s, cs0, cs1, conv, emit);
   }
   // value rows of the new tokens into the cache
   for (int e = tid; e < m * (D / 4); e += 256) {
@@ -558,12 +570,12 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
     const float2 cs0 = rope_cs_theta(L + jr, s.theta[2 * li], s.rope_base);
     const float2 cs1 = rope_cs_theta(L + jr, s.theta[2 * li + 1], s.rope_base);
     const float *cur = tile + (Wt + jr) * CW + 4 * li;
-    auto conv = [&](int slot, float (&bb)[4]) {
+    auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
       const f32x4 v = *reinterpret_cast<const f32x4 *>(bt + jr * QK + slot * D + 4 * li);
 #pragma unroll
       for (int c = 0; c < 4; ++c) bb[c] = v[c];
+      pre = *reinterpret_cast<const f32x4 *>(cur + slot * D);
     };
-    auto pre = [&](int slot) { return ld4f<float>(cur + slot * D); };
     auto emit = [&](int slot, float *y) {
       if (!active) return;
       size_t row;
@@ -572,7 +584,7 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
       else if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
         Store4<TV>::st(kc + row * D + 4 * li, y);
     };
-    mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
+    mix_row<D>(G, s, cs0, cs1, conv, emit);
   }
   for (int e = tid; e < m * (D / 4); e += 256) {
     const int j = e / (D / 4), c4 = e % (D / 4);
@@ -683,11 +695,9 @@ __global__ __launch_bounds__(256, 1) void downproj_mix_kernel(MixShape s, MixTap
     const int tok = t0 + r;
     const float2 cs0 = rope_cs_theta(tok, s.theta[2 * li], s.rope_base);
     const float2 cs1 = rope_cs_theta(tok, s.theta[2 * li + 1], s.rope_base);
-    const float *cur = tile + (r + HALO) * CW + 4 * li;
-    auto conv = [&](int slot, float (&bb)[4]) {
-      conv_slot<D, float>(tile, CW, r + HALO, slot, li, staps, ctaps, bb);
+    auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
+      conv_slot<D, float>(tile, CW, r + HALO, slot, li, staps, ctaps, bb, pre);
     };
-    auto pre = [&](int slot) { return ld4f<float>(cur + slot * D); };
     auto emit = [&](int slot, float *y) {
       if (slot < G) {
         const float sc = tsc[slot];
@@ -698,7 +708,7 @@ __global__ __launch_bounds__(256, 1) void downproj_mix_kernel(MixShape s, MixTap
         Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
       }
     };
-    mix_row<D>(G, s, cs0, cs1, conv, pre, emit);
+    mix_row<D>(G, s, cs0, cs1, conv, emit);
   }
   // value head, transposed: vt[b, g, dd, perm(t)]
   const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
@@ -752,16 +762,16 @@ template hipError_t launch_downproj_mix<bf16, bf16>(const MixShape &, const MixT
                                                     const bf16 *, int, void *, bf16 *, bf16 *,
                                                     bf16 *, hipStream_t);
 
-// LDS of the prefill kernel for chunks of TC tokens, es-byte tile elements.
-static size_t mix_lds_bytes(int TC, int G, int D, int es) {
-  return tile_bytes(TC + HALO, G, D, es) + (size_t)taps_floats(G, D) * 4;
+// LDS of the prefill kernel for chunks of TC tokens (fp32 tile).
+static size_t mix_lds_bytes(int TC, int G, int D) {
+  return tile_bytes(TC + HALO, G, D, 4) + (size_t)taps_floats(G, D) * 4;
 }
 
 // Tokens per workgroup: the largest of 64 / 32 / 16 whose tile stays within
 // 40 KiB (several workgroups per CU keep many rows in flight).
-static int mix_chunk(int G, int D, int es) {
+static int mix_chunk(int G, int D) {
   for (int tc = 64; tc > 16; tc /= 2)
-    if (mix_lds_bytes(tc, G, D, es) <= 40 * 1024) return tc;
+    if (mix_lds_bytes(tc, G, D) <= 40 * 1024) return tc;
   return 16;
 }
 
@@ -773,18 +783,18 @@ bool convmix_decode_fits(int G, int d, int m) {
   return m >= 1 && decode_lds_bytes(3 + m, G, d) <= 65536;
 }
 
-bool convmix_fits(int G, int d, int es) {
-  return mix_lds_bytes(16, G, d, es) <= 65536 && convmix_decode_fits(G, d, 1);
+bool convmix_fits(int G, int d) {
+  return mix_lds_bytes(16, G, d) <= 65536 && convmix_decode_fits(G, d, 1);
 }
 
 template <typename TI, typename TQ, typename TV, int D>
 static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const TI *qkv, TQ *q,
                                     TQ *k, TV *vt, const StateOut &st, const float *r1b,
                                     float *bout, hipStream_t stream) {
-  const int TC = mix_chunk(s.G, D, (int)sizeof(TI));
+  const int TC = mix_chunk(s.G, D);
   const long long grid = (long long)s.B * s.Hkv * (s.Tp / TC);
   if (grid >= (1ll << 31)) return hipErrorInvalidValue;
-  const size_t lds = mix_lds_bytes(TC, s.G, D, (int)sizeof(TI));
+  const size_t lds = mix_lds_bytes(TC, s.G, D);
   hipLaunchKernelGGL((convmix_prefill_kernel<TI, TQ, TV, D>), dim3((unsigned)grid), dim3(256), lds,
                      stream, s, w, qkv, q, k, vt, st, r1b, bout, TC);
   return hipGetLastError();
