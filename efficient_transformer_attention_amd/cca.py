@@ -22,6 +22,7 @@ CCA_BF16, CCA_F32 = 0, 1
 CCA_CHAN_PER_HEAD, CCA_CHAN_GROUPED = 0, 1
 CCA_QK_MEAN_PRE_POST, CCA_QK_MEAN_PRE = 0, 1
 WS_QKV, WS_Q, WS_K, WS_VT, WS_O, WS_PART, WS_SPLITK, WS_COUNT = range(8)
+NOALLOC_SCRATCH_BYTES = 16 << 20       # CCA_NOALLOC_SCRATCH
 
 # Every entry point declared in include/cca.h.
 EXPORTS = (
@@ -34,7 +35,7 @@ EXPORTS = (
     "cca_train_workspace_size", "cca_prefill_forward_train", "cca_prefill_backward",
     "cca_decode_step_paged", "cca_prefill_forward_paged",
     "cca_decode_multi_workspace_size", "cca_decode_multi", "cca_decode_multi_paged",
-    "cca_prefill_forward_fused",
+    "cca_prefill_forward_fused", "cca_decode_step_noalloc",
 )
 
 
@@ -95,6 +96,7 @@ def _load():
         "cca_decode_workspace_layout": (C.c_int, [cfgp, C.c_int32, P(sz)]),
         "cca_prefill_forward": (C.c_int, [cfgp, wp, vp, vp, sp, vp, sz, vp]),
         "cca_decode_step": (C.c_int, [cfgp, wp, vp, C.c_int32, sp, sp, vp, vp, sz, vp]),
+        "cca_decode_step_noalloc": (C.c_int, [cfgp, wp, vp, C.c_int32, sp, sp, vp, vp]),
         "cca_decode_step_varlen": (C.c_int, [cfgp, wp, vp, vp, C.c_int32, sp, sp, vp, vp, sz, vp]),
         "cca_status_string": (C.c_char_p, [C.c_int]),
         "cca_stage_downproj": (C.c_int, [cfgp, wp, vp, vp, sz, vp]),
@@ -279,6 +281,15 @@ def decode_step(cfg: Config, w: Weights, x_t, cache_len: int, state_in: State, s
                                C.byref(state_in.struct()), C.byref(state_out.struct()), _ptr(y_t),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(stream)), "cca_decode_step")
+
+
+def decode_step_noalloc(cfg: Config, w: Weights, x_t, cache_len: int, state_in: State,
+                        state_out: State, y_t, stream=None):
+    """cca_decode_step with the library's own per-GPU scratch array as the
+    workspace (no allocation; calls that overlap on one GPU race)."""
+    _check(lib.cca_decode_step_noalloc(C.byref(cfg), C.byref(w.struct()), _ptr(x_t), int(cache_len),
+                                       C.byref(state_in.struct()), C.byref(state_out.struct()),
+                                       _ptr(y_t), _stream(stream)), "cca_decode_step_noalloc")
 
 
 def decode_step_varlen(cfg: Config, w: Weights, x_t, cache_lens, max_cache_len: int,

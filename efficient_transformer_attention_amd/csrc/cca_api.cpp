@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "cca.h"
@@ -996,6 +997,59 @@ cca_status cca_decode_multi_paged(const cca_config *cfg, const cca_weights *w, c
   CCA_TRY(dec_mix(c, w, max_cache_len, cache_lens, in, out, ws, L, st, n_new));
   CCA_TRY(dec_attn(c, w, max_cache_len, cache_lens, in, ws, L, st, n_new));
   return run_upproj(c, w, y_new, ws, L, c.batch * n_new, st);
+}
+
+}  // extern "C"
+
+// ---- decode step without a caller workspace ----------------------------------
+//
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid allocation): the decode
+// step's workspace lives in a file-scope device array of CCA_NOALLOC_SCRATCH
+// bytes.  Each GPU the library runs on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address: the first call
+// on a device takes the array's device address with hipGetSymbolAddress
+// (that device current) and keeps it per device.
+
+static constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)CCA_NOALLOC_SCRATCH;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_ptrs[MAX_DEVICES] = {};
+
+// The current device's copy of `scratch`.
+cca_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CCA_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return CCA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptrs[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CCA_ERR_HIP;
+    scratch_ptrs[dev] = p;
+  }
+  *out = scratch_ptrs[dev];
+  return CCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cca_status cca_decode_step_noalloc(const cca_config *cfg, const cca_weights *w, const void *x_t,
+                                   int32_t cache_len, const cca_state *si, const cca_state *so,
+                                   void *y_t, void *stream) {
+  CCA_TRY(validate_shape(cfg, false));
+  if (cache_len < 0) return CCA_ERR_INVALID_ARG;
+  // the workspace the step needs must fit the array; checked before any HIP call
+  const size_t need = decode_layout(decode_cfg(cfg), cache_len).total;
+  if (need > NOALLOC_SCRATCH_BYTES) return CCA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  CCA_TRY(scratch_of_current_device(&ws));
+  return cca_decode_step(cfg, w, x_t, cache_len, si, so, y_t, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -359,6 +359,23 @@ cca_status cca_decode_multi_paged(const cca_config *cfg, const cca_weights *w, c
                                   const cca_paged_state *state_out, void *y_new, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* cca_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; the step's workspace is a device array of
+ * CCA_NOALLOC_SCRATCH bytes inside the library, one per GPU, held until the
+ * process ends.  The call allocates nothing.  Its first call on a device
+ * looks up that device's array (hipGetSymbolAddress, the device current).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, different threads) race and must be serialised by the
+ * caller.  Arguments and results as cca_decode_step.  CCA_ERR_WORKSPACE,
+ * before any launch, when cca_decode_workspace_size(cfg, cache_len) exceeds
+ * CCA_NOALLOC_SCRATCH (the decode workload of 64 sequences, 16 query / 4 kv
+ * heads of 64, E = 2048 and a 32768-token cache needs 7.8 MiB). */
+#define CCA_NOALLOC_SCRATCH (16u << 20)
+cca_status cca_decode_step_noalloc(const cca_config *cfg, const cca_weights *w, const void *x_t,
+                                   int32_t cache_len, const cca_state *state_in,
+                                   const cca_state *state_out, void *y_t, void *stream);
+
 /* Static description of a status code. */
 const char *cca_status_string(cca_status s);
 

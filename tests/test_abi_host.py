@@ -316,3 +316,24 @@ def test_grouped_channel_conv_validation(L):
                                    head_dim=64), chan_conv="grouped")
     assert L.lib.cca_prefill_forward_fused(C.byref(fused), C.byref(w), 0x10000, 0x20000, 0x100000,
                                            1 << 30, None) == L.CCA_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_rejects_oversized_workspace_before_launch(L):
+    """cca_decode_step_noalloc refuses a step whose workspace exceeds its
+    scratch array, before any HIP call (host-only)."""
+    from synth import workload
+    base = workload("ccgqa_decode_b64_l32768")
+    B = 64
+    while L.decode_workspace_size(L.make_config(base.with_(batch=B)), base.cache_len) <= \
+            L.NOALLOC_SCRATCH_BYTES:
+        B *= 2
+    cfg = L.make_config(base.with_(batch=B))
+    w = _fake_weights(L)
+    st = L._State(0x10000, 0x10000, base.cache_len + 1, 0, 0x10000, 0x10000, 0x10000)
+    r = L.lib.cca_decode_step_noalloc(C.byref(cfg), C.byref(w), 0x10000, base.cache_len,
+                                      C.byref(st), C.byref(st), 0x20000, None)
+    assert r == L.CCA_ERR_WORKSPACE
+    # and an invalid configuration is rejected as for cca_decode_step
+    bad = L.make_config(base.with_(n_kv_heads=3, n_q_heads=3))
+    assert L.lib.cca_decode_step_noalloc(C.byref(bad), C.byref(w), 0x10000, 5, C.byref(st),
+                                         C.byref(st), 0x20000, None) == L.CCA_ERR_INVALID_ARG
