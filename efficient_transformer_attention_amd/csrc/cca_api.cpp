@@ -687,6 +687,9 @@ static cca_status decode_checks(const cca_config *cfg, const cca_weights *w, int
   return check_ws(ws, wsb, lay->total);
 }
 
+// The decode down-projection.  With few rows it leaves the split-contraction
+// partials in CCA_WS_SPLITK for the mixing kernel to sum (no reduction
+// launch); dec_qkv() describes what it left.
 static cca_status dec_downproj(const cca_config &c, const cca_weights *w, const void *x_t,
                                void *ws, const Layout &L, hipStream_t st, int m = 1) {
   const int M = c.batch * m, E = c.d_model;
@@ -694,14 +697,27 @@ static cca_status dec_downproj(const cca_config &c, const cca_weights *w, const 
   float *qkv = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_QKV));
   size_t skf;
   float *sk = splitk_ptr(ws, L, &skf);
+  int slices = 0;
   hipError_t e;
   if (c.dtype == CCA_BF16)
-    e = launch_gemm_nt<bf16, float>((const bf16 *)x_t, (const bf16 *)w->w_qkv, qkv, M, N, E, E, E,
-                                    N, st, sk, skf);
+    e = launch_gemm_nt_partials<bf16>((const bf16 *)x_t, (const bf16 *)w->w_qkv, qkv, M, N, E, E,
+                                      E, sk, skf, &slices, st);
   else
-    e = launch_gemm_nt<float, float>((const float *)x_t, (const float *)w->w_qkv, qkv, M, N, E, E,
-                                     E, N, st, sk, skf);
+    e = launch_gemm_nt_partials<float>((const float *)x_t, (const float *)w->w_qkv, qkv, M, N, E,
+                                       E, E, sk, skf, &slices, st);
   return check_launch(e, st);
+}
+
+static DecQkv dec_qkv(const cca_config &c, void *ws, const Layout &L, int m) {
+  const int M = c.batch * m, E = c.d_model;
+  const int N = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  size_t skf;
+  float *sk = splitk_ptr(ws, L, &skf);
+  DecQkv d;
+  d.qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
+  d.parts = sk;
+  d.slices = sk ? gemm_nt_partial_slices(M, N, E, (int)elem_size(c.dtype), skf) : 0;
+  return d;
 }
 
 static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
@@ -710,7 +726,7 @@ static cca_status dec_mix(const cca_config &c, const cca_weights *w, int32_t Lc,
   MixShape s = mix_shape(c);
   s.T = m;                       // new tokens per sequence
   s.Tp = m;
-  const float *qkv = reinterpret_cast<const float *>(wsp(ws, L, CCA_WS_QKV));
+  const DecQkv qkv = dec_qkv(c, ws, L, m);
   float *q = reinterpret_cast<float *>(wsp(ws, L, CCA_WS_Q));
   hipError_t e;
   if (c.chan_conv_mode == CCA_CHAN_GROUPED) {

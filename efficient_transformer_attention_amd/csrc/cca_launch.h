@@ -20,6 +20,17 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
 // Contraction slices the skinny path uses for an M x N x K product.
 int gemm_splitk_slices(int M, int N, int K, int elem_bytes);
 
+// The skinny split-contraction product without its reduction kernel: with
+// M <= 64 and room in splitk_ws, writes the S fp32 partial products
+// [S][M][N] there and sets *slices = S (gemm_nt_partial_slices); otherwise
+// writes the fp32 product to C (ldc = N) and sets *slices = 0.  Consumers sum
+// slice 0 .. S-1 in that order.
+int gemm_nt_partial_slices(int M, int N, int K, int elem_bytes, size_t splitk_floats);
+template <typename Tin>
+hipError_t launch_gemm_nt_partials(const Tin *A, const Tin *B, float *C, int M, int N, int K,
+                                   int lda, int ldb, float *splitk_ws, size_t splitk_floats,
+                                   int *slices, hipStream_t stream);
+
 // C[M,N] (fp32, ldc = N) = A[M,K] * B[N,K]^T for few output tiles and a long
 // contraction (weight gradients): the contraction is split over
 // gemm_long_k_slices() workgroup slices whose fp32 partials go to ws
@@ -124,13 +135,21 @@ hipError_t launch_grouped_conv_prefill(const MixShape &s, const MixTaps &w, cons
                                        bool f32, hipStream_t stream);
 bool grouped_conv_supported(int d, bool f32);
 
+// The down-projection output of a decode step: qkv [M, N] fp32 when
+// slices == 0, else the sum over s < slices of parts [slices][M][N] (the
+// split-contraction partials, summed in slice order).
+struct DecQkv {
+  const float *qkv, *parts;
+  int slices;
+};
+
 // The same mixing for m = s.T new tokens per sequence at positions L .. L+m-1
 // (L per sequence lens[b], clamped to [0, L], when lens is not null), using
-// the carried window / vshift of state_in; qkv is [B*m, e_q + 2 e_kv]; writes
-// q (fp32 [B, m, Hq, d]), the k and v rows at those cache slots, and the
-// rolled state into state_out.
+// the carried window / vshift of state_in; the down-projection output has
+// rows [B*m, e_q + 2 e_kv]; writes q (fp32 [B, m, Hq, d]), the k and v rows
+// at those cache slots, and the rolled state into state_out.
 template <typename TV>
-hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const float *qkv, int L,
+hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const DecQkv &qkv, int L,
                                  const int *lens, const StateOut &in, const StateOut &out,
                                  float *q, hipStream_t stream);
 
@@ -139,7 +158,7 @@ hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const floa
 // rows and the dense per-lag channel weights (fp32 [H, d, k_c, d]).
 template <typename TV>
 hipError_t launch_convmix_decode_grouped(const MixShape &s, const MixTaps &w, const float *dense_q,
-                                         const float *dense_k, const float *qkv, int L,
+                                         const float *dense_k, const DecQkv &qkv, int L,
                                          const int *lens, const StateOut &in, const StateOut &out,
                                          float *q, hipStream_t stream);
 bool convmix_decode_grouped_fits(int G, int d, int m, int ks, int kc);

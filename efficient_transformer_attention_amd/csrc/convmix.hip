@@ -190,9 +190,68 @@ __device__ __forceinline__ void load_taps(const MixShape &s, const MixTaps &w, i
   for (int h = threadIdx.x; h < G; h += blockDim.x) tsc[h] = w.tau[g * G + h] * 1.4426950408889634f;
 }
 
+// The group's taps and tau scales held in registers between their loads and
+// their LDS stores (the layout of load_taps), so that the loads can be
+// issued before other work: thread t owns seq-tap channels t + 256 i
+// ((G + 1) d < 1024 when (G + 2) d / 4 <= 256, which the host checks;
+// zero-padded past k_s), channel-tap / tau slot t.
+template <int D> struct TapRegs {
+  static constexpr int NS = 4;
+  f32x4 sq[NS];
+  f32x4 ch;
+  float tau;
+  __device__ __forceinline__ void load(const MixShape &s, const MixTaps &w, int g) {
+    const int G = s.G, t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int c = t + 256 * i;
+      sq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < (G + 1) * D) {
+        const float *src = c < G * D ? w.q_seq + (size_t)(g * G * D + c) * s.ks
+                                     : w.k_seq + (size_t)(g * D + c - G * D) * s.ks;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sq[i][j] = j < s.ks ? src[j] : 0.f;
+      }
+    }
+    ch = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t < G + 1) {
+      const float *src = t < G ? w.q_chan + (size_t)(g * G + t) * s.kc : w.k_chan + (size_t)g * s.kc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ch[j] = j < s.kc ? src[j] : 0.f;
+    }
+    tau = t < G ? w.tau[g * G + t] * 1.4426950408889634f : 0.f;
+  }
+  __device__ __forceinline__ void store(const MixShape &s, float *staps, float *ctaps, float *tsc) const {
+    const int G = s.G, t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (t + 256 * i < (G + 1) * D) *reinterpret_cast<f32x4 *>(staps + (t + 256 * i) * 4) = sq[i];
+    if (t < G + 1) *reinterpret_cast<f32x4 *>(ctaps + t * 4) = ch;
+    if (t < G) tsc[t] = tau;
+  }
+};
+
 // Floats of the tap area after the tile: seq taps, channel taps, tau scales.
 __host__ __device__ inline int taps_floats(int G, int D) {
   return (G + 1) * D * 4 + (G + 1) * 4 + (G + 3) / 4 * 4;
+}
+
+// Element i of a decode step's down-projection output (see DecQkv).
+// The slices are summed in order; their loads go out four at a time.
+__device__ __forceinline__ float dec_qkv(const DecQkv &d, size_t i, size_t mn) {
+  if (d.slices == 0) return d.qkv[i];
+  const float *p = d.parts + i;
+  float acc = p[0];
+  int sl = 1;
+  for (; sl + 4 <= d.slices; sl += 4) {
+    const float a0 = p[sl * mn], a1 = p[(sl + 1) * mn], a2 = p[(sl + 2) * mn], a3 = p[(sl + 3) * mn];
+    acc += a0;
+    acc += a1;
+    acc += a2;
+    acc += a3;
+  }
+  for (; sl < d.slices; ++sl) acc += p[sl * mn];
+  return acc;
 }
 
 // Map a column of the group tile to its column in the qkv row.
@@ -207,7 +266,12 @@ __host__ __device__ inline size_t tile_bytes(int rows, int G, int D, int es) {
   return ((size_t)rows * (G + 2) * D * es + 15) / 16 * 16;
 }
 
-template <typename TI, typename TQ, typename TV, int D>
+// MEAN: the q-k-mean mode (s.use_mean: 0 off, 1 pre-conv, 2 pre- and
+// post-conv); R1B: the channel conv's output comes from r1b (the grouped
+// reading) instead of the two convolutions; OUT: some of the cache, the
+// conv window, vshift or bout is written (without it none of that code is
+// in the kernel).
+template <typename TI, typename TQ, typename TV, int D, int MEAN, bool R1B, bool OUT>
 __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTaps w,
                                                               const TI *__restrict__ qkv,
                                                               TQ *__restrict__ q, TQ *__restrict__ k,
@@ -234,33 +298,43 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   const int vcol = (G + 1) * D;
   const TI *src = qkv + (size_t)b * s.T * N;
 
-  // the tile, in fp32: 16-byte chunks of the down-projection output, in
-  // batches of 8 per thread (every load of a batch issued before its LDS
-  // stores), converted once on the way in; tokens outside [0, T) read as zero
+  // the group's taps, tau and this lane's RoPE frequencies are requested
+  // first, so their latency overlaps the tile's
+  TapRegs<D> tr;
+  tr.load(s, w, g);
+  constexpr int LPU = D / 4;
+  const int li = tid % LPU, ui = tid / LPU;
+  const double th0 = s.theta[2 * li], th1 = s.theta[2 * li + 1];
+
+  // the tile, in fp32: each thread owns one 16-byte column chunk of the
+  // group and walks the rows with a fixed stride (all loads of a batch of
+  // rows issued before their LDS stores, converted once on the way in);
+  // tokens outside [0, T) read as zero
   {
-    constexpr int EPC = 16 / (int)sizeof(TI), NB = 8;
-    const int cpr = CW / EPC, total = (TC + HALO) * cpr;
-    for (int e0 = 0; e0 < total; e0 += 256 * NB) {
+    constexpr int EPC = 16 / (int)sizeof(TI), NB = 4;
+    const int cpr = CW / EPC, rstep = 256 / cpr;          // cpr <= 256 (checked on the host)
+    const int cc = tid % cpr, r0 = tid / cpr;
+    const bool col_active = r0 < rstep;
+    const TI *colp = src + group_col(cc * EPC, g, G, D, eq, ekv);
+    float *dcol = tile + cc * EPC;
+    const int rows = TC + HALO;
+    for (int rb = r0; rb < rows; rb += rstep * NB) {
       u32x4 v[NB];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int e = e0 + tid + 256 * u;
-        const int r = e / cpr, cc = e - r * cpr, tok = t0 - HALO + r;
+        const int r = rb + rstep * u, tok = t0 - HALO + r;
         v[u] = zero_u32x4();
-        if (e < total && tok >= 0 && tok < s.T)
-          v[u] = ld16(src + (size_t)tok * N + group_col(cc * EPC, g, G, D, eq, ekv));
+        if (col_active && r < rows && tok >= 0 && tok < s.T) v[u] = ld16(colp + tok * N);
       }
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int e = e0 + tid + 256 * u;
-        if (e < total) {
-          const int r = e / cpr, cc = e - r * cpr;
-          float *dst = tile + r * CW + cc * EPC;
+        const int r = rb + rstep * u;
+        if (col_active && r < rows) {
+          float *dst = dcol + r * CW;
           if constexpr (EPC == 8) {
-            const f32x4 lo = ld4f<TI>(reinterpret_cast<const TI *>(&v[u])),
-                        hi = ld4f<TI>(reinterpret_cast<const TI *>(&v[u]) + 4);
-            *reinterpret_cast<f32x4 *>(dst) = lo;
-            *reinterpret_cast<f32x4 *>(dst + 4) = hi;
+            const TI *h = reinterpret_cast<const TI *>(&v[u]);
+            *reinterpret_cast<f32x4 *>(dst) = ld4f<TI>(h);
+            *reinterpret_cast<f32x4 *>(dst + 4) = ld4f<TI>(h + 4);
           } else {
             st16(dst, v[u]);
           }
@@ -268,18 +342,23 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
       }
     }
   }
-  load_taps<D>(s, w, g, staps, ctaps, tsc);
+  tr.store(s, staps, ctaps, tsc);
   __syncthreads();
 
   // one token row per lane group, every head slot of the group
-  constexpr int LPU = D / 4;
   const int upp = 256 / LPU;
-  const int li = tid % LPU, ui = tid / LPU;
-  TV *kcache = reinterpret_cast<TV *>(st.k_cache);
+  MixShape sm = s;
+  sm.use_mean = MEAN;
+  // per-lane bases: row r of this chunk adds r * D to the q / k offsets
+  TQ *qlane = q + ((size_t)(b * s.Hq + g * G) * s.Tp + t0) * D + 4 * li;
+  TQ *klane = k + ((size_t)(b * s.Hkv + g) * s.Tp + t0) * D + 4 * li;
+  const size_t qhead = (size_t)s.Tp * D;               // between the group's query heads
+  TV *kcache = OUT ? reinterpret_cast<TV *>(st.k_cache) : nullptr;
+  float *blane = OUT && bout ? bout + (size_t)b * s.T * (eq + ekv) + 4 * li : nullptr;
   for (int r = ui; r < TC; r += upp) {
     const int tok = t0 + r;
-    const float2 cs0 = rope_cs_theta(tok, s.theta[2 * li], s.rope_base);
-    const float2 cs1 = rope_cs_theta(tok, s.theta[2 * li + 1], s.rope_base);
+    const float2 cs0 = rope_cs_theta(tok, th0, s.rope_base);
+    const float2 cs1 = rope_cs_theta(tok, th1, s.rope_base);
     const float *cur = tile + (r + HALO) * CW + 4 * li;
     auto emit = [&](int slot, float *y) {
       if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
@@ -287,15 +366,17 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
         const float sc = tsc[slot];
 #pragma unroll
         for (int c = 0; c < 4; ++c) y[c] *= sc;
-        Store4<TQ>::st(q + ((size_t)(b * s.Hq + g * G + slot) * s.Tp + tok) * D + 4 * li, y);
+        Store4<TQ>::st(qlane + slot * qhead + r * D, y);
       } else {
-        Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
-        size_t row;
-        if (kcache && tok < s.T && cache_row_store(st, b, s.Hkv, g, tok, &row))
-          Store4<TV>::st(kcache + row * D + 4 * li, y);
+        Store4<TQ>::st(klane + r * D, y);
+        if constexpr (OUT) {
+          size_t row;
+          if (kcache && tok < s.T && cache_row_store(st, b, s.Hkv, g, tok, &row))
+            Store4<TV>::st(kcache + row * D + 4 * li, y);
+        }
       }
     };
-    if (r1b) {
+    if constexpr (R1B) {
       // grouped channel conv: b comes from the MFMA kernel's output rows
       const float *brow = r1b + (size_t)(b * s.T + min(tok, s.T - 1)) * (eq + ekv) + 4 * li;
       auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
@@ -306,16 +387,16 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
         for (int c = 0; c < 4; ++c) bb[c] = v[c];
         pre = *reinterpret_cast<const f32x4 *>(cur + slot * D);
       };
-      mix_row<D>(G, s, cs0, cs1, conv, emit);
+      mix_row<D>(G, sm, cs0, cs1, conv, emit);
     } else {
       auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
         conv_slot<D, float>(tile, CW, r + HALO, slot, li, staps, ctaps, bb, pre);
-        if (bout && tok < s.T)
-          *reinterpret_cast<f32x4 *>(bout + (size_t)(b * s.T + tok) * (eq + ekv) +
-                                     (slot < G ? (g * G + slot) * D : eq + g * D) + 4 * li) =
+        if (OUT && blane && tok < s.T)
+          *reinterpret_cast<f32x4 *>(blane + (size_t)tok * (eq + ekv) +
+                                     (slot < G ? (g * G + slot) * D : eq + g * D)) =
               f32x4{bb[0], bb[1], bb[2], bb[3]};
       };
-      mix_row<D>(G, s, cs0, cs1, conv, emit);
+      mix_row<D>(G, sm, cs0, cs1, conv, emit);
     }
   }
 
@@ -332,7 +413,7 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
     Store4<TV>::st(dst, vals);
     Store4<TV>::st(dst + 4, vals + 4);
   }
-  if (st.v_cache) {
+  if (OUT && st.v_cache) {
     for (int e = tid; e < TC * (D / 4); e += 256) {
       const int r = e / (D / 4), c4 = e % (D / 4), tok = t0 + r;
       if (tok >= s.T) continue;
@@ -346,7 +427,7 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
 
   // decode state after the last token: conv window (k_s - 1 pre-conv rows,
   // plus k_c - 1 under the grouped channel conv) and value-shift state
-  if (chunk == 0) {
+  if (OUT && chunk == 0) {
     const int ks1 = s.ks - 1 + (s.grouped ? s.kc - 1 : 0);
     if (st.conv_q)
       for (int e = tid; e < ks1 * G * D; e += 256) {
@@ -374,8 +455,7 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
 // barrier, so state_out may alias state_in.
 template <typename TV, int D>
 __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps w,
-                                                             const float *__restrict__ qkv,
-                                                             int Lmax,
+                                                             DecQkv qkv, int Lmax,
                                                              const int *__restrict__ lens,
                                                              StateOut in, StateOut out,
                                                              float *__restrict__ qout) {
@@ -396,20 +476,24 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
   const TV *cq = reinterpret_cast<const TV *>(in.conv_q);
   const TV *ck = reinterpret_cast<const TV *>(in.conv_k);
   const TV *vs = reinterpret_cast<const TV *>(in.vshift);
+  // taps, tau and this lane's RoPE frequencies first: their latency overlaps the tile's
+  TapRegs<D> tr;
+  tr.load(s, w, g);
+  constexpr int LPU = D / 4;
+  const int li = tid % LPU, ui = tid / LPU;
+  const double th0 = s.theta[2 * li], th1 = s.theta[2 * li + 1];
 
-  // all loads of the tile are issued before their LDS stores
+  // the three carried rows (all loads issued before their LDS stores)
   constexpr int LB = 8;
-  for (int e0 = 0; e0 < R * CW; e0 += 256 * LB) {
+  for (int e0 = 0; e0 < 3 * CW; e0 += 256 * LB) {
     float v[LB];
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
       const int e = e0 + tid + 256 * u;
       const int r = e / CW, col = e % CW;
       v[u] = 0.f;
-      if (e >= R * CW) continue;
-      if (r >= 3) {
-        v[u] = qkv[(size_t)(b * m + r - 3) * N + group_col(col, g, G, D, eq, ekv)];
-      } else if (r >= 4 - s.ks && col < (G + 1) * D) {
+      if (e >= 3 * CW) continue;
+      if (r >= 4 - s.ks && col < (G + 1) * D) {
         const int sl = r - (4 - s.ks);           // window slot of token L-3+r
         v[u] = col < G * D ? to_f32(cq[(size_t)(b * ks1 + sl) * eq + g * G * D + col])
                            : to_f32(ck[(size_t)(b * ks1 + sl) * ekv + g * D + col - G * D]);
@@ -420,15 +504,34 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
       const int e = e0 + tid + 256 * u;
-      if (e < R * CW) tile[e] = v[u];
+      if (e < 3 * CW) tile[e] = v[u];
     }
   }
-  load_taps<D>(s, w, g, staps, ctaps, tsc);
+  // the m new rows: the down-projection output, or the sum of its
+  // split-contraction slices in slice order (all slice loads of an element
+  // issued before the sum)
+  for (int e = tid; e < m * CW; e += 256) {
+    const int j = e / CW, col = e % CW;
+    const size_t i = (size_t)(b * m + j) * N + group_col(col, g, G, D, eq, ekv);
+    float acc;
+    if (qkv.slices == 0) {
+      acc = qkv.qkv[i];
+    } else {
+      const size_t mn = (size_t)s.B * m * N;
+      float a[16];
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) a[sl] = sl < qkv.slices ? qkv.parts[sl * mn + i] : 0.f;
+      acc = a[0];
+#pragma unroll
+      for (int sl = 1; sl < 16; ++sl)
+        if (sl < qkv.slices) acc += a[sl];
+    }
+    tile[(3 + j) * CW + col] = acc;
+  }
+  tr.store(s, staps, ctaps, tsc);
   __syncthreads();
 
-  constexpr int LPU = D / 4;
   const int upp = 256 / LPU;
-  const int li = tid % LPU, ui = tid / LPU;
   TV *kc = reinterpret_cast<TV *>(in.k_cache);
   TV *vc = reinterpret_cast<TV *>(in.v_cache);
   // one new token per lane group; groups past the last token compute on row
@@ -437,8 +540,8 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
     const int j = j0 + ui;
     const bool active = j < m;
     const int jr = active ? j : 0;
-    const float2 cs0 = rope_cs_theta(L + jr, s.theta[2 * li], s.rope_base);
-    const float2 cs1 = rope_cs_theta(L + jr, s.theta[2 * li + 1], s.rope_base);
+    const float2 cs0 = rope_cs_theta(L + jr, th0, s.rope_base);
+    const float2 cs1 = rope_cs_theta(L + jr, th1, s.rope_base);
     auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
       conv_slot<D, float>(tile, CW, 3 + jr, slot, li, staps, ctaps, bb, pre);
     };
@@ -487,7 +590,7 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
 template <typename TV, int D>
 __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
     MixShape s, MixTaps w, const float *__restrict__ dense_q, const float *__restrict__ dense_k,
-    const float *__restrict__ qkv, int Lmax, const int *__restrict__ lens, StateOut in,
+    DecQkv qkv, int Lmax, const int *__restrict__ lens, StateOut in,
     StateOut out, float *__restrict__ qout) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int G = s.G, CW = (G + 2) * D, QK = (G + 1) * D;
@@ -512,7 +615,8 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
     const int r = e / CW, col = e % CW;
     float v = 0.f;
     if (r >= Wt) {
-      v = qkv[(size_t)(b * m + r - Wt) * N + group_col(col, g, G, D, eq, ekv)];
+      v = dec_qkv(qkv, (size_t)(b * m + r - Wt) * N + group_col(col, g, G, D, eq, ekv),
+                  (size_t)s.B * m * N);
     } else if (col < QK) {
       const int sl = r - (Wt - W);               // window slot of token L - Wt + r
       if (sl >= 0)
@@ -784,20 +888,50 @@ bool convmix_decode_fits(int G, int d, int m) {
 }
 
 bool convmix_fits(int G, int d) {
-  return mix_lds_bytes(16, G, d) <= 65536 && convmix_decode_fits(G, d, 1);
+  // the prefill staging gives each thread one 16-byte column chunk of a row
+  return (G + 2) * d / 4 <= 256 && mix_lds_bytes(16, G, d) <= 65536 && convmix_decode_fits(G, d, 1);
+}
+
+template <typename TI, typename TQ, typename TV, int D, int MEAN, bool R1B, bool OUT>
+static hipError_t convmix_prefill_launch(const MixShape &s, const MixTaps &w, const TI *qkv, TQ *q,
+                                         TQ *k, TV *vt, const StateOut &st, const float *r1b,
+                                         float *bout, hipStream_t stream) {
+  const int TC = mix_chunk(s.G, D);
+  const long long grid = (long long)s.B * s.Hkv * (s.Tp / TC);
+  if (grid >= (1ll << 31)) return hipErrorInvalidValue;
+  const size_t lds = mix_lds_bytes(TC, s.G, D);
+  hipLaunchKernelGGL((convmix_prefill_kernel<TI, TQ, TV, D, MEAN, R1B, OUT>), dim3((unsigned)grid),
+                     dim3(256), lds, stream, s, w, qkv, q, k, vt, st, r1b, bout, TC);
+  return hipGetLastError();
 }
 
 template <typename TI, typename TQ, typename TV, int D>
 static hipError_t convmix_prefill_d(const MixShape &s, const MixTaps &w, const TI *qkv, TQ *q,
                                     TQ *k, TV *vt, const StateOut &st, const float *r1b,
                                     float *bout, hipStream_t stream) {
-  const int TC = mix_chunk(s.G, D);
-  const long long grid = (long long)s.B * s.Hkv * (s.Tp / TC);
-  if (grid >= (1ll << 31)) return hipErrorInvalidValue;
-  const size_t lds = mix_lds_bytes(TC, s.G, D);
-  hipLaunchKernelGGL((convmix_prefill_kernel<TI, TQ, TV, D>), dim3((unsigned)grid), dim3(256), lds,
-                     stream, s, w, qkv, q, k, vt, st, r1b, bout, TC);
-  return hipGetLastError();
+#define CCA_MIX_LAUNCH(M, R, O) \
+  convmix_prefill_launch<TI, TQ, TV, D, M, R, O>(s, w, qkv, q, k, vt, st, r1b, bout, stream)
+  const bool out = st.k_cache || st.v_cache || st.conv_q || st.conv_k || st.vshift || bout;
+  if (r1b) {   // the grouped reading, always with the outputs switch on
+    switch (s.use_mean) {
+      case 0: return CCA_MIX_LAUNCH(0, true, true);
+      case 1: return CCA_MIX_LAUNCH(1, true, true);
+      default: return CCA_MIX_LAUNCH(2, true, true);
+    }
+  }
+  if (out) {
+    switch (s.use_mean) {
+      case 0: return CCA_MIX_LAUNCH(0, false, true);
+      case 1: return CCA_MIX_LAUNCH(1, false, true);
+      default: return CCA_MIX_LAUNCH(2, false, true);
+    }
+  }
+  switch (s.use_mean) {
+    case 0: return CCA_MIX_LAUNCH(0, false, false);
+    case 1: return CCA_MIX_LAUNCH(1, false, false);
+    default: return CCA_MIX_LAUNCH(2, false, false);
+  }
+#undef CCA_MIX_LAUNCH
 }
 
 template <typename TI, typename TQ, typename TV>
@@ -814,7 +948,7 @@ hipError_t launch_convmix_prefill(const MixShape &s, const MixTaps &w, const TI 
 }
 
 template <typename TV, int D>
-static hipError_t convmix_decode_d(const MixShape &s, const MixTaps &w, const float *qkv, int L,
+static hipError_t convmix_decode_d(const MixShape &s, const MixTaps &w, const DecQkv &qkv, int L,
                                    const int *lens,
                                    const StateOut &in, const StateOut &out, float *q,
                                    hipStream_t stream) {
@@ -825,7 +959,7 @@ static hipError_t convmix_decode_d(const MixShape &s, const MixTaps &w, const fl
 }
 
 template <typename TV>
-hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const float *qkv, int L,
+hipError_t launch_convmix_decode(const MixShape &s, const MixTaps &w, const DecQkv &qkv, int L,
                                  const int *lens, const StateOut &in, const StateOut &out, float *q,
                                  hipStream_t stream) {
   switch (s.d) {
@@ -849,7 +983,7 @@ bool convmix_decode_grouped_fits(int G, int d, int m, int ks, int kc) {
 
 template <typename TV, int D>
 static hipError_t convmix_decode_grouped_d(const MixShape &s, const MixTaps &w, const float *dq,
-                                           const float *dk, const float *qkv, int L,
+                                           const float *dk, const DecQkv &qkv, int L,
                                            const int *lens, const StateOut &in,
                                            const StateOut &out, float *q, hipStream_t stream) {
   const size_t lds = decode_grouped_lds_bytes(s.G, D, s.T, s.ks, s.kc);
@@ -861,7 +995,7 @@ static hipError_t convmix_decode_grouped_d(const MixShape &s, const MixTaps &w, 
 
 template <typename TV>
 hipError_t launch_convmix_decode_grouped(const MixShape &s, const MixTaps &w, const float *dense_q,
-                                         const float *dense_k, const float *qkv, int L,
+                                         const float *dense_k, const DecQkv &qkv, int L,
                                          const int *lens, const StateOut &in, const StateOut &out,
                                          float *q, hipStream_t stream) {
   switch (s.d) {
@@ -873,11 +1007,11 @@ hipError_t launch_convmix_decode_grouped(const MixShape &s, const MixTaps &w, co
 }
 
 template hipError_t launch_convmix_decode_grouped<bf16>(const MixShape &, const MixTaps &,
-                                                        const float *, const float *, const float *,
+                                                        const float *, const float *, const DecQkv &,
                                                         int, const int *, const StateOut &,
                                                         const StateOut &, float *, hipStream_t);
 template hipError_t launch_convmix_decode_grouped<float>(const MixShape &, const MixTaps &,
-                                                         const float *, const float *, const float *,
+                                                         const float *, const float *, const DecQkv &,
                                                          int, const int *, const StateOut &,
                                                          const StateOut &, float *, hipStream_t);
 
@@ -893,10 +1027,10 @@ template hipError_t launch_convmix_prefill<float, float, float>(const MixShape &
                                                                 const float *, float *, float *,
                                                                 float *, const StateOut &,
                                                                 hipStream_t, const float *, float *);
-template hipError_t launch_convmix_decode<bf16>(const MixShape &, const MixTaps &, const float *,
+template hipError_t launch_convmix_decode<bf16>(const MixShape &, const MixTaps &, const DecQkv &,
                                                 int, const int *, const StateOut &, const StateOut &, float *,
                                                 hipStream_t);
-template hipError_t launch_convmix_decode<float>(const MixShape &, const MixTaps &, const float *,
+template hipError_t launch_convmix_decode<float>(const MixShape &, const MixTaps &, const DecQkv &,
                                                 int, const int *, const StateOut &, const StateOut &, float *,
                                                  hipStream_t);
 

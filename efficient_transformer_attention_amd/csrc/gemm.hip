@@ -484,6 +484,44 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
   return hipGetLastError();
 }
 
+// The split-contraction product without its reduction: for M <= 64 and room
+// for the slices, the S fp32 partial products [S][M][N] go to splitk_ws and
+// S is returned; otherwise the product goes to C (fp32, ldc = N) and 0 is
+// returned.  A consumer sums the slices in order s = 0 .. S-1 (the order of
+// splitk_reduce_kernel).
+int gemm_nt_partial_slices(int M, int N, int K, int elem_bytes, size_t splitk_floats) {
+  if (M > 64 || (N % 4) != 0) return 0;
+  const int BK = 128 / elem_bytes;
+  const int S = gemm_splitk_slices(M, N, K, elem_bytes);
+  const int ksteps = (K + BK - 1) / BK;
+  const int kchunk = (ksteps + S - 1) / S * BK;
+  const int Sused = (K + kchunk - 1) / kchunk;
+  return (size_t)Sused * M * N <= splitk_floats ? Sused : 0;
+}
+
+template <typename Tin>
+hipError_t launch_gemm_nt_partials(const Tin *A, const Tin *B, float *C, int M, int N, int K,
+                                   int lda, int ldb, float *splitk_ws, size_t splitk_floats,
+                                   int *slices, hipStream_t stream) {
+  *slices = splitk_ws ? gemm_nt_partial_slices(M, N, K, (int)sizeof(Tin), splitk_floats) : 0;
+  if (*slices == 0) return launch_gemm_nt<Tin, float>(A, B, C, M, N, K, lda, ldb, N, stream);
+  constexpr int BM = 64, BN = 64, BK = 128 / (int)sizeof(Tin);
+  const int S = gemm_splitk_slices(M, N, K, (int)sizeof(Tin));
+  const int ksteps = (K + BK - 1) / BK;
+  const int kchunk = (ksteps + S - 1) / S * BK;
+  const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_nt_kernel<Tin, float, BM, BN>), dim3(grid, *slices), dim3(256), 0,
+                     stream, A, B, splitk_ws, M, N, K, lda, ldb, N, kchunk);
+  return hipGetLastError();
+}
+
+template hipError_t launch_gemm_nt_partials<bf16>(const bf16 *, const bf16 *, float *, int, int,
+                                                  int, int, int, float *, size_t, int *,
+                                                  hipStream_t);
+template hipError_t launch_gemm_nt_partials<float>(const float *, const float *, float *, int, int,
+                                                   int, int, int, float *, size_t, int *,
+                                                   hipStream_t);
+
 // Contraction slices for a product with few output tiles and a long K (the
 // weight gradients): enough 128 x 128 tiles x slices for one round of two
 // workgroups per CU (more slices only add fp32 partial traffic), slices of
