@@ -21,6 +21,7 @@ CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_WORKSPACE, CCA_ERR_HIP
 CCA_BF16, CCA_F32 = 0, 1
 CCA_CHAN_PER_HEAD, CCA_CHAN_GROUPED = 0, 1
 CCA_QK_MEAN_PRE_POST, CCA_QK_MEAN_PRE = 0, 1
+CCA_ATTN_AUTO, CCA_ATTN_FOUR_WAVE, CCA_ATTN_PING_PONG = 0, 1, 2
 WS_QKV, WS_Q, WS_K, WS_VT, WS_O, WS_PART, WS_SPLITK, WS_COUNT = range(8)
 NOALLOC_SCRATCH_BYTES = 16 << 20       # CCA_NOALLOC_SCRATCH
 
@@ -52,7 +53,7 @@ class Config(C.Structure):
         ("seq_conv_k", C.c_int32), ("chan_conv_k", C.c_int32),
         ("use_qk_mean", C.c_int32), ("use_value_shift", C.c_int32), ("use_qk_norm", C.c_int32),
         ("rope_base", C.c_float), ("norm_eps", C.c_float), ("dtype", C.c_int32),
-        ("chan_conv_mode", C.c_int32), ("qk_mean_mode", C.c_int32),
+        ("chan_conv_mode", C.c_int32), ("qk_mean_mode", C.c_int32), ("attn_kernel", C.c_int32),
     ]
 
 
@@ -134,21 +135,24 @@ def status_string(status: int) -> str:
     return lib.cca_status_string(int(status)).decode()
 
 
-def make_config(shape, chan_conv: str = "per_head", qk_mean: str = "pre_post") -> Config:
+def make_config(shape, chan_conv: str = "per_head", qk_mean: str = "pre_post",
+                attn: str = "auto") -> Config:
     """Config from any object with the cca_config field names (dtype given as
     "bf16" / "f32" or as the enum value); ``chan_conv`` "per_head" or
     "grouped" selects the channel-conv reading, ``qk_mean`` "pre_post" or
-    "pre" the q-k-mean reading."""
+    "pre" the q-k-mean reading, ``attn`` "auto", "four_wave" or "ping_pong"
+    the prefill attention kernel."""
     dt = shape.dtype
     if isinstance(dt, str):
         dt = {"bf16": CCA_BF16, "f32": CCA_F32}[dt]
     mode = {"per_head": CCA_CHAN_PER_HEAD, "grouped": CCA_CHAN_GROUPED}[chan_conv]
     mean = {"pre_post": CCA_QK_MEAN_PRE_POST, "pre": CCA_QK_MEAN_PRE}[qk_mean]
+    ak = {"auto": CCA_ATTN_AUTO, "four_wave": CCA_ATTN_FOUR_WAVE, "ping_pong": CCA_ATTN_PING_PONG}[attn]
     return Config(int(shape.batch), int(shape.seq_len), int(shape.d_model), int(shape.n_q_heads),
                   int(shape.n_kv_heads), int(shape.head_dim), int(shape.seq_conv_k),
                   int(shape.chan_conv_k), int(shape.use_qk_mean), int(shape.use_value_shift),
                   int(shape.use_qk_norm), float(shape.rope_base), float(shape.norm_eps), int(dt),
-                  mode, mean)
+                  mode, mean, ak)
 
 
 def _ptr(t) -> Optional[int]:

@@ -38,8 +38,8 @@
 //    product.  Otherwise the usual online softmax runs: the rescale of O runs
 //    only when some row's running max grew (a wave-uniform vote).
 //  * The row sums add the bf16-rounded probabilities that the P*V product
-//    consumes (v_dot2_f32_bf16); each half-wave keeps its own partial sum
-//    until the end.
+//    consumes, in four independent chains of plain adds; each half-wave
+//    keeps its own partial sums until the end.
 //  * Causal blocks: a workgroup walks the key tiles up to its last query;
 //    only tiles that reach past a wave's first query are masked (tiles past
 //    its last query come out fully masked and add nothing), and the heavy
@@ -60,6 +60,22 @@ template <typename TQ, typename TV, int D> struct AttnTile {
   static constexpr int KB = NBUF * bytes(64) <= 65536 ? 64 : 32;
   static constexpr bool fits = NBUF * bytes(KB) <= 65536;
 };
+
+// l4[e] += p[2e] + p[2e+1] for the 8 bf16 probabilities of one P*V operand:
+// the row sum adds exactly the rounded values that the product consumes, so
+// that the normalised weights sum to one (a query with one key returns that
+// key's value, bit for bit).  Each bf16 widens to fp32 by a shift or a mask
+// of its half of the packed pair; four independent chains of plain adds.
+// (A v_dot2 against ones would take one instruction per pair, but the dot
+// unit is shared with the matrix cores and runs several times slower while
+// MFMAs execute.)
+__device__ __forceinline__ void row_sum_add(float (&l4)[4], const bf16x8 &pf) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v u = __builtin_bit_cast(u32x4v, pf);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    l4[e] += __uint_as_float(u[e] << 16) + __uint_as_float(u[e] & 0xffff0000u);
+}
 
 template <typename TQ, typename TV, int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__ q,
@@ -197,7 +213,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   f32x16 acc[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc[i] = zero16();
-  float m_run = -INFINITY, l_run = 0.f;
+  // the row sum in four partial sums (independent add chains)
+  float m_run = -INFINITY, l4[4] = {0.f, 0.f, 0.f, 0.f};
 
   // the whole key loop is instantiated once per softmax form, so that the
   // branch between them stays outside the loop
@@ -236,7 +253,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
           if (__any(mx > m_run)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) l4[e] *= alpha;
 #pragma unroll
             for (int i = 0; i < ND; ++i)
 #pragma unroll
@@ -255,17 +273,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
                                                     : s_cur[hf][KSV * cc + sl] - m_run);
             const typename MV::frag pf = pack_frag<TV>(pv);
             if constexpr (KSV == 8) {
-              // row sum of the rounded probabilities the P*V product uses
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                const bf16x2 pair = {pf[2 * e], pf[2 * e + 1]};
-                const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run, false);
-              }
+              row_sum_add(l4, pf);
             } else {
-#pragma unroll
-              for (int sl = 0; sl < KSV; ++sl) l_run += pv[sl];
+              l4[cc & 3] += pv[0];
             }
             // first key of this lane's k-slots, in the permuted tile order
             const int a0 = KSV * cc;
@@ -309,6 +319,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   else run(std::false_type{});
 
   // each half-wave summed its own keys (and both saw the same rescales)
+  float l_run = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   l_run += __shfl_xor(l_run, 32, 64);
   if (qpos >= T) return;
   // log2 of the softmax denominator in the exp2 domain, kept for the backward
@@ -332,14 +343,372 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave ping-pong variant (d = 64, 16-bit q/k, bf16 v).
+//
+// Per 64-key tile a wave runs 16 MFMAs (512 matrix-core cycles) and the
+// softmax on VALU (32 exponentials per lane, the bf16 packing and the row
+// sums), about as long again.  Here a workgroup holds 8 waves = 256 query
+// rows; the hardware places waves w and w + 4 on the same SIMD, and the two
+// halves of the workgroup (waves 0-3 = A, 4-7 = B) run in opposite phases,
+// separated by workgroup barriers:
+//
+//   slot 2j   : A  softmax of tile j            B  P*V of tile j-1, S of tile j
+//   slot 2j+1 : A  P*V of tile j, S of tile j+1  B  softmax of tile j
+//
+// so every SIMD holds one wave in its VALU phase and one in its MFMA phase.
+// A wave reads the LDS fragments of its next matrix phase during its
+// softmax phase.  K/V^T tiles (16 KiB) stream into a ring of NBUF slots by
+// LDS-DMA, two instructions per wave per tile.  Both kernels take the same
+// tiles in the same order with the same per-lane arithmetic, so their
+// outputs agree bit for bit.
+//
+// Measured on MI355X it does not beat the four-wave kernel: the softmax
+// phase (about 1.1k cycles with the fragment reads) stays longer than the
+// matrix phase (about 0.7k), so each slot is VALU-bound; CCA_ATTN_AUTO keeps
+// the four-wave kernel.
+// ---------------------------------------------------------------------------
+constexpr int PP_NBUF = 6;
+
+template <typename TQ>
+__global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restrict__ q,
+                                                             const TQ *__restrict__ k,
+                                                             const bf16 *__restrict__ vt,
+                                                             const float *__restrict__ tau,
+                                                             bf16 *__restrict__ o,
+                                                             float *__restrict__ lse, int B, int T,
+                                                             int Tp, int Hq, int Hkv, int G, int hq,
+                                                             int nsub, int npb, int use_norm) {
+  typedef Mfma32<TQ> MQ;
+  typedef Mfma32<bf16> MV;
+  constexpr int D = 64, KB = 64, NH = 2, KS = 8;
+  constexpr int QC = D / (2 * KS);                    // QK^T contraction chunks (4)
+  constexpr int ND = D / 32;                          // O^T row blocks (2)
+  constexpr int PC = 16 / KS;                         // P*V chunks per 32-key half (2)
+  constexpr int ROW = 128, CPR = 8;                   // K row = V^T row = 128 bytes
+  constexpr int KTILE = KB * ROW, VTILE = D * ROW, BUF = KTILE + VTILE;
+  constexpr int NBUF = PP_NBUF;
+  constexpr int K_INS = KTILE / 1024, V_INS = VTILE / 1024;
+  constexpr int PER_WAVE = (K_INS + V_INS) / 8;
+  static_assert(K_INS == 8 && V_INS == 8 && PER_WAVE == 2, "tile split");
+  static_assert(PER_WAVE * (NBUF - 2) < 64, "vmcnt field");
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * BUF];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int l32 = lane & 31, hl = lane >> 5;
+  const bool grp_a = wave < 4;                        // wave-uniform
+  const int pos_per = 256 / hq;
+
+  // heavy-first order over position blocks, as the four-wave kernel
+  int id = blockIdx.x;
+  const int rest = B * Hkv * nsub;
+  const int pb = npb - 1 - id / rest;
+  id %= rest;
+  const int sub = id % nsub;
+  id /= nsub;
+  const int g = id % Hkv, b = id / Hkv;
+
+  const int hslot = wave % hq, rchunk = wave / hq;
+  const int h = g * G + sub * hq + hslot;
+  const int blk0 = pb * pos_per;
+  const int p0 = blk0 + 32 * rchunk;
+  const int qpos = p0 + l32;
+  const int last_row = min(blk0 + pos_per, T) - 1;
+  const int ntiles = last_row / KB + 1;
+
+  const float c_h = tau[h] * 1.4426950408889634f;
+  const bool fixed_shift = use_norm && c_h >= 0.f && c_h <= 60.f;
+  f32x16 s_init;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) s_init[a] = fixed_shift ? -c_h : 0.f;
+
+  // rows past the padded length (256-row blocks over a 128-padded buffer)
+  // read the last padded row; their outputs are never stored
+  typename MQ::frag qf[QC];
+  {
+    const TQ *qrow = q + ((size_t)(b * Hq + h) * Tp + min(qpos, Tp - 1)) * D;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) qf[c] = load_frag<TQ>(qrow + c * 2 * KS + hl * KS);
+  }
+
+  const TQ *kbase = k + (size_t)(b * Hkv + g) * Tp * D;
+  const bf16 *vbase = vt + (size_t)(b * Hkv + g) * D * Tp;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void *)kbase, 0, (unsigned)(Tp * ROW), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void *)vbase, 0, (unsigned)(D * Tp * 2), 0x00020000);
+  // wave w moves 1 KiB chunk w of the K tile and chunk w of the V^T tile
+  unsigned koff, voff;
+  {
+    const int c = wave * 64 + lane, row = c / CPR, ch = (c % CPR) ^ swz_key(row, CPR);
+    koff = (unsigned)(row * ROW + ch * 16);
+    voff = (unsigned)(row * Tp * 2 + ch * 16);
+  }
+  auto issue = [&](int kt) {
+    unsigned char *sk = smem + (kt % NBUF) * BUF;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, as_lds(sk + wave * 1024), 16, (int)koff,
+                                             (unsigned)(kt * KB * ROW), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, as_lds(sk + KTILE + wave * 1024), 16, (int)voff,
+                                             (unsigned)(kt * KB * 2), 0, 0);
+  };
+  // wait until at most `after` tiles issued after the awaited one are in flight
+  auto wait_tiles = [&](int after) {
+    switch (after) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<PER_WAVE>(); break;
+      case 2: wait_vmcnt<2 * PER_WAVE>(); break;
+      case 3: wait_vmcnt<3 * PER_WAVE>(); break;
+      default: wait_vmcnt<4 * PER_WAVE>(); break;
+    }
+  };
+  static_assert(NBUF - 2 <= 4, "wait_tiles covers at most four tiles in flight");
+  // tile t resident: issued so far are tiles [0, max(NBUF-2, t+NBUF-3)] (clipped)
+  auto wait_tile = [&](int t) {
+    wait_tiles(min(max(NBUF - 2, t + NBUF - 3), ntiles - 1) - t);
+  };
+  auto slot_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc[i] = zero16();
+  float m_run = -INFINITY, l4[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x16 s[NH];
+  typename MV::frag pf[NH][PC];
+
+  // MFMA operands read from LDS: the V^T fragments of one tile (V) and the K
+  // fragments of one tile (K).  A wave reads the fragments of its next matrix
+  // phase during its softmax phase, so that the matrix phase issues nothing
+  // but MFMAs.
+  typename MV::frag vf[NH][PC][ND];
+  typename MQ::frag kf[QC][NH];
+  auto load_frags = [&](int jv, int jk, auto v_tag, auto k_tag) {
+    constexpr bool V = decltype(v_tag)::value, K = decltype(k_tag)::value;
+    if constexpr (V) {
+      const unsigned char *sv = smem + (jv % NBUF) * BUF + KTILE;
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+        for (int cc = 0; cc < PC; ++cc) {
+          const int a0 = KS * cc;
+          const int key_rel = 8 * (a0 >> 2) + 4 * hl + (a0 & 3);
+          const int kb = (hf * 32 + vt_perm(key_rel)) * 2;
+#pragma unroll
+          for (int i = 0; i < ND; ++i) {
+            const int row = i * 32 + l32;
+            vf[hf][cc][i] = load_frag<bf16>(reinterpret_cast<const bf16 *>(sv + row * ROW + swz(row, kb, CPR)));
+          }
+        }
+    }
+    if constexpr (K) {
+      const unsigned char *sk = smem + (jk % NBUF) * BUF;
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
+          const int row = hf * 32 + l32;
+          const int kb = (c * 2 * KS + hl * KS) * (int)sizeof(TQ);
+          kf[c][hf] = load_frag<TQ>(reinterpret_cast<const TQ *>(sk + row * ROW + swz(row, kb, CPR)));
+        }
+    }
+  };
+  // One matrix phase on the loaded fragments: O^T += V^T P^T (V) and/or
+  // S = K Q^T (K).
+  auto mfma_phase = [&](auto v_tag, auto k_tag) {
+    constexpr bool V = decltype(v_tag)::value, K = decltype(k_tag)::value;
+    if constexpr (V) {
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+        for (int cc = 0; cc < PC; ++cc)
+#pragma unroll
+          for (int i = 0; i < ND; ++i) acc[i] = MV::mma(vf[hf][cc][i], pf[hf][cc], acc[i]);
+    }
+    if constexpr (K) {
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) s[hf] = s_init;
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) s[hf] = MQ::mma(kf[c][hf], qf[c], s[hf]);
+    }
+  };
+  const std::true_type Y{};
+  const std::false_type X{};
+
+  auto run = [&](auto fixed_tag) {
+    constexpr bool FIXED = decltype(fixed_tag)::value;
+    auto softmax = [&](int j, auto diag_tag) {
+      constexpr bool DIAG = decltype(diag_tag)::value;
+      if constexpr (DIAG) {
+        const int k0 = j * KB;
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) {
+            const int key = k0 + hf * 32 + 8 * (a >> 2) + 4 * hl + (a & 3);
+            if (key > qpos) s[hf][a] = -INFINITY;
+          }
+      }
+      if constexpr (!FIXED) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[hf][a]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (__any(mx > m_run)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) l4[e] *= alpha;
+#pragma unroll
+          for (int i = 0; i < ND; ++i)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) acc[i][a] *= alpha;
+          m_run = m_new;
+        }
+#pragma unroll
+        for (int i = 0; i < ND; ++i) asm volatile("" : "+v"(acc[i]));
+      }
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+        for (int cc = 0; cc < PC; ++cc) {
+          float p8[KS];
+#pragma unroll
+          for (int sl = 0; sl < KS; ++sl)
+            p8[sl] = __builtin_amdgcn_exp2f(FIXED ? s[hf][KS * cc + sl] : s[hf][KS * cc + sl] - m_run);
+          pf[hf][cc] = pack_frag<bf16>(p8);
+          row_sum_add(l4, pf[hf][cc]);
+        }
+      // the softmax's results are formed here, inside its VALU phase: without
+      // these register fences the compiler may sink the packing or the row
+      // sums past the barrier into the next (matrix) phase
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+        for (int cc = 0; cc < PC; ++cc) asm volatile("" : "+v"(pf[hf][cc]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(l4[e]));
+    };
+    // tiles past a wave's last query come out fully masked and add exact
+    // zeros, so every wave walks the same tiles with no branch around the
+    // products
+    auto sm = [&](int j) {
+      if (j * KB + KB - 1 > p0) softmax(j, std::true_type{});
+      else softmax(j, std::false_type{});
+    };
+
+    // the softmax phase of tile j, with the reads of the next matrix phase's
+    // fragments (V^T of tile j, K of tile j + 1) issued first
+    auto softmax_phase = [&](int j) {
+      if (j + 1 < ntiles) load_frags(j, j + 1, Y, Y);
+      else load_frags(j, 0, Y, X);
+      __builtin_amdgcn_sched_barrier(0);
+      sm(j);
+    };
+
+    // Slots, both halves (2 * ntiles + 2 barriers):
+    //   slot -1  : A  S of tile 0
+    //   slot 2j  : A  softmax j (+ reads V^T j, K j+1)   B  P*V j-1, S of tile j
+    //   slot 2j+1: A  P*V j, S of tile j+1               B  softmax j (+ the same reads)
+    //   after    :                                      B  P*V of the last tile
+    // Tile t is resident from the barrier that ends slot 2t - 3; tile
+    // j + NBUF - 1 is issued at the end of slot 2j (after the phase's own
+    // work) into the ring slot of tile j - 1, whose last reads were B's in
+    // slot 2j - 1.
+    for (int t = 0; t < NBUF - 1 && t < ntiles; ++t) issue(t);
+    wait_tile(0);
+    slot_end();
+    // each half runs its own loop of straight-line phases
+    if (grp_a) {
+      load_frags(0, 0, X, Y);
+      mfma_phase(X, Y);
+      if (ntiles > 1) wait_tile(1);
+      slot_end();
+      for (int j = 0; j + 1 < ntiles; ++j) {
+        softmax_phase(j);
+        if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
+        slot_end();
+        mfma_phase(Y, Y);
+        if (j + 2 < ntiles) wait_tile(j + 2);
+        slot_end();
+      }
+      softmax_phase(ntiles - 1);
+      slot_end();
+      mfma_phase(Y, X);
+      slot_end();
+    } else {
+      if (ntiles > 1) wait_tile(1);
+      slot_end();
+      load_frags(0, 0, X, Y);
+      mfma_phase(X, Y);
+      if (NBUF - 1 < ntiles) issue(NBUF - 1);
+      slot_end();
+      softmax_phase(0);
+      if (2 < ntiles) wait_tile(2);
+      slot_end();
+      for (int j = 1; j < ntiles; ++j) {
+        mfma_phase(Y, Y);
+        if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
+        slot_end();
+        softmax_phase(j);
+        if (j + 2 < ntiles) wait_tile(j + 2);
+        slot_end();
+      }
+      mfma_phase(Y, X);
+    }
+  };
+  if (fixed_shift) run(std::true_type{});
+  else run(std::false_type{});
+
+  float l_run = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (qpos >= T) return;
+  if (lse && hl == 0) lse[(size_t)(b * Hq + h) * Tp + qpos] = (fixed_shift ? c_h : m_run) + __log2f(l_run);
+  const float inv_l = 1.f / l_run;
+  bf16 *orow = o + ((size_t)(b * T + qpos)) * (Hq * D) + h * D;
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dd = i * 32 + 8 * j + 4 * hl;
+      bf16 v4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = from_f32<bf16>(acc[i][4 * j + e] * inv_l);
+      *reinterpret_cast<u32x2 *>(orow + dd) = *reinterpret_cast<u32x2 *>(v4);
+    }
+}
+
 static int gcd_int(int a, int b) {
   while (b) { int t = a % b; a = b; b = t; }
   return a;
 }
 
+template <typename TQ>
+static hipError_t attn_pp(const MixShape &s, const TQ *q, const TQ *k, const bf16 *vt,
+                          const float *tau, bf16 *o, float *lse, hipStream_t stream) {
+  const int hq = gcd_int(s.G, 4);
+  const int nsub = s.G / hq;
+  const int pos_per = 256 / hq;
+  const int npb = (s.T + pos_per - 1) / pos_per;
+  const int grid = npb * s.B * s.Hkv * nsub;
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<TQ>), dim3(grid), dim3(512), 0, stream, q, k, vt, tau, o,
+                     lse, s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb, s.use_norm);
+  return hipGetLastError();
+}
+
 template <typename TQ, typename TV, int D>
 static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
                          const float *tau, TV *o, float *lse, hipStream_t stream) {
+  if constexpr (D == 64 && sizeof(TQ) == 2 && std::is_same<TV, bf16>::value) {
+    if (s.attn_kernel == 2) return attn_pp<TQ>(s, q, k, vt, tau, o, lse, stream);
+  }
   const int hq = gcd_int(s.G, 4);
   const int nsub = s.G / hq;
   const int pos_per = 128 / hq;

@@ -66,6 +66,15 @@ bool qk_is_f16(const cca_config &c) { return c.dtype == CCA_BF16 && c.use_qk_nor
 
 int padded_T(int T) { return (T + TILE_T - 1) / TILE_T * TILE_T; }
 
+// The prefill attention kernel for c: the ping-pong kernel takes bf16 with
+// d = 64; CCA_ATTN_AUTO chooses it for every such shape.
+int attn_kernel_for(const cca_config &c) {
+  const bool pp_ok = c.dtype == CCA_BF16 && c.head_dim == 64;
+  if (!pp_ok || c.attn_kernel == CCA_ATTN_FOUR_WAVE) return 1;
+  if (c.attn_kernel == CCA_ATTN_PING_PONG) return 2;
+  return 1;
+}
+
 MixShape mix_shape(const cca_config &c) {
   MixShape s;
   s.B = c.batch;
@@ -84,6 +93,7 @@ MixShape mix_shape(const cca_config &c) {
   s.grouped = c.chan_conv_mode == CCA_CHAN_GROUPED ? 1 : 0;
   s.rope_base = c.rope_base;
   s.eps = c.norm_eps;
+  s.attn_kernel = attn_kernel_for(c);
   for (int i = 0; i < 64; ++i)
     s.theta[i] = (c.rope_base > 0.f && 2 * i < c.head_dim)
                      ? std::pow((double)c.rope_base, -2.0 * (double)i / (double)c.head_dim)
@@ -107,6 +117,9 @@ cca_status validate_shape(const cca_config *c, bool need_seq) {
   if (c->chan_conv_mode != CCA_CHAN_PER_HEAD && c->chan_conv_mode != CCA_CHAN_GROUPED)
     return CCA_ERR_INVALID_ARG;
   if (c->qk_mean_mode != CCA_QK_MEAN_PRE_POST && c->qk_mean_mode != CCA_QK_MEAN_PRE)
+    return CCA_ERR_INVALID_ARG;
+  if (c->attn_kernel != CCA_ATTN_AUTO && c->attn_kernel != CCA_ATTN_FOUR_WAVE &&
+      c->attn_kernel != CCA_ATTN_PING_PONG)
     return CCA_ERR_INVALID_ARG;
   const int d = c->head_dim;
   if (d != 16 && d != 32 && d != 64 && d != 128) return CCA_ERR_UNSUPPORTED;

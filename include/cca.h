@@ -98,6 +98,15 @@ typedef enum { CCA_CHAN_PER_HEAD = 0, CCA_CHAN_GROUPED = 1 } cca_chan_conv;
  *   k += (k~ + avg q~) / 2. */
 typedef enum { CCA_QK_MEAN_PRE_POST = 0, CCA_QK_MEAN_PRE = 1 } cca_qk_mean;
 
+/* Prefill attention kernel.  Both compute the same values in the same
+ * summation order; they differ in how the work maps onto the CU.
+ * CCA_ATTN_FOUR_WAVE: 4 waves (128 query rows) per workgroup, 2 per CU.
+ * CCA_ATTN_PING_PONG: 8 waves (256 query rows) per workgroup, 1 per CU, two
+ *   halves alternating between the softmax and the matrix products; bf16
+ *   with head_dim 64 only (other configurations use the four-wave kernel).
+ * CCA_ATTN_AUTO picks one from the shape. */
+typedef enum { CCA_ATTN_AUTO = 0, CCA_ATTN_FOUR_WAVE = 1, CCA_ATTN_PING_PONG = 2 } cca_attn_kernel;
+
 /* Shape and switches of one attention layer.  C (compression) and G are
  * derived: e_q = n_q_heads*head_dim, e_kv = n_kv_heads*head_dim,
  * G = n_q_heads / n_kv_heads. */
@@ -121,6 +130,7 @@ typedef struct {
                            * fused prefill entry points reject it (CCA_ERR_UNSUPPORTED) */
   int32_t qk_mean_mode;   /* cca_qk_mean; 0 (zero-initialised) is the pre- and
                            * post-convolution mean.  Only read when use_qk_mean is 1. */
+  int32_t attn_kernel;    /* cca_attn_kernel; 0 (zero-initialised) is CCA_ATTN_AUTO */
 } cca_config;
 
 /* Weights.  w_qkv: [e_q + 2*e_kv, E] in cfg.dtype, rows q | k | v.
@@ -169,7 +179,8 @@ typedef struct {
  * H_kv with value-shift, E not a multiple of 8, bad eps/base) or
  * CCA_ERR_UNSUPPORTED (d outside {16,32,64,128}, fp32 prefill with d = 128,
  * taps outside 1..4, dtype, a kv group too wide for the mixing kernel).
- * A qk_mean_mode or chan_conv_mode outside its enum is CCA_ERR_INVALID_ARG. */
+ * A qk_mean_mode, chan_conv_mode or attn_kernel outside its enum is
+ * CCA_ERR_INVALID_ARG. */
 cca_status cca_validate_config(const cca_config *cfg);
 
 /* Bytes of device workspace cca_prefill_forward needs for cfg (0 if cfg is

@@ -76,10 +76,10 @@ class PrefillRun:
     """Device buffers and one prefill through cca_prefill_forward."""
 
     def __init__(self, shape: CCAShape, P, capacity: int = 0, dev="cuda", chan_conv="per_head",
-                 qk_mean="pre_post"):
+                 qk_mean="pre_post", attn="auto"):
         L, T = lib(), tens()
         self.shape, self.P = shape, P
-        self.cfg = L.make_config(shape, chan_conv=chan_conv, qk_mean=qk_mean)
+        self.cfg = L.make_config(shape, chan_conv=chan_conv, qk_mean=qk_mean, attn=attn)
         assert L.validate_config(self.cfg) == L.CCA_OK
         self.w = upload_weights(P.weights, dev)
         self.x = T.to_device(P.x_s, dev)

@@ -88,7 +88,8 @@ def test_invalid_configs(L, kw, err):
 
 
 @pytest.mark.parametrize("field,value", [("qk_mean_mode", 2), ("qk_mean_mode", -1),
-                                         ("chan_conv_mode", 2)])
+                                         ("chan_conv_mode", 2), ("attn_kernel", 3),
+                                         ("attn_kernel", -1)])
 def test_reading_switch_out_of_range(L, field, value):
     cfg = L.make_config(CCAShape(batch=1, seq_len=16, d_model=256, n_q_heads=4, n_kv_heads=2,
                                  head_dim=64))
@@ -106,6 +107,21 @@ def test_both_qk_mean_readings_validate(L):
     # the default reading keeps the channel-conv output for the backward
     assert (L.train_workspace_size(L.make_config(s)) >
             L.train_workspace_size(L.make_config(s, qk_mean="pre")))
+
+
+def test_attention_kernel_choices_validate(L):
+    """Every attention kernel choice is a valid configuration for every head
+    size and dtype: the ping-pong kernel is taken where it applies (bf16,
+    d = 64), the four-wave kernel elsewhere."""
+    for dt in ("bf16", "f32"):
+        for d in (16, 32, 64):
+            s = CCAShape(batch=1, seq_len=16, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=d,
+                         dtype=dt)
+            for kern in ("auto", "four_wave", "ping_pong"):
+                cfg = L.make_config(s, attn=kern)
+                assert L.validate_config(cfg) == L.CCA_OK, (dt, d, kern)
+                assert (L.prefill_workspace_size(cfg) ==
+                        L.prefill_workspace_size(L.make_config(s)))
 
 
 def _fake_weights(L, dense=0x10000):

@@ -38,10 +38,10 @@ def _say(msg):
 class TrainRun:
     """Device buffers of one forward_train + backward."""
 
-    def __init__(self, shape, P, dyB, dev="cuda", qk_mean="pre_post"):
+    def __init__(self, shape, P, dyB, dev="cuda", qk_mean="pre_post", attn="auto"):
         L, T = lib(), tens()
         self.shape, self.P = shape, P
-        self.cfg = L.make_config(shape, qk_mean=qk_mean)
+        self.cfg = L.make_config(shape, qk_mean=qk_mean, attn=attn)
         assert L.validate_config(self.cfg) == L.CCA_OK
         self.w = upload_weights(P.weights, dev)
         self.x = T.to_device(P.x_s, dev)
