@@ -111,7 +111,7 @@ def test_ping_pong_training_lse_and_gradients():
     """forward_train keeps the log-sum-exp that the backward pass reads: with
     the ping-pong kernel every gradient equals the four-wave one bit for bit,
     and the parameter gradients match the fp64 backward oracle."""
-    from test_gpu_backward import GRADS, TrainRun, check_grads
+    from test_gpu_backward import GRADS, TrainRun, bf16_bounds, check_grads
     shape = CCAShape(batch=1, seq_len=300, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64)
     _say(f"[attn-kernels] training {shape}")
     P = make_prefill(shape, seed=3)
@@ -128,4 +128,5 @@ def test_ping_pong_training_lse_and_gradients():
         iv = torch.int16 if a.element_size() == 2 else torch.int32
         assert torch.equal(a.view(iv), b.view(iv)), n
     ref = BW.prefill_backward(P.x, P.weights.f64(), shape, dyB.dy)
-    check_grads({n: tens().to_f64(got["ping_pong"][n]) for n in GRADS}, ref, "bf16", "ping_pong")
+    check_grads({n: tens().to_f64(got["ping_pong"][n]) for n in GRADS}, ref, "bf16", "ping_pong",
+                bf16_bounds(P, dyB, shape, ref))

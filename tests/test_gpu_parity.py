@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle.cca as O
-from synth import CCAShape, make_decode, make_prefill, workload
+from synth import COMPARISON_OVERRIDES, COMPARISONS, CCAShape, make_decode, make_prefill, workload
 from gpu_helpers import (PrefillRun, assert_parity, lib, rel_l2, sample_rows, set_taps,
                          tau_inv_sqrt_d, tens, upload_weights, vt_unpermute)
 
@@ -86,6 +86,27 @@ def test_prefill_mha_reduction_gpu():
     set_taps(P, seq=(qs, ks), chan=(qc, qc.copy()), tau=tau_inv_sqrt_d(shape))
     y = PrefillRun(shape, P).run()
     assert_parity(y, O.prefill(P.x, P.weights.f64(), shape), "bf16", "mha")
+
+
+@pytest.mark.parametrize("name", list(COMPARISONS))
+def test_comparison_baseline_parity(name):
+    """The full-width baselines of the prefill comparison at their own head
+    shapes (E = 4096, 64 query heads over 64 or 8 kv heads, d = 64), shortened
+    to T = 1024: taps of length one set to 1 (identity convolutions), mean,
+    shift and norm off, tau = 1/sqrt(d), exactly as the comparison runs them.
+    Sampled rows against the oracle."""
+    import math
+    shape = COMPARISONS[name].with_(seq_len=1024)
+    _say(f"[prefill] comparison baseline {name} {shape}")
+    P = make_prefill(shape, seed=5)
+    W = P.weights
+    for a in (W.q_seq_taps, W.k_seq_taps, W.q_chan_taps, W.k_chan_taps):
+        a[...] = COMPARISON_OVERRIDES["taps"]
+    W.tau = np.full(shape.n_q_heads, 1.0 / math.sqrt(shape.head_dim), dtype=np.float32)
+    y = PrefillRun(shape, P).run()
+    rows = sample_rows(shape.seq_len, 40, seed=2)
+    ref = O.prefill(P.x, W.f64(), shape, rows=rows)
+    assert_parity(y[:, rows], ref, "bf16", name)
 
 
 def test_prefill_stage_intermediates():

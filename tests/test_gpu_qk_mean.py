@@ -20,7 +20,7 @@ import oracle.backward as BW
 import oracle.cca as O
 from synth import CCAShape, make_decode, make_prefill, make_upstream_grad
 from gpu_helpers import PrefillRun, assert_parity, lib, rel_l2, tens, upload_weights
-from test_gpu_backward import TrainRun, check_grads
+from test_gpu_backward import TrainRun, bf16_bounds, check_grads
 from test_gpu_multi import _run_multi
 
 pytestmark = pytest.mark.gpu
@@ -157,4 +157,5 @@ def test_backward_pre_reading(name):
     run.forward()
     got = run.backward()
     ref = BW.prefill_backward(P.x, P.weights.f64(), shape, dyB.dy, readings=PRE)
-    check_grads(got, ref, shape.dtype, f"pre {name}")
+    bounds = bf16_bounds(P, dyB, shape, ref, readings=PRE) if shape.dtype == "bf16" else None
+    check_grads(got, ref, shape.dtype, f"pre {name}", bounds)
