@@ -55,9 +55,15 @@ def parse():
     p.add_argument("--kernels-only", action="store_true",
                    help="only run the stage calls of the three bf16 prefill workloads and the decode "
                         "step, --steps times each (a short program for counter collection)")
+    p.add_argument("--only", default="",
+                   help="with --kernels-only: a comma-separated subset of cca_prefill_b4_t2048, "
+                        "ccgqa_prefill_t8192, ccgqa_prefill_t16384, ccgqa_decode_b64_l32768")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--summarize-profiles", metavar="DIR", default="",
+                   help="write the profiles/ summaries from the rocprofv3 outputs under DIR "
+                        "(layout in profile_summaries' docstring); needs no GPU")
     return p.parse_args()
 
 
@@ -388,6 +394,10 @@ def prefill_config(cca, T, name, K, dev):
     }
 
 
+KERNEL_WORKLOADS = ("cca_prefill_b4_t2048", "ccgqa_prefill_t8192", "ccgqa_prefill_t16384",
+                    "ccgqa_decode_b64_l32768")
+
+
 def kernels_only(args):
     """The stage calls of the three bf16 prefill workloads and of the decode
     step, --steps times each after one warm-up call: a short program whose
@@ -397,7 +407,10 @@ def kernels_only(args):
     from synth import make_decode, make_prefill, workload
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    only = [n for n in args.only.split(",") if n] or list(KERNEL_WORKLOADS)
     for name in ("cca_prefill_b4_t2048", "ccgqa_prefill_t8192", "ccgqa_prefill_t16384"):
+        if name not in only:
+            continue
         sp = workload(name)
         P = make_prefill(sp, seed=0)
         pw = upload_weights(cca, T, P.weights, dev)
@@ -414,6 +427,8 @@ def kernels_only(args):
         print(f"[kernels] {name} done", file=sys.stderr, flush=True)
         del ws, x, y, pw, P
         torch.cuda.empty_cache()
+    if "ccgqa_decode_b64_l32768" not in only:
+        return
     sd = workload("ccgqa_decode_b64_l32768")
     D = make_decode(sd, seed=0)
     dw = upload_weights(cca, T, D.weights, dev)
@@ -508,8 +523,193 @@ def compare(args):
                                    "L2 norm, tau = 1/sqrt(d)); GQA-8 = 8 kv heads"}), flush=True)
 
 
+# ---- profile summaries (rocprofv3 outputs -> profiles/) ---------------------
+
+PROFILE_SOURCES = {
+    "downproj": ["gemm.hip", "gemm_tile.h", "cca_device.h", "cca_launch.h"],
+    "upproj": ["gemm.hip", "gemm_tile.h", "cca_device.h", "cca_launch.h"],
+    "convmix": ["convmix.hip", "gemm_tile.h", "cca_device.h", "cca_launch.h"],
+    "attention": ["attn_fwd.hip", "cca_device.h", "cca_launch.h"],
+    "dec_attention": ["attn_decode.hip", "cca_device.h", "cca_launch.h"],
+}
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                 "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_WAVES")
+
+
+def _source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "efficient_transformer_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _counter_dispatches(path):
+    """Per dispatch of a rocprofv3 counter pass (its rocpd database under
+    path): kernel name, duration in ns and every counter summed over the
+    instances that report it, in dispatch order."""
+    import glob
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(path, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise FileNotFoundError(f"no rocpd database under {path}")
+    rows = sqlite3.connect(dbs[0]).execute(
+        "select dispatch_id, kernel_name, counter_name, value, duration from counters_collection").fetchall()
+    out = {}
+    for did, name, cn, v, dur in rows:
+        d = out.setdefault(did, {"name": name, "dur_ns": float(dur)})
+        d[cn] = d.get(cn, 0.0) + float(v)
+    return [out[k] for k in sorted(out)]
+
+
+def _stages(dispatches):
+    """Label the libcca dispatches of a kernels-only run by pipeline stage
+    (the first dispatch of every stage is the warm-up and is dropped)."""
+    lab, prev = {}, None
+    for d in dispatches:
+        n = d["name"]
+        if "convmix_prefill" in n:
+            st = "convmix"
+        elif "attn_fwd" in n:
+            st = "attention"
+        elif "gemm_nt_dma" in n:
+            st = "upproj" if prev == "attention" else "downproj"
+        elif "attn_decode_mfma" in n:
+            st = "dec_attention"
+        elif "attn_decode_combine" in n:
+            st = "dec_combine"
+        elif "convmix_decode" in n:
+            st = "dec_mix"
+        elif "splitk_reduce" in n:
+            st = "dec_upproj_reduce"
+        elif "gemm_nt_kernel" in n:
+            st = "dec_upproj" if prev in ("dec_combine", "dec_attention") else "dec_downproj"
+        else:
+            continue
+        prev = st
+        lab.setdefault(st, []).append(d)
+    return {k: v[1:] or v for k, v in lab.items()}
+
+
+def _avg(ds, key):
+    return sum(d.get(key, 0.0) for d in ds) / len(ds)
+
+
+def profile_summaries(d):
+    """Writes the profiles/ summaries from rocprofv3 outputs under d:
+      d/trace        kernel trace (--kernel-trace --stats --output-format csv) of
+                     `bench.py --steps 5 --warmup 1 --no-cpu`;
+      d/<pass>_<w>   counter passes (rocpd output) of `bench.py --kernels-only
+                     --steps 3 --only <w>` for pass in mfma (MFMA_COUNTERS),
+                     fetch (FETCH_SIZE), write (WRITE_SIZE) and w in
+                     KERNEL_WORKLOADS;
+      d/fetch_copy, d/write_copy   the same two counters on `bench.py
+                     --calibrate-copy` (a plain 1 GiB copy, which scales them).
+    The command lines are recorded in the summaries."""
+    import csv
+    import glob
+    from synth import workload
+    prof = os.path.join(ROOT, "profiles")
+    ws = list(KERNEL_WORKLOADS)
+    run = "cd /tmp && rocprofv3"
+    # ---- kernel trace of the default bench command
+    stats = sorted(glob.glob(os.path.join(d, "trace", "**", "*kernel_stats.csv"), recursive=True))
+    if stats:
+        rows = list(csv.DictReader(open(stats[0])))
+        lines = [
+            "# Kernel durations: bench.py default run (prefill B4 x T2048, the 8192- and 16384-token "
+            "CCGQA prefills, decode B64 x L32768)", "",
+            "```", f"{run} --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace -o run "
+                   "-- python3 $REPO/bench.py --steps 5 --warmup 1 --no-cpu", "```", "",
+            "| kernel | calls | average (us) | share |", "|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+        open(os.path.join(prof, "kernel_trace_prefill_b4_t2048_t8192_t16384_decode_b64_l32768.md"),
+             "w").write("\n".join(lines) + "\n")
+    # ---- copy calibration of FETCH_SIZE / WRITE_SIZE
+    cf = [x for x in _counter_dispatches(os.path.join(d, "fetch_copy")) if "FETCH_SIZE" in x]
+    cw = [x for x in _counter_dispatches(os.path.join(d, "write_copy")) if "WRITE_SIZE" in x]
+    big = lambda xs, k: max(xs, key=lambda x: x[k])
+    n_copy = 1 << 30
+    fetch_factor = n_copy / (big(cf, "FETCH_SIZE")["FETCH_SIZE"] * 1024)
+    write_factor = n_copy / (big(cw, "WRITE_SIZE")["WRITE_SIZE"] * 1024)
+    # ---- per workload: MFMA utilisation and HBM traffic per stage
+    mf_lines = ["# MFMA utilisation per kernel (rocprofv3 counters)", "",
+                "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), the "
+                "share of the kernel's cycles in which the matrix cores were busy (at whatever clock "
+                "the chip ran); MFMA TFLOP/s = (SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F16) x 512 / duration; "
+                "algorithmic TFLOP/s counts only the product's own flops (no padding or masked "
+                "work) against the 2.5 PFLOP/s bf16 peak.  Durations are those of the profiled run "
+                "(short kernels run longer under the profiler).", "",
+                "```", f"{run} --pmc {MFMA_COUNTERS} -d gpurun_out/prof/mfma_<w> -o k -- python3 "
+                       "$REPO/bench.py --kernels-only --steps 3 --only <w>", "```", ""]
+    tr_lines = ["# HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "",
+                "Each counter in its own pass, scaled by what it reads for a plain 1 GiB device copy "
+                f"(factors: FETCH x{fetch_factor:.3f}, WRITE x{write_factor:.3f}).", "",
+                "```",
+                f"{run} --pmc FETCH_SIZE -d gpurun_out/prof/fetch_<w> -o k -- python3 $REPO/bench.py "
+                "--kernels-only --steps 3 --only <w>",
+                f"{run} --pmc WRITE_SIZE -d gpurun_out/prof/write_<w> -o k -- python3 $REPO/bench.py "
+                "--kernels-only --steps 3 --only <w>",
+                f"{run} --pmc FETCH_SIZE -d gpurun_out/prof/fetch_copy -o k -- python3 $REPO/bench.py "
+                "--calibrate-copy",
+                f"{run} --pmc WRITE_SIZE -d gpurun_out/prof/write_copy -o k -- python3 $REPO/bench.py "
+                "--calibrate-copy", "```", ""]
+    traffic = {"fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4),
+               "calibration": "1 GiB device copy", "kernels": {}}
+    for w in ws:
+        sp = workload(w)
+        if sp.cache_len > 0:   # decode: the cache stream of one step
+            alg = {"decode_attn_bytes": 2 * sp.batch * sp.n_kv_heads * (sp.cache_len + 1) * sp.head_dim * 2}
+        else:
+            alg = algorithmic(sp, None)
+        mf = _stages(_counter_dispatches(os.path.join(d, f"mfma_{w}")))
+        fe = _stages(_counter_dispatches(os.path.join(d, f"fetch_{w}")))
+        wr = _stages(_counter_dispatches(os.path.join(d, f"write_{w}")))
+        mf_lines += [f"## {w}", "", "| kernel | stage | avg (us) | MfmaUtil | MFMA TFLOP/s | "
+                     "algorithmic TFLOP/s (of 2500) |", "|---|---|---|---|---|---|"]
+        tr_lines += [f"## {w}", "", "| kernel | stage | FETCH (KiB) | WRITE (KiB) | scaled bytes | "
+                     "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|"]
+        for st, ds in mf.items():
+            dur = _avg(ds, "dur_ns")
+            cyc = _avg(ds, "GRBM_GUI_ACTIVE") / 8
+            util = _avg(ds, "SQ_VALU_MFMA_BUSY_CYCLES") / (cyc * 1024) if cyc else 0.0
+            mops = (_avg(ds, "SQ_INSTS_VALU_MFMA_MOPS_BF16") + _avg(ds, "SQ_INSTS_VALU_MFMA_MOPS_F16")) * 512
+            af = {"downproj": "downproj_flops", "upproj": "upproj_flops", "attention": "attn_flops"}.get(st)
+            atf = f"{alg[af] / (dur * 1e-9) / 1e12:.0f} ({alg[af] / (dur * 1e-9) / 1e12 / 25:.1f}%)" if af else "-"
+            mf_lines.append(f"| `{ds[0]['name'][:70]}` | {st} | {dur / 1e3:.1f} | "
+                            f"{100 * util:.1f}% | {mops / dur / 1e3:.0f} | {atf} |")
+        for st in fe:
+            if st not in wr:
+                continue
+            fk, wk = _avg(fe[st], "FETCH_SIZE"), _avg(wr[st], "WRITE_SIZE")
+            byt = fk * 1024 * fetch_factor + wk * 1024 * write_factor
+            ab = {"convmix": "convmix_bytes", "dec_attention": "decode_attn_bytes"}.get(st)
+            abs_ = f"{alg[ab]:.4g} | {byt / alg[ab]:.3f}" if ab else "- | -"
+            tr_lines.append(f"| `{fe[st][0]['name'][:70]}` | {st} | {fk:.1f} | {wk:.1f} | {byt:.4g} | {abs_} |")
+            key = st if w in ("cca_prefill_b4_t2048", "ccgqa_decode_b64_l32768") else None
+            if key in PROFILE_SOURCES:
+                traffic["kernels"][key] = {"kernel": fe[st][0]["name"], "workload": w,
+                                           "sources": PROFILE_SOURCES[key],
+                                           "source_sha256_16": _source_hash(PROFILE_SOURCES[key]),
+                                           "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                                           "bytes": int(byt)}
+        mf_lines.append("")
+        tr_lines.append("")
+    open(os.path.join(prof, "mfma_util_prefill_b4_t2048_t8192_t16384_decode_b64_l32768.md"), "w").write(
+        "\n".join(mf_lines) + "\n")
+    open(os.path.join(prof, "hbm_traffic_prefill_b4_t2048_t8192_t16384_decode_b64_l32768.md"), "w").write(
+        "\n".join(tr_lines) + "\n")
+    json.dump(traffic, open(os.path.join(prof, "pmc_traffic.json"), "w"), indent=1)
+    print("wrote profiles/ summaries", flush=True)
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        profile_summaries(args.summarize_profiles)
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return
