@@ -30,16 +30,20 @@
 //    of tile j+1, and tiles j+2 and j+3 are in flight; one barrier per tile.
 //  * With the L2 norm on, |q_hat| <= 1 and |k_hat| <= 1, so every exp2-domain
 //    logit lies in [-c_h, c_h] with c_h = tau_h * log2(e).  Softmax is
-//    unchanged by a constant shift, so for c_h <= 60 the kernel subtracts c_h
-//    instead of the running row maximum: 2^(s - c_h) stays within
-//    [2^-120, ~1], normal in fp32 and bf16, and no row maximum, rescale or
-//    cross-lane exchange is needed.  The shift enters as the MFMA's initial
-//    accumulator, so the probabilities are one v_exp_f32 away from the
-//    product.  Otherwise the usual online softmax runs: the rescale of O runs
-//    only when some row's running max grew (a wave-uniform vote).
-//  * The row sums add the bf16-rounded probabilities that the P*V product
-//    consumes, in four independent chains of plain adds; each half-wave
-//    keeps its own partial sums until the end.
+//    unchanged by a constant shift, so for c_h <= 60 the kernel takes 2^s
+//    as it is, without the running row maximum: 2^s stays within
+//    [2^-60, 2^60], normal in fp32 and bf16, the row sums stay below
+//    2^60 * T, and no row maximum, rescale or cross-lane exchange is needed;
+//    the probabilities are one v_exp_f32 away from the product.  Otherwise
+//    the usual online softmax runs: the rescale of O runs only when some
+//    row's running max grew (a wave-uniform vote).
+//  * The row sums are the bf16-rounded probabilities that the P*V product
+//    consumes, summed on the matrix cores: one more MFMA per 16-key chunk,
+//    with an A operand whose row 0 is all ones (row 0 of that accumulator is
+//    the running sum, every other row stays zero).  The VALU is the busier
+//    side of a key tile at d = 64, and these sums would cost it a widening
+//    and an add per probability (a v_dot2 against ones shares the matrix
+//    cores' unit and runs several times slower while MFMAs execute).
 //  * Causal blocks: a workgroup walks the key tiles up to its last query;
 //    only tiles that reach past a wave's first query are masked (tiles past
 //    its last query come out fully masked and add nothing), and the heavy
@@ -60,22 +64,6 @@ template <typename TQ, typename TV, int D> struct AttnTile {
   static constexpr int KB = NBUF * bytes(64) <= 65536 ? 64 : 32;
   static constexpr bool fits = NBUF * bytes(KB) <= 65536;
 };
-
-// l4[e] += p[2e] + p[2e+1] for the 8 bf16 probabilities of one P*V operand:
-// the row sum adds exactly the rounded values that the product consumes, so
-// that the normalised weights sum to one (a query with one key returns that
-// key's value, bit for bit).  Each bf16 widens to fp32 by a shift or a mask
-// of its half of the packed pair; four independent chains of plain adds.
-// (A v_dot2 against ones would take one instruction per pair, but the dot
-// unit is shared with the matrix cores and runs several times slower while
-// MFMAs execute.)
-__device__ __forceinline__ void row_sum_add(float (&l4)[4], const bf16x8 &pf) {
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  const u32x4v u = __builtin_bit_cast(u32x4v, pf);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    l4[e] += __uint_as_float(u[e] << 16) + __uint_as_float(u[e] & 0xffff0000u);
-}
 
 template <typename TQ, typename TV, int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__ q,
@@ -133,12 +121,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   const int last_row = min(blk0 + pos_per, T) - 1;    // last valid query of the block
   const int ntiles = last_row / KB + 1;
 
-  // constant logit shift when the normalised logits are bounded by c_h
+  // no running maximum when the normalised logits are bounded by c_h <= 60
   const float c_h = tau[h] * 1.4426950408889634f;
   const bool fixed_shift = use_norm && c_h >= 0.f && c_h <= 60.f;   // wave-uniform
-  f32x16 s_init;
-#pragma unroll
-  for (int a = 0; a < 16; ++a) s_init[a] = fixed_shift ? -c_h : 0.f;
+  const f32x16 s_init = zero16();
 
   // zero the padding rows of the V^T tiles (d < 32)
   if (D < DP) {
@@ -213,8 +199,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   f32x16 acc[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc[i] = zero16();
-  // the row sum in four partial sums (independent add chains)
+  // the row sum: on the matrix cores for 16-bit V (row 0 of lacc), else in
+  // four partial sums (independent add chains)
   float m_run = -INFINITY, l4[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x16 lacc = zero16();
+  typename MV::frag ones;
+  if constexpr (KSV == 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = l32 == 0 ? (TV)1.f : (TV)0.f;
+  }
 
   // the whole key loop is instantiated once per softmax form, so that the
   // branch between them stays outside the loop
@@ -255,6 +248,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
             for (int e = 0; e < 4; ++e) l4[e] *= alpha;
+            lacc[0] *= alpha;
 #pragma unroll
             for (int i = 0; i < ND; ++i)
 #pragma unroll
@@ -273,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
                                                     : s_cur[hf][KSV * cc + sl] - m_run);
             const typename MV::frag pf = pack_frag<TV>(pv);
             if constexpr (KSV == 8) {
-              row_sum_add(l4, pf);
+              lacc = MV::mma(ones, pf, lacc);
             } else {
               l4[cc & 3] += pv[0];
             }
@@ -318,12 +312,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   if (fixed_shift) run(std::true_type{});
   else run(std::false_type{});
 
-  // each half-wave summed its own keys (and both saw the same rescales)
-  float l_run = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  // 16-bit V: the sum sits in lacc[0] of the lower half-wave (0 in the upper
+  // one); else each half-wave summed its own keys (and both saw the same
+  // rescales)
+  float l_run = KSV == 8 ? lacc[0] : (l4[0] + l4[1]) + (l4[2] + l4[3]);
   l_run += __shfl_xor(l_run, 32, 64);
   if (qpos >= T) return;
   // log2 of the softmax denominator in the exp2 domain, kept for the backward
-  if (lse && hl == 0) lse[(size_t)(b * Hq + h) * Tp + qpos] = (fixed_shift ? c_h : m_run) + __log2f(l_run);
+  if (lse && hl == 0) lse[(size_t)(b * Hq + h) * Tp + qpos] = (fixed_shift ? 0.f : m_run) + __log2f(l_run);
   const float inv_l = 1.f / l_run;
   TV *orow = o + ((size_t)(b * T + qpos)) * (Hq * D) + h * D;
 #pragma unroll
@@ -357,8 +353,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
 //   slot 2j+1 : A  P*V of tile j, S of tile j+1  B  softmax of tile j
 //
 // so every SIMD holds one wave in its VALU phase and one in its MFMA phase.
-// A wave reads the LDS fragments of its next matrix phase during its
-// softmax phase.  K/V^T tiles (16 KiB) stream into a ring of NBUF slots by
+// A wave reads the V^T fragments of its next matrix phase during its
+// softmax phase, the K fragments at the start of the matrix phase.  K/V^T tiles (16 KiB) stream into a ring of NBUF slots by
 // LDS-DMA, two instructions per wave per tile.  Both kernels take the same
 // tiles in the same order with the same per-lane arithmetic, so their
 // outputs agree bit for bit.
@@ -419,9 +415,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
 
   const float c_h = tau[h] * 1.4426950408889634f;
   const bool fixed_shift = use_norm && c_h >= 0.f && c_h <= 60.f;
-  f32x16 s_init;
-#pragma unroll
-  for (int a = 0; a < 16; ++a) s_init[a] = fixed_shift ? -c_h : 0.f;
+  const f32x16 s_init = zero16();
 
   // rows past the padded length (256-row blocks over a 128-padded buffer)
   // read the last padded row; their outputs are never stored
@@ -476,7 +470,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
   f32x16 acc[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc[i] = zero16();
-  float m_run = -INFINITY, l4[4] = {0.f, 0.f, 0.f, 0.f};
+  // row sums on the matrix cores (row 0 of lacc), as in the four-wave kernel
+  float m_run = -INFINITY;
+  f32x16 lacc = zero16();
+  typename MV::frag ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = l32 == 0 ? (bf16)1.f : (bf16)0.f;
   f32x16 s[NH];
   typename MV::frag pf[NH][PC];
 
@@ -527,6 +526,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
         for (int cc = 0; cc < PC; ++cc)
 #pragma unroll
           for (int i = 0; i < ND; ++i) acc[i] = MV::mma(vf[hf][cc][i], pf[hf][cc], acc[i]);
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+        for (int cc = 0; cc < PC; ++cc) lacc = MV::mma(ones, pf[hf][cc], lacc);
     }
     if constexpr (K) {
 #pragma unroll
@@ -564,8 +567,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
         if (__any(mx > m_run)) {
           const float m_new = fmaxf(m_run, mx);
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) l4[e] *= alpha;
+          lacc[0] *= alpha;
 #pragma unroll
           for (int i = 0; i < ND; ++i)
 #pragma unroll
@@ -574,6 +576,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
         }
 #pragma unroll
         for (int i = 0; i < ND; ++i) asm volatile("" : "+v"(acc[i]));
+        asm volatile("" : "+v"(lacc));
       }
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf)
@@ -584,17 +587,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
           for (int sl = 0; sl < KS; ++sl)
             p8[sl] = __builtin_amdgcn_exp2f(FIXED ? s[hf][KS * cc + sl] : s[hf][KS * cc + sl] - m_run);
           pf[hf][cc] = pack_frag<bf16>(p8);
-          row_sum_add(l4, pf[hf][cc]);
         }
       // the softmax's results are formed here, inside its VALU phase: without
-      // these register fences the compiler may sink the packing or the row
-      // sums past the barrier into the next (matrix) phase
+      // these register fences the compiler may sink the packing past the
+      // barrier into the next (matrix) phase
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
         for (int cc = 0; cc < PC; ++cc) asm volatile("" : "+v"(pf[hf][cc]));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(l4[e]));
     };
     // tiles past a wave's last query come out fully masked and add exact
     // zeros, so every wave walks the same tiles with no branch around the
@@ -604,20 +604,24 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
       else softmax(j, std::false_type{});
     };
 
-    // the softmax phase of tile j, with the reads of the next matrix phase's
-    // fragments (V^T of tile j, K of tile j + 1) issued first
+    // the softmax phase of tile j, with the reads of the V^T fragments of
+    // the next matrix phase issued first; that phase reads its K fragments
+    // itself, under its P*V and row-sum MFMAs
     auto softmax_phase = [&](int j) {
-      if (j + 1 < ntiles) load_frags(j, j + 1, Y, Y);
-      else load_frags(j, 0, Y, X);
+      load_frags(j, 0, Y, X);
       __builtin_amdgcn_sched_barrier(0);
       sm(j);
+    };
+    auto pv_qk_phase = [&](int jk) {
+      load_frags(0, jk, X, Y);
+      mfma_phase(Y, Y);
     };
 
     // Slots, both halves (2 * ntiles + 2 barriers):
     //   slot -1  : A  S of tile 0
-    //   slot 2j  : A  softmax j (+ reads V^T j, K j+1)   B  P*V j-1, S of tile j
-    //   slot 2j+1: A  P*V j, S of tile j+1               B  softmax j (+ the same reads)
-    //   after    :                                      B  P*V of the last tile
+    //   slot 2j  : A  softmax j (+ reads V^T j)   B  P*V j-1, S of tile j
+    //   slot 2j+1: A  P*V j, S of tile j+1        B  softmax j (+ reads V^T j)
+    //   after    :                               B  P*V of the last tile
     // Tile t is resident from the barrier that ends slot 2t - 3; tile
     // j + NBUF - 1 is issued at the end of slot 2j (after the phase's own
     // work) into the ring slot of tile j - 1, whose last reads were B's in
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
         softmax_phase(j);
         if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
         slot_end();
-        mfma_phase(Y, Y);
+        pv_qk_phase(j + 1);
         if (j + 2 < ntiles) wait_tile(j + 2);
         slot_end();
       }
@@ -654,7 +658,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
       if (2 < ntiles) wait_tile(2);
       slot_end();
       for (int j = 1; j < ntiles; ++j) {
-        mfma_phase(Y, Y);
+        pv_qk_phase(j);
         if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
         slot_end();
         softmax_phase(j);
@@ -667,10 +671,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
   if (fixed_shift) run(std::true_type{});
   else run(std::false_type{});
 
-  float l_run = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  float l_run = lacc[0];                              // 0 in the upper half-wave
   l_run += __shfl_xor(l_run, 32, 64);
   if (qpos >= T) return;
-  if (lse && hl == 0) lse[(size_t)(b * Hq + h) * Tp + qpos] = (fixed_shift ? c_h : m_run) + __log2f(l_run);
+  if (lse && hl == 0) lse[(size_t)(b * Hq + h) * Tp + qpos] = (fixed_shift ? 0.f : m_run) + __log2f(l_run);
   const float inv_l = 1.f / l_run;
   bf16 *orow = o + ((size_t)(b * T + qpos)) * (Hq * D) + h * D;
 #pragma unroll
