@@ -359,10 +359,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
 // tiles in the same order with the same per-lane arithmetic, so their
 // outputs agree bit for bit.
 //
-// Measured on MI355X it does not beat the four-wave kernel: the softmax
-// phase (about 1.1k cycles with the fragment reads) stays longer than the
-// matrix phase (about 0.7k), so each slot is VALU-bound; CCA_ATTN_AUTO keeps
-// the four-wave kernel.
+// Measured on MI355X (row sums on the matrix cores), a slot pair (one 64-key
+// tile for all 256 rows) takes about 3.3k cycles, against 1.3k cycles of
+// matrix-core work per SIMD (2 waves x 20 MFMAs).  The kernel beats the four-wave one when its grid takes more than
+// one round of the CUs (the 8192- and 16384-token GQA prefills: 167 against
+// 170 us and 318 against 341 us) and loses when one round holds the whole
+// grid (B = 4, T = 2048: 41 against 33 us), where the block with the most
+// causal tiles sets the time and a 256-row block holds twice the tiles of a
+// 128-row one; CCA_ATTN_AUTO chooses by that grid size.
 // ---------------------------------------------------------------------------
 constexpr int PP_NBUF = 6;
 
@@ -707,11 +711,34 @@ static hipError_t attn_pp(const MixShape &s, const TQ *q, const TQ *k, const bf1
   return hipGetLastError();
 }
 
+// Compute units of the current device, queried once per device.
+static int device_cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// attn_kernel 0 (automatic) takes the ping-pong kernel when its grid (one
+// workgroup per CU) needs more than one round of the device's CUs.
+static bool pp_auto(const MixShape &s) {
+  const int hq = gcd_int(s.G, 4);
+  const long grid = (long)((s.T + 256 / hq - 1) / (256 / hq)) * s.B * s.Hkv * (s.G / hq);
+  return grid > device_cu_count();
+}
+
 template <typename TQ, typename TV, int D>
 static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *vt,
                          const float *tau, TV *o, float *lse, hipStream_t stream) {
   if constexpr (D == 64 && sizeof(TQ) == 2 && std::is_same<TV, bf16>::value) {
-    if (s.attn_kernel == 2) return attn_pp<TQ>(s, q, k, vt, tau, o, lse, stream);
+    if (s.attn_kernel == 2 || (s.attn_kernel == 0 && pp_auto(s)))
+      return attn_pp<TQ>(s, q, k, vt, tau, o, lse, stream);
   }
   const int hq = gcd_int(s.G, 4);
   const int nsub = s.G / hq;

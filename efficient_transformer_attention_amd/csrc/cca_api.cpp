@@ -66,13 +66,13 @@ bool qk_is_f16(const cca_config &c) { return c.dtype == CCA_BF16 && c.use_qk_nor
 
 int padded_T(int T) { return (T + TILE_T - 1) / TILE_T * TILE_T; }
 
-// The prefill attention kernel for c: the ping-pong kernel takes bf16 with
-// d = 64; CCA_ATTN_AUTO chooses it for every such shape.
+// The prefill attention kernel for c: 1 four-wave, 2 ping-pong, 0 chosen at
+// launch from the grid size.  The ping-pong kernel takes bf16 with d = 64.
 int attn_kernel_for(const cca_config &c) {
   const bool pp_ok = c.dtype == CCA_BF16 && c.head_dim == 64;
   if (!pp_ok || c.attn_kernel == CCA_ATTN_FOUR_WAVE) return 1;
   if (c.attn_kernel == CCA_ATTN_PING_PONG) return 2;
-  return 1;
+  return 0;
 }
 
 MixShape mix_shape(const cca_config &c) {

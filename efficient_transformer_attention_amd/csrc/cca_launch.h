@@ -60,7 +60,7 @@ struct MixShape {
   int use_shift, use_norm;
   int grouped;             // channel conv: 0 per-head filter along channels, 1 dense per lag
   float rope_base, eps;
-  int attn_kernel;         // prefill attention: 1 four-wave kernel, 2 eight-wave ping-pong
+  int attn_kernel;         // prefill attention: 1 four-wave, 2 eight-wave ping-pong, 0 by grid size
   // RoPE frequencies base^(-2i/d), i < d/2, evaluated on the host in double
   // precision (all zero when RoPE is off); passed by value with the launch.
   double theta[64];

@@ -104,7 +104,9 @@ typedef enum { CCA_QK_MEAN_PRE_POST = 0, CCA_QK_MEAN_PRE = 1 } cca_qk_mean;
  * CCA_ATTN_PING_PONG: 8 waves (256 query rows) per workgroup, 1 per CU, two
  *   halves alternating between the softmax and the matrix products; bf16
  *   with head_dim 64 only (other configurations use the four-wave kernel).
- * CCA_ATTN_AUTO picks one from the shape. */
+ * CCA_ATTN_AUTO takes the ping-pong kernel where it applies and its grid
+ *   (one workgroup per CU) needs more than one round of the device's CUs,
+ *   else the four-wave kernel. */
 typedef enum { CCA_ATTN_AUTO = 0, CCA_ATTN_FOUR_WAVE = 1, CCA_ATTN_PING_PONG = 2 } cca_attn_kernel;
 
 /* Shape and switches of one attention layer.  C (compression) and G are
