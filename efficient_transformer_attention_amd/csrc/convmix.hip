@@ -23,10 +23,9 @@
 //
 // Work split (prefill): one workgroup per (batch b, kv group g, chunk of TC
 // tokens).  The group's pre-conv columns (G query heads, its key head, its
-// value head) for tokens t0-3 .. t0+TC-1 are staged in LDS in the type the
-// down-projection wrote (fp16 in bf16 mode), every 16-byte load of a batch
-// issued before its LDS stores; the 3-token halo of the causal window comes
-// along.  A lane group of d/4 lanes takes one token row and walks every head
+// value head) for tokens t0-3 .. t0+TC-1 move HBM -> LDS by LDS-DMA in the
+// type the down-projection wrote (fp16 in bf16 mode), together with the
+// group's taps; the 3-token halo of the causal window comes along.  A lane group of d/4 lanes takes one token row and walks every head
 // slot of the group, 4 channels per lane: the channel convolution is three
 // lane shifts, RoPE pairs stay inside a lane, the L2 norm is a reduction over
 // the d/4 lanes, and the q-k-mean finds the pre- and post-convolution values
@@ -49,8 +48,14 @@ template <> struct Store4<float> {
   }
 };
 template <> struct Store4<f16> {
+  // the values are rounded to fp32 first, then to fp16: the empty asm keeps
+  // the compiler from folding the conversion into the producing fma (one
+  // rounding instead of two), which it does in some instantiations and not in
+  // others, so every kernel writes the same bits
   __device__ __forceinline__ static void st(f16 *p, const float *v) {
-    *reinterpret_cast<f16x4 *>(p) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+    float a = v[0], b = v[1], c = v[2], d = v[3];
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+    *reinterpret_cast<f16x4 *>(p) = f16x4{(f16)a, (f16)b, (f16)c, (f16)d};
   }
 };
 template <> struct Store4<bf16> {
@@ -59,20 +64,22 @@ template <> struct Store4<bf16> {
   }
 };
 
-// a6 and a7 on this lane's 4 channels of one head: b / max(||b||, eps) over
-// the d/4 lanes of the head, then the rotation of the pairs (4li, 4li+1) and
-// (4li+2, 4li+3) by (cos, sin) = cs0, cs1.
+// a6 and a7 on this lane's 4 channels of one head: sc * b / max(||b||, eps)
+// over the d/4 lanes of the head (sc * b without the norm), then the rotation
+// of the pairs (4li, 4li+1) and (4li+2, 4li+3) by (cos, sin) = cs0, cs1.  sc
+// carries an output scale into the normalisation's factor (1 for none).
 template <int D>
-__device__ __forceinline__ void norm_rope(const MixShape &s, float2 cs0, float2 cs1,
+__device__ __forceinline__ void norm_rope(const MixShape &s, float2 cs0, float2 cs1, float sc,
                                           float (&b)[4], float y[4]) {
   constexpr int LPU = D / 4;
+  float f = sc;
   if (s.use_norm) {
     // 1 / max(||b||, eps) == rsqrt(max(||b||^2, eps^2))
     const float ss = group_sum<LPU>(b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3]);
-    const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, s.eps * s.eps));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) b[c] *= inv;
+    f *= __builtin_amdgcn_rsqf(fmaxf(ss, s.eps * s.eps));
   }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) b[c] *= f;
   y[0] = b[0] * cs0.x - b[1] * cs0.y;
   y[1] = b[0] * cs0.y + b[1] * cs0.x;
   y[2] = b[2] * cs1.x - b[3] * cs1.y;
@@ -115,7 +122,8 @@ __device__ __forceinline__ void conv_slot(const TT *tile, int CW, int row, int s
     p2 = __shfl_up(a[2], 1, LPU);
     p3 = __shfl_up(a[3], 1, LPU);
   }
-  if (li == 0) p1 = p2 = p3 = 0.f;
+  // with 16 lanes per head the DPP row is the head: its lane 0 already reads 0
+  if (LPU != 16 && li == 0) p1 = p2 = p3 = 0.f;
   const f32x4 w = *reinterpret_cast<const f32x4 *>(ctaps + slot * 4);
   b[0] = w[0] * a[0] + w[1] * p3 + w[2] * p2 + w[3] * p1;
   b[1] = w[0] * a[1] + w[1] * a[0] + w[2] * p3 + w[3] * p2;
@@ -128,11 +136,12 @@ __device__ __forceinline__ void conv_slot(const TT *tile, int CW, int row, int s
 //   conv(slot, b, p)  the slot's channel-conv output b and its
 //                     pre-convolution values p (f32x4)
 //   emit(slot, y)     receives the normalised, rotated result
+//   scale(slot)       a factor applied to the slot's output (see norm_rope)
 // s.use_mean: 0 off; 1 q += (q~ + k~)/2, k += (k~ + avg q~)/2; 2 q += (q~ + b_q
 // + k~ + b_k)/4, k += (k~ + b_k + avg q~ + avg b_q)/4.
-template <int D, typename ConvFn, typename EmitFn>
+template <int D, typename ConvFn, typename EmitFn, typename ScaleFn>
 __device__ __forceinline__ void mix_row(int G, const MixShape &s, float2 cs0, float2 cs1,
-                                        ConvFn &&conv, EmitFn &&emit) {
+                                        ConvFn &&conv, EmitFn &&emit, ScaleFn &&scale) {
   const bool mean = s.use_mean != 0, post = s.use_mean == 2;
   const float coef = post ? 0.25f : 0.5f;
   float bk[4];
@@ -156,7 +165,7 @@ __device__ __forceinline__ void mix_row(int G, const MixShape &s, float2 cs0, fl
       }
     }
     float y[4];
-    norm_rope<D>(s, cs0, cs1, b, y);
+    norm_rope<D>(s, cs0, cs1, scale(h), b, y);
     emit(h, y);
   }
   if (mean) {
@@ -165,7 +174,7 @@ __device__ __forceinline__ void mix_row(int G, const MixShape &s, float2 cs0, fl
     for (int c = 0; c < 4; ++c) bk[c] += coef * (sk[c] + sq[c] * invg);
   }
   float y[4];
-  norm_rope<D>(s, cs0, cs1, bk, y);
+  norm_rope<D>(s, cs0, cs1, scale(G), bk, y);
   emit(G, y);
 }
 
@@ -280,12 +289,16 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
                                                               float *__restrict__ bout, int TC) {
   extern __shared__ __attribute__((aligned(16))) unsigned char mix_smem[];
   const int G = s.G, CW = (G + 2) * D;
-  float *tile = reinterpret_cast<float *>(mix_smem);           // rows: tokens t0-HALO .. t0+TC-1
-  float *staps = reinterpret_cast<float *>(mix_smem + tile_bytes(TC + HALO, G, D, 4));
+  // LDS: the tile (rows: tokens t0-HALO .. t0+TC-1), then the group's seq
+  // taps [(G+1) D][4], channel taps [G+1][4], tau [G] (rounded up to 4
+  // floats) and the RoPE frequencies [D/2] (double)
+  TI *tile = reinterpret_cast<TI *>(mix_smem);
+  float *staps = reinterpret_cast<float *>(mix_smem + tile_bytes(TC + HALO, G, D, sizeof(TI)));
   float *ctaps = staps + (G + 1) * D * 4;
-  float *tsc = ctaps + (G + 1) * 4;
+  float *ltau = ctaps + (G + 1) * 4;
+  double *lth = reinterpret_cast<double *>(ltau + (G + 3) / 4 * 4);
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int nchunks = s.Tp / TC;
   // consecutive chunks of a (b, g) on one XCD: the halo rows and the value
   // tile's partial lines meet in one L2
@@ -297,53 +310,76 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
   const int vcol = (G + 1) * D;
   const TI *src = qkv + (size_t)b * s.T * N;
-
-  // the group's taps, tau and this lane's RoPE frequencies are requested
-  // first, so their latency overlaps the tile's
-  TapRegs<D> tr;
-  tr.load(s, w, g);
   constexpr int LPU = D / 4;
   const int li = tid % LPU, ui = tid / LPU;
-  const double th0 = s.theta[2 * li], th1 = s.theta[2 * li + 1];
 
-  // the tile, in fp32: each thread owns one 16-byte column chunk of the
-  // group and walks the rows with a fixed stride (all loads of a batch of
-  // rows issued before their LDS stores, converted once on the way in);
-  // tokens outside [0, T) read as zero
+  // Everything the mixing reads reaches LDS by LDS-DMA, with no register
+  // staging: the taps and tau, then the tile.  Out-of-range offsets (taps
+  // past k_s / k_c, tokens outside [0, T)) land as zeros.
   {
-    constexpr int EPC = 16 / (int)sizeof(TI), NB = 4;
-    const int cpr = CW / EPC, rstep = 256 / cpr;          // cpr <= 256 (checked on the host)
-    const int cc = tid % cpr, r0 = tid / cpr;
-    const bool col_active = r0 < rstep;
-    const TI *colp = src + group_col(cc * EPC, g, G, D, eq, ekv);
-    float *dcol = tile + cc * EPC;
-    const int rows = TC + HALO;
-    for (int rb = r0; rb < rows; rb += rstep * NB) {
-      u32x4 v[NB];
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int r = rb + rstep * u, tok = t0 - HALO + r;
-        v[u] = zero_u32x4();
-        if (col_active && r < rows && tok >= 0 && tok < s.T) v[u] = ld16(colp + tok * N);
-      }
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int r = rb + rstep * u;
-        if (col_active && r < rows) {
-          float *dst = dcol + r * CW;
-          if constexpr (EPC == 8) {
-            const TI *h = reinterpret_cast<const TI *>(&v[u]);
-            *reinterpret_cast<f32x4 *>(dst) = ld4f<TI>(h);
-            *reinterpret_cast<f32x4 *>(dst + 4) = ld4f<TI>(h + 4);
-          } else {
-            st16(dst, v[u]);
-          }
-        }
-      }
+    const int ks = s.ks, kc = s.kc;
+    const unsigned qb = (unsigned)(G * D * ks * 4), kb = (unsigned)(D * ks * 4);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(w.q_seq + (size_t)g * G * D * ks), 0, qb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(w.k_seq + (size_t)g * D * ks), 0, kb, 0x00020000);
+    const int nq = G * D / 16, nk = D / 16;               // 64-float instructions ([c][4] rows)
+    for (int i = wv; i < nq + nk; i += 4) {
+      const bool isq = i < nq;
+      const int f = (isq ? i : i - nq) * 64 + lane, c = f >> 2, j = f & 3;
+      const unsigned off = j < ks ? (unsigned)((c * ks + j) * 4) : (isq ? qb : kb);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isq ? rq : rk, as_lds(staps + i * 64), 4, (int)off, 0, 0, 0);
+    }
+    if (wv == 3) {
+      const unsigned cqb = (unsigned)(G * kc * 4), ckb = (unsigned)(kc * 4), tb = (unsigned)(G * 4);
+      const __amdgpu_buffer_rsrc_t rcq =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(w.q_chan + (size_t)g * G * kc), 0, cqb, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rck =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(w.k_chan + (size_t)g * kc), 0, ckb, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rt =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(w.tau + (size_t)g * G), 0, tb, 0x00020000);
+      const int c = lane >> 2, j = lane & 3;
+      if (lane < G * 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rcq, as_lds(ctaps), 4,
+                                                 j < kc ? (int)((c * kc + j) * 4) : (int)cqb, 0, 0, 0);
+      if (lane < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rck, as_lds(ctaps + G * 4), 4,
+                                                 j < kc ? (int)(j * 4) : (int)ckb, 0, 0, 0);
+      if (lane < G)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, as_lds(ltau), 4, lane * 4, 0, 0, 0);
     }
   }
-  tr.store(s, staps, ctaps, tsc);
-  __syncthreads();
+  // the tile: row-major [TC + HALO][CW] without padding, so instruction i
+  // fills its bytes [1024 i, 1024 i + 1024): lane l moves 16-byte chunk
+  // 64 i + l (row chunk / cpr); instruction i goes out from wave i % 4
+  {
+    constexpr int EPC = 16 / (int)sizeof(TI);
+    const int cpr = CW / EPC, nck = (TC + HALO) * cpr;
+    const int tlo = max(t0 - HALO, 0), thi = min(t0 + TC, s.T);
+    const unsigned nbytes = thi > tlo ? (unsigned)((size_t)(thi - tlo) * N * sizeof(TI)) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(src + (size_t)tlo * N), 0, nbytes, 0x00020000);
+    for (int i = wv; i * 64 < nck; i += 4) {
+      const int c = i * 64 + lane;
+      const int row = c / cpr, tok = t0 - HALO + row;
+      const unsigned off =
+          tok >= tlo && tok < thi
+              ? (unsigned)(((size_t)(tok - tlo) * N + group_col((c - row * cpr) * EPC, g, G, D, eq, ekv)) *
+                           sizeof(TI))
+              : nbytes;
+      if (c < nck)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(mix_smem + (size_t)i * 1024), 16, (int)off,
+                                                 0, 0, 0);
+    }
+  }
+  // the RoPE frequencies come from the kernel arguments (scalar loads)
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) lth[i] = s.theta[i];
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+  const double th0 = lth[2 * li], th1 = lth[2 * li + 1];
 
   // one token row per lane group, every head slot of the group
   const int upp = 256 / LPU;
@@ -359,13 +395,15 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
     const int tok = t0 + r;
     const float2 cs0 = rope_cs_theta(tok, th0, s.rope_base);
     const float2 cs1 = rope_cs_theta(tok, th1, s.rope_base);
-    const float *cur = tile + (r + HALO) * CW + 4 * li;
+    const TI *cur = tile + (r + HALO) * CW + 4 * li;
+    // q leaves scaled by tau_h * log2(e); rows past the sequence's end are
+    // zero: both factors ride on the normalisation's
+    const bool live = tok < s.T;
+    auto scale = [&](int slot) {
+      return live ? (slot < G ? ltau[slot] * 1.4426950408889634f : 1.f) : 0.f;
+    };
     auto emit = [&](int slot, float *y) {
-      if (tok >= s.T) y[0] = y[1] = y[2] = y[3] = 0.f;
       if (slot < G) {
-        const float sc = tsc[slot];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) y[c] *= sc;
         Store4<TQ>::st(qlane + slot * qhead + r * D, y);
       } else {
         Store4<TQ>::st(klane + r * D, y);
@@ -385,41 +423,61 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
                                   : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) bb[c] = v[c];
-        pre = *reinterpret_cast<const f32x4 *>(cur + slot * D);
+        pre = ld4f<TI>(cur + slot * D);
       };
-      mix_row<D>(G, sm, cs0, cs1, conv, emit);
+      mix_row<D>(G, sm, cs0, cs1, conv, emit, scale);
     } else {
       auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
-        conv_slot<D, float>(tile, CW, r + HALO, slot, li, staps, ctaps, bb, pre);
+        conv_slot<D, TI>(tile, CW, r + HALO, slot, li, staps, ctaps, bb, pre);
         if (OUT && blane && tok < s.T)
           *reinterpret_cast<f32x4 *>(blane + (size_t)tok * (eq + ekv) +
                                      (slot < G ? (g * G + slot) * D : eq + g * D)) =
               f32x4{bb[0], bb[1], bb[2], bb[3]};
       };
-      mix_row<D>(G, sm, cs0, cs1, conv, emit);
+      mix_row<D>(G, sm, cs0, cs1, conv, emit, scale);
     }
   }
 
-  // value head, transposed: vt[b, g, dd, perm(t)] for the chunk's tokens
-  for (int e = tid; e < D * (TC / 8); e += 256) {
-    const int dd = e / (TC / 8), grp = e % (TC / 8);
-    float vals[8];
+  // value head, transposed: vt[b, g, dd, p] holds token vt_perm(p) of the
+  // chunk.  A thread takes 4 channels at the 8 positions 8 grp .. 8 grp + 7,
+  // i.e. tokens tb + {0, 1, 2, 3, 8, 9, 10, 11} with tb = 16 (grp >> 1) +
+  // 4 (grp & 1): 8 LDS reads of 4 elements at fixed row strides, every row
+  // inside the tile.  Only the chunk holding the sequence's end zeroes the
+  // positions past it.
+  auto write_vt = [&](auto tail) {
+    const int rb = CW * (int)sizeof(TI);
+    for (int e = tid; e < (D / 4) * (TC / 8); e += 256) {
+      const int d4 = e / (TC / 8), grp = e % (TC / 8);
+      const int tb = 16 * (grp >> 1) + 4 * (grp & 1);
+      const unsigned char *base = reinterpret_cast<const unsigned char *>(tile) +
+                                  (tb + HALO - shifted) * rb + (vcol + 4 * d4) * (int)sizeof(TI);
+      float vals[4][8];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int tl = vt_perm(8 * grp + jj);
-      vals[jj] = (t0 + tl < s.T) ? tile[(tl + HALO - shifted) * CW + vcol + dd] : 0.f;
+      for (int jj = 0; jj < 8; ++jj) {
+        const int dt = jj < 4 ? jj : jj + 4;
+        f32x4 v = ld4f<TI>(reinterpret_cast<const TI *>(base + dt * rb));
+        if constexpr (decltype(tail)::value)
+          if (t0 + tb + dt >= s.T) v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vals[c][jj] = v[c];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + 4 * d4 + c) * s.Tp + t0 + 8 * grp;
+        Store4<TV>::st(dst, vals[c]);
+        Store4<TV>::st(dst + 4, vals[c] + 4);
+      }
     }
-    TV *dst = vt + ((size_t)(b * s.Hkv + g) * D + dd) * s.Tp + t0 + 8 * grp;
-    Store4<TV>::st(dst, vals);
-    Store4<TV>::st(dst + 4, vals + 4);
-  }
+  };
+  if (t0 + TC > s.T) write_vt(std::true_type{});
+  else write_vt(std::false_type{});
   if (OUT && st.v_cache) {
     for (int e = tid; e < TC * (D / 4); e += 256) {
       const int r = e / (D / 4), c4 = e % (D / 4), tok = t0 + r;
       if (tok >= s.T) continue;
       size_t row;
       if (!cache_row_store(st, b, s.Hkv, g, tok, &row)) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(tile + (r + HALO - shifted) * CW + vcol + 4 * c4);
+      const f32x4 v = ld4f<TI>(tile + (r + HALO - shifted) * CW + vcol + 4 * c4);
       const float vv[4] = {v[0], v[1], v[2], v[3]};
       Store4<TV>::st(reinterpret_cast<TV *>(st.v_cache) + row * D + 4 * c4, vv);
     }
@@ -553,7 +611,7 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
       else if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
         Store4<TV>::st(kc + row * D + 4 * li, y);
     };
-    mix_row<D>(G, s, cs0, cs1, conv, emit);
+    mix_row<D>(G, s, cs0, cs1, conv, emit, [](int) { return 1.f; });
   }
   // value rows of the new tokens into the cache
   for (int e = tid; e < m * (D / 4); e += 256) {
@@ -688,7 +746,7 @@ __global__ __launch_bounds__(256) void convmix_decode_grouped_kernel(
       else if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
         Store4<TV>::st(kc + row * D + 4 * li, y);
     };
-    mix_row<D>(G, s, cs0, cs1, conv, emit);
+    mix_row<D>(G, s, cs0, cs1, conv, emit, [](int) { return 1.f; });
   }
   for (int e = tid; e < m * (D / 4); e += 256) {
     const int j = e / (D / 4), c4 = e % (D / 4);
@@ -803,16 +861,13 @@ __global__ __launch_bounds__(256, 1) void downproj_mix_kernel(MixShape s, MixTap
       conv_slot<D, float>(tile, CW, r + HALO, slot, li, staps, ctaps, bb, pre);
     };
     auto emit = [&](int slot, float *y) {
-      if (slot < G) {
-        const float sc = tsc[slot];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) y[c] *= sc;
+      if (slot < G)
         Store4<TQ>::st(q + ((size_t)(b * s.Hq + g * G + slot) * s.Tp + tok) * D + 4 * li, y);
-      } else {
+      else
         Store4<TQ>::st(k + ((size_t)(b * s.Hkv + g) * s.Tp + tok) * D + 4 * li, y);
-      }
     };
-    mix_row<D>(G, s, cs0, cs1, conv, emit);
+    // q leaves scaled by tau_h * log2(e), folded into the normalisation
+    mix_row<D>(G, s, cs0, cs1, conv, emit, [&](int slot) { return slot < G ? tsc[slot] : 1.f; });
   }
   // value head, transposed: vt[b, g, dd, perm(t)]
   const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
@@ -867,15 +922,15 @@ template hipError_t launch_downproj_mix<bf16, bf16>(const MixShape &, const MixT
                                                     bf16 *, hipStream_t);
 
 // LDS of the prefill kernel for chunks of TC tokens (fp32 tile).
-static size_t mix_lds_bytes(int TC, int G, int D) {
-  return tile_bytes(TC + HALO, G, D, 4) + (size_t)taps_floats(G, D) * 4;
+static size_t mix_lds_bytes(int TC, int G, int D, int es) {
+  return tile_bytes(TC + HALO, G, D, es) + (size_t)taps_floats(G, D) * 4 + (size_t)D / 2 * 8;
 }
 
-// Tokens per workgroup: the largest of 64 / 32 / 16 whose tile stays within
+// Tokens per workgroup: the largest of 64 / 32 / 16 whose LDS stays within
 // 40 KiB (several workgroups per CU keep many rows in flight).
-static int mix_chunk(int G, int D) {
+static int mix_chunk(int G, int D, int es) {
   for (int tc = 64; tc > 16; tc /= 2)
-    if (mix_lds_bytes(tc, G, D) <= 40 * 1024) return tc;
+    if (mix_lds_bytes(tc, G, D, es) <= 40 * 1024) return tc;
   return 16;
 }
 
@@ -889,17 +944,17 @@ bool convmix_decode_fits(int G, int d, int m) {
 
 bool convmix_fits(int G, int d) {
   // the prefill staging gives each thread one 16-byte column chunk of a row
-  return (G + 2) * d / 4 <= 256 && mix_lds_bytes(16, G, d) <= 65536 && convmix_decode_fits(G, d, 1);
+  return (G + 2) * d / 4 <= 256 && mix_lds_bytes(16, G, d, 4) <= 65536 && convmix_decode_fits(G, d, 1);
 }
 
 template <typename TI, typename TQ, typename TV, int D, int MEAN, bool R1B, bool OUT>
 static hipError_t convmix_prefill_launch(const MixShape &s, const MixTaps &w, const TI *qkv, TQ *q,
                                          TQ *k, TV *vt, const StateOut &st, const float *r1b,
                                          float *bout, hipStream_t stream) {
-  const int TC = mix_chunk(s.G, D);
+  const int TC = mix_chunk(s.G, D, sizeof(TI));
   const long long grid = (long long)s.B * s.Hkv * (s.Tp / TC);
   if (grid >= (1ll << 31)) return hipErrorInvalidValue;
-  const size_t lds = mix_lds_bytes(TC, s.G, D);
+  const size_t lds = mix_lds_bytes(TC, s.G, D, sizeof(TI));
   hipLaunchKernelGGL((convmix_prefill_kernel<TI, TQ, TV, D, MEAN, R1B, OUT>), dim3((unsigned)grid),
                      dim3(256), lds, stream, s, w, qkv, q, k, vt, st, r1b, bout, TC);
   return hipGetLastError();
