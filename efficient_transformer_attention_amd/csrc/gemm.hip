@@ -167,12 +167,52 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const Tin *__restrict__ A,
 //   chunk that the swizzle places there.  Rows past M / N read as zero (buffer
 //   range check).
 // ---------------------------------------------------------------------------
+// Tile (tm, tn) of workgroup bid on a tile grid of ntm x ntn.  The hardware
+// deals workgroup ids round-robin to the 8 XCDs; with py in {1, 2, 4, 8} the
+// XCDs form a (8/py) x py grid over the tiles, XCD bid % 8 owning a band of
+// ntm/(8/py) x ntn/py tiles that it walks row by row in dispatch order
+// (bid / 8), so its L2 holds the band's columns of B while rows of A stream
+// through.  py = 0: each XCD takes a contiguous run of tiles in row-major
+// order (grids that do not split evenly).
+__device__ __forceinline__ void xcd_tile(int bid, int ntm, int ntn, int py, int &tm, int &tn) {
+  if (py == 0) {
+    const int lid = xcd_remap(bid, ntm * ntn);
+    tm = lid / ntn;
+    tn = lid % ntn;
+    return;
+  }
+  const int px = 8 / py, bm = ntm / px, bn = ntn / py;
+  const int x = bid & 7, slot = bid >> 3;
+  tm = (x / py) * bm + slot / bn;
+  tn = (x % py) * bn + slot % bn;
+}
+
+// The XCD split for xcd_tile: among the splits that divide the tile grid, the
+// one with the fewest bytes brought into the L2s, py |A| + (8/py) |B| (each
+// XCD reads its rows of A and its columns of B once); ties go to the larger
+// py, whose narrower band of B is likelier to stay in L2.  0 when none
+// divides the grid.
+static int xcd_split(int ntm, int ntn, double abytes, double bbytes) {
+  int best = 0;
+  double bc = 0.0;
+  for (int py = 1; py <= 8; py *= 2) {
+    const int px = 8 / py;
+    if (ntm % px || ntn % py) continue;
+    const double c = py * abytes + px * bbytes;
+    if (best == 0 || c <= bc * (1.0 + 1e-9)) {
+      best = py;
+      bc = c;
+    }
+  }
+  return best;
+}
+
 template <typename Tout, int BM, int BN, int BK, int STAGES, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__restrict__ A,
                                                              const bf16 *__restrict__ Bm,
                                                              Tout *__restrict__ C, int M, int N,
                                                              int K, int lda, int ldb, int ldc,
-                                                             int kchunk) {
+                                                             int kchunk, int xsplit) {
   typedef Mfma32<bf16> MF;
   typedef MF::frag Frag;
   constexpr int ROWB = BK * 2, CPR = ROWB / 16, KK = BK / 16;   // row bytes, chunks, k-chunks
@@ -189,8 +229,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_nt_dma_kernel(const bf16 *__res
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hl = lane >> 5;
   const int ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
-  const int lid = xcd_remap(blockIdx.x, ntn * ntm);
-  const int m0 = (lid / ntn) * BM, n0 = (lid % ntn) * BN;
+  int tm, tn;
+  xcd_tile(blockIdx.x, ntm, ntn, xsplit, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   // split contraction: slice blockIdx.y covers K range [kbeg, kbeg + kchunk)
   // and writes its own M x ldc block of C
   const int kbeg = blockIdx.y * kchunk;
@@ -464,17 +505,21 @@ hipError_t launch_gemm_nt(const Tin *A, const Tin *B, Tout *C, int M, int N, int
       // backward's dx = dz W_qkv at K = 1536: 12% faster than 128 x 128 there,
       // slower at K = 512 and no faster at K = 1024); else 128 x 128 tiles (two
       // workgroups per CU)
+      const double ab = 2.0 * M * K, bb = 2.0 * N * K;
       const int g256 = ((M + 255) / 256) * ((N + 191) / 192);
       if (g256 >= 224 && g256 <= 256) {
+        const int xs = xcd_split((M + 255) / 256, (N + 191) / 192, ab, bb);
         hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 256, 192, 32, 5, 1>), dim3(g256), dim3(256), 0,
-                           stream, A, B, C, M, N, K, lda, ldb, ldc, K);
+                           stream, A, B, C, M, N, K, lda, ldb, ldc, K, xs);
       } else if (N % 256 == 0 && N >= 2048 && K >= 1536 && M >= 4096) {
         const int g = ((M + 127) / 128) * (N / 256);
+        const int xs = xcd_split((M + 127) / 128, N / 256, ab, bb);
         hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 256, 32, 5, 1>), dim3(g), dim3(256), 0,
-                           stream, A, B, C, M, N, K, lda, ldb, ldc, K);
+                           stream, A, B, C, M, N, K, lda, ldb, ldc, K, xs);
       } else {
+        const int xs = xcd_split((M + BM - 1) / BM, (N + BN - 1) / BN, ab, bb);
         hipLaunchKernelGGL((gemm_nt_dma_kernel<Tout, 128, 128, 32, 5, 2>), dim3(grid), dim3(256), 0,
-                           stream, A, B, C, M, N, K, lda, ldb, ldc, K);
+                           stream, A, B, C, M, N, K, lda, ldb, ldc, K, xs);
       }
       return hipGetLastError();
     }
@@ -559,7 +604,7 @@ hipError_t launch_gemm_nt_long_k(const Tin *A, const Tin *B, float *C, int M, in
         (size_t)Sused * M * N <= ws_floats && (size_t)M * N % 4 == 0) {
       const int grid = ((M + 127) / 128) * ((N + 127) / 128);
       hipLaunchKernelGGL((gemm_nt_dma_kernel<float, 128, 128, 32, 5, 2>), dim3(grid, Sused),
-                         dim3(256), 0, stream, A, B, ws, M, N, K, lda, ldb, N, kchunk);
+                         dim3(256), 0, stream, A, B, ws, M, N, K, lda, ldb, N, kchunk, 0);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const size_t n = (size_t)M * N;
