@@ -541,13 +541,17 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
   const int li = tid % LPU, ui = tid / LPU;
   const double th0 = s.theta[2 * li], th1 = s.theta[2 * li + 1];
 
-  // the three carried rows (all loads issued before their LDS stores)
-  constexpr int LB = 8;
-  for (int e0 = 0; e0 < 3 * CW; e0 += 256 * LB) {
+  // the tile: the three carried rows, then the m new rows (the down-
+  // projection output, or the sum of its split-contraction slices in slice
+  // order).  Each pass issues every load of LB carried and NU new elements
+  // per thread before the first LDS store: one pass at the decode shapes.
+  constexpr int LB = 8, NU = 2;
+  const size_t mn = (size_t)s.B * m * N;
+  for (int p = 0; p * 256 * LB < 3 * CW || p * 256 * NU < m * CW; ++p) {
     float v[LB];
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
-      const int e = e0 + tid + 256 * u;
+      const int e = p * 256 * LB + tid + 256 * u;
       const int r = e / CW, col = e % CW;
       v[u] = 0.f;
       if (e >= 3 * CW) continue;
@@ -559,32 +563,40 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
         v[u] = to_f32(vs[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + col - (G + 1) * D]);
       }
     }
+    float a[NU][16];
+#pragma unroll
+    for (int n = 0; n < NU; ++n) {
+      const int e = p * 256 * NU + tid + 256 * n;
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) a[n][sl] = 0.f;
+      if (e >= m * CW) continue;
+      const int j = e / CW, col = e % CW;
+      const size_t i = (size_t)(b * m + j) * N + group_col(col, g, G, D, eq, ekv);
+      if (qkv.slices == 0) {
+        a[n][0] = qkv.qkv[i];
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < 16; ++sl)
+          if (sl < qkv.slices) a[n][sl] = qkv.parts[sl * mn + i];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
-      const int e = e0 + tid + 256 * u;
+      const int e = p * 256 * LB + tid + 256 * u;
       if (e < 3 * CW) tile[e] = v[u];
     }
-  }
-  // the m new rows: the down-projection output, or the sum of its
-  // split-contraction slices in slice order (all slice loads of an element
-  // issued before the sum)
-  for (int e = tid; e < m * CW; e += 256) {
-    const int j = e / CW, col = e % CW;
-    const size_t i = (size_t)(b * m + j) * N + group_col(col, g, G, D, eq, ekv);
-    float acc;
-    if (qkv.slices == 0) {
-      acc = qkv.qkv[i];
-    } else {
-      const size_t mn = (size_t)s.B * m * N;
-      float a[16];
 #pragma unroll
-      for (int sl = 0; sl < 16; ++sl) a[sl] = sl < qkv.slices ? qkv.parts[sl * mn + i] : 0.f;
-      acc = a[0];
+    for (int n = 0; n < NU; ++n) {
+      const int e = p * 256 * NU + tid + 256 * n;
+      if (e >= m * CW) continue;
+      float acc = a[n][0];
+      if (qkv.slices > 0) {
 #pragma unroll
-      for (int sl = 1; sl < 16; ++sl)
-        if (sl < qkv.slices) acc += a[sl];
+        for (int sl = 1; sl < 16; ++sl)
+          if (sl < qkv.slices) acc += a[n][sl];
+      }
+      tile[3 * CW + e] = acc;
     }
-    tile[(3 + j) * CW + col] = acc;
   }
   tr.store(s, staps, ctaps, tsc);
   __syncthreads();
@@ -592,6 +604,81 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
   const int upp = 256 / LPU;
   TV *kc = reinterpret_cast<TV *>(in.k_cache);
   TV *vc = reinterpret_cast<TV *>(in.v_cache);
+  // the value rows of the new tokens and the rolled state depend on the tile
+  // only: their stores go out before the mixing
+  for (int e = tid; e < m * (D / 4); e += 256) {
+    const int j = e / (D / 4), c4 = e % (D / 4);
+    size_t row;
+    if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
+      Store4<TV>::st(vc + row * D + 4 * c4, tile + (3 + j - shifted) * CW + (G + 1) * D + 4 * c4);
+  }
+  // rolled state: slot sl holds token L + m - ks1 + sl = tile row m + 3 - ks1 + sl
+  {
+    TV *oq = reinterpret_cast<TV *>(out.conv_q);
+    TV *ok = reinterpret_cast<TV *>(out.conv_k);
+    for (int e = tid; e < ks1 * G * D; e += 256) {
+      const int sl = e / (G * D), c = e % (G * D);
+      oq[(size_t)(b * ks1 + sl) * eq + g * G * D + c] = from_f32<TV>(tile[(m + 3 - ks1 + sl) * CW + c]);
+    }
+    for (int e = tid; e < ks1 * D; e += 256) {
+      const int sl = e / D, c = e % D;
+      ok[(size_t)(b * ks1 + sl) * ekv + g * D + c] = from_f32<TV>(tile[(m + 3 - ks1 + sl) * CW + G * D + c]);
+    }
+    if (shifted && out.vshift)
+      for (int c = tid; c < D; c += 256)
+        reinterpret_cast<TV *>(out.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
+            from_f32<TV>(tile[(m + 2) * CW + (G + 1) * D + c]);
+  }
+
+  auto emit_to = [&](int j, int slot, float *y) {
+    size_t row;
+    if (slot < G)
+      Store4<float>::st(qout + ((size_t)(b * m + j) * s.Hq + g * G + slot) * D + 4 * li, y);
+    else if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
+      Store4<TV>::st(kc + row * D + 4 * li, y);
+  };
+  if (m * (G + 1) <= upp) {
+    // one (token, head slot) unit per lane group, all in parallel: the
+    // convolutions, then the q-k-mean terms exchanged through LDS (own[u]:
+    // the values unit u contributes to the mean), then norm and RoPE.  The
+    // same arithmetic, in the same order, as mix_row.
+    float *own = tsc + (G + 3) / 4 * 4;
+    const int units = m * (G + 1), u = ui < units ? ui : units - 1;
+    const int j = u / (G + 1), sl = u % (G + 1);
+    const float2 cs0 = rope_cs_theta(L + j, th0, s.rope_base);
+    const float2 cs1 = rope_cs_theta(L + j, th1, s.rope_base);
+    float bb[4];
+    f32x4 pre;
+    conv_slot<D, float>(tile, CW, 3 + j, sl, li, staps, ctaps, bb, pre);
+    const bool mean = s.use_mean != 0, post = s.use_mean == 2;
+    float o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = post ? pre[c] + bb[c] : pre[c];
+    if (ui < units) *reinterpret_cast<f32x4 *>(own + u * D + 4 * li) = f32x4{o[0], o[1], o[2], o[3]};
+    __syncthreads();
+    if (mean) {
+      const float coef = post ? 0.25f : 0.5f;
+      const f32x4 sk = *reinterpret_cast<const f32x4 *>(own + (j * (G + 1) + G) * D + 4 * li);
+      if (sl < G) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bb[c] += coef * (o[c] + sk[c]);
+      } else {
+        float sq[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < G; ++h) {
+          const f32x4 oh = *reinterpret_cast<const f32x4 *>(own + (j * (G + 1) + h) * D + 4 * li);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sq[c] += oh[c];
+        }
+        const float invg = 1.f / (float)G;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bb[c] += coef * (sk[c] + sq[c] * invg);
+      }
+    }
+    float y[4];
+    norm_rope<D>(s, cs0, cs1, 1.f, bb, y);
+    if (ui < units) emit_to(j, sl, y);
+    return;
+  }
   // one new token per lane group; groups past the last token compute on row
   // 0 and store nothing
   for (int j0 = 0; j0 < m; j0 += upp) {
@@ -604,37 +691,10 @@ __global__ __launch_bounds__(256) void convmix_decode_kernel(MixShape s, MixTaps
       conv_slot<D, float>(tile, CW, 3 + jr, slot, li, staps, ctaps, bb, pre);
     };
     auto emit = [&](int slot, float *y) {
-      if (!active) return;
-      size_t row;
-      if (slot < G)
-        Store4<float>::st(qout + ((size_t)(b * m + j) * s.Hq + g * G + slot) * D + 4 * li, y);
-      else if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
-        Store4<TV>::st(kc + row * D + 4 * li, y);
+      if (active) emit_to(j, slot, y);
     };
     mix_row<D>(G, s, cs0, cs1, conv, emit, [](int) { return 1.f; });
   }
-  // value rows of the new tokens into the cache
-  for (int e = tid; e < m * (D / 4); e += 256) {
-    const int j = e / (D / 4), c4 = e % (D / 4);
-    size_t row;
-    if (cache_row_store(in, b, s.Hkv, g, L + j, &row))
-      Store4<TV>::st(vc + row * D + 4 * c4, tile + (3 + j - shifted) * CW + (G + 1) * D + 4 * c4);
-  }
-  // rolled state: slot sl holds token L + m - ks1 + sl = tile row m + 3 - ks1 + sl
-  TV *oq = reinterpret_cast<TV *>(out.conv_q);
-  TV *ok = reinterpret_cast<TV *>(out.conv_k);
-  for (int e = tid; e < ks1 * G * D; e += 256) {
-    const int sl = e / (G * D), c = e % (G * D);
-    oq[(size_t)(b * ks1 + sl) * eq + g * G * D + c] = from_f32<TV>(tile[(m + 3 - ks1 + sl) * CW + c]);
-  }
-  for (int e = tid; e < ks1 * D; e += 256) {
-    const int sl = e / D, c = e % D;
-    ok[(size_t)(b * ks1 + sl) * ekv + g * D + c] = from_f32<TV>(tile[(m + 3 - ks1 + sl) * CW + G * D + c]);
-  }
-  if (shifted && out.vshift)
-    for (int c = tid; c < D; c += 256)
-      reinterpret_cast<TV *>(out.vshift)[(size_t)(b * (s.Hkv / 2) + g - s.Hkv / 2) * D + c] =
-          from_f32<TV>(tile[(m + 2) * CW + (G + 1) * D + c]);
 }
 
 // The decode mixing under the grouped channel conv (m = s.T new tokens per
@@ -934,8 +994,10 @@ static int mix_chunk(int G, int D, int es) {
   return 16;
 }
 
+// tile, taps, and the q-k-mean exchange of the parallel path (256 / (D/4)
+// lane groups x D floats = 4 KiB)
 static size_t decode_lds_bytes(int rows, int G, int D) {
-  return tile_bytes(rows, G, D, 4) + (size_t)taps_floats(G, D) * 4;
+  return tile_bytes(rows, G, D, 4) + (size_t)taps_floats(G, D) * 4 + 4096;
 }
 
 bool convmix_decode_fits(int G, int d, int m) {
