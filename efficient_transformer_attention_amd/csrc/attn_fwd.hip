@@ -616,9 +616,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const TQ *__restric
       __builtin_amdgcn_sched_barrier(0);
       sm(j);
     };
+    // the matrix phase runs at a raised wave priority: on each SIMD its wave
+    // and the other half's softmax wave compete for issue, and the K
+    // fragment reads and MFMAs going first keeps the matrix core fed (5%
+    // faster than equal priorities at T = 8192 and 16384)
     auto pv_qk_phase = [&](int jk) {
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
       load_frags(0, jk, X, Y);
       mfma_phase(Y, Y);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
     };
 
     // Slots, both halves (2 * ntiles + 2 barriers):
