@@ -194,7 +194,11 @@ size_t cca_prefill_workspace_size(const cca_config *cfg);
 size_t cca_decode_workspace_size(const cca_config *cfg, int32_t cache_len);
 
 /* Prefill: the whole forward pass over x [B, T, E] -> y [B, T, E]
- * (x, y in cfg.dtype; they must not overlap).
+ * (x, y in cfg.dtype; they must not overlap): down-projection, the
+ * convolutions, q-k-mean, value-shift, norm and RoPE in the latent space,
+ * causal attention among the latent heads, up-projection [GS-EN "1. Problem
+ * Statement" (training and prefill over whole sequences); GS-EN "2.
+ * Methodology" (the steps)].
  * state_out (nullable): when given, also writes the decode state after the
  * T tokens: k_cache / v_cache slots [0, T) (capacity >= T), conv_q, conv_k
  * and (with value-shift) vshift.  Members left NULL are skipped.
@@ -217,7 +221,10 @@ cca_status cca_prefill_forward_fused(const cca_config *cfg, const cca_weights *w
                                      void *stream);
 
 /* Decode step: one new token per sequence at position cache_len (uniform over
- * the batch).  x_t [B, E] -> y_t [B, E].
+ * the batch).  x_t [B, E] -> y_t [B, E].  The new token's latent k and v join
+ * the compressed cache, which its query heads attend over [GS-EN "1. Problem
+ * Statement" (the cache read at every decoding step); GS-EN "2. Methodology"
+ * / Extension: CCGQA (one compressed kv head per query group)].
  * state_in: cache slots [0, cache_len) and the carried conv window / vshift.
  *   The new k and v rows are written into state_in's cache at slot cache_len
  *   (capacity must exceed cache_len).
@@ -395,7 +402,12 @@ const char *cca_status_string(cca_status s);
 /* ------------------------------------------------------------------------
  * Stage calls.  Each launches exactly the kernel(s) of one step of the
  * forward pass on the buffers of a prefill or decode workspace, so the steps
- * can be checked against the oracle's intermediates and timed one by one.
+ * can be checked against the oracle's intermediates and timed one by one:
+ * downproj [GS-EN "2. Methodology" / Down-Projection]; convmix
+ * [/ Convolutional Mixing, / Q-K-Mean, / Value-Shift, / RoPE Integration];
+ * attention [/ Latent Space Operations, / Extension: CCGQA]; upproj (the
+ * projection back to the model width after the latent attention [/ Latent
+ * Space Operations]).
  * cca_prefill_forward == downproj, convmix, attention, upproj in this order
  * on the same workspace; cca_decode_step == decode_downproj, decode_mix,
  * decode_attention, decode_upproj.
@@ -428,8 +440,11 @@ const char *cca_status_string(cca_status s);
 enum { CCA_WS_QKV = 0, CCA_WS_Q = 1, CCA_WS_K = 2, CCA_WS_VT = 3, CCA_WS_O = 4,
        CCA_WS_PART = 5, CCA_WS_SPLITK = 6, CCA_WS_COUNT = 7 };
 
-/* Byte offsets of the buffers above inside a prefill (decode: cache_len >= 0)
- * workspace; unused slots are set to SIZE_MAX.  Host-only. */
+/* Byte offsets of the buffers above (the intermediates between the steps of
+ * GS-EN "2. Methodology") inside a prefill (decode: cache_len >= 0)
+ * workspace; unused slots are set to SIZE_MAX.  Returns the status
+ * cca_validate_config gives an invalid cfg, CCA_ERR_INVALID_ARG for a NULL
+ * offsets or a negative cache_len.  Host-only. */
 cca_status cca_prefill_workspace_layout(const cca_config *cfg, size_t offsets[CCA_WS_COUNT]);
 cca_status cca_decode_workspace_layout(const cca_config *cfg, int32_t cache_len,
                                        size_t offsets[CCA_WS_COUNT]);
