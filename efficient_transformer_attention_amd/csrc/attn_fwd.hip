@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
                                                           TV *__restrict__ o,
                                                           float *__restrict__ lse, int B, int T, int Tp,
                                                           int Hq, int Hkv, int G, int hq, int nsub,
-                                                          int npb, int use_norm) {
+                                                          int npb, int use_norm, int fold) {
   typedef Mfma32<TQ> MQ;
   typedef Mfma32<TV> MV;
   typedef AttnTile<TQ, TV, D> TL;
@@ -104,10 +104,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const TQ *__restrict__
   const int l32 = lane & 31, hl = lane >> 5;
   const int pos_per = 128 / hq;
 
-  // heavy-first: logical block order walks position blocks from the end
+  // heavy-first: logical block order walks position blocks from the end.
+  // fold (a grid of one round, two workgroups per CU, even npb): the second
+  // half of the grid walks them from the start instead, so that workgroups
+  // id and id + grid/2, which the dispatcher places on one CU, hold causal
+  // work that adds up to the same total on every CU
   int id = blockIdx.x;
   const int rest = B * Hkv * nsub;
-  const int pb = npb - 1 - id / rest;
+  const int half = (npb / 2) * rest;
+  const int pb = fold && id >= half ? (id - half) / rest : npb - 1 - id / rest;
   id %= rest;
   const int sub = id % nsub;
   id /= nsub;
@@ -753,8 +758,12 @@ static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *
   const int pos_per = 128 / hq;
   const int npb = (s.T + pos_per - 1) / pos_per;
   const int grid = npb * s.B * s.Hkv * nsub;
+#ifndef CCA_ATTN_FOLD
+#define CCA_ATTN_FOLD 1
+#endif
+  const int fold = CCA_ATTN_FOLD && npb % 2 == 0 && grid <= 2 * device_cu_count() ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_kernel<TQ, TV, D>), dim3(grid), dim3(256), 0, stream, q, k, vt, tau,
-                     o, lse, s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb, s.use_norm);
+                     o, lse, s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb, s.use_norm, fold);
   return hipGetLastError();
 }
 
