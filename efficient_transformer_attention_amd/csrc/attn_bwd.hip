@@ -767,11 +767,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_dma_kernel(
 #pragma unroll
   for (int i = 0; i < 2; ++i) dvt[i] = dkt[i] = zero16();
 
-  // one 32-query half of a stage
-  auto half = [&](const unsigned char *st, int t0, int sh, auto edge_tag) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
+  // one 32-query half of a stage, in three steps: S = Q K^T and dP = dO V^T
+  // (mm1), P and dS (sm), dV^T += dO^T P and dK^T += Q^T dS (mm2)
+  auto mm1 = [&](const unsigned char *st, int sh, f32x16 &sacc, f32x16 &dpacc) {
     const int row = 32 * sh + l32;
-    f32x16 sacc = zero16(), dpacc = zero16();
+    sacc = zero16();
+    dpacc = zero16();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int col = c * 16 + hl * 8;
@@ -779,6 +780,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_dma_kernel(
       dpacc = MV::mma(*reinterpret_cast<const typename MV::frag *>(st + OFF_DO + tile_off(row, col)),
                       vf[c], dpacc);
     }
+  };
+  auto sm = [&](const unsigned char *st, int t0, int sh, f32x16 &sacc, f32x16 &dpacc, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const float *ld = reinterpret_cast<const float *>(st + OFF_LD);
     const int u = u0 + l32;
 #pragma unroll
@@ -796,6 +800,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_dma_kernel(
         dpacc[a] = ds;
       }
     }
+  };
+  auto mm2 = [&](const unsigned char *st, int sh, const f32x16 &sacc, const f32x16 &dpacc) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       float pv[8], dsv[8];
@@ -816,6 +822,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_dma_kernel(
       }
     }
   };
+  auto half = [&](const unsigned char *st, int t0, int sh, auto edge_tag) {
+    f32x16 sacc, dpacc;
+    mm1(st, sh, sacc, dpacc);
+    sm(st, t0, sh, sacc, dpacc, edge_tag);
+    mm2(st, sh, sacc, dpacc);
+  };
+  // both halves away from the diagonal and the sequence end, in one block:
+  // the second half's S and dP MFMAs run under the first half's exponentials
+  // and its dV / dK MFMAs under the second half's (same sums, same order)
+  auto both = [&](const unsigned char *st, int t0) {
+    f32x16 s0, d0, s1, d1;
+    mm1(st, 0, s0, d0);
+    mm1(st, 1, s1, d1);
+    sm(st, t0, 0, s0, d0, std::false_type{});
+    mm2(st, 0, s0, d0);
+    sm(st, t0, 1, s1, d1, std::false_type{});
+    mm2(st, 1, s1, d1);
+  };
 
   // ring: at the top of stage it, stages it + 1 .. it + 3 may be in flight
   issue(0, 0);
@@ -835,12 +859,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_dma_kernel(
     const int t0 = kblk0 + (it % ntq) * 64;
     const unsigned char *st = smem + (it % NBUF) * STAGE;
     if (u0 < T) {
+      if (t0 >= u0 + 32 && t0 + 63 < T) {
+        both(st, t0);
+      } else {
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const int ts = t0 + 32 * sh;
-        if (ts + 31 < u0) continue;                        // every query before this wave's keys
-        if (ts < u0 + 32 || ts + 31 >= T) half(st, t0, sh, std::true_type{});
-        else half(st, t0, sh, std::false_type{});
+        for (int sh = 0; sh < 2; ++sh) {
+          const int ts = t0 + 32 * sh;
+          if (ts + 31 < u0) continue;                      // every query before this wave's keys
+          if (ts < u0 + 32 || ts + 31 >= T) half(st, t0, sh, std::true_type{});
+          else half(st, t0, sh, std::false_type{});
+        }
       }
     }
     // stage it + 1 landed (this wave's part), then every wave's part
@@ -942,10 +970,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(
   f32x16 acc[2];
   acc[0] = acc[1] = zero16();
 
-  auto half = [&](const unsigned char *st, int k0, int sh, auto edge_tag) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
+  // one 32-key half of a stage: S^T and dP^T (mm1), dS (sm), dQ^T += K^T
+  // dS^T (mm2)
+  auto mm1 = [&](const unsigned char *st, int sh, f32x16 &sacc, f32x16 &dpacc) {
     const int row = 32 * sh + l32;
-    f32x16 sacc = zero16(), dpacc = zero16();
+    sacc = zero16();
+    dpacc = zero16();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int col = c * 16 + hl * 8;
@@ -953,6 +983,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(
       dpacc = MV::mma(*reinterpret_cast<const typename MV::frag *>(st + OFF_V + tile_off(row, col)),
                       of[c], dpacc);
     }
+  };
+  auto sm = [&](int k0, int sh, const f32x16 &sacc, f32x16 &dpacc, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const float p = __builtin_amdgcn_exp2f(sacc[a] - lq);
@@ -964,6 +997,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(
         dpacc[a] = ds;
       }
     }
+  };
+  auto mm2 = [&](const unsigned char *st, int sh, const f32x16 &dpacc) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       float dsv[8];
@@ -978,6 +1013,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(
                          df, acc[i]);
       }
     }
+  };
+  auto half = [&](const unsigned char *st, int k0, int sh, auto edge_tag) {
+    f32x16 sacc, dpacc;
+    mm1(st, sh, sacc, dpacc);
+    sm(k0, sh, sacc, dpacc, edge_tag);
+    mm2(st, sh, dpacc);
+  };
+  // both halves below the diagonal, in one block: the second half's S and
+  // dP MFMAs run under the first half's exponentials, its dQ MFMAs under the
+  // second half's (same sums, same order)
+  auto both = [&](const unsigned char *st, int k0) {
+    f32x16 s0, d0, s1, d1;
+    mm1(st, 0, s0, d0);
+    mm1(st, 1, s1, d1);
+    sm(k0, 0, s0, d0, std::false_type{});
+    mm2(st, 0, d0);
+    sm(k0, 1, s1, d1, std::false_type{});
+    mm2(st, 1, d1);
   };
 
   const int last = min(qb * 128 + 127, T - 1);
@@ -995,12 +1048,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(
     const int k0 = kt * 64;
     const unsigned char *st = smem + (kt % NBUF) * STAGE;
     if (t0w < T) {
+      if (k0 + 63 <= t0w && t0w + 31 < T) {
+        both(st, k0);
+      } else {
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const int ks = k0 + 32 * sh;
-        if (ks > t0w + 31) continue;                       // every key after this wave's queries
-        if (ks + 31 > t0w || t0w + 31 >= T) half(st, k0, sh, std::true_type{});
-        else half(st, k0, sh, std::false_type{});
+        for (int sh = 0; sh < 2; ++sh) {
+          const int ks = k0 + 32 * sh;
+          if (ks > t0w + 31) continue;                     // every key after this wave's queries
+          if (ks + 31 > t0w || t0w + 31 >= T) half(st, k0, sh, std::true_type{});
+          else half(st, k0, sh, std::false_type{});
+        }
       }
     }
     if (kt + 2 < nkt) wait_vmcnt<PER_WAVE>();
