@@ -394,6 +394,7 @@ def prefill_config(cca, T, name, K, dev):
     }
 
 
+TRAIN_WORKLOAD = "train_cca_prefill_b4_t2048"
 KERNEL_WORKLOADS = ("cca_prefill_b4_t2048", "ccgqa_prefill_t8192", "ccgqa_prefill_t16384",
                     "ccgqa_decode_b64_l32768")
 
@@ -426,6 +427,32 @@ def kernels_only(args):
         torch.cuda.synchronize()
         print(f"[kernels] {name} done", file=sys.stderr, flush=True)
         del ws, x, y, pw, P
+        torch.cuda.empty_cache()
+    if TRAIN_WORKLOAD in only:
+        # forward_train + backward on the B4 x T2048 prefill shape
+        from synth import make_upstream_grad
+        sp = workload("cca_prefill_b4_t2048")
+        P = make_prefill(sp, seed=0)
+        pw = upload_weights(cca, T, P.weights, dev)
+        cfg = cca.make_config(sp)
+        x = T.to_device(P.x_s, dev)
+        y = torch.empty_like(x)
+        dy = T.to_device(make_upstream_grad(sp, seed=0).dy_s, dev)
+        tws = T.workspace(cca.train_workspace_size(cfg), dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        g = cca.Grads(torch.empty_like(x), torch.empty((sp.n_qkv, sp.d_model), **f32),
+                      torch.empty((sp.d_model, sp.e_q), **f32),
+                      torch.empty((sp.e_q, sp.seq_conv_k), **f32),
+                      torch.empty((sp.e_kv, sp.seq_conv_k), **f32),
+                      torch.empty((sp.n_q_heads, sp.chan_conv_k), **f32),
+                      torch.empty((sp.n_kv_heads, sp.chan_conv_k), **f32),
+                      torch.empty((sp.n_q_heads,), **f32))
+        for _ in range(args.steps + 1):
+            cca.prefill_forward_train(cfg, pw, x, y, tws)
+            cca.prefill_backward(cfg, pw, x, dy, g, tws)
+        torch.cuda.synchronize()
+        print("[kernels] training step done", file=sys.stderr, flush=True)
+        del tws, g, dy, x, y
         torch.cuda.empty_cache()
     if "ccgqa_decode_b64_l32768" not in only:
         return
@@ -697,6 +724,36 @@ def profile_summaries(d):
                                            "bytes": int(byt)}
         mf_lines.append("")
         tr_lines.append("")
+    # ---- training step: the attention backward kernels (and the rest of the
+    # backward, without algorithmic figures), grouped by kernel
+    tdir = os.path.join(d, f"mfma_{TRAIN_WORKLOAD}")
+    if os.path.isdir(tdir):
+        sp = workload("cca_prefill_b4_t2048")
+        pairs = sp.batch * sp.n_q_heads * sp.seq_len * (sp.seq_len + 1) / 2
+        bwd_flops = {"attn_bwd_dkdv": 4 * 2 * sp.head_dim * pairs,   # S, dP, dV, dK
+                     "attn_bwd_dq": 3 * 2 * sp.head_dim * pairs}     # S, dP, dQ
+        byname = {}
+        for x in _counter_dispatches(tdir):
+            if "cca" in x["name"]:
+                byname.setdefault(x["name"], []).append(x)
+        mf_lines += [f"## {TRAIN_WORKLOAD} (forward_train + backward on the B4 x T2048 shape)", "",
+                     f"`--only {TRAIN_WORKLOAD}`; every kernel of the step, averaged over its "
+                     "dispatches after the first.  Algorithmic flops of the two attention-backward "
+                     "kernels: 2 d per visible (query, key) pair and matrix product, 4 products in "
+                     "dK/dV (S, dP, dV, dK) and 3 in dQ (S, dP, dQ; S is recomputed in both).", "",
+                     "| kernel | dispatches | avg (us) | MfmaUtil | MFMA TFLOP/s | algorithmic TFLOP/s "
+                     "(of 2500) |", "|---|---|---|---|---|---|"]
+        for name, ds in sorted(byname.items(), key=lambda kv: -sum(x["dur_ns"] for x in kv[1])):
+            ds = ds[1:] or ds
+            dur = _avg(ds, "dur_ns")
+            cyc = _avg(ds, "GRBM_GUI_ACTIVE") / 8
+            util = _avg(ds, "SQ_VALU_MFMA_BUSY_CYCLES") / (cyc * 1024) if cyc else 0.0
+            mops = (_avg(ds, "SQ_INSTS_VALU_MFMA_MOPS_BF16") + _avg(ds, "SQ_INSTS_VALU_MFMA_MOPS_F16")) * 512
+            fl = next((v for k, v in bwd_flops.items() if k in name), None)
+            atf = f"{fl / (dur * 1e-9) / 1e12:.0f} ({fl / (dur * 1e-9) / 1e12 / 25:.1f}%)" if fl else "-"
+            mf_lines.append(f"| `{name[:70]}` | {len(ds)} | {dur / 1e3:.1f} | {100 * util:.1f}% | "
+                            f"{mops / dur / 1e3:.0f} | {atf} |")
+        mf_lines.append("")
     open(os.path.join(prof, "mfma_util_prefill_b4_t2048_t8192_t16384_decode_b64_l32768.md"), "w").write(
         "\n".join(mf_lines) + "\n")
     open(os.path.join(prof, "hbm_traffic_prefill_b4_t2048_t8192_t16384_decode_b64_l32768.md"), "w").write(
