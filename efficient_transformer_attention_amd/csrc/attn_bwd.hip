@@ -841,21 +841,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_dma_kernel(
     mm2(st, 1, s1, d1);
   };
 
-  // ring: at the top of stage it, stages it + 1 .. it + 3 may be in flight
-  issue(0, 0);
-  if (nst > 1) issue(1, 1);
-  if (nst > 2) {
-    issue(2, 2);
-    wait_vmcnt<2 * PER_WAVE>();
-  } else if (nst > 1) {
-    wait_vmcnt<PER_WAVE>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  // ring: at the top of stage it, stages it + 1 .. it + NBUF - 1 may be in
+  // flight; wait_ahead(n): this wave's DMA of all but the last n issued
+  // stages has landed
+  auto wait_ahead = [&](int n) {
+    if (n >= 2) wait_vmcnt<2 * PER_WAVE>();
+    else if (n == 1) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
+  };
+  for (int s0 = 0; s0 < NBUF - 1 && s0 < nst; ++s0) issue(s0, s0);
+  wait_ahead(min(nst, NBUF - 1) - 1);
   lds_barrier();
   for (int it = 0; it < nst; ++it) {
     // the slot of stage it - 1 is free since the last barrier
-    if (it + 3 < nst) issue(it + 3, (it + 3) % NBUF);
+    if (it + NBUF - 1 < nst) issue(it + NBUF - 1, (it + NBUF - 1) % NBUF);
     const int t0 = kblk0 + (it % ntq) * 64;
     const unsigned char *st = smem + (it % NBUF) * STAGE;
     if (u0 < T) {
@@ -872,9 +871,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_dma_kernel(
       }
     }
     // stage it + 1 landed (this wave's part), then every wave's part
-    if (it + 3 < nst) wait_vmcnt<2 * PER_WAVE>();
-    else if (it + 2 < nst) wait_vmcnt<PER_WAVE>();
-    else wait_vmcnt<0>();
+    wait_ahead(min(nst, it + NBUF) - (it + 2));
     lds_barrier();
   }
 
