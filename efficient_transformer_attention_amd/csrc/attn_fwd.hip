@@ -758,10 +758,7 @@ static hipError_t attn_d(const MixShape &s, const TQ *q, const TQ *k, const TV *
   const int pos_per = 128 / hq;
   const int npb = (s.T + pos_per - 1) / pos_per;
   const int grid = npb * s.B * s.Hkv * nsub;
-#ifndef CCA_ATTN_FOLD
-#define CCA_ATTN_FOLD 1
-#endif
-  const int fold = CCA_ATTN_FOLD && npb % 2 == 0 && grid <= 2 * device_cu_count() ? 1 : 0;
+  const int fold = npb % 2 == 0 && grid <= 2 * device_cu_count() ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_kernel<TQ, TV, D>), dim3(grid), dim3(256), 0, stream, q, k, vt, tau,
                      o, lse, s.B, s.T, s.Tp, s.Hq, s.Hkv, s.G, hq, nsub, npb, s.use_norm, fold);
   return hipGetLastError();
