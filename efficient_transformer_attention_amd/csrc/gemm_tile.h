@@ -62,14 +62,28 @@ __device__ __forceinline__ void dma_gemm_tile(const bf16 *__restrict__ A,
     doff[u] = grow < (isA ? M : N) ? (unsigned)(((size_t)grow * (isA ? lda : ldb) + chunk * 8) * 2)
                                    : (isA ? a_bytes : b_bytes);
   }
+  const int nk = klen / BK;
+  // SPREAD (tiles with at least 3 MFMAs per DMA instruction of a wave): the
+  // refill DMAs and the next tile's fragment reads are placed among the
+  // MFMAs instead of in a burst after the barrier.  Keeping them in the
+  // MFMAs' basic block means issuing every refill, so tiles at or past nk go
+  // out as reads past the operand (zeros, no memory access) into a slot that
+  // is never read again, and every wave always has STAGES - 2 stages ahead.
+  constexpr int NMMA = KK * TM * TN;
+  constexpr bool SPREAD = NMMA >= 3 * PER_WAVE;
   auto issue = [&](int kt, int slot) {
     unsigned char *base = smem + slot * STAGE + wave * 1024;
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       const bool isA = u < A_INS / 4;
       unsigned char *dst = isA ? base + u * 4096 : base + A_INS * 1024 + (u - A_INS / 4) * 4096;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(dst), 16, (int)doff[u],
-                                               (kbeg + kt * BK) * 2, 0, 0);
+      if constexpr (SPREAD) {
+        const unsigned off = kt < nk ? doff[u] + (unsigned)((kbeg + kt * BK) * 2) : (isA ? a_bytes : b_bytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(dst), 16, (int)off, 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, as_lds(dst), 16, (int)doff[u],
+                                                 (kbeg + kt * BK) * 2, 0, 0);
+      }
     }
   };
 
@@ -123,25 +137,38 @@ __device__ __forceinline__ void dma_gemm_tile(const bf16 *__restrict__ A,
     wait_vmcnt<0>();
   };
 
-  const int nk = klen / BK;
   // iteration kt < nk - 1: tile kt + 1 is read into registers while tile kt
   // (already in registers) is multiplied; tiles up to kt + STAGES - 2 fly
   auto iter = [&](int kt, Frag (&ca)[KK][TM], Frag (&cb)[KK][TN], Frag (&na)[KK][TM],
                   Frag (&nb)[KK][TN]) {
     // tile kt + 1 landed: of the tiles issued so far, those after it may fly
-    wait_stages(min(nk, kt + STAGES - 1) - (kt + 2));
+    wait_stages(SPREAD ? STAGES - 3 : min(nk, kt + STAGES - 1) - (kt + 2));
     // every wave's DMA of tile kt + 1 has landed, and every read of the slot
     // refilled below (tile kt - 1, read during iteration kt - 2) is done
     lds_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    if (SPREAD || kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
     load((kt + 1) % STAGES, na, nb);
     mma(ca, cb);
+    if constexpr (SPREAD) {
+      // two fragment reads per MFMA, then one DMA per two MFMAs, then the rest
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      }
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM: the DMA
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMMA - 3 * PER_WAVE, 0);
+    }
   };
 
 #pragma unroll
   for (int s0 = 0; s0 < STAGES - 1; ++s0)
-    if (s0 < nk) issue(s0, s0);
-  wait_stages(min(nk, STAGES - 1) - 1);
+    if (SPREAD || s0 < nk) issue(s0, s0);
+  wait_stages(SPREAD ? STAGES - 2 : min(nk, STAGES - 1) - 1);
   lds_barrier();
   Frag fa0[KK][TM], fb0[KK][TN], fa1[KK][TM], fb1[KK][TN];
   load(0, fa0, fb0);
@@ -156,7 +183,8 @@ __device__ __forceinline__ void dma_gemm_tile(const bf16 *__restrict__ A,
   } else {
     mma(fa0, fb0);
   }
-
+  // the zero-fill DMAs of the tail land before the caller reuses LDS
+  if constexpr (SPREAD) wait_vmcnt<0>();
 }
 
 }  // namespace cca
