@@ -275,7 +275,8 @@ def multi_decode(cca, T, sd, dcfg, dw, dl, Lmax, st, K, dev, m):
 
 
 def training_step(cca, T, sp, pcfg, pw, x, dev, K):
-    """forward_train + backward on the prefill workload, timed with HIP events."""
+    """forward_train + backward on the prefill workload: the step and each half
+    timed K calls back to back between two HIP events."""
     import torch
     from synth import make_upstream_grad
     dy = T.to_device(make_upstream_grad(sp, seed=0).dy_s, dev)
@@ -288,20 +289,15 @@ def training_step(cca, T, sp, pcfg, pw, x, dev, K):
                   torch.empty((sp.n_q_heads, sp.chan_conv_k), **f32),
                   torch.empty((sp.n_kv_heads, sp.chan_conv_k), **f32),
                   torch.empty((sp.n_q_heads,), **f32))
-    for _ in range(2):
+
+    def step():
         cca.prefill_forward_train(pcfg, pw, x, y, tws)
         cca.prefill_backward(pcfg, pw, x, dy, g, tws)
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for e in ev:
-        e[0].record()
-        cca.prefill_forward_train(pcfg, pw, x, y, tws)
-        e[1].record()
-        cca.prefill_backward(pcfg, pw, x, dy, g, tws)
-        e[2].record()
-    torch.cuda.synchronize()
-    fwd = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    bwd = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    # the step, then each half on its own (the backward reads the activations
+    # the last forward left in the workspace), each K calls back to back
+    step_ms = launch_ms(step, K)
+    fwd = launch_ms(lambda: cca.prefill_forward_train(pcfg, pw, x, y, tws), K)
+    bwd = launch_ms(lambda: cca.prefill_backward(pcfg, pw, x, dy, g, tws), K)
     print(f"[bench] training step: forward {fwd:.3f} ms backward {bwd:.3f} ms", file=sys.stderr,
           flush=True)
     B, Tn, d, H = sp.batch, sp.seq_len, sp.head_dim, sp.n_q_heads
@@ -310,8 +306,8 @@ def training_step(cca, T, sp, pcfg, pw, x, dev, K):
     torch.cuda.empty_cache()
     return {"workload": "the prefill workload above, forward_train + backward, seeded dy ~ N(0,1)",
             "forward_ms": round(fwd, 4), "backward_ms": round(bwd, 4),
-            "step_ms": round(fwd + bwd, 4),
-            "tokens_per_s": round(sp.tokens / ((fwd + bwd) * 1e-3), 1),
+            "step_ms": round(step_ms, 4),
+            "tokens_per_s": round(sp.tokens / (step_ms * 1e-3), 1),
             "backward_over_forward": round(bwd / fwd, 3),
             # algorithmic flops of the backward: 5 matmuls of 2d flops per visible
             # pair (S recomputed, dP, dV, dQ, dK) plus the 4 gradient GEMMs
@@ -339,10 +335,11 @@ def settle(fn, seconds=0.3):
 
 def launch_ms(fn, n):
     """Average launch duration of fn (one kernel, or a short fixed sequence):
-    one untimed call, then n calls back to back between two HIP events on
-    torch's current stream, the one the library launches on."""
+    0.05 s of untimed calls (the clocks settle under that kernel's own load),
+    then n calls back to back between two HIP events on torch's current
+    stream, the one the library launches on."""
     import torch
-    fn()
+    settle(fn, 0.05)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a.record()
@@ -361,19 +358,25 @@ def cold_convmix_ms(cca, T, cfg, pw, x, n, dev, call_bytes):
     nw workspaces, each holding the qkv~ that the down-projection wrote there,
     taken round-robin, so a call's input was last touched nw - 1 calls earlier,
     after at least MIX_EVICT_BYTES of other reads and writes.  One untimed
-    pass over all of them, then n calls back to back between two HIP events."""
+    pass over all of them and 0.05 s of round-robin calls (clock settling),
+    then n calls back to back between two HIP events, the rotation carried
+    on."""
     import torch
     nw = 1 + -(-MIX_EVICT_BYTES // int(call_bytes))
     wss = [T.workspace(cca.prefill_workspace_size(cfg), dev) for _ in range(nw)]
     for ws in wss:
         cca.stage_downproj(cfg, pw, x, ws)
-    for ws in wss:
-        cca.stage_convmix(cfg, pw, ws)
+    turn = [0]
+
+    def rr():
+        cca.stage_convmix(cfg, pw, wss[turn[0] % nw])
+        turn[0] += 1
+    settle(rr, 0.05)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a.record()
     for i in range(n):
-        cca.stage_convmix(cfg, pw, wss[i % nw])
+        cca.stage_convmix(cfg, pw, wss[(turn[0] + i) % nw])
     b.record()
     torch.cuda.synchronize()
     del wss
@@ -711,8 +714,14 @@ def profile_summaries(d):
         open(os.path.join(prof, "kernel_trace_prefill_b4_t2048_t8192_t16384_decode_b64_l32768.md"),
              "w").write("\n".join(lines) + "\n")
     # ---- copy calibration of FETCH_SIZE / WRITE_SIZE
+    if not os.path.isdir(os.path.join(d, "fetch_copy")) or not os.path.isdir(os.path.join(d, "write_copy")):
+        print("no counter passes under " + d + ": kernel trace summary only", file=sys.stderr)
+        return
     cf = [x for x in _counter_dispatches(os.path.join(d, "fetch_copy")) if "FETCH_SIZE" in x]
     cw = [x for x in _counter_dispatches(os.path.join(d, "write_copy")) if "WRITE_SIZE" in x]
+    if not cf or not cw:
+        print("no counter passes under " + d + ": kernel trace summary only", file=sys.stderr)
+        return
     big = lambda xs, k: max(xs, key=lambda x: x[k])
     n_copy = 1 << 30
     fetch_factor = n_copy / (big(cf, "FETCH_SIZE")["FETCH_SIZE"] * 1024)
