@@ -310,8 +310,6 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   const int shifted = (s.use_shift && g >= s.Hkv / 2) ? 1 : 0;
   const int vcol = (G + 1) * D;
   const TI *src = qkv + (size_t)b * s.T * N;
-  constexpr int LPU = D / 4;
-  const int li = tid % LPU, ui = tid / LPU;
 
   // Everything the mixing reads reaches LDS by LDS-DMA, with no register
   // staging: the taps and tau, then the tile.  Out-of-range offsets (taps
@@ -349,29 +347,48 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, as_lds(ltau), 4, lane * 4, 0, 0, 0);
     }
   }
-  // the tile: row-major [TC + HALO][CW] without padding, so instruction i
-  // fills its bytes [1024 i, 1024 i + 1024): lane l moves 16-byte chunk
-  // 64 i + l (row chunk / cpr); instruction i goes out from wave i % 4
-  {
-    constexpr int EPC = 16 / (int)sizeof(TI);
-    const int cpr = CW / EPC, nck = (TC + HALO) * cpr;
-    const int tlo = max(t0 - HALO, 0), thi = min(t0 + TC, s.T);
-    const unsigned nbytes = thi > tlo ? (unsigned)((size_t)(thi - tlo) * N * sizeof(TI)) : 0u;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(src + (size_t)tlo * N), 0, nbytes, 0x00020000);
-    for (int i = wv; i * 64 < nck; i += 4) {
-      const int c = i * 64 + lane;
+  // the tile: row-major [TC + HALO][CW] without padding.  It arrives in
+  // steps of srows token rows (upp, the rows the lane groups take in one pass
+  // of the row loop, when the chunk holds four or more such passes): the
+  // halo and the first step's rows before the loop, then the next step's
+  // rows while this step's are mixed, so with the input in HBM the rows of
+  // the first step start before the rest of the tile has arrived (a 64-token
+  // chunk at G = 1: 16.3 against 17.8 us for one wait at B = 4, T = 2048; in
+  // the two-step case of 32-token chunks the extra barrier cost as much as it
+  // saved).  issue_rows(rlo, rhi)
+  // moves tile rows [rlo, rhi): 16-byte chunk c of the tile (row c / cpr)
+  // goes to LDS byte 16 c; instruction i of the range starts at its chunk
+  // c_lo + 64 i, lane l moves chunk c_lo + 64 i + l, and instruction i goes
+  // out from wave i % 4.
+  constexpr int LPU = D / 4;
+  const int upp = 256 / LPU;
+  const int li = tid % LPU, ui = tid / LPU;
+  constexpr int EPC = 16 / (int)sizeof(TI);
+  const int cpr = CW / EPC;
+  const int tlo = max(t0 - HALO, 0), thi = min(t0 + TC, s.T);
+  const unsigned nbytes = thi > tlo ? (unsigned)((size_t)(thi - tlo) * N * sizeof(TI)) : 0u;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(src + (size_t)tlo * N), 0, nbytes, 0x00020000);
+  auto issue_rows = [&](int rlo, int rhi) {
+    const int c_lo = rlo * cpr, c_hi = rhi * cpr;
+    for (int i = wv; c_lo + i * 64 < c_hi; i += 4) {
+      const int c = c_lo + i * 64 + lane;
       const int row = c / cpr, tok = t0 - HALO + row;
       const unsigned off =
           tok >= tlo && tok < thi
               ? (unsigned)(((size_t)(tok - tlo) * N + group_col((c - row * cpr) * EPC, g, G, D, eq, ekv)) *
                            sizeof(TI))
               : nbytes;
-      if (c < nck)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(mix_smem + (size_t)i * 1024), 16, (int)off,
-                                                 0, 0, 0);
+      if (c < c_hi)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(mix_smem + (size_t)(c_lo + i * 64) * 16), 16,
+                                                 (int)off, 0, 0, 0);
     }
-  }
+  };
+  // steps of upp rows when a chunk holds at least four of them, else the
+  // whole chunk at once (always under the grouped channel conv, whose rows
+  // also read the MFMA kernel's output)
+  const int srows = !R1B && TC >= 4 * upp ? upp : TC;
+  issue_rows(0, min(HALO + srows, TC + HALO));
   // the RoPE frequencies come from the kernel arguments (scalar loads)
   if (tid == 0) {
 #pragma unroll
@@ -382,7 +399,6 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   const double th0 = lth[2 * li], th1 = lth[2 * li + 1];
 
   // one token row per lane group, every head slot of the group
-  const int upp = 256 / LPU;
   MixShape sm = s;
   sm.use_mean = MEAN;
   // per-lane bases: row r of this chunk adds r * D to the q / k offsets
@@ -391,50 +407,58 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   const size_t qhead = (size_t)s.Tp * D;               // between the group's query heads
   TV *kcache = OUT ? reinterpret_cast<TV *>(st.k_cache) : nullptr;
   float *blane = OUT && bout ? bout + (size_t)b * s.T * (eq + ekv) + 4 * li : nullptr;
-  for (int r = ui; r < TC; r += upp) {
-    const int tok = t0 + r;
-    const float2 cs0 = rope_cs_theta(tok, th0, s.rope_base);
-    const float2 cs1 = rope_cs_theta(tok, th1, s.rope_base);
-    const TI *cur = tile + (r + HALO) * CW + 4 * li;
-    // q leaves scaled by tau_h * log2(e); rows past the sequence's end are
-    // zero: both factors ride on the normalisation's
-    const bool live = tok < s.T;
-    auto scale = [&](int slot) {
-      return live ? (slot < G ? ltau[slot] * 1.4426950408889634f : 1.f) : 0.f;
-    };
-    auto emit = [&](int slot, float *y) {
-      if (slot < G) {
-        Store4<TQ>::st(qlane + slot * qhead + r * D, y);
-      } else {
-        Store4<TQ>::st(klane + r * D, y);
-        if constexpr (OUT) {
-          size_t row;
-          if (kcache && tok < s.T && cache_row_store(st, b, s.Hkv, g, tok, &row))
-            Store4<TV>::st(kcache + row * D + 4 * li, y);
+  for (int r0 = 0; r0 < TC; r0 += srows) {
+    if (r0 > 0) {
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+    if (r0 + srows < TC) issue_rows(HALO + r0 + srows, min(HALO + r0 + 2 * srows, TC + HALO));
+    const int rend = min(r0 + srows, TC);
+    for (int r = r0 + ui; r < rend; r += upp) {
+      const int tok = t0 + r;
+      const float2 cs0 = rope_cs_theta(tok, th0, s.rope_base);
+      const float2 cs1 = rope_cs_theta(tok, th1, s.rope_base);
+      const TI *cur = tile + (r + HALO) * CW + 4 * li;
+      // q leaves scaled by tau_h * log2(e); rows past the sequence's end are
+      // zero: both factors ride on the normalisation's
+      const bool live = tok < s.T;
+      auto scale = [&](int slot) __attribute__((always_inline)) {
+        return live ? (slot < G ? ltau[slot] * 1.4426950408889634f : 1.f) : 0.f;
+      };
+      auto emit = [&](int slot, float *y) __attribute__((always_inline)) {
+        if (slot < G) {
+          Store4<TQ>::st(qlane + slot * qhead + r * D, y);
+        } else {
+          Store4<TQ>::st(klane + r * D, y);
+          if constexpr (OUT) {
+            size_t row;
+            if (kcache && tok < s.T && cache_row_store(st, b, s.Hkv, g, tok, &row))
+              Store4<TV>::st(kcache + row * D + 4 * li, y);
+          }
         }
+      };
+      if constexpr (R1B) {
+        // grouped channel conv: b comes from the MFMA kernel's output rows
+        const float *brow = r1b + (size_t)(b * s.T + min(tok, s.T - 1)) * (eq + ekv) + 4 * li;
+        auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) __attribute__((always_inline)) {
+          const f32x4 v = tok < s.T ? *reinterpret_cast<const f32x4 *>(
+                                          brow + (slot < G ? (g * G + slot) * D : eq + g * D))
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) bb[c] = v[c];
+          pre = ld4f<TI>(cur + slot * D);
+        };
+        mix_row<D>(G, sm, cs0, cs1, conv, emit, scale);
+      } else {
+        auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) __attribute__((always_inline)) {
+          conv_slot<D, TI>(tile, CW, r + HALO, slot, li, staps, ctaps, bb, pre);
+          if (OUT && blane && tok < s.T)
+            *reinterpret_cast<f32x4 *>(blane + (size_t)tok * (eq + ekv) +
+                                       (slot < G ? (g * G + slot) * D : eq + g * D)) =
+                f32x4{bb[0], bb[1], bb[2], bb[3]};
+        };
+        mix_row<D>(G, sm, cs0, cs1, conv, emit, scale);
       }
-    };
-    if constexpr (R1B) {
-      // grouped channel conv: b comes from the MFMA kernel's output rows
-      const float *brow = r1b + (size_t)(b * s.T + min(tok, s.T - 1)) * (eq + ekv) + 4 * li;
-      auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
-        const f32x4 v = tok < s.T ? *reinterpret_cast<const f32x4 *>(
-                                        brow + (slot < G ? (g * G + slot) * D : eq + g * D))
-                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) bb[c] = v[c];
-        pre = ld4f<TI>(cur + slot * D);
-      };
-      mix_row<D>(G, sm, cs0, cs1, conv, emit, scale);
-    } else {
-      auto conv = [&](int slot, float (&bb)[4], f32x4 &pre) {
-        conv_slot<D, TI>(tile, CW, r + HALO, slot, li, staps, ctaps, bb, pre);
-        if (OUT && blane && tok < s.T)
-          *reinterpret_cast<f32x4 *>(blane + (size_t)tok * (eq + ekv) +
-                                     (slot < G ? (g * G + slot) * D : eq + g * D)) =
-              f32x4{bb[0], bb[1], bb[2], bb[3]};
-      };
-      mix_row<D>(G, sm, cs0, cs1, conv, emit, scale);
     }
   }
 
