@@ -355,11 +355,11 @@ __global__ __launch_bounds__(256) void convmix_prefill_kernel(MixShape s, MixTap
   // the first step start before the rest of the tile has arrived (a 64-token
   // chunk at G = 1: 16.3 against 17.8 us for one wait at B = 4, T = 2048; in
   // the two-step case of 32-token chunks the extra barrier cost as much as it
-  // saved).  issue_rows(rlo, rhi)
-  // moves tile rows [rlo, rhi): 16-byte chunk c of the tile (row c / cpr)
-  // goes to LDS byte 16 c; instruction i of the range starts at its chunk
-  // c_lo + 64 i, lane l moves chunk c_lo + 64 i + l, and instruction i goes
-  // out from wave i % 4.
+  // saved).
+  // issue_rows(rlo, rhi) moves tile rows [rlo, rhi): 16-byte chunk c of the
+  // tile (row c / cpr) goes to LDS byte 16 c; instruction i of the range
+  // starts at its chunk c_lo + 64 i, lane l moves chunk c_lo + 64 i + l (lanes
+  // past the range stay idle), and instruction i goes out from wave i % 4.
   constexpr int LPU = D / 4;
   const int upp = 256 / LPU;
   const int li = tid % LPU, ui = tid / LPU;
