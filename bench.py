@@ -561,20 +561,11 @@ def compare(args):
         y = torch.empty_like(x)
         ws = T.workspace(cca.prefill_workspace_size(cfg), dev)
         del P
-        for _ in range(2):
-            cca.prefill_forward(cfg, pw, x, y, ws)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-        for e in ev:
-            e[0].record()
-            cca.prefill_forward(cfg, pw, x, y, ws)
-            e[1].record()
-            cca.stage_attention(cfg, pw, ws)
-            e[2].record()
-        torch.cuda.synchronize()
-        pre = sum(a.elapsed_time(b) for a, b, _ in ev) / K
-        att = sum(b.elapsed_time(c) for _, b, c in ev) / K
+        # as in the main run: clocks settled, K calls back to back between two
+        # HIP events (the attention stage reads what the last prefill left)
+        settle(lambda: cca.prefill_forward(cfg, pw, x, y, ws), 0.2)
+        pre = launch_ms(lambda: cca.prefill_forward(cfg, pw, x, y, ws), K)
+        att = launch_ms(lambda: cca.stage_attention(cfg, pw, ws), K)
         flops = 2 * 2 * sp.batch * sp.n_q_heads * sp.head_dim * sp.seq_len * (sp.seq_len + 1) / 2
         r = {"T": sp.seq_len, "E": sp.d_model, "heads": f"{sp.n_q_heads}q/{sp.n_kv_heads}kv x {sp.head_dim}",
              "prefill_ms": round(pre, 4), "tokens_per_s": round(sp.tokens / (pre * 1e-3), 1),
